@@ -1,0 +1,223 @@
+"""Python binding of libcsa2 (the CSA2 hot path for MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind the
+C ABI declared in include/csa2.h.  Tensors are torch device tensors (torch provides
+memory and streams); each wrapper checks dtype, shape and contiguity, then passes raw
+pointers and the current HIP stream.  There is no fallback: if the shared library is
+missing or cannot load, importing the binding's entry points raises.
+
+bf16 values travel as their bit patterns in int16 tensors (or as torch.bfloat16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "csa2_index_score", "csa2_topk", "csa2_sparse_attn_decode", "csa2_prefill_chunk",
+    "csa2_topk_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
+    "topk_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
+    "CSA2_TOPK_HIST_FUSED", "Csa2Error",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libcsa2.so")
+CSA2_TOPK_HIST_FUSED = 1
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
+_U32 = ctypes.c_uint32
+
+_SIGS = {
+    "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "csa2_version": (ctypes.c_int, []),
+    "csa2_index_score": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
+    "csa2_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "csa2_topk": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _U32, _P, _SZ, _P]),
+    "csa2_attn_workspace_size": (_SZ, [_I32, _I32]),
+    "csa2_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _F32, _I32, _P, _P,
+                                               _SZ, _P]),
+    "csa2_prefill_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "csa2_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
+                                          _F32, _P, _P, _P, _SZ, _P]),
+}
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+def load_library():
+    """Load libcsa2.so (built by compressed_sparse_kv_csa2_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise Csa2Error(f"{lib_path} is missing: build it with "
+                        "`python -m compressed_sparse_kv_csa2_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(lib_path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().csa2_status_string(status).decode()
+        raise Csa2Error(f"csa2 call failed: {msg} ({status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None:
+        want = tuple(shape)
+        if len(want) != t.dim() or any(w is not None and w != s for w, s in zip(want, t.shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+
+
+_BF16 = (torch.int16, torch.bfloat16)
+_U8 = (torch.uint8,)
+
+
+# ----------------------------------------------------------------------------- sizes
+def csa2_topk_workspace_size(batch: int, n_cols: int, k: int) -> int:
+    return int(load_library().csa2_topk_workspace_size(batch, n_cols, k))
+
+
+def csa2_attn_workspace_size(batch: int, k: int) -> int:
+    return int(load_library().csa2_attn_workspace_size(batch, k))
+
+
+def csa2_prefill_workspace_size(T: int, n_entries: int, k: int) -> int:
+    return int(load_library().csa2_prefill_workspace_size(T, n_entries, k))
+
+
+def _zeros(nbytes: int, device) -> torch.Tensor:
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def topk_workspace(batch, n_cols, k, device="cuda"):
+    """Zero-filled workspace for csa2_topk (and the fused histogram of csa2_index_score)."""
+    return _zeros(csa2_topk_workspace_size(batch, n_cols, k), device)
+
+
+def attn_workspace(batch, k, device="cuda"):
+    return _zeros(csa2_attn_workspace_size(batch, k), device)
+
+
+def prefill_workspace(T, n_entries, k, device="cuda"):
+    return _zeros(csa2_prefill_workspace_size(T, n_entries, k), device)
+
+
+# ----------------------------------------------------------------------------- calls
+def csa2_index_score(q_idx, idx_codes, idx_scale, seq_base, n_valid, scores, cand=None,
+                     topk_ws=None, stream=None):
+    """Scores [B, n_cols] of entries seq_base[b] + (cand[b][c] or c) against q_idx[b]."""
+    B, n_cols = scores.shape
+    _need(q_idx, "q_idx", _BF16, (B, 128))
+    _need(idx_codes, "idx_codes", _U8, (None, 64))
+    _need(idx_scale, "idx_scale", (torch.float32,), (idx_codes.shape[0],))
+    _need(seq_base, "seq_base", (torch.int64,), (B,))
+    _need(n_valid, "n_valid", (torch.int32,), (B,))
+    _need(scores, "scores", (torch.float32,), (B, n_cols))
+    if cand is not None:
+        _need(cand, "cand", (torch.int32,), (B, n_cols))
+    if topk_ws is not None:
+        _need(topk_ws, "topk_ws", _U8)
+    lib = load_library()
+    _check(lib.csa2_index_score(_ptr(q_idx), _ptr(idx_codes), _ptr(idx_scale), _ptr(seq_base),
+                                _ptr(n_valid), _ptr(cand), B, n_cols, _ptr(scores), _ptr(topk_ws),
+                                0 if topk_ws is None else topk_ws.numel(), _stream(stream)))
+
+
+def csa2_topk(scores, n_valid, k, idx_out, score_out=None, cand=None, hist_fused=False,
+              workspace=None, stream=None):
+    """idx_out [B, k]: the k best columns of each row, ascending entry ids, -1 padded."""
+    B, n_cols = scores.shape
+    _need(scores, "scores", (torch.float32,), (B, n_cols))
+    _need(n_valid, "n_valid", (torch.int32,), (B,))
+    _need(idx_out, "idx_out", (torch.int32,), (B, k))
+    if score_out is not None:
+        _need(score_out, "score_out", (torch.float32,), (B, k))
+    if cand is not None:
+        _need(cand, "cand", (torch.int32,), (B, n_cols))
+    if workspace is not None:
+        _need(workspace, "workspace", _U8)
+    lib = load_library()
+    _check(lib.csa2_topk(_ptr(scores), B, n_cols, _ptr(n_valid), _ptr(cand), k, _ptr(idx_out),
+                         _ptr(score_out), CSA2_TOPK_HIST_FUSED if hist_fused else 0, _ptr(workspace),
+                         0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def csa2_sparse_attn_decode(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, out, workspace,
+                            softmax_scale=512 ** -0.5, stream=None):
+    """out [B, 16, 512] f32: one softmax over the selected entries and the window rows."""
+    B = q.shape[0]
+    _need(q, "q", _BF16, (B, 16, 512))
+    _need(kv_codes, "kv_codes", _U8, (None, 256))
+    _need(kv_scale, "kv_scale", _U8, (kv_codes.shape[0], 32))
+    _need(seq_base, "seq_base", (torch.int64,), (B,))
+    k = 0
+    if idx is not None:
+        _need(idx, "idx", (torch.int32,), (B, None))
+        k = idx.shape[1]
+    _need(swa, "swa", _U8, (B, 128, 512))
+    _need(swa_len, "swa_len", (torch.int32,), (B,))
+    _need(out, "out", (torch.float32,), (B, 16, 512))
+    _need(workspace, "workspace", _U8)
+    lib = load_library()
+    _check(lib.csa2_sparse_attn_decode(_ptr(q), _ptr(kv_codes), _ptr(kv_scale), _ptr(seq_base),
+                                       _ptr(idx) if k > 0 else None, k, _ptr(swa), _ptr(swa_len),
+                                       float(softmax_scale), B, _ptr(out), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
+
+
+def csa2_prefill_chunk(q_idx, q, idx_codes, idx_scale, kv_codes, kv_scale, n_entries, ratio, pos0,
+                       k, swa, idx_out, out, workspace, softmax_scale=512 ** -0.5, stream=None):
+    """T queries at positions pos0..pos0+T-1: causal scoring, per-query top-k, attention."""
+    T = q_idx.shape[0]
+    _need(q_idx, "q_idx", _BF16, (T, 128))
+    _need(q, "q", _BF16, (T, 16, 512))
+    _need(idx_codes, "idx_codes", _U8, (None, 64))
+    _need(idx_scale, "idx_scale", (torch.float32,), (idx_codes.shape[0],))
+    _need(kv_codes, "kv_codes", _U8, (None, 256))
+    _need(kv_scale, "kv_scale", _U8, (kv_codes.shape[0], 32))
+    if idx_codes.shape[0] < n_entries or kv_codes.shape[0] < n_entries:
+        raise ValueError("fewer cache entries than n_entries")
+    _need(swa, "swa", _U8, (T + 127, 512))
+    _need(idx_out, "idx_out", (torch.int32,), (T, k))
+    _need(out, "out", (torch.float32,), (T, 16, 512))
+    _need(workspace, "workspace", _U8)
+    lib = load_library()
+    _check(lib.csa2_prefill_chunk(_ptr(q_idx), _ptr(q), _ptr(idx_codes), _ptr(idx_scale),
+                                  _ptr(kv_codes), _ptr(kv_scale), int(n_entries), int(ratio),
+                                  int(pos0), T, int(k), _ptr(swa), float(softmax_scale),
+                                  _ptr(idx_out), _ptr(out), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))

@@ -1,0 +1,126 @@
+// C-ABI front end: argument validation on the host, workspace carving, launches.
+// Declarations and their contracts are in include/csa2.h.
+#include "../../include/csa2.h"
+#include "csa2_internal.h"
+
+#include <stdint.h>
+
+using namespace csa2;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_ALIGNMENT: return "misaligned pointer";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported shape";
+    case CSA2_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int csa2_version(void) { return 100; }
+
+int csa2_index_score(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                     const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
+                     int32_t batch, int32_t n_cols, float* scores, void* topk_ws,
+                     size_t topk_ws_size, void* stream) {
+  if (!q_idx || !idx_codes || !idx_scale || !seq_base || !n_valid || !scores) return CSA2_ERR_INVALID_ARG;
+  if (batch < 1 || n_cols < 1) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(idx_codes, 16) || !aligned(idx_scale, 4) ||
+      !aligned(seq_base, 8) || !aligned(n_valid, 4) || !aligned(scores, 4) ||
+      (cand && !aligned(cand, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  uint32_t* hist1 = nullptr;
+  if (topk_ws) {
+    if (topk_ws_size < topk_ws_bytes(batch, n_cols)) return CSA2_ERR_WORKSPACE;
+    if (!aligned(topk_ws, 256)) return CSA2_ERR_ALIGNMENT;
+    hist1 = topk_ws_carve(topk_ws, batch, n_cols).hist1;
+  }
+  return from_hip(launch_index_score(q_idx, idx_codes, idx_scale, seq_base, n_valid, cand, batch,
+                                     n_cols, scores, hist1, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_topk_workspace_size(int32_t batch, int32_t n_cols, int32_t k) {
+  (void)k;
+  if (batch < 1 || n_cols < 1) return 0;
+  return topk_ws_bytes(batch, n_cols);
+}
+
+int csa2_topk(const float* scores, int32_t batch, int32_t n_cols, const int32_t* n_valid,
+              const int32_t* cand, int32_t k, int32_t* idx_out, float* score_out, uint32_t flags,
+              void* workspace, size_t ws_bytes, void* stream) {
+  if (!scores || !n_valid || !idx_out) return CSA2_ERR_INVALID_ARG;
+  if (batch < 1 || n_cols < 1 || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_INVALID_ARG;
+  if (flags & ~CSA2_TOPK_HIST_FUSED) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(scores, 4) || !aligned(n_valid, 4) || !aligned(idx_out, 4) ||
+      (score_out && !aligned(score_out, 4)) || (cand && !aligned(cand, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  const bool fused = (flags & CSA2_TOPK_HIST_FUSED) != 0;
+  const bool needs_ws = fused || n_cols > kTopkSmallMax;
+  TopkWs ws{};
+  if (needs_ws) {
+    if (!workspace || ws_bytes < topk_ws_bytes(batch, n_cols)) return CSA2_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+    ws = topk_ws_carve(workspace, batch, n_cols);
+  }
+  return from_hip(launch_topk(scores, batch, n_cols, n_valid, cand, k, idx_out, score_out, fused, ws,
+                              static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_attn_workspace_size(int32_t batch, int32_t k) {
+  if (batch < 1 || k < 0) return 0;
+  return attn_ws_bytes(batch, k);
+}
+
+int csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                            const int64_t* seq_base, const int32_t* idx, int32_t k, const uint8_t* swa,
+                            const int32_t* swa_len, float softmax_scale, int32_t batch, float* out,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !kv_codes || !kv_scale || !seq_base || !swa || !swa_len || !out) return CSA2_ERR_INVALID_ARG;
+  if (batch < 1 || k < 0 || k > CSA2_MAX_K || (k > 0 && !idx)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv_codes, 16) || !aligned(swa, 16) || !aligned(seq_base, 8) ||
+      !aligned(swa_len, 4) || !aligned(out, 16) || (idx && !aligned(idx, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  if (!workspace || ws_bytes < attn_ws_bytes(batch, k)) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_attn(0, q, kv_codes, kv_scale, seq_base, idx, k, swa, swa_len, 0,
+                              softmax_scale, batch, out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_prefill_workspace_size(int32_t T, int32_t n_entries, int32_t k) {
+  if (T < 1 || n_entries < 0 || k < 1) return 0;
+  return prefill_ws_bytes(T, n_entries, k);
+}
+
+int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* idx_codes,
+                       const float* idx_scale, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                       int32_t n_entries, int32_t ratio, int64_t pos0, int32_t T, int32_t k,
+                       const uint8_t* swa, float softmax_scale, int32_t* idx_out, float* out,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (!q_idx || !q || !swa || !idx_out || !out) return CSA2_ERR_INVALID_ARG;
+  if (n_entries > 0 && (!idx_codes || !idx_scale || !kv_codes || !kv_scale)) return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || n_entries < 0 || ratio < 1 || pos0 < 0 || k < 1 || k > CSA2_MAX_K)
+    return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(q, 16) || !aligned(swa, 16) || !aligned(idx_out, 4) ||
+      !aligned(out, 16) || (idx_codes && !aligned(idx_codes, 16)) ||
+      (idx_scale && !aligned(idx_scale, 4)) || (kv_codes && !aligned(kv_codes, 16)))
+    return CSA2_ERR_ALIGNMENT;
+  if (!workspace || ws_bytes < prefill_ws_bytes(T, n_entries, k)) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_prefill(q_idx, q, idx_codes, idx_scale, kv_codes, kv_scale, n_entries, ratio,
+                                 pos0, T, k, swa, softmax_scale, idx_out, out, workspace,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

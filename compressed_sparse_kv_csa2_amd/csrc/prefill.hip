@@ -1,0 +1,488 @@
+// a7 causal indexer contraction (BF16 MFMA) and a8 per-query top-k + attention for a
+// prefill chunk: T consecutive query positions of one sequence, each scoring every
+// entry it can see, taking its own top-k and attending over it plus its window
+// ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash", content summary and the
+// Q&A on prefill: prompt tokens run the encoder, whose Full layers score and select for
+// every token; "从V4到V4.1 Flash：架构的激进进化", encoder section: one entry per two
+// tokens).  Visibility is this library's reading: entry j is visible to position p once
+// its last token (j+1)*ratio - 1 is at or before p.
+//
+// S[t][j] = scale_j * (q_t . e2m1(K_j)) is a dense T x N x 128 contraction.  The codes are
+// expanded to bf16 exactly (v_cvt_scalef32_pk_bf16_fp4) straight into the B operand of
+// v_mfma_f32_32x32x16_bf16; the 128 dims are permuted identically on both sides so each
+// lane reads 32 contiguous code bytes.  The fp32 entry scale is applied to the fp32
+// accumulators.  The T x N score matrix is never stored.  Instead:
+//   pass 1 keeps, per row, the maximum over small groups of entries (a lane's column in
+//          8 consecutive 32-entry tiles) and stores it as a 16-bit key prefix (rounded
+//          down).  At least k groups have maxima >= the k-th largest of those maxima, so
+//          that value, theta_t, is a rigorous lower bound on the row's k-th score;
+//   pass 2 recomputes the contraction and appends only scores >= theta_t (typically a
+//          few hundred per row) to a per-row candidate list;
+//   select  resolves each row exactly in LDS (largest scores, ties to the lower entry),
+//          sorts the chosen entries ascending.  A row whose candidates overflow the list
+//          (only possible with massive score ties) is resolved by recomputing its scores
+//          in a streaming radix select.
+// Tiles past the causal frontier of a wave's rows are skipped.
+#include "csa2_device.h"
+#include "csa2_internal.h"
+
+namespace csa2 {
+
+constexpr int kGemmThreads = 256;           // 4 waves x 32 query rows
+constexpr int kGemmRows = 128;
+constexpr int kSplitEntries = 4096;         // entries per workgroup (128 tiles of 32)
+constexpr int kRunTiles = 8;                // group = one lane column over 8 tiles
+constexpr int kGroupsPerSplit = kSplitEntries / (32 * kRunTiles) * 32;  // 512
+constexpr int kCandCap = 8192;              // candidates kept per row
+constexpr int kSelThreads = 256;
+constexpr int kMaxKPow2 = 16384;           // largest k (power of two) the select kernel sorts
+
+struct PrefillWs {
+  uint16_t* gmax;               // [T][G] group maxima as key >> 16 (0 = empty group)
+  float* theta;                 // [T]
+  uint32_t* cnt;                // [T] candidate counts
+  unsigned long long* cand;     // [T][kCandCap] (key << 32 | entry)
+  void* attn;                   // attention workspace (unused by the prefill attention)
+  int G;
+};
+
+static int prefill_splits(int n_entries) { return n_entries > 0 ? (n_entries + kSplitEntries - 1) / kSplitEntries : 1; }
+
+size_t prefill_ws_bytes(int T, int n_entries, int k) {
+  (void)k;
+  const size_t G = (size_t)prefill_splits(n_entries) * kGroupsPerSplit;
+  size_t s = 0;
+  s += align_up((size_t)T * G * 2, 256);
+  s += align_up((size_t)T * 4, 256);
+  s += align_up((size_t)T * 4, 256);
+  s += align_up((size_t)T * kCandCap * 8, 256);
+  return s;
+}
+
+static PrefillWs prefill_ws_carve(void* base, int T, int n_entries) {
+  PrefillWs w;
+  w.G = prefill_splits(n_entries) * kGroupsPerSplit;
+  char* p = static_cast<char*>(base);
+  w.gmax = reinterpret_cast<uint16_t*>(p);
+  p += align_up((size_t)T * w.G * 2, 256);
+  w.theta = reinterpret_cast<float*>(p);
+  p += align_up((size_t)T * 4, 256);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)T * 4, 256);
+  w.cand = reinterpret_cast<unsigned long long*>(p);
+  p += align_up((size_t)T * kCandCap * 8, 256);
+  w.attn = p;
+  return w;
+}
+
+__device__ __forceinline__ int visible(int64_t pos, int ratio, int n_entries) {
+  const int64_t v = (pos + 1) / ratio;
+  return (int)(v < n_entries ? v : n_entries);
+}
+
+// Eight E2M1 codes (one dword) -> bf16x8 B/A operand slice.
+__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w) {
+  const bf16x2 a = fp4x2_bf16<0>(w), b = fp4x2_bf16<1>(w), c = fp4x2_bf16<2>(w),
+               d = fp4x2_bf16<3>(w);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// PASS 1: group maxima.  PASS 2: candidate emission.
+// Accumulator layout of v_mfma_f32_32x32x16_bf16: lane l holds column l % 32 and rows
+// 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  Operands: lane l holds row/column l % 32 and
+// k-slice 8*(l/32)..+7; the dims behind k-step kk for half h are 64h + 8kk .. +7.
+template <int PASS>
+__global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
+    const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = blockIdx.x * kGemmRows + wave * 32;
+  if (row0 >= T) return;  // no LDS / barriers in this kernel
+  const int split = blockIdx.y;
+  const int e_begin = split * kSplitEntries;
+  const int e_end = min(e_begin + kSplitEntries, n_entries);
+  const int rl = lane & 31, half = lane >> 5;
+
+  // A operand: query row row0 + rl, dims 64*half .. +63
+  bf16x8 a[8];
+  {
+    const int ar = min(row0 + rl, T - 1);
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)ar * kDIdx + 64 * half);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) a[kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+  }
+  int nvis[16];
+  int rowid[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+    rowid[r] = t;
+    nvis[r] = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
+  }
+  const int wave_nmax = visible(pos0 + min(row0 + 31, T - 1), ratio, n_entries);
+  float th[16];
+  if (PASS == 2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) th[r] = rowid[r] < T ? ws.theta[rowid[r]] : __builtin_inff();
+  }
+
+  const int n_runs = kSplitEntries / (32 * kRunTiles);
+  for (int run = 0; run < n_runs; ++run) {
+    const int run_e0 = e_begin + run * 32 * kRunTiles;
+    float rm[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rm[r] = -__builtin_inff();
+    if (run_e0 < e_end && run_e0 < wave_nmax) {
+      for (int tt = 0; tt < kRunTiles; ++tt) {
+        const int e0 = run_e0 + tt * 32;
+        if (e0 >= e_end || e0 >= wave_nmax) break;
+        const int col = e0 + rl;
+        uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0;
+        float sc = 0.f;
+        if (col < n_entries) {
+          const uint4* cp = reinterpret_cast<const uint4*>(codes + (size_t)col * kIdxCodeBytes + 32 * half);
+          c0 = cp[0];
+          c1 = cp[1];
+          sc = scale[col];
+        }
+        f32x16 acc = {};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp4x8_bf16(c0.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp4x8_bf16(c0.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], fp4x8_bf16(c0.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], fp4x8_bf16(c0.w), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[4], fp4x8_bf16(c1.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[5], fp4x8_bf16(c1.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp4x8_bf16(c1.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp4x8_bf16(c1.w), acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = acc[r] * sc;
+          const bool vis = col < nvis[r];
+          if (PASS == 1) {
+            rm[r] = vis ? fmaxf(rm[r], s) : rm[r];
+          } else if (vis && s >= th[r]) {
+            const uint32_t slot = atomic_add_agent(&ws.cnt[rowid[r]], 1u);
+            if (slot < (uint32_t)kCandCap)
+              ws.cand[(size_t)rowid[r] * kCandCap + slot] =
+                  ((unsigned long long)score_key(s) << 32) | (uint32_t)col;
+          }
+        }
+      }
+    }
+    if (PASS == 1) {
+      const int g = split * kGroupsPerSplit + run * 32 + rl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (rowid[r] < T) {
+          const uint16_t key16 =
+              rm[r] == -__builtin_inff() ? (uint16_t)0 : (uint16_t)(score_key(rm[r]) >> 16);
+          ws.gmax[(size_t)rowid[r] * ws.G + g] = key16;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- helpers
+__device__ void find_bin_wave(const uint32_t* h, int nbins, uint32_t need, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) {
+    out[0] = 0u;
+    out[1] = 0u;
+  }
+  const int per = nbins / 64;
+  const int hi = nbins - lane * per;
+  uint32_t sum = 0;
+  for (int i = 1; i <= per; ++i) sum += h[hi - i];
+  uint32_t incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  const uint32_t excl = incl - sum;
+  if (excl < need && need <= incl) {
+    uint32_t acc = excl;
+    for (int i = 1; i <= per; ++i) {
+      uint32_t c = h[hi - i];
+      if (acc + c >= need) {
+        out[0] = (uint32_t)(hi - i);
+        out[1] = acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+}
+
+__device__ uint32_t block_scan_excl(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      uint32_t t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[16] = run;
+  }
+  __syncthreads();
+  const uint32_t r = scratch[wave] + incl - v;
+  *total = scratch[16];
+  __syncthreads();
+  return r;
+}
+
+// theta_t: the k-th largest group maximum of row t as a float lower bound, or -inf when
+// the row has at most k visible entries or fewer than k non-empty groups.
+__global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, int ratio,
+                                                               int64_t pos0, int T, int k,
+                                                               PrefillWs ws) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_res[4];
+  __shared__ uint32_t s_scan[32];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_t = visible(pos0 + t, ratio, n_entries);
+  if (tid == 0) ws.cnt[t] = 0u;  // fresh candidate count for pass 2
+  if (n_t <= k) {
+    if (tid == 0) ws.theta[t] = -__builtin_inff();
+    return;
+  }
+  const uint16_t* g = ws.gmax + (size_t)t * ws.G;
+  uint32_t nonempty = 0;
+  for (int i = tid; i < ws.G; i += kSelThreads) nonempty += g[i] != 0 ? 1u : 0u;
+  uint32_t total;
+  block_scan_excl(nonempty, s_scan, &total);
+  if (total < (uint32_t)k) {
+    if (tid == 0) ws.theta[t] = -__builtin_inff();
+    return;
+  }
+  uint32_t need = (uint32_t)k, prefix = 0;
+  for (int level = 0; level < 2; ++level) {
+    const int shift = 8 - 8 * level;
+    s_hist[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < ws.G; i += kSelThreads) {
+      const uint32_t v = g[i];
+      if (v != 0u && (level == 0 || (v >> 8) == prefix)) atomicAdd(&s_hist[(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) find_bin_wave(s_hist, 256, need, s_res);
+    __syncthreads();
+    need -= s_res[1];
+    prefix = level == 0 ? s_res[0] : (prefix << 8) | s_res[0];
+    __syncthreads();
+  }
+  if (tid == 0) ws.theta[t] = key_score(prefix << 16);
+}
+
+// Score of entry j for a query held as 64 bf16 pairs (fp32, same rounding class as the
+// MFMA path: exact products, fp32 sums).
+__device__ __forceinline__ float score_row(const bf16x2 (&qq)[64], const uint8_t* codes, const float* scale,
+                                           int j) {
+  const uint4* cp = reinterpret_cast<const uint4*>(codes + (size_t)j * kIdxCodeBytes);
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = cp[i];
+    const uint32_t ws_[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int base = 16 * i + 4 * d;
+      a0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_bf16<0>(ws_[d]), qq[base + 0], a0, false);
+      a1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_bf16<1>(ws_[d]), qq[base + 1], a1, false);
+      a0 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_bf16<2>(ws_[d]), qq[base + 2], a0, false);
+      a1 = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_bf16<3>(ws_[d]), qq[base + 3], a1, false);
+    }
+  }
+  return (a0 + a1) * scale[j];
+}
+
+// Exact per-row top-k from the candidate list (or, on overflow, from recomputed scores),
+// ascending entry ids, -1 padded.
+__global__ __launch_bounds__(kSelThreads) void k_prefill_select(
+    const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, int k,
+    int k_pow2, int32_t* __restrict__ idx_out, PrefillWs ws) {
+  extern __shared__ unsigned long long s_dyn[];
+  unsigned long long* s_cand = s_dyn;                                         // [kCandCap]
+  uint32_t* s_sel = reinterpret_cast<uint32_t*>(s_dyn + kCandCap);             // [k_pow2]
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_res[4];
+  __shared__ uint32_t s_scan[32];
+  __shared__ uint32_t s_nsel;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n_t = visible(pos0 + t, ratio, n_entries);
+  const uint32_t C = ws.cnt[t];
+  int32_t* orow = idx_out + (size_t)t * k;
+  const uint32_t k_eff = (uint32_t)min(k, n_t);
+
+  if (C <= (uint32_t)kCandCap) {
+    // ---- fast path: exact selection among the candidates
+    for (uint32_t i = tid; i < C; i += kSelThreads) s_cand[i] = ws.cand[(size_t)t * kCandCap + i];
+    if (tid == 0) s_nsel = 0u;
+    __syncthreads();
+    // composite: key (32 bits) then ~entry (a lower entry ranks higher); 8 digits of 8 bits
+    uint32_t need = k_eff;
+    unsigned long long prefix = 0ull, pmask = 0ull;
+    uint32_t remaining = C;
+    for (int level = 0; level < 8 && need > 0 && need < remaining; ++level) {
+      const int shift = 56 - 8 * level;
+      s_hist[tid] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < C; i += kSelThreads) {
+        const unsigned long long v = s_cand[i];
+        const unsigned long long comp = (v & 0xffffffff00000000ull) | (uint32_t)~(uint32_t)v;
+        if ((comp & pmask) == prefix) atomicAdd(&s_hist[(comp >> shift) & 255ull], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) find_bin_wave(s_hist, 256, need, s_res);
+      __syncthreads();
+      const uint32_t sel = s_res[0];
+      // everything above the bin at this level (within the prefix) is taken
+      for (uint32_t i = tid; i < C; i += kSelThreads) {
+        const unsigned long long v = s_cand[i];
+        const unsigned long long comp = (v & 0xffffffff00000000ull) | (uint32_t)~(uint32_t)v;
+        if ((comp & pmask) == prefix && ((comp >> shift) & 255ull) > sel) {
+          const uint32_t p = atomicAdd(&s_nsel, 1u);
+          if (p < (uint32_t)k_pow2) s_sel[p] = (uint32_t)v;
+        }
+      }
+      need -= s_res[1];
+      remaining = s_hist[sel];
+      prefix |= (unsigned long long)sel << shift;
+      pmask |= 255ull << shift;
+      __syncthreads();
+    }
+    if (need > 0) {  // take every candidate still matching the prefix
+      for (uint32_t i = tid; i < C; i += kSelThreads) {
+        const unsigned long long v = s_cand[i];
+        const unsigned long long comp = (v & 0xffffffff00000000ull) | (uint32_t)~(uint32_t)v;
+        if ((comp & pmask) == prefix) {
+          const uint32_t p = atomicAdd(&s_nsel, 1u);
+          if (p < (uint32_t)k_pow2) s_sel[p] = (uint32_t)v;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t ns = min(s_nsel, (uint32_t)k);
+    for (int i = tid; i < k_pow2; i += kSelThreads) if ((uint32_t)i >= ns) s_sel[i] = 0xffffffffu;
+    __syncthreads();
+    // bitonic sort ascending
+    for (int size = 2; size <= k_pow2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < k_pow2 / 2; i += kSelThreads) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint32_t x = s_sel[lo], y = s_sel[hi];
+          if ((x > y) == up) {
+            s_sel[lo] = y;
+            s_sel[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < k; i += kSelThreads) orow[i] = (uint32_t)i < ns ? (int32_t)s_sel[i] : -1;
+    return;
+  }
+
+  // ---- overflow: recompute the row's scores in a streaming exact selection
+  bf16x2 qq[64];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)t * kDIdx);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = qp[i];
+      qq[4 * i + 0] = __builtin_bit_cast(bf16x2, v.x);
+      qq[4 * i + 1] = __builtin_bit_cast(bf16x2, v.y);
+      qq[4 * i + 2] = __builtin_bit_cast(bf16x2, v.z);
+      qq[4 * i + 3] = __builtin_bit_cast(bf16x2, v.w);
+    }
+  }
+  uint32_t need = k_eff;
+  unsigned long long prefix = 0ull, pmask = 0ull;
+  for (int level = 0; level < 8 && need > 0; ++level) {
+    const int shift = 56 - 8 * level;
+    s_hist[tid] = 0u;
+    __syncthreads();
+    for (int j = tid; j < n_t; j += kSelThreads) {
+      const unsigned long long comp =
+          ((unsigned long long)score_key(score_row(qq, codes, scale, j)) << 32) | (uint32_t)~(uint32_t)j;
+      if ((comp & pmask) == prefix) atomicAdd(&s_hist[(comp >> shift) & 255ull], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) find_bin_wave(s_hist, 256, need, s_res);
+    __syncthreads();
+    need -= s_res[1];
+    prefix |= (unsigned long long)s_res[0] << shift;
+    pmask |= 255ull << shift;
+    __syncthreads();
+  }
+  // composites are unique: select comp >= prefix (all 64 bits resolved) in entry order
+  uint32_t written = 0;
+  for (int c0 = 0; c0 < n_t; c0 += kSelThreads) {
+    const int j = c0 + tid;
+    bool take = false;
+    if (j < n_t) {
+      const unsigned long long comp =
+          ((unsigned long long)score_key(score_row(qq, codes, scale, j)) << 32) | (uint32_t)~(uint32_t)j;
+      take = k_eff > 0 && comp >= prefix;
+    }
+    uint32_t tot;
+    const uint32_t p = block_scan_excl(take ? 1u : 0u, s_scan, &tot);
+    if (take && written + p < (uint32_t)k) orow[written + p] = j;
+    written += tot;
+  }
+  for (int i = (int)written + tid; i < k; i += kSelThreads) orow[i] = -1;
+}
+
+hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_t* idx_codes,
+                          const float* idx_scale, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                          int n_entries, int ratio, int64_t pos0, int T, int k, const uint8_t* swa,
+                          float softmax_scale, int32_t* idx_out, float* out, void* ws_base,
+                          hipStream_t stream) {
+  PrefillWs ws = prefill_ws_carve(ws_base, T, n_entries);
+  const int n_splits = prefill_splits(n_entries);
+  const dim3 ggrid((T + kGemmRows - 1) / kGemmRows, n_splits);
+  if (n_entries > 0) {
+    hipLaunchKernelGGL(k_prefill_gemm<1>, ggrid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
+                       idx_scale, n_entries, ratio, pos0, T, ws);
+  }
+  hipLaunchKernelGGL(k_prefill_theta, dim3(T), dim3(kSelThreads), 0, stream, n_entries, ratio, pos0, T,
+                     k, ws);
+  if (n_entries > 0) {
+    hipLaunchKernelGGL(k_prefill_gemm<2>, ggrid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
+                       idx_scale, n_entries, ratio, pos0, T, ws);
+  }
+  int k_pow2 = 1;
+  while (k_pow2 < k) k_pow2 <<= 1;
+  const size_t lds = (size_t)kCandCap * 8 + (size_t)k_pow2 * 4;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_prefill_select), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)((size_t)kCandCap * 8 + (size_t)kMaxKPow2 * 4));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), lds, stream, q_idx, idx_codes,
+                     idx_scale, n_entries, ratio, pos0, T, k, k_pow2, idx_out, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn(1, q, kv_codes, kv_scale, nullptr, idx_out, k, swa, nullptr, pos0, softmax_scale,
+                     T, out, ws.attn, stream);
+}
+
+}  // namespace csa2

@@ -1,0 +1,201 @@
+/*
+ * csa2.h -- C ABI of the CSA2 compressed-sparse-attention hot path for MI355X (gfx950).
+ *
+ * The library computes one CSA2 attention step over an FP4 global KV cache:
+ *   1. index score  -- every visible 68-byte indexer key (128 x E2M1 + fp32 scale) is
+ *                      scored against a 128-d bf16 indexer query (Full mode), or only the
+ *                      entries of a candidate pool are (Reindex mode);
+ *   2. top-k        -- the k best entries, ties to the lower entry index, listed ascending;
+ *   3. attention    -- the selected 288-byte main entries (512 x E2M1 + 32 E4M3 scales) are
+ *                      gathered, dequantised and attended by 16 query heads, merged in one
+ *                      softmax with the layer's own 128-row E4M3 sliding window;
+ *   4. prefill      -- a chunk of queries, each scoring its causally visible keys (a BF16
+ *                      MFMA contraction), taking its own top-k and attending.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [STRUCT] "DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash" (xhh.club):
+ *            Q&A on how the 890-byte global KV figure is derived (entry sizes 288 B and
+ *            68 B); commentary on the four layer modes (Full / Reindex / Reuse, top-512).
+ *   [DEEP]   "DeepSeek V4.1 Flash 深度解析" (daiw.net): part-1 entry on CSA2 (cross-layer
+ *            sharing, hierarchical candidate pool in the decoder); part-4 entry on FP4 in
+ *            the KV cache (main KV 4-bit in its own format, sliding window FP8).
+ *   [V4TO41] "从V4到V4.1 Flash：架构的激进进化" (prism.simon-ai.net): section on the CSA2
+ *            architecture (three modes); section on global KV sharing with per-layer sliding
+ *            windows; decoder section (a first full scan builds a pool of about 16K
+ *            positions, later layers search their top-512 inside it).
+ * Where the pages are silent the readings are: score = fp32 scale x (query . E2M1 codes);
+ * ties to the lowest entry index; every entry and window row is both key and value; one
+ * softmax over their union with the caller's scale (1/sqrt(512)); causal visibility of an
+ * entry once its last token is at or before the query position.
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless stated; the caller owns every buffer.  The
+ *    library allocates nothing, keeps no mutable global state and is re-entrant, except
+ *    that calls sharing one workspace must not overlap in time.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *    asynchronous; kernel faults surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host BEFORE anything is enqueued; on error nothing is
+ *    launched and a negative status is returned (csa2_status_string names it).
+ *  - bf16 values are passed as their 16-bit patterns (uint16_t).  Code planes must be
+ *    16-byte aligned; fp32/int planes 4-byte aligned (int64 8-byte).
+ *  - Workspaces: size them with the *_workspace_size query, zero-fill them ONCE before
+ *    first use (e.g. hipMemset or torch.zeros); every call returns the counters it uses to
+ *    zero before it completes, so a workspace can be reused call after call without
+ *    clearing.  Reusing a workspace across calls on different streams needs the caller's
+ *    ordering.
+ */
+#ifndef CSA2_H_
+#define CSA2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_D_IDX 128      /* indexer key / query width */
+#define CSA2_D_KV 512       /* main KV width */
+#define CSA2_HEADS 16       /* query heads; one shared KV head */
+#define CSA2_SWA 128        /* sliding-window rows per layer and sequence */
+#define CSA2_MAX_K 16384    /* largest k accepted by csa2_topk / csa2_prefill_chunk */
+
+enum csa2_status {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = -1, /* null pointer, negative or out-of-range size */
+  CSA2_ERR_ALIGNMENT = -2,   /* a plane is not aligned as stated above */
+  CSA2_ERR_WORKSPACE = -3,   /* workspace pointer missing or smaller than the query says */
+  CSA2_ERR_UNSUPPORTED = -4, /* a shape the kernels do not handle */
+  CSA2_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+};
+
+/* flags for csa2_topk */
+#define CSA2_TOPK_HIST_FUSED 1u /* csa2_index_score already accumulated the level-1
+                                   radix histogram of `scores` into this workspace */
+
+/* Static description of a status code. */
+const char* csa2_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int csa2_version(void);
+
+/*
+ * csa2_index_score -- a1 Full scan / a3 Reindex re-score.
+ *   [V4TO41] CSA2 architecture section (Full runs the sparse indexer over its keys;
+ *   Reindex picks again with its own indexer query); [STRUCT] Q&A on the 890-byte count
+ *   (68-byte indexer entry = 128 x 4 bit + 4-byte scale).
+ *
+ *   q_idx      bf16 [batch][128]              indexer query of each sequence
+ *   idx_codes  u8   [n_total][64]             E2M1 codes, element 2i in the low nibble
+ *   idx_scale  f32  [n_total]                 per-entry scale
+ *   seq_base   i64  [batch]                   entry number of column 0 of sequence b
+ *   n_valid    i32  [batch]                   visible columns of sequence b (<= n_cols)
+ *   cand       i32  [batch][n_cols] or NULL   Reindex: column c scores entry
+ *                                             seq_base[b] + cand[b][c]; cand < 0 is a hole.
+ *                                             NULL (Full): column c scores seq_base[b] + c.
+ *   scores     f32  [batch][n_cols]  (out)    score_c = scale * sum_d q_d * e2m1(code_cd);
+ *                                             -inf for holes and columns >= n_valid[b].
+ *   topk_ws / topk_ws_bytes  optional: a csa2_topk workspace sized for (batch, n_cols, k);
+ *              when given, the level-1 radix histogram of the scores is accumulated into
+ *              it and the next csa2_topk call on these scores must pass
+ *              CSA2_TOPK_HIST_FUSED.  NULL: no histogram.
+ * Errors: INVALID_ARG (null planes, batch < 1, n_cols < 1), ALIGNMENT, WORKSPACE.
+ */
+int csa2_index_score(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                     const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
+                     int32_t batch, int32_t n_cols, float* scores,
+                     void* topk_ws, size_t topk_ws_bytes, void* stream);
+
+/* Bytes of workspace csa2_topk needs for this shape. */
+size_t csa2_topk_workspace_size(int32_t batch, int32_t n_cols, int32_t k);
+
+/*
+ * csa2_topk -- a2 top-k selection (pool of 16,384 and top-512 alike).
+ *   [STRUCT] commentary on the four layer modes (Reindex re-picks a top-512 inside the
+ *   pool); [V4TO41] decoder section (first layer's full scan yields a pool of about 16K
+ *   positions, later layers search their top-512 in it).
+ *
+ *   scores     f32 [batch][n_cols]            finite scores; columns >= n_valid[b] ignored
+ *   n_valid    i32 [batch]                    device
+ *   cand       i32 [batch][n_cols] or NULL    column -> entry id map; a column whose
+ *                                             cand < 0 is ignored.  Must be ascending in
+ *                                             the entry id over its valid columns (a pool
+ *                                             from a previous call is) so ties by column
+ *                                             are ties by entry id.
+ *   k          1..16384
+ *   idx_out    i32 [batch][k]  (out)          the k best columns (score descending, ties to
+ *                                             the lower column), written ASCENDING as entry
+ *                                             ids (cand[b][c] or c); -1 padded when fewer
+ *                                             than k columns are valid.
+ *   score_out  f32 [batch][k] or NULL (out)   score of each listed entry, -inf for padding
+ *   flags      CSA2_TOPK_HIST_FUSED or 0
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE.
+ */
+int csa2_topk(const float* scores, int32_t batch, int32_t n_cols, const int32_t* n_valid,
+              const int32_t* cand, int32_t k, int32_t* idx_out, float* score_out,
+              uint32_t flags, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace csa2_sparse_attn_decode needs for this shape. */
+size_t csa2_attn_workspace_size(int32_t batch, int32_t k);
+
+/*
+ * csa2_sparse_attn_decode -- a5 gather-dequant + a6 attention (also a4 Reuse: pass the
+ * source layer's index list unchanged; k = 0 gives a window-only layer).
+ *   [V4TO41] CSA2 architecture section (Reuse attends over the earlier layer's selected
+ *   entries without an indexer); section on global KV sharing with per-layer windows;
+ *   [STRUCT] Q&A on the 890-byte count (288-byte main entry = 512 x 4 bit + 32 B scale);
+ *   [DEEP] part-4 entry on FP4 in the KV cache (window stays FP8).
+ *
+ *   q          bf16 [batch][16][512]
+ *   kv_codes   u8   [n_total][256]   E2M1, element 2i in the low nibble
+ *   kv_scale   u8   [n_total][32]    E4M3, scale g covers values 16g..16g+15
+ *   seq_base   i64  [batch]
+ *   idx        i32  [batch][k] or NULL when k == 0; entry seq_base[b] + idx; -1 = skip
+ *   swa        u8   [batch][128][512] E4M3 window rows; rows 0..swa_len[b]-1 are used
+ *   swa_len    i32  [batch]          0..128
+ *   out        f32  [batch][16][512] (out) softmax over (selected entries U window rows),
+ *              z = (q_h . v) * softmax_scale, out_h = sum p v; zero when nothing attends.
+ * Errors: INVALID_ARG (k < 0 or > 16384, null planes), ALIGNMENT, WORKSPACE.
+ */
+int csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                            const int64_t* seq_base, const int32_t* idx, int32_t k,
+                            const uint8_t* swa, const int32_t* swa_len, float softmax_scale,
+                            int32_t batch, float* out, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Bytes of workspace csa2_prefill_chunk needs for this shape. */
+size_t csa2_prefill_workspace_size(int32_t T, int32_t n_entries, int32_t k);
+
+/*
+ * csa2_prefill_chunk -- a7 causal indexer contraction (BF16 MFMA) + a8 per-query top-k
+ * and attention, for T consecutive query positions of one sequence.
+ *   [STRUCT] content summary and Q&A on prefill (prompt tokens run the encoder, whose
+ *   Full layers score and select per token); [V4TO41] encoder section (1:2 token
+ *   compression: one entry per two tokens) and section on the sliding window.
+ *
+ *   q_idx      bf16 [T][128]        indexer queries, query t at position pos0 + t
+ *   q          bf16 [T][16][512]
+ *   idx_codes, idx_scale, kv_codes, kv_scale   entries 0..n_entries-1 of the sequence
+ *   ratio      tokens per entry (>= 1); entry j is visible to position p when
+ *              (j+1)*ratio - 1 <= p, i.e. j < (p+1)/ratio
+ *   pos0       position of query 0 (>= 0)
+ *   k          1..16384 entries per query
+ *   swa        u8 [T+127][512]      E4M3 window rows; row r holds position pos0-127+r.
+ *              Query t attends rows for positions max(0,p-127)..p.  Rows for negative
+ *              positions are never read.
+ *   idx_out    i32 [T][k] (out)     ascending entry ids, -1 padded
+ *   out        f32 [T][16][512] (out)
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE.
+ */
+int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* idx_codes,
+                       const float* idx_scale, const uint8_t* kv_codes,
+                       const uint8_t* kv_scale, int32_t n_entries, int32_t ratio, int64_t pos0,
+                       int32_t T, int32_t k, const uint8_t* swa, float softmax_scale,
+                       int32_t* idx_out, float* out, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H_ */

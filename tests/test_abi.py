@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every symbol include/csa2.h declares, and rejects bad
+arguments on the host before anything is launched (runs without a GPU: no call here
+reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_sparse_kv_csa2_amd as csa2
+from _util import ROOT
+
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(csa2.lib_path):
+        pytest.fail("libcsa2.so is not built; run `python -m compressed_sparse_kv_csa2_amd.build`")
+    return csa2.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"csa2_index_score", "csa2_topk", "csa2_sparse_attn_decode",
+            "csa2_prefill_chunk"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+    # and the binding wraps the four path calls under the same names
+    for n in ("csa2_index_score", "csa2_topk", "csa2_sparse_attn_decode", "csa2_prefill_chunk"):
+        assert callable(getattr(csa2, n))
+
+
+def test_status_strings_and_version(lib):
+    assert lib.csa2_status_string(0) == b"ok"
+    for s in range(-5, 0):
+        assert lib.csa2_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.csa2_status_string(-99) == b"unknown status"
+    assert lib.csa2_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    a = lib.csa2_topk_workspace_size(4, 1 << 20, 16384)
+    b = lib.csa2_topk_workspace_size(4, 1 << 19, 16384)
+    assert a > b > 0
+    assert lib.csa2_topk_workspace_size(0, 10, 1) == 0
+    assert lib.csa2_attn_workspace_size(4, 512) > lib.csa2_attn_workspace_size(4, 0) > 0
+    assert lib.csa2_prefill_workspace_size(4096, 131072, 512) > 0
+    assert lib.csa2_prefill_workspace_size(0, 131072, 512) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
+ODD = ctypes.c_void_p((1 << 20) + 2)   # misaligned
+
+
+def test_index_score_validation(lib):
+    f = lib.csa2_index_score
+    args = [FAKE] * 6 + [4, 1024, FAKE, None, 0, None]
+    bad = list(args); bad[0] = None
+    assert f(*bad) == -1
+    bad = list(args); bad[6] = 0
+    assert f(*bad) == -1
+    bad = list(args); bad[1] = ODD
+    assert f(*bad) == -2
+    bad = list(args); bad[9] = FAKE; bad[10] = 16
+    assert f(*bad) == -3
+
+
+def test_topk_validation(lib):
+    f = lib.csa2_topk
+    base = [FAKE, 4, 1 << 20, FAKE, None, 512, FAKE, None, 0, FAKE, 1 << 40, None]
+    for pos, val, want in [(5, 0, -1), (5, 16385, -1), (0, None, -1), (8, 7, -1), (0, ODD, -2),
+                           (10, 100, -3)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
+    a = list(base); a[9] = None
+    assert f(*a) == -3  # long rows need a workspace
+
+
+def test_attn_validation(lib):
+    f = lib.csa2_sparse_attn_decode
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 512, FAKE, FAKE, 0.04, 4, FAKE, FAKE, 1 << 40, None]
+    for pos, val, want in [(5, -1, -1), (4, None, -1), (9, 0, -1), (0, ODD, -2), (12, 10, -3)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
+
+
+def test_prefill_validation(lib):
+    f = lib.csa2_prefill_chunk
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 131072, 2, 258048, 4096, 512, FAKE, 0.04, FAKE,
+            FAKE, FAKE, 1 << 40, None]
+    for pos, val, want in [(7, 0, -1), (8, -1, -1), (10, 0, -1), (9, 0, -1), (1, ODD, -2),
+                           (16, 10, -3)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
