@@ -1,6 +1,7 @@
-"""Throughput of the CSA2 decode step on one MI355X, with its HBM roofline and the CPU oracle.
+"""Throughput of the CSA2 path on one MI355X, with its roofline and the CPU oracle beside it.
 
-One step is the decoder step at a 2^20-token context for a batch of 4 sequences:
+Default workload (the one the headline line is quoted on), the decoder step at a 2^20-token
+context for a batch of 4 sequences:
   Full scan of 1,048,576 FP4 indexer keys per sequence (csa2_index_score, fused level-1
   radix histogram) -> candidate pool of 16,384 (csa2_topk) -> Reindex re-score of the pool
   with the next layer's indexer query (csa2_index_score over the pool) -> its top-512
@@ -10,21 +11,25 @@ Layer modes and pool: "DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepS
 on the four layer modes; "从V4到V4.1 Flash：架构的激进进化", decoder section (a first full scan
 builds a pool of about 16K positions; later layers pick their top-512 inside it).
 
-Inputs are seeded synthetic N(0,1) values quantised to the entry formats (synth.py), already
-resident in HBM when timing starts.  Several independent input sets are rotated step by
-step so that the caches never hold the bytes a step reads (a set's indexer keys alone are
-285 MB, more than the 256 MiB last-level cache).
+Other workloads (--workload): c2 = 32 sequences x 32,768 entries, Full decode; c3 = the
+20-layer decoder chain (1 Full + 4 Reindex + 15 Reuse) at 131,072 entries x 16 sequences;
+c5 = a 4,096-query prefill chunk against 131,072 entries (causal BF16 MFMA indexer, per-query
+top-512, attention).
 
-Prints ONE JSON line.  `roofline` is for the dominant kernel (the Full scan): algorithmic
-bytes (68 B per scanned entry) per launch divided by its average launch time, measured
-with events on the launch stream inside the timed region.
+Inputs are seeded synthetic N(0,1) values quantised to the entry formats (synth.py), already
+resident in HBM when timing starts.  Independent input sets are rotated step by step so the
+caches never hold the bytes a step reads (a decode set's indexer keys are larger than the
+256 MiB last-level cache, or enough sets are kept to exceed it).
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel: its algorithmic bytes (or
+flops) per launch divided by its average launch time, measured with events on the launch
+stream inside the timed region.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -36,9 +41,10 @@ if ROOT not in sys.path:
 
 METRIC = "CSA2 decode query-tokens/s at 2^20 ctx; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense BF16 MFMA, published
 IDX_ENTRY_BYTES = 68         # 128 x 4 bit + 4-byte scale
 MAIN_ENTRY_BYTES = 288       # 512 x 4 bit + 32 E4M3 scale bytes
-D_KV, HEADS, SWA = 512, 16, 128
+D_KV, HEADS, SWA, D_IDX = 512, 16, 128, 128
 SCAN_SOURCES = ("compressed_sparse_kv_csa2_amd/csrc/index_score.hip",
                 "compressed_sparse_kv_csa2_amd/csrc/csa2_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_c4_long_decode_traffic.md")
@@ -49,15 +55,17 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--sets", type=int, default=4, help="independent input sets rotated per step")
+    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5"])
+    p.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: the "
+                   "workload's default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=2,
-                   help="sequences of the first input set the CPU oracle runs")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="queries of the first input set the CPU oracle runs (0: default)")
     p.add_argument("--no-phases", action="store_true",
                    help="skip the separate, untimed per-phase timing pass")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                   help="instead of the step, run 5 plain device copies of MIB MiB (the known-size "
-                        "reference for scaling the HBM counters) and exit")
+                   help="instead of a workload, run 5 plain device copies of MIB MiB (the "
+                        "known-size reference for scaling the HBM counters) and exit")
     return p.parse_args()
 
 
@@ -98,16 +106,278 @@ def read_traffic():
     return float(m_b.group(1))
 
 
-class Workload:
-    """One input set of the 2^20-context decoder step: B sequences x N decoder entries."""
+def host(t):
+    import numpy as np
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
 
-    def __init__(self, synth, torch, B, N, seed, dev):
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS pool size unknown
+        return 1
+
+
+class _NullEvent:
+    def record(self, stream=None):
+        pass
+
+
+_NULL = _NullEvent()
+
+
+class Marks:
+    """Phase-boundary events of one step; unset slots record nothing."""
+
+    def __init__(self, events):
+        self.events = events
+
+    def __getitem__(self, j):
+        e = self.events[j]
+        return e if e is not None else _NULL
+
+
+# ------------------------------------------------------------------------------------ decode
+class DecodeSet:
+    """One input set: B sequences x N entries, plus per-layer queries and windows."""
+
+    def __init__(self, synth, torch, B, N, seed, dev, layers):
         self.cache = synth.make_entries([N] * B, seed=seed, device=dev)
-        self.q_full = synth.make_index_queries(B, seed, device=dev, sub=20)
-        self.q_re = synth.make_index_queries(B, seed, device=dev, sub=24)
-        self.q = synth.make_queries(B, seed, device=dev, sub=24)
-        self.swa = synth.make_swa(B, SWA, seed, device=dev, sub=24)
+        self.q_idx = {l: synth.make_index_queries(B, seed, device=dev, sub=l) for l in layers}
+        self.q = {l: synth.make_queries(B, seed, device=dev, sub=l) for l in layers}
+        self.swa = {l: synth.make_swa(B, SWA, seed, device=dev, sub=l) for l in layers}
         self.swa_len = torch.full((B,), SWA, dtype=torch.int32, device=dev)
+
+
+class Decode:
+    """Decode workloads: c4 (2^20, pool + one Reindex), c2 (Full, no pool), c3 (decoder chain)."""
+
+    REINDEX = (24, 28, 32, 36)
+
+    def __init__(self, name, args, torch, synth, csa2, dev):
+        self.name, self.torch, self.csa2, self.dev = name, torch, csa2, dev
+        key = {"c4": "c4_long_decode", "c2": "c2_batched_full", "c3": "c3_decoder_chain"}[name]
+        self.cfg = cfg = synth.CONFIGS[key]
+        self.B, self.N = cfg["B"], cfg["ctx"] // cfg["ratio"]
+        self.K, self.POOL = cfg["k"], cfg["pool"]
+        self.layers = {"c3": list(range(20, 40)), "c4": [20, 24], "c2": [2]}[name]
+        n_sets = args.sets or {"c4": 4, "c2": 8, "c3": 2}[name]
+        print(f"generating {n_sets} input sets of {self.B} x {self.N} entries", file=sys.stderr,
+              flush=True)
+        self.sets = [DecodeSet(synth, torch, self.B, self.N, cfg["seed"] + 1000 * s, dev, self.layers)
+                     for s in range(n_sets)]
+        B, N = self.B, self.N
+        self.ws = [csa2.topk_workspace(B, N, self.POOL or self.K, device=dev) for _ in self.sets]
+        self.scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+        if self.POOL:
+            self.pool = torch.empty((B, self.POOL), dtype=torch.int32, device=dev)
+            self.pool_scores = torch.empty((B, self.POOL), dtype=torch.float32, device=dev)
+            self.rescore = torch.empty((B, self.POOL), dtype=torch.float32, device=dev)
+            self.pool_valid = torch.full((B,), self.POOL, dtype=torch.int32, device=dev)
+        self.idx = {l: torch.empty((B, self.K), dtype=torch.int32, device=dev) for l in self.layers}
+        self.out = {l: torch.empty((B, HEADS, D_KV), dtype=torch.float32, device=dev)
+                    for l in self.layers}
+        self.attn_ws = csa2.attn_workspace(B, self.K, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.queries_per_step = B
+        self.n_marks = 4
+        self.phase_names = ["scan_us", "select_us", "attention_us"]
+
+    def step(self, i, marks=None):
+        """One pass of the whole path over input set i % n.  marks[j] (events) are recorded at
+        the phase boundaries: 0 before the scan, 1 after it, 2 before the attentions, 3 at the end."""
+        csa2, s = self.csa2, self.stream
+        w, tw = self.sets[i % len(self.sets)], self.ws[i % len(self.sets)]
+        c = w.cache
+        m = marks if marks is not None else Marks([None] * 4)
+        first = self.layers[0]
+        m[0].record(s)
+        csa2.csa2_index_score(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                              self.scores, topk_ws=tw, stream=s)
+        m[1].record(s)
+        lists = {}
+        if self.name == "c2":
+            csa2.csa2_topk(self.scores, c.n_entries, self.K, self.idx[first], hist_fused=True,
+                           workspace=tw, stream=s)
+            lists[first] = self.idx[first]
+        else:
+            csa2.csa2_topk(self.scores, c.n_entries, self.POOL, self.pool,
+                           score_out=self.pool_scores if self.name == "c3" else None,
+                           hist_fused=True, workspace=tw, stream=s)
+            if self.name == "c3":  # the Full layer's own top-512, inside its pool
+                csa2.csa2_topk(self.pool_scores, self.pool_valid, self.K, self.idx[first],
+                               cand=self.pool, stream=s)
+                lists[first] = self.idx[first]
+            for l in self.layers[1:]:
+                if l in self.REINDEX:
+                    csa2.csa2_index_score(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
+                                          self.pool_valid, self.rescore, cand=self.pool,
+                                          topk_ws=tw, stream=s)
+                    csa2.csa2_topk(self.rescore, self.pool_valid, self.K, self.idx[l], cand=self.pool,
+                                   hist_fused=True, workspace=tw, stream=s)
+                    lists[l] = self.idx[l]
+                else:  # Reuse: the list of the most recent Full/Reindex layer
+                    lists[l] = lists[max(x for x in lists if x <= l)]
+        m[2].record(s)
+        att_layers = self.layers if self.name == "c3" else [self.layers[-1]]
+        for l in att_layers:
+            csa2.csa2_sparse_attn_decode(w.q[l], c.kv_codes, c.kv_scale, c.seq_base, lists[l],
+                                         w.swa[l], w.swa_len, self.out[l], self.attn_ws, stream=s)
+        m[3].record(s)
+        self.last_lists, self.last_out = lists, [self.out[l] for l in att_layers]
+
+    def dominant(self):
+        return {"kernel": "k_index_score (Full scan)", "bound": "hbm", "unit": "GB/s",
+                "peak": HBM_PEAK_GBS, "work": self.B * self.N * IDX_ENTRY_BYTES,
+                "scale": 1e9, "marks": (0, 1)}
+
+    def step_bytes(self):
+        """Algorithmic bytes of one step: every scanned key, the pool ids, every re-scored pool
+        entry with its id, each attention's gathered entries with their ids, window, q, out."""
+        B, N, K = self.B, self.N, self.K
+        n_att = 20 if self.name == "c3" else 1
+        n_re = {"c3": 4, "c4": 1, "c2": 0}[self.name]
+        per_q = N * IDX_ENTRY_BYTES + D_IDX * 2 * (1 + n_re)
+        if self.POOL:
+            per_q += self.POOL * 4 + n_re * self.POOL * (IDX_ENTRY_BYTES + 4)
+        per_q += n_att * (K * (MAIN_ENTRY_BYTES + 4) + SWA * D_KV + HEADS * D_KV * 2 + HEADS * D_KV * 4)
+        return B * per_q
+
+    def valid(self):
+        ok = True
+        for lst in self.last_lists.values():
+            ok &= bool(((lst[:, 1:] > lst[:, :-1]).all() & (lst >= 0).all()).item())
+        for o in self.last_out:
+            ok &= bool(self.torch.isfinite(o).all().item())
+        return ok
+
+    def config(self, n_sets):
+        desc = {"c4": "c4_long_decode: decoder step at 2^20 ctx, batch 4, Full scan of 1,048,576 "
+                      "entries -> pool 16,384 -> Reindex top-512 -> attention 16x512 + SWA 128",
+                "c2": "c2_batched_full: Full decode, batch 32 x 32,768 entries (65,536-token ctx at "
+                      "1:2), top-512, attention 16x512 + SWA 128",
+                "c3": "c3_decoder_chain: 20 decoder layers (1 Full + 4 Reindex + 15 Reuse), batch "
+                      "16 x 131,072 entries, pool 16,384, top-512, 20 attentions 16x512 + SWA 128"}
+        return {"workload": desc[self.name], "batch": self.B, "context_tokens": self.cfg["ctx"],
+                "entries": self.N, "pool": self.POOL, "top_k": self.K, "heads": HEADS,
+                "head_dim": D_KV, "swa": SWA, "input_sets_rotated": n_sets}
+
+    def cpu_baseline(self, rows):
+        """The fp64 oracle on the host: the same step for `rows` sequences of the first set."""
+        import oracle
+        w, B, N = self.sets[0], self.B, self.N
+        rows = max(1, min(rows or {"c4": 2, "c2": 8, "c3": 1}[self.name], B))
+        c = w.cache
+        codes, scale = host(c.idx_codes[: rows * N]), host(c.idx_scale[: rows * N])
+        kvc, kvs = host(c.kv_codes[: rows * N]), host(c.kv_scale[: rows * N])
+        qi = {l: host(v) for l, v in w.q_idx.items()}
+        q = {l: host(v) for l, v in w.q.items()}
+        sw = {l: host(v) for l, v in w.swa.items()}
+        t0 = time.perf_counter()
+        for b in range(rows):
+            base = b * N
+            if self.name == "c4":
+                oracle.decode_step_long(qi[20][b], qi[24][b], q[24][b], codes, scale, kvc, kvs, base,
+                                        N, sw[24][b], SWA, self.POOL, self.K)
+            elif self.name == "c2":
+                _, _, own = oracle.full_layer(qi[2][b], codes[base:base + N], scale[base:base + N],
+                                              N, None, self.K)
+                oracle.decode_attention(q[2][b], kvc, kvs, base, own, sw[2][b], SWA)
+            else:
+                oracle.decoder_chain({l: v[b] for l, v in qi.items()}, {l: v[b] for l, v in q.items()},
+                                     {l: v[b] for l, v in sw.items()}, SWA, codes, scale, kvc, kvs,
+                                     base, N, self.POOL, self.K)
+        dt = time.perf_counter() - t0
+        what = {"c4": "full 1,048,576-entry scan, pool, Reindex, attention each",
+                "c2": "full 32,768-entry scan, top-512, attention each",
+                "c3": "the 20-layer chain over 131,072 entries each"}[self.name]
+        bt = blas_threads()
+        return {"value": round(rows / dt, 4), "unit": "query-tokens/s", "cores": bt,
+                "kind": "oracle",
+                "sample": f"{rows} of the {B} sequences of one step ({what}), fp64 numpy; BLAS calls "
+                          f"on {bt} threads, element-wise decoding on one; {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------------------------ prefill
+class Prefill:
+    """c5: T = 4,096 queries at the tail of a 262,144-token context (131,072 entries at 1:2)."""
+
+    def __init__(self, args, torch, synth, csa2, dev):
+        self.name, self.torch, self.csa2, self.dev = "c5", torch, csa2, dev
+        self.cfg = cfg = synth.CONFIGS["c5_prefill"]
+        self.T, self.ratio, self.K = cfg["T"], cfg["ratio"], cfg["k"]
+        self.N = cfg["ctx"] // self.ratio
+        self.pos0 = cfg["ctx"] - self.T
+        n_sets = args.sets or 2
+        print(f"generating {n_sets} prefill sets ({self.T} queries, {self.N} entries)",
+              file=sys.stderr, flush=True)
+        self.sets = []
+        for s in range(n_sets):
+            seed = cfg["seed"] + 1000 * s
+            self.sets.append((synth.make_entries([self.N], seed=seed, device=dev),
+                              synth.make_index_queries(self.T, seed, device=dev),
+                              synth.make_queries(self.T, seed, device=dev),
+                              synth.make_swa(1, self.T + SWA - 1, seed, device=dev)[0]))
+        self.idx = torch.empty((self.T, self.K), dtype=torch.int32, device=dev)
+        self.out = torch.empty((self.T, HEADS, D_KV), dtype=torch.float32, device=dev)
+        self.ws = csa2.prefill_workspace(self.T, self.N, self.K, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.queries_per_step = self.T
+        self.n_marks = 2
+        self.phase_names = ["chunk_us"]
+        # visible entry-pairs of the causal contraction: query t sees (pos0 + t + 1) // ratio
+        self.pairs = sum(min(self.N, (self.pos0 + t + 1) // self.ratio) for t in range(self.T))
+
+    def step(self, i, marks=None):
+        c, qi, q, sw = self.sets[i % len(self.sets)]
+        s = self.stream
+        m = marks if marks is not None else Marks([None] * 2)
+        m[0].record(s)
+        self.csa2.csa2_prefill_chunk(qi, q, c.idx_codes, c.idx_scale, c.kv_codes, c.kv_scale, self.N,
+                                     self.ratio, self.pos0, self.K, sw, self.idx, self.out, self.ws,
+                                     stream=s)
+        m[1].record(s)
+
+    def dominant(self):
+        # both passes of the causal indexer contraction, 2 flops per multiply-add; timed as the
+        # whole chunk call, so this is a lower bound on the contraction's own rate
+        return {"kernel": "csa2_prefill_chunk (2 causal BF16 MFMA passes; whole call timed)",
+                "bound": "mfma", "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+                "work": 2 * 2 * D_IDX * self.pairs, "scale": 1e12, "marks": (0, 1)}
+
+    def step_bytes(self):
+        return (self.N * IDX_ENTRY_BYTES + self.T * (D_IDX * 2 + HEADS * D_KV * 2 + HEADS * D_KV * 4 +
+                                                     self.K * (MAIN_ENTRY_BYTES + 4) + SWA * D_KV))
+
+    def valid(self):
+        return bool(((self.idx[:, 1:] > self.idx[:, :-1]).all() & (self.idx >= 0).all()).item()) and \
+            bool(self.torch.isfinite(self.out).all().item())
+
+    def config(self, n_sets):
+        return {"workload": "c5_prefill: 4,096 queries at positions 258,048..262,143 of a "
+                            "262,144-token context (131,072 entries at 1:2), causal indexer, "
+                            "top-512 per query, attention 16x512 + causal SWA 128",
+                "queries": self.T, "context_tokens": self.cfg["ctx"], "entries": self.N,
+                "top_k": self.K, "heads": HEADS, "head_dim": D_KV, "swa": SWA,
+                "input_sets_rotated": n_sets}
+
+    def cpu_baseline(self, rows):
+        import oracle
+        c, qi, q, sw = self.sets[0]
+        rows = max(1, rows or 4)
+        sample = [self.T - 1 - r * (self.T // rows) for r in range(rows)]
+        args = (host(qi), host(q), host(c.idx_codes), host(c.idx_scale), host(c.kv_codes),
+                host(c.kv_scale), self.N, self.ratio, self.pos0, self.K, host(sw))
+        t0 = time.perf_counter()
+        oracle.prefill_chunk(*args, rows=sample)
+        dt = time.perf_counter() - t0
+        bt = blas_threads()
+        return {"value": round(rows / dt, 4), "unit": "query-tokens/s", "cores": bt, "kind": "oracle",
+                "sample": f"{rows} of the {self.T} queries (spread over the chunk), fp64 numpy; BLAS "
+                          f"calls on {bt} threads, element-wise decoding on one; {dt:.1f} s"}
 
 
 def main():
@@ -132,108 +402,55 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    cfg = synth.CONFIGS["c4_long_decode"]
-    B, N, POOL, K = cfg["B"], cfg["ctx"] // cfg["ratio"], cfg["pool"], cfg["k"]
-    print(f"generating {args.sets} input sets of {B} x {N} entries", file=sys.stderr, flush=True)
-    sets = [Workload(synth, torch, B, N, cfg["seed"] + 1000 * s, dev) for s in range(args.sets)]
+    wl = Prefill(args, torch, synth, csa2, dev) if args.workload == "c5" else \
+        Decode(args.workload, args, torch, synth, csa2, dev)
     torch.cuda.synchronize()
     print("inputs ready", file=sys.stderr, flush=True)
 
-    # Preallocated outputs and workspaces (the library allocates nothing).
-    ws = [csa2.topk_workspace(B, N, POOL, device=dev) for _ in sets]
-    scores = torch.empty((B, N), dtype=torch.float32, device=dev)
-    pool = torch.empty((B, POOL), dtype=torch.int32, device=dev)
-    rescore = torch.empty((B, POOL), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, K), dtype=torch.int32, device=dev)
-    out = torch.empty((B, HEADS, D_KV), dtype=torch.float32, device=dev)
-    attn_ws = csa2.attn_workspace(B, K, device=dev)
-    pool_valid = torch.full((B,), POOL, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        w, tw = sets[i % len(sets)], ws[i % len(sets)]
-        c = w.cache
-        if ev is not None:
-            ev[0].record(stream)
-        csa2.csa2_index_score(w.q_full, c.idx_codes, c.idx_scale, c.seq_base, c.n_entries, scores,
-                              topk_ws=tw, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        csa2.csa2_topk(scores, c.n_entries, POOL, pool, hist_fused=True, workspace=tw, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        csa2.csa2_index_score(w.q_re, c.idx_codes, c.idx_scale, c.seq_base, pool_valid, rescore,
-                              cand=pool, stream=stream)
-        csa2.csa2_topk(rescore, pool_valid, K, idx, cand=pool, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
-        csa2.csa2_sparse_attn_decode(w.q, c.kv_codes, c.kv_scale, c.seq_base, idx, w.swa, w.swa_len,
-                                     out, attn_ws, stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
-
     for i in range(args.warmup):
-        step(i)
+        wl.step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps; scan launches bracketed by events
-    scan_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+    # ---- timed region: exactly `steps` steps; the dominant launch bracketed by events
+    dom = wl.dominant()
+    a, b = dom["marks"]
+    marks = [Marks([torch.cuda.Event(enable_timing=True) if j in (a, b) else None
+                    for j in range(wl.n_marks)]) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        w, tw = sets[i % len(sets)], ws[i % len(sets)]
-        c = w.cache
-        scan_ev[i][0].record(stream)
-        csa2.csa2_index_score(w.q_full, c.idx_codes, c.idx_scale, c.seq_base, c.n_entries, scores,
-                              topk_ws=tw, stream=stream)
-        scan_ev[i][1].record(stream)
-        csa2.csa2_topk(scores, c.n_entries, POOL, pool, hist_fused=True, workspace=tw, stream=stream)
-        csa2.csa2_index_score(w.q_re, c.idx_codes, c.idx_scale, c.seq_base, pool_valid, rescore,
-                              cand=pool, stream=stream)
-        csa2.csa2_topk(rescore, pool_valid, K, idx, cand=pool, stream=stream)
-        csa2.csa2_sparse_attn_decode(w.q, c.kv_codes, c.kv_scale, c.seq_base, idx, w.swa, w.swa_len,
-                                     out, attn_ws, stream=stream)
+        wl.step(i, marks[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    dom_ms = sum(m[a].elapsed_time(m[b]) for m in marks) / args.steps
+    achieved = dom["work"] / (dom_ms * 1e-3) / dom["scale"]
     ms_per_step = elapsed * 1e3 / args.steps
-    value = B * args.steps / elapsed
-    scan_ms = sum(a.elapsed_time(b) for a, b in scan_ev) / args.steps
-    scan_bytes = B * N * IDX_ENTRY_BYTES
-    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    traffic = read_traffic()
-
-    # Bytes the whole step must move (per query: scan, pool re-score with its index list,
-    # 512 gathered main entries with their index, the window, q and the output).
-    step_bytes = B * (N * IDX_ENTRY_BYTES + POOL * (IDX_ENTRY_BYTES + 4) +
-                      K * (MAIN_ENTRY_BYTES + 4) + SWA * D_KV + HEADS * D_KV * 2 + 256 * 2 +
-                      HEADS * D_KV * 4 + POOL * 4)
+    value = wl.queries_per_step * args.steps / elapsed
+    step_bytes = wl.step_bytes()
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     phases = None
     if not args.no_phases:
         reps = max(20, min(100, args.steps))
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(wl.n_marks)] for _ in range(reps)]
         for i in range(reps):
-            step(i, evs[i])
+            wl.step(i, Marks(evs[i]))
         torch.cuda.synchronize()
-        names = ["scan_us", "pool_topk_us", "reindex_us", "attention_us"]
         phases = {n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3 / reps, 2)
-                  for j, n in enumerate(names)}
+                  for j, n in enumerate(wl.phase_names)}
 
-    # Correctness guard: the last step's selection must be a valid ascending list.
     torch.cuda.synchronize()
-    ok = bool(((idx[:, 1:] > idx[:, :-1]).all() & (idx >= 0).all()).item()) and \
-        bool(torch.isfinite(out).all().item())
-
+    ok = wl.valid()
     print(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(sets[0], B, N, POOL, K, args.cpu_rows)
+    cpu = None if args.no_cpu_baseline else wl.cpu_baseline(args.cpu_rows)
 
+    headline = args.workload == "c4"
     line = {
-        "metric": METRIC,
+        "metric": METRIC if headline else
+        {"c2": "CSA2 batched Full decode query-tokens/s (32 x 32,768 entries)",
+         "c3": "CSA2 decoder-chain query-tokens/s (20 layers, 16 x 131,072 entries)",
+         "c5": "CSA2 prefill query-tokens/s (4,096-query chunk, 131,072 entries)"}[args.workload],
         "value": round(value, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -245,18 +462,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "c4_long_decode: decoder step at 2^20 ctx, batch 4, Full scan of "
-                               "1,048,576 entries -> pool 16,384 -> Reindex top-512 -> "
-                               "attention 16x512 + SWA 128",
-                   "batch": B, "context_tokens": cfg["ctx"], "decoder_entries": N,
-                   "pool": POOL, "top_k": K, "heads": HEADS, "head_dim": D_KV, "swa": SWA,
-                   "input_sets_rotated": args.sets},
-        "roofline": {"kernel": "k_index_score (Full scan)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": scan_bytes,
-                     "avg_launch_us": round(scan_ms * 1e3, 2)},
+        "config": wl.config(len(wl.sets)),
+        "roofline": {"kernel": dom["kernel"], "bound": dom["bound"], "achieved": round(achieved, 1),
+                     "peak": dom["peak"], "unit": dom["unit"],
+                     "frac": round(achieved / dom["peak"], 4),
+                     "traffic": read_traffic() if headline else None,
+                     "algorithmic_per_launch": dom["work"],
+                     "avg_launch_us": round(dom_ms * 1e3, 2)},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_gbs": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "phases_us": phases,
@@ -266,40 +478,6 @@ def main():
     print(json.dumps(line), flush=True)
     if not ok:
         sys.exit(3)
-
-
-def cpu_baseline(w, B, N, POOL, K, rows):
-    """The fp64 oracle on the host: the same decoder step for `rows` sequences of the first
-    input set, timed around the oracle calls only."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS pool size unknown
-        blas_threads = 1
-
-    def h(t):
-        a = t.detach().cpu().numpy()
-        return a.view(np.uint16) if a.dtype == np.int16 else a
-
-    c = w.cache
-    rows = max(1, min(rows, B))
-    data = dict(codes=h(c.idx_codes[: rows * N]), scale=h(c.idx_scale[: rows * N]),
-                kvc=h(c.kv_codes[: rows * N]), kvs=h(c.kv_scale[: rows * N]),
-                qf=h(w.q_full), qr=h(w.q_re), q=h(w.q), swa=h(w.swa))
-    t0 = time.perf_counter()
-    for b in range(rows):
-        oracle.decode_step_long(data["qf"][b], data["qr"][b], data["q"][b], data["codes"],
-                                data["scale"], data["kvc"], data["kvs"], b * N, N, data["swa"][b],
-                                SWA, POOL, K)
-    dt = time.perf_counter() - t0
-    return {"value": round(rows / dt, 4), "unit": "query-tokens/s", "cores": blas_threads,
-            "kind": "oracle",
-            "sample": f"{rows} of the {B} sequences of one step (full 1,048,576-entry scan, pool, "
-                      f"Reindex, attention each), fp64 numpy; BLAS calls on {blas_threads} "
-                      f"threads, element-wise decoding on one; {dt:.1f} s"}
 
 
 if __name__ == "__main__":

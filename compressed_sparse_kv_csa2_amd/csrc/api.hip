@@ -1,6 +1,6 @@
 // C-ABI front end: argument validation on the host, workspace carving, launches.
 // Declarations and their contracts are in include/csa2.h.
-#include "../../include/csa2.h"
+#include "csa2.h"
 #include "csa2_internal.h"
 
 #include <stdint.h>
@@ -43,6 +43,7 @@ int csa2_index_score(const uint16_t* q_idx, const uint8_t* idx_codes, const floa
     return CSA2_ERR_ALIGNMENT;
   uint32_t* hist1 = nullptr;
   if (topk_ws) {
+    if (n_cols > kTopkMaxCols) return CSA2_ERR_UNSUPPORTED;
     if (topk_ws_size < topk_ws_bytes(batch, n_cols)) return CSA2_ERR_WORKSPACE;
     if (!aligned(topk_ws, 256)) return CSA2_ERR_ALIGNMENT;
     hist1 = topk_ws_carve(topk_ws, batch, n_cols).hist1;
@@ -53,7 +54,7 @@ int csa2_index_score(const uint16_t* q_idx, const uint8_t* idx_codes, const floa
 
 size_t csa2_topk_workspace_size(int32_t batch, int32_t n_cols, int32_t k) {
   (void)k;
-  if (batch < 1 || n_cols < 1) return 0;
+  if (batch < 1 || n_cols < 1 || n_cols > kTopkMaxCols) return 0;
   return topk_ws_bytes(batch, n_cols);
 }
 
@@ -63,6 +64,7 @@ int csa2_topk(const float* scores, int32_t batch, int32_t n_cols, const int32_t*
   if (!scores || !n_valid || !idx_out) return CSA2_ERR_INVALID_ARG;
   if (batch < 1 || n_cols < 1 || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_INVALID_ARG;
   if (flags & ~CSA2_TOPK_HIST_FUSED) return CSA2_ERR_INVALID_ARG;
+  if (n_cols > kTopkMaxCols) return CSA2_ERR_UNSUPPORTED;
   if (!aligned(scores, 4) || !aligned(n_valid, 4) || !aligned(idx_out, 4) ||
       (score_out && !aligned(score_out, 4)) || (cand && !aligned(cand, 4)))
     return CSA2_ERR_ALIGNMENT;
@@ -89,8 +91,9 @@ int csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_codes, const ui
                             void* workspace, size_t ws_bytes, void* stream) {
   if (!q || !kv_codes || !kv_scale || !seq_base || !swa || !swa_len || !out) return CSA2_ERR_INVALID_ARG;
   if (batch < 1 || k < 0 || k > CSA2_MAX_K || (k > 0 && !idx)) return CSA2_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(kv_codes, 16) || !aligned(swa, 16) || !aligned(seq_base, 8) ||
-      !aligned(swa_len, 4) || !aligned(out, 16) || (idx && !aligned(idx, 4)))
+  if (!aligned(q, 16) || !aligned(kv_codes, 16) || !aligned(kv_scale, 4) || !aligned(swa, 16) ||
+      !aligned(seq_base, 8) || !aligned(swa_len, 4) || !aligned(out, 16) ||
+      (idx && !aligned(idx, 4)))
     return CSA2_ERR_ALIGNMENT;
   if (!workspace || ws_bytes < attn_ws_bytes(batch, k)) return CSA2_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
@@ -114,7 +117,8 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
     return CSA2_ERR_INVALID_ARG;
   if (!aligned(q_idx, 16) || !aligned(q, 16) || !aligned(swa, 16) || !aligned(idx_out, 4) ||
       !aligned(out, 16) || (idx_codes && !aligned(idx_codes, 16)) ||
-      (idx_scale && !aligned(idx_scale, 4)) || (kv_codes && !aligned(kv_codes, 16)))
+      (idx_scale && !aligned(idx_scale, 4)) || (kv_codes && !aligned(kv_codes, 16)) ||
+      (kv_scale && !aligned(kv_scale, 4)))
     return CSA2_ERR_ALIGNMENT;
   if (!workspace || ws_bytes < prefill_ws_bytes(T, n_entries, k)) return CSA2_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;

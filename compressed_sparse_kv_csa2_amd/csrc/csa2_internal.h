@@ -11,16 +11,26 @@ constexpr int kHist1Bins = 4096;   // level-1 digit: key bits 31..20
 constexpr int kHist2Bins = 2048;   // level-2 digit: key bits 19..9
 constexpr int kTopkSmallMax = 16384;  // rows this long or shorter are selected in LDS
 
+constexpr int kRowInfo = 8;           // per-row counters of the long-row top-k
+constexpr int kInfoCand = 0, kInfoKeff = 1, kInfoTotal = 2, kInfoBin1 = 3, kInfoAbove1 = 4;
+constexpr int kMaxChunks = 8192;      // column chunks per row of the long-row path
+constexpr int kTopkMaxCols = 1 << 26; // longest row csa2_topk accepts
+
 struct TopkWs {
-  uint32_t* hist1;         // [batch][4096]
-  uint32_t* hist2;         // [batch][2048]
-  uint32_t* counters;      // [batch][4]: candidate count, arrivals
-  unsigned long long* bitmap;  // [batch][words]
-  unsigned long long* listA;   // [batch][n_cols]  (key << 32 | column)
-  unsigned long long* listB;   // [batch][n_cols]
-  int64_t words;
+  uint32_t* hist1;               // [batch][4096] level-1 histogram (fused into the scan)
+  uint32_t* counters;            // [batch][kRowInfo], indices kInfo*
+  unsigned long long* thr;       // [batch] k-th composite (key << 32 | ~column)
+  uint32_t* chunk_cnt;           // [batch][n_chunks] columns above the level-1 bin
+  uint32_t* chunk_ccnt;          // [batch][n_chunks] candidates (columns in the bin)
+  uint32_t* chunk_off;           // [batch][n_chunks] output offset of each chunk
+  unsigned long long* list;      // [batch][n_cols] candidates (key << 32 | column), each
+                                 // chunk in its own slots starting at its first column
+  unsigned long long* tied;      // [batch][n_cols] tied candidates when too many for LDS
+  int n_chunks;
 };
 
+int topk_chunk_iters(int n_cols);
+int topk_n_chunks(int n_cols);
 size_t topk_ws_bytes(int batch, int n_cols);
 TopkWs topk_ws_carve(void* base, int batch, int n_cols);
 
@@ -34,8 +44,8 @@ hipError_t launch_topk(const float* scores, int batch, int n_cols, const int32_t
                        bool hist_ready, const TopkWs& ws, hipStream_t stream);
 
 // ---- attention ----
-constexpr int kAttnSplit = 32;  // list positions per wave
-int attn_splits(int k);          // main splits + window splits
+int attn_chunks(int k);          // 32-position chunks of k entries + a full window
+int attn_splits(int k);          // decode splits per row
 size_t attn_ws_bytes(int rows, int k);
 
 // mode 0: decode (row b uses seq_base[b], swa + b*128 rows, swa_len[b])

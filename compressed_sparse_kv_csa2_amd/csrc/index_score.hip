@@ -5,36 +5,33 @@
 // the 890-byte count: 128 x 4 bit + a 4-byte scale; the dot-product score is this
 // library's reading, the pages do not state the indexer's formula).
 //
-// HBM-bound stream: 68 bytes per entry.  Each wave reads 64 consecutive entries as four
-// fully coalesced 1 KiB slabs (lane = 4 * entry + quarter, 16 bytes = 32 codes per lane).
+// HBM-bound stream: 68 bytes per entry.  Each wave reads a group of 64 consecutive
+// entries as four fully coalesced 1 KiB slabs (lane = 4 * entry + quarter, 16 bytes = 32
+// codes per lane) plus the 256 bytes of their scales, all five loads issued together
+// from addresses that are always in bounds (columns past the end are clamped and masked
+// afterwards), and the next group's five loads are in flight while a group is computed.
 // Codes become packed bf16 pairs with one v_cvt_scalef32_pk_bf16_fp4 each and meet the
 // bf16 query in v_dot2_f32_bf16 (exact products, fp32 sums): about one VALU op per value,
 // well under the VALU budget of streaming at full HBM rate.  The four quarter sums are
-// combined with two lane swaps; lanes are then re-assigned so one 256-byte store writes
-// the 64 scores.  Optionally a 4096-bin histogram of the score keys' top 12 bits is
-// accumulated (LDS, then one global add per non-empty bin) for the top-k that follows.
+// combined with two lane swaps; lane (entry, quarter) then owns column 16*quarter + entry.
+// Scores are staged in LDS and written in one coalesced burst per workgroup at the end.
+// Optionally a 4096-bin histogram of the
+// score keys' top 12 bits is accumulated (LDS, then one global add per non-empty bin) for
+// the top-k that follows.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
 namespace csa2 {
 
 constexpr int kScanThreads = 256;
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kScanMaxCols = 4096;  // columns per workgroup at most (scores staged in LDS)
 
-struct ScanSlab {
-  uint4 w[4];  // 16 bytes of codes for each of the four 16-entry sub-slabs
+struct ScanGroup {
+  uint4 w[4];   // 16 code bytes of entry 16*it + ent, it = 0..3
+  float sc;     // scale of the lane's own column 16*quarter + ent
+  int own_ok;   // the own column's candidate id is not a hole (Reindex)
 };
-
-template <bool CAND>
-__device__ __forceinline__ int64_t scan_entry(int col, int nv, const int32_t* __restrict__ cand_row,
-                                              int64_t base, bool& valid) {
-  valid = col < nv;
-  if (CAND) {
-    int cj = valid ? cand_row[col] : -1;
-    valid = valid && cj >= 0;
-    return base + (int64_t)(valid ? cj : 0);
-  }
-  return base + (int64_t)(valid ? col : 0);
-}
 
 __device__ __forceinline__ float dot32(const uint4 w, const bf16x2 (&q)[16]) {
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -57,6 +54,39 @@ __device__ __forceinline__ float dot32(const uint4 w, const bf16x2 (&q)[16]) {
   return (a0 + a1) + (a2 + a3);
 }
 
+// Issues the five loads of the group starting at column g.  Columns are clamped to
+// nv - 1 (>= 0), and a hole in the candidate list reads entry 0 of the sequence, so every
+// address is in bounds; the caller masks those columns.
+template <bool CAND>
+__device__ __forceinline__ ScanGroup load_group(const uint8_t* __restrict__ codes,
+                                                const float* __restrict__ scale,
+                                                const int32_t* __restrict__ cand_row, int64_t base,
+                                                int g, int nv_m1, int ent, int quarter) {
+  ScanGroup s;
+  int64_t e[4];
+  if (CAND) {
+    int cj[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) cj[it] = cand_row[min(g + 16 * it + ent, nv_m1)];
+    int own = cj[0];
+#pragma unroll
+    for (int it = 1; it < 4; ++it) own = quarter == it ? cj[it] : own;
+    s.own_ok = own >= 0;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) e[it] = base + (cj[it] >= 0 ? cj[it] : 0);
+    s.sc = scale[base + (own >= 0 ? own : 0)];
+  } else {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) e[it] = base + min(g + 16 * it + ent, nv_m1);
+    s.own_ok = 1;
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+    s.w[it] = *reinterpret_cast<const uint4*>(codes + e[it] * kIdxCodeBytes + quarter * 16);
+  if (!CAND) s.sc = scale[base + min(g + 16 * quarter + ent, nv_m1)];
+  return s;
+}
+
 template <bool CAND, bool HIST>
 __global__ __launch_bounds__(kScanThreads) void k_index_score(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
@@ -64,15 +94,28 @@ __global__ __launch_bounds__(kScanThreads) void k_index_score(
     const int32_t* __restrict__ n_valid, const int32_t* __restrict__ cand, int n_cols,
     int cols_per_wg, float* __restrict__ scores, uint32_t* __restrict__ hist1) {
   __shared__ uint32_t s_hist[HIST ? kHist1Bins : 1];
+  __shared__ __align__(16) float s_sc[kScanMaxCols];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int quarter = lane & 3;  // which 32 of the 128 values
   const int ent = lane >> 2;     // entry within a 16-entry sub-slab
 
-  if (HIST) {
-    for (int i = threadIdx.x; i < kHist1Bins; i += kScanThreads) s_hist[i] = 0u;
+  const int nv = min(n_valid[b], n_cols);
+  const int64_t base = seq_base[b];
+  const int32_t* cand_row = CAND ? cand + (size_t)b * n_cols : nullptr;
+  float* out_row = scores + (size_t)b * n_cols;
+  const int c0 = blockIdx.x * cols_per_wg;
+  const int c1 = min(c0 + cols_per_wg, n_cols);
+
+  if (nv <= 0) {  // nothing visible: every column of the range is -inf, no histogram
+    for (int c = c0 + threadIdx.x; c < c1; c += kScanThreads) out_row[c] = -__builtin_inff();
+    return;
   }
+  const int nv_m1 = nv - 1;
+
+  // The query goes first: loads complete in order, so waiting for a group never waits
+  // for a load issued after it.
   bf16x2 q[16];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)b * kDIdx) + quarter * 4;
@@ -85,33 +128,24 @@ __global__ __launch_bounds__(kScanThreads) void k_index_score(
       q[4 * i + 3] = __builtin_bit_cast(bf16x2, v.w);
     }
   }
-  const int nv = min(n_valid[b], n_cols);
-  const int64_t base = seq_base[b];
-  const int32_t* cand_row = CAND ? cand + (size_t)b * n_cols : nullptr;
-  float* out_row = scores + (size_t)b * n_cols;
-  const int c0 = blockIdx.x * cols_per_wg;
-  const int c1 = min(c0 + cols_per_wg, n_cols);
+
+  // The wave's groups are g0, g0 + 256, ... < c1.  Two buffers alternate: while one group
+  // is computed the other's loads are in flight.  Prefetches past the wave's last group
+  // re-read the last group (cached), so every iteration issues the same loads.
+  const int g0 = c0 + wave * 64;
+  const int stride = kScanWaves * 64;
+  const int g_last = g0 < c1 ? g0 + (c1 - 1 - g0) / stride * stride : c0;
+  ScanGroup A = load_group<CAND>(codes, scale, cand_row, base, min(g0, g_last), nv_m1, ent, quarter);
+  ScanGroup B = load_group<CAND>(codes, scale, cand_row, base, min(g0 + stride, g_last), nv_m1, ent,
+                                 quarter);
+
+  if (HIST) {
+    for (int i = threadIdx.x; i < kHist1Bins; i += kScanThreads) s_hist[i] = 0u;
+  }
   if (HIST) __syncthreads();
 
-  // Load the 4 sub-slabs of the 64-column group starting at g.
-  auto load_group = [&](int g, ScanSlab& s) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      bool valid;
-      int64_t e = scan_entry<CAND>(g + it * 16 + ent, nv, cand_row, base, valid);
-      s.w[it] = valid ? *reinterpret_cast<const uint4*>(codes + e * kIdxCodeBytes + quarter * 16)
-                      : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-
-  int g = c0 + wave * 64;
-  ScanSlab cur;
-  if (g < c1) load_group(g, cur);
-  for (; g < c1; g += 4 * 64) {
-    ScanSlab nxt;
-    const int gn = g + 4 * 64;
-    if (gn < c1) load_group(gn, nxt);  // keep the next group's loads in flight
-
+  // Scores the group at column g from its loaded bytes.
+  auto process = [&](const ScanGroup& cur, int g) {
     float s[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -121,18 +155,38 @@ __global__ __launch_bounds__(kScanThreads) void k_index_score(
       s[it] = v;
     }
     // lane (4*ent + quarter) now owns column g + 16*quarter + ent
-    float mine = quarter == 0 ? s[0] : quarter == 1 ? s[1] : quarter == 2 ? s[2] : s[3];
+    const float mine = quarter == 0 ? s[0] : quarter == 1 ? s[1] : quarter == 2 ? s[2] : s[3];
     const int col = g + 16 * quarter + ent;
-    bool valid;
-    int64_t e = scan_entry<CAND>(col, nv, cand_row, base, valid);
-    float score = valid ? mine * scale[e] : -__builtin_inff();
-    if (col < c1) out_row[col] = score;
-    if (HIST && valid) atomicAdd(&s_hist[score_key(score) >> 20], 1u);
-    cur = nxt;
+    const bool valid = col < nv && cur.own_ok;
+    const float score = valid ? mine * cur.sc : -__builtin_inff();
+    if (col < c1) s_sc[col - c0] = score;
+    if (HIST && valid) {
+      const uint32_t key = score_key(score);
+      if (key != 0u) atomicAdd(&s_hist[key >> 20], 1u);
+    }
+  };
+
+  for (int g = g0; g < c1; g += 2 * stride) {
+    process(A, g);
+    A = load_group<CAND>(codes, scale, cand_row, base, min(g + 2 * stride, g_last), nv_m1, ent,
+                         quarter);
+    if (g + stride < c1) process(B, g + stride);
+    B = load_group<CAND>(codes, scale, cand_row, base, min(g + 3 * stride, g_last), nv_m1, ent,
+                         quarter);
   }
 
+  // The scores leave in one coalesced burst: stores inside the loop would sit in the same
+  // in-order counter as the prefetched loads and hold them up.
+  __syncthreads();
+  const int n = c1 - c0;
+  for (int i = 4 * threadIdx.x; i < n; i += 4 * kScanThreads) {
+    if (i + 3 < n && (reinterpret_cast<uintptr_t>(&out_row[c0 + i]) & 15) == 0) {
+      *reinterpret_cast<float4*>(&out_row[c0 + i]) = *reinterpret_cast<const float4*>(&s_sc[i]);
+    } else {
+      for (int u = 0; u < 4 && i + u < n; ++u) out_row[c0 + i + u] = s_sc[i + u];
+    }
+  }
   if (HIST) {
-    __syncthreads();
     uint32_t* h = hist1 + (size_t)b * kHist1Bins;
     for (int i = threadIdx.x; i < kHist1Bins; i += kScanThreads) {
       uint32_t v = s_hist[i];
@@ -142,7 +196,7 @@ __global__ __launch_bounds__(kScanThreads) void k_index_score(
 }
 
 static int scan_cols_per_wg(int batch, int n_cols) {
-  // aim for >= ~1024 workgroups on 256 CUs, 256..4096 columns each, a multiple of 256
+  // aim for ~1024 workgroups on 256 CUs, 256..4096 columns each, a multiple of 256
   long long want = ((long long)n_cols * batch + 1023) / 1024;
   int c = (int)((want + 255) / 256 * 256);
   if (c < 256) c = 256;
