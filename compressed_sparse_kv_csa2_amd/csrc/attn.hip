@@ -9,19 +9,24 @@
 // Main entry value e = e2m1(code_e) * e4m3(scale_{e/16}); window rows are raw E4M3
 // ("DeepSeek V4.1 Flash 深度解析", part-4 entry on FP4 in the KV cache).
 //
-// Every dequantised value is exact in bf16 (an E2M1 magnitude has at most 2 significant
-// bits, an E4M3 scale at most 4, so the product has at most 6; window values have 4), so
-// entries are staged in LDS as bf16 without rounding and q . v runs on v_dot2_f32_bf16
-// (exact products, fp32 sums).  p . v accumulates in fp32.
-//
-// One 256-thread workgroup per (row, split).  A split walks its list positions (the k
+// All 16 heads share every entry, so per query the work is a dense [16 x 512] x [512 x n]
+// contraction (about 114 flop per gathered byte) and runs on the matrix cores:
+//   * every dequantised value is exact in bf16 (an E2M1 magnitude has at most 2 significant
+//     bits, an E4M3 scale at most 4, so the product has at most 6; window values have 4),
+//     so q . v on v_mfma_f32_16x16x32_bf16 has exact products and fp32 sums;
+//   * p . v takes p as the sum of two bf16 halves (hi = p truncated, lo = bf16(p - hi)),
+//     two MFMAs, relative error about 2^-16, fp32 sums.
+// One 256-thread workgroup (4 waves) per (row, split) walks its list positions (the k
 // selected entries, then the window rows) in chunks of 32:
-//   gather   thread (entry e, eighth) loads 32 code bytes + 4 scale bytes (or 64 window
-//            bytes), dequantises 64 values and writes them to LDS;
-//   q . v    thread (4 heads, 4 entries, dim slice) accumulates a 4x4 tile over 64 dims,
-//            then the 8 slices are summed with 3 lane swaps;
-//   softmax  16 lanes per head: running max / sum per head, rescale factor;
-//   p . v    thread owns 2 dims of all 16 heads (32 fp32 accumulators).
+//   gather   thread (wave w, lane l) loads dims 8l..8l+7 of positions 8w..8w+7 (4 code bytes
+//            + 1 scale byte, or 8 window bytes each), dequantises them, and writes them to
+//            LDS twice: row-major (position x dims, B operand of q . v) and, after an 8x8
+//            register transpose, dims x positions (B operand of p . v).  Both layouts are
+//            XOR-swizzled so that the 16-byte writes and the operand reads hit distinct banks;
+//   q . v    wave w: entries 16(w&1)..+15 over half of the 512 dims (8 MFMAs); the two
+//            halves are added in the softmax step;
+//   softmax  16 lanes per head: running max and sum, rescale factor, p split into hi/lo;
+//   p . v    wave w: 128 output dims (8 tiles of 16), 2 MFMAs each.
 // Decode uses several splits per row; each leaves (max, sum, acc[16][512]) in the
 // workspace and k_attn_merge combines them by log-sum-exp.  The prefill chunk has many
 // rows and runs one split per row, writing its output directly.  exp2 with log2(e)
@@ -32,10 +37,12 @@
 namespace csa2 {
 
 constexpr int kAttnThreads = 256;
-constexpr int kChunk = 32;                      // list positions per chunk
-constexpr int kRowWords = kDKv / 2 + 4;         // LDS row of 512 bf16 + 16 B pad, in u32
-constexpr int kMaxSplits = 64;                  // splits per decode row
+constexpr int kChunk = 32;                         // list positions per chunk
+constexpr int kMaxSplits = 64;                     // splits per decode row
+constexpr int kIdxWin = 1024;                      // list positions whose ids sit in LDS
 constexpr int kPart = 2 * kHeads + kHeads * kDKv;  // floats per split: m[16], l[16], acc
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 int attn_chunks(int k) { return (k + kSwa + kChunk - 1) / kChunk; }
 int attn_splits(int k) { return min(attn_chunks(k), kMaxSplits); }
@@ -44,99 +51,120 @@ size_t attn_ws_bytes(int rows, int k) {
   return align_up((size_t)rows * attn_splits(k) * kPart * sizeof(float), 256);
 }
 
-// 8 E2M1 codes (one dword) times one scale -> 4 u32 of packed bf16 (exact).
+// ---- LDS layouts (16-byte blocks)
+// V row-major: 32 position rows x 64 blocks (8 dims each); block c of row p at c ^ (p & 15).
+__device__ __forceinline__ int v_blk(int p, int c) { return p * 64 + (c ^ (p & 15)); }
+// V transposed: 512 dim rows x 4 blocks (8 positions each).  Dim d lives in row
+// R = (d & ~15) | ((d + (d >> 4)) & 15), block kb at kb ^ ((R >> 2) & 3).
+__device__ __forceinline__ int vt_blk(int d, int kb) {
+  const int R = (d & ~15) | ((d + (d >> 4)) & 15);
+  return R * 4 + (kb ^ ((R >> 2) & 3));
+}
+// P (either half): 16 head rows x 4 blocks (8 positions each); block kb of head h at
+// kb ^ ((h >> 2) & 3).
+__device__ __forceinline__ int p_blk(int h, int kb) { return h * 4 + (kb ^ ((h >> 2) & 3)); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// 8 E2M1 codes (one dword) times one scale -> 8 bf16 (exact), element i from nibble i.
 __device__ __forceinline__ uint4 fp4x8_scaled_bf16(uint32_t w, float s) {
   const f32x2 a = fp4x2<0>(w), b = fp4x2<1>(w), c = fp4x2<2>(w), d = fp4x2<3>(w);
-  auto pk = [](float lo, float hi) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-  };
-  return make_uint4(pk(a.x * s, a.y * s), pk(b.x * s, b.y * s), pk(c.x * s, c.y * s),
-                    pk(d.x * s, d.y * s));
+  return make_uint4(pack_bf16(a.x * s, a.y * s), pack_bf16(b.x * s, b.y * s),
+                    pack_bf16(c.x * s, c.y * s), pack_bf16(d.x * s, d.y * s));
 }
 
-// 4 E4M3 bytes -> 2 u32 of packed bf16 (exact).
-__device__ __forceinline__ uint2 fp8x4_bf16(uint32_t w) {
-  const f32x2 a = fp8x2<false>(w), b = fp8x2<true>(w);
-  return make_uint2((__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xffff0000u),
-                    (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xffff0000u));
+// 8 E4M3 bytes -> 8 bf16 (exact).
+__device__ __forceinline__ uint4 fp8x8_bf16(uint2 w) {
+  const f32x2 a = fp8x2<false>(w.x), b = fp8x2<true>(w.x);
+  const f32x2 c = fp8x2<false>(w.y), d = fp8x2<true>(w.y);
+  return make_uint4(pack_bf16(a.x, a.y), pack_bf16(b.x, b.y), pack_bf16(c.x, c.y),
+                    pack_bf16(d.x, d.y));
 }
 
-__device__ __forceinline__ float dot8(const uint4 a, const uint4 b, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
-  return acc;
-}
-
-// Raw bytes of one list position for one gather thread: 32 code bytes + 4 scale bytes of a
-// main entry (kind 1) or 64 bytes of a window row (kind 2); kind 0 contributes nothing.
+// Raw bytes of the thread's 8 positions: main bit pp set = main entry (x: 4 code bytes,
+// y: the aligned scale dword holding the lane's scale byte); window bit = window row (x, y:
+// 8 E4M3 bytes); neither = nothing (x, y read from a window row and ignored).
 struct GatherRaw {
-  uint4 w[4];
-  uint32_t sc;
-  int kind;
+  uint2 r[8];
+  uint32_t main_bits, win_bits;
 };
 
-// Issues the loads of position pos for the thread's eighth `part` (no waiting here).
-__device__ __forceinline__ GatherRaw gather_issue(int pos, int part, int k, int n_pos,
-                                                  const int32_t* irow, int64_t base,
+// Issues the loads of positions p0 + 8w .. p0 + 8w + 7, dims 8l .. 8l + 7: exactly two dword
+// loads per position whatever its kind (the source address is selected, not branched on), so
+// the loads of later chunks stay in flight while an earlier chunk is used.  Entry ids come
+// from the LDS window s_idx, which holds list positions idx_base onward.
+__device__ __forceinline__ GatherRaw gather_issue(int p0, int w, int l, int k, int n_pos,
+                                                  const int32_t* s_idx, int idx_base, int64_t base,
                                                   const uint8_t* kv_codes, const uint8_t* kv_scale,
                                                   const uint8_t* rows) {
-  GatherRaw r;
-  r.kind = 0;
-  r.sc = 0u;
+  GatherRaw g;
+  g.main_bits = 0u;
+  g.win_bits = 0u;
+  const uint8_t* pa[8];
+  const uint8_t* pb[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.w[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (pos < n_pos) {
-    if (pos < k) {
-      const int j = irow[pos];
-      if (j >= 0) {
-        const int64_t e = base + j;
-        const uint4* cp = reinterpret_cast<const uint4*>(kv_codes + e * kKvCodeBytes + 32 * part);
-        r.w[0] = cp[0];
-        r.w[1] = cp[1];
-        r.sc = *reinterpret_cast<const uint32_t*>(kv_scale + e * kKvScaleBytes + 4 * part);
-        r.kind = 1;
-      }
-    } else {
-      const uint4* rp = reinterpret_cast<const uint4*>(rows + (size_t)(pos - k) * kDKv + 64 * part);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r.w[i] = rp[i];
-      r.kind = 2;
-    }
+  for (int pp = 0; pp < 8; ++pp) {
+    const int pos = p0 + 8 * w + pp;
+    const int j = pos < k ? s_idx[pos - idx_base] : -1;
+    const bool is_main = pos < k && j >= 0;
+    const bool is_win = pos >= k && pos < n_pos;
+    const int64_t e = base + (j > 0 ? j : 0);
+    const uint8_t* wrow = rows + (size_t)(is_win ? pos - k : 0) * kDKv + 8 * l;
+    pa[pp] = is_main ? kv_codes + e * kKvCodeBytes + 4 * l : wrow;
+    pb[pp] = is_main ? kv_scale + e * kKvScaleBytes + ((l >> 1) & ~3) : wrow + 4;
+    g.main_bits |= is_main ? 1u << pp : 0u;
+    g.win_bits |= is_win ? 1u << pp : 0u;
   }
-  return r;
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    g.r[pp].x = *reinterpret_cast<const uint32_t*>(pa[pp]);
+    g.r[pp].y = *reinterpret_cast<const uint32_t*>(pb[pp]);
+  }
+  return g;
 }
 
-// Dequantises the raw bytes to 64 bf16 values and writes them to the LDS row slice.
-__device__ __forceinline__ void gather_commit(const GatherRaw& r, uint32_t* dst) {
-  uint4 o[8];
-  if (r.kind == 1) {
-    const float s0 = e4m3_to_f32(r.sc & 0xffu), s1 = e4m3_to_f32((r.sc >> 8) & 0xffu);
-    const float s2 = e4m3_to_f32((r.sc >> 16) & 0xffu), s3 = e4m3_to_f32(r.sc >> 24);
-    o[0] = fp4x8_scaled_bf16(r.w[0].x, s0);
-    o[1] = fp4x8_scaled_bf16(r.w[0].y, s0);
-    o[2] = fp4x8_scaled_bf16(r.w[0].z, s1);
-    o[3] = fp4x8_scaled_bf16(r.w[0].w, s1);
-    o[4] = fp4x8_scaled_bf16(r.w[1].x, s2);
-    o[5] = fp4x8_scaled_bf16(r.w[1].y, s2);
-    o[6] = fp4x8_scaled_bf16(r.w[1].z, s3);
-    o[7] = fp4x8_scaled_bf16(r.w[1].w, s3);
-  } else if (r.kind == 2) {
+// Dequantises the thread's 8 x 8 block and writes it to both LDS layouts.
+__device__ __forceinline__ void gather_commit(const GatherRaw& g, int w, int l, uint4* s_v,
+                                              uint4* s_vt) {
+  uint4 v[8];
+  const int sh = 8 * ((l >> 1) & 3);  // the lane's scale byte within its dword
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint2 a = fp8x4_bf16(r.w[i].x), bb = fp8x4_bf16(r.w[i].y);
-      const uint2 cc = fp8x4_bf16(r.w[i].z), d = fp8x4_bf16(r.w[i].w);
-      o[2 * i] = make_uint4(a.x, a.y, bb.x, bb.y);
-      o[2 * i + 1] = make_uint4(cc.x, cc.y, d.x, d.y);
+  for (int pp = 0; pp < 8; ++pp) {
+    if (g.main_bits & (1u << pp)) {
+      v[pp] = fp4x8_scaled_bf16(g.r[pp].x, e4m3_to_f32((g.r[pp].y >> sh) & 0xffu));
+    } else if (g.win_bits & (1u << pp)) {
+      v[pp] = fp8x8_bf16(g.r[pp]);
+    } else {
+      v[pp] = make_uint4(0u, 0u, 0u, 0u);
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = make_uint4(0u, 0u, 0u, 0u);
+    s_v[v_blk(8 * w + pp, l)] = v[pp];
   }
+  // 8x8 transpose of 16-bit elements: dims 8l+2i (low halves) and 8l+2i+1 (high halves),
+  // each as positions 8w..8w+7
+  const uint32_t lo_sel = 0x05040100u, hi_sel = 0x07060302u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 4 * i) = o[i];
+  for (int i = 0; i < 4; ++i) {
+    uint32_t wd[8];
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp)
+      wd[pp] = i == 0 ? v[pp].x : i == 1 ? v[pp].y : i == 2 ? v[pp].z : v[pp].w;
+    uint4 te, to;
+    te.x = __builtin_amdgcn_perm(wd[1], wd[0], lo_sel);
+    te.y = __builtin_amdgcn_perm(wd[3], wd[2], lo_sel);
+    te.z = __builtin_amdgcn_perm(wd[5], wd[4], lo_sel);
+    te.w = __builtin_amdgcn_perm(wd[7], wd[6], lo_sel);
+    to.x = __builtin_amdgcn_perm(wd[1], wd[0], hi_sel);
+    to.y = __builtin_amdgcn_perm(wd[3], wd[2], hi_sel);
+    to.z = __builtin_amdgcn_perm(wd[5], wd[4], hi_sel);
+    to.w = __builtin_amdgcn_perm(wd[7], wd[6], hi_sel);
+    s_vt[vt_blk(8 * l + 2 * i, w)] = te;
+    s_vt[vt_blk(8 * l + 2 * i + 1, w)] = to;
+  }
 }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // MODE 0: decode row b (entries seq_base[b] + idx, window rows swa[b][0..swa_len[b])).
 // MODE 1: prefill row t at position pos0 + t (entries idx from 0, window positions
@@ -148,21 +176,26 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_part(
     const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa,
     const int32_t* __restrict__ swa_len, int64_t pos0, float qscale, float* __restrict__ out,
     float* __restrict__ part, int chunks_per_split, int n_splits) {
-  __shared__ __align__(16) uint32_t s_q[kHeads * kRowWords];
-  __shared__ __align__(16) uint32_t s_v[kChunk * kRowWords];
-  __shared__ float s_z[kHeads][kChunk + 1];
-  __shared__ __align__(16) float s_p[kChunk][kHeads];
+  __shared__ uint4 s_v[kChunk * 64];          // 32 KiB
+  __shared__ uint4 s_vt[kDKv * 4];            // 32 KiB
+  __shared__ uint4 s_p[2][kHeads * 4];        // 2 KiB: p hi, p lo
+  __shared__ float s_s[2][kHeads][kChunk + 1];
   __shared__ float s_m[kHeads], s_l[kHeads], s_alpha[kHeads];
+  __shared__ uint32_t s_valid[4];
+  __shared__ int32_t s_idx[kIdxWin];
 
   const int split = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int n16 = l & 15, g16 = l >> 4;
 
-  // ---- issue the q row (16 x 512 bf16) and the first chunk's loads together
-  uint4 qr[4];
+  // ---- q as A operands: head n16, dims 32*ks + 8*g16 .. +7 for this wave's 8 k-steps
+  const int et = w & 1, kh = w >> 1;
+  bf16x8 qa[8];
   {
-    const uint4* qg = reinterpret_cast<const uint4*>(q + (size_t)b * kHeads * kDKv);
+    const uint16_t* qrow = q + ((size_t)b * kHeads + n16) * kDKv + 8 * g16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qr[i] = qg[tid + i * kAttnThreads];  // 1024 uint4 = 16 rows x 64
+    for (int kk = 0; kk < 8; ++kk)
+      qa[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + (8 * kh + kk) * 32));
   }
   const int64_t base = MODE == 0 ? seq_base[b] : 0;
   const uint8_t* rows;
@@ -179,83 +212,62 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_part(
   const int n_pos = k + nrows;
   const int32_t* irow = k > 0 ? idx + (size_t)b * k : nullptr;
 
-  // thread roles
-  const int g_e = tid >> 3, g_part = tid & 7;                 // gather: entry, eighth
-  const int t_ds = tid & 7, t_jb = (tid >> 3) & 7, t_hb = tid >> 6;  // q . v tile
-  const int s_h = tid >> 4, s_jj = tid & 15;                  // softmax: head, entry pair
-  uint32_t* g_dst = &s_v[g_e * kRowWords + 32 * g_part];
-
   const int c_begin = split * chunks_per_split;
   const int c_end = min(c_begin + chunks_per_split, (n_pos + kChunk - 1) / kChunk);
-  GatherRaw raw = gather_issue(c_begin * kChunk + g_e, g_part, k, n_pos, irow, base, kv_codes,
-                               kv_scale, rows);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = tid + i * kAttnThreads;
-    *reinterpret_cast<uint4*>(&s_q[(v >> 6) * kRowWords + 4 * (v & 63)]) = qr[i];
-  }
+
   if (tid < kHeads) {
     s_m[tid] = -__builtin_inff();
     s_l[tid] = 0.f;
   }
-  float acc[kHeads][2];
+  f32x4v acc[8];
 #pragma unroll
-  for (int h = 0; h < kHeads; ++h) acc[h][0] = acc[h][1] = 0.f;
+  for (int tt = 0; tt < 8; ++tt) acc[tt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  const int s_h = tid >> 4, s_jj = tid & 15;  // softmax roles: head, position pair
 
-  for (int c = c_begin; c < c_end; ++c) {
-    const int p0 = c * kChunk;
-    gather_commit(raw, g_dst);
+  // Outer loop: windows of kIdxWin list positions whose entry ids are staged in LDS.
+  // Inner loop: the window's chunks, each issuing exactly the same loads (the prefetch past
+  // the window's last chunk re-reads that chunk), so the next two chunks stay in flight.
+  for (int wc0 = c_begin; wc0 < c_end; wc0 += kIdxWin / kChunk) {
+    const int wc1 = min(wc0 + kIdxWin / kChunk, c_end);
+    const int idx_base = wc0 * kChunk;
+    __syncthreads();  // the previous window's ids are no longer read
+    for (int i = tid; i < kIdxWin; i += kAttnThreads)
+      s_idx[i] = idx_base + i < k ? irow[idx_base + i] : -1;
     __syncthreads();
-    if (c + 1 < c_end)  // next chunk's loads fly while this one is computed
-      raw = gather_issue(p0 + kChunk + g_e, g_part, k, n_pos, irow, base, kv_codes, kv_scale, rows);
+    GatherRaw raw_a = gather_issue(wc0 * kChunk, w, l, k, n_pos, s_idx, idx_base, base, kv_codes,
+                                   kv_scale, rows);
+    GatherRaw raw_b = gather_issue(min(wc0 + 1, wc1 - 1) * kChunk, w, l, k, n_pos, s_idx, idx_base,
+                                   base, kv_codes, kv_scale, rows);
+  for (int c = wc0; c < wc1; ++c) {
+    gather_commit(raw_a, w, l, s_v, s_vt);
+    if (l == 0) s_valid[w] = raw_a.main_bits | raw_a.win_bits;
+    raw_a = raw_b;
+    __syncthreads();
+    raw_b = gather_issue(min(c + 2, wc1 - 1) * kChunk, w, l, k, n_pos, s_idx, idx_base, base,
+                         kv_codes, kv_scale, rows);
 
-    // ---- z = q . v for 16 heads x 32 entries
+    // ---- z partials: entries 16*et + n16, dims of k-steps 8*kh .. 8*kh + 7
     {
-      float t[4][4];
+      f32x4v sacc = {0.f, 0.f, 0.f, 0.f};
+      const int e = 16 * et + n16;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[a][e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int w0 = 4 * t_ds + 32 * i;  // u32 offset of dims 8*t_ds + 64*i
-        uint4 qv[4], vv[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) qv[a] = *reinterpret_cast<const uint4*>(&s_q[(4 * t_hb + a) * kRowWords + w0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = *reinterpret_cast<const uint4*>(&s_v[(4 * t_jb + e) * kRowWords + w0]);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) t[a][e] = dot8(qv[a], vv[e], t[a][e]);
+      for (int kk = 0; kk < 8; ++kk) {
+        const int ks = 8 * kh + kk;
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(s_v[v_blk(e, 4 * ks + g16)]),
+                                                        sacc, 0, 0, 0);
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = t[a][e];
-          v += __shfl_xor(v, 1);
-          v += __shfl_xor(v, 2);
-          v += __shfl_xor(v, 4);
-          t[a][e] = v;
-        }
-      if (t_ds == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * t_jb + e;
-          const int pos = p0 + j;
-          bool valid = pos < n_pos;
-          if (valid && pos < k) valid = irow[pos] >= 0;
-#pragma unroll
-          for (int a = 0; a < 4; ++a) s_z[4 * t_hb + a][j] = valid ? t[a][e] * qscale : -__builtin_inff();
-        }
-      }
+      for (int j = 0; j < 4; ++j) s_s[kh][4 * g16 + j][e] = sacc[j];
     }
     __syncthreads();
 
-    // ---- online softmax update, 16 lanes per head
+    // ---- online softmax update, 16 lanes per head, 2 positions per lane
     {
-      const float z0 = s_z[s_h][2 * s_jj], z1 = s_z[s_h][2 * s_jj + 1];
+      const int pa = 2 * s_jj, pb = pa + 1;
+      const uint32_t vm = s_valid[pa >> 3];
+      const bool va = (vm >> (pa & 7)) & 1u, vb = (vm >> (pb & 7)) & 1u;
+      const float z0 = va ? (s_s[0][s_h][pa] + s_s[1][s_h][pa]) * qscale : -__builtin_inff();
+      const float z1 = vb ? (s_s[0][s_h][pb] + s_s[1][s_h][pb]) * qscale : -__builtin_inff();
       float cm = fmaxf(z0, z1);
       cm = fmaxf(cm, __shfl_xor(cm, 1));
       cm = fmaxf(cm, __shfl_xor(cm, 2));
@@ -273,8 +285,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_part(
       ps += __shfl_xor(ps, 2);
       ps += __shfl_xor(ps, 4);
       ps += __shfl_xor(ps, 8);
-      s_p[2 * s_jj][s_h] = p0v;
-      s_p[2 * s_jj + 1][s_h] = p1v;
+      // p = hi + lo: hi = p truncated to bf16, lo = bf16(p - hi)
+      const uint32_t h0 = __float_as_uint(p0v) & 0xffff0000u, h1 = __float_as_uint(p1v) & 0xffff0000u;
+      const float r0 = p0v - __uint_as_float(h0), r1 = p1v - __uint_as_float(h1);
+      const uint32_t l0 = __builtin_bit_cast(uint16_t, (__bf16)r0);
+      const uint32_t l1 = __builtin_bit_cast(uint16_t, (__bf16)r1);
+      uint32_t* ph = reinterpret_cast<uint32_t*>(&s_p[0][p_blk(s_h, pa >> 3)]);
+      uint32_t* pl = reinterpret_cast<uint32_t*>(&s_p[1][p_blk(s_h, pa >> 3)]);
+      ph[(pa & 7) >> 1] = (h0 >> 16) | h1;
+      pl[(pa & 7) >> 1] = l0 | (l1 << 16);
       __syncthreads();  // every lane has read s_m before it changes
       if (s_jj == 0) {
         const float alpha = m_old == -__builtin_inff() ? 0.f : exp2f(m_old - m_new);
@@ -285,42 +304,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_part(
     }
     __syncthreads();
 
-    // ---- acc = acc * alpha + p . v, thread owns dims 2*tid, 2*tid + 1
+    // ---- acc = acc * alpha + p . v for output dims (8w + tt)*16 + n16, heads 4*g16 + j
     {
+      float al[4];
 #pragma unroll
-      for (int h = 0; h < kHeads; ++h) {
-        const float al = s_alpha[h];
-        acc[h][0] *= al;
-        acc[h][1] *= al;
-      }
-#pragma unroll 4
-      for (int j = 0; j < kChunk; ++j) {
-        const uint32_t w = s_v[j * kRowWords + tid];
-        const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xffff0000u);
-        const float4* pp = reinterpret_cast<const float4*>(&s_p[j][0]);
+      for (int j = 0; j < 4; ++j) al[j] = s_alpha[4 * g16 + j];
+      const bf16x8 a_hi = as_bf16x8(s_p[0][p_blk(n16, g16)]);
+      const bf16x8 a_lo = as_bf16x8(s_p[1][p_blk(n16, g16)]);
 #pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) {
-          const float4 p4 = pp[h4];
-          const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+      for (int tt = 0; tt < 8; ++tt) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            acc[4 * h4 + u][0] = fmaf(pv[u], v0, acc[4 * h4 + u][0]);
-            acc[4 * h4 + u][1] = fmaf(pv[u], v1, acc[4 * h4 + u][1]);
-          }
-        }
+        for (int j = 0; j < 4; ++j) acc[tt][j] *= al[j];
+        const bf16x8 bv = as_bf16x8(s_vt[vt_blk((8 * w + tt) * 16 + n16, g16)]);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bv, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bv, acc[tt], 0, 0, 0);
       }
     }
-    __syncthreads();  // s_v / s_p are rewritten by the next chunk
+    __syncthreads();  // LDS is rewritten by the next chunk
   }
-
+  }
   __syncthreads();  // s_m / s_l final (also when this split had no positions)
+
   if (MODE == 1 || n_splits == 1) {
     float* O = out + (size_t)b * kHeads * kDKv;
 #pragma unroll
-    for (int h = 0; h < kHeads; ++h) {
-      const float l = s_l[h];
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      *reinterpret_cast<float2*>(&O[h * kDKv + 2 * tid]) = make_float2(acc[h][0] * inv, acc[h][1] * inv);
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * g16 + j;
+      const float lsum = s_l[h];
+      const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) O[h * kDKv + (8 * w + tt) * 16 + n16] = acc[tt][j] * inv;
     }
     return;
   }
@@ -330,12 +343,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_part(
     P[kHeads + tid] = s_l[tid];
   }
 #pragma unroll
-  for (int h = 0; h < kHeads; ++h)
-    *reinterpret_cast<float2*>(&P[2 * kHeads + h * kDKv + 2 * tid]) = make_float2(acc[h][0], acc[h][1]);
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+      P[2 * kHeads + (4 * g16 + j) * kDKv + (8 * w + tt) * 16 + n16] = acc[tt][j];
 }
 
 // Log-sum-exp merge of a decode row's splits for one head: 128 threads x 4 dims.  Each
-// lane of every wave first takes one split's (max, sum), so the weights come from two wave
+// lane of the first wave takes one split's (max, sum), so the weights come from two wave
 // reductions, then all splits' accumulators are read with independent loads.
 __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, int n_splits,
                                                     float* __restrict__ out) {
@@ -349,11 +364,11 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
     float M = ms;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float w = (ms == -__builtin_inff()) ? 0.f : exp2f(ms - M);
-    float L = w * ls;
+    const float wgt = (ms == -__builtin_inff()) ? 0.f : exp2f(ms - M);
+    float L = wgt * ls;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-    if (lane < n_splits) s_w[lane] = w;
+    if (lane < n_splits) s_w[lane] = wgt;
     if (lane == 0) s_L = L;
   }
   __syncthreads();
@@ -361,12 +376,12 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
   const float* A = P0 + 2 * kHeads + h * kDKv + 4 * tid;
 #pragma unroll 8
   for (int s = 0; s < n_splits; ++s) {
-    const float w = s_w[s];
+    const float wgt = s_w[s];
     const float4 a = *reinterpret_cast<const float4*>(A + (size_t)s * kPart);
-    o.x = fmaf(a.x, w, o.x);
-    o.y = fmaf(a.y, w, o.y);
-    o.z = fmaf(a.z, w, o.z);
-    o.w = fmaf(a.w, w, o.w);
+    o.x = fmaf(a.x, wgt, o.x);
+    o.y = fmaf(a.y, wgt, o.y);
+    o.z = fmaf(a.z, wgt, o.z);
+    o.w = fmaf(a.w, wgt, o.w);
   }
   const float L = s_L;
   const float inv = L > 0.f ? 1.0f / L : 0.f;

@@ -7,22 +7,28 @@
 // tokens).  Visibility is this library's reading: entry j is visible to position p once
 // its last token (j+1)*ratio - 1 is at or before p.
 //
-// S[t][j] = scale_j * (q_t . e2m1(K_j)) is a dense T x N x 128 contraction.  The codes are
-// expanded to bf16 exactly (v_cvt_scalef32_pk_bf16_fp4) straight into the B operand of
-// v_mfma_f32_32x32x16_bf16; the 128 dims are permuted identically on both sides so each
-// lane reads 32 contiguous code bytes.  The fp32 entry scale is applied to the fp32
-// accumulators.  The T x N score matrix is never stored.  Instead:
-//   pass 1 keeps, per row, the maximum over small groups of entries (a lane's column in
-//          8 consecutive 32-entry tiles) and stores it as a 16-bit key prefix (rounded
-//          down).  At least k groups have maxima >= the k-th largest of those maxima, so
-//          that value, theta_t, is a rigorous lower bound on the row's k-th score;
-//   pass 2 recomputes the contraction and appends only scores >= theta_t (typically a
-//          few hundred per row) to a per-row candidate list;
-//   select  resolves each row exactly in LDS (largest scores, ties to the lower entry),
-//          sorts the chosen entries ascending.  A row whose candidates overflow the list
-//          (only possible with massive score ties) is resolved by recomputing its scores
-//          in a streaming radix select.
-// Tiles past the causal frontier of a wave's rows are skipped.
+// S[t][j] = scale_j * (q_t . e2m1(K_j)) is a dense T x N x 128 contraction on
+// v_mfma_f32_32x32x16_bf16.  A workgroup owns 128 query rows (32 per wave, held as A
+// operands) and one split of 4,096 entries, which it streams through LDS in stages of 256
+// entries (raw 64 code bytes + fp32 scale each, double buffered, the next stage's loads in
+// flight during the current stage's MFMAs, shared by the four waves).  Each wave expands
+// its B operands from LDS to bf16 exactly (v_cvt_scalef32_pk_bf16_fp4); the 128 dims are
+// permuted identically on both sides so each lane reads 32 contiguous code bytes.  The
+// fp32 entry scale is applied to the fp32 accumulators.  The T x N score matrix is never
+// stored:
+//   pass 1 keeps, per row, the maximum of each group of 32 entries (a lane's column over
+//          32 consecutive 32-entry tiles) as a 16-bit key prefix rounded down.  At least k
+//          groups have maxima >= the k-th largest group maximum, so that value, theta_t,
+//          is a rigorous lower bound on the row's k-th score;
+//   pass 2 recomputes the contraction and writes the scores >= theta_t (typically a few
+//          hundred per row) into the row's slots for this split (LDS counters, no global
+//          atomics);
+//   select resolves each row exactly in LDS (largest scores, ties to the lower entry) and
+//          sorts the chosen entries ascending.  A row whose candidates overflow a split's
+//          slots (only possible with massive score ties) is resolved by recomputing its
+//          scores in a streaming radix select; a row that sees at most k entries takes them
+//          all.
+// Stages past the causal frontier of a workgroup's rows are skipped.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -30,47 +36,56 @@ namespace csa2 {
 
 constexpr int kGemmThreads = 256;           // 4 waves x 32 query rows
 constexpr int kGemmRows = 128;
-constexpr int kSplitEntries = 4096;         // entries per workgroup (128 tiles of 32)
-constexpr int kRunTiles = 8;                // group = one lane column over 8 tiles
-constexpr int kGroupsPerSplit = kSplitEntries / (32 * kRunTiles) * 32;  // 512
-constexpr int kCandCap = 8192;              // candidates kept per row
+constexpr int kSplitEntries = 4096;         // entries per workgroup
+constexpr int kStage = 256;                 // entries per LDS stage (8 tiles of 32)
+constexpr int kStages = kSplitEntries / kStage;
+constexpr int kRunStages = 4;               // group = one lane column over 32 tiles
+constexpr int kGroupsPerSplit = kStages / kRunStages * 32;  // 128
+constexpr int kSlots = 64;                  // candidate slots per (row, split): one per lane
+static_assert(kSlots == 64, "select copies one split per wave, one slot per lane");
+constexpr int kCandLds = 8192;              // candidates a row may gather into LDS
 constexpr int kSelThreads = 256;
-constexpr int kMaxKPow2 = 16384;           // largest k (power of two) the select kernel sorts
+constexpr int kSelMaxSplits = 1024;         // splits a row's fast path can gather (N <= 4M)
+constexpr int kMaxKPow2 = 16384;            // largest k (power of two) the select kernel sorts
 
 struct PrefillWs {
   uint16_t* gmax;               // [T][G] group maxima as key >> 16 (0 = empty group)
   float* theta;                 // [T]
-  uint32_t* cnt;                // [T] candidate counts
-  unsigned long long* cand;     // [T][kCandCap] (key << 32 | entry)
+  uint32_t* ccount;             // [T][n_splits] candidates found per split
+  unsigned long long* cand;     // [T][n_splits][kSlots] (key << 32 | entry)
   void* attn;                   // attention workspace (unused by the prefill attention)
-  int G;
+  int G, n_splits;
 };
 
-static int prefill_splits(int n_entries) { return n_entries > 0 ? (n_entries + kSplitEntries - 1) / kSplitEntries : 1; }
+static int prefill_splits(int n_entries) {
+  return n_entries > 0 ? (n_entries + kSplitEntries - 1) / kSplitEntries : 1;
+}
 
 size_t prefill_ws_bytes(int T, int n_entries, int k) {
   (void)k;
-  const size_t G = (size_t)prefill_splits(n_entries) * kGroupsPerSplit;
+  const size_t S = (size_t)prefill_splits(n_entries);
+  const size_t G = S * kGroupsPerSplit;
   size_t s = 0;
   s += align_up((size_t)T * G * 2, 256);
   s += align_up((size_t)T * 4, 256);
-  s += align_up((size_t)T * 4, 256);
-  s += align_up((size_t)T * kCandCap * 8, 256);
+  s += align_up((size_t)T * S * 4, 256);
+  s += align_up((size_t)T * S * kSlots * 8, 256);
   return s;
 }
 
 static PrefillWs prefill_ws_carve(void* base, int T, int n_entries) {
   PrefillWs w;
-  w.G = prefill_splits(n_entries) * kGroupsPerSplit;
+  w.n_splits = prefill_splits(n_entries);
+  w.G = w.n_splits * kGroupsPerSplit;
   char* p = static_cast<char*>(base);
   w.gmax = reinterpret_cast<uint16_t*>(p);
   p += align_up((size_t)T * w.G * 2, 256);
   w.theta = reinterpret_cast<float*>(p);
   p += align_up((size_t)T * 4, 256);
-  w.cnt = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)T * 4, 256);
+  w.ccount = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)T * w.n_splits * 4, 256);
   w.cand = reinterpret_cast<unsigned long long*>(p);
-  p += align_up((size_t)T * kCandCap * 8, 256);
+  p += align_up((size_t)T * w.n_splits * kSlots * 8, 256);
   w.attn = p;
   return w;
 }
@@ -80,7 +95,7 @@ __device__ __forceinline__ int visible(int64_t pos, int ratio, int n_entries) {
   return (int)(v < n_entries ? v : n_entries);
 }
 
-// Eight E2M1 codes (one dword) -> bf16x8 B/A operand slice.
+// Eight E2M1 codes (one dword) -> bf16x8 operand slice (exact).
 __device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w) {
   const bf16x2 a = fp4x2_bf16<0>(w), b = fp4x2_bf16<1>(w), c = fp4x2_bf16<2>(w),
                d = fp4x2_bf16<3>(w);
@@ -90,7 +105,11 @@ __device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w) {
   return r;
 }
 
-// PASS 1: group maxima.  PASS 2: candidate emission.
+// LDS stage: entry i's 64 code bytes as 4 blocks of 16 bytes, block b at b ^ ((i >> 2) & 3)
+// so that 16 consecutive entries' reads of one block land in 16 distinct bank groups.
+__device__ __forceinline__ int stage_blk(int i, int b) { return i * 4 + (b ^ ((i >> 2) & 3)); }
+
+// PASS 1: group maxima.  PASS 2: candidate slots.
 // Accumulator layout of v_mfma_f32_32x32x16_bf16: lane l holds column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  Operands: lane l holds row/column l % 32 and
 // k-slice 8*(l/32)..+7; the dims behind k-step kk for half h are 64h + 8kk .. +7.
@@ -98,13 +117,22 @@ template <int PASS>
 __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row0 = blockIdx.x * kGemmRows + wave * 32;
-  if (row0 >= T) return;  // no LDS / barriers in this kernel
+  __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
+  __shared__ float s_sc[2][kStage];
+  __shared__ uint32_t s_ccnt[kGemmRows];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wg_row0 = blockIdx.x * kGemmRows;
+  const int row0 = wg_row0 + wave * 32;
   const int split = blockIdx.y;
   const int e_begin = split * kSplitEntries;
   const int e_end = min(e_begin + kSplitEntries, n_entries);
   const int rl = lane & 31, half = lane >> 5;
+
+  // entries any row of the workgroup can see, and of this wave's rows
+  const int wg_nmax = visible(pos0 + min(wg_row0 + kGemmRows - 1, T - 1), ratio, n_entries);
+  const int wave_nmax = row0 < T ? visible(pos0 + min(row0 + 31, T - 1), ratio, n_entries) : 0;
+  const int e_stop = min(e_end, wg_nmax);
+  const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
 
   // A operand: query row row0 + rl, dims 64*half .. +63
   bf16x8 a[8];
@@ -115,39 +143,59 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
     for (int kk = 0; kk < 8; ++kk) a[kk] = __builtin_bit_cast(bf16x8, qp[kk]);
   }
   int nvis[16];
-  int rowid[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    rowid[r] = t;
     nvis[r] = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
   }
-  const int wave_nmax = visible(pos0 + min(row0 + 31, T - 1), ratio, n_entries);
   float th[16];
   if (PASS == 2) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) th[r] = rowid[r] < T ? ws.theta[rowid[r]] : __builtin_inff();
+    for (int r = 0; r < 16; ++r) {
+      const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      th[r] = t < T ? ws.theta[t] : __builtin_inff();
+    }
+    if (tid < kGemmRows) s_ccnt[tid] = 0u;
   }
 
-  const int n_runs = kSplitEntries / (32 * kRunTiles);
-  for (int run = 0; run < n_runs; ++run) {
-    const int run_e0 = e_begin + run * 32 * kRunTiles;
-    float rm[16];
+  // one entry per thread per stage: 4 x 16 code bytes + scale, clamped to a real entry
+  uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
+  float psc = 0.f;
+#define CSA2_LOAD_STAGE(st)                                                                   \
+  do {                                                                                        \
+    const int e_ = min(e_begin + (st) * kStage + tid, n_entries - 1);                         \
+    const uint4* cp_ = reinterpret_cast<const uint4*>(codes + (size_t)e_ * kIdxCodeBytes);    \
+    pc0 = cp_[0];                                                                             \
+    pc1 = cp_[1];                                                                             \
+    pc2 = cp_[2];                                                                             \
+    pc3 = cp_[3];                                                                             \
+    psc = scale[e_];                                                                          \
+  } while (0)
+  if (n_active > 0) CSA2_LOAD_STAGE(0);
+
+  float rm[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rm[r] = -__builtin_inff();
-    if (run_e0 < e_end && run_e0 < wave_nmax) {
-      for (int tt = 0; tt < kRunTiles; ++tt) {
-        const int e0 = run_e0 + tt * 32;
-        if (e0 >= e_end || e0 >= wave_nmax) break;
-        const int col = e0 + rl;
-        uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0;
-        float sc = 0.f;
-        if (col < n_entries) {
-          const uint4* cp = reinterpret_cast<const uint4*>(codes + (size_t)col * kIdxCodeBytes + 32 * half);
-          c0 = cp[0];
-          c1 = cp[1];
-          sc = scale[col];
-        }
+  for (int r = 0; r < 16; ++r) rm[r] = -__builtin_inff();
+
+  for (int st = 0; st < kStages; ++st) {
+    if (st < n_active) {
+      const int buf = st & 1;
+      s_code[buf][stage_blk(tid, 0)] = pc0;
+      s_code[buf][stage_blk(tid, 1)] = pc1;
+      s_code[buf][stage_blk(tid, 2)] = pc2;
+      s_code[buf][stage_blk(tid, 3)] = pc3;
+      s_sc[buf][tid] = psc;
+      __syncthreads();
+      if (st + 1 < n_active) CSA2_LOAD_STAGE(st + 1);  // in flight during the MFMAs
+
+      const int st_e0 = e_begin + st * kStage;
+      for (int tt = 0; tt < kStage / 32; ++tt) {
+        const int e0 = st_e0 + tt * 32;
+        if (e0 >= wave_nmax) break;  // wave-uniform: the rest of the stage is beyond every row
+        const int i = tt * 32 + rl;  // entry within the stage
+        const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
+        const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
+        const float sc = s_sc[buf][i];
         f32x16 acc = {};
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp4x8_bf16(c0.x), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp4x8_bf16(c0.y), acc, 0, 0, 0);
@@ -157,6 +205,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[5], fp4x8_bf16(c1.y), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp4x8_bf16(c1.z), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp4x8_bf16(c1.w), acc, 0, 0, 0);
+        const int col = e0 + rl;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float s = acc[r] * sc;
@@ -164,25 +213,34 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
           if (PASS == 1) {
             rm[r] = vis ? fmaxf(rm[r], s) : rm[r];
           } else if (vis && s >= th[r]) {
-            const uint32_t slot = atomic_add_agent(&ws.cnt[rowid[r]], 1u);
-            if (slot < (uint32_t)kCandCap)
-              ws.cand[(size_t)rowid[r] * kCandCap + slot] =
+            const int lr = wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const uint32_t slot = atomicAdd(&s_ccnt[lr], 1u);
+            if (slot < (uint32_t)kSlots)
+              ws.cand[(((size_t)(wg_row0 + lr)) * ws.n_splits + split) * kSlots + slot] =
                   ((unsigned long long)score_key(s) << 32) | (uint32_t)col;
           }
         }
       }
     }
-    if (PASS == 1) {
-      const int g = split * kGroupsPerSplit + run * 32 + rl;
+    if (PASS == 1 && (st + 1) % kRunStages == 0) {  // end of a run: publish the group maxima
+      const int g = split * kGroupsPerSplit + (st / kRunStages) * 32 + rl;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (rowid[r] < T) {
+        const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (t < T) {
           const uint16_t key16 =
               rm[r] == -__builtin_inff() ? (uint16_t)0 : (uint16_t)(score_key(rm[r]) >> 16);
-          ws.gmax[(size_t)rowid[r] * ws.G + g] = key16;
+          ws.gmax[(size_t)t * ws.G + g] = key16;
         }
+        rm[r] = -__builtin_inff();
       }
     }
+  }
+#undef CSA2_LOAD_STAGE
+  if (PASS == 2) {
+    __syncthreads();
+    if (tid < kGemmRows && wg_row0 + tid < T)
+      ws.ccount[(size_t)(wg_row0 + tid) * ws.n_splits + split] = s_ccnt[tid];
   }
 }
 
@@ -256,7 +314,6 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, in
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_t = visible(pos0 + t, ratio, n_entries);
-  if (tid == 0) ws.cnt[t] = 0u;  // fresh candidate count for pass 2
   if (n_t <= k) {
     if (tid == 0) ws.theta[t] = -__builtin_inff();
     return;
@@ -311,30 +368,72 @@ __device__ __forceinline__ float score_row(const bf16x2 (&qq)[64], const uint8_t
   return (a0 + a1) * scale[j];
 }
 
-// Exact per-row top-k from the candidate list (or, on overflow, from recomputed scores),
+// Exact per-row top-k from the candidate slots (or, on overflow, from recomputed scores),
 // ascending entry ids, -1 padded.
 __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, int k,
     int k_pow2, int32_t* __restrict__ idx_out, PrefillWs ws) {
   extern __shared__ unsigned long long s_dyn[];
-  unsigned long long* s_cand = s_dyn;                                         // [kCandCap]
-  uint32_t* s_sel = reinterpret_cast<uint32_t*>(s_dyn + kCandCap);             // [k_pow2]
+  unsigned long long* s_cand = s_dyn;                                         // [kCandLds]
+  uint32_t* s_sel = reinterpret_cast<uint32_t*>(s_dyn + kCandLds);             // [k_pow2]
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_res[4];
   __shared__ uint32_t s_scan[32];
-  __shared__ uint32_t s_nsel;
+  __shared__ uint32_t s_nsel, s_total, s_over;
+  __shared__ uint32_t s_cnt[kSelMaxSplits], s_off[kSelMaxSplits];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_t = visible(pos0 + t, ratio, n_entries);
-  const uint32_t C = ws.cnt[t];
   int32_t* orow = idx_out + (size_t)t * k;
   const uint32_t k_eff = (uint32_t)min(k, n_t);
 
-  if (C <= (uint32_t)kCandCap) {
+  if (n_t <= k) {  // every visible entry is selected
+    for (int i = tid; i < k; i += kSelThreads) orow[i] = i < n_t ? i : -1;
+    return;
+  }
+
+  // ---- gather the row's candidates from its split slots (wave 0 counts and offsets them,
+  // then each wave copies whole splits, one slot per lane)
+  const int S = ws.n_splits;
+  const uint32_t* cc = ws.ccount + (size_t)t * S;
+  if (tid < 64) {
+    const int lane = tid;
+    uint32_t carry = 0, over = S > kSelMaxSplits ? 1u : 0u;
+    for (int s0 = 0; s0 < S && !over; s0 += 64) {
+      const int s = s0 + lane;
+      const uint32_t c = s < S ? cc[s] : 0u;
+      over |= __ballot(c > (uint32_t)kSlots) != 0ull ? 1u : 0u;
+      const uint32_t n = min(c, (uint32_t)kSlots);
+      uint32_t incl = n;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      if (s < S) {
+        s_cnt[s] = n;
+        s_off[s] = carry + incl - n;
+      }
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      s_total = carry;
+      s_over = over | (carry > (uint32_t)kCandLds ? 1u : 0u);
+      s_nsel = 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t C = s_total;
+  if (!s_over) {
     // ---- fast path: exact selection among the candidates
-    for (uint32_t i = tid; i < C; i += kSelThreads) s_cand[i] = ws.cand[(size_t)t * kCandCap + i];
-    if (tid == 0) s_nsel = 0u;
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      for (int s = wave; s < S; s += kSelThreads / 64) {
+        const unsigned long long* src = ws.cand + ((size_t)t * S + s) * kSlots;
+        if (lane < (int)s_cnt[s]) s_cand[s_off[s] + lane] = src[lane];
+      }
+    }
     __syncthreads();
     // composite: key (32 bits) then ~entry (a lower entry ranks higher); 8 digits of 8 bits
     uint32_t need = k_eff;
@@ -458,8 +557,7 @@ hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_
                           float softmax_scale, int32_t* idx_out, float* out, void* ws_base,
                           hipStream_t stream) {
   PrefillWs ws = prefill_ws_carve(ws_base, T, n_entries);
-  const int n_splits = prefill_splits(n_entries);
-  const dim3 ggrid((T + kGemmRows - 1) / kGemmRows, n_splits);
+  const dim3 ggrid((T + kGemmRows - 1) / kGemmRows, ws.n_splits);
   if (n_entries > 0) {
     hipLaunchKernelGGL(k_prefill_gemm<1>, ggrid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
                        idx_scale, n_entries, ratio, pos0, T, ws);
@@ -472,10 +570,10 @@ hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_
   }
   int k_pow2 = 1;
   while (k_pow2 < k) k_pow2 <<= 1;
-  const size_t lds = (size_t)kCandCap * 8 + (size_t)k_pow2 * 4;
+  const size_t lds = (size_t)kCandLds * 8 + (size_t)k_pow2 * 4;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_prefill_select), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)((size_t)kCandCap * 8 + (size_t)kMaxKPow2 * 4));
+      (int)((size_t)kCandLds * 8 + (size_t)kMaxKPow2 * 4));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), lds, stream, q_idx, idx_codes,
                      idx_scale, n_entries, ratio, pos0, T, k, k_pow2, idx_out, ws);
