@@ -45,9 +45,10 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense BF16 MFMA, published
 IDX_ENTRY_BYTES = 68         # 128 x 4 bit + 4-byte scale
 MAIN_ENTRY_BYTES = 288       # 512 x 4 bit + 32 E4M3 scale bytes
 D_KV, HEADS, SWA, D_IDX = 512, 16, 128, 128
-SCAN_SOURCES = ("compressed_sparse_kv_csa2_amd/csrc/index_score.hip",
-                "compressed_sparse_kv_csa2_amd/csrc/csa2_device.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_c4_long_decode_traffic.md")
+SCAN_SOURCES = tuple("compressed_sparse_kv_csa2_amd/csrc/" + f for f in
+                     ("index_topk.hip", "scan_device.h", "select_device.h", "csa2_device.h",
+                      "csa2_internal.h"))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_topk_c4_long_decode_traffic.md")
 
 
 def parse():
@@ -59,6 +60,8 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: the "
                    "workload's default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unfused", action="store_true",
+                   help="decode: csa2_index_score + csa2_topk instead of csa2_index_topk")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="queries of the first input set the CPU oracle runs (0: default)")
     p.add_argument("--no-phases", action="store_true",
@@ -93,8 +96,8 @@ def scan_source_digest() -> str:
 
 
 def read_traffic():
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary, or None when
-    the summary is absent or was taken on a different version of the scan kernel."""
+    """HBM bytes per launch of the fused Full scan + top-k from the committed rocprofv3 counter
+    summary, or None when the summary is absent or was taken on other kernel sources."""
     try:
         text = open(TRAFFIC_FILE, encoding="utf-8").read()
     except OSError:
@@ -170,8 +173,14 @@ class Decode:
         self.sets = [DecodeSet(synth, torch, self.B, self.N, cfg["seed"] + 1000 * s, dev, self.layers)
                      for s in range(n_sets)]
         B, N = self.B, self.N
-        self.ws = [csa2.topk_workspace(B, N, self.POOL or self.K, device=dev) for _ in self.sets]
-        self.scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+        self.unfused = args.unfused
+        if self.unfused:  # csa2_index_score + csa2_topk, the scores written out in between
+            self.ws = [csa2.topk_workspace(B, N, self.POOL or self.K, device=dev) for _ in self.sets]
+            self.scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+        else:             # csa2_index_topk: scores stay on chip
+            self.fws = csa2.index_topk_workspace(B, N, self.POOL or self.K, device=dev)
+            if self.POOL:
+                self.rws = csa2.index_topk_workspace(B, self.POOL, self.K, device=dev)
         if self.POOL:
             self.pool = torch.empty((B, self.POOL), dtype=torch.int32, device=dev)
             self.pool_scores = torch.empty((B, self.POOL), dtype=torch.float32, device=dev)
@@ -184,40 +193,51 @@ class Decode:
         self.stream = torch.cuda.current_stream()
         self.queries_per_step = B
         self.n_marks = 4
-        self.phase_names = ["scan_us", "select_us", "attention_us"]
+        self.phase_names = ["full_scan_select_us", "reindex_select_us", "attention_us"]
 
     def step(self, i, marks=None):
         """One pass of the whole path over input set i % n.  marks[j] (events) are recorded at
-        the phase boundaries: 0 before the scan, 1 after it, 2 before the attentions, 3 at the end."""
+        the phase boundaries: 0 before the Full layer, 1 after its scan and selection, 2 before
+        the attentions, 3 at the end."""
         csa2, s = self.csa2, self.stream
-        w, tw = self.sets[i % len(self.sets)], self.ws[i % len(self.sets)]
+        w = self.sets[i % len(self.sets)]
         c = w.cache
         m = marks if marks is not None else Marks([None] * 4)
         first = self.layers[0]
+        full_k = self.POOL or self.K
+        full_out = self.pool if self.POOL else self.idx[first]
+        full_scores = self.pool_scores if self.name == "c3" else None
         m[0].record(s)
-        csa2.csa2_index_score(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
-                              self.scores, topk_ws=tw, stream=s)
+        if self.unfused:
+            tw = self.ws[i % len(self.sets)]
+            csa2.csa2_index_score(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                                  self.scores, topk_ws=tw, stream=s)
+            csa2.csa2_topk(self.scores, c.n_entries, full_k, full_out, score_out=full_scores,
+                           hist_fused=True, workspace=tw, stream=s)
+        else:
+            csa2.csa2_index_topk(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                                 full_k, full_out, self.fws, self.N, score_out=full_scores, stream=s)
         m[1].record(s)
         lists = {}
         if self.name == "c2":
-            csa2.csa2_topk(self.scores, c.n_entries, self.K, self.idx[first], hist_fused=True,
-                           workspace=tw, stream=s)
             lists[first] = self.idx[first]
         else:
-            csa2.csa2_topk(self.scores, c.n_entries, self.POOL, self.pool,
-                           score_out=self.pool_scores if self.name == "c3" else None,
-                           hist_fused=True, workspace=tw, stream=s)
             if self.name == "c3":  # the Full layer's own top-512, inside its pool
                 csa2.csa2_topk(self.pool_scores, self.pool_valid, self.K, self.idx[first],
                                cand=self.pool, stream=s)
                 lists[first] = self.idx[first]
             for l in self.layers[1:]:
                 if l in self.REINDEX:
-                    csa2.csa2_index_score(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
-                                          self.pool_valid, self.rescore, cand=self.pool,
-                                          topk_ws=tw, stream=s)
-                    csa2.csa2_topk(self.rescore, self.pool_valid, self.K, self.idx[l], cand=self.pool,
-                                   hist_fused=True, workspace=tw, stream=s)
+                    if self.unfused:
+                        csa2.csa2_index_score(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
+                                              self.pool_valid, self.rescore, cand=self.pool,
+                                              topk_ws=tw, stream=s)
+                        csa2.csa2_topk(self.rescore, self.pool_valid, self.K, self.idx[l],
+                                       cand=self.pool, hist_fused=True, workspace=tw, stream=s)
+                    else:
+                        csa2.csa2_index_topk(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
+                                             self.pool_valid, self.K, self.idx[l], self.rws,
+                                             self.POOL, cand=self.pool, stream=s)
                     lists[l] = self.idx[l]
                 else:  # Reuse: the list of the most recent Full/Reindex layer
                     lists[l] = lists[max(x for x in lists if x <= l)]
@@ -230,7 +250,9 @@ class Decode:
         self.last_lists, self.last_out = lists, [self.out[l] for l in att_layers]
 
     def dominant(self):
-        return {"kernel": "k_index_score (Full scan)", "bound": "hbm", "unit": "GB/s",
+        kernel = ("Full scan + top-k as separate launches (k_index_score, k_topk_*)"
+                  if self.unfused else "k_index_topk<false> (Full scan + top-k in one launch)")
+        return {"kernel": kernel, "bound": "hbm", "unit": "GB/s",
                 "peak": HBM_PEAK_GBS, "work": self.B * self.N * IDX_ENTRY_BYTES,
                 "scale": 1e9, "marks": (0, 1)}
 
@@ -269,7 +291,7 @@ class Decode:
         """The fp64 oracle on the host: the same step for `rows` sequences of the first set."""
         import oracle
         w, B, N = self.sets[0], self.B, self.N
-        rows = max(1, min(rows or {"c4": 2, "c2": 8, "c3": 1}[self.name], B))
+        rows = max(1, min(rows or {"c4": 4, "c2": 32, "c3": 4}[self.name], B))
         c = w.cache
         codes, scale = host(c.idx_codes[: rows * N]), host(c.idx_scale[: rows * N])
         kvc, kvs = host(c.kv_codes[: rows * N]), host(c.kv_scale[: rows * N])
@@ -466,7 +488,8 @@ def main():
         "roofline": {"kernel": dom["kernel"], "bound": dom["bound"], "achieved": round(achieved, 1),
                      "peak": dom["peak"], "unit": dom["unit"],
                      "frac": round(achieved / dom["peak"], 4),
-                     "traffic": read_traffic() if headline else None,
+                     "traffic": read_traffic() if headline and not getattr(args, "unfused", False)
+                     else None,
                      "algorithmic_per_launch": dom["work"],
                      "avg_launch_us": round(dom_ms * 1e3, 2)},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_gbs": round(step_gbs, 1),

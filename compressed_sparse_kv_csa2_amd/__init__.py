@@ -17,9 +17,9 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "csa2_index_score", "csa2_topk", "csa2_sparse_attn_decode", "csa2_prefill_chunk",
-    "csa2_topk_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
-    "topk_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
+    "csa2_index_score", "csa2_topk", "csa2_index_topk", "csa2_sparse_attn_decode",
+    "csa2_prefill_chunk", "csa2_topk_workspace_size", "csa2_index_topk_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
+    "topk_workspace", "index_topk_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
     "CSA2_TOPK_HIST_FUSED", "Csa2Error",
 ]
 
@@ -41,6 +41,9 @@ _SIGS = {
     "csa2_index_score": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "csa2_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "csa2_topk": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _U32, _P, _SZ, _P]),
+    "csa2_index_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "csa2_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _SZ,
+                                       _P]),
     "csa2_attn_workspace_size": (_SZ, [_I32, _I32]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _F32, _I32, _P, _P,
                                                _SZ, _P]),
@@ -111,6 +114,10 @@ def csa2_topk_workspace_size(batch: int, n_cols: int, k: int) -> int:
     return int(load_library().csa2_topk_workspace_size(batch, n_cols, k))
 
 
+def csa2_index_topk_workspace_size(batch: int, n_cols: int, k: int) -> int:
+    return int(load_library().csa2_index_topk_workspace_size(batch, n_cols, k))
+
+
 def csa2_attn_workspace_size(batch: int, k: int) -> int:
     return int(load_library().csa2_attn_workspace_size(batch, k))
 
@@ -126,6 +133,11 @@ def _zeros(nbytes: int, device) -> torch.Tensor:
 def topk_workspace(batch, n_cols, k, device="cuda"):
     """Zero-filled workspace for csa2_topk (and the fused histogram of csa2_index_score)."""
     return _zeros(csa2_topk_workspace_size(batch, n_cols, k), device)
+
+
+def index_topk_workspace(batch, n_cols, k, device="cuda"):
+    """Zero-filled workspace for csa2_index_topk (its first int32 is the status word)."""
+    return _zeros(csa2_index_topk_workspace_size(batch, n_cols, k), device)
 
 
 def attn_workspace(batch, k, device="cuda"):
@@ -174,6 +186,28 @@ def csa2_topk(scores, n_valid, k, idx_out, score_out=None, cand=None, hist_fused
     _check(lib.csa2_topk(_ptr(scores), B, n_cols, _ptr(n_valid), _ptr(cand), k, _ptr(idx_out),
                          _ptr(score_out), CSA2_TOPK_HIST_FUSED if hist_fused else 0, _ptr(workspace),
                          0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def csa2_index_topk(q_idx, idx_codes, idx_scale, seq_base, n_valid, k, idx_out, workspace,
+                    n_cols, score_out=None, cand=None, stream=None):
+    """csa2_index_score + csa2_topk in one call: idx_out [B, k] of the n_cols columns."""
+    B = q_idx.shape[0]
+    _need(q_idx, "q_idx", _BF16, (B, 128))
+    _need(idx_codes, "idx_codes", _U8, (None, 64))
+    _need(idx_scale, "idx_scale", (torch.float32,), (idx_codes.shape[0],))
+    _need(seq_base, "seq_base", (torch.int64,), (B,))
+    _need(n_valid, "n_valid", (torch.int32,), (B,))
+    _need(idx_out, "idx_out", (torch.int32,), (B, k))
+    if score_out is not None:
+        _need(score_out, "score_out", (torch.float32,), (B, k))
+    if cand is not None:
+        _need(cand, "cand", (torch.int32,), (B, n_cols))
+    _need(workspace, "workspace", _U8)
+    lib = load_library()
+    _check(lib.csa2_index_topk(_ptr(q_idx), _ptr(idx_codes), _ptr(idx_scale), _ptr(seq_base),
+                               _ptr(n_valid), _ptr(cand), B, n_cols, k, _ptr(idx_out),
+                               _ptr(score_out), _ptr(workspace), workspace.numel(),
+                               _stream(stream)))
 
 
 def csa2_sparse_attn_decode(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, out, workspace,

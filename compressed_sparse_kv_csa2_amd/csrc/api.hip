@@ -80,6 +80,31 @@ int csa2_topk(const float* scores, int32_t batch, int32_t n_cols, const int32_t*
                               static_cast<hipStream_t>(stream)));
 }
 
+size_t csa2_index_topk_workspace_size(int32_t batch, int32_t n_cols, int32_t k) {
+  (void)k;
+  if (batch < 1 || n_cols < 1 || n_cols > kTopkMaxCols) return 0;
+  return index_topk_ws_bytes(batch, n_cols);
+}
+
+int csa2_index_topk(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                    const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
+                    int32_t batch, int32_t n_cols, int32_t k, int32_t* idx_out, float* score_out,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  if (!q_idx || !idx_codes || !idx_scale || !seq_base || !n_valid || !idx_out)
+    return CSA2_ERR_INVALID_ARG;
+  if (batch < 1 || n_cols < 1 || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_INVALID_ARG;
+  if (n_cols > kTopkMaxCols) return CSA2_ERR_UNSUPPORTED;
+  if (!aligned(q_idx, 16) || !aligned(idx_codes, 16) || !aligned(idx_scale, 4) ||
+      !aligned(seq_base, 8) || !aligned(n_valid, 4) || !aligned(idx_out, 4) ||
+      (score_out && !aligned(score_out, 4)) || (cand && !aligned(cand, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  if (!workspace || ws_bytes < index_topk_ws_bytes(batch, n_cols)) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_index_topk(q_idx, idx_codes, idx_scale, seq_base, n_valid, cand, batch,
+                                    n_cols, k, idx_out, score_out, workspace,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 size_t csa2_attn_workspace_size(int32_t batch, int32_t k) {
   if (batch < 1 || k < 0) return 0;
   return attn_ws_bytes(batch, k);

@@ -69,41 +69,12 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(u);
 }
 
-// Agent-scope release / acquire used by the "last workgroup of a row finishes the row"
-// pattern: every workgroup publishes its results, then bumps a per-row counter; the one
-// that sees the final count reads everything the others wrote.
+// Agent-scope release / acquire around the row barriers of the fused scan + top-k.
 __device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ unsigned long long atomic_or_agent(unsigned long long* p,
-                                                              unsigned long long v) {
-  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Bumps the row counter after a release fence; returns true in the workgroup that
-// arrives last (all threads of the block get the answer).  `flag` is LDS scratch.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected,
-                                            uint32_t* flag) {
-  fence_release();  // every wave publishes its own global writes at agent scope
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (old == expected - 1u) ? 1u : 0u;
-  }
-  __syncthreads();
-  bool last = *flag != 0u;
-  if (last) fence_acquire();
-  return last;
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_bcast_first(T v) {
-  return __builtin_amdgcn_readfirstlane(v);
 }
 
 }  // namespace csa2

@@ -27,8 +27,8 @@
 //   k_topk_compact  many workgroups per row: columns with comp >= T in column order at
 //                   their chunk's offset (wave ballots, one LDS scan).
 // No host round trip and no global atomics beyond the fused histogram.
-#include "csa2_device.h"
 #include "csa2_internal.h"
+#include "select_device.h"
 
 namespace csa2 {
 
@@ -78,105 +78,6 @@ TopkWs topk_ws_carve(void* base, int batch, int n_cols) {
 }
 
 // ---------------------------------------------------------------------------- helpers
-// Executed by ONE wave: finds the bin holding the need-th largest element of h[0..nbins)
-// (nbins a multiple of 64, 1 <= need <= total).  out[0] = bin, out[1] = elements above.
-__device__ void find_threshold_bin(const uint32_t* h, int nbins, uint32_t need, uint32_t* out) {
-  const int lane = threadIdx.x & 63;
-  if (lane == 0) {  // defined result even if need exceeded the total (it never should)
-    out[0] = 0u;
-    out[1] = 0u;
-  }
-  const int per = nbins / 64;
-  const int hi = nbins - lane * per;  // lane 0 owns the top bins
-  uint32_t sum = 0;
-  for (int i = 1; i <= per; ++i) sum += h[hi - i];
-  uint32_t incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  const uint32_t excl = incl - sum;
-  if (excl < need && need <= incl) {
-    uint32_t acc = excl;
-    for (int i = 1; i <= per; ++i) {
-      uint32_t c = h[hi - i];
-      if (acc + c >= need) {
-        out[0] = (uint32_t)(hi - i);
-        out[1] = acc;
-        break;
-      }
-      acc += c;
-    }
-  }
-}
-
-// Block-wide exclusive scan of one u32 per thread; returns the exclusive prefix and
-// stores the block total in *total.  `scratch` holds >= 17 u32 of LDS.  Ends with a barrier.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  __syncthreads();
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      uint32_t t = scratch[w];
-      scratch[w] = run;
-      run += t;
-    }
-    scratch[16] = run;
-  }
-  __syncthreads();
-  uint32_t r = scratch[wave] + incl - v;
-  *total = scratch[16];
-  __syncthreads();
-  return r;
-}
-
-// Block-wide search of a histogram h[0..PER * blockDim.x) in LDS for the bin holding the
-// need-th largest element (1 <= need <= total): thread t owns the PER bins just below bin
-// PER*(blockDim - t), and one block scan orders them from the top.  out[0] = bin,
-// out[1] = elements in higher bins.  Ends with a barrier.
-template <int PER>
-__device__ void find_bin_block(const uint32_t* h, uint32_t need, uint32_t* s_scan, uint32_t* out) {
-  const int top = PER * (int)(blockDim.x - threadIdx.x);
-  uint32_t c[PER];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = h[top - 1 - i];
-    sum += c[i];
-  }
-  if (threadIdx.x == 0) {  // defined result even if need exceeded the total (it never should)
-    out[0] = 0u;
-    out[1] = 0u;
-  }
-  uint32_t total;
-  const uint32_t excl = block_exclusive_scan(sum, s_scan, &total);
-  if (excl < need && need <= excl + sum) {
-    uint32_t acc = excl;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (acc + c[i] >= need) {
-        out[0] = (uint32_t)(top - 1 - i);
-        out[1] = acc;
-        break;
-      }
-      acc += c[i];
-    }
-  }
-  __syncthreads();
-}
-
 // Key of column col of a row, 0 when the column is not selectable.
 __device__ __forceinline__ uint32_t col_key(const float* srow, const int32_t* crow, int nv, int col) {
   if (col >= nv) return 0u;
@@ -206,35 +107,7 @@ __device__ __forceinline__ void load_keys(const float* srow, const int32_t* crow
     key[i] = (col0 + i * step < nv && id[i] >= 0) ? score_key(s[i]) : 0u;
 }
 
-__device__ __forceinline__ unsigned long long composite(uint32_t key, uint32_t col) {
-  return ((unsigned long long)key << 32) | (uint32_t)~col;
-}
-
-__device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 __device__ __forceinline__ uint32_t digit2(uint32_t key) { return (key >> 9) & (kHist2Bins - 1); }
-
-// Exclusive scan, in place, of the n <= 128 per-(iteration, wave) counts in s_cnt, by wave 0;
-// returns the total to every lane of wave 0.
-__device__ uint32_t scan_counts_wave0(uint32_t* s_cnt, int n) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t a = 2 * lane < n ? s_cnt[2 * lane] : 0u;
-  const uint32_t b = 2 * lane + 1 < n ? s_cnt[2 * lane + 1] : 0u;
-  const uint32_t pair = a + b;
-  uint32_t incl = pair;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  const uint32_t excl = incl - pair;
-  if (2 * lane < n) s_cnt[2 * lane] = excl;
-  if (2 * lane + 1 < n) s_cnt[2 * lane + 1] = excl + a;
-  return __shfl(incl, 63);
-}
 
 // Radix passes over the 41 composite bits below the 23 key bits fixed by the level-1 and
 // level-2 bins: `visit(f)` calls f(composite) for every candidate still in play.  Returns

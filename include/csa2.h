@@ -135,6 +135,37 @@ int csa2_topk(const float* scores, int32_t batch, int32_t n_cols, const int32_t*
               const int32_t* cand, int32_t k, int32_t* idx_out, float* score_out,
               uint32_t flags, void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of workspace csa2_index_topk needs for this shape on the current device. */
+size_t csa2_index_topk_workspace_size(int32_t batch, int32_t n_cols, int32_t k);
+
+/*
+ * csa2_index_topk -- a1 + a2 (Full) or a3 + a2 (Reindex) in one call: scores the columns
+ * exactly as csa2_index_score does and selects the top-k exactly as csa2_topk does on
+ * those scores (same rule, same output), without writing the scores to memory.
+ *   [V4TO41] CSA2 architecture section (Full runs the sparse indexer over its keys and
+ *   keeps the best entries; Reindex re-picks with its own indexer query) and decoder
+ *   section (pool of about 16K positions); [STRUCT] commentary on the four layer modes.
+ *
+ *   q_idx, idx_codes, idx_scale, seq_base, n_valid, cand   as for csa2_index_score
+ *                                             (cand ascending in the entry id over its
+ *                                             valid columns, as for csa2_topk)
+ *   k          1..16384
+ *   idx_out    i32 [batch][k]  (out)          as for csa2_topk
+ *   score_out  f32 [batch][k] or NULL (out)   as for csa2_topk
+ *   workspace  device, 256-byte aligned, csa2_index_topk_workspace_size bytes, zero-filled
+ *              before its first use; each call leaves it ready for the next one.  Its
+ *              first 4 bytes are a sticky status word that stays 0 unless a row barrier of
+ *              the single-launch kernel gave up waiting (results of that call undefined).
+ *              Calls sharing one workspace must not run concurrently.
+ * A row whose workgroups all fit on the device at once is scored and selected in one
+ * cooperative launch; longer rows run csa2_index_score's and csa2_topk's kernels.
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_cols > 2^26), HIP.
+ */
+int csa2_index_topk(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                    const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
+                    int32_t batch, int32_t n_cols, int32_t k, int32_t* idx_out, float* score_out,
+                    void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace csa2_sparse_attn_decode needs for this shape. */
 size_t csa2_attn_workspace_size(int32_t batch, int32_t k);
 

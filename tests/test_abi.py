@@ -99,3 +99,14 @@ def test_prefill_validation(lib):
                            (16, 10, -3)]:
         a = list(base); a[pos] = val
         assert f(*a) == want, (pos, val)
+
+
+def test_index_topk_validation(lib):
+    f = lib.csa2_index_topk
+    base = [FAKE] * 6 + [4, 1 << 20, 16384, FAKE, None, FAKE, 1 << 40, None]
+    for pos, val, want in [(8, 0, -1), (8, 16385, -1), (6, 0, -1), (0, None, -1), (9, None, -1),
+                           (1, ODD, -2), (11, None, -3), (12, 100, -3), (7, (1 << 26) + 1, -4)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
+    assert lib.csa2_index_topk_workspace_size(0, 10, 1) == 0
+    assert lib.csa2_index_topk_workspace_size(4, 1 << 20, 16384) > 0

@@ -1,0 +1,226 @@
+"""GPU parity of csa2_index_topk (scan + top-k in one call) through the C ABI.
+
+Its selection is compared (1) bit for bit with the oracle's selection rule applied to the
+GPU's own fp32 scores from csa2_index_score (both calls run the same scan arithmetic),
+(2) with csa2_index_score + csa2_topk, output for output, and (3) against fp64 oracle
+scores under the gap rule.  The workspace must come back ready for the next call: the
+status word stays 0 and the histograms and barrier counters return to zero.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_kv_csa2_amd as csa2
+import oracle
+import synth
+from _util import check_topk
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    csa2.load_library()
+
+
+def h(t):
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def i32(x):
+    return torch.tensor(x, dtype=torch.int32, device=DEV)
+
+
+def fused(cache, q_idx, n_cols, k, n_valid=None, cand=None, ws=None):
+    B = q_idx.shape[0]
+    nv = cache.n_entries if n_valid is None else n_valid
+    ws = csa2.index_topk_workspace(B, n_cols, k) if ws is None else ws
+    idx = torch.full((B, k), -7, dtype=torch.int32, device=DEV)
+    so = torch.full((B, k), 7.0, dtype=torch.float32, device=DEV)
+    csa2.csa2_index_topk(q_idx, cache.idx_codes, cache.idx_scale, cache.seq_base, nv, k, idx, ws,
+                         n_cols, score_out=so, cand=cand)
+    return idx, so, ws
+
+
+def two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None):
+    B = q_idx.shape[0]
+    nv = cache.n_entries if n_valid is None else n_valid
+    sc = torch.empty((B, n_cols), dtype=torch.float32, device=DEV)
+    csa2.csa2_index_score(q_idx, cache.idx_codes, cache.idx_scale, cache.seq_base, nv, sc, cand=cand)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    so = torch.empty((B, k), dtype=torch.float32, device=DEV)
+    ws = csa2.topk_workspace(B, n_cols, k) if n_cols > 16384 else None
+    csa2.csa2_topk(sc, nv, k, idx, score_out=so, cand=cand, workspace=ws)
+    return sc, idx, so
+
+
+def ws_clean(ws, B):
+    """Status word 0; histograms and barrier counters back to zero."""
+    w = h(ws)
+    assert w[:4].view(np.uint32)[0] == 0, "a row barrier gave up waiting"
+    a = 256
+    n = 0
+    for per_row in (4096, 2048, 512, 32):  # hist1, hist2, hist3, barrier counters
+        n += -(-B * per_row * 4 // 256) * 256
+    assert not w[a:a + n].any(), "histograms or barrier counters not returned to zero"
+
+
+def same_as_two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None, rows=None):
+    idx, so, ws = fused(cache, q_idx, n_cols, k, n_valid, cand)
+    sc, idx2, so2 = two_step(cache, q_idx, n_cols, k, n_valid, cand)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2), "differs from csa2_index_score + csa2_topk"
+    assert torch.equal(so, so2), "scores of the selection differ"
+    nv = h(cache.n_entries if n_valid is None else n_valid)
+    s = h(sc)
+    c = None if cand is None else h(cand)
+    for b in (range(q_idx.shape[0]) if rows is None else rows):
+        if c is None:
+            want = oracle.topk(s[b].astype(np.float64), k, n_valid=int(nv[b]))
+            assert np.array_equal(h(idx)[b], want), f"row {b}"
+        else:
+            keep = np.arange(n_cols) < nv[b]
+            keep &= c[b] >= 0
+            sel = oracle.topk(np.where(keep, s[b].astype(np.float64), -np.inf), k)
+            want = np.where(sel >= 0, c[b][np.maximum(sel, 0)], -1)
+            assert np.array_equal(h(idx)[b], want), f"row {b}"
+    return idx, so, ws
+
+
+@pytest.mark.parametrize("n,k", [(1, 4), (700, 512), (2048, 512), (5000, 512), (33_000, 512),
+                                 (70_000, 16384), (131_072 + 77, 16384), (16384, 16384)])
+def test_full_matches_two_step_and_oracle_rule(n, k):
+    log(f"index_topk full n={n} k={k}")
+    B = 3
+    lens = [n, max(1, n // 3), max(1, n - 129)]
+    cache = synth.make_entries(lens, seed=200 + n % 97, device=DEV)
+    q = synth.make_index_queries(B, 200 + n % 97, device=DEV)
+    _, _, ws = same_as_two_step(cache, q, n, k)
+    ws_clean(ws, B)
+
+
+def test_full_against_fp64_oracle_scores():
+    log("index_topk gap rule")
+    n = 20_000
+    cache = synth.make_entries([n, n - 11], seed=31, device=DEV)
+    q = synth.make_index_queries(2, 31, device=DEV)
+    idx, _, _ = fused(cache, q, n, 512)
+    torch.cuda.synchronize()
+    codes, scale = h(cache.idx_codes), h(cache.idx_scale)
+    for b, (base, cnt) in enumerate([(0, n), (n, n - 11)]):
+        ref = oracle.index_scores(h(q)[b], codes[base:base + cnt], scale[base:base + cnt])
+        check_topk(h(idx)[b], ref, 512, label=f"row {b}")
+
+
+def test_reindex_candidates_with_holes():
+    log("index_topk reindex")
+    n, P = 40_000, 16384
+    cache = synth.make_entries([n, n, n], seed=32, device=DEV)
+    q = synth.make_index_queries(3, 32, device=DEV)
+    rng = np.random.default_rng(32)
+    cand = np.stack([np.sort(rng.choice(n, P, replace=False)) for _ in range(3)]).astype(np.int32)
+    cand[1, 5000:5100] = -1
+    cand[2, P - 300:] = -1
+    cand_t = torch.from_numpy(cand).to(DEV)
+    _, _, ws = same_as_two_step(cache, q, P, 512, n_valid=i32([P, P, P - 17]), cand=cand_t)
+    ws_clean(ws, 3)
+
+
+def test_empty_rows_and_more_k_than_columns():
+    log("index_topk empty / short")
+    cache = synth.make_entries([3000, 3000, 3000], seed=33, device=DEV)
+    q = synth.make_index_queries(3, 33, device=DEV)
+    idx, so, ws = fused(cache, q, 3000, 600, n_valid=i32([0, 3000, 450]))
+    torch.cuda.synchronize()
+    g, s = h(idx), h(so)
+    assert np.all(g[0] == -1) and np.all(np.isneginf(s[0]))
+    assert np.all(g[2][:450] == np.arange(450)) and np.all(g[2][450:] == -1)
+    assert np.all(np.isneginf(s[2][450:]))
+    ws_clean(ws, 3)
+
+
+def test_all_ties_take_lowest_columns():
+    log("index_topk ties")
+    n = 50_000
+    cache = synth.make_entries([n], seed=34, device=DEV)
+    q = torch.zeros((1, 128), dtype=torch.int16, device=DEV)  # every score is 0
+    for k in (512, 16384):
+        idx, _, ws = fused(cache, q, n, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(h(idx)[0], np.arange(k))
+        ws_clean(ws, 1)
+
+
+@pytest.mark.parametrize("dims,k", [(1, 512), (1, 16384), (3, 512), (3, 16384)])
+def test_ties_at_the_threshold(dims, k):
+    """Unit scales and a query with few non-zero components: scores take few distinct
+    values, so the k-th score is shared by many columns across many workgroups (with one
+    component: thousands, the massive-tie path; with three: a handful)."""
+    log(f"index_topk threshold ties dims={dims} k={k}")
+    n = 300_000
+    cache = synth.make_entries([n, n - 1000], seed=40 + dims, device=DEV)
+    cache.idx_scale.fill_(1.0)
+    q = torch.zeros((2, 128), dtype=torch.float32)
+    q[:, :dims] = torch.tensor([1.0, 0.5, 0.25][:dims])
+    q_bits = q.to(torch.bfloat16).view(torch.int16).to(DEV)
+    _, _, ws = same_as_two_step(cache, q_bits, n, k)
+    ws_clean(ws, 2)
+
+
+def test_workspace_reuse_is_deterministic():
+    log("index_topk reuse")
+    n = 100_000
+    caches = [synth.make_entries([n, n], seed=35 + i, device=DEV) for i in range(2)]
+    qs = [synth.make_index_queries(2, 35 + i, device=DEV) for i in range(2)]
+    ws = csa2.index_topk_workspace(2, n, 16384)
+    outs = []
+    for it in range(4):
+        idx, _, _ = fused(caches[it % 2], qs[it % 2], n, 16384, ws=ws)
+        outs.append(idx.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
+    assert not torch.equal(outs[0], outs[1])
+    ws_clean(ws, 2)
+
+
+def test_long_decode_pool_and_reindex_at_full_size():
+    """4 x 2^20 Full scan -> pool of 16,384 -> Reindex top-512, as the benchmark runs it."""
+    cfg = synth.CONFIGS["c4_long_decode"]
+    B, N = cfg["B"], 1 << 20
+    log(f"index_topk 2^20 B={B}")
+    cache = synth.make_entries([N] * B, seed=cfg["seed"], device=DEV)
+    q_full = synth.make_index_queries(B, cfg["seed"], device=DEV)
+    q_re = synth.make_index_queries(B, cfg["seed"] + 1000, device=DEV)
+    pool, _, ws = same_as_two_step(cache, q_full, N, 16384, rows=[0, 3])
+    ws_clean(ws, B)
+    same_as_two_step(cache, q_re, 16384, 512, n_valid=i32([16384] * B), cand=pool)
+
+
+def test_rows_split_over_several_launches():
+    """5 x 2^20 columns need more workgroups than fit at once: rows go in several launches."""
+    B, N = 5, 1 << 20
+    log(f"index_topk split B={B}")
+    cache = synth.make_entries([N] * B, seed=36, device=DEV)
+    q = synth.make_index_queries(B, 36, device=DEV)
+    _, _, ws = same_as_two_step(cache, q, N, 512, rows=[0, 4])
+    ws_clean(ws, B)
+
+
+def test_row_longer_than_one_resident_grid():
+    """A row of more than 256 x 16,384 columns (more workgroups than CUs) takes the two-launch
+    path inside the call."""
+    n = 256 * 16384 + 5000
+    log(f"index_topk long row n={n}")
+    cache = synth.make_entries([n], seed=37, device=DEV)
+    q = synth.make_index_queries(1, 37, device=DEV)
+    same_as_two_step(cache, q, n, 16384)
