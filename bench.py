@@ -60,8 +60,9 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: the "
                    "workload's default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--unfused", action="store_true",
-                   help="decode: csa2_index_score + csa2_topk instead of csa2_index_topk")
+    p.add_argument("--select", default="chain", choices=["chain", "fused", "unfused"],
+                   help="decode selections: csa2_select_chain (one launch), csa2_index_topk per "
+                        "layer, or csa2_index_score + csa2_topk per layer")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="queries of the first input set the CPU oracle runs (0: default)")
     p.add_argument("--no-phases", action="store_true",
@@ -173,14 +174,21 @@ class Decode:
         self.sets = [DecodeSet(synth, torch, self.B, self.N, cfg["seed"] + 1000 * s, dev, self.layers)
                      for s in range(n_sets)]
         B, N = self.B, self.N
-        self.unfused = args.unfused
-        if self.unfused:  # csa2_index_score + csa2_topk, the scores written out in between
+        self.mode = args.select
+        if self.mode == "unfused":  # csa2_index_score + csa2_topk, the scores written out
             self.ws = [csa2.topk_workspace(B, N, self.POOL or self.K, device=dev) for _ in self.sets]
             self.scores = torch.empty((B, N), dtype=torch.float32, device=dev)
-        else:             # csa2_index_topk: scores stay on chip
+        elif self.mode == "fused" or not self.POOL:  # csa2_index_topk per selection
             self.fws = csa2.index_topk_workspace(B, N, self.POOL or self.K, device=dev)
             if self.POOL:
                 self.rws = csa2.index_topk_workspace(B, self.POOL, self.K, device=dev)
+        else:                       # csa2_select_chain: every selection in one launch
+            self.cws = csa2.select_chain_workspace(B, N, self.POOL, device=dev)
+            re = [l for l in self.layers[1:] if l in self.REINDEX]
+            self.re_layers = re
+            self.re_out = torch.empty((len(re), B, self.K), dtype=torch.int32, device=dev)
+            for s_ in self.sets:
+                s_.q_re = torch.stack([s_.q_idx[l] for l in re]).contiguous()
         if self.POOL:
             self.pool = torch.empty((B, self.POOL), dtype=torch.int32, device=dev)
             self.pool_scores = torch.empty((B, self.POOL), dtype=torch.float32, device=dev)
@@ -193,7 +201,9 @@ class Decode:
         self.stream = torch.cuda.current_stream()
         self.queries_per_step = B
         self.n_marks = 4
-        self.phase_names = ["full_scan_select_us", "reindex_select_us", "attention_us"]
+        self.phase_names = (["select_chain_us", None, "attention_us"]
+                            if self.mode == "chain" and self.POOL else
+                            ["full_scan_select_us", "reindex_select_us", "attention_us"])
 
     def step(self, i, marks=None):
         """One pass of the whole path over input set i % n.  marks[j] (events) are recorded at
@@ -208,39 +218,54 @@ class Decode:
         full_out = self.pool if self.POOL else self.idx[first]
         full_scores = self.pool_scores if self.name == "c3" else None
         m[0].record(s)
-        if self.unfused:
-            tw = self.ws[i % len(self.sets)]
-            csa2.csa2_index_score(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
-                                  self.scores, topk_ws=tw, stream=s)
-            csa2.csa2_topk(self.scores, c.n_entries, full_k, full_out, score_out=full_scores,
-                           hist_fused=True, workspace=tw, stream=s)
-        else:
-            csa2.csa2_index_topk(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
-                                 full_k, full_out, self.fws, self.N, score_out=full_scores, stream=s)
-        m[1].record(s)
         lists = {}
-        if self.name == "c2":
-            lists[first] = self.idx[first]
-        else:
-            if self.name == "c3":  # the Full layer's own top-512, inside its pool
-                csa2.csa2_topk(self.pool_scores, self.pool_valid, self.K, self.idx[first],
-                               cand=self.pool, stream=s)
-                lists[first] = self.idx[first]
+        if self.mode == "chain" and self.POOL:
+            own = self.idx[first] if self.name == "c3" else None
+            csa2.csa2_select_chain(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                                   self.N, self.pool, self.cws, k=self.K, own_out=own,
+                                   q_re=w.q_re, re_out=self.re_out, stream=s)
+            m[1].record(s)
+            if own is not None:
+                lists[first] = own
+            for j, l in enumerate(self.re_layers):
+                lists[l] = self.re_out[j]
             for l in self.layers[1:]:
-                if l in self.REINDEX:
-                    if self.unfused:
-                        csa2.csa2_index_score(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
-                                              self.pool_valid, self.rescore, cand=self.pool,
-                                              topk_ws=tw, stream=s)
-                        csa2.csa2_topk(self.rescore, self.pool_valid, self.K, self.idx[l],
-                                       cand=self.pool, hist_fused=True, workspace=tw, stream=s)
-                    else:
-                        csa2.csa2_index_topk(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
-                                             self.pool_valid, self.K, self.idx[l], self.rws,
-                                             self.POOL, cand=self.pool, stream=s)
-                    lists[l] = self.idx[l]
-                else:  # Reuse: the list of the most recent Full/Reindex layer
+                if l not in lists:  # Reuse: the list of the most recent Full/Reindex layer
                     lists[l] = lists[max(x for x in lists if x <= l)]
+        else:
+            if self.mode == "unfused":
+                tw = self.ws[i % len(self.sets)]
+                csa2.csa2_index_score(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base,
+                                      c.n_entries, self.scores, topk_ws=tw, stream=s)
+                csa2.csa2_topk(self.scores, c.n_entries, full_k, full_out, score_out=full_scores,
+                               hist_fused=True, workspace=tw, stream=s)
+            else:
+                csa2.csa2_index_topk(w.q_idx[first], c.idx_codes, c.idx_scale, c.seq_base,
+                                     c.n_entries, full_k, full_out, self.fws, self.N,
+                                     score_out=full_scores, stream=s)
+            m[1].record(s)
+            if self.name == "c2":
+                lists[first] = self.idx[first]
+            else:
+                if self.name == "c3":  # the Full layer's own top-512, inside its pool
+                    csa2.csa2_topk(self.pool_scores, self.pool_valid, self.K, self.idx[first],
+                                   cand=self.pool, stream=s)
+                    lists[first] = self.idx[first]
+                for l in self.layers[1:]:
+                    if l in self.REINDEX:
+                        if self.mode == "unfused":
+                            csa2.csa2_index_score(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
+                                                  self.pool_valid, self.rescore, cand=self.pool,
+                                                  topk_ws=tw, stream=s)
+                            csa2.csa2_topk(self.rescore, self.pool_valid, self.K, self.idx[l],
+                                           cand=self.pool, hist_fused=True, workspace=tw, stream=s)
+                        else:
+                            csa2.csa2_index_topk(w.q_idx[l], c.idx_codes, c.idx_scale, c.seq_base,
+                                                 self.pool_valid, self.K, self.idx[l], self.rws,
+                                                 self.POOL, cand=self.pool, stream=s)
+                        lists[l] = self.idx[l]
+                    else:  # Reuse: the list of the most recent Full/Reindex layer
+                        lists[l] = lists[max(x for x in lists if x <= l)]
         m[2].record(s)
         att_layers = self.layers if self.name == "c3" else [self.layers[-1]]
         for l in att_layers:
@@ -250,8 +275,10 @@ class Decode:
         self.last_lists, self.last_out = lists, [self.out[l] for l in att_layers]
 
     def dominant(self):
-        kernel = ("Full scan + top-k as separate launches (k_index_score, k_topk_*)"
-                  if self.unfused else "k_index_topk<false> (Full scan + top-k in one launch)")
+        kernel = {"unfused": "Full scan + top-k as separate launches (k_index_score, k_topk_*)",
+                  "fused": "k_index_topk<false> (Full scan + top-k in one launch)",
+                  "chain": "k_index_topk<false> (Full scan, pool, own and Reindex top-512s in one "
+                           "launch)"}[self.mode if self.POOL else "fused"]
         return {"kernel": kernel, "bound": "hbm", "unit": "GB/s",
                 "peak": HBM_PEAK_GBS, "work": self.B * self.N * IDX_ENTRY_BYTES,
                 "scale": 1e9, "marks": (0, 1)}
@@ -460,7 +487,7 @@ def main():
             wl.step(i, Marks(evs[i]))
         torch.cuda.synchronize()
         phases = {n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3 / reps, 2)
-                  for j, n in enumerate(wl.phase_names)}
+                  for j, n in enumerate(wl.phase_names) if n}
 
     torch.cuda.synchronize()
     ok = wl.valid()
@@ -488,8 +515,7 @@ def main():
         "roofline": {"kernel": dom["kernel"], "bound": dom["bound"], "achieved": round(achieved, 1),
                      "peak": dom["peak"], "unit": dom["unit"],
                      "frac": round(achieved / dom["peak"], 4),
-                     "traffic": read_traffic() if headline and not getattr(args, "unfused", False)
-                     else None,
+                     "traffic": read_traffic() if headline and args.select == "chain" else None,
                      "algorithmic_per_launch": dom["work"],
                      "avg_launch_us": round(dom_ms * 1e3, 2)},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved_gbs": round(step_gbs, 1),

@@ -17,9 +17,10 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "csa2_index_score", "csa2_topk", "csa2_index_topk", "csa2_sparse_attn_decode",
-    "csa2_prefill_chunk", "csa2_topk_workspace_size", "csa2_index_topk_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
-    "topk_workspace", "index_topk_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
+    "csa2_index_score", "csa2_topk", "csa2_index_topk", "csa2_select_chain",
+    "csa2_sparse_attn_decode", "csa2_prefill_chunk", "csa2_topk_workspace_size",
+    "csa2_index_topk_workspace_size", "csa2_select_chain_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
+    "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
     "CSA2_TOPK_HIST_FUSED", "Csa2Error",
 ]
 
@@ -44,6 +45,9 @@ _SIGS = {
     "csa2_index_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "csa2_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _SZ,
                                        _P]),
+    "csa2_select_chain_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "csa2_select_chain": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
+                                         _I32, _P, _P, _P, _SZ, _P]),
     "csa2_attn_workspace_size": (_SZ, [_I32, _I32]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _F32, _I32, _P, _P,
                                                _SZ, _P]),
@@ -118,6 +122,10 @@ def csa2_index_topk_workspace_size(batch: int, n_cols: int, k: int) -> int:
     return int(load_library().csa2_index_topk_workspace_size(batch, n_cols, k))
 
 
+def csa2_select_chain_workspace_size(batch: int, n_cols: int, pool_k: int) -> int:
+    return int(load_library().csa2_select_chain_workspace_size(batch, n_cols, pool_k))
+
+
 def csa2_attn_workspace_size(batch: int, k: int) -> int:
     return int(load_library().csa2_attn_workspace_size(batch, k))
 
@@ -138,6 +146,11 @@ def topk_workspace(batch, n_cols, k, device="cuda"):
 def index_topk_workspace(batch, n_cols, k, device="cuda"):
     """Zero-filled workspace for csa2_index_topk (its first int32 is the status word)."""
     return _zeros(csa2_index_topk_workspace_size(batch, n_cols, k), device)
+
+
+def select_chain_workspace(batch, n_cols, pool_k, device="cuda"):
+    """Zero-filled workspace for csa2_select_chain (its first int32 is the status word)."""
+    return _zeros(csa2_select_chain_workspace_size(batch, n_cols, pool_k), device)
 
 
 def attn_workspace(batch, k, device="cuda"):
@@ -208,6 +221,38 @@ def csa2_index_topk(q_idx, idx_codes, idx_scale, seq_base, n_valid, k, idx_out, 
                                _ptr(n_valid), _ptr(cand), B, n_cols, k, _ptr(idx_out),
                                _ptr(score_out), _ptr(workspace), workspace.numel(),
                                _stream(stream)))
+
+
+def csa2_select_chain(q_full, idx_codes, idx_scale, seq_base, n_valid, n_cols, pool_out, workspace,
+                      k=512, pool_score_out=None, own_out=None, q_re=None, re_out=None,
+                      re_score_out=None, stream=None):
+    """Full scan -> pool_out [B, pool_k]; own_out [B, k] (the Full layer's top-k inside the
+    pool); re_out [R, B, k] for the Reindex queries q_re [R, B, 128]."""
+    B, pool_k = pool_out.shape
+    _need(q_full, "q_full", _BF16, (B, 128))
+    _need(idx_codes, "idx_codes", _U8, (None, 64))
+    _need(idx_scale, "idx_scale", (torch.float32,), (idx_codes.shape[0],))
+    _need(seq_base, "seq_base", (torch.int64,), (B,))
+    _need(n_valid, "n_valid", (torch.int32,), (B,))
+    _need(pool_out, "pool_out", (torch.int32,), (B, pool_k))
+    if pool_score_out is not None:
+        _need(pool_score_out, "pool_score_out", (torch.float32,), (B, pool_k))
+    if own_out is not None:
+        _need(own_out, "own_out", (torch.int32,), (B, k))
+    n_re = 0
+    if q_re is not None:
+        n_re = q_re.shape[0]
+        _need(q_re, "q_re", _BF16, (n_re, B, 128))
+        _need(re_out, "re_out", (torch.int32,), (n_re, B, k))
+        if re_score_out is not None:
+            _need(re_score_out, "re_score_out", (torch.float32,), (n_re, B, k))
+    _need(workspace, "workspace", _U8)
+    lib = load_library()
+    _check(lib.csa2_select_chain(_ptr(q_full), _ptr(idx_codes), _ptr(idx_scale), _ptr(seq_base),
+                                 _ptr(n_valid), B, n_cols, pool_k, _ptr(pool_out),
+                                 _ptr(pool_score_out), k, _ptr(own_out), _ptr(q_re), n_re,
+                                 _ptr(re_out), _ptr(re_score_out), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
 
 
 def csa2_sparse_attn_decode(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, out, workspace,

@@ -105,6 +105,39 @@ int csa2_index_topk(const uint16_t* q_idx, const uint8_t* idx_codes, const float
                                     static_cast<hipStream_t>(stream)));
 }
 
+size_t csa2_select_chain_workspace_size(int32_t batch, int32_t n_cols, int32_t pool_k) {
+  if (batch < 1 || n_cols < 1 || n_cols > kTopkMaxCols || pool_k < 1 || pool_k > CSA2_MAX_K)
+    return 0;
+  return select_chain_ws_bytes(batch, n_cols, pool_k);
+}
+
+int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const float* idx_scale,
+                      const int64_t* seq_base, const int32_t* n_valid, int32_t batch,
+                      int32_t n_cols, int32_t pool_k, int32_t* pool_out, float* pool_score_out,
+                      int32_t k, int32_t* own_out, const uint16_t* q_re, int32_t n_re,
+                      int32_t* re_out, float* re_score_out, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (!q_full || !idx_codes || !idx_scale || !seq_base || !n_valid || !pool_out)
+    return CSA2_ERR_INVALID_ARG;
+  if (batch < 1 || n_cols < 1 || pool_k < 1 || pool_k > CSA2_MAX_K || k < 1 || k > CSA2_MAX_K)
+    return CSA2_ERR_INVALID_ARG;
+  if (n_re < 0 || n_re > CSA2_MAX_REINDEX || (n_re > 0 && (!q_re || !re_out)))
+    return CSA2_ERR_INVALID_ARG;
+  if (n_cols > kTopkMaxCols) return CSA2_ERR_UNSUPPORTED;
+  if (!aligned(q_full, 16) || !aligned(idx_codes, 16) || !aligned(idx_scale, 4) ||
+      !aligned(seq_base, 8) || !aligned(n_valid, 4) || !aligned(pool_out, 4) ||
+      (pool_score_out && !aligned(pool_score_out, 4)) || (own_out && !aligned(own_out, 4)) ||
+      (q_re && !aligned(q_re, 16)) || (re_out && !aligned(re_out, 4)) ||
+      (re_score_out && !aligned(re_score_out, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  if (!workspace || ws_bytes < select_chain_ws_bytes(batch, n_cols, pool_k)) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_select_chain(q_full, idx_codes, idx_scale, seq_base, n_valid, batch,
+                                      n_cols, pool_k, pool_out, pool_score_out, k, own_out, q_re,
+                                      n_re > 0 ? n_re : 0, re_out, re_score_out, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 size_t csa2_attn_workspace_size(int32_t batch, int32_t k) {
   if (batch < 1 || k < 0) return 0;
   return attn_ws_bytes(batch, k);

@@ -29,27 +29,25 @@ struct TopkWs {
   int n_chunks;
 };
 
-// ---- fused scan + top-k workspace ----
+// ---- fused scan + top-k (index_topk.hip) ----
 constexpr int kHist3Bins = 512;       // level-3 digit: key bits 8..0
-constexpr int kFuseMaxWg = 256;       // workgroups per row of the fused kernel (one per CU)
-constexpr int kTiedPerWg = 4;         // tied keys a workgroup publishes before the slow path
+constexpr int kFuseMaxWg = 256;       // workgroups per row (one per CU at most)
+constexpr int kPubSlots = 2048;       // published composites per row and selection
+constexpr int kMaxSel = 6;            // selections per row: scan, own top-k, 4 Reindex
+constexpr int kMaxReindex = kMaxSel - 2;
 constexpr int kSyncStride = 32;       // u32 per row of barrier counters (one 128-byte line)
-
-struct FuseWs {
-  uint32_t* status;  // [1] sticky: nonzero once a row barrier gave up waiting
-  uint32_t* hist1;   // [batch][4096] level-1 histogram, returned to zero by each call
-  uint32_t* hist2;   // [batch][2048] level-2 histogram, likewise
-  uint32_t* hist3;   // [batch][512]  level-3 histogram (massive ties only), likewise
-  uint32_t* sync;    // [batch][kSyncStride]: [0] barrier arrivals, [1] departures
-  uint32_t* wgcnt;   // [batch][kFuseMaxWg] per-workgroup counts (two u16 halves)
-  unsigned long long* tied;  // [batch][kFuseMaxWg][kTiedPerWg] tied composites
-};
 
 size_t index_topk_ws_bytes(int batch, int n_cols);
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
                              const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
                              int batch, int n_cols, int k, int32_t* idx_out, float* score_out,
                              void* ws, hipStream_t stream);
+size_t select_chain_ws_bytes(int batch, int n_cols, int pool_k);
+hipError_t launch_select_chain(const uint16_t* q_full, const uint8_t* codes, const float* scale,
+                               const int64_t* seq_base, const int32_t* n_valid, int batch,
+                               int n_cols, int pool_k, int32_t* pool_out, float* pool_score_out,
+                               int k, int32_t* own_out, const uint16_t* q_re, int n_re,
+                               int32_t* re_out, float* re_score_out, void* ws, hipStream_t stream);
 
 int topk_chunk_iters(int n_cols);
 int topk_n_chunks(int n_cols);

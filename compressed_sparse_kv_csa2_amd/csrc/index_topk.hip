@@ -1,31 +1,40 @@
 // a1 + a2 (and a3 + a2): score the indexer keys and select the top-k in one launch,
-// without writing the scores to memory.
+// without writing the scores to memory; optionally followed, in the same launch, by the
+// selections a decoder layer chain makes inside that pool: the Full layer's own top-k by
+// its scores, and the top-k of Reindex layers that re-score the pool with their own
+// indexer queries ("从V4到V4.1 Flash：架构的激进进化", decoder section: the first layer's
+// full scan yields a pool of about 16K positions that later layers search; "DeepSeek-V4.1
+// 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash", commentary on the four layer modes).
 //
-// Same result as k_index_score followed by the top-k of topk.hip: the k largest scores of
-// a row, ties to the lower column, written in ascending column order as entry ids
-// (cand[c] or c), -1 padded ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash",
-// commentary on the four layer modes; "从V4到V4.1 Flash：架构的激进进化", decoder section on
-// the pool of about 16K positions that later layers search).
+// Every selection returns what csa2_topk returns for the same scores: the k largest of a
+// row, ties to the lower column, written in ascending column order as entry ids, -1
+// padded.  Inside the pool, "column" means the pool position, which ascends with the
+// entry id, so ties again go to the lowest entry.
 //
 // Every 1,024-thread workgroup scores up to 16,384 columns of one row with the stream of
 // scan_device.h (16 waves: as many loads in flight per CU as the stand-alone scan) and
-// keeps their order-preserving u32 keys in LDS (key 0 = not selectable).  The row's
-// workgroups (64 for a 2^20-column row) then find the exact k-th composite
-// (key << 32 | ~column, unique per column) digit by digit, meeting at row barriers:
-//   1. level 1, key bits 31..20: each workgroup's LDS histogram is added to the row's;
-//   2. level 2, bits 19..9, over the keys in the level-1 bin b1;
-//   3. each workgroup publishes how many of its keys lie above the level-2 bin (b1, b2)
-//      and the composites of its keys inside it (a handful per row).  Every workgroup then
-//      ranks those few composites itself: that fixes the k-th composite T, which of the
-//      row's tied keys are taken, and every workgroup's output offset.
-// Only when some workgroup holds more than 4 keys of the level-2 bin (massive ties) do
-// the workgroups take two more barriers: a level-3 histogram (bits 8..0) fixes the
-// threshold key, then (#keys above it, #keys equal to it) of every workgroup fix each
-// workgroup's share of the equal keys (the lowest columns win) and its offset.
-// Each workgroup then compacts its selected columns in column order with wave ballots.
-// The histograms are returned to zero by workgroup 0 of the row once every workgroup has
-// read them, and the last workgroup to leave resets the row's barrier counters, so the
-// workspace is ready for the next call without a separate clearing launch.
+// keeps their order-preserving u32 keys in LDS (key 0 = not selectable).  A selection
+// over keys held by the row's workgroups (64 for a 2^20-column row) finds the exact k-th
+// composite (key << 32 | ~position, unique) digit by digit, meeting at row barriers:
+//   1. level 1, key bits 31..20: each workgroup's LDS histogram is added to the row's.
+//      If the bin b1 of the k-th key holds at most 1,024 keys, go to 3 with that bin;
+//   2. level 2, bits 19..9, over the keys in b1: the bin (b1, b2);
+//   3. each workgroup publishes how many of its keys lie above the bin and the composites
+//      of its keys inside it.  Every workgroup ranks the published composites itself:
+//      that fixes the k-th composite T, which tied keys are taken, and each workgroup's
+//      output offset (the sum of the selections of the workgroups before it).
+// When a workgroup has more keys in the bin than it may publish (massive ties), the row
+// goes one level deeper instead: a level-3 histogram (bits 8..0) fixes the threshold key,
+// then (#keys above it, #keys equal to it) of every workgroup fix each workgroup's share
+// of the equal keys (the lowest positions win) and its offset.
+// Each workgroup then writes its selected entries in position order with wave ballots.
+// For the chained selections each workgroup keeps the pool entries it selected (their
+// keys and columns, in LDS); the Full layer's own top-k reuses those keys, a Reindex layer
+// first gathers and re-scores those entries with its query (the same arithmetic as the
+// scan, so the same scores as csa2_index_score).  Workgroup 0 of the row returns every
+// histogram to zero once all workgroups have read it, and the last workgroup to leave
+// resets the row's barrier counters: the workspace is ready for the next call without a
+// clearing launch.
 //
 // Everything one workgroup tells another goes through agent-scope atomics: read-modify-
 // writes whose returned values are waited for before the workgroup arrives at the next
@@ -39,6 +48,10 @@
 // dispatches at once.  Each wait is bounded: after 2^20 polls (about a second) it gives
 // up and sets a sticky status word in the workspace, so every wave exits even when the
 // device is shared and that assumption fails (the call's result is then undefined).
+//
+// Workspace: [status: 256 B][barrier counters: batch x 32 u32, 256-aligned]
+// [batch x kMaxSel selection blocks of kSelBytes: h1 u32[4096] | h2 u32[2048] |
+//  h3 u32[512] | per-workgroup counts u32[256] | published composites u64[2048]].
 #include "csa2_internal.h"
 #include "scan_device.h"
 #include "select_device.h"
@@ -49,14 +62,26 @@ constexpr int kFuseThreads = 1024;                        // 16 waves
 constexpr int kFuseWaves = kFuseThreads / 64;
 constexpr int kFuseKeysPerThread = 16;
 constexpr int kFuseMaxCols = kFuseThreads * kFuseKeysPerThread;  // 16,384 keys in LDS
+constexpr int kPubMax = 1024;                             // published composites ranked in LDS
 constexpr uint32_t kSpinLimit = 1u << 20;
+
+constexpr size_t kSelH2 = kHist1Bins * 4;
+constexpr size_t kSelH3 = kSelH2 + kHist2Bins * 4;
+constexpr size_t kSelCnt = kSelH3 + kHist3Bins * 4;
+constexpr size_t kSelPub = kSelCnt + kFuseMaxWg * 4;
+constexpr size_t kSelBytes = kSelPub + kPubSlots * 8;
 
 static_assert(kFuseThreads * 4 == kHist1Bins, "level-1 bins: 4 per thread");
 static_assert(kFuseThreads * 2 == kHist2Bins, "level-2 bins: 2 per thread");
 static_assert(kHist3Bins == 8 * 64, "level-3 bins: 8 per lane of one wave");
-static_assert(kFuseMaxWg <= kFuseThreads, "offsets: one workgroup per thread");
+static_assert(kFuseMaxWg <= kFuseThreads, "per-workgroup counts: one per thread");
+static_assert(kPubSlots == 2 * kFuseThreads, "published slots: two per thread");
+static_assert(kSelBytes % 256 == 0, "selection blocks stay 256-byte aligned");
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
@@ -65,31 +90,70 @@ __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+template <typename T>
+__device__ __forceinline__ uint32_t xchg_agent(T* p, T v) {
+  return (uint32_t)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// Barrier of the workgroups of one row: returns once the row's arrival counter has reached
-// `target` (= barriers passed so far x workgroups per row).  `pending` combines the values
-// returned by this thread's atomics since the previous barrier: using it makes the thread
+// Barriers of the workgroups of one row.  sync(pending): `pending` combines the values
+// returned by this thread's atomics since the previous barrier; using it makes the thread
 // wait until they have been performed before its workgroup arrives.
-__device__ void row_sync(uint32_t* arrivals, uint32_t target, uint32_t* status,
-                         uint32_t pending) {
-  asm volatile("" ::"v"(pending));
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    add_agent(arrivals, 1u);
-    uint32_t spins = 0;
-    while (ld_agent(arrivals) < target) {
-      if (++spins == kSpinLimit) {
-        st_agent(status, 1u);
-        break;
+struct RowSync {
+  uint32_t* arrivals;
+  uint32_t* status;
+  uint32_t nw;     // workgroups in the row
+  uint32_t done;   // barriers passed (the same in every workgroup of the row)
+
+  __device__ void sync(uint32_t pending) {
+    asm volatile("" ::"v"(pending));
+    __syncthreads();
+    ++done;
+    if (threadIdx.x == 0) {
+      const uint32_t target = done * nw;
+      add_agent(arrivals, 1u);
+      uint32_t spins = 0;
+      while (ld_agent(arrivals) < target) {
+        if (++spins == kSpinLimit) {
+          st_agent(status, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      __builtin_amdgcn_s_sleep(2);
     }
+    __syncthreads();
   }
-  __syncthreads();
+};
+
+// LDS scratch of a selection.
+struct SelLds {
+  uint32_t* h;                 // [4096] histograms
+  uint32_t* cnt;               // [16 x 16] per-(iteration, wave) counts
+  unsigned long long* pub;     // [2 x kPubMax] staged / gathered composites
+  uint32_t* selt;              // [kFuseMaxWg] per-workgroup counts
+  uint32_t* scan;              // [32] block-scan scratch
+  uint32_t* res;               // [4]
+  uint32_t* misc;              // [4]
+  unsigned long long* T;       // [1]
+};
+
+// One selection's global arrays for this row.
+struct SelWs {
+  uint32_t* h1;
+  uint32_t* h2;
+  uint32_t* h3;
+  uint32_t* cnt;               // [kFuseMaxWg]
+  unsigned long long* pub;     // [kPubSlots]: workgroup w owns [w * cap, (w + 1) * cap)
+};
+
+__device__ __forceinline__ SelWs sel_ws(char* sel_base, int row, int sel) {
+  char* p = sel_base + ((size_t)row * kMaxSel + sel) * kSelBytes;
+  return SelWs{reinterpret_cast<uint32_t*>(p), reinterpret_cast<uint32_t*>(p + kSelH2),
+               reinterpret_cast<uint32_t*>(p + kSelH3), reinterpret_cast<uint32_t*>(p + kSelCnt),
+               reinterpret_cast<unsigned long long*>(p + kSelPub)};
 }
 
 // Adds the non-empty bins of an LDS histogram of N * 1,024 bins (N = 1: 512 bins) to a
-// global one; returns the combined values the atomics returned (for row_sync).  The
+// global one; returns the combined values the atomics returned (for RowSync::sync).  The
 // atomics are issued back to back and their returns only combined at the end.
 template <int N>
 __device__ __forceinline__ uint32_t flush_hist(const uint32_t* s_h, int nbins, uint32_t* g) {
@@ -107,9 +171,25 @@ __device__ __forceinline__ uint32_t flush_hist(const uint32_t* s_h, int nbins, u
   return pending;
 }
 
+// LDS histogram, over `nbins` bins of (key >> shift) & (nbins - 1), of the non-zero keys
+// with key >> (shift + dbits) == pre (dbits = log2 nbins; pre = 0 with shift + dbits = 32
+// takes every key).  Whole workgroup; ends with a barrier.
+__device__ __forceinline__ void local_hist(const uint32_t* keys, int n_local, uint32_t pre,
+                                           int shift, int nbins, int dbits, uint32_t* s_h) {
+  for (int i = threadIdx.x; i < nbins; i += kFuseThreads) s_h[i] = 0u;
+  __syncthreads();
+  const int top = shift + dbits;
+  for (int i = threadIdx.x; i < n_local; i += kFuseThreads) {
+    const uint32_t key = keys[i];
+    if (key != 0u && (top >= 32 || (key >> top) == pre))
+      atomicAdd(&s_h[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+  }
+  __syncthreads();
+}
+
 // Searches an LDS histogram h[0..PER * 1024) for the bin holding the k-th largest element,
-// from the top.  Returns the total count; when 1 <= k <= total, out[0] = the bin and out[1] = the
-// elements in higher bins.  Whole workgroup; ends with a barrier.
+// from the top.  Returns the total count; when 1 <= k <= total, out[0] = the bin and
+// out[1] = the elements in higher bins.  Whole workgroup; ends with a barrier.
 template <int PER>
 __device__ uint32_t hist_select(const uint32_t* h, uint32_t k, uint32_t* s_scan, uint32_t* out) {
   const int top = PER * (kFuseThreads - (int)threadIdx.x);
@@ -138,42 +218,362 @@ __device__ uint32_t hist_select(const uint32_t* h, uint32_t k, uint32_t* s_scan,
   return total;
 }
 
+// Publishes this workgroup's count of keys above the bin (key >> shift > pre; every
+// non-zero key when `all`) and the composites of its keys inside it (key >> shift == pre,
+// at most `cap` of them; the count says how many there were).  Returns the combined
+// values of the atomics (for RowSync::sync).
+__device__ __forceinline__ uint32_t publish(const uint32_t* keys, int n_local, uint32_t pos0, uint32_t pre,
+                            int shift, bool all, int cap, uint32_t* cnt_slot,
+                            unsigned long long* pub, const SelLds& L) {
+  const int tid = threadIdx.x;
+  if (tid == 0) L.misc[0] = 0u;
+  __syncthreads();
+  uint32_t n_above = 0;
+  for (int i = tid; i < n_local; i += kFuseThreads) {
+    const uint32_t key = keys[i];
+    if (key == 0u) continue;
+    const uint32_t d = key >> shift;
+    if (all || d > pre) {
+      ++n_above;
+    } else if (d == pre) {
+      const uint32_t slot = atomicAdd(&L.misc[0], 1u);
+      if (slot < (uint32_t)cap) L.pub[slot] = composite(key, pos0 + (uint32_t)i);
+    }
+  }
+  uint32_t above;
+  block_exclusive_scan(n_above, L.scan, &above);  // barrier: L.misc[0] and L.pub complete
+  const uint32_t n_pub = L.misc[0];
+  uint32_t pending = 0;
+  if (tid < (int)min(n_pub, (uint32_t)cap)) pending |= xchg_agent(&pub[tid], L.pub[tid]);
+  if (tid == kFuseThreads - 1) pending |= xchg_agent(cnt_slot, (above << 16) | min(n_pub, 0xffffu));
+  return pending;
+}
+
+struct SelResult {
+  uint32_t sel;     // entries this workgroup selected
+  uint32_t offset;  // output position of its first one
+};
+
+// One selection over keys[0..n_local) of every workgroup of the row (LDS; local index i =
+// j * 1024 + thread, at position pos0 + i; key 0 = not selectable).  h1_ready: L.h already
+// holds this workgroup's level-1 histogram.  Writes orow[0..k) (id_of(i), ascending
+// positions, -1 padded) and srow (scores, -inf padded) if given; calls on_sel(rank, i) for
+// the workgroup's selected entries in position order.  Whole workgroup, every workgroup of
+// the row; ends with a barrier.
+template <typename IdOf, typename OnSel>
+__device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_local, uint32_t pos0, int k,
+                                bool h1_ready, const SelWs& g, RowSync& rs, const SelLds& L,
+                                int wg, int nwg, int32_t* orow, float* srow, IdOf id_of,
+                                OnSel on_sel) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int iters = (n_local + kFuseThreads - 1) / kFuseThreads;
+  const int cap = min(kPubSlots / nwg, kPubMax);
+  uint32_t pending = 0;
+
+  // ---- level 1: every workgroup's histogram into the row's, then the bin of the k-th key
+  if (!h1_ready) local_hist(keys, n_local, 0u, 20, kHist1Bins, 12, L.h);
+  pending |= flush_hist<4>(L.h, kHist1Bins, g.h1);
+  rs.sync(pending);
+  pending = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) L.h[tid + i * kFuseThreads] = ld_agent(&g.h1[tid + i * kFuseThreads]);
+  __syncthreads();
+  const uint32_t total = hist_select<4>(L.h, (uint32_t)k, L.scan, L.res);
+  const uint32_t k_eff = min((uint32_t)k, total);
+  const bool all = k_eff == total;  // the same in every workgroup of the row
+  uint32_t pre = 0, need = 0;       // need: keys still to take at or below the bin
+  int shift = 20;
+  bool pub_now = true;  // publish at level 1 (always when every key is taken)
+  if (!all) {
+    pre = L.res[0];
+    need = k_eff - L.res[1];
+    pub_now = L.h[pre] <= (uint32_t)kPubMax;
+  }
+  __syncthreads();  // L.h and L.res are read before they are rewritten
+  if (pub_now) {
+    pending |= publish(keys, n_local, pos0, pre, shift, all, cap, g.cnt + wg, g.pub + wg * cap, L);
+  } else {
+    local_hist(keys, n_local, pre, 9, kHist2Bins, 11, L.h);
+    pending |= flush_hist<2>(L.h, kHist2Bins, g.h2);
+  }
+  rs.sync(pending);
+  pending = 0;
+  if (wg == 0)
+    for (int i = tid; i < kHist1Bins; i += kFuseThreads) st_agent(&g.h1[i], 0u);
+
+  // ---- level 2 (when b1 held too many keys): the bin (b1, b2), then publish
+  if (!pub_now) {
+    L.h[tid] = ld_agent(&g.h2[tid]);
+    L.h[tid + kFuseThreads] = ld_agent(&g.h2[tid + kFuseThreads]);
+    __syncthreads();
+    hist_select<2>(L.h, need, L.scan, L.res);
+    pre = (pre << 11) | L.res[0];
+    need -= L.res[1];
+    shift = 9;
+    pending |= publish(keys, n_local, pos0, pre, shift, false, cap, g.cnt + wg, g.pub + wg * cap, L);
+    rs.sync(pending);
+    pending = 0;
+    if (wg == 0)
+      for (int i = tid; i < kHist2Bins; i += kFuseThreads) st_agent(&g.h2[i], 0u);
+  }
+
+  // ---- the published composites: every workgroup ranks them itself
+  const uint32_t cv = tid < nwg ? ld_agent(&g.cnt[tid]) : 0u;
+  const int s0 = tid, s1 = tid + kFuseThreads;
+  const int v0 = s0 / cap, v1 = s1 / cap;
+  const unsigned long long t0 = v0 < nwg ? ld_agent(&g.pub[s0]) : 0ull;
+  const unsigned long long t1 = v1 < nwg ? ld_agent(&g.pub[s1]) : 0ull;
+  const uint32_t npub_v = cv & 0xffffu;
+  if (tid < nwg) L.selt[tid] = npub_v;
+  uint32_t pub_total;
+  block_exclusive_scan(npub_v, L.scan, &pub_total);  // barrier: L.selt complete
+  const bool overflow =
+      (__syncthreads_or(tid < nwg && npub_v > (uint32_t)cap) != 0) || pub_total > (uint32_t)kPubMax;
+
+  // selected: key > tkey, or key == tkey at a position <= cut (when has_cut)
+  uint32_t tkey = 0u, cut = 0u;
+  bool has_cut = false;
+  uint32_t offset;
+  if (!overflow) {
+    const bool ok0 = v0 < nwg && (uint32_t)(s0 - v0 * cap) < L.selt[v0];
+    const bool ok1 = v1 < nwg && (uint32_t)(s1 - v1 * cap) < L.selt[v1];
+    uint32_t nt;
+    const uint32_t p = block_exclusive_scan((ok0 ? 1u : 0u) + (ok1 ? 1u : 0u), L.scan, &nt);
+    if (ok0) L.pub[p] = t0;
+    if (ok1) L.pub[p + (ok0 ? 1u : 0u)] = t1;
+    if (tid < nwg) L.selt[tid] = 0u;
+    if (tid == 0) *L.T = ~0ull;
+    __syncthreads();
+    if (!all && nt <= 64) {
+      // few composites: wave 0 ranks them directly (they are unique: exactly one has rank
+      // need - 1)
+      if (wave == 0) {
+        const unsigned long long c = (uint32_t)lane < nt ? L.pub[lane] : 0ull;
+        const uint32_t chi = (uint32_t)(c >> 32), clo = (uint32_t)c;
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < nt; ++j) {
+          const uint32_t ohi = __builtin_amdgcn_readlane(chi, j);
+          const uint32_t olo = __builtin_amdgcn_readlane(clo, j);
+          r += (ohi > chi || (ohi == chi && olo > clo)) ? 1u : 0u;
+        }
+        if ((uint32_t)lane < nt && r == need - 1u) *L.T = c;
+      }
+    } else if (!all) {
+      // the need-th largest published composite: one 256-bin radix pass over the 8 key
+      // bits below the bin, then the few composites left in the chosen digit are ranked
+      // directly (they are unique: exactly one has rank need - 1 among them)
+      const int dsh = shift - 8;
+      if (tid < 256) L.h[tid] = 0u;
+      if (tid == 0) L.misc[0] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < nt; i += kFuseThreads)
+        atomicAdd(&L.h[(uint32_t)(L.pub[i] >> (32 + dsh)) & 255u], 1u);
+      __syncthreads();
+      if (wave == 0) find_threshold_bin(L.h, 256, need, L.res);
+      __syncthreads();
+      const uint32_t da = L.res[0], need_b = need - L.res[1];
+      for (uint32_t i = tid; i < nt; i += kFuseThreads) {
+        const unsigned long long c = L.pub[i];
+        if (((uint32_t)(c >> (32 + dsh)) & 255u) == da) L.pub[kPubMax + atomicAdd(&L.misc[0], 1u)] = c;
+      }
+      __syncthreads();
+      const uint32_t nb = L.misc[0];
+      const unsigned long long* cb = L.pub + kPubMax;
+      for (uint32_t i = tid; i < nb; i += kFuseThreads) {
+        const unsigned long long c = cb[i];
+        uint32_t r = 0;
+        uint32_t j = 0;
+        for (; j + 8 <= nb; j += 8) {  // eight loads in flight per step
+          unsigned long long x[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) x[u] = cb[j + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) r += x[u] > c ? 1u : 0u;
+        }
+        for (; j < nb; ++j) r += cb[j] > c ? 1u : 0u;
+        if (r == need_b - 1u) *L.T = c;
+      }
+    }
+    __syncthreads();
+    if (!all) {
+      const unsigned long long T = *L.T;
+      tkey = (uint32_t)(T >> 32);
+      cut = ~(uint32_t)T;
+      has_cut = true;
+      if (ok0 && t0 >= T) atomicAdd(&L.selt[v0], 1u);
+      if (ok1 && t1 >= T) atomicAdd(&L.selt[v1], 1u);
+    }
+    __syncthreads();
+    const uint32_t sel_v = tid < nwg ? (cv >> 16) + L.selt[tid] : 0u;
+    block_exclusive_scan(tid < wg ? sel_v : 0u, L.scan, &offset);
+  } else {
+    // massive ties: the threshold key from a level-3 histogram (after level 2, if the
+    // keys were published at level 1), then each workgroup's share of the equal keys
+    if (shift == 20) {
+      local_hist(keys, n_local, pre, 9, kHist2Bins, 11, L.h);
+      pending |= flush_hist<2>(L.h, kHist2Bins, g.h2);
+      rs.sync(pending);
+      pending = 0;
+      L.h[tid] = ld_agent(&g.h2[tid]);
+      L.h[tid + kFuseThreads] = ld_agent(&g.h2[tid + kFuseThreads]);
+      __syncthreads();
+      hist_select<2>(L.h, need, L.scan, L.res);
+      pre = (pre << 11) | L.res[0];
+      need -= L.res[1];
+    }
+    local_hist(keys, n_local, pre, 0, kHist3Bins, 9, L.h);
+    pending |= flush_hist<1>(L.h, kHist3Bins, g.h3);
+    rs.sync(pending);
+    pending = 0;
+    if (wg == 0)
+      for (int i = tid; i < kHist2Bins; i += kFuseThreads) st_agent(&g.h2[i], 0u);
+    if (tid < kHist3Bins) L.h[tid] = ld_agent(&g.h3[tid]);
+    __syncthreads();
+    if (wave == 0) find_threshold_bin(L.h, kHist3Bins, need, L.res);
+    __syncthreads();
+    tkey = (pre << 9) | L.res[0];
+    const uint32_t need_eq = need - L.res[1];  // keys equal to tkey still to take, >= 1
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int i = tid; i < n_local; i += kFuseThreads) {
+      const uint32_t key = keys[i];
+      n_gt += key > tkey ? 1u : 0u;
+      n_eq += key == tkey ? 1u : 0u;
+    }
+    uint32_t packed;  // both counts are <= 16,384
+    block_exclusive_scan((n_gt << 16) | n_eq, L.scan, &packed);
+    if (tid == 0) pending |= xchg_agent(g.cnt + wg, packed);
+    rs.sync(pending);
+    pending = 0;
+    if (wg == 0 && tid < kHist3Bins) st_agent(&g.h3[tid], 0u);
+    // the equal keys go to the lowest positions: workgroup by workgroup, then locally
+    const uint32_t cw = tid < nwg ? ld_agent(&g.cnt[tid]) : 0u;
+    const uint32_t eq_v = cw & 0xffffu;
+    uint32_t unused;
+    const uint32_t eq_before = block_exclusive_scan(eq_v, L.scan, &unused);
+    const uint32_t take_v = min(eq_v, need_eq > eq_before ? need_eq - eq_before : 0u);
+    if (tid == wg) L.misc[2] = take_v;
+    block_exclusive_scan(tid < wg ? (cw >> 16) + take_v : 0u, L.scan, &offset);  // barrier
+    const uint32_t take = L.misc[2];
+    if (take > 0u) {  // position of this workgroup's take-th equal key
+      for (int j = 0; j < iters; ++j) {
+        const int i = j * kFuseThreads + tid;
+        const unsigned long long m = __ballot(i < n_local && keys[i] == tkey);
+        if (lane == 0) L.cnt[j * kFuseWaves + wave] = (uint32_t)__popcll(m);
+      }
+      __syncthreads();
+      if (wave == 0) scan_counts_wave0_n<4>(L.cnt, iters * kFuseWaves);
+      __syncthreads();
+      for (int j = 0; j < iters; ++j) {
+        const int i = j * kFuseThreads + tid;
+        const bool eq = i < n_local && keys[i] == tkey;
+        const unsigned long long m = __ballot(eq);
+        if (eq && L.cnt[j * kFuseWaves + wave] + lanes_below(m) == take - 1u)
+          L.misc[3] = pos0 + (uint32_t)i;
+      }
+      __syncthreads();
+      cut = L.misc[3];
+      has_cut = true;
+    }
+  }
+
+  // ---- the selected entries in position order
+  uint32_t selbits = 0;
+  for (int j = 0; j < iters; ++j) {
+    const int i = j * kFuseThreads + tid;
+    const uint32_t key = i < n_local ? keys[i] : 0u;
+    const bool take =
+        key != 0u && (key > tkey || (key == tkey && has_cut && pos0 + (uint32_t)i <= cut));
+    selbits |= (take ? 1u : 0u) << j;
+    const unsigned long long m = __ballot(take);
+    if (lane == 0) L.cnt[j * kFuseWaves + wave] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t n = scan_counts_wave0_n<4>(L.cnt, iters * kFuseWaves);
+    if (lane == 0) L.misc[1] = n;
+  }
+  __syncthreads();
+  for (int j = 0; j < iters; ++j) {
+    const bool take = (selbits >> j) & 1u;
+    const unsigned long long m = __ballot(take);
+    if (take) {
+      const int i = j * kFuseThreads + tid;
+      const uint32_t rank = L.cnt[j * kFuseWaves + wave] + lanes_below(m);
+      const uint32_t pos = offset + rank;
+      if (pos < (uint32_t)k) {
+        orow[pos] = id_of(i);
+        if (srow) srow[pos] = key_score(keys[i]);
+      }
+      on_sel(rank, i);
+    }
+  }
+  for (int p = (int)k_eff + wg * kFuseThreads + tid; p < k; p += nwg * kFuseThreads) {
+    orow[p] = -1;
+    if (srow) srow[p] = -__builtin_inff();
+  }
+  const SelResult r{L.misc[1], offset};
+  __syncthreads();
+  return r;
+}
+
+struct ChainArgs {
+  const uint16_t* q_idx;     // [batch][128] query of the scan
+  const uint8_t* codes;
+  const float* scale;
+  const int64_t* seq_base;
+  const int32_t* n_valid;
+  const int32_t* cand;       // candidate map of the scan (CAND)
+  int n_cols, cols_per_wg, row0;
+  int k;                     // the scan's selection (the pool)
+  int32_t* idx_out;          // [batch][k]
+  float* score_out;          // [batch][k] or null
+  int own_k;                 // top-own_k of the pool by the scan's scores (0: none)
+  int32_t* own_out;          // [batch][own_k]
+  int n_re;                  // Reindex layers re-scoring the pool (0..kMaxReindex)
+  int re_k;
+  const uint16_t* q_re;      // [n_re][batch][128]
+  int32_t* re_out;           // [n_re][batch][re_k]
+  float* re_score_out;       // [n_re][batch][re_k] or null
+  int batch;
+  uint32_t* status;
+  uint32_t* sync;
+  char* sel_base;
+};
+
 template <bool CAND>
-__global__ __launch_bounds__(kFuseThreads) void k_index_topk(
-    const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
-    const float* __restrict__ scale, const int64_t* __restrict__ seq_base,
-    const int32_t* __restrict__ n_valid, const int32_t* __restrict__ cand, int n_cols,
-    int cols_per_wg, int row0, int k, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, FuseWs ws) {
-  __shared__ uint32_t s_h[kHist1Bins];
+__global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
   __shared__ uint32_t s_key[kFuseMaxCols];
+  __shared__ uint32_t s_h[kHist1Bins];
+  __shared__ uint16_t s_plist[CAND ? 1 : kFuseMaxCols];  // columns of this workgroup's pool
+  __shared__ unsigned long long s_pub[2 * kPubMax];
   __shared__ uint32_t s_cnt[kFuseKeysPerThread * kFuseWaves];
-  __shared__ unsigned long long s_tied[kFuseMaxWg * kTiedPerWg];
   __shared__ uint32_t s_selt[kFuseMaxWg];
   __shared__ uint32_t s_scan[32];
   __shared__ uint32_t s_res[4];
   __shared__ uint32_t s_misc[4];
   __shared__ unsigned long long s_T;
-  const int b = row0 + (int)blockIdx.y, wg = blockIdx.x, nwg = gridDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nv = min(n_valid[b], n_cols);
-  const int c0 = wg * cols_per_wg, c1 = min(c0 + cols_per_wg, n_cols);
-  const int iters = cols_per_wg / kFuseThreads;  // key i = j * 1024 + tid, j < iters
-  const int32_t* cand_row = CAND ? cand + (size_t)b * n_cols : nullptr;
-  uint32_t* arrivals = ws.sync + (size_t)b * kSyncStride;
-  uint32_t* g1 = ws.hist1 + (size_t)b * kHist1Bins;
-  uint32_t* g2 = ws.hist2 + (size_t)b * kHist2Bins;
-  uint32_t* g3 = ws.hist3 + (size_t)b * kHist3Bins;
-  uint32_t* cnt = ws.wgcnt + (size_t)b * kFuseMaxWg;
-  unsigned long long* tied = ws.tied + (size_t)b * kFuseMaxWg * kTiedPerWg;
-  const uint32_t nw = (uint32_t)nwg;
-  uint32_t pending = 0;
+  const int b = a.row0 + (int)blockIdx.y, wg = blockIdx.x, nwg = gridDim.x;
+  const int tid = threadIdx.x;
+  const int nv = min(a.n_valid[b], a.n_cols);
+  const int c0 = wg * a.cols_per_wg, c1 = min(c0 + a.cols_per_wg, a.n_cols);
+  const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
+  const int64_t base = a.seq_base[b];
+  RowSync rs{a.sync + (size_t)b * kSyncStride, a.status, (uint32_t)nwg, 0u};
+  SelLds L;
+  L.h = s_h;
+  L.cnt = s_cnt;
+  L.pub = s_pub;
+  L.selt = s_selt;
+  L.scan = s_scan;
+  L.res = s_res;
+  L.misc = s_misc;
+  L.T = &s_T;
 
-  // ---- score the columns [c0, c1): keys into LDS, level-1 histogram into the row's
+  // ---- score the columns [c0, c1): keys into LDS, level-1 histogram in LDS
   for (int i = tid; i < kFuseMaxCols; i += kFuseThreads) s_key[i] = 0u;
   if (nv > 0) {
     scan_columns<CAND, kFuseThreads>(
-        q_idx + (size_t)b * kDIdx, codes, scale, cand_row, seq_base[b], nv, c0, c1,
+        a.q_idx + (size_t)b * kDIdx, a.codes, a.scale, cand_row, base, nv, c0, c1,
         [&]() {
           for (int i = tid; i < kHist1Bins; i += kFuseThreads) s_h[i] = 0u;
         },
@@ -183,218 +583,122 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(
           if (key != 0u) atomicAdd(&s_h[key >> 20], 1u);
         });
     __syncthreads();
-    pending |= flush_hist<4>(s_h, kHist1Bins, g1);
   }
-  row_sync(arrivals, nw, ws.status, pending);
-  pending = 0;
 
-  // ---- level 1: the bin b1 of the k-th key (or every selectable column)
+  // ---- the selections: stage 0 over the scanned columns (the pool when chained), then
+  // the Full layer's own top-k and the Reindex layers inside this workgroup's pool entries
+  const bool chain = !CAND && (a.own_k > 0 || a.n_re > 0);
+  const int n_stages = chain ? 1 + (a.own_k > 0 ? 1 : 0) + a.n_re : 1;
+  const int lane = tid & 63, wave = tid >> 6, quarter = lane & 3, ent = lane >> 2;
+  int n_pool = 0;
+  uint32_t pool_off = 0;
+  for (int st = 0; st < n_stages; ++st) {
+    const int r = st - 1 - (a.own_k > 0 ? 1 : 0);  // Reindex layer of this stage, if >= 0
+    if (st == 1) {
+      // this workgroup's pool entries, in pool order: their scan keys to the front
+      uint32_t kk[kFuseKeysPerThread];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s_h[tid + i * kFuseThreads] = ld_agent(&g1[tid + i * kFuseThreads]);
-  __syncthreads();
-  const uint32_t total = hist_select<4>(s_h, (uint32_t)k, s_scan, s_res);
-  const uint32_t k_eff = min((uint32_t)k, total);
-  const bool all = k_eff == total;  // the same in every workgroup of the row
-  uint32_t b1 = 0, need = 0;        // need: keys still to take at or below the prefix
-  if (!all) {
-    b1 = s_res[0];
-    need = k_eff - s_res[1];
-    __syncthreads();
-    for (int i = tid; i < kHist2Bins; i += kFuseThreads) s_h[i] = 0u;
-    __syncthreads();
-    for (int j = 0; j < iters; ++j) {
-      const uint32_t key = s_key[j * kFuseThreads + tid];
-      if (key != 0u && (key >> 20) == b1) atomicAdd(&s_h[(key >> 9) & (kHist2Bins - 1)], 1u);
-    }
-    __syncthreads();
-    pending |= flush_hist<2>(s_h, kHist2Bins, g2);
-  }
-  row_sync(arrivals, 2u * nw, ws.status, pending);
-  pending = 0;
-
-  // ---- level 2: the bin (b1, b2); publish the keys above it and the composites inside it
-  if (wg == 0)
-    for (int i = tid; i < kHist1Bins; i += kFuseThreads) st_agent(&g1[i], 0u);
-  uint32_t pre = 0;  // key >> 9 of the level-2 bin
-  if (!all) {
-    s_h[tid] = ld_agent(&g2[tid]);
-    s_h[tid + kFuseThreads] = ld_agent(&g2[tid + kFuseThreads]);
-    __syncthreads();
-    hist_select<2>(s_h, need, s_scan, s_res);
-    pre = (b1 << 11) | s_res[0];
-    need -= s_res[1];
-  }
-  {
-    if (tid == 0) s_misc[0] = 0u;
-    __syncthreads();
-    uint32_t n_above = 0;
-    for (int j = 0; j < iters; ++j) {
-      const uint32_t key = s_key[j * kFuseThreads + tid];
-      if (key == 0u) continue;
-      if (all || (key >> 9) > pre) {
-        ++n_above;
-      } else if ((key >> 9) == pre) {  // staged in LDS, published below
-        const uint32_t slot = atomicAdd(&s_misc[0], 1u);
-        if (slot < (uint32_t)kTiedPerWg)
-          s_tied[slot] = composite(key, (uint32_t)(c0 + j * kFuseThreads + tid));
-      }
-    }
-    uint32_t above_total;
-    block_exclusive_scan(n_above, s_scan, &above_total);  // barrier: s_misc[0], s_tied ready
-    // one round trip: the tied composites and the counts leave together
-    const uint32_t n_tied = s_misc[0];
-    if (tid < (int)min(n_tied, (uint32_t)kTiedPerWg))
-      pending |= (uint32_t)__hip_atomic_exchange(&tied[wg * kTiedPerWg + tid], s_tied[tid],
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == kTiedPerWg)
-      pending |= __hip_atomic_exchange(&cnt[wg], (above_total << 16) | min(n_tied, 0xffffu),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  row_sync(arrivals, 3u * nw, ws.status, pending);
-  pending = 0;
-
-  // ---- the k-th composite T from the published tied keys; this workgroup's offset
-  if (wg == 0)
-    for (int i = tid; i < kHist2Bins; i += kFuseThreads) st_agent(&g2[i], 0u);
-  const uint32_t cv = tid < nwg ? ld_agent(&cnt[tid]) : 0u;
-  const unsigned long long tv =
-      tid < nwg * kTiedPerWg
-          ? __hip_atomic_load(&tied[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-          : 0ull;
-  const uint32_t n_tied_v = cv & 0xffffu;  // of workgroup v = tid
-  if (tid < nwg) s_selt[tid] = n_tied_v;
-  // massive ties: some workgroup could not publish all of its tied keys
-  const bool slow = __syncthreads_or(n_tied_v > (uint32_t)kTiedPerWg) != 0;
-  // selected: key > tkey, or key == tkey and column <= col_cut (-1: no equal key)
-  uint32_t tkey = 0u;
-  int col_cut = -1;
-  uint32_t offset;
-  if (!slow) {
-    const int v = tid / kTiedPerWg;
-    const bool valid = v < nwg && (uint32_t)(tid % kTiedPerWg) < s_selt[v];
-    uint32_t nt;
-    const uint32_t pos = block_exclusive_scan(valid ? 1u : 0u, s_scan, &nt);  // barrier
-    if (valid) s_tied[pos] = tv;
-    if (tid < nwg) s_selt[tid] = 0u;
-    if (tid == 0) s_T = ~0ull;
-    __syncthreads();
-    if (!all && valid) {
-      uint32_t r = 0;  // composites are unique: exactly one has rank need - 1
-      for (uint32_t i = 0; i < nt; ++i) r += s_tied[i] > tv ? 1u : 0u;
-      if (r == need - 1u) s_T = tv;
-    }
-    __syncthreads();
-    if (!all) {
-      const unsigned long long T = s_T;
-      tkey = (uint32_t)(T >> 32);
-      col_cut = (int)~(uint32_t)T;
-      if (valid && tv >= T) atomicAdd(&s_selt[v], 1u);
-    }
-    __syncthreads();
-    const uint32_t sel_v = tid < nwg ? (cv >> 16) + s_selt[tid] : 0u;
-    block_exclusive_scan(tid < wg ? sel_v : 0u, s_scan, &offset);
-  } else {
-    // level 3 over the keys of the level-2 bin: the threshold key
-    for (int i = tid; i < kHist3Bins; i += kFuseThreads) s_h[i] = 0u;
-    __syncthreads();
-    for (int j = 0; j < iters; ++j) {
-      const uint32_t key = s_key[j * kFuseThreads + tid];
-      if (key != 0u && (key >> 9) == pre) atomicAdd(&s_h[key & (kHist3Bins - 1)], 1u);
-    }
-    __syncthreads();
-    pending |= flush_hist<1>(s_h, kHist3Bins, g3);
-    row_sync(arrivals, 4u * nw, ws.status, pending);
-    pending = 0;
-    if (tid < kHist3Bins) s_h[tid] = ld_agent(&g3[tid]);
-    __syncthreads();
-    if (wave == 0) find_threshold_bin(s_h, kHist3Bins, need, s_res);
-    __syncthreads();
-    tkey = (pre << 9) | s_res[0];
-    const uint32_t need_eq = need - s_res[1];  // keys equal to tkey still to take, >= 1
-    uint32_t n_gt = 0, n_eq = 0;
-    for (int j = 0; j < iters; ++j) {
-      const uint32_t key = s_key[j * kFuseThreads + tid];
-      n_gt += key > tkey ? 1u : 0u;
-      n_eq += key == tkey ? 1u : 0u;
-    }
-    uint32_t packed;  // both counts are <= 16,384
-    block_exclusive_scan((n_gt << 16) | n_eq, s_scan, &packed);
-    if (tid == 0)
-      pending |= __hip_atomic_exchange(&cnt[wg], packed, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    row_sync(arrivals, 5u * nw, ws.status, pending);
-    pending = 0;
-    if (wg == 0 && tid < kHist3Bins) st_agent(&g3[tid], 0u);
-    // the equal keys go to the lowest columns: workgroup by workgroup, then by column
-    const uint32_t cw = tid < nwg ? ld_agent(&cnt[tid]) : 0u;
-    const uint32_t eq_v = cw & 0xffffu;
-    uint32_t unused;
-    const uint32_t eq_before = block_exclusive_scan(eq_v, s_scan, &unused);
-    const uint32_t take_v = min(eq_v, need_eq > eq_before ? need_eq - eq_before : 0u);
-    if (tid == wg) s_misc[2] = take_v;
-    if (tid == 0) s_misc[3] = 0xffffffffu;
-    block_exclusive_scan(tid < wg ? (cw >> 16) + take_v : 0u, s_scan, &offset);  // barrier
-    const uint32_t take = s_misc[2];
-    if (take > 0u) {  // column of this workgroup's take-th equal key, in column order
-      for (int j = 0; j < iters; ++j) {
-        const unsigned long long m = __ballot(s_key[j * kFuseThreads + tid] == tkey);
-        if (lane == 0) s_cnt[j * kFuseWaves + wave] = (uint32_t)__popcll(m);
+      for (int j = 0; j < kFuseKeysPerThread; ++j) {
+        const int i = j * kFuseThreads + tid;
+        kk[j] = i < n_pool ? s_key[s_plist[i]] : 0u;
       }
       __syncthreads();
-      if (wave == 0) scan_counts_wave0_n<4>(s_cnt, iters * kFuseWaves);
-      __syncthreads();
-      for (int j = 0; j < iters; ++j) {
-        const bool eq = s_key[j * kFuseThreads + tid] == tkey;
-        const unsigned long long m = __ballot(eq);
-        if (eq && s_cnt[j * kFuseWaves + wave] + lanes_below(m) == take - 1u)
-          s_misc[3] = (uint32_t)(c0 + j * kFuseThreads + tid);
+#pragma unroll
+      for (int j = 0; j < kFuseKeysPerThread; ++j) {
+        const int i = j * kFuseThreads + tid;
+        if (i < n_pool) s_key[i] = kk[j];
       }
       __syncthreads();
-      col_cut = (int)s_misc[3];
     }
-  }
-
-  // ---- compaction in column order of the selected columns
-  uint32_t selbits = 0;
-  for (int j = 0; j < iters; ++j) {
-    const uint32_t key = s_key[j * kFuseThreads + tid];
-    const int col = c0 + j * kFuseThreads + tid;
-    const bool take = key > tkey || (key == tkey && key != 0u && col <= col_cut);
-    selbits |= (take ? 1u : 0u) << j;
-    const unsigned long long m = __ballot(take);
-    if (lane == 0) s_cnt[j * kFuseWaves + wave] = (uint32_t)__popcll(m);
-  }
-  __syncthreads();
-  if (wave == 0) scan_counts_wave0_n<4>(s_cnt, iters * kFuseWaves);
-  __syncthreads();
-  int32_t* orow = idx_out + (size_t)b * k;
-  float* srow = score_out ? score_out + (size_t)b * k : nullptr;
-  for (int j = 0; j < iters; ++j) {
-    const bool take = (selbits >> j) & 1u;
-    const unsigned long long m = __ballot(take);
-    if (take) {
-      const uint32_t pos = offset + s_cnt[j * kFuseWaves + wave] + lanes_below(m);
-      const int col = c0 + j * kFuseThreads + tid;
-      if (pos < (uint32_t)k) {
-        orow[pos] = CAND ? cand_row[col] : col;
-        if (srow) srow[pos] = key_score(s_key[j * kFuseThreads + tid]);
+    if (r >= 0) {
+      // re-score the pool entries with this layer's query (the scan's arithmetic)
+      bf16x2 q[16];
+      {
+        const uint4* qp =
+            reinterpret_cast<const uint4*>(a.q_re + ((size_t)r * a.batch + b) * kDIdx) + quarter * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = qp[i];
+          q[4 * i + 0] = __builtin_bit_cast(bf16x2, v.x);
+          q[4 * i + 1] = __builtin_bit_cast(bf16x2, v.y);
+          q[4 * i + 2] = __builtin_bit_cast(bf16x2, v.z);
+          q[4 * i + 3] = __builtin_bit_cast(bf16x2, v.w);
+        }
       }
+      constexpr int kU = 4;  // groups of 16 entries per wave in flight
+      for (int g0 = wave * 16 * kU; g0 < n_pool; g0 += kFuseWaves * 16 * kU) {
+        uint4 w[kU];
+        float sc[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = min(g0 + u * 16 + ent, n_pool - 1);
+          const int64_t e = base + c0 + s_plist[i];
+          w[u] = *reinterpret_cast<const uint4*>(a.codes + e * kIdxCodeBytes + quarter * 16);
+          sc[u] = a.scale[e];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          float v = dot32(w[u], q);
+          v += __shfl_xor(v, 1);
+          v += __shfl_xor(v, 2);
+          const int i = g0 + u * 16 + ent;
+          if (quarter == 0 && i < n_pool) s_key[i] = score_key(v * sc[u]);
+        }
+      }
+      __syncthreads();
     }
-  }
-  for (int p = (int)k_eff + wg * kFuseThreads + tid; p < k; p += nwg * kFuseThreads) {
-    orow[p] = -1;
-    if (srow) srow[p] = -__builtin_inff();
+    int kst;
+    int32_t* orow;
+    float* srow;
+    if (st == 0) {
+      kst = a.k;
+      orow = a.idx_out + (size_t)b * a.k;
+      srow = a.score_out ? a.score_out + (size_t)b * a.k : nullptr;
+    } else if (r < 0) {
+      kst = a.own_k;
+      orow = a.own_out + (size_t)b * a.own_k;
+      srow = nullptr;
+    } else {
+      kst = a.re_k;
+      orow = a.re_out + ((size_t)r * a.batch + b) * a.re_k;
+      srow = a.re_score_out ? a.re_score_out + ((size_t)r * a.batch + b) * a.re_k : nullptr;
+    }
+    const SelResult res = row_select(
+        s_key, st == 0 ? c1 - c0 : n_pool, st == 0 ? (uint32_t)c0 : pool_off, kst,
+        st == 0 && nv > 0, sel_ws(a.sel_base, b, st), rs, L, wg, nwg, orow, srow,
+        [&](int i) {
+          if (st == 0) return CAND ? cand_row[c0 + i] : c0 + i;
+          return c0 + (int)s_plist[i];
+        },
+        [&](uint32_t rank, int i) {
+          if (st == 0 && chain) s_plist[rank] = (uint16_t)i;
+        });
+    if (st == 0) {
+      n_pool = (int)res.sel;
+      pool_off = res.offset;
+    }
   }
 
   // ---- the last workgroup of the row to leave resets the row's barrier counters
-  __syncthreads();
   if (tid == 0) {
-    const uint32_t old = add_agent(arrivals + 1, 1u);
-    if (old == nw - 1u) {
-      st_agent(arrivals, 0u);
-      st_agent(arrivals + 1, 0u);
+    const uint32_t old = add_agent(rs.arrivals + 1, 1u);
+    if (old == rs.nw - 1u) {
+      st_agent(rs.arrivals, 0u);
+      st_agent(rs.arrivals + 1, 0u);
     }
   }
+}
+
+// Valid (non-negative) leading entries of each row of a -1 padded list.
+__global__ __launch_bounds__(256) void k_count_valid(const int32_t* __restrict__ list, int k,
+                                                     int32_t* __restrict__ n_out) {
+  __shared__ uint32_t s_scan[32];
+  const int b = blockIdx.x;
+  uint32_t c = 0;
+  for (int i = threadIdx.x; i < k; i += 256) c += list[(size_t)b * k + i] >= 0 ? 1u : 0u;
+  uint32_t total;
+  block_exclusive_scan(c, s_scan, &total);
+  if (threadIdx.x == 0) n_out[b] = (int32_t)total;
 }
 
 // ---------------------------------------------------------------------------- host side
@@ -414,12 +718,12 @@ int fused_capacity() {
           &per_cu_b, reinterpret_cast<const void*>(k_index_topk<true>), kFuseThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  g_capacity[dev] = min(per_cu_a, per_cu_b) * n_cu;
+  g_capacity[dev] = min(min(per_cu_a, per_cu_b) * n_cu, kFuseMaxWg);
   return g_capacity[dev];
 }
 
 // Columns per workgroup: a multiple of 1,024 up to 16,384, spreading the whole batch over
-// the device's capacity (one workgroup per CU) where it can.
+// the device's capacity where it can.
 int fused_cols_per_wg(int batch, int n_cols, int capacity) {
   const long long want = ((long long)n_cols * batch + capacity - 1) / capacity;
   long long c = (want + kFuseThreads - 1) / kFuseThreads * kFuseThreads;
@@ -428,56 +732,95 @@ int fused_cols_per_wg(int batch, int n_cols, int capacity) {
   return (int)c;
 }
 
-// The fused launch applies when one row's workgroups fit the device at once.
-bool fused_fits(int n_cols, int capacity, int* cpw_out, int* nwg_out, int batch) {
+// The single-launch kernel applies when one row's workgroups fit the device at once.
+bool fused_fits(int batch, int n_cols, int capacity, int* cpw_out, int* nwg_out) {
   if (capacity <= 0) return false;
   const int cpw = fused_cols_per_wg(batch, n_cols, capacity);
   const long long nwg = ((long long)n_cols + cpw - 1) / cpw;
-  if (nwg > kFuseMaxWg || nwg > capacity) return false;
+  if (nwg > capacity) return false;
   *cpw_out = cpw;
   *nwg_out = (int)nwg;
   return true;
 }
 
 size_t fuse_part_bytes(int batch) {
-  size_t s = 256;  // status
-  s += align_up((size_t)batch * kHist1Bins * 4, 256);
-  s += align_up((size_t)batch * kHist2Bins * 4, 256);
-  s += align_up((size_t)batch * kHist3Bins * 4, 256);
-  s += align_up((size_t)batch * kSyncStride * 4, 256);
-  s += align_up((size_t)batch * kFuseMaxWg * 4, 256);
-  s += align_up((size_t)batch * kFuseMaxWg * kTiedPerWg * 8, 256);
-  return s;
+  return 256 + align_up((size_t)batch * kSyncStride * 4, 256) + (size_t)batch * kMaxSel * kSelBytes;
 }
 
-FuseWs fuse_carve(void* base, int batch) {
-  FuseWs w;
+struct FuseParts {
+  uint32_t* status;
+  uint32_t* sync;
+  char* sel_base;
+};
+
+FuseParts fuse_carve(void* base, int batch) {
   char* p = static_cast<char*>(base);
-  w.status = reinterpret_cast<uint32_t*>(p);
-  p += 256;
-  w.hist1 = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * kHist1Bins * 4, 256);
-  w.hist2 = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * kHist2Bins * 4, 256);
-  w.hist3 = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * kHist3Bins * 4, 256);
-  w.sync = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * kSyncStride * 4, 256);
-  w.wgcnt = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * kFuseMaxWg * 4, 256);
-  w.tied = reinterpret_cast<unsigned long long*>(p);
-  return w;
+  FuseParts f;
+  f.status = reinterpret_cast<uint32_t*>(p);
+  f.sync = reinterpret_cast<uint32_t*>(p + 256);
+  f.sel_base = p + 256 + align_up((size_t)batch * kSyncStride * 4, 256);
+  return f;
+}
+
+// Two-launch path of one selection: [scores f32 batch x n_cols][top-k workspace].
+size_t two_step_bytes(int batch, int n_cols) {
+  return align_up((size_t)batch * n_cols * 4, 256) + topk_ws_bytes(batch, n_cols);
+}
+
+hipError_t two_step(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
+                    const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand, int batch,
+                    int n_cols, int k, int32_t* idx_out, float* score_out, char* p,
+                    hipStream_t stream) {
+  float* scores = reinterpret_cast<float*>(p);
+  const TopkWs tw = topk_ws_carve(p + align_up((size_t)batch * n_cols * 4, 256), batch, n_cols);
+  hipError_t e = launch_index_score(q_idx, codes, scale, seq_base, n_valid, cand, batch, n_cols,
+                                    scores, tw.hist1, stream);
+  if (e != hipSuccess) return e;
+  return launch_topk(scores, batch, n_cols, n_valid, cand, k, idx_out, score_out, true, tw, stream);
+}
+
+hipError_t launch_fused(ChainArgs a, int batch, int nwg, int capacity, bool cand,
+                        hipStream_t stream) {
+  const int rows_per_launch = max(1, capacity / nwg);
+  for (int r0 = 0; r0 < batch; r0 += rows_per_launch) {
+    a.row0 = r0;
+    const int rows = min(rows_per_launch, batch - r0);
+    if (cand)
+      hipLaunchKernelGGL(k_index_topk<true>, dim3(nwg, rows), dim3(kFuseThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_index_topk<false>, dim3(nwg, rows), dim3(kFuseThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+ChainArgs base_args(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
+                    const int64_t* seq_base, const int32_t* n_valid, int batch, int n_cols, int cpw,
+                    void* ws_base) {
+  const FuseParts f = fuse_carve(ws_base, batch);
+  ChainArgs a{};
+  a.q_idx = q_idx;
+  a.codes = codes;
+  a.scale = scale;
+  a.seq_base = seq_base;
+  a.n_valid = n_valid;
+  a.n_cols = n_cols;
+  a.cols_per_wg = cpw;
+  a.batch = batch;
+  a.status = f.status;
+  a.sync = f.sync;
+  a.sel_base = f.sel_base;
+  return a;
 }
 
 }  // namespace
 
-// Fused layout: [FuseWs part].  Otherwise (a row too long for one resident grid):
-// [FuseWs part][scores f32 batch x n_cols][top-k workspace] for the two-launch path.
 size_t index_topk_ws_bytes(int batch, int n_cols) {
   int cpw = 0, nwg = 0;
   const size_t fuse = fuse_part_bytes(batch);
-  if (fused_fits(n_cols, fused_capacity(), &cpw, &nwg, batch)) return fuse;
-  return fuse + align_up((size_t)batch * n_cols * 4, 256) + topk_ws_bytes(batch, n_cols);
+  if (fused_fits(batch, n_cols, fused_capacity(), &cpw, &nwg)) return fuse;
+  return fuse + two_step_bytes(batch, n_cols);
 }
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
@@ -486,29 +829,72 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const uint8_t* codes, const 
                              void* ws_base, hipStream_t stream) {
   const int capacity = fused_capacity();
   int cpw = 0, nwg = 0;
-  if (!fused_fits(n_cols, capacity, &cpw, &nwg, batch)) {
-    char* p = static_cast<char*>(ws_base) + fuse_part_bytes(batch);
-    float* scores = reinterpret_cast<float*>(p);
-    p += align_up((size_t)batch * n_cols * 4, 256);
-    const TopkWs tw = topk_ws_carve(p, batch, n_cols);
-    hipError_t e = launch_index_score(q_idx, codes, scale, seq_base, n_valid, cand, batch, n_cols,
-                                      scores, tw.hist1, stream);
-    if (e != hipSuccess) return e;
-    return launch_topk(scores, batch, n_cols, n_valid, cand, k, idx_out, score_out, true, tw, stream);
+  if (!fused_fits(batch, n_cols, capacity, &cpw, &nwg))
+    return two_step(q_idx, codes, scale, seq_base, n_valid, cand, batch, n_cols, k, idx_out,
+                    score_out, static_cast<char*>(ws_base) + fuse_part_bytes(batch), stream);
+  ChainArgs a = base_args(q_idx, codes, scale, seq_base, n_valid, batch, n_cols, cpw, ws_base);
+  a.cand = cand;
+  a.k = k;
+  a.idx_out = idx_out;
+  a.score_out = score_out;
+  return launch_fused(a, batch, nwg, capacity, cand != nullptr, stream);
+}
+
+// Two-launch layout: [fuse part][two-step part][pool scores f32 batch x pool_k][pool sizes].
+size_t select_chain_ws_bytes(int batch, int n_cols, int pool_k) {
+  int cpw = 0, nwg = 0;
+  const size_t fuse = fuse_part_bytes(batch);
+  if (fused_fits(batch, n_cols, fused_capacity(), &cpw, &nwg)) return fuse;
+  return fuse + two_step_bytes(batch, n_cols) + align_up((size_t)batch * pool_k * 4, 256) +
+         align_up((size_t)batch * 4, 256);
+}
+
+hipError_t launch_select_chain(const uint16_t* q_full, const uint8_t* codes, const float* scale,
+                               const int64_t* seq_base, const int32_t* n_valid, int batch,
+                               int n_cols, int pool_k, int32_t* pool_out, float* pool_score_out,
+                               int k, int32_t* own_out, const uint16_t* q_re, int n_re,
+                               int32_t* re_out, float* re_score_out, void* ws_base,
+                               hipStream_t stream) {
+  const int capacity = fused_capacity();
+  int cpw = 0, nwg = 0;
+  if (fused_fits(batch, n_cols, capacity, &cpw, &nwg)) {
+    ChainArgs a = base_args(q_full, codes, scale, seq_base, n_valid, batch, n_cols, cpw, ws_base);
+    a.k = pool_k;
+    a.idx_out = pool_out;
+    a.score_out = pool_score_out;
+    a.own_k = own_out ? k : 0;
+    a.own_out = own_out;
+    a.n_re = n_re;
+    a.re_k = k;
+    a.q_re = q_re;
+    a.re_out = re_out;
+    a.re_score_out = re_score_out;
+    return launch_fused(a, batch, nwg, capacity, false, stream);
   }
-  FuseWs ws = fuse_carve(ws_base, batch);
-  const int rows_per_launch = max(1, capacity / nwg);
-  for (int r0 = 0; r0 < batch; r0 += rows_per_launch) {
-    const int rows = min(rows_per_launch, batch - r0);
-    if (cand)
-      hipLaunchKernelGGL(k_index_topk<true>, dim3(nwg, rows), dim3(kFuseThreads), 0, stream, q_idx,
-                         codes, scale, seq_base, n_valid, cand, n_cols, cpw, r0, k, idx_out,
-                         score_out, ws);
-    else
-      hipLaunchKernelGGL(k_index_topk<false>, dim3(nwg, rows), dim3(kFuseThreads), 0, stream, q_idx,
-                         codes, scale, seq_base, n_valid, cand, n_cols, cpw, r0, k, idx_out,
-                         score_out, ws);
-    const hipError_t e = hipGetLastError();
+  // rows too long for one resident grid: the same selections one call at a time (the
+  // pool selections use the fused kernel with the still-clean fuse part of the workspace)
+  char* p = static_cast<char*>(ws_base) + fuse_part_bytes(batch);
+  char* after = p + two_step_bytes(batch, n_cols);
+  float* pool_scores =
+      pool_score_out ? pool_score_out : reinterpret_cast<float*>(after);
+  int32_t* pool_n = reinterpret_cast<int32_t*>(after + align_up((size_t)batch * pool_k * 4, 256));
+  hipError_t e = two_step(q_full, codes, scale, seq_base, n_valid, nullptr, batch, n_cols, pool_k,
+                          pool_out, pool_scores, p, stream);
+  if (e != hipSuccess) return e;
+  if (own_out == nullptr && n_re == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_count_valid, dim3(batch), dim3(256), 0, stream, pool_out, pool_k, pool_n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (own_out) {
+    e = launch_topk(pool_scores, batch, pool_k, pool_n, pool_out, k, own_out, nullptr, false,
+                    TopkWs{}, stream);
+    if (e != hipSuccess) return e;
+  }
+  for (int r = 0; r < n_re; ++r) {
+    e = launch_index_topk(q_re + (size_t)r * batch * kDIdx, codes, scale, seq_base, pool_n,
+                          pool_out, batch, pool_k, k, re_out + (size_t)r * batch * k,
+                          re_score_out ? re_score_out + (size_t)r * batch * k : nullptr, ws_base,
+                          stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

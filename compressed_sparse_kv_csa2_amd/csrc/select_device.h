@@ -5,6 +5,22 @@
 
 namespace csa2 {
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8 within
+// each row of 16 lanes, then row_bcast:15 (rows 1 and 3 add the last lane of the row
+// before) and row_bcast:31 (rows 2 and 3 add lane 31).  Lanes outside a shift's row, or
+// rows masked off, add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return (uint32_t)x;
+}
+
+
 // Executed by ONE wave: finds the bin holding the need-th largest element of h[0..nbins)
 // (nbins a multiple of 64, 1 <= need <= total).  out[0] = bin, out[1] = elements above.
 inline __device__ void find_threshold_bin(const uint32_t* h, int nbins, uint32_t need, uint32_t* out) {
@@ -17,12 +33,7 @@ inline __device__ void find_threshold_bin(const uint32_t* h, int nbins, uint32_t
   const int hi = nbins - lane * per;  // lane 0 owns the top bins
   uint32_t sum = 0;
   for (int i = 1; i <= per; ++i) sum += h[hi - i];
-  uint32_t incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(sum);
   const uint32_t excl = incl - sum;
   if (excl < need && need <= incl) {
     uint32_t acc = excl;
@@ -39,34 +50,24 @@ inline __device__ void find_threshold_bin(const uint32_t* h, int nbins, uint32_t
 }
 
 // Block-wide exclusive scan of one u32 per thread; returns the exclusive prefix and
-// stores the block total in *total.  `scratch` holds >= 17 u32 of LDS.  Ends with a barrier.
+// stores the block total in *total.  `scratch` holds >= 16 u32 of LDS.  Two barriers; ends
+// with one (scratch is free again).
 inline __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  __syncthreads();
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      uint32_t t = scratch[w];
-      scratch[w] = run;
-      run += t;
-    }
-    scratch[16] = run;
+  uint32_t before = 0, tot = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const uint32_t t = scratch[w];
+    before += w < wave ? t : 0u;
+    tot += t;
   }
+  *total = tot;
   __syncthreads();
-  uint32_t r = scratch[wave] + incl - v;
-  *total = scratch[16];
-  __syncthreads();
-  return r;
+  return before + incl - v;
 }
 
 // Block-wide search of a histogram h[0..PER * blockDim.x) in LDS for the bin holding the
@@ -125,12 +126,7 @@ __device__ uint32_t scan_counts_wave0_n(uint32_t* s_cnt, int n) {
     c[i] = PER * lane + i < n ? s_cnt[PER * lane + i] : 0u;
     part += c[i];
   }
-  uint32_t incl = part;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(part);
   uint32_t run = incl - part;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {

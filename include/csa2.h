@@ -59,6 +59,7 @@ extern "C" {
 #define CSA2_HEADS 16       /* query heads; one shared KV head */
 #define CSA2_SWA 128        /* sliding-window rows per layer and sequence */
 #define CSA2_MAX_K 16384    /* largest k accepted by csa2_topk / csa2_prefill_chunk */
+#define CSA2_MAX_REINDEX 4  /* Reindex layers one csa2_select_chain call serves */
 
 enum csa2_status {
   CSA2_OK = 0,
@@ -165,6 +166,43 @@ int csa2_index_topk(const uint16_t* q_idx, const uint8_t* idx_codes, const float
                     const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
                     int32_t batch, int32_t n_cols, int32_t k, int32_t* idx_out, float* score_out,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace csa2_select_chain needs for this shape on the current device. */
+size_t csa2_select_chain_workspace_size(int32_t batch, int32_t n_cols, int32_t pool_k);
+
+/*
+ * csa2_select_chain -- the selections of a decoder layer chain in one call: the Full
+ * layer's scan and pool (a1 + a2), its own top-k inside the pool, and the top-k of up to
+ * four Reindex layers that re-score the pool with their own indexer queries (a3 + a2).
+ *   [V4TO41] decoder section (the first layer's full scan yields a pool of about 16K
+ *   positions that later layers search for their top-512); [STRUCT] commentary on the
+ *   four layer modes (Reindex re-picks inside the pool).
+ *
+ *   q_full, idx_codes, idx_scale, seq_base, n_valid, batch, n_cols   as csa2_index_topk
+ *   pool_k         1..16384: pool size
+ *   pool_out       i32 [batch][pool_k] (out)  = csa2_index_topk(q_full, k = pool_k)
+ *   pool_score_out f32 [batch][pool_k] or NULL (out), its scores
+ *   k              1..16384: top-k of the layers below
+ *   own_out        i32 [batch][k] or NULL (out) = csa2_topk(pool scores, cand = pool, k):
+ *                  the Full layer's own top-k, inside its pool
+ *   q_re           bf16 [n_re][batch][128]     Reindex queries (NULL when n_re = 0)
+ *   n_re           0..4
+ *   re_out         i32 [n_re][batch][k] (out)  = csa2_index_topk(q_re[r], cand = pool,
+ *                  n_valid = pool entries, k) for each layer r
+ *   re_score_out   f32 [n_re][batch][k] or NULL (out), their scores
+ *   workspace      as csa2_index_topk (zero-filled before first use, left ready; first
+ *                  4 bytes: sticky status word)
+ * Outputs are bit-identical to the separate calls named above.  When one row's
+ * workgroups fit the device at once, everything runs in one launch; otherwise the
+ * separate calls run.
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_cols > 2^26), HIP.
+ */
+int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const float* idx_scale,
+                      const int64_t* seq_base, const int32_t* n_valid, int32_t batch,
+                      int32_t n_cols, int32_t pool_k, int32_t* pool_out, float* pool_score_out,
+                      int32_t k, int32_t* own_out, const uint16_t* q_re, int32_t n_re,
+                      int32_t* re_out, float* re_score_out, void* workspace, size_t ws_bytes,
+                      void* stream);
 
 /* Bytes of workspace csa2_sparse_attn_decode needs for this shape. */
 size_t csa2_attn_workspace_size(int32_t batch, int32_t k);

@@ -110,3 +110,18 @@ def test_index_topk_validation(lib):
         assert f(*a) == want, (pos, val)
     assert lib.csa2_index_topk_workspace_size(0, 10, 1) == 0
     assert lib.csa2_index_topk_workspace_size(4, 1 << 20, 16384) > 0
+
+
+def test_select_chain_validation(lib):
+    f = lib.csa2_select_chain
+    base = [FAKE] * 5 + [4, 1 << 20, 16384, FAKE, None, 512, None, FAKE, 1, FAKE, None, FAKE,
+                         1 << 40, None]
+    for pos, val, want in [(7, 0, -1), (7, 16385, -1), (10, 0, -1), (13, 5, -1), (13, -1, -1),
+                           (12, None, -1), (14, None, -1), (8, None, -1), (0, ODD, -2),
+                           (17, 100, -3), (16, None, -3), (6, (1 << 26) + 1, -4)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
+    a = list(base); a[12] = None; a[13] = 0; a[14] = None
+    assert f(*a[:17] + [100, None]) == -3  # no Reindex layer: still needs its workspace
+    assert lib.csa2_select_chain_workspace_size(4, 1 << 20, 0) == 0
+    assert lib.csa2_select_chain_workspace_size(4, 1 << 20, 16384) > 0

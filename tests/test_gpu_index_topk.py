@@ -64,15 +64,22 @@ def two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None):
     return sc, idx, so
 
 
+SEL_BYTES = 4096 * 4 + 2048 * 4 + 512 * 4 + 256 * 4 + 2048 * 8  # one selection block
+SEL_HISTS = 4096 * 4 + 2048 * 4 + 512 * 4                       # its three histograms
+MAX_SEL = 6
+
+
 def ws_clean(ws, B):
-    """Status word 0; histograms and barrier counters back to zero."""
+    """Status word 0; barrier counters and every selection's histograms back to zero
+    (layout: status 256 B | counters B x 32 u32, 256-aligned | B x 6 selection blocks)."""
     w = h(ws)
     assert w[:4].view(np.uint32)[0] == 0, "a row barrier gave up waiting"
-    a = 256
-    n = 0
-    for per_row in (4096, 2048, 512, 32):  # hist1, hist2, hist3, barrier counters
-        n += -(-B * per_row * 4 // 256) * 256
-    assert not w[a:a + n].any(), "histograms or barrier counters not returned to zero"
+    sync = -(-B * 32 * 4 // 256) * 256
+    assert not w[256:256 + sync].any(), "barrier counters not reset"
+    base = 256 + sync
+    for blk in range(B * MAX_SEL):
+        o = base + blk * SEL_BYTES
+        assert not w[o:o + SEL_HISTS].any(), f"histograms of block {blk} not returned to zero"
 
 
 def same_as_two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None, rows=None):
@@ -224,3 +231,99 @@ def test_row_longer_than_one_resident_grid():
     cache = synth.make_entries([n], seed=37, device=DEV)
     q = synth.make_index_queries(1, 37, device=DEV)
     same_as_two_step(cache, q, n, 16384)
+
+
+# --------------------------------------------------------------------------- chained selections
+def chain(cache, q_full, n_cols, pool_k, k, q_re=None, own=True, ws=None):
+    B = q_full.shape[0]
+    ws = csa2.select_chain_workspace(B, n_cols, pool_k) if ws is None else ws
+    pool = torch.full((B, pool_k), -7, dtype=torch.int32, device=DEV)
+    pscore = torch.full((B, pool_k), 7.0, dtype=torch.float32, device=DEV)
+    own_out = torch.full((B, k), -7, dtype=torch.int32, device=DEV) if own else None
+    n_re = 0 if q_re is None else q_re.shape[0]
+    re_out = torch.full((n_re, B, k), -7, dtype=torch.int32, device=DEV) if n_re else None
+    re_sc = torch.full((n_re, B, k), 7.0, dtype=torch.float32, device=DEV) if n_re else None
+    csa2.csa2_select_chain(q_full, cache.idx_codes, cache.idx_scale, cache.seq_base, cache.n_entries,
+                           n_cols, pool, ws, k=k, pool_score_out=pscore, own_out=own_out,
+                           q_re=q_re, re_out=re_out, re_score_out=re_sc)
+    return pool, pscore, own_out, re_out, re_sc, ws
+
+
+def separate(cache, q_full, n_cols, pool_k, k, q_re=None):
+    B = q_full.shape[0]
+    pool, pscore, _ = fused(cache, q_full, n_cols, pool_k)
+    pool_n = (pool >= 0).sum(dim=1, dtype=torch.int32)
+    own = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    csa2.csa2_topk(pscore, pool_n, k, own, cand=pool)
+    res = []
+    for r in range(0 if q_re is None else q_re.shape[0]):
+        idx, sc, _ = fused(cache, q_re[r].contiguous(), pool_k, k, n_valid=pool_n, cand=pool)
+        res.append((idx, sc))
+    return pool, pscore, pool_n, own, res
+
+
+def check_chain(cache, q_full, n_cols, pool_k, k, q_re=None, rows=None):
+    pool, pscore, own, re_out, re_sc, ws = chain(cache, q_full, n_cols, pool_k, k, q_re)
+    pool2, pscore2, pool_n, own2, res2 = separate(cache, q_full, n_cols, pool_k, k, q_re)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, pool2) and torch.equal(pscore, pscore2), "pool differs"
+    assert torch.equal(own, own2), "own top-k differs"
+    for r, (idx2, sc2) in enumerate(res2):
+        assert torch.equal(re_out[r], idx2), f"Reindex layer {r} differs"
+        assert torch.equal(re_sc[r], sc2), f"Reindex layer {r} scores differ"
+    # the own top-k against the oracle's rule on the pool's scores
+    P, S, N, O = h(pool), h(pscore), h(pool_n), h(own)
+    for b in (range(q_full.shape[0]) if rows is None else rows):
+        sel = oracle.topk(S[b].astype(np.float64), k, n_valid=int(N[b]))
+        want = np.where(sel >= 0, P[b][np.maximum(sel, 0)], -1)
+        assert np.array_equal(O[b], want), f"own top-k row {b}"
+    ws_clean(ws, q_full.shape[0])
+    return pool, own, re_out
+
+
+@pytest.mark.parametrize("n,pool_k,n_re", [(70_000, 16384, 2), (5000, 600, 1), (300_000, 16384, 4)])
+def test_chain_matches_separate_calls(n, pool_k, n_re):
+    log(f"select_chain n={n} pool={pool_k} re={n_re}")
+    B = 3
+    lens = [n, max(1, n // 7), max(1, n - 333)]
+    cache = synth.make_entries(lens, seed=50 + n_re, device=DEV)
+    q = synth.make_index_queries(B, 50 + n_re, device=DEV)
+    q_re = torch.stack([synth.make_index_queries(B, 60 + n_re + r, device=DEV)
+                        for r in range(n_re)]).contiguous()
+    check_chain(cache, q, n, pool_k, 512, q_re)
+
+
+def test_chain_with_ties():
+    """Zero queries: every score ties, in the pool and in every Reindex layer."""
+    log("select_chain ties")
+    n = 40_000
+    cache = synth.make_entries([n, n], seed=70, device=DEV)
+    q = torch.zeros((2, 128), dtype=torch.int16, device=DEV)
+    q_re = torch.zeros((2, 2, 128), dtype=torch.int16, device=DEV)
+    pool, own, re_out = check_chain(cache, q, n, 16384, 512, q_re)
+    assert np.array_equal(h(pool)[0], np.arange(16384))
+    assert np.array_equal(h(own)[1], np.arange(512))
+    assert np.array_equal(h(re_out)[1][0], np.arange(512))
+
+
+def test_chain_long_decode_at_full_size():
+    """4 x 2^20 Full scan -> pool 16,384 -> own top-512 and one Reindex layer."""
+    cfg = synth.CONFIGS["c4_long_decode"]
+    B, N = cfg["B"], 1 << 20
+    log(f"select_chain 2^20 B={B}")
+    cache = synth.make_entries([N] * B, seed=cfg["seed"], device=DEV)
+    q = synth.make_index_queries(B, cfg["seed"], device=DEV)
+    q_re = synth.make_index_queries(B, cfg["seed"] + 1000, device=DEV)[None].contiguous()
+    check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 3])
+
+
+def test_chain_decoder_layer_chain_at_full_size():
+    """16 x 131,072: one Full layer (pool + own top-512) and four Reindex layers."""
+    cfg = synth.CONFIGS["c3_decoder_chain"]
+    B, N = cfg["B"], cfg["ctx"] // cfg["ratio"]
+    log(f"select_chain chain B={B} N={N}")
+    cache = synth.make_entries([N] * B, seed=cfg["seed"], device=DEV)
+    q = synth.make_index_queries(B, cfg["seed"], device=DEV)
+    q_re = torch.stack([synth.make_index_queries(B, cfg["seed"] + 10 + r, device=DEV)
+                        for r in range(4)]).contiguous()
+    check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 15])
