@@ -49,9 +49,18 @@
 // up and sets a sticky status word in the workspace, so every wave exits even when the
 // device is shared and that assumption fails (the call's result is then undefined).
 //
-// Workspace: [status: 256 B][barrier counters: batch x 32 u32, 256-aligned]
-// [batch x kMaxSel selection blocks of kSelBytes: h1 u32[4096] | h2 u32[2048] |
-//  h3 u32[512] | per-workgroup counts u32[256] | published composites u64[2048]].
+// Speculative fine window (the scan's selection on rows of at least 64K columns): the scan
+// also counts key bits 31..16 for the 16 level-1 bins around the bin b1 of the previous
+// call on this row (a hint kept in the workspace; successive decode steps see similar
+// score distributions).  When the new b1 falls in that window, its fine counts are
+// complete and the sub-bin of the k-th key usually holds few enough keys to publish at
+// once, which saves the level-2 round; otherwise level 2 runs.  The result never depends
+// on the hint, only the time does.
+//
+// Workspace: [status: 256 B][per row 32 u32, 256-aligned: barrier arrivals, departures,
+// fine-window hint][batch x kMaxSel selection blocks of kSelBytes: h1 u32[4096] |
+// h2 u32[2048] | h3 u32[512] | per-workgroup counts u32[256] | published composites
+// u64[2048]][batch x fine counts u32[4096 x 16]].
 #include "csa2_internal.h"
 #include "scan_device.h"
 #include "select_device.h"
@@ -70,6 +79,10 @@ constexpr size_t kSelH3 = kSelH2 + kHist2Bins * 4;
 constexpr size_t kSelCnt = kSelH3 + kHist3Bins * 4;
 constexpr size_t kSelPub = kSelCnt + kFuseMaxWg * 4;
 constexpr size_t kSelBytes = kSelPub + kPubSlots * 8;
+constexpr int kFineSub = 16;           // sub-bins (key bits 19..16) per level-1 bin
+constexpr int kFineWin = 16;           // level-1 bins of the scan's fine window
+constexpr uint32_t kFineMinRow = 65536;  // rows this long count the window
+constexpr size_t kFineBytes = (size_t)kHist1Bins * kFineSub * 4;  // per row
 
 static_assert(kFuseThreads * 4 == kHist1Bins, "level-1 bins: 4 per thread");
 static_assert(kFuseThreads * 2 == kHist2Bins, "level-2 bins: 2 per thread");
@@ -134,6 +147,7 @@ struct SelLds {
   uint32_t* res;               // [4]
   uint32_t* misc;              // [4]
   unsigned long long* T;       // [1]
+  uint32_t* bits;              // [512] selection bitmap over the local index
 };
 
 // One selection's global arrays for this row.
@@ -143,13 +157,18 @@ struct SelWs {
   uint32_t* h3;
   uint32_t* cnt;               // [kFuseMaxWg]
   unsigned long long* pub;     // [kPubSlots]: workgroup w owns [w * cap, (w + 1) * cap)
+  uint32_t* fine;              // [4096][16] counts inside the scan's window (stage 0)
+  uint32_t* hint;              // [1] b1 + 1 of the previous call (0: none)
 };
 
-__device__ __forceinline__ SelWs sel_ws(char* sel_base, int row, int sel) {
+__device__ __forceinline__ SelWs sel_ws(char* sel_base, int row, int sel, char* fine_base,
+                                        uint32_t* sync) {
   char* p = sel_base + ((size_t)row * kMaxSel + sel) * kSelBytes;
   return SelWs{reinterpret_cast<uint32_t*>(p), reinterpret_cast<uint32_t*>(p + kSelH2),
                reinterpret_cast<uint32_t*>(p + kSelH3), reinterpret_cast<uint32_t*>(p + kSelCnt),
-               reinterpret_cast<unsigned long long*>(p + kSelPub)};
+               reinterpret_cast<unsigned long long*>(p + kSelPub),
+               reinterpret_cast<uint32_t*>(fine_base + (size_t)row * kFineBytes),
+               sync + (size_t)row * kSyncStride + 2};
 }
 
 // Adds the non-empty bins of an LDS histogram of N * 1,024 bins (N = 1: 512 bins) to a
@@ -220,32 +239,41 @@ __device__ uint32_t hist_select(const uint32_t* h, uint32_t k, uint32_t* s_scan,
 
 // Publishes this workgroup's count of keys above the bin (key >> shift > pre; every
 // non-zero key when `all`) and the composites of its keys inside it (key >> shift == pre,
-// at most `cap` of them; the count says how many there were).  Returns the combined
-// values of the atomics (for RowSync::sync).
-__device__ __forceinline__ uint32_t publish(const uint32_t* keys, int n_local, uint32_t pos0, uint32_t pre,
-                            int shift, bool all, int cap, uint32_t* cnt_slot,
-                            unsigned long long* pub, const SelLds& L) {
-  const int tid = threadIdx.x;
+// at most `cap` of them; the count says how many there were).  The keys above the bin are
+// also marked in L.bits (local index i -> bit i; every word below n_local is written).
+// Returns the combined values of the atomics (for RowSync::sync).
+__device__ __forceinline__ uint32_t publish(const uint32_t* keys, int n_local, uint32_t pos0,
+                                            uint32_t pre, int shift, bool all, int cap,
+                                            uint32_t* cnt_slot, unsigned long long* pub,
+                                            const SelLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) L.misc[0] = 0u;
   __syncthreads();
+  const int iters = (n_local + kFuseThreads - 1) / kFuseThreads;
   uint32_t n_above = 0;
-  for (int i = tid; i < n_local; i += kFuseThreads) {
-    const uint32_t key = keys[i];
-    if (key == 0u) continue;
+  for (int j = 0; j < iters; ++j) {
+    const int i = j * kFuseThreads + tid;
+    const uint32_t key = i < n_local ? keys[i] : 0u;
     const uint32_t d = key >> shift;
-    if (all || d > pre) {
-      ++n_above;
-    } else if (d == pre) {
+    const bool above = key != 0u && (all || d > pre);
+    const unsigned long long m = __ballot(above);
+    if (lane == 0) {
+      L.bits[(j * kFuseThreads + wave * 64) >> 5] = (uint32_t)m;
+      L.bits[((j * kFuseThreads + wave * 64) >> 5) + 1] = (uint32_t)(m >> 32);
+    }
+    n_above += above ? 1u : 0u;
+    if (key != 0u && !above && d == pre) {
       const uint32_t slot = atomicAdd(&L.misc[0], 1u);
       if (slot < (uint32_t)cap) L.pub[slot] = composite(key, pos0 + (uint32_t)i);
     }
   }
-  uint32_t above;
-  block_exclusive_scan(n_above, L.scan, &above);  // barrier: L.misc[0] and L.pub complete
+  uint32_t total_above;
+  block_exclusive_scan(n_above, L.scan, &total_above);  // barrier: L.misc[0], L.pub complete
   const uint32_t n_pub = L.misc[0];
   uint32_t pending = 0;
   if (tid < (int)min(n_pub, (uint32_t)cap)) pending |= xchg_agent(&pub[tid], L.pub[tid]);
-  if (tid == kFuseThreads - 1) pending |= xchg_agent(cnt_slot, (above << 16) | min(n_pub, 0xffffu));
+  if (tid == kFuseThreads - 1)
+    pending |= xchg_agent(cnt_slot, (total_above << 16) | min(n_pub, 0xffffu));
   return pending;
 }
 
@@ -262,13 +290,16 @@ struct SelResult {
 // the row; ends with a barrier.
 template <typename IdOf, typename OnSel>
 __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_local, uint32_t pos0, int k,
-                                bool h1_ready, const SelWs& g, RowSync& rs, const SelLds& L,
+                                bool h1_ready, bool keep_hint, uint32_t fine_lo,
+                                uint32_t pending_in,
+                                const SelWs& g, RowSync& rs, const SelLds& L,
                                 int wg, int nwg, int32_t* orow, float* srow, IdOf id_of,
                                 OnSel on_sel) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int iters = (n_local + kFuseThreads - 1) / kFuseThreads;
   const int cap = min(kPubSlots / nwg, kPubMax);
-  uint32_t pending = 0;
+  const bool fine_on = fine_lo != 0xffffffffu;  // the scan counted the fine window
+  uint32_t pending = pending_in;
 
   // ---- level 1: every workgroup's histogram into the row's, then the bin of the k-th key
   if (!h1_ready) local_hist(keys, n_local, 0u, 20, kHist1Bins, 12, L.h);
@@ -282,12 +313,36 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
   const uint32_t k_eff = min((uint32_t)k, total);
   const bool all = k_eff == total;  // the same in every workgroup of the row
   uint32_t pre = 0, need = 0;       // need: keys still to take at or below the bin
+  uint32_t b1 = 0, need1 = 0;
   int shift = 20;
-  bool pub_now = true;  // publish at level 1 (always when every key is taken)
+  bool pub_now = true;  // publish now (always when every key is taken)
   if (!all) {
-    pre = L.res[0];
-    need = k_eff - L.res[1];
+    b1 = pre = L.res[0];
+    need1 = need = k_eff - L.res[1];
     pub_now = L.h[pre] <= (uint32_t)kPubMax;
+    if (keep_hint && wg == 0 && tid == 0) st_agent(g.hint, b1 + 1u);  // for the next call
+    if (!pub_now && fine_on && b1 - fine_lo < (uint32_t)kFineWin) {
+      // the fine counts of b1 are complete: the sub-bin of the need-th key
+      __syncthreads();
+      if (tid < kFineSub) L.h[tid] = ld_agent(&g.fine[(b1 << 4) + tid]);
+      __syncthreads();
+      if (wave == 0) {
+        const uint32_t c = lane < kFineSub ? L.h[kFineSub - 1 - lane] : 0u;  // from the top
+        const uint32_t incl = wave_incl_scan(c);
+        if (lane < kFineSub && incl - c < need && need <= incl) {
+          L.res[0] = (uint32_t)(kFineSub - 1 - lane);
+          L.res[1] = incl - c;
+          L.res[2] = c;
+        }
+      }
+      __syncthreads();
+      if (L.res[2] <= (uint32_t)kPubMax) {
+        pre = (b1 << 4) | L.res[0];
+        need -= L.res[1];
+        shift = 16;
+        pub_now = true;
+      }
+    }
   }
   __syncthreads();  // L.h and L.res are read before they are rewritten
   if (pub_now) {
@@ -298,8 +353,10 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
   }
   rs.sync(pending);
   pending = 0;
-  if (wg == 0)
+  if (wg == 0) {
     for (int i = tid; i < kHist1Bins; i += kFuseThreads) st_agent(&g.h1[i], 0u);
+    if (fine_on && tid < kFineWin * kFineSub) st_agent(&g.fine[(fine_lo << 4) + tid], 0u);
+  }
 
   // ---- level 2 (when b1 held too many keys): the bin (b1, b2), then publish
   if (!pub_now) {
@@ -400,8 +457,20 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
       tkey = (uint32_t)(T >> 32);
       cut = ~(uint32_t)T;
       has_cut = true;
-      if (ok0 && t0 >= T) atomicAdd(&L.selt[v0], 1u);
-      if (ok1 && t1 >= T) atomicAdd(&L.selt[v1], 1u);
+      if (ok0 && t0 >= T) {
+        atomicAdd(&L.selt[v0], 1u);
+        if (v0 == wg) {  // this workgroup's own tied key is taken
+          const uint32_t i = ~(uint32_t)t0 - pos0;
+          atomicOr(&L.bits[i >> 5], 1u << (i & 31));
+        }
+      }
+      if (ok1 && t1 >= T) {
+        atomicAdd(&L.selt[v1], 1u);
+        if (v1 == wg) {
+          const uint32_t i = ~(uint32_t)t1 - pos0;
+          atomicOr(&L.bits[i >> 5], 1u << (i & 31));
+        }
+      }
     }
     __syncthreads();
     const uint32_t sel_v = tid < nwg ? (cv >> 16) + L.selt[tid] : 0u;
@@ -409,7 +478,9 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
   } else {
     // massive ties: the threshold key from a level-3 histogram (after level 2, if the
     // keys were published at level 1), then each workgroup's share of the equal keys
-    if (shift == 20) {
+    if (shift != 9) {  // published from b1 or its fine sub-bin: level 2 from b1
+      pre = b1;
+      need = need1;
       local_hist(keys, n_local, pre, 9, kHist2Bins, 11, L.h);
       pending |= flush_hist<2>(L.h, kHist2Bins, g.h2);
       rs.sync(pending);
@@ -477,34 +548,58 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
   }
 
   // ---- the selected entries in position order
-  uint32_t selbits = 0;
-  for (int j = 0; j < iters; ++j) {
-    const int i = j * kFuseThreads + tid;
-    const uint32_t key = i < n_local ? keys[i] : 0u;
-    const bool take =
-        key != 0u && (key > tkey || (key == tkey && has_cut && pos0 + (uint32_t)i <= cut));
-    selbits |= (take ? 1u : 0u) << j;
-    const unsigned long long m = __ballot(take);
-    if (lane == 0) L.cnt[j * kFuseWaves + wave] = (uint32_t)__popcll(m);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t n = scan_counts_wave0_n<4>(L.cnt, iters * kFuseWaves);
-    if (lane == 0) L.misc[1] = n;
-  }
-  __syncthreads();
-  for (int j = 0; j < iters; ++j) {
-    const bool take = (selbits >> j) & 1u;
-    const unsigned long long m = __ballot(take);
-    if (take) {
-      const int i = j * kFuseThreads + tid;
-      const uint32_t rank = L.cnt[j * kFuseWaves + wave] + lanes_below(m);
+  int32_t* const out_ids = orow;
+  if (!overflow) {
+    // from the bitmap: thread t owns local indices [16t, 16t + 16)
+    const int i0 = 16 * tid;
+    const uint32_t w = L.bits[tid >> 1];
+    uint32_t m = (tid & 1) ? (w >> 16) : (w & 0xffffu);
+    if (i0 >= n_local) m = 0u;
+    else if (i0 + 16 > n_local) m &= (1u << (n_local - i0)) - 1u;
+    uint32_t n_sel;
+    uint32_t rank = block_exclusive_scan((uint32_t)__popc(m), L.scan, &n_sel);
+    if (tid == 0) L.misc[1] = n_sel;
+    while (m) {
+      const int i = i0 + __builtin_ctz(m);
+      m &= m - 1u;
       const uint32_t pos = offset + rank;
       if (pos < (uint32_t)k) {
-        orow[pos] = id_of(i);
+        out_ids[pos] = id_of(i);
         if (srow) srow[pos] = key_score(keys[i]);
       }
       on_sel(rank, i);
+      ++rank;
+    }
+  } else {
+    uint32_t selbits = 0;
+    for (int j = 0; j < iters; ++j) {
+      const int i = j * kFuseThreads + tid;
+      const uint32_t key = i < n_local ? keys[i] : 0u;
+      const bool take =
+          key != 0u && (key > tkey || (key == tkey && has_cut && pos0 + (uint32_t)i <= cut));
+      selbits |= (take ? 1u : 0u) << j;
+      const unsigned long long m = __ballot(take);
+      if (lane == 0) L.cnt[j * kFuseWaves + wave] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t n = scan_counts_wave0_n<4>(L.cnt, iters * kFuseWaves);
+      if (lane == 0) L.misc[1] = n;
+    }
+    __syncthreads();
+    for (int j = 0; j < iters; ++j) {
+      const bool take = (selbits >> j) & 1u;
+      const unsigned long long m = __ballot(take);
+      if (take) {
+        const int i = j * kFuseThreads + tid;
+        const uint32_t rank = L.cnt[j * kFuseWaves + wave] + lanes_below(m);
+        const uint32_t pos = offset + rank;
+        if (pos < (uint32_t)k) {
+          out_ids[pos] = id_of(i);
+          if (srow) srow[pos] = key_score(keys[i]);
+        }
+        on_sel(rank, i);
+      }
     }
   }
   for (int p = (int)k_eff + wg * kFuseThreads + tid; p < k; p += nwg * kFuseThreads) {
@@ -538,6 +633,7 @@ struct ChainArgs {
   uint32_t* status;
   uint32_t* sync;
   char* sel_base;
+  char* fine_base;
 };
 
 template <bool CAND>
@@ -552,6 +648,8 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
   __shared__ uint32_t s_res[4];
   __shared__ uint32_t s_misc[4];
   __shared__ unsigned long long s_T;
+  __shared__ uint32_t s_bits[kFuseMaxCols / 32];
+  __shared__ uint32_t s_fine[kFineWin * kFineSub];
   const int b = a.row0 + (int)blockIdx.y, wg = blockIdx.x, nwg = gridDim.x;
   const int tid = threadIdx.x;
   const int nv = min(a.n_valid[b], a.n_cols);
@@ -568,21 +666,41 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
   L.res = s_res;
   L.misc = s_misc;
   L.T = &s_T;
+  L.bits = s_bits;
 
-  // ---- score the columns [c0, c1): keys into LDS, level-1 histogram in LDS
+  // ---- score the columns [c0, c1): keys into LDS, level-1 histogram in LDS, and the fine
+  // counts of the window around the previous call's level-1 bin (long rows)
+  uint32_t fine_lo = 0xffffffffu;
+  const bool long_row = (uint32_t)nv >= kFineMinRow;
+  if (long_row) {
+    const uint32_t h = ld_agent(sel_ws(a.sel_base, b, 0, a.fine_base, a.sync).hint);
+    if (h != 0u) fine_lo = min(h - 1u >= 8u ? h - 9u : 0u, (uint32_t)(kHist1Bins - kFineWin));
+  }
+  const bool fine_on = fine_lo != 0xffffffffu;
   for (int i = tid; i < kFuseMaxCols; i += kFuseThreads) s_key[i] = 0u;
   if (nv > 0) {
     scan_columns<CAND, kFuseThreads>(
         a.q_idx + (size_t)b * kDIdx, a.codes, a.scale, cand_row, base, nv, c0, c1,
         [&]() {
           for (int i = tid; i < kHist1Bins; i += kFuseThreads) s_h[i] = 0u;
+          if (tid < kFineWin * kFineSub) s_fine[tid] = 0u;
         },
         [&](int col, float score, bool valid) {
           const uint32_t key = valid ? score_key(score) : 0u;
           s_key[col - c0] = key;
-          if (key != 0u) atomicAdd(&s_h[key >> 20], 1u);
+          if (key != 0u) {
+            atomicAdd(&s_h[key >> 20], 1u);
+            const uint32_t cw = (key >> 20) - fine_lo;
+            if (fine_on && cw < (uint32_t)kFineWin)
+              atomicAdd(&s_fine[(cw << 4) | ((key >> 16) & 15u)], 1u);
+          }
         });
     __syncthreads();
+  }
+  uint32_t fine_pending = 0;
+  if (fine_on && nv > 0 && tid < kFineWin * kFineSub) {
+    const uint32_t v = s_fine[tid];
+    if (v) fine_pending = add_agent(&sel_ws(a.sel_base, b, 0, a.fine_base, a.sync).fine[(fine_lo << 4) + tid], v);
   }
 
   // ---- the selections: stage 0 over the scanned columns (the pool when chained), then
@@ -665,7 +783,9 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
     }
     const SelResult res = row_select(
         s_key, st == 0 ? c1 - c0 : n_pool, st == 0 ? (uint32_t)c0 : pool_off, kst,
-        st == 0 && nv > 0, sel_ws(a.sel_base, b, st), rs, L, wg, nwg, orow, srow,
+        st == 0 && nv > 0, st == 0 && long_row, st == 0 ? fine_lo : 0xffffffffu,
+        st == 0 ? fine_pending : 0u,
+        sel_ws(a.sel_base, b, st, a.fine_base, a.sync), rs, L, wg, nwg, orow, srow,
         [&](int i) {
           if (st == 0) return CAND ? cand_row[c0 + i] : c0 + i;
           return c0 + (int)s_plist[i];
@@ -744,13 +864,15 @@ bool fused_fits(int batch, int n_cols, int capacity, int* cpw_out, int* nwg_out)
 }
 
 size_t fuse_part_bytes(int batch) {
-  return 256 + align_up((size_t)batch * kSyncStride * 4, 256) + (size_t)batch * kMaxSel * kSelBytes;
+  return 256 + align_up((size_t)batch * kSyncStride * 4, 256) + (size_t)batch * kMaxSel * kSelBytes +
+         (size_t)batch * kFineBytes;
 }
 
 struct FuseParts {
   uint32_t* status;
   uint32_t* sync;
   char* sel_base;
+  char* fine_base;
 };
 
 FuseParts fuse_carve(void* base, int batch) {
@@ -759,6 +881,7 @@ FuseParts fuse_carve(void* base, int batch) {
   f.status = reinterpret_cast<uint32_t*>(p);
   f.sync = reinterpret_cast<uint32_t*>(p + 256);
   f.sel_base = p + 256 + align_up((size_t)batch * kSyncStride * 4, 256);
+  f.fine_base = f.sel_base + (size_t)batch * kMaxSel * kSelBytes;
   return f;
 }
 
@@ -811,6 +934,7 @@ ChainArgs base_args(const uint16_t* q_idx, const uint8_t* codes, const float* sc
   a.status = f.status;
   a.sync = f.sync;
   a.sel_base = f.sel_base;
+  a.fine_base = f.fine_base;
   return a;
 }
 

@@ -67,19 +67,24 @@ def two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None):
 SEL_BYTES = 4096 * 4 + 2048 * 4 + 512 * 4 + 256 * 4 + 2048 * 8  # one selection block
 SEL_HISTS = 4096 * 4 + 2048 * 4 + 512 * 4                       # its three histograms
 MAX_SEL = 6
+FINE_BYTES = 4096 * 16 * 4                                       # fine counts per row
 
 
 def ws_clean(ws, B):
-    """Status word 0; barrier counters and every selection's histograms back to zero
-    (layout: status 256 B | counters B x 32 u32, 256-aligned | B x 6 selection blocks)."""
+    """Status word 0; barrier counters, every selection's histograms and the fine window
+    counts back to zero.  Layout: status 256 B | per row 32 u32 (arrivals, departures,
+    fine-window hint), 256-aligned | B x 6 selection blocks | B x fine counts."""
     w = h(ws)
     assert w[:4].view(np.uint32)[0] == 0, "a row barrier gave up waiting"
     sync = -(-B * 32 * 4 // 256) * 256
-    assert not w[256:256 + sync].any(), "barrier counters not reset"
+    rows = w[256:256 + B * 128].view(np.uint32).reshape(B, 32)
+    assert not rows[:, :2].any(), "barrier counters not reset"
     base = 256 + sync
     for blk in range(B * MAX_SEL):
         o = base + blk * SEL_BYTES
         assert not w[o:o + SEL_HISTS].any(), f"histograms of block {blk} not returned to zero"
+    fine = base + B * MAX_SEL * SEL_BYTES
+    assert not w[fine:fine + B * FINE_BYTES].any(), "fine window counts not cleared"
 
 
 def same_as_two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None, rows=None):
@@ -200,6 +205,26 @@ def test_workspace_reuse_is_deterministic():
     ws_clean(ws, 2)
 
 
+def test_fine_window_hint_hits_and_misses():
+    """Long rows count a fine window around the previous call's level-1 bin.  Calls on one
+    workspace alternate between queries whose k-th score lies in that window and queries
+    scaled by 8 (three octaves away: the window misses); every call stays exact."""
+    log("index_topk fine-window hint")
+    n = 200_000
+    cache = synth.make_entries([n, n - 3], seed=38, device=DEV)
+    q = synth.make_index_queries(2, 38, device=DEV)
+    q8 = (q.view(torch.bfloat16).float() * 8).to(torch.bfloat16).view(torch.int16)
+    ws = csa2.index_topk_workspace(2, n, 16384)
+    for qq in (q, q, q8, q, q8, q8, q):
+        idx, so, _ = fused(cache, qq, n, 16384, ws=ws)
+        _, idx2, so2 = two_step(cache, qq, n, 16384)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx2) and torch.equal(so, so2)
+    ws_clean(ws, 2)
+    hint = h(ws)[256:256 + 2 * 128].view(np.uint32).reshape(2, 32)[:, 2]
+    assert np.all(hint > 0), "the hint was not kept"
+
+
 def test_long_decode_pool_and_reindex_at_full_size():
     """4 x 2^20 Full scan -> pool of 16,384 -> Reindex top-512, as the benchmark runs it."""
     cfg = synth.CONFIGS["c4_long_decode"]
@@ -262,8 +287,8 @@ def separate(cache, q_full, n_cols, pool_k, k, q_re=None):
     return pool, pscore, pool_n, own, res
 
 
-def check_chain(cache, q_full, n_cols, pool_k, k, q_re=None, rows=None):
-    pool, pscore, own, re_out, re_sc, ws = chain(cache, q_full, n_cols, pool_k, k, q_re)
+def check_chain(cache, q_full, n_cols, pool_k, k, q_re=None, rows=None, ws=None):
+    pool, pscore, own, re_out, re_sc, ws = chain(cache, q_full, n_cols, pool_k, k, q_re, ws=ws)
     pool2, pscore2, pool_n, own2, res2 = separate(cache, q_full, n_cols, pool_k, k, q_re)
     torch.cuda.synchronize()
     assert torch.equal(pool, pool2) and torch.equal(pscore, pscore2), "pool differs"
@@ -307,14 +332,17 @@ def test_chain_with_ties():
 
 
 def test_chain_long_decode_at_full_size():
-    """4 x 2^20 Full scan -> pool 16,384 -> own top-512 and one Reindex layer."""
+    """4 x 2^20 Full scan -> pool 16,384 -> own top-512 and one Reindex layer; the second
+    and third calls on the workspace use the fine window of the first."""
     cfg = synth.CONFIGS["c4_long_decode"]
     B, N = cfg["B"], 1 << 20
     log(f"select_chain 2^20 B={B}")
     cache = synth.make_entries([N] * B, seed=cfg["seed"], device=DEV)
-    q = synth.make_index_queries(B, cfg["seed"], device=DEV)
-    q_re = synth.make_index_queries(B, cfg["seed"] + 1000, device=DEV)[None].contiguous()
-    check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 3])
+    ws = csa2.select_chain_workspace(B, N, 16384)
+    for rep in range(3):
+        q = synth.make_index_queries(B, cfg["seed"] + rep, device=DEV)
+        q_re = synth.make_index_queries(B, cfg["seed"] + 1000 + rep, device=DEV)[None].contiguous()
+        check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 3], ws=ws)
 
 
 def test_chain_decoder_layer_chain_at_full_size():
