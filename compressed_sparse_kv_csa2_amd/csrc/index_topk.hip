@@ -277,9 +277,65 @@ __device__ __forceinline__ uint32_t publish(const uint32_t* keys, int n_local, u
   return pending;
 }
 
+// The need-th largest (1 <= need <= nt) of the nt unique composites in L.pub[0..nt), whose
+// keys agree above bit `shift`; stored in *L.T (*L.T must be ~0 before).  Few composites:
+// wave 0 ranks them directly; otherwise one 256-bin radix pass over the 8 key bits below
+// `shift` and the few composites left in the chosen digit are ranked directly.  Whole
+// workgroup; the caller's barrier publishes *L.T.  Uses L.pub[kPubMax..2 kPubMax) and L.h.
+__device__ __forceinline__ void rank_composites(const SelLds& L, uint32_t nt, uint32_t need,
+                                                int shift) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (nt <= 64u) {
+    if (wave == 0) {
+      const unsigned long long c = (uint32_t)lane < nt ? L.pub[lane] : 0ull;
+      const uint32_t chi = (uint32_t)(c >> 32), clo = (uint32_t)c;
+      uint32_t r = 0;
+      for (uint32_t j = 0; j < nt; ++j) {
+        const uint32_t ohi = __builtin_amdgcn_readlane(chi, j);
+        const uint32_t olo = __builtin_amdgcn_readlane(clo, j);
+        r += (ohi > chi || (ohi == chi && olo > clo)) ? 1u : 0u;
+      }
+      if ((uint32_t)lane < nt && r == need - 1u) *L.T = c;
+    }
+    return;
+  }
+  const int dsh = shift - 8;
+  if (tid < 256) L.h[tid] = 0u;
+  if (tid == 0) L.misc[0] = 0u;
+  __syncthreads();
+  for (uint32_t i = tid; i < nt; i += kFuseThreads)
+    atomicAdd(&L.h[(uint32_t)(L.pub[i] >> (32 + dsh)) & 255u], 1u);
+  __syncthreads();
+  if (wave == 0) find_threshold_bin(L.h, 256, need, L.res);
+  __syncthreads();
+  const uint32_t da = L.res[0], need_b = need - L.res[1];
+  for (uint32_t i = tid; i < nt; i += kFuseThreads) {
+    const unsigned long long c = L.pub[i];
+    if (((uint32_t)(c >> (32 + dsh)) & 255u) == da) L.pub[kPubMax + atomicAdd(&L.misc[0], 1u)] = c;
+  }
+  __syncthreads();
+  const uint32_t nb = L.misc[0];
+  const unsigned long long* cb = L.pub + kPubMax;
+  for (uint32_t i = tid; i < nb; i += kFuseThreads) {
+    const unsigned long long c = cb[i];
+    uint32_t r = 0;
+    uint32_t j = 0;
+    for (; j + 8 <= nb; j += 8) {  // eight loads in flight per step
+      unsigned long long x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = cb[j + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += x[u] > c ? 1u : 0u;
+    }
+    for (; j < nb; ++j) r += cb[j] > c ? 1u : 0u;
+    if (r == need_b - 1u) *L.T = c;
+  }
+}
+
 struct SelResult {
   uint32_t sel;     // entries this workgroup selected
   uint32_t offset;  // output position of its first one
+  uint32_t total;   // entries the row selected
 };
 
 // One selection over keys[0..n_local) of every workgroup of the row (LDS; local index i =
@@ -401,56 +457,7 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
     if (tid < nwg) L.selt[tid] = 0u;
     if (tid == 0) *L.T = ~0ull;
     __syncthreads();
-    if (!all && nt <= 64) {
-      // few composites: wave 0 ranks them directly (they are unique: exactly one has rank
-      // need - 1)
-      if (wave == 0) {
-        const unsigned long long c = (uint32_t)lane < nt ? L.pub[lane] : 0ull;
-        const uint32_t chi = (uint32_t)(c >> 32), clo = (uint32_t)c;
-        uint32_t r = 0;
-        for (uint32_t j = 0; j < nt; ++j) {
-          const uint32_t ohi = __builtin_amdgcn_readlane(chi, j);
-          const uint32_t olo = __builtin_amdgcn_readlane(clo, j);
-          r += (ohi > chi || (ohi == chi && olo > clo)) ? 1u : 0u;
-        }
-        if ((uint32_t)lane < nt && r == need - 1u) *L.T = c;
-      }
-    } else if (!all) {
-      // the need-th largest published composite: one 256-bin radix pass over the 8 key
-      // bits below the bin, then the few composites left in the chosen digit are ranked
-      // directly (they are unique: exactly one has rank need - 1 among them)
-      const int dsh = shift - 8;
-      if (tid < 256) L.h[tid] = 0u;
-      if (tid == 0) L.misc[0] = 0u;
-      __syncthreads();
-      for (uint32_t i = tid; i < nt; i += kFuseThreads)
-        atomicAdd(&L.h[(uint32_t)(L.pub[i] >> (32 + dsh)) & 255u], 1u);
-      __syncthreads();
-      if (wave == 0) find_threshold_bin(L.h, 256, need, L.res);
-      __syncthreads();
-      const uint32_t da = L.res[0], need_b = need - L.res[1];
-      for (uint32_t i = tid; i < nt; i += kFuseThreads) {
-        const unsigned long long c = L.pub[i];
-        if (((uint32_t)(c >> (32 + dsh)) & 255u) == da) L.pub[kPubMax + atomicAdd(&L.misc[0], 1u)] = c;
-      }
-      __syncthreads();
-      const uint32_t nb = L.misc[0];
-      const unsigned long long* cb = L.pub + kPubMax;
-      for (uint32_t i = tid; i < nb; i += kFuseThreads) {
-        const unsigned long long c = cb[i];
-        uint32_t r = 0;
-        uint32_t j = 0;
-        for (; j + 8 <= nb; j += 8) {  // eight loads in flight per step
-          unsigned long long x[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) x[u] = cb[j + u];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) r += x[u] > c ? 1u : 0u;
-        }
-        for (; j < nb; ++j) r += cb[j] > c ? 1u : 0u;
-        if (r == need_b - 1u) *L.T = c;
-      }
-    }
+    if (!all) rank_composites(L, nt, need, shift);
     __syncthreads();
     if (!all) {
       const unsigned long long T = *L.T;
@@ -606,9 +613,134 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
     orow[p] = -1;
     if (srow) srow[p] = -__builtin_inff();
   }
-  const SelResult r{L.misc[1], offset};
+  const SelResult r{L.misc[1], offset, k_eff};
   __syncthreads();
   return r;
+}
+
+// Top-k of keys[0..n) (LDS; key 0 = not selectable; position = index) by one workgroup,
+// with the rule of the row selections: the k largest, ties to the lower position, written
+// in position order as id_of(i) into orow[0..k), -1 padded; scores into srow if given.
+// L.h holds the keys' level-1 histogram on entry.  The level-1 bin (or the level-2 bin
+// when it holds too many) is ranked from its composites, gathered in the same pass that
+// marks the keys above it in a bitmap; massive ties take level 3 and the lowest positions
+// among the equal keys.
+template <typename IdOf>
+__device__ __forceinline__ void wg_select(const uint32_t* keys, int n, int k, const SelLds& L,
+                                          int32_t* orow, float* srow, IdOf id_of) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int iters = (n + kFuseThreads - 1) / kFuseThreads;
+  const uint32_t total = hist_select<4>(L.h, (uint32_t)k, L.scan, L.res);
+  const uint32_t k_eff = min((uint32_t)k, total);
+  // selected: key > tkey, or key == tkey at index <= cut (when has_cut); marked in L.bits
+  uint32_t tkey = 0u, cut = 0u;
+  bool has_cut = false, marked = false;
+  if (k_eff < total) {
+    uint32_t pre = L.res[0], need = k_eff - L.res[1];
+    int shift = 20;
+    bool small = L.h[pre] <= (uint32_t)kPubMax;
+    __syncthreads();
+    if (!small) {
+      local_hist(keys, n, pre, 9, kHist2Bins, 11, L.h);
+      hist_select<2>(L.h, need, L.scan, L.res);
+      const uint32_t b2 = L.res[0];
+      need -= L.res[1];
+      small = L.h[b2] <= (uint32_t)kPubMax;
+      pre = (pre << 11) | b2;
+      shift = 9;
+      __syncthreads();
+    }
+    if (small) {
+      // one pass: the keys above the bin into the bitmap, the bin's composites into L.pub
+      if (tid == 0) {
+        L.misc[0] = 0u;
+        *L.T = ~0ull;
+      }
+      __syncthreads();
+      for (int j = 0; j < iters; ++j) {
+        const int i = j * kFuseThreads + tid;
+        const uint32_t key = i < n ? keys[i] : 0u;
+        const uint32_t d = key >> shift;
+        const unsigned long long m = __ballot(key != 0u && d > pre);
+        if (lane == 0) {
+          L.bits[(j * kFuseThreads + wave * 64) >> 5] = (uint32_t)m;
+          L.bits[((j * kFuseThreads + wave * 64) >> 5) + 1] = (uint32_t)(m >> 32);
+        }
+        if (key != 0u && d == pre) L.pub[atomicAdd(&L.misc[0], 1u)] = composite(key, (uint32_t)i);
+      }
+      __syncthreads();
+      const uint32_t nt = L.misc[0];
+      rank_composites(L, nt, need, shift);
+      __syncthreads();
+      const unsigned long long T = *L.T;
+      for (uint32_t t = tid; t < nt; t += kFuseThreads) {
+        const unsigned long long c = L.pub[t];
+        if (c >= T) {
+          const uint32_t i = ~(uint32_t)c;
+          atomicOr(&L.bits[i >> 5], 1u << (i & 31));
+        }
+      }
+      marked = true;
+    } else {
+      local_hist(keys, n, pre, 0, kHist3Bins, 9, L.h);
+      if (wave == 0) find_threshold_bin(L.h, kHist3Bins, need, L.res);
+      __syncthreads();
+      tkey = (pre << 9) | L.res[0];
+      const uint32_t need_eq = need - L.res[1];
+      for (int j = 0; j < iters; ++j) {
+        const int i = j * kFuseThreads + tid;
+        const unsigned long long m = __ballot(i < n && keys[i] == tkey);
+        if (lane == 0) L.cnt[j * kFuseWaves + wave] = (uint32_t)__popcll(m);
+      }
+      __syncthreads();
+      if (wave == 0) scan_counts_wave0_n<4>(L.cnt, iters * kFuseWaves);
+      __syncthreads();
+      for (int j = 0; j < iters; ++j) {
+        const int i = j * kFuseThreads + tid;
+        const bool eq = i < n && keys[i] == tkey;
+        const unsigned long long m = __ballot(eq);
+        if (eq && L.cnt[j * kFuseWaves + wave] + lanes_below(m) == need_eq - 1u) L.misc[3] = (uint32_t)i;
+      }
+      __syncthreads();
+      cut = L.misc[3];
+      has_cut = true;
+    }
+  }
+  if (!marked) {  // every selectable key, or the massive-tie rule: mark by wave ballots
+    for (int j = 0; j < iters; ++j) {
+      const int i = j * kFuseThreads + tid;
+      const uint32_t key = i < n ? keys[i] : 0u;
+      const bool take = key != 0u && (key > tkey || (key == tkey && has_cut && (uint32_t)i <= cut));
+      const unsigned long long m = __ballot(take);
+      if (lane == 0) {
+        L.bits[(j * kFuseThreads + wave * 64) >> 5] = (uint32_t)m;
+        L.bits[((j * kFuseThreads + wave * 64) >> 5) + 1] = (uint32_t)(m >> 32);
+      }
+    }
+  }
+  __syncthreads();
+  // one scan over the bitmap gives every output position
+  const int i0 = 16 * tid;
+  const uint32_t w = L.bits[tid >> 1];
+  uint32_t m = (tid & 1) ? (w >> 16) : (w & 0xffffu);
+  if (i0 >= n) m = 0u;
+  else if (i0 + 16 > n) m &= (1u << (n - i0)) - 1u;
+  uint32_t n_sel;
+  uint32_t rank = block_exclusive_scan((uint32_t)__popc(m), L.scan, &n_sel);
+  while (m) {
+    const int i = i0 + __builtin_ctz(m);
+    m &= m - 1u;
+    if (rank < (uint32_t)k) {
+      orow[rank] = id_of(i);
+      if (srow) srow[rank] = key_score(keys[i]);
+    }
+    ++rank;
+  }
+  for (int p = (int)k_eff + tid; p < k; p += kFuseThreads) {
+    orow[p] = -1;
+    if (srow) srow[p] = -__builtin_inff();
+  }
+  __syncthreads();
 }
 
 struct ChainArgs {
@@ -634,6 +766,7 @@ struct ChainArgs {
   uint32_t* sync;
   char* sel_base;
   char* fine_base;
+  uint32_t* pool_base;       // [batch][kMaxSel][16384]: pool ids, then each layer's keys
 };
 
 template <bool CAND>
@@ -703,99 +836,136 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
     if (v) fine_pending = add_agent(&sel_ws(a.sel_base, b, 0, a.fine_base, a.sync).fine[(fine_lo << 4) + tid], v);
   }
 
-  // ---- the selections: stage 0 over the scanned columns (the pool when chained), then
-  // the Full layer's own top-k and the Reindex layers inside this workgroup's pool entries
+  // ---- the scan's selection (the pool when chained)
   const bool chain = !CAND && (a.own_k > 0 || a.n_re > 0);
-  const int n_stages = chain ? 1 + (a.own_k > 0 ? 1 : 0) + a.n_re : 1;
-  const int lane = tid & 63, wave = tid >> 6, quarter = lane & 3, ent = lane >> 2;
-  int n_pool = 0;
-  uint32_t pool_off = 0;
-  for (int st = 0; st < n_stages; ++st) {
-    const int r = st - 1 - (a.own_k > 0 ? 1 : 0);  // Reindex layer of this stage, if >= 0
-    if (st == 1) {
-      // this workgroup's pool entries, in pool order: their scan keys to the front
+  const SelResult pool = row_select(
+      s_key, c1 - c0, (uint32_t)c0, a.k, nv > 0, long_row, fine_lo, fine_pending,
+      sel_ws(a.sel_base, b, 0, a.fine_base, a.sync), rs, L, wg, nwg,
+      a.idx_out + (size_t)b * a.k, a.score_out ? a.score_out + (size_t)b * a.k : nullptr,
+      [&](int i) { return CAND ? cand_row[c0 + i] : c0 + i; },
+      [&](uint32_t rank, int i) {
+        if (chain) s_plist[rank] = (uint16_t)i;
+      });
+
+  if (chain) {
+    // Every workgroup writes its pool entries' ids and, for every layer, their keys (the
+    // Full layer's own keys, or the Reindex layer's re-scores) at their pool positions;
+    // after one barrier, workgroup L selects layer L's top-k from the whole pool in LDS.
+    const int n_pool = (int)pool.sel;
+    const int own = a.own_k > 0 ? 1 : 0;
+    const int n_layers = own + a.n_re;
+    uint32_t* parr = a.pool_base + (size_t)b * kMaxSel * kFuseMaxCols;
+    uint32_t pending = 0;
+    {
+      uint32_t r[kFuseKeysPerThread];
+#pragma unroll
+      for (int j = 0; j < kFuseKeysPerThread; ++j) {
+        const int i = j * kFuseThreads + tid;
+        r[j] = i < n_pool ? xchg_agent(&parr[pool.offset + i], (uint32_t)(c0 + s_plist[i])) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kFuseKeysPerThread; ++j) pending |= r[j];
+    }
+    const int lane = tid & 63, wave = tid >> 6, quarter = lane & 3, ent = lane >> 2;
+    for (int lyr = 0; lyr < n_layers; ++lyr) {
+      // this layer's keys of the pool entries: written at their pool positions and
+      // counted into the layer's level-1 histogram (the selector's first step)
+      uint32_t* pk = parr + (size_t)(1 + lyr) * kFuseMaxCols + pool.offset;
+      for (int i = tid; i < kHist1Bins; i += kFuseThreads) s_h[i] = 0u;
+      __syncthreads();
+      if (own && lyr == 0) {
+        uint32_t r[kFuseKeysPerThread];
+#pragma unroll
+        for (int j = 0; j < kFuseKeysPerThread; ++j) {
+          const int i = j * kFuseThreads + tid;
+          r[j] = 0u;
+          if (i < n_pool) {
+            const uint32_t key = s_key[s_plist[i]];
+            r[j] = xchg_agent(&pk[i], key);
+            atomicAdd(&s_h[key >> 20], 1u);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kFuseKeysPerThread; ++j) pending |= r[j];
+      } else {
+        // re-score with the Reindex layer's query (the scan's arithmetic)
+        const int rl = lyr - own;
+        bf16x2 q[16];
+        {
+          const uint4* qp =
+              reinterpret_cast<const uint4*>(a.q_re + ((size_t)rl * a.batch + b) * kDIdx) + quarter * 4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = qp[i];
+            q[4 * i + 0] = __builtin_bit_cast(bf16x2, v.x);
+            q[4 * i + 1] = __builtin_bit_cast(bf16x2, v.y);
+            q[4 * i + 2] = __builtin_bit_cast(bf16x2, v.z);
+            q[4 * i + 3] = __builtin_bit_cast(bf16x2, v.w);
+          }
+        }
+        constexpr int kU = 4;  // groups of 16 entries per wave in flight
+        for (int g0 = wave * 16 * kU; g0 < n_pool; g0 += kFuseWaves * 16 * kU) {
+          uint4 w[kU];
+          float sc[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int i = min(g0 + u * 16 + ent, n_pool - 1);
+            const int64_t e = base + c0 + s_plist[i];
+            w[u] = *reinterpret_cast<const uint4*>(a.codes + e * kIdxCodeBytes + quarter * 16);
+            sc[u] = a.scale[e];
+          }
+          uint32_t rr[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            float v = dot32(w[u], q);
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            const int i = g0 + u * 16 + ent;
+            rr[u] = 0u;
+            if (quarter == 0 && i < n_pool) {
+              const uint32_t key = score_key(v * sc[u]);
+              rr[u] = xchg_agent(&pk[i], key);
+              atomicAdd(&s_h[key >> 20], 1u);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kU; ++u) pending |= rr[u];
+        }
+      }
+      __syncthreads();
+      pending |= flush_hist<4>(s_h, kHist1Bins, sel_ws(a.sel_base, b, 1 + lyr, a.fine_base, a.sync).h1);
+    }
+    rs.sync(pending);
+    for (int lyr = wg; lyr < n_layers; lyr += nwg) {
+      const uint32_t* pk = parr + (size_t)(1 + lyr) * kFuseMaxCols;
+      uint32_t* gh = sel_ws(a.sel_base, b, 1 + lyr, a.fine_base, a.sync).h1;
+      const int n_all = (int)pool.total;
       uint32_t kk[kFuseKeysPerThread];
 #pragma unroll
       for (int j = 0; j < kFuseKeysPerThread; ++j) {
         const int i = j * kFuseThreads + tid;
-        kk[j] = i < n_pool ? s_key[s_plist[i]] : 0u;
+        kk[j] = i < n_all ? ld_agent(&pk[i]) : 0u;
+      }
+      uint32_t hh[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hh[u] = ld_agent(&gh[tid + u * kFuseThreads]);
+#pragma unroll
+      for (int j = 0; j < kFuseKeysPerThread; ++j) s_key[j * kFuseThreads + tid] = kk[j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s_h[tid + u * kFuseThreads] = hh[u];
+        st_agent(&gh[tid + u * kFuseThreads], 0u);  // ready for the next call
       }
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kFuseKeysPerThread; ++j) {
-        const int i = j * kFuseThreads + tid;
-        if (i < n_pool) s_key[i] = kk[j];
-      }
-      __syncthreads();
-    }
-    if (r >= 0) {
-      // re-score the pool entries with this layer's query (the scan's arithmetic)
-      bf16x2 q[16];
-      {
-        const uint4* qp =
-            reinterpret_cast<const uint4*>(a.q_re + ((size_t)r * a.batch + b) * kDIdx) + quarter * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 v = qp[i];
-          q[4 * i + 0] = __builtin_bit_cast(bf16x2, v.x);
-          q[4 * i + 1] = __builtin_bit_cast(bf16x2, v.y);
-          q[4 * i + 2] = __builtin_bit_cast(bf16x2, v.z);
-          q[4 * i + 3] = __builtin_bit_cast(bf16x2, v.w);
-        }
-      }
-      constexpr int kU = 4;  // groups of 16 entries per wave in flight
-      for (int g0 = wave * 16 * kU; g0 < n_pool; g0 += kFuseWaves * 16 * kU) {
-        uint4 w[kU];
-        float sc[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int i = min(g0 + u * 16 + ent, n_pool - 1);
-          const int64_t e = base + c0 + s_plist[i];
-          w[u] = *reinterpret_cast<const uint4*>(a.codes + e * kIdxCodeBytes + quarter * 16);
-          sc[u] = a.scale[e];
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          float v = dot32(w[u], q);
-          v += __shfl_xor(v, 1);
-          v += __shfl_xor(v, 2);
-          const int i = g0 + u * 16 + ent;
-          if (quarter == 0 && i < n_pool) s_key[i] = score_key(v * sc[u]);
-        }
-      }
-      __syncthreads();
-    }
-    int kst;
-    int32_t* orow;
-    float* srow;
-    if (st == 0) {
-      kst = a.k;
-      orow = a.idx_out + (size_t)b * a.k;
-      srow = a.score_out ? a.score_out + (size_t)b * a.k : nullptr;
-    } else if (r < 0) {
-      kst = a.own_k;
-      orow = a.own_out + (size_t)b * a.own_k;
-      srow = nullptr;
-    } else {
-      kst = a.re_k;
-      orow = a.re_out + ((size_t)r * a.batch + b) * a.re_k;
-      srow = a.re_score_out ? a.re_score_out + ((size_t)r * a.batch + b) * a.re_k : nullptr;
-    }
-    const SelResult res = row_select(
-        s_key, st == 0 ? c1 - c0 : n_pool, st == 0 ? (uint32_t)c0 : pool_off, kst,
-        st == 0 && nv > 0, st == 0 && long_row, st == 0 ? fine_lo : 0xffffffffu,
-        st == 0 ? fine_pending : 0u,
-        sel_ws(a.sel_base, b, st, a.fine_base, a.sync), rs, L, wg, nwg, orow, srow,
-        [&](int i) {
-          if (st == 0) return CAND ? cand_row[c0 + i] : c0 + i;
-          return c0 + (int)s_plist[i];
-        },
-        [&](uint32_t rank, int i) {
-          if (st == 0 && chain) s_plist[rank] = (uint16_t)i;
-        });
-    if (st == 0) {
-      n_pool = (int)res.sel;
-      pool_off = res.offset;
+      const bool is_own = own && lyr == 0;
+      const int kl = is_own ? a.own_k : a.re_k;
+      int32_t* orow = is_own ? a.own_out + (size_t)b * a.own_k
+                             : a.re_out + ((size_t)(lyr - own) * a.batch + b) * a.re_k;
+      float* srow = is_own || !a.re_score_out
+                        ? nullptr
+                        : a.re_score_out + ((size_t)(lyr - own) * a.batch + b) * a.re_k;
+      wg_select(s_key, n_all, kl, L, orow, srow,
+                [&](int i) { return (int32_t)ld_agent(&parr[i]); });
     }
   }
 
@@ -865,7 +1035,7 @@ bool fused_fits(int batch, int n_cols, int capacity, int* cpw_out, int* nwg_out)
 
 size_t fuse_part_bytes(int batch) {
   return 256 + align_up((size_t)batch * kSyncStride * 4, 256) + (size_t)batch * kMaxSel * kSelBytes +
-         (size_t)batch * kFineBytes;
+         (size_t)batch * kFineBytes + (size_t)batch * kMaxSel * kFuseMaxCols * 4;
 }
 
 struct FuseParts {
@@ -873,6 +1043,7 @@ struct FuseParts {
   uint32_t* sync;
   char* sel_base;
   char* fine_base;
+  uint32_t* pool_base;
 };
 
 FuseParts fuse_carve(void* base, int batch) {
@@ -882,6 +1053,7 @@ FuseParts fuse_carve(void* base, int batch) {
   f.sync = reinterpret_cast<uint32_t*>(p + 256);
   f.sel_base = p + 256 + align_up((size_t)batch * kSyncStride * 4, 256);
   f.fine_base = f.sel_base + (size_t)batch * kMaxSel * kSelBytes;
+  f.pool_base = reinterpret_cast<uint32_t*>(f.fine_base + (size_t)batch * kFineBytes);
   return f;
 }
 
@@ -935,6 +1107,7 @@ ChainArgs base_args(const uint16_t* q_idx, const uint8_t* codes, const float* sc
   a.sync = f.sync;
   a.sel_base = f.sel_base;
   a.fine_base = f.fine_base;
+  a.pool_base = f.pool_base;
   return a;
 }
 
