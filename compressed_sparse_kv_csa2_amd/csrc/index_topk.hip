@@ -148,6 +148,7 @@ struct SelLds {
   uint32_t* misc;              // [4]
   unsigned long long* T;       // [1]
   uint32_t* bits;              // [512] selection bitmap over the local index
+  uint32_t* bits2;             // [512] keys inside the threshold bin
 };
 
 // One selection's global arrays for this row.
@@ -159,6 +160,7 @@ struct SelWs {
   unsigned long long* pub;     // [kPubSlots]: workgroup w owns [w * cap, (w + 1) * cap)
   uint32_t* fine;              // [4096][16] counts inside the scan's window (stage 0)
   uint32_t* hint;              // [1] b1 + 1 of the previous call (0: none)
+  uint32_t* above;             // [1] keys above the scan's window (stage 0)
 };
 
 __device__ __forceinline__ SelWs sel_ws(char* sel_base, int row, int sel, char* fine_base,
@@ -168,7 +170,7 @@ __device__ __forceinline__ SelWs sel_ws(char* sel_base, int row, int sel, char* 
                reinterpret_cast<uint32_t*>(p + kSelH3), reinterpret_cast<uint32_t*>(p + kSelCnt),
                reinterpret_cast<unsigned long long*>(p + kSelPub),
                reinterpret_cast<uint32_t*>(fine_base + (size_t)row * kFineBytes),
-               sync + (size_t)row * kSyncStride + 2};
+               sync + (size_t)row * kSyncStride + 2, sync + (size_t)row * kSyncStride + 3};
 }
 
 // Adds the non-empty bins of an LDS histogram of N * 1,024 bins (N = 1: 512 bins) to a
@@ -237,39 +239,74 @@ __device__ uint32_t hist_select(const uint32_t* h, uint32_t k, uint32_t* s_scan,
   return total;
 }
 
+// One pass of wave ballots over the 16,384 LDS keys (wave w covers local indices
+// [1024 w, 1024 w + 1024); keys past the row's end are 0): L.bits marks key > top and,
+// when `inside`, L.bits2 marks lo <= key <= top (1 <= lo).  Every key is loaded before
+// the first ballot, and lane 0 writes each wave's words four iterations at a time.
+// Whole workgroup; ends with a barrier.
+__device__ __forceinline__ void mark_pass(const uint32_t* keys, uint32_t lo, uint32_t top,
+                                          bool inside, const SelLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t* kw = keys + wave * (kFuseMaxCols / kFuseWaves);
+  uint32_t kv[kFuseKeysPerThread];
+#pragma unroll
+  for (int j = 0; j < kFuseKeysPerThread; ++j) kv[j] = kw[j * 64 + lane];
+  uint4* ba = reinterpret_cast<uint4*>(L.bits) + wave * (kFuseKeysPerThread / 2);
+  uint4* bi = reinterpret_cast<uint4*>(L.bits2) + wave * (kFuseKeysPerThread / 2);
+#pragma unroll
+  for (int g = 0; g < kFuseKeysPerThread / 4; ++g) {
+    uint32_t wa[8], wi[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t key = kv[4 * g + u];
+      const unsigned long long ma = __ballot(key > top);
+      const unsigned long long mi = __ballot(inside && key - lo <= top - lo);
+      wa[2 * u] = (uint32_t)ma;
+      wa[2 * u + 1] = (uint32_t)(ma >> 32);
+      wi[2 * u] = (uint32_t)mi;
+      wi[2 * u + 1] = (uint32_t)(mi >> 32);
+    }
+    if (lane == 0) {
+      ba[2 * g] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+      ba[2 * g + 1] = make_uint4(wa[4], wa[5], wa[6], wa[7]);
+      bi[2 * g] = make_uint4(wi[0], wi[1], wi[2], wi[3]);
+      bi[2 * g + 1] = make_uint4(wi[4], wi[5], wi[6], wi[7]);
+    }
+  }
+  __syncthreads();
+}
+
 // Publishes this workgroup's count of keys above the bin (key >> shift > pre; every
 // non-zero key when `all`) and the composites of its keys inside it (key >> shift == pre,
 // at most `cap` of them; the count says how many there were).  The keys above the bin are
 // also marked in L.bits (local index i -> bit i; every word below n_local is written).
-// Returns the combined values of the atomics (for RowSync::sync).
+// One pass of wave ballots marks both sets; the composites are then compacted in position
+// order from the second bitmap.  Returns the combined values of the atomics (for
+// RowSync::sync).
 __device__ __forceinline__ uint32_t publish(const uint32_t* keys, int n_local, uint32_t pos0,
                                             uint32_t pre, int shift, bool all, int cap,
                                             uint32_t* cnt_slot, unsigned long long* pub,
                                             const SelLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) L.misc[0] = 0u;
-  __syncthreads();
-  const int iters = (n_local + kFuseThreads - 1) / kFuseThreads;
-  uint32_t n_above = 0;
-  for (int j = 0; j < iters; ++j) {
-    const int i = j * kFuseThreads + tid;
-    const uint32_t key = i < n_local ? keys[i] : 0u;
-    const uint32_t d = key >> shift;
-    const bool above = key != 0u && (all || d > pre);
-    const unsigned long long m = __ballot(above);
-    if (lane == 0) {
-      L.bits[(j * kFuseThreads + wave * 64) >> 5] = (uint32_t)m;
-      L.bits[((j * kFuseThreads + wave * 64) >> 5) + 1] = (uint32_t)(m >> 32);
-    }
-    n_above += above ? 1u : 0u;
-    if (key != 0u && !above && d == pre) {
-      const uint32_t slot = atomicAdd(&L.misc[0], 1u);
-      if (slot < (uint32_t)cap) L.pub[slot] = composite(key, pos0 + (uint32_t)i);
-    }
+  const int tid = threadIdx.x;
+  // above: key > top; inside: lo <= key <= top (key 0 is never either)
+  const uint32_t lo = all ? 1u : max(pre << shift, 1u);
+  const uint32_t top = all ? 0u : (pre << shift) + ((1u << shift) - 1u);
+  mark_pass(keys, lo, top, !all, L);
+  // thread t owns local indices [16t, 16t + 16)
+  const uint32_t wa = L.bits[tid >> 1], wi = L.bits2[tid >> 1];
+  uint32_t ma = (tid & 1) ? (wa >> 16) : (wa & 0xffffu);
+  uint32_t mi = (tid & 1) ? (wi >> 16) : (wi & 0xffffu);
+  uint32_t tot;
+  uint32_t slot = block_exclusive_scan(((uint32_t)__popc(ma) << 16) | (uint32_t)__popc(mi), L.scan,
+                                       &tot) & 0xffffu;
+  const uint32_t n_pub = tot & 0xffffu, total_above = tot >> 16;
+  while (mi) {
+    const uint32_t i = 16u * tid + (uint32_t)__builtin_ctz(mi);
+    mi &= mi - 1u;
+    if (slot < (uint32_t)cap) L.pub[slot] = composite(keys[i], pos0 + i);
+    ++slot;
   }
-  uint32_t total_above;
-  block_exclusive_scan(n_above, L.scan, &total_above);  // barrier: L.misc[0], L.pub complete
-  const uint32_t n_pub = L.misc[0];
+  __syncthreads();
   uint32_t pending = 0;
   if (tid < (int)min(n_pub, (uint32_t)cap)) pending |= xchg_agent(&pub[tid], L.pub[tid]);
   if (tid == kFuseThreads - 1)
@@ -362,41 +399,110 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
   pending |= flush_hist<4>(L.h, kHist1Bins, g.h1);
   rs.sync(pending);
   pending = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) L.h[tid + i * kFuseThreads] = ld_agent(&g.h1[tid + i * kFuseThreads]);
-  __syncthreads();
-  const uint32_t total = hist_select<4>(L.h, (uint32_t)k, L.scan, L.res);
-  const uint32_t k_eff = min((uint32_t)k, total);
-  const bool all = k_eff == total;  // the same in every workgroup of the row
-  uint32_t pre = 0, need = 0;       // need: keys still to take at or below the bin
+  uint32_t k_eff = (uint32_t)k;
+  bool all = false;           // the same in every workgroup of the row
+  uint32_t pre = 0, need = 0;  // need: keys still to take at or below the bin
   uint32_t b1 = 0, need1 = 0;
   int shift = 20;
   bool pub_now = true;  // publish now (always when every key is taken)
-  if (!all) {
-    b1 = pre = L.res[0];
-    need1 = need = k_eff - L.res[1];
-    pub_now = L.h[pre] <= (uint32_t)kPubMax;
-    if (keep_hint && wg == 0 && tid == 0) st_agent(g.hint, b1 + 1u);  // for the next call
-    if (!pub_now && fine_on && b1 - fine_lo < (uint32_t)kFineWin) {
-      // the fine counts of b1 are complete: the sub-bin of the need-th key
-      __syncthreads();
-      if (tid < kFineSub) L.h[tid] = ld_agent(&g.fine[(b1 << 4) + tid]);
-      __syncthreads();
-      if (wave == 0) {
-        const uint32_t c = lane < kFineSub ? L.h[kFineSub - 1 - lane] : 0u;  // from the top
-        const uint32_t incl = wave_incl_scan(c);
-        if (lane < kFineSub && incl - c < need && need <= incl) {
-          L.res[0] = (uint32_t)(kFineSub - 1 - lane);
-          L.res[1] = incl - c;
-          L.res[2] = c;
+  bool fast = false;    // the k-th key's fine sub-bin came from the scan's window
+  if (fine_on) {
+    // the window's 256 fine counts (index (bin - fine_lo) * 16 + sub-bin) and the keys
+    // above it: when the k-th key falls inside and its sub-bin is small enough, level 1
+    // and its histogram are skipped
+    if (tid < kFineWin * kFineSub) L.h[tid] = ld_agent(&g.fine[(fine_lo << 4) + tid]);
+    if (tid == kFineWin * kFineSub) L.misc[2] = ld_agent(g.above);
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t above = L.misc[2];
+      const int hi = kFineWin * kFineSub - 4 * lane;  // lane 0 owns the top counts
+      uint32_t c4[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c4[j] = L.h[hi - 1 - j];
+        sum += c4[j];
+      }
+      const uint32_t incl = wave_incl_scan(sum);
+      const uint32_t win = __builtin_amdgcn_readlane(incl, 63);
+      const bool hit = above < (uint32_t)k && (uint32_t)k - above <= win;
+      uint32_t idx = 0u, before = 0u;  // the sub-bin and the keys above it (absolute)
+      if (hit) {
+        const uint32_t want = (uint32_t)k - above;
+        uint32_t acc = incl - sum;
+        bool mine = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!mine && acc < want && want <= acc + c4[j]) {
+            mine = true;
+            idx = (uint32_t)(hi - 1 - j);
+            before = above + acc;
+          }
+          acc += c4[j];
+        }
+        const unsigned long long owner = __ballot(mine);
+        const int ol = (int)__builtin_ctzll(owner);
+        idx = __builtin_amdgcn_readlane(idx, ol);
+        before = __builtin_amdgcn_readlane(before, ol);
+        // keys above the sub-bin's level-1 bin (for the massive-tie rule)
+        const uint32_t bin_top = ((idx >> 4) + 1u) << 4;
+        uint32_t part = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part += (uint32_t)(hi - 1 - j) >= bin_top ? c4[j] : 0u;
+        const uint32_t above_bin = above + __builtin_amdgcn_readlane(wave_incl_scan(part), 63);
+        if (lane == 0) {
+          L.res[0] = idx;
+          L.res[1] = before;
+          L.res[2] = L.h[idx];
+          L.res[3] = above_bin;
         }
       }
-      __syncthreads();
-      if (L.res[2] <= (uint32_t)kPubMax) {
-        pre = (b1 << 4) | L.res[0];
-        need -= L.res[1];
-        shift = 16;
-        pub_now = true;
+      if (lane == 0) L.misc[1] = hit ? 1u : 0u;
+    }
+    __syncthreads();
+    if (L.misc[1] != 0u && L.res[2] <= (uint32_t)kPubMax) {
+      fast = true;
+      b1 = fine_lo + (L.res[0] >> 4);
+      need1 = (uint32_t)k - L.res[3];
+      pre = (b1 << 4) | (L.res[0] & 15u);
+      need = (uint32_t)k - L.res[1];
+      shift = 16;
+      if (keep_hint && wg == 0 && tid == 0) st_agent(g.hint, b1 + 1u);  // for the next call
+    }
+    __syncthreads();  // L.h, L.res and L.misc are read before they are rewritten
+  }
+  if (!fast) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.h[tid + i * kFuseThreads] = ld_agent(&g.h1[tid + i * kFuseThreads]);
+    __syncthreads();
+    const uint32_t total = hist_select<4>(L.h, (uint32_t)k, L.scan, L.res);
+    k_eff = min((uint32_t)k, total);
+    all = k_eff == total;
+    if (!all) {
+      b1 = pre = L.res[0];
+      need1 = need = k_eff - L.res[1];
+      pub_now = L.h[pre] <= (uint32_t)kPubMax;
+      if (keep_hint && wg == 0 && tid == 0) st_agent(g.hint, b1 + 1u);  // for the next call
+      if (!pub_now && fine_on && b1 - fine_lo < (uint32_t)kFineWin) {
+        // the fine counts of b1 are complete: the sub-bin of the need-th key
+        __syncthreads();
+        if (tid < kFineSub) L.h[tid] = ld_agent(&g.fine[(b1 << 4) + tid]);
+        __syncthreads();
+        if (wave == 0) {
+          const uint32_t c = lane < kFineSub ? L.h[kFineSub - 1 - lane] : 0u;  // from the top
+          const uint32_t incl = wave_incl_scan(c);
+          if (lane < kFineSub && incl - c < need && need <= incl) {
+            L.res[0] = (uint32_t)(kFineSub - 1 - lane);
+            L.res[1] = incl - c;
+            L.res[2] = c;
+          }
+        }
+        __syncthreads();
+        if (L.res[2] <= (uint32_t)kPubMax) {
+          pre = (b1 << 4) | L.res[0];
+          need -= L.res[1];
+          shift = 16;
+          pub_now = true;
+        }
       }
     }
   }
@@ -412,6 +518,7 @@ __device__ __forceinline__ SelResult row_select(const uint32_t* keys, int n_loca
   if (wg == 0) {
     for (int i = tid; i < kHist1Bins; i += kFuseThreads) st_agent(&g.h1[i], 0u);
     if (fine_on && tid < kFineWin * kFineSub) st_agent(&g.fine[(fine_lo << 4) + tid], 0u);
+    if (fine_on && tid == kFineWin * kFineSub) st_agent(g.above, 0u);
   }
 
   // ---- level 2 (when b1 held too many keys): the bin (b1, b2), then publish
@@ -651,25 +758,20 @@ __device__ __forceinline__ void wg_select(const uint32_t* keys, int n, int k, co
       __syncthreads();
     }
     if (small) {
-      // one pass: the keys above the bin into the bitmap, the bin's composites into L.pub
-      if (tid == 0) {
-        L.misc[0] = 0u;
-        *L.T = ~0ull;
+      // one pass of ballots: the keys above the bin into L.bits, the bin's keys into
+      // L.bits2; then the bin's composites are compacted into L.pub
+      if (tid == 0) *L.T = ~0ull;
+      mark_pass(keys, max(pre << shift, 1u), (pre << shift) + ((1u << shift) - 1u), true, L);
+      const uint32_t wi = L.bits2[tid >> 1];
+      uint32_t mi = (tid & 1) ? (wi >> 16) : (wi & 0xffffu);
+      uint32_t nt;
+      uint32_t slot = block_exclusive_scan((uint32_t)__popc(mi), L.scan, &nt);
+      while (mi) {
+        const uint32_t i = 16u * tid + (uint32_t)__builtin_ctz(mi);
+        mi &= mi - 1u;
+        L.pub[slot++] = composite(keys[i], i);
       }
       __syncthreads();
-      for (int j = 0; j < iters; ++j) {
-        const int i = j * kFuseThreads + tid;
-        const uint32_t key = i < n ? keys[i] : 0u;
-        const uint32_t d = key >> shift;
-        const unsigned long long m = __ballot(key != 0u && d > pre);
-        if (lane == 0) {
-          L.bits[(j * kFuseThreads + wave * 64) >> 5] = (uint32_t)m;
-          L.bits[((j * kFuseThreads + wave * 64) >> 5) + 1] = (uint32_t)(m >> 32);
-        }
-        if (key != 0u && d == pre) L.pub[atomicAdd(&L.misc[0], 1u)] = composite(key, (uint32_t)i);
-      }
-      __syncthreads();
-      const uint32_t nt = L.misc[0];
       rank_composites(L, nt, need, shift);
       __syncthreads();
       const unsigned long long T = *L.T;
@@ -781,8 +883,10 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
   __shared__ uint32_t s_res[4];
   __shared__ uint32_t s_misc[4];
   __shared__ unsigned long long s_T;
-  __shared__ uint32_t s_bits[kFuseMaxCols / 32];
+  __shared__ __align__(16) uint32_t s_bits[kFuseMaxCols / 32];
+  __shared__ __align__(16) uint32_t s_bits2[kFuseMaxCols / 32];
   __shared__ uint32_t s_fine[kFineWin * kFineSub];
+  __shared__ __align__(16) uint16_t s_qre[CAND ? 1 : kMaxReindex * kDIdx];  // Reindex queries
   const int b = a.row0 + (int)blockIdx.y, wg = blockIdx.x, nwg = gridDim.x;
   const int tid = threadIdx.x;
   const int nv = min(a.n_valid[b], a.n_cols);
@@ -800,6 +904,7 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
   L.misc = s_misc;
   L.T = &s_T;
   L.bits = s_bits;
+  L.bits2 = s_bits2;
 
   // ---- score the columns [c0, c1): keys into LDS, level-1 histogram in LDS, and the fine
   // counts of the window around the previous call's level-1 bin (long rows)
@@ -810,6 +915,12 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
     if (h != 0u) fine_lo = min(h - 1u >= 8u ? h - 9u : 0u, (uint32_t)(kHist1Bins - kFineWin));
   }
   const bool fine_on = fine_lo != 0xffffffffu;
+  if (!CAND && tid < a.n_re * (kDIdx / 8)) {  // read long before the re-scores use them
+    const int rl = tid / (kDIdx / 8), part = tid % (kDIdx / 8);
+    reinterpret_cast<uint4*>(s_qre)[tid] =
+        reinterpret_cast<const uint4*>(a.q_re + ((size_t)rl * a.batch + b) * kDIdx)[part];
+  }
+  uint32_t n_above_win = 0;  // this thread's keys above the window
   for (int i = tid; i < kFuseMaxCols; i += kFuseThreads) s_key[i] = 0u;
   if (nv > 0) {
     scan_columns<CAND, kFuseThreads>(
@@ -817,6 +928,7 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
         [&]() {
           for (int i = tid; i < kHist1Bins; i += kFuseThreads) s_h[i] = 0u;
           if (tid < kFineWin * kFineSub) s_fine[tid] = 0u;
+          if (tid == 0) s_misc[3] = 0u;
         },
         [&](int col, float score, bool valid) {
           const uint32_t key = valid ? score_key(score) : 0u;
@@ -826,14 +938,20 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
             const uint32_t cw = (key >> 20) - fine_lo;
             if (fine_on && cw < (uint32_t)kFineWin)
               atomicAdd(&s_fine[(cw << 4) | ((key >> 16) & 15u)], 1u);
+            n_above_win += (fine_on && (key >> 20) >= fine_lo + kFineWin) ? 1u : 0u;
           }
         });
+    if (fine_on) {
+      const uint32_t wsum = wave_incl_scan(n_above_win);
+      if ((tid & 63) == 63 && wsum) atomicAdd(&s_misc[3], wsum);
+    }
     __syncthreads();
   }
   uint32_t fine_pending = 0;
-  if (fine_on && nv > 0 && tid < kFineWin * kFineSub) {
-    const uint32_t v = s_fine[tid];
-    if (v) fine_pending = add_agent(&sel_ws(a.sel_base, b, 0, a.fine_base, a.sync).fine[(fine_lo << 4) + tid], v);
+  if (fine_on && nv > 0 && tid <= kFineWin * kFineSub) {
+    const SelWs g0 = sel_ws(a.sel_base, b, 0, a.fine_base, a.sync);
+    const uint32_t v = tid < kFineWin * kFineSub ? s_fine[tid] : s_misc[3];
+    if (v) fine_pending = add_agent(tid < kFineWin * kFineSub ? &g0.fine[(fine_lo << 4) + tid] : g0.above, v);
   }
 
   // ---- the scan's selection (the pool when chained)
@@ -892,8 +1010,7 @@ __global__ __launch_bounds__(kFuseThreads) void k_index_topk(ChainArgs a) {
         const int rl = lyr - own;
         bf16x2 q[16];
         {
-          const uint4* qp =
-              reinterpret_cast<const uint4*>(a.q_re + ((size_t)rl * a.batch + b) * kDIdx) + quarter * 4;
+          const uint4* qp = reinterpret_cast<const uint4*>(s_qre + rl * kDIdx) + quarter * 4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint4 v = qp[i];

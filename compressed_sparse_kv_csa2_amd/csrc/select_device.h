@@ -50,8 +50,9 @@ inline __device__ void find_threshold_bin(const uint32_t* h, int nbins, uint32_t
 }
 
 // Block-wide exclusive scan of one u32 per thread; returns the exclusive prefix and
-// stores the block total in *total.  `scratch` holds >= 16 u32 of LDS.  Two barriers; ends
-// with one (scratch is free again).
+// stores the block total in *total.  `scratch` holds >= 16 u32 of LDS.  Each wave scans the
+// per-wave totals itself (one LDS read per lane, then DPP), so no wave walks the others'
+// totals one by one.  Two barriers; ends with one (scratch is free again).
 inline __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -59,13 +60,10 @@ inline __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, u
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
-  for (int w = 0; w < nwaves; ++w) {
-    const uint32_t t = scratch[w];
-    before += w < wave ? t : 0u;
-    tot += t;
-  }
-  *total = tot;
+  const uint32_t wincl = wave_incl_scan(lane < nwaves ? scratch[lane] : 0u);
+  const int src = __builtin_amdgcn_readfirstlane(wave > 0 ? wave - 1 : 0);
+  const uint32_t before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)wincl, src) : 0u;
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)wincl, 63);
   __syncthreads();
   return before + incl - v;
 }

@@ -71,14 +71,16 @@ FINE_BYTES = 4096 * 16 * 4                                       # fine counts p
 
 
 def ws_clean(ws, B):
-    """Status word 0; barrier counters, every selection's histograms and the fine window
-    counts back to zero.  Layout: status 256 B | per row 32 u32 (arrivals, departures,
-    fine-window hint), 256-aligned | B x 6 selection blocks | B x fine counts."""
+    """Status word 0; barrier counters, the above-window count, every selection's
+    histograms and the fine window counts back to zero.  Layout: status 256 B | per row
+    32 u32 (arrivals, departures, fine-window hint, keys above the window), 256-aligned |
+    B x 6 selection blocks | B x fine counts."""
     w = h(ws)
     assert w[:4].view(np.uint32)[0] == 0, "a row barrier gave up waiting"
     sync = -(-B * 32 * 4 // 256) * 256
     rows = w[256:256 + B * 128].view(np.uint32).reshape(B, 32)
     assert not rows[:, :2].any(), "barrier counters not reset"
+    assert not rows[:, 3].any(), "above-window count not reset"
     base = 256 + sync
     for blk in range(B * MAX_SEL):
         o = base + blk * SEL_BYTES
@@ -223,6 +225,29 @@ def test_fine_window_hint_hits_and_misses():
     ws_clean(ws, 2)
     hint = h(ws)[256:256 + 2 * 128].view(np.uint32).reshape(2, 32)[:, 2]
     assert np.all(hint > 0), "the hint was not kept"
+
+
+def test_fine_window_fast_path_with_clustered_ties():
+    """Repeated calls on one workspace take the pool's threshold straight from the fine
+    window.  Five hundred copies of the k-th entry inside one workgroup's columns put more
+    tied keys in the threshold sub-bin than a workgroup may publish, so the tie rule runs
+    from the window's bin; every call stays exact."""
+    log("index_topk fine-window fast path, clustered ties")
+    n, k = 300_000, 16384
+    cache = synth.make_entries([n], seed=44, device=DEV)
+    q = synth.make_index_queries(1, 44, device=DEV)
+    s = oracle.index_scores(h(q)[0], h(cache.idx_codes), h(cache.idx_scale))
+    src = int(np.argsort(-s, kind="stable")[k - 1])
+    dst = torch.arange(3 * 2048 + 100, 3 * 2048 + 600, device=DEV)
+    cache.idx_codes[dst] = cache.idx_codes[src].clone()
+    cache.idx_scale[dst] = cache.idx_scale[src].clone()
+    ws = csa2.index_topk_workspace(1, n, k)
+    for _ in range(3):
+        idx, so, _ = fused(cache, q, n, k, ws=ws)
+        _, idx2, so2 = two_step(cache, q, n, k)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx2) and torch.equal(so, so2)
+    ws_clean(ws, 1)
 
 
 def test_long_decode_pool_and_reindex_at_full_size():
