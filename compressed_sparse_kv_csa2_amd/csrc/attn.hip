@@ -10,193 +10,214 @@
 // ("DeepSeek V4.1 Flash 深度解析", part-4 entry on FP4 in the KV cache).
 //
 // All 16 heads share every entry, so per query the work is a dense [16 x 512] x [512 x n]
-// contraction (about 114 flop per gathered byte) and runs on the matrix cores:
-//   * every dequantised value is exact in bf16 (an E2M1 magnitude has at most 2 significant
-//     bits, an E4M3 scale at most 4, so the product has at most 6; window values have 4),
-//     so q . v on v_mfma_f32_16x16x32_bf16 has exact products and fp32 sums;
-//   * p . v takes p as the sum of two bf16 halves (hi = p truncated, lo = bf16(p - hi)),
-//     two MFMAs, relative error about 2^-16, fp32 sums.
-// One 256-thread workgroup (4 waves) per (row, split) walks its list positions (the k
-// selected entries, then the window rows) in chunks of 32:
-//   gather   thread (wave w, lane l) loads dims 8l..8l+7 of positions 8w..8w+7 (4 code bytes
-//            + 1 scale byte, or 8 window bytes each), dequantises them, and writes them to
-//            LDS twice: row-major (position x dims, B operand of q . v) and, after an 8x8
-//            register transpose, dims x positions (B operand of p . v).  Both layouts are
-//            XOR-swizzled so that the 16-byte writes and the operand reads hit distinct banks;
-//   q . v    wave w: entries 16(w&1)..+15 over half of the 512 dims (8 MFMAs); the two
-//            halves are added in the softmax step;
-//   softmax  16 lanes per head: running max and sum, rescale factor, p split into hi/lo;
-//   p . v    wave w: 128 output dims (8 tiles of 16), 2 MFMAs each.
-// Decode uses several splits per row; each leaves (max, sum, acc[16][512]) in the
-// workspace and k_attn_merge combines them by log-sum-exp.  The prefill chunk has many
-// rows and runs one split per row, writing its output directly.  exp2 with log2(e)
-// folded into the scale.
+// contraction and runs on the matrix cores in fp16:
+//   * every dequantised value is exact in fp16: an E2M1 magnitude has at most 2
+//     significant bits and an E4M3 scale at most 4, so the product has at most 6 and lies
+//     in [2^-10, 2688]; window values are E4M3 themselves.  gfx950 converts FP4 / FP8 to
+//     fp16 pairs directly and the scale is one packed fp16 multiply per pair;
+//   * q is scaled per head by a power of two so that its largest element lies in
+//     [2^14, 2^15) and rounded to fp16 (exact unless an element is below 2^-28 of its
+//     head's largest); the power of two is folded back into the softmax scale.  q . v on
+//     v_mfma_f32_16x16x32_f16 then has exact products and fp32 sums;
+//   * p . v takes p as the sum of two fp16 halves (hi = fp16(p), lo = fp16(p - hi)), two
+//     v_mfma_f32_16x16x16_f16, relative error about 2^-22, fp32 sums.
+// Work split: one 128-thread workgroup (2 waves) per (row, split) walks the split's
+// 16-position segments of the row's list (the k selected entries, then the window rows);
+// wave w owns dims 256 w .. 256 w + 255 of every segment:
+//   gather   lane (position n, dim group g) loads dims 256 w + 64 g .. + 63 of position n
+//            (32 code bytes + 4 scale bytes, or 64 window bytes), one segment ahead;
+//   q . v    8 k-steps; k-step s of dim group g covers dims 256 w + 64 g + 8 s .. + 7, so
+//            each lane dequantises exactly its own loaded bytes into the B operand; the two
+//            waves' partial scores meet in LDS and are added in the same order by both;
+//   softmax  per head over the segment's 16 positions (DPP row reductions), computed by
+//            both waves alike; the running max moves only when a score exceeds it by more
+//            than 2^8, so rescaling the accumulators is rare;
+//   p . v    the dequantised half-segment is also written to the wave's LDS tile (positions
+//            x dims, XOR-swizzled) and read back transposed with ds_read_b64_tr_b16 as the
+//            B operand of 16 output tiles of 16 dims; p (hi from wave 0, lo from wave 1)
+//            goes through LDS the same way.  Two workgroup barriers per segment.
+// A decode row with several splits leaves (max, sum, acc[16][512]) per split in the
+// workspace and k_attn_merge combines them by log-sum-exp.  exp2 with log2(e) folded into
+// the scale.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
+#include <math.h>
+
 namespace csa2 {
 
-constexpr int kAttnThreads = 256;
-constexpr int kChunk = 32;                         // list positions per chunk
-constexpr int kMaxSplits = 64;                     // splits per decode row
-constexpr int kIdxWin = 1024;                      // list positions whose ids sit in LDS
-constexpr int kPart = 2 * kHeads + kHeads * kDKv;  // floats per split: m[16], l[16], acc
-
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-int attn_chunks(int k) { return (k + kSwa + kChunk - 1) / kChunk; }
-int attn_splits(int k) { return min(attn_chunks(k), kMaxSplits); }
+constexpr int kAW = 2;                       // waves per workgroup, one per half of the dims
+constexpr int kAThreads = 64 * kAW;
+constexpr int kHalf = kDKv / kAW;            // dims per wave
+constexpr int kHalfTiles = kHalf / 16;       // output tiles of 16 dims per wave
+constexpr int kSeg = 16;                     // list positions per wave step
+constexpr int kIdxStage = 1024;              // list positions whose entry ids sit in LDS
+constexpr int kMaxSplits = 64;               // splits per decode row
+constexpr int kSplitSlots = 1024;            // decode workgroups aimed for (4 per CU)
+constexpr int kPart = 2 * kHeads + kHeads * kDKv;  // floats per split: m[16], l[16], acc
+constexpr float kRescale = 8.0f;             // log2 headroom before the running max moves
+
+int attn_segments(int k) { return (k + kSwa + kSeg - 1) / kSeg; }
+int attn_splits(int k) { return min(attn_segments(k), kMaxSplits); }
+
+// Decode segments per split.  Each extra segment in a split adds about one gather latency
+// (~1.6 us: the next segment's loads are issued one segment ahead), while each split's
+// partial (16 x 512 fp32) is written and read back once (~0.5 us of the device's
+// bandwidth per 40 splits and row); the sum is smallest near sqrt(rows x segments / 123)
+// segments per split (1 for 4 rows of 640 positions, 2 for 16, 3 for 32).
+static int attn_segs_per_split(int rows, int k) {
+  const int segs = attn_segments(k);
+  int sps = max(1, (int)lround(sqrt((double)rows * segs / 123.0)));
+  sps = max(sps, (int)(((long long)rows * segs + kSplitSlots - 1) / kSplitSlots));
+  sps = max(sps, (segs + kMaxSplits - 1) / kMaxSplits);
+  return min(sps, segs);
+}
 
 size_t attn_ws_bytes(int rows, int k) {
   return align_up((size_t)rows * attn_splits(k) * kPart * sizeof(float), 256);
 }
 
-// ---- LDS layouts (16-byte blocks)
-// V row-major: 32 position rows x 64 blocks (8 dims each); block c of row p at c ^ (p & 15).
-__device__ __forceinline__ int v_blk(int p, int c) { return p * 64 + (c ^ (p & 15)); }
-// V transposed: 512 dim rows x 4 blocks (8 positions each).  Dim d lives in row
-// R = (d & ~15) | ((d + (d >> 4)) & 15), block kb at kb ^ ((R >> 2) & 3).
-__device__ __forceinline__ int vt_blk(int d, int kb) {
-  const int R = (d & ~15) | ((d + (d >> 4)) & 15);
-  return R * 4 + (kb ^ ((R >> 2) & 3));
-}
-// P (either half): 16 head rows x 4 blocks (8 positions each); block kb of head h at
-// kb ^ ((h >> 2) & 3).
-__device__ __forceinline__ int p_blk(int h, int kb) { return h * 4 + (kb ^ ((h >> 2) & 3)); }
+// ---- LDS tiles
+// V of one wave's half of a segment: 16 position rows x 32 blocks of 8 fp16 (512 B per
+// row); block b of row r at b ^ vswz(r).  Conflict-free for the 16-byte row writes (16
+// rows, one block) and for the transposed 8-byte reads (4 rows x 2 blocks per 16 lanes).
+__device__ __forceinline__ int vswz(int r) { return ((r << 1) & 14) | ((r >> 3) & 1); }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+__device__ __forceinline__ f16x4 tr_read(const f16* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(f16x4, v);
 }
 
-// 8 E2M1 codes (one dword) times one scale -> 8 bf16 (exact), element i from nibble i.
-__device__ __forceinline__ uint4 fp4x8_scaled_bf16(uint32_t w, float s) {
-  const f32x2 a = fp4x2<0>(w), b = fp4x2<1>(w), c = fp4x2<2>(w), d = fp4x2<3>(w);
-  return make_uint4(pack_bf16(a.x * s, a.y * s), pack_bf16(b.x * s, b.y * s),
-                    pack_bf16(c.x * s, c.y * s), pack_bf16(d.x * s, d.y * s));
+// DPP reductions over the 16 lanes of a row (xor 1, xor 2, half-row mirror, row mirror).
+template <bool MAX>
+__device__ __forceinline__ float row16(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false)));
+  return v;
 }
 
-// 8 E4M3 bytes -> 8 bf16 (exact).
-__device__ __forceinline__ uint4 fp8x8_bf16(uint2 w) {
-  const f32x2 a = fp8x2<false>(w.x), b = fp8x2<true>(w.x);
-  const f32x2 c = fp8x2<false>(w.y), d = fp8x2<true>(w.y);
-  return make_uint4(pack_bf16(a.x, a.y), pack_bf16(b.x, b.y), pack_bf16(c.x, c.y),
-                    pack_bf16(d.x, d.y));
-}
-
-// Raw bytes of the thread's 8 positions: main bit pp set = main entry (x: 4 code bytes,
-// y: the aligned scale dword holding the lane's scale byte); window bit = window row (x, y:
-// 8 E4M3 bytes); neither = nothing (x, y read from a window row and ignored).
-struct GatherRaw {
-  uint2 r[8];
-  uint32_t main_bits, win_bits;
+// Raw bytes of one lane's 64 dims of a position in a segment: main entry (u[0..1] = 32
+// code bytes, sc = its 4 scale bytes), window row (u[0..3] = 64 bytes), or nothing.  Every
+// lane issues the same five loads whatever its kind (unused ones re-read a valid
+// address), so the compiler can keep later segments' loads in flight.
+struct Raw {
+  uint4 u[4];
+  uint32_t sc;
+  int kind;  // 0 nothing, 1 main entry, 2 window row
 };
 
-// Issues the loads of positions p0 + 8w .. p0 + 8w + 7, dims 8l .. 8l + 7: exactly two dword
-// loads per position whatever its kind (the source address is selected, not branched on), so
-// the loads of later chunks stay in flight while an earlier chunk is used.  Entry ids come
-// from the LDS window s_idx, which holds list positions idx_base onward.
-__device__ __forceinline__ GatherRaw gather_issue(int p0, int w, int l, int k, int n_pos,
-                                                  const int32_t* s_idx, int idx_base, int64_t base,
-                                                  const uint8_t* kv_codes, const uint8_t* kv_scale,
-                                                  const uint8_t* rows) {
-  GatherRaw g;
-  g.main_bits = 0u;
-  g.win_bits = 0u;
-  const uint8_t* pa[8];
-  const uint8_t* pb[8];
-#pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
-    const int pos = p0 + 8 * w + pp;
-    const int j = pos < k ? s_idx[pos - idx_base] : -1;
-    const bool is_main = pos < k && j >= 0;
-    const bool is_win = pos >= k && pos < n_pos;
-    const int64_t e = base + (j > 0 ? j : 0);
-    const uint8_t* wrow = rows + (size_t)(is_win ? pos - k : 0) * kDKv + 8 * l;
-    pa[pp] = is_main ? kv_codes + e * kKvCodeBytes + 4 * l : wrow;
-    pb[pp] = is_main ? kv_scale + e * kKvScaleBytes + ((l >> 1) & ~3) : wrow + 4;
-    g.main_bits |= is_main ? 1u << pp : 0u;
-    g.win_bits |= is_win ? 1u << pp : 0u;
-  }
-#pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
-    g.r[pp].x = *reinterpret_cast<const uint32_t*>(pa[pp]);
-    g.r[pp].y = *reinterpret_cast<const uint32_t*>(pb[pp]);
-  }
-  return g;
+__device__ __forceinline__ f16x8 deq_main(uint32_t w, f16 s) {
+  const f16x2 ss = {s, s};
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// Dequantises the thread's 8 x 8 block and writes it to both LDS layouts.
-__device__ __forceinline__ void gather_commit(const GatherRaw& g, int w, int l, uint4* s_v,
-                                              uint4* s_vt) {
-  uint4 v[8];
-  const int sh = 8 * ((l >> 1) & 3);  // the lane's scale byte within its dword
-#pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
-    if (g.main_bits & (1u << pp)) {
-      v[pp] = fp4x8_scaled_bf16(g.r[pp].x, e4m3_to_f32((g.r[pp].y >> sh) & 0xffu));
-    } else if (g.win_bits & (1u << pp)) {
-      v[pp] = fp8x8_bf16(g.r[pp]);
-    } else {
-      v[pp] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    s_v[v_blk(8 * w + pp, l)] = v[pp];
-  }
-  // 8x8 transpose of 16-bit elements: dims 8l+2i (low halves) and 8l+2i+1 (high halves),
-  // each as positions 8w..8w+7
-  const uint32_t lo_sel = 0x05040100u, hi_sel = 0x07060302u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t wd[8];
-#pragma unroll
-    for (int pp = 0; pp < 8; ++pp)
-      wd[pp] = i == 0 ? v[pp].x : i == 1 ? v[pp].y : i == 2 ? v[pp].z : v[pp].w;
-    uint4 te, to;
-    te.x = __builtin_amdgcn_perm(wd[1], wd[0], lo_sel);
-    te.y = __builtin_amdgcn_perm(wd[3], wd[2], lo_sel);
-    te.z = __builtin_amdgcn_perm(wd[5], wd[4], lo_sel);
-    te.w = __builtin_amdgcn_perm(wd[7], wd[6], lo_sel);
-    to.x = __builtin_amdgcn_perm(wd[1], wd[0], hi_sel);
-    to.y = __builtin_amdgcn_perm(wd[3], wd[2], hi_sel);
-    to.z = __builtin_amdgcn_perm(wd[5], wd[4], hi_sel);
-    to.w = __builtin_amdgcn_perm(wd[7], wd[6], hi_sel);
-    s_vt[vt_blk(8 * l + 2 * i, w)] = te;
-    s_vt[vt_blk(8 * l + 2 * i + 1, w)] = to;
-  }
+__device__ __forceinline__ f16x8 deq_win(uint32_t w0, uint32_t w1) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
 
 // MODE 0: decode row b (entries seq_base[b] + idx, window rows swa[b][0..swa_len[b])).
 // MODE 1: prefill row t at position pos0 + t (entries idx from 0, window positions
 //         max(0,p-127)..p, row r of `swa` holding position pos0 - 127 + r); one split.
 template <int MODE>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_part(
+__global__ __launch_bounds__(kAThreads, 2) void k_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_codes,
     const uint8_t* __restrict__ kv_scale, const int64_t* __restrict__ seq_base,
     const int32_t* __restrict__ idx, int k, const uint8_t* __restrict__ swa,
     const int32_t* __restrict__ swa_len, int64_t pos0, float qscale, float* __restrict__ out,
-    float* __restrict__ part, int chunks_per_split, int n_splits) {
-  __shared__ uint4 s_v[kChunk * 64];          // 32 KiB
-  __shared__ uint4 s_vt[kDKv * 4];            // 32 KiB
-  __shared__ uint4 s_p[2][kHeads * 4];        // 2 KiB: p hi, p lo
-  __shared__ float s_s[2][kHeads][kChunk + 1];
-  __shared__ float s_m[kHeads], s_l[kHeads], s_alpha[kHeads];
-  __shared__ uint32_t s_valid[4];
-  __shared__ int32_t s_idx[kIdxWin];
+    float* __restrict__ part, int segs_per_split, int n_splits) {
+  __shared__ __align__(16) f16 s_v[kAW][kSeg * kHalf];         // each wave's half of a segment
+  __shared__ __align__(16) f16 s_p[2][kSeg * kHeads];          // p hi / lo, [position][head]
+  __shared__ __align__(16) f32x4v s_z[kAW][64];                // partial scores per lane
+  __shared__ int32_t s_idx[kIdxStage];
 
   const int split = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int n16 = l & 15, g16 = l >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n16 = lane & 15, g16 = lane >> 4;
+  const int d0 = kHalf * w + 64 * g16;  // this lane's first dim in the q . v steps
+  const int32_t* irow = k > 0 ? idx + (size_t)b * k : nullptr;
+  const int seg_begin = split * segs_per_split;
 
-  // ---- q as A operands: head n16, dims 32*ks + 8*g16 .. +7 for this wave's 8 k-steps
-  const int et = w & 1, kh = w >> 1;
-  bf16x8 qa[8];
+  // the first stage's entry ids, loaded before q so that both latencies overlap
+  constexpr int kIdPer = kIdxStage / kAThreads;
+  int32_t ids[kIdPer];
   {
-    const uint16_t* qrow = q + ((size_t)b * kHeads + n16) * kDKv + 8 * g16;
+    const int n_first = min(min(segs_per_split, kIdxStage / kSeg) * kSeg, k - seg_begin * kSeg);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qa[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + (8 * kh + kk) * 32));
+    for (int i = 0; i < kIdPer; ++i) {
+      const int j = tid + i * kAThreads;
+      ids[i] = j < n_first ? irow[seg_begin * kSeg + j] : -1;
+    }
   }
+
+  // ---- q as A operands (head n16, dims d0 + 8 s .. + 7 for k-step s), scaled per head by
+  // a power of two into fp16's range
+  const uint16_t* qrow = q + ((size_t)b * kHeads + n16) * kDKv;
+  f16x8 qa[8];
+  float qs[4];  // softmax scale of heads 4 g16 + r (log2 units), with the head's power of two
+  {
+    uint4 raw[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) raw[s] = reinterpret_cast<const uint4*>(qrow + d0)[s];
+    float amax = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = word_of(raw[s], i);
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(u & 0xffffu)), fabsf(bf16_bits_to_f32(u >> 16))));
+      }
+    }
+    // the head's largest element: over the four dim groups of this wave, then the waves
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (g16 == 0) s_z[w][n16][0] = amax;
+    __syncthreads();
+    amax = fmaxf(s_z[0][n16][0], s_z[1][n16][0]);
+    int e = 0;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1)
+      e = ex - 15;        // amax * 2^-e in [2^14, 2^15)
+    }
+    const float up = ldexpf(1.0f, -e);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      f16 v[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = word_of(raw[s], i);
+        v[2 * i] = (f16)(bf16_bits_to_f32(u & 0xffffu) * up);
+        v[2 * i + 1] = (f16)(bf16_bits_to_f32(u >> 16) * up);
+      }
+      qa[s] = f16x8{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qs[r] = qscale * ldexpf(1.0f, __shfl(e, 4 * g16 + r));
+  }
+
   const int64_t base = MODE == 0 ? seq_base[b] : 0;
   const uint8_t* rows;
   int nrows;
@@ -210,154 +231,203 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_part(
     nrows = (int)(p - lo + 1);
   }
   const int n_pos = k + nrows;
-  const int32_t* irow = k > 0 ? idx + (size_t)b * k : nullptr;
+  const int n_seg = (n_pos + kSeg - 1) / kSeg;
+  const int seg_end = min(seg_begin + segs_per_split, n_seg);
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(qrow);  // any valid 64 bytes
 
-  const int c_begin = split * chunks_per_split;
-  const int c_end = min(c_begin + chunks_per_split, (n_pos + kChunk - 1) / kChunk);
-
-  if (tid < kHeads) {
-    s_m[tid] = -__builtin_inff();
-    s_l[tid] = 0.f;
+  // running softmax state of heads 4 g16 + r (the same in both waves) and this wave's
+  // accumulators: acc[t] = tile t of its half, lane (dim 16 t + n16, heads 4 g16 + r)
+  float m[4], l[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -__builtin_inff();
+    l[r] = 0.f;
   }
-  f32x4v acc[8];
+  f32x4v acc[kHalfTiles];
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt) acc[tt] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  const int s_h = tid >> 4, s_jj = tid & 15;  // softmax roles: head, position pair
+  for (int t = 0; t < kHalfTiles; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-  // Outer loop: windows of kIdxWin list positions whose entry ids are staged in LDS.
-  // Inner loop: the window's chunks, each issuing exactly the same loads (the prefetch past
-  // the window's last chunk re-reads that chunk), so the next two chunks stay in flight.
-  for (int wc0 = c_begin; wc0 < c_end; wc0 += kIdxWin / kChunk) {
-    const int wc1 = min(wc0 + kIdxWin / kChunk, c_end);
-    const int idx_base = wc0 * kChunk;
-    __syncthreads();  // the previous window's ids are no longer read
-    for (int i = tid; i < kIdxWin; i += kAttnThreads)
-      s_idx[i] = idx_base + i < k ? irow[idx_base + i] : -1;
-    __syncthreads();
-    GatherRaw raw_a = gather_issue(wc0 * kChunk, w, l, k, n_pos, s_idx, idx_base, base, kv_codes,
-                                   kv_scale, rows);
-    GatherRaw raw_b = gather_issue(min(wc0 + 1, wc1 - 1) * kChunk, w, l, k, n_pos, s_idx, idx_base,
-                                   base, kv_codes, kv_scale, rows);
-  for (int c = wc0; c < wc1; ++c) {
-    gather_commit(raw_a, w, l, s_v, s_vt);
-    if (l == 0) s_valid[w] = raw_a.main_bits | raw_a.win_bits;
-    raw_a = raw_b;
-    __syncthreads();
-    raw_b = gather_issue(min(c + 2, wc1 - 1) * kChunk, w, l, k, n_pos, s_idx, idx_base, base,
-                         kv_codes, kv_scale, rows);
+  f16* vt = s_v[w];
+  // transposed-read coordinates: lane = 16 g + 4 mm + qq reads row 4 g + mm, columns 4 qq
+  const int tr_row = 4 * g16 + ((lane >> 2) & 3), tr_q = lane & 3;
 
-    // ---- z partials: entries 16*et + n16, dims of k-steps 8*kh .. 8*kh + 7
-    {
-      f32x4v sacc = {0.f, 0.f, 0.f, 0.f};
-      const int e = 16 * et + n16;
+  for (int stage0 = seg_begin; stage0 < seg_end; stage0 += kIdxStage / kSeg) {
+    const int stage1 = min(stage0 + kIdxStage / kSeg, seg_end);
+    const int idx_base = stage0 * kSeg;
+    const int idx_n = min(stage1 * kSeg, k) - idx_base;  // ids this stage reads
+    __syncthreads();  // the previous stage's ids are no longer read
+    if (stage0 == seg_begin) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int ks = 8 * kh + kk;
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(s_v[v_blk(e, 4 * ks + g16)]),
-                                                        sacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s_s[kh][4 * g16 + j][e] = sacc[j];
+      for (int i = 0; i < kIdPer; ++i) s_idx[tid + i * kAThreads] = ids[i];
+    } else {
+      for (int i = tid; i < idx_n; i += kAThreads) s_idx[i] = irow[idx_base + i];
     }
     __syncthreads();
+    const int n_i = stage1 - stage0;
 
-    // ---- online softmax update, 16 lanes per head, 2 positions per lane
-    {
-      const int pa = 2 * s_jj, pb = pa + 1;
-      const uint32_t vm = s_valid[pa >> 3];
-      const bool va = (vm >> (pa & 7)) & 1u, vb = (vm >> (pb & 7)) & 1u;
-      const float z0 = va ? (s_s[0][s_h][pa] + s_s[1][s_h][pa]) * qscale : -__builtin_inff();
-      const float z1 = vb ? (s_s[0][s_h][pb] + s_s[1][s_h][pb]) * qscale : -__builtin_inff();
-      float cm = fmaxf(z0, z1);
-      cm = fmaxf(cm, __shfl_xor(cm, 1));
-      cm = fmaxf(cm, __shfl_xor(cm, 2));
-      cm = fmaxf(cm, __shfl_xor(cm, 4));
-      cm = fmaxf(cm, __shfl_xor(cm, 8));
-      const float m_old = s_m[s_h];
-      const float m_new = fmaxf(m_old, cm);
-      float p0v = 0.f, p1v = 0.f;
-      if (m_new != -__builtin_inff()) {
-        p0v = exp2f(z0 - m_new);
-        p1v = exp2f(z1 - m_new);
+    auto issue = [&](int i) {
+      Raw r;
+      const int p = (stage0 + i) * kSeg + n16;
+      int kind = 0;
+      int j = 0;
+      if (i < n_i && p < n_pos) {
+        if (p < k) {
+          j = s_idx[p - idx_base];
+          kind = j >= 0 ? 1 : 0;
+        } else {
+          kind = 2;
+        }
       }
-      float ps = p0v + p1v;
-      ps += __shfl_xor(ps, 1);
-      ps += __shfl_xor(ps, 2);
-      ps += __shfl_xor(ps, 4);
-      ps += __shfl_xor(ps, 8);
-      // p = hi + lo: hi = p truncated to bf16, lo = bf16(p - hi)
-      const uint32_t h0 = __float_as_uint(p0v) & 0xffff0000u, h1 = __float_as_uint(p1v) & 0xffff0000u;
-      const float r0 = p0v - __uint_as_float(h0), r1 = p1v - __uint_as_float(h1);
-      const uint32_t l0 = __builtin_bit_cast(uint16_t, (__bf16)r0);
-      const uint32_t l1 = __builtin_bit_cast(uint16_t, (__bf16)r1);
-      uint32_t* ph = reinterpret_cast<uint32_t*>(&s_p[0][p_blk(s_h, pa >> 3)]);
-      uint32_t* pl = reinterpret_cast<uint32_t*>(&s_p[1][p_blk(s_h, pa >> 3)]);
-      ph[(pa & 7) >> 1] = (h0 >> 16) | h1;
-      pl[(pa & 7) >> 1] = l0 | (l1 << 16);
-      __syncthreads();  // every lane has read s_m before it changes
-      if (s_jj == 0) {
-        const float alpha = m_old == -__builtin_inff() ? 0.f : exp2f(m_old - m_new);
-        s_alpha[s_h] = alpha;
-        s_l[s_h] = s_l[s_h] * alpha + ps;
-        s_m[s_h] = m_new;
+      const int64_t e = base + (kind == 1 ? j : 0);
+      const uint8_t* am = kv_codes + e * kKvCodeBytes + d0 / 2;
+      const uint8_t* aw = rows + (size_t)(kind == 2 ? p - k : 0) * kDKv + d0;
+      const uint8_t* a = kind == 1 ? am : kind == 2 ? aw : dummy;
+      const uint8_t* a2 = kind == 2 ? aw + 32 : a;
+      const uint8_t* asc = kind == 1 ? kv_scale + e * kKvScaleBytes + d0 / 16 : a;
+      r.u[0] = reinterpret_cast<const uint4*>(a)[0];
+      r.u[1] = reinterpret_cast<const uint4*>(a)[1];
+      r.u[2] = reinterpret_cast<const uint4*>(a2)[0];
+      r.u[3] = reinterpret_cast<const uint4*>(a2)[1];
+      r.sc = *reinterpret_cast<const uint32_t*>(asc);
+      r.kind = kind;
+      return r;
+    };
+
+    auto compute = [&](const Raw& r) {
+      // ---- dequantise this wave's half into B operands, stage it for p . v, and q . v
+      f16 sc[4];
+      {
+        const f16x2 s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, false);
+        const f16x2 s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, true);
+        sc[0] = s0.x; sc[1] = s0.y; sc[2] = s1.x; sc[3] = s1.y;
       }
+      f32x4v z = {0.f, 0.f, 0.f, 0.f};
+      f16* vrow = vt + n16 * kHalf;
+      int sw = vswz(n16);
+      asm volatile("" : "+v"(sw));  // recomputed per segment: no 8 addresses held live
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        f16x8 bv = {};
+        if (r.kind == 1) {
+          bv = deq_main(word_of(r.u[s >> 2], s & 3), sc[s >> 1]);
+        } else if (r.kind == 2) {
+          const uint4 v = r.u[s >> 1];
+          bv = (s & 1) ? deq_win(v.z, v.w) : deq_win(v.x, v.y);
+        }
+        *reinterpret_cast<f16x8*>(vrow + 8 * ((8 * g16 + s) ^ sw)) = bv;
+        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], bv, z, 0, 0, 0);
+      }
+      // ---- the two halves' scores, added in the same order in both waves
+      s_z[w][lane] = z;
+      __syncthreads();
+      const f32x4v z0 = s_z[0][lane], z1 = s_z[1][lane];
+      // ---- online softmax over the segment's positions (lane: position n16, heads 4 g16 + r)
+      const bool valid = r.kind != 0;
+      float p[4], alpha[4];
+      bool moved = false;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float zs = valid ? (z0[rr] + z1[rr]) * qs[rr] : -__builtin_inff();
+        const float cm = row16<true>(zs);
+        const float mu = cm > m[rr] + kRescale ? cm : m[rr];
+        alpha[rr] = mu == m[rr] ? 1.0f : (m[rr] == -__builtin_inff() ? 0.f : exp2f(m[rr] - mu));
+        moved |= mu != m[rr];
+        m[rr] = mu;
+        p[rr] = zs == -__builtin_inff() ? 0.f : exp2f(zs - mu);
+        l[rr] = l[rr] * alpha[rr] + row16<false>(p[rr]);
+      }
+      if (__ballot(moved) != 0ull) {
+#pragma unroll
+        for (int t = 0; t < kHalfTiles; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[t][rr] *= alpha[rr];
+      }
+      // p = hi + lo in fp16, staged as [position][head]: wave 0 writes hi, wave 1 lo
+      f16 pp[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f16 hi = (f16)p[rr];
+        pp[rr] = w == 0 ? hi : (f16)(p[rr] - (float)hi);
+      }
+      *reinterpret_cast<f16x4*>(s_p[w] + n16 * kHeads + 4 * g16) = f16x4{pp[0], pp[1], pp[2], pp[3]};
+      __syncthreads();
+      // ---- acc += p . v over this wave's half: A = p (head, 4 positions), B = v, transposed
+      const f16x4 a_hi = tr_read(s_p[0] + tr_row * kHeads + 4 * tr_q);
+      const f16x4 a_lo = tr_read(s_p[1] + tr_row * kHeads + 4 * tr_q);
+      int tsw = vswz(tr_row);
+      asm volatile("" : "+v"(tsw));
+      // tiles t and t + 8 share the swizzled block's low bits: 8 bases, immediate offsets
+      const f16* vr[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        vr[t] = vt + tr_row * kHalf + 8 * ((2 * t + (tr_q >> 1)) ^ tsw) + 4 * (tr_q & 1);
+#pragma unroll
+      for (int t = 0; t < kHalfTiles; ++t) {
+        const f16x4 bv = tr_read(vr[t & 7] + 128 * (t >> 3));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a_hi, bv, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a_lo, bv, acc[t], 0, 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // the next segment rewrites this wave's tile
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // the next segment's loads are in flight while one is computed
+    Raw r0 = issue(0);
+    for (int i = 0; i < n_i; ++i) {
+      const Raw nx = issue(i + 1);
+      compute(r0);
+      r0 = nx;
     }
-    __syncthreads();
-
-    // ---- acc = acc * alpha + p . v for output dims (8w + tt)*16 + n16, heads 4*g16 + j
-    {
-      float al[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = s_alpha[4 * g16 + j];
-      const bf16x8 a_hi = as_bf16x8(s_p[0][p_blk(n16, g16)]);
-      const bf16x8 a_lo = as_bf16x8(s_p[1][p_blk(n16, g16)]);
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[tt][j] *= al[j];
-        const bf16x8 bv = as_bf16x8(s_vt[vt_blk((8 * w + tt) * 16 + n16, g16)]);
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bv, acc[tt], 0, 0, 0);
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bv, acc[tt], 0, 0, 0);
-      }
-    }
-    __syncthreads();  // LDS is rewritten by the next chunk
   }
-  }
-  __syncthreads();  // s_m / s_l final (also when this split had no positions)
 
+  // ---- out (one split) or this split's (max, sum, acc)
   if (MODE == 1 || n_splits == 1) {
-    float* O = out + (size_t)b * kHeads * kDKv;
+    float* O = out + (size_t)b * kHeads * kDKv + kHalf * w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = 4 * g16 + j;
-      const float lsum = s_l[h];
-      const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g16 + r;
+      const float inv = l[r] > 0.f ? 1.0f / l[r] : 0.f;
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) O[h * kDKv + (8 * w + tt) * 16 + n16] = acc[tt][j] * inv;
+      for (int t = 0; t < kHalfTiles; ++t) O[h * kDKv + 16 * t + n16] = acc[t][r] * inv;
     }
     return;
   }
   float* P = part + ((size_t)b * n_splits + split) * kPart;
-  if (tid < kHeads) {
-    P[tid] = s_m[tid];
-    P[kHeads + tid] = s_l[tid];
+  if (w == 0 && n16 == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      P[4 * g16 + r] = m[r];
+      P[kHeads + 4 * g16 + r] = l[r];
+    }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
-      P[2 * kHeads + (4 * g16 + j) * kDKv + (8 * w + tt) * 16 + n16] = acc[tt][j];
+    for (int t = 0; t < kHalfTiles; ++t)
+      P[2 * kHeads + (4 * g16 + r) * kDKv + kHalf * w + 16 * t + n16] = acc[t][r];
 }
 
-// Log-sum-exp merge of a decode row's splits for one head: 128 threads x 4 dims.  Each
-// lane of the first wave takes one split's (max, sum), so the weights come from two wave
-// reductions, then all splits' accumulators are read with independent loads.
-__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, int n_splits,
-                                                    float* __restrict__ out) {
+// Log-sum-exp merge of a decode row's splits for one head: 256 threads; thread t sums dims
+// 4 (t % 128) .. + 3 over the splits of parity t / 128, with every load issued before the
+// first is used, and the two parities meet in LDS.  The first wave turns each split's
+// (max, sum) into its weight meanwhile (two wave reductions).
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __restrict__ part,
+                                                              int n_splits, float* __restrict__ out) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_L;
+  __shared__ float4 s_o[kMergeThreads / 2];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int par = tid >> 7, d = 4 * (tid & 127);
   const float* P0 = part + (size_t)b * n_splits * kPart;
+  float4 a[kMaxSplits / 2];
+#pragma unroll
+  for (int i = 0; i < kMaxSplits / 2; ++i) {
+    const int sp = 2 * i + par;
+    a[i] = sp < n_splits ? *reinterpret_cast<const float4*>(P0 + (size_t)sp * kPart + 2 * kHeads + h * kDKv + d)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (tid < 64) {
     const float ms = lane < n_splits ? P0[(size_t)lane * kPart + h] : -__builtin_inff();
     const float ls = lane < n_splits ? P0[(size_t)lane * kPart + kHeads + h] : 0.f;
@@ -373,20 +443,26 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
   }
   __syncthreads();
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* A = P0 + 2 * kHeads + h * kDKv + 4 * tid;
-#pragma unroll 8
-  for (int s = 0; s < n_splits; ++s) {
-    const float wgt = s_w[s];
-    const float4 a = *reinterpret_cast<const float4*>(A + (size_t)s * kPart);
-    o.x = fmaf(a.x, wgt, o.x);
-    o.y = fmaf(a.y, wgt, o.y);
-    o.z = fmaf(a.z, wgt, o.z);
-    o.w = fmaf(a.w, wgt, o.w);
+#pragma unroll
+  for (int i = 0; i < kMaxSplits / 2; ++i) {
+    const int sp = 2 * i + par;
+    if (sp < n_splits) {
+      const float wgt = s_w[sp];
+      o.x = fmaf(a[i].x, wgt, o.x);
+      o.y = fmaf(a[i].y, wgt, o.y);
+      o.z = fmaf(a[i].z, wgt, o.z);
+      o.w = fmaf(a[i].w, wgt, o.w);
+    }
   }
-  const float L = s_L;
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  *reinterpret_cast<float4*>(&out[((size_t)b * kHeads + h) * kDKv + 4 * tid]) =
-      make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (par == 1) s_o[tid & 127] = o;
+  __syncthreads();
+  if (par == 0) {
+    const float4 o1 = s_o[tid];
+    const float L = s_L;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    *reinterpret_cast<float4*>(&out[((size_t)b * kHeads + h) * kDKv + d]) =
+        make_float4((o.x + o1.x) * inv, (o.y + o1.y) * inv, (o.z + o1.z) * inv, (o.w + o1.w) * inv);
+  }
 }
 
 hipError_t launch_attn(int mode, const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
@@ -394,19 +470,20 @@ hipError_t launch_attn(int mode, const uint16_t* q, const uint8_t* kv_codes, con
                        const int32_t* swa_len, int64_t pos0, float softmax_scale, int rows,
                        float* out, void* ws, hipStream_t stream) {
   const float qscale = softmax_scale * 1.4426950408889634f;  // log2(e)
-  const int chunks = attn_chunks(k);
+  const int segs = attn_segments(k);
   if (mode == 1) {
-    hipLaunchKernelGGL(k_attn_part<1>, dim3(1, rows), dim3(kAttnThreads), 0, stream, q, kv_codes,
-                       kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, nullptr, chunks, 1);
+    hipLaunchKernelGGL(k_attn<1>, dim3(1, rows), dim3(kAThreads), 0, stream, q, kv_codes,
+                       kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, nullptr, segs, 1);
     return hipGetLastError();
   }
-  const int n_splits = attn_splits(k);
-  const int cps = (chunks + n_splits - 1) / n_splits;
+  const int sps = attn_segs_per_split(rows, k);
+  const int used = (segs + sps - 1) / sps;  // splits, each with at least one segment
   float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL(k_attn_part<0>, dim3(n_splits, rows), dim3(kAttnThreads), 0, stream, q, kv_codes,
-                     kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, part, cps, n_splits);
-  if (n_splits > 1)
-    hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, rows), dim3(128), 0, stream, part, n_splits, out);
+  hipLaunchKernelGGL(k_attn<0>, dim3(used, rows), dim3(kAThreads), 0, stream, q, kv_codes,
+                     kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, part, sps, used);
+  if (used > 1)
+    hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, rows), dim3(kMergeThreads), 0, stream, part, used,
+                       out);
   return hipGetLastError();
 }
 

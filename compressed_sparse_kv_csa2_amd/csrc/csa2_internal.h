@@ -64,7 +64,7 @@ hipError_t launch_topk(const float* scores, int batch, int n_cols, const int32_t
                        bool hist_ready, const TopkWs& ws, hipStream_t stream);
 
 // ---- attention ----
-int attn_chunks(int k);          // 32-position chunks of k entries + a full window
+int attn_segments(int k);        // 16-position segments of k entries + a full window
 int attn_splits(int k);          // decode splits per row
 size_t attn_ws_bytes(int rows, int k);
 

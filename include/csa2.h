@@ -41,8 +41,10 @@
  *  - Workspaces: size them with the *_workspace_size query, zero-fill them ONCE before
  *    first use (e.g. hipMemset or torch.zeros); every call returns the counters it uses to
  *    zero before it completes, so a workspace can be reused call after call without
- *    clearing.  Reusing a workspace across calls on different streams needs the caller's
- *    ordering.
+ *    clearing -- by calls of the shape it was last zero-filled for (the same batch and
+ *    sizes given to the size query): the layout of its counters depends on that shape,
+ *    so a call of another shape needs the workspace zero-filled again first.  Reusing a
+ *    workspace across calls on different streams needs the caller's ordering.
  */
 #ifndef CSA2_H_
 #define CSA2_H_

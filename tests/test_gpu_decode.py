@@ -184,7 +184,7 @@ def test_topk_all_ties_take_lowest_indices():
 
 
 # --------------------------------------------------------------------------- a5 / a6
-@pytest.mark.parametrize("k,swa_len", [(512, 128), (37, 5), (0, 128), (64, 0), (512, 0)])
+@pytest.mark.parametrize("k,swa_len", [(512, 128), (37, 5), (0, 128), (64, 0), (512, 0), (2900, 128)])
 def test_attention_matches_oracle(k, swa_len):
     log(f"attn k={k} swa={swa_len}")
     n = 3000
