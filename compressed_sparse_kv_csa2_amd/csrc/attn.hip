@@ -268,16 +268,8 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     auto issue = [&](int i) {
       Raw r;
       const int p = (stage0 + i) * kSeg + n16;
-      int kind = 0;
-      int j = 0;
-      if (i < n_i && p < n_pos) {
-        if (p < k) {
-          j = s_idx[p - idx_base];
-          kind = j >= 0 ? 1 : 0;
-        } else {
-          kind = 2;
-        }
-      }
+      const int j = s_idx[min(max(p - idx_base, 0), kIdxStage - 1)];  // read whatever the kind
+      const int kind = (i < n_i && p < n_pos) ? (p < k ? (j >= 0 ? 1 : 0) : 2) : 0;
       const int64_t e = base + (kind == 1 ? j : 0);
       const uint8_t* am = kv_codes + e * kKvCodeBytes + d0 / 2;
       const uint8_t* aw = rows + (size_t)(kind == 2 ? p - k : 0) * kDKv + d0;
@@ -294,28 +286,44 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     };
 
     auto compute = [&](const Raw& r) {
-      // ---- dequantise this wave's half into B operands, stage it for p . v, and q . v
+      // ---- dequantise this wave's half into B operands, stage it for p . v, and q . v.
+      // The segment's kinds pick one of three straight-line paths (wave-uniform): main
+      // entries (a lane with nothing dequantises with scale 0), window rows, or both.
+      const bool any_win = __ballot(r.kind == 2) != 0ull;
+      const bool any_main = __ballot(r.kind != 2) != 0ull;
       f16 sc[4];
       {
-        const f16x2 s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, false);
-        const f16x2 s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, true);
+        const uint32_t scw = r.kind == 1 ? r.sc : 0u;
+        const f16x2 s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scw, 1.0f, false);
+        const f16x2 s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scw, 1.0f, true);
         sc[0] = s0.x; sc[1] = s0.y; sc[2] = s1.x; sc[3] = s1.y;
       }
       f32x4v z = {0.f, 0.f, 0.f, 0.f};
       f16* vrow = vt + n16 * kHalf;
       int sw = vswz(n16);
       asm volatile("" : "+v"(sw));  // recomputed per segment: no 8 addresses held live
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        f16x8 bv = {};
-        if (r.kind == 1) {
-          bv = deq_main(word_of(r.u[s >> 2], s & 3), sc[s >> 1]);
-        } else if (r.kind == 2) {
-          const uint4 v = r.u[s >> 1];
-          bv = (s & 1) ? deq_win(v.z, v.w) : deq_win(v.x, v.y);
-        }
+      auto step = [&](int s, const f16x8& bv) {
         *reinterpret_cast<f16x8*>(vrow + 8 * ((8 * g16 + s) ^ sw)) = bv;
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], bv, z, 0, 0, 0);
+      };
+      if (!any_win) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) step(s, deq_main(word_of(r.u[s >> 2], s & 3), sc[s >> 1]));
+      } else if (!any_main) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint4 v = r.u[s >> 1];
+          step(s, (s & 1) ? deq_win(v.z, v.w) : deq_win(v.x, v.y));
+        }
+      } else {
+        const bool win = r.kind == 2;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint4 v = r.u[s >> 1];
+          const f16x8 bw = (s & 1) ? deq_win(v.z, v.w) : deq_win(v.x, v.y);
+          const f16x8 bm = deq_main(word_of(r.u[s >> 2], s & 3), sc[s >> 1]);
+          step(s, win ? bw : bm);
+        }
       }
       // ---- the two halves' scores, added in the same order in both waves
       s_z[w][lane] = z;
@@ -330,10 +338,10 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
         const float zs = valid ? (z0[rr] + z1[rr]) * qs[rr] : -__builtin_inff();
         const float cm = row16<true>(zs);
         const float mu = cm > m[rr] + kRescale ? cm : m[rr];
-        alpha[rr] = mu == m[rr] ? 1.0f : (m[rr] == -__builtin_inff() ? 0.f : exp2f(m[rr] - mu));
+        alpha[rr] = mu == m[rr] ? 1.0f : (m[rr] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[rr] - mu));
         moved |= mu != m[rr];
         m[rr] = mu;
-        p[rr] = zs == -__builtin_inff() ? 0.f : exp2f(zs - mu);
+        p[rr] = zs == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(zs - mu);
         l[rr] = l[rr] * alpha[rr] + row16<false>(p[rr]);
       }
       if (__ballot(moved) != 0ull) {
