@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
   // entries any row of the workgroup can see, and of this wave's rows
   const int wg_nmax = visible(pos0 + min(wg_row0 + kGemmRows - 1, T - 1), ratio, n_entries);
   const int wave_nmax = row0 < T ? visible(pos0 + min(row0 + 31, T - 1), ratio, n_entries) : 0;
+  const int wave_nmin = row0 < T ? visible(pos0 + row0, ratio, n_entries) : 0;
   const int e_stop = min(e_end, wg_nmax);
   const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
 
@@ -206,6 +207,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp4x8_bf16(c1.z), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp4x8_bf16(c1.w), acc, 0, 0, 0);
         const int col = e0 + rl;
+        if (PASS == 1 && e0 + 32 <= wave_nmin) {  // wave-uniform: every row sees the tile
+#pragma unroll
+          for (int r = 0; r < 16; ++r) rm[r] = __builtin_amdgcn_fmed3f(acc[r] * sc, rm[r], __builtin_inff());
+          continue;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float s = acc[r] * sc;
