@@ -391,11 +391,13 @@ class Prefill:
         m[1].record(s)
 
     def dominant(self):
-        # both passes of the causal indexer contraction, 2 flops per multiply-add; timed as the
-        # whole chunk call, so this is a lower bound on the contraction's own rate
-        return {"kernel": "csa2_prefill_chunk (2 causal BF16 MFMA passes; whole call timed)",
+        # the causal indexer contraction counted once (2 flops per multiply-add; the library
+        # runs it twice, the second time to collect candidates), timed as the whole chunk
+        # call: a lower bound on the contraction's own rate (per-kernel times: rocprofv3)
+        return {"kernel": "csa2_prefill_chunk (causal BF16 MFMA indexer contraction; whole call "
+                          "timed)",
                 "bound": "mfma", "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
-                "work": 2 * 2 * D_IDX * self.pairs, "scale": 1e12, "marks": (0, 1)}
+                "work": 2 * D_IDX * self.pairs, "scale": 1e12, "marks": (0, 1)}
 
     def step_bytes(self):
         return (self.N * IDX_ENTRY_BYTES + self.T * (D_IDX * 2 + HEADS * D_KV * 2 + HEADS * D_KV * 4 +
