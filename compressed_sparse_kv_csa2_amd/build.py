@@ -29,9 +29,14 @@ COMMON_FLAGS = [
 ]
 
 
+# The indexer GEMM reads every accumulator in VALU code right after its MFMA chain: MFMAs
+# that accumulate in VGPRs save the 16 AGPR-to-VGPR copies per tile.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

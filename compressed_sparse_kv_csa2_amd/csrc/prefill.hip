@@ -21,16 +21,17 @@
 //          groups have maxima >= the k-th largest group maximum, so that value, theta_t,
 //          is a rigorous lower bound on the row's k-th score;
 //   pass 2 recomputes the contraction and writes the scores >= theta_t (typically a few
-//          hundred per row) into the row's slots for this split (LDS counters, no global
-//          atomics);
+//          hundred per row) into the row's slots for this split, in entry order (a wave owns
+//          its rows: slots come from the compare ballots, no atomics);
 //   select resolves each row exactly in LDS (largest scores, ties to the lower entry) and
-//          sorts the chosen entries ascending.  A row whose candidates overflow a split's
+//          emits the chosen entries in ascending order.  A row whose candidates overflow a split's
 //          slots (only possible with massive score ties) is resolved by recomputing its
 //          scores in a streaming radix select; a row that sees at most k entries takes them
 //          all.
 // Stages past the causal frontier of a workgroup's rows are skipped.
 #include "csa2_device.h"
 #include "csa2_internal.h"
+#include "select_device.h"
 
 namespace csa2 {
 
@@ -46,7 +47,6 @@ static_assert(kSlots == 64, "select copies one split per wave, one slot per lane
 constexpr int kCandLds = 8192;              // candidates a row may gather into LDS
 constexpr int kSelThreads = 256;
 constexpr int kSelMaxSplits = 1024;         // splits a row's fast path can gather (N <= 4M)
-constexpr int kMaxKPow2 = 16384;            // largest k (power of two) the select kernel sorts
 
 struct PrefillWs {
   uint16_t* gmax;               // [T][G] group maxima as key >> 16 (0 = empty group)
@@ -105,6 +105,25 @@ __device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w) {
   return r;
 }
 
+// v_max_f32 without the quieting of signalling NaNs that fmaxf adds (scores are finite or -inf).
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Lane masks of a >= b (floats) and a < b (ints), straight from v_cmp (every lane active).
+__device__ __forceinline__ uint64_t mask_ge(float a, float b) {
+  uint64_t m;
+  asm("v_cmp_ge_f32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
+  return m;
+}
+__device__ __forceinline__ uint64_t mask_lt(int a, int b) {
+  uint64_t m;
+  asm("v_cmp_lt_i32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
+  return m;
+}
+
 // LDS stage: entry i's 64 code bytes as 4 blocks of 16 bytes, block b at b ^ ((i >> 2) & 3)
 // so that 16 consecutive entries' reads of one block land in 16 distinct bank groups.
 __device__ __forceinline__ int stage_blk(int i, int b) { return i * 4 + (b ^ ((i >> 2) & 3)); }
@@ -119,8 +138,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
   __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
   __shared__ float s_sc[2][kStage];
-  __shared__ uint32_t s_ccnt[kGemmRows];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kGemmRows;
   const int row0 = wg_row0 + wave * 32;
   const int split = blockIdx.y;
@@ -149,14 +167,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
     const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
     nvis[r] = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
   }
+  // PASS 2: row thresholds, and the wave's candidate counts per accumulator row r for the
+  // rows of lanes 0-31 (clo) and 32-63 (chi); the wave owns its rows, so the counts are
+  // wave-uniform and slots follow the compare ballots in entry order
   float th[16];
+  uint32_t clo[16], chi[16];
   if (PASS == 2) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
       th[r] = t < T ? ws.theta[t] : __builtin_inff();
+      clo[r] = 0u;
+      chi[r] = 0u;
     }
-    if (tid < kGemmRows) s_ccnt[tid] = 0u;
   }
 
   // one entry per thread per stage: 4 x 16 code bytes + scale, clamped to a real entry
@@ -207,23 +230,37 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp4x8_bf16(c1.z), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp4x8_bf16(c1.w), acc, 0, 0, 0);
         const int col = e0 + rl;
-        if (PASS == 1 && e0 + 32 <= wave_nmin) {  // wave-uniform: every row sees the tile
+        const bool full = e0 + 32 <= wave_nmin;  // wave-uniform: every row sees the tile
+        if (PASS == 1) {
+          if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) rm[r] = __builtin_amdgcn_fmed3f(acc[r] * sc, rm[r], __builtin_inff());
-          continue;
-        }
+            for (int r = 0; r < 16; ++r) rm[r] = vmax(acc[r] * sc, rm[r]);
+          } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s = acc[r] * sc;
-          const bool vis = col < nvis[r];
-          if (PASS == 1) {
-            rm[r] = vis ? fmaxf(rm[r], s) : rm[r];
-          } else if (vis && s >= th[r]) {
-            const int lr = wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const uint32_t slot = atomicAdd(&s_ccnt[lr], 1u);
-            if (slot < (uint32_t)kSlots)
-              ws.cand[(((size_t)(wg_row0 + lr)) * ws.n_splits + split) * kSlots + slot] =
+            for (int r = 0; r < 16; ++r) {
+              const float s = acc[r] * sc;
+              rm[r] = col < nvis[r] ? vmax(s, rm[r]) : rm[r];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float s = acc[r] * sc;
+            uint64_t m = mask_ge(s, th[r]);
+            if (!full) m &= mask_lt(col, nvis[r]);
+            if (m == 0ull) continue;
+            const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+            const uint32_t nlo = (uint32_t)__builtin_popcount(mlo);
+            // hits in lanes below this one; lanes 32-63 subtract the other row's (lanes 0-31)
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+            const uint32_t slot = below + (half ? chi[r] - nlo : clo[r]);
+            clo[r] += nlo;
+            chi[r] += (uint32_t)__builtin_popcount(mhi);
+            if (((m >> lane) & 1ull) && slot < (uint32_t)kSlots) {
+              const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+              ws.cand[((size_t)t * ws.n_splits + split) * kSlots + slot] =
                   ((unsigned long long)score_key(s) << 32) | (uint32_t)col;
+            }
           }
         }
       }
@@ -243,10 +280,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
     }
   }
 #undef CSA2_LOAD_STAGE
-  if (PASS == 2) {
-    __syncthreads();
-    if (tid < kGemmRows && wg_row0 + tid < T)
-      ws.ccount[(size_t)(wg_row0 + tid) * ws.n_splits + split] = s_ccnt[tid];
+  if (PASS == 2) {  // lane l < 32 reports wave row l: r = 4 * (l / 8) + l % 4, half (l / 4) % 2
+    uint32_t c = 0u;
+    const int lr_ = ((lane >> 3) << 2) | (lane & 3);
+    const bool lhi = (lane >> 2) & 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c = lr_ == r ? (lhi ? chi[r] : clo[r]) : c;
+    if (lane < 32 && row0 + lane < T) ws.ccount[(size_t)(row0 + lane) * ws.n_splits + split] = c;
   }
 }
 
@@ -379,15 +419,14 @@ __device__ __forceinline__ float score_row(const bf16x2 (&qq)[64], const uint8_t
 __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, int k,
-    int k_pow2, int32_t* __restrict__ idx_out, PrefillWs ws) {
+    int32_t* __restrict__ idx_out, PrefillWs ws) {
   extern __shared__ unsigned long long s_dyn[];
   unsigned long long* s_cand = s_dyn;                                         // [kCandLds]
-  uint32_t* s_sel = reinterpret_cast<uint32_t*>(s_dyn + kCandLds);             // [k_pow2]
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_res[4];
   __shared__ uint32_t s_scan[32];
-  __shared__ uint32_t s_nsel, s_total, s_over;
-  __shared__ uint32_t s_cnt[kSelMaxSplits], s_off[kSelMaxSplits];
+  __shared__ uint32_t s_total, s_over;
+  __shared__ uint32_t s_cnt[kSelMaxSplits], s_off[kSelMaxSplits], s_sel[kSelMaxSplits];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_t = visible(pos0 + t, ratio, n_entries);
@@ -426,7 +465,6 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     if (lane == 0) {
       s_total = carry;
       s_over = over | (carry > (uint32_t)kCandLds ? 1u : 0u);
-      s_nsel = 0u;
     }
   }
   __syncthreads();
@@ -435,13 +473,26 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     // ---- fast path: exact selection among the candidates
     {
       const int wave = tid >> 6, lane = tid & 63;
-      for (int s = wave; s < S; s += kSelThreads / 64) {
-        const unsigned long long* src = ws.cand + ((size_t)t * S + s) * kSlots;
-        if (lane < (int)s_cnt[s]) s_cand[s_off[s] + lane] = src[lane];
+      constexpr int kBatch = 8;  // splits per wave with loads in flight together
+      for (int s0 = wave; s0 < S; s0 += kBatch * (kSelThreads / 64)) {
+        unsigned long long v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int s = s0 + j * (kSelThreads / 64);
+          const bool have = s < S && lane < (int)s_cnt[min(s, S - 1)];
+          v[j] = have ? ws.cand[((size_t)t * S + s) * kSlots + lane] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int s = s0 + j * (kSelThreads / 64);
+          if (s < S && lane < (int)s_cnt[s]) s_cand[s_off[s] + lane] = v[j];
+        }
       }
     }
     __syncthreads();
-    // composite: key (32 bits) then ~entry (a lower entry ranks higher); 8 digits of 8 bits
+    // composite: key (32 bits) then ~entry (a lower entry ranks higher); 8 digits of 8 bits.
+    // Radix levels find the threshold composite: the row takes every candidate >= prefix
+    // (lower digits zero once a level's bin is taken whole).
     uint32_t need = k_eff;
     unsigned long long prefix = 0ull, pmask = 0ull;
     uint32_t remaining = C;
@@ -458,52 +509,41 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
       if (tid < 64) find_bin_wave(s_hist, 256, need, s_res);
       __syncthreads();
       const uint32_t sel = s_res[0];
-      // everything above the bin at this level (within the prefix) is taken
-      for (uint32_t i = tid; i < C; i += kSelThreads) {
-        const unsigned long long v = s_cand[i];
-        const unsigned long long comp = (v & 0xffffffff00000000ull) | (uint32_t)~(uint32_t)v;
-        if ((comp & pmask) == prefix && ((comp >> shift) & 255ull) > sel) {
-          const uint32_t p = atomicAdd(&s_nsel, 1u);
-          if (p < (uint32_t)k_pow2) s_sel[p] = (uint32_t)v;
-        }
-      }
       need -= s_res[1];
       remaining = s_hist[sel];
       prefix |= (unsigned long long)sel << shift;
       pmask |= 255ull << shift;
       __syncthreads();
     }
-    if (need > 0) {  // take every candidate still matching the prefix
-      for (uint32_t i = tid; i < C; i += kSelThreads) {
-        const unsigned long long v = s_cand[i];
+    // ---- the selected candidates in ascending entry order: splits hold ascending entry
+    // ranges and a split's slots are in entry order, so each wave compacts one split's
+    // selected slots after the selected entries of the splits before it
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      auto take = [&](int sp, uint32_t* e) {
+        const bool have = lane < (int)s_cnt[sp];
+        const unsigned long long v = have ? s_cand[s_off[sp] + lane] : 0ull;
         const unsigned long long comp = (v & 0xffffffff00000000ull) | (uint32_t)~(uint32_t)v;
-        if ((comp & pmask) == prefix) {
-          const uint32_t p = atomicAdd(&s_nsel, 1u);
-          if (p < (uint32_t)k_pow2) s_sel[p] = (uint32_t)v;
-        }
+        *e = (uint32_t)v;
+        return have && comp >= prefix;
+      };
+      for (int sp = wave; sp < S; sp += kSelThreads / 64) {
+        uint32_t e;
+        const unsigned long long m = __ballot(take(sp, &e));
+        if (lane == 0) s_sel[sp] = (uint32_t)__popcll(m);
       }
-    }
-    __syncthreads();
-    const uint32_t ns = min(s_nsel, (uint32_t)k);
-    for (int i = tid; i < k_pow2; i += kSelThreads) if ((uint32_t)i >= ns) s_sel[i] = 0xffffffffu;
-    __syncthreads();
-    // bitonic sort ascending
-    for (int size = 2; size <= k_pow2; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < k_pow2 / 2; i += kSelThreads) {
-          const int lo = 2 * i - (i & (stride - 1));
-          const int hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const uint32_t x = s_sel[lo], y = s_sel[hi];
-          if ((x > y) == up) {
-            s_sel[lo] = y;
-            s_sel[hi] = x;
-          }
-        }
-        __syncthreads();
+      __syncthreads();
+      if (tid < 64) scan_counts_wave0_n<kSelMaxSplits / 64>(s_sel, S);
+      __syncthreads();
+      for (int sp = wave; sp < S; sp += kSelThreads / 64) {
+        uint32_t e;
+        const bool tk = take(sp, &e);
+        const unsigned long long m = __ballot(tk);
+        const uint32_t at = s_sel[sp] + lanes_below(m);
+        if (tk && at < (uint32_t)k) orow[at] = (int32_t)e;
       }
+      for (int i = (int)k_eff + tid; i < k; i += kSelThreads) orow[i] = -1;
     }
-    for (int i = tid; i < k; i += kSelThreads) orow[i] = (uint32_t)i < ns ? (int32_t)s_sel[i] : -1;
     return;
   }
 
@@ -574,15 +614,12 @@ hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_
     hipLaunchKernelGGL(k_prefill_gemm<2>, ggrid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
                        idx_scale, n_entries, ratio, pos0, T, ws);
   }
-  int k_pow2 = 1;
-  while (k_pow2 < k) k_pow2 <<= 1;
-  const size_t lds = (size_t)kCandLds * 8 + (size_t)k_pow2 * 4;
+  const size_t lds = (size_t)kCandLds * 8;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_prefill_select), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)((size_t)kCandLds * 8 + (size_t)kMaxKPow2 * 4));
+      reinterpret_cast<const void*>(&k_prefill_select), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), lds, stream, q_idx, idx_codes,
-                     idx_scale, n_entries, ratio, pos0, T, k, k_pow2, idx_out, ws);
+                     idx_scale, n_entries, ratio, pos0, T, k, idx_out, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_attn(1, q, kv_codes, kv_scale, nullptr, idx_out, k, swa, nullptr, pos0, softmax_scale,
