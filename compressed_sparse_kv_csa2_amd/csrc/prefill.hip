@@ -44,8 +44,11 @@ constexpr int kRunStages = 4;               // group = one lane column over 32 t
 constexpr int kGroupsPerSplit = kStages / kRunStages * 32;  // 128
 constexpr int kSlots = 64;                  // candidate slots per (row, split): one per lane
 static_assert(kSlots == 64, "select copies one split per wave, one slot per lane");
+static_assert(kSplitEntries <= 4096, "queued hits hold the entry within its split in 12 bits");
+constexpr int kQueue = 64 + 256;           // pass-2 hit queue per wave: a batch + 4 rows' worst
 constexpr int kCandLds = 8192;              // candidates a row may gather into LDS
 constexpr int kSelThreads = 256;
+static_assert(kSelThreads == 256, "the theta and select kernels give each of 256 bins a thread");
 constexpr int kSelMaxSplits = 1024;         // splits a row's fast path can gather (N <= 4M)
 
 struct PrefillWs {
@@ -133,11 +136,15 @@ __device__ __forceinline__ int stage_blk(int i, int b) { return i * 4 + (b ^ ((i
 // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  Operands: lane l holds row/column l % 32 and
 // k-slice 8*(l/32)..+7; the dims behind k-step kk for half h are 64h + 8kk .. +7.
 template <int PASS>
-__global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
+__global__ __launch_bounds__(kGemmThreads, 3) void k_prefill_gemm(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
   __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
   __shared__ float s_sc[2][kStage];
+  // PASS 2: per wave, a queue of hits (score bits; entry - split start | wave row << 12) in
+  // (tile, r, lane) order, and the candidate count of each of the workgroup's rows
+  __shared__ uint2 s_q[4][PASS == 2 ? kQueue : 1];
+  __shared__ uint32_t s_rcnt[PASS == 2 ? kGemmRows : 1];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kGemmRows;
   const int row0 = wg_row0 + wave * 32;
@@ -167,20 +174,51 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
     const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
     nvis[r] = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
   }
-  // PASS 2: row thresholds, and the wave's candidate counts per accumulator row r for the
-  // rows of lanes 0-31 (clo) and 32-63 (chi); the wave owns its rows, so the counts are
-  // wave-uniform and slots follow the compare ballots in entry order
+  // PASS 2: row thresholds; the hit queue's fill (wave-uniform)
   float th[16];
-  uint32_t clo[16], chi[16];
+  uint32_t qn = 0;
   if (PASS == 2) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
       th[r] = t < T ? ws.theta[t] : __builtin_inff();
-      clo[r] = 0u;
-      chi[r] = 0u;
     }
+    if (lane < 32) s_rcnt[wave * 32 + lane] = 0u;
   }
+  // PASS 2: moves queued hits into their rows' slots, 64 at a time (all of them if `all`,
+  // else whole batches, the rest moved to the queue's front).  A hit's slot is its row's
+  // count so far plus the hits of the same row in lower lanes (lanes compared on the five
+  // row bits), so every row's slots stay in queue order, i.e. ascending entries.
+  auto flush = [&](bool all) {
+    uint32_t b = 0;
+    for (; b + 64 <= qn || (all && b < qn); b += 64) {
+      const bool valid = b + lane < qn;
+      const uint2 e = valid ? s_q[wave][b + lane] : make_uint2(0u, 0u);
+      const uint32_t lrow = e.y >> 12;
+      uint64_t eq = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 5; ++bit) {
+        const bool set = (lrow >> bit) & 1u;
+        const uint64_t bm = __ballot(set);
+        eq &= set ? bm : ~bm;
+      }
+      const uint32_t rank = lanes_below(eq);
+      const bool last = ((eq >> lane) >> 1) == 0ull;  // no higher lane holds this row
+      const uint32_t gr = wave * 32 + lrow;
+      const uint32_t slot = (valid ? s_rcnt[gr] : 0u) + rank;
+      if (valid && slot < (uint32_t)kSlots)
+        ws.cand[((size_t)(row0 + lrow) * ws.n_splits + split) * kSlots + slot] =
+            ((unsigned long long)score_key(__uint_as_float(e.x)) << 32) | (uint32_t)(e_begin + (e.y & 0xfffu));
+      if (valid && last) s_rcnt[gr] = slot + 1u;
+    }
+    if (!all) {
+      if (b + lane < qn) {
+        const uint2 e = s_q[wave][b + lane];  // b >= 64: source and destination are apart
+        s_q[wave][lane] = e;
+      }
+      qn -= b;
+    }
+  };
 
   // one entry per thread per stage: 4 x 16 code bytes + scale, clamped to a real entry
   uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
@@ -243,23 +281,26 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
             }
           }
         } else {
+          const uint32_t tag = (uint32_t)(col - e_begin) | ((uint32_t)half << 14);  // row bit 2 = half
+          auto push = [&](int r, float s, bool hit, uint64_t m) {  // m: the wave's hits
+            if (m == 0ull) return;
+            const uint32_t pos = qn + lanes_below(m);
+            if (hit) s_q[wave][pos] = make_uint2(__float_as_uint(s), tag | ((uint32_t)(8 * (r >> 2) + (r & 3)) << 12));
+            qn += (uint32_t)__builtin_popcountll(m);
+          };
+          if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float s = acc[r] * sc;
-            uint64_t m = mask_ge(s, th[r]);
-            if (!full) m &= mask_lt(col, nvis[r]);
-            if (m == 0ull) continue;
-            const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-            const uint32_t nlo = (uint32_t)__builtin_popcount(mlo);
-            // hits in lanes below this one; lanes 32-63 subtract the other row's (lanes 0-31)
-            const uint32_t below = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
-            const uint32_t slot = below + (half ? chi[r] - nlo : clo[r]);
-            clo[r] += nlo;
-            chi[r] += (uint32_t)__builtin_popcount(mhi);
-            if (((m >> lane) & 1ull) && slot < (uint32_t)kSlots) {
-              const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-              ws.cand[((size_t)t * ws.n_splits + split) * kSlots + slot] =
-                  ((unsigned long long)score_key(s) << 32) | (uint32_t)col;
+            for (int r = 0; r < 16; ++r) {
+              const float s = acc[r] * sc;
+              push(r, s, s >= th[r], mask_ge(s, th[r]));
+              if ((r & 3) == 3 && qn >= 64u) flush(false);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float s = acc[r] * sc;
+              push(r, s, s >= th[r] && col < nvis[r], mask_ge(s, th[r]) & mask_lt(col, nvis[r]));
+              if ((r & 3) == 3 && qn >= 64u) flush(false);
             }
           }
         }
@@ -280,13 +321,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_prefill_gemm(
     }
   }
 #undef CSA2_LOAD_STAGE
-  if (PASS == 2) {  // lane l < 32 reports wave row l: r = 4 * (l / 8) + l % 4, half (l / 4) % 2
-    uint32_t c = 0u;
-    const int lr_ = ((lane >> 3) << 2) | (lane & 3);
-    const bool lhi = (lane >> 2) & 1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) c = lr_ == r ? (lhi ? chi[r] : clo[r]) : c;
-    if (lane < 32 && row0 + lane < T) ws.ccount[(size_t)(row0 + lane) * ws.n_splits + split] = c;
+  if (PASS == 2) {
+    flush(true);
+    if (lane < 32 && row0 + lane < T)
+      ws.ccount[(size_t)(row0 + lane) * ws.n_splits + split] = s_rcnt[wave * 32 + lane];
   }
 }
 
@@ -349,42 +387,82 @@ __device__ uint32_t block_scan_excl(uint32_t v, uint32_t* scratch, uint32_t* tot
   return r;
 }
 
-// theta_t: the k-th largest group maximum of row t as a float lower bound, or -inf when
-// the row has at most k visible entries or fewer than k non-empty groups.
+// theta_t: +inf for a row that takes all its (at most k) visible entries; otherwise the
+// k-th largest group maximum of row t as a float lower bound, or -inf when the row has
+// fewer than k non-empty groups.
 __global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, int ratio,
                                                                int64_t pos0, int T, int k,
                                                                PrefillWs ws) {
-  __shared__ uint32_t s_hist[256];
+  // 256 bins, each spread over 16 copies (copy = lane % 16) so that the many lanes whose
+  // maxima share a bin do not serialise on one LDS word
+  __shared__ uint32_t s_hist[256 * 16];
+  __shared__ uint32_t s_bin[256];
   __shared__ uint32_t s_res[4];
-  __shared__ uint32_t s_scan[32];
   const int t = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n_t = visible(pos0 + t, ratio, n_entries);
-  if (n_t <= k) {
-    if (tid == 0) ws.theta[t] = -__builtin_inff();
+  if (n_t <= k) {  // the select takes every visible entry: no candidates
+    if (tid == 0) ws.theta[t] = __builtin_inff();
     return;
   }
-  const uint16_t* g = ws.gmax + (size_t)t * ws.G;
-  uint32_t nonempty = 0;
-  for (int i = tid; i < ws.G; i += kSelThreads) nonempty += g[i] != 0 ? 1u : 0u;
-  uint32_t total;
-  block_scan_excl(nonempty, s_scan, &total);
-  if (total < (uint32_t)k) {
-    if (tid == 0) ws.theta[t] = -__builtin_inff();
-    return;
+  // the row's G = 128 * n_splits maxima as 16-byte chunks; up to kRegChunks per thread stay
+  // in registers, a longer row is read again from memory at each level
+  constexpr int kRegChunks = 4;
+  const uint4* g4 = reinterpret_cast<const uint4*>(ws.gmax + (size_t)t * ws.G);
+  const int nch = ws.G / 8;
+  const bool cached = nch <= kRegChunks * kSelThreads;
+  uint4 w[kRegChunks];
+#pragma unroll
+  for (int j = 0; j < kRegChunks; ++j) {
+    const int c = tid + j * kSelThreads;
+    w[j] = cached && c < nch ? g4[c] : make_uint4(0u, 0u, 0u, 0u);
   }
+  auto count = [&](const uint4& v, int shift, int level, uint32_t prefix) {
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const uint32_t m = (x[h >> 1] >> (16 * (h & 1))) & 0xffffu;
+      if (m != 0u && (level == 0 || (m >> 8) == prefix))
+        atomicAdd(&s_hist[((m >> shift) & 255u) * 16 + (lane & 15)], 1u);
+    }
+  };
   uint32_t need = (uint32_t)k, prefix = 0;
   for (int level = 0; level < 2; ++level) {
     const int shift = 8 - 8 * level;
-    s_hist[tid] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) reinterpret_cast<uint4*>(s_hist)[tid + j * kSelThreads] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    for (int i = tid; i < ws.G; i += kSelThreads) {
-      const uint32_t v = g[i];
-      if (v != 0u && (level == 0 || (v >> 8) == prefix)) atomicAdd(&s_hist[(v >> shift) & 255u], 1u);
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < kRegChunks; ++j) count(w[j], shift, level, prefix);
+    } else {
+      for (int c = tid; c < nch; c += kSelThreads) count(g4[c], shift, level, prefix);
     }
     __syncthreads();
-    if (tid < 64) find_bin_wave(s_hist, 256, need, s_res);
+    {
+      const uint4* hp = reinterpret_cast<const uint4*>(s_hist + tid * 16);
+      uint32_t b = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = hp[i];
+        b += v.x + v.y + v.z + v.w;
+      }
+      s_bin[tid] = b;
+    }
     __syncthreads();
+    if (tid < 64) {
+      find_bin_wave(s_bin, 256, need, s_res);
+      if (level == 0) {  // non-empty groups: the histogram's total
+        uint32_t tot = s_bin[4 * lane] + s_bin[4 * lane + 1] + s_bin[4 * lane + 2] + s_bin[4 * lane + 3];
+        tot = wave_incl_scan(tot);
+        if (lane == 63) s_res[2] = tot;
+      }
+    }
+    __syncthreads();
+    if (level == 0 && s_res[2] < (uint32_t)k) {  // fewer than k non-empty groups
+      if (tid == 0) ws.theta[t] = -__builtin_inff();
+      return;
+    }
     need -= s_res[1];
     prefix = level == 0 ? s_res[0] : (prefix << 8) | s_res[0];
     __syncthreads();
