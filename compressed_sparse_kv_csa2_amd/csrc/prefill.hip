@@ -46,10 +46,10 @@ constexpr int kSlots = 64;                  // candidate slots per (row, split):
 static_assert(kSlots == 64, "select copies one split per wave, one slot per lane");
 static_assert(kSplitEntries <= 4096, "queued hits hold the entry within its split in 12 bits");
 constexpr int kQueue = 64 + 256;           // pass-2 hit queue per wave: a batch + 4 rows' worst
-constexpr int kCandLds = 8192;              // candidates a row may gather into LDS
+constexpr int kCandLds = 4096;              // candidates a row may gather into LDS
 constexpr int kSelThreads = 256;
 static_assert(kSelThreads == 256, "the theta and select kernels give each of 256 bins a thread");
-constexpr int kSelMaxSplits = 1024;         // splits a row's fast path can gather (N <= 4M)
+constexpr int kSelMaxSplits = 512;          // splits a row's fast path can gather (N <= 2M)
 
 struct PrefillWs {
   uint16_t* gmax;               // [T][G] group maxima as key >> 16 (0 = empty group)
@@ -498,13 +498,13 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, int k,
     int32_t* __restrict__ idx_out, PrefillWs ws) {
-  extern __shared__ unsigned long long s_dyn[];
-  unsigned long long* s_cand = s_dyn;                                         // [kCandLds]
-  __shared__ uint32_t s_hist[256];
+  __shared__ unsigned long long s_cand[kCandLds];
+  __shared__ uint32_t s_hist[3][256];  // radix levels cycle through three histograms
   __shared__ uint32_t s_res[4];
   __shared__ uint32_t s_scan[32];
   __shared__ uint32_t s_total, s_over;
-  __shared__ uint32_t s_cnt[kSelMaxSplits], s_off[kSelMaxSplits], s_sel[kSelMaxSplits];
+  __shared__ uint32_t s_co[kSelMaxSplits];   // split's first candidate | its count << 16
+  __shared__ uint32_t s_sel[kSelMaxSplits];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_t = visible(pos0 + t, ratio, n_entries);
@@ -535,8 +535,7 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
         if (lane >= off) incl += v;
       }
       if (s < S) {
-        s_cnt[s] = n;
-        s_off[s] = carry + incl - n;
+        s_co[s] = (carry + incl - n) | (n << 16);  // offsets < 512 * 64
       }
       carry += __shfl(incl, 63);
     }
@@ -557,41 +556,58 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const int s = s0 + j * (kSelThreads / 64);
-          const bool have = s < S && lane < (int)s_cnt[min(s, S - 1)];
+          const bool have = s < S && lane < (int)(s_co[min(s, S - 1)] >> 16);
           v[j] = have ? ws.cand[((size_t)t * S + s) * kSlots + lane] : 0ull;
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const int s = s0 + j * (kSelThreads / 64);
-          if (s < S && lane < (int)s_cnt[s]) s_cand[s_off[s] + lane] = v[j];
+          if (s < S && lane < (int)(s_co[s] >> 16)) s_cand[(s_co[s] & 0xffffu) + lane] = v[j];
         }
       }
     }
+    s_hist[0][tid] = 0u;
     __syncthreads();
     // composite: key (32 bits) then ~entry (a lower entry ranks higher); 8 digits of 8 bits.
     // Radix levels find the threshold composite: the row takes every candidate >= prefix
-    // (lower digits zero once a level's bin is taken whole).
+    // (lower digits zero once a level's bin is taken whole).  Level L counts into histogram
+    // L % 3 while clearing histogram (L + 1) % 3, and every wave finds the level's bin
+    // itself, so a level costs one barrier.
     uint32_t need = k_eff;
     unsigned long long prefix = 0ull, pmask = 0ull;
     uint32_t remaining = C;
+    const int lane = tid & 63;
     for (int level = 0; level < 8 && need > 0 && need < remaining; ++level) {
       const int shift = 56 - 8 * level;
-      s_hist[tid] = 0u;
-      __syncthreads();
+      uint32_t* h = s_hist[level % 3];
+      s_hist[(level + 1) % 3][tid] = 0u;
       for (uint32_t i = tid; i < C; i += kSelThreads) {
         const unsigned long long v = s_cand[i];
         const unsigned long long comp = (v & 0xffffffff00000000ull) | (uint32_t)~(uint32_t)v;
-        if ((comp & pmask) == prefix) atomicAdd(&s_hist[(comp >> shift) & 255ull], 1u);
+        if ((comp & pmask) == prefix) atomicAdd(&h[(comp >> shift) & 255ull], 1u);
       }
       __syncthreads();
-      if (tid < 64) find_bin_wave(s_hist, 256, need, s_res);
-      __syncthreads();
-      const uint32_t sel = s_res[0];
-      need -= s_res[1];
-      remaining = s_hist[sel];
+      // the bin holding the need-th largest: lane l sums bins 255-4l .. 252-4l
+      const uint4 hv = reinterpret_cast<const uint4*>(h)[63 - lane];  // bins 252-4l .. 255-4l
+      const uint32_t c3 = hv.w, c2 = hv.z, c1 = hv.y, c0 = hv.x;
+      const uint32_t sum = c0 + c1 + c2 + c3;
+      const uint32_t incl = wave_incl_scan(sum);
+      const uint32_t excl = incl - sum;
+      const uint64_t hitm = __ballot(excl < need && need <= incl);
+      const int src = __builtin_amdgcn_readfirstlane(max(__builtin_ffsll((long long)hitm) - 1, 0));
+      uint32_t sel, above;
+      {
+        uint32_t a = excl, b = 252u - 4u * (uint32_t)lane + 3u, r = c3;
+        if (a + c3 < need) { a += c3; b -= 1; r = c2;
+          if (a + c2 < need) { a += c2; b -= 1; r = c1;
+            if (a + c1 < need) { a += c1; b -= 1; r = c0; } } }
+        sel = (uint32_t)__builtin_amdgcn_readlane((int)b, src);
+        above = (uint32_t)__builtin_amdgcn_readlane((int)a, src);
+        remaining = (uint32_t)__builtin_amdgcn_readlane((int)r, src);
+      }
+      need -= above;
       prefix |= (unsigned long long)sel << shift;
       pmask |= 255ull << shift;
-      __syncthreads();
     }
     // ---- the selected candidates in ascending entry order: splits hold ascending entry
     // ranges and a split's slots are in entry order, so each wave compacts one split's
@@ -599,8 +615,9 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     {
       const int wave = tid >> 6, lane = tid & 63;
       auto take = [&](int sp, uint32_t* e) {
-        const bool have = lane < (int)s_cnt[sp];
-        const unsigned long long v = have ? s_cand[s_off[sp] + lane] : 0ull;
+        const uint32_t co = s_co[sp];
+        const bool have = lane < (int)(co >> 16);
+        const unsigned long long v = have ? s_cand[(co & 0xffffu) + lane] : 0ull;
         const unsigned long long comp = (v & 0xffffffff00000000ull) | (uint32_t)~(uint32_t)v;
         *e = (uint32_t)v;
         return have && comp >= prefix;
@@ -642,15 +659,15 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
   unsigned long long prefix = 0ull, pmask = 0ull;
   for (int level = 0; level < 8 && need > 0; ++level) {
     const int shift = 56 - 8 * level;
-    s_hist[tid] = 0u;
+    s_hist[0][tid] = 0u;
     __syncthreads();
     for (int j = tid; j < n_t; j += kSelThreads) {
       const unsigned long long comp =
           ((unsigned long long)score_key(score_row(qq, codes, scale, j)) << 32) | (uint32_t)~(uint32_t)j;
-      if ((comp & pmask) == prefix) atomicAdd(&s_hist[(comp >> shift) & 255ull], 1u);
+      if ((comp & pmask) == prefix) atomicAdd(&s_hist[0][(comp >> shift) & 255ull], 1u);
     }
     __syncthreads();
-    if (tid < 64) find_bin_wave(s_hist, 256, need, s_res);
+    if (tid < 64) find_bin_wave(s_hist[0], 256, need, s_res);
     __syncthreads();
     need -= s_res[1];
     prefix |= (unsigned long long)s_res[0] << shift;
@@ -692,11 +709,7 @@ hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_
     hipLaunchKernelGGL(k_prefill_gemm<2>, ggrid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
                        idx_scale, n_entries, ratio, pos0, T, ws);
   }
-  const size_t lds = (size_t)kCandLds * 8;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_prefill_select), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), lds, stream, q_idx, idx_codes,
+  hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), 0, stream, q_idx, idx_codes,
                      idx_scale, n_entries, ratio, pos0, T, k, idx_out, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
