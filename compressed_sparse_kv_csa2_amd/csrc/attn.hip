@@ -151,6 +151,9 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
   __shared__ __align__(16) f16 s_v[kAW][kSeg * kHalf];         // each wave's half of a segment
   __shared__ __align__(16) f16 s_p[2][kSeg * kHeads];          // p hi / lo, [position][head]
   __shared__ __align__(16) f32x4v s_z[kAW][64];                // partial scores per lane
+  __shared__ __align__(16) float s_alpha[kHeads];              // this segment's rescale per head
+  __shared__ __align__(16) float s_ml[2][kHeads];              // final max and sum per head
+  __shared__ uint32_t s_mv[kAW];                               // a wave's heads moved their max
   __shared__ int32_t s_idx[kIdxStage];
 
   const int split = blockIdx.x, b = blockIdx.y;
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
   // a power of two into fp16's range
   const uint16_t* qrow = q + ((size_t)b * kHeads + n16) * kDKv;
   f16x8 qa[8];
-  float qs[4];  // softmax scale of heads 4 g16 + r (log2 units), with the head's power of two
+  float qs[2];  // softmax scale of heads 8 w + 2 g16 + j (log2 units), with the head's power of two
   {
     uint4 raw[8];
 #pragma unroll
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       qa[s] = f16x8{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) qs[r] = qscale * ldexpf(1.0f, __shfl(e, 4 * g16 + r));
+    for (int j = 0; j < 2; ++j) qs[j] = qscale * ldexpf(1.0f, __shfl(e, 8 * w + 2 * g16 + j));
   }
 
   const int64_t base = MODE == 0 ? seq_base[b] : 0;
@@ -235,13 +238,15 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
   const int seg_end = min(seg_begin + segs_per_split, n_seg);
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(qrow);  // any valid 64 bytes
 
-  // running softmax state of heads 4 g16 + r (the same in both waves) and this wave's
-  // accumulators: acc[t] = tile t of its half, lane (dim 16 t + n16, heads 4 g16 + r)
-  float m[4], l[4];
+  // running softmax state: wave w, lane (position n16, g16) runs heads 8 w + 2 g16 + j
+  // (j = 0, 1): the running max (the same in the head's 16 lanes) and this lane's share of
+  // the sum (its position's terms, added over the lanes at the end).  Accumulators of this
+  // wave: acc[t] = tile t of its half, lane (dim 16 t + n16, heads 4 g16 + r)
+  float m[2], lp[2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -__builtin_inff();
-    l[r] = 0.f;
+  for (int j = 0; j < 2; ++j) {
+    m[j] = -__builtin_inff();
+    lp[j] = 0.f;
   }
   f32x4v acc[kHalfTiles];
 #pragma unroll
@@ -328,37 +333,45 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       // ---- the two halves' scores, added in the same order in both waves
       s_z[w][lane] = z;
       __syncthreads();
-      const f32x4v z0 = s_z[0][lane], z1 = s_z[1][lane];
-      // ---- online softmax over the segment's positions (lane: position n16, heads 4 g16 + r)
+      // ---- online softmax over the segment's positions for this wave's eight heads
+      const int zl = 16 * (2 * w + (g16 >> 1)) + n16;  // tile lane holding heads 8w+2g16+j
+      const float2 za = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&s_z[0][zl]) + 2 * (g16 & 1));
+      const float2 zb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&s_z[1][zl]) + 2 * (g16 & 1));
+      const float zsum[2] = {za.x + zb.x, za.y + zb.y};
       const bool valid = r.kind != 0;
-      float p[4], alpha[4];
+      float p[2], alpha[2];
       bool moved = false;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float zs = valid ? (z0[rr] + z1[rr]) * qs[rr] : -__builtin_inff();
+      for (int j = 0; j < 2; ++j) {
+        const float zs = valid ? zsum[j] * qs[j] : -__builtin_inff();
         const float cm = row16<true>(zs);
-        const float mu = cm > m[rr] + kRescale ? cm : m[rr];
-        alpha[rr] = mu == m[rr] ? 1.0f : (m[rr] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[rr] - mu));
-        moved |= mu != m[rr];
-        m[rr] = mu;
-        p[rr] = zs == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(zs - mu);
-        l[rr] = l[rr] * alpha[rr] + row16<false>(p[rr]);
+        const float mu = cm > m[j] + kRescale ? cm : m[j];
+        alpha[j] = mu == m[j] ? 1.0f : (m[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[j] - mu));
+        moved |= mu != m[j];
+        m[j] = mu;
+        p[j] = zs == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(zs - mu);
+        lp[j] = lp[j] * alpha[j] + p[j];
       }
-      if (__ballot(moved) != 0ull) {
+      // p = hi + lo in fp16, staged as [position][head]; each head's rescale and whether a
+      // wave's maxima moved
+      {
+        const f16 h0 = (f16)p[0], h1 = (f16)p[1];
+        const f16 o0 = (f16)(p[0] - (float)h0), o1 = (f16)(p[1] - (float)h1);
+        const int at = n16 * kHeads + 8 * w + 2 * g16;
+        *reinterpret_cast<f16x2*>(s_p[0] + at) = f16x2{h0, h1};
+        *reinterpret_cast<f16x2*>(s_p[1] + at) = f16x2{o0, o1};
+        if (n16 == 0) *reinterpret_cast<float2*>(s_alpha + 8 * w + 2 * g16) = float2{alpha[0], alpha[1]};
+        const bool mv = __ballot(moved) != 0ull;
+        if (lane == 0) s_mv[w] = mv ? 1u : 0u;
+      }
+      __syncthreads();
+      if ((s_mv[0] | s_mv[1]) != 0u) {
+        const f32x4v al = *reinterpret_cast<const f32x4v*>(s_alpha + 4 * g16);
 #pragma unroll
         for (int t = 0; t < kHalfTiles; ++t)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) acc[t][rr] *= alpha[rr];
+          for (int rr = 0; rr < 4; ++rr) acc[t][rr] *= al[rr];
       }
-      // p = hi + lo in fp16, staged as [position][head]: wave 0 writes hi, wave 1 lo
-      f16 pp[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f16 hi = (f16)p[rr];
-        pp[rr] = w == 0 ? hi : (f16)(p[rr] - (float)hi);
-      }
-      *reinterpret_cast<f16x4*>(s_p[w] + n16 * kHeads + 4 * g16) = f16x4{pp[0], pp[1], pp[2], pp[3]};
-      __syncthreads();
       // ---- acc += p . v over this wave's half: A = p (head, 4 positions), B = v, transposed
       const f16x4 a_hi = tr_read(s_p[0] + tr_row * kHeads + 4 * tr_q);
       const f16x4 a_lo = tr_read(s_p[1] + tr_row * kHeads + 4 * tr_q);
@@ -389,25 +402,32 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     }
   }
 
-  // ---- out (one split) or this split's (max, sum, acc)
+  // ---- each head's max and sum (over its 16 lanes' shares), then out (one split) or this
+  // split's (max, sum, acc)
+  {
+    const float lt0 = row16<false>(lp[0]), lt1 = row16<false>(lp[1]);
+    if (n16 == 0) {
+      *reinterpret_cast<float2*>(s_ml[0] + 8 * w + 2 * g16) = float2{m[0], m[1]};
+      *reinterpret_cast<float2*>(s_ml[1] + 8 * w + 2 * g16) = float2{lt0, lt1};
+    }
+  }
+  __syncthreads();
   if (MODE == 1 || n_splits == 1) {
     float* O = out + (size_t)b * kHeads * kDKv + kHalf * w;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * g16 + r;
-      const float inv = l[r] > 0.f ? 1.0f / l[r] : 0.f;
+      const float lh = s_ml[1][h];
+      const float inv = lh > 0.f ? 1.0f / lh : 0.f;
 #pragma unroll
       for (int t = 0; t < kHalfTiles; ++t) O[h * kDKv + 16 * t + n16] = acc[t][r] * inv;
     }
     return;
   }
   float* P = part + ((size_t)b * n_splits + split) * kPart;
-  if (w == 0 && n16 == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      P[4 * g16 + r] = m[r];
-      P[kHeads + 4 * g16 + r] = l[r];
-    }
+  if (tid < kHeads) {
+    P[tid] = s_ml[0][tid];
+    P[kHeads + tid] = s_ml[1][tid];
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r)
