@@ -8,9 +8,10 @@
 // its last token (j+1)*ratio - 1 is at or before p.
 //
 // S[t][j] = scale_j * (q_t . e2m1(K_j)) is a dense T x N x 128 contraction on
-// v_mfma_f32_32x32x16_bf16.  A workgroup owns 128 query rows (32 per wave, held as A
-// operands) and one split of 4,096 entries, which it streams through LDS in stages of 256
-// entries (raw 64 code bytes + fp32 scale each, double buffered, the next stage's loads in
+// v_mfma_f32_32x32x16_bf16.  A workgroup owns 256 query rows (64 per wave, held as two
+// sets of A operands that share every expanded B operand) and one split of 4,096 entries,
+// which it streams through LDS in stages of 256 entries (raw 64 code bytes + fp32 scale
+// each, double buffered, the next stage's loads in
 // flight during the current stage's MFMAs, shared by the four waves).  Each wave expands
 // its B operands from LDS to bf16 exactly (v_cvt_scalef32_pk_bf16_fp4); the 128 dims are
 // permuted identically on both sides so each lane reads 32 contiguous code bytes.  The
@@ -35,8 +36,10 @@
 
 namespace csa2 {
 
-constexpr int kGemmThreads = 256;           // 4 waves x 32 query rows
-constexpr int kGemmRows = 128;
+constexpr int kGemmThreads = 256;           // 4 waves x 64 query rows
+constexpr int kSets = 2;                    // 32-row A operand sets per wave
+constexpr int kWaveRows = 32 * kSets;
+constexpr int kGemmRows = 4 * kWaveRows;
 constexpr int kSplitEntries = 4096;         // entries per workgroup
 constexpr int kStage = 256;                 // entries per LDS stage (8 tiles of 32)
 constexpr int kStages = kSplitEntries / kStage;
@@ -115,15 +118,15 @@ __device__ __forceinline__ float vmax(float a, float b) {
   return r;
 }
 
-// Lane masks of a >= b (floats) and a < b (ints), straight from v_cmp (every lane active).
+// Lane masks of a >= b (floats) and a <= b (ints), straight from v_cmp (every lane active).
 __device__ __forceinline__ uint64_t mask_ge(float a, float b) {
   uint64_t m;
   asm("v_cmp_ge_f32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
   return m;
 }
-__device__ __forceinline__ uint64_t mask_lt(int a, int b) {
+__device__ __forceinline__ uint64_t mask_le(int a, int b) {
   uint64_t m;
-  asm("v_cmp_lt_i32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
+  asm("v_cmp_le_i32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
   return m;
 }
 
@@ -135,19 +138,21 @@ __device__ __forceinline__ int stage_blk(int i, int b) { return i * 4 + (b ^ ((i
 // Accumulator layout of v_mfma_f32_32x32x16_bf16: lane l holds column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  Operands: lane l holds row/column l % 32 and
 // k-slice 8*(l/32)..+7; the dims behind k-step kk for half h are 64h + 8kk .. +7.
+// A wave owns 64 rows as two sets of 32 (set s: rows 32s ..); each expanded B operand
+// feeds one MFMA per set.
 template <int PASS>
-__global__ __launch_bounds__(kGemmThreads, 3) void k_prefill_gemm(
+__global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
   __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
   __shared__ float s_sc[2][kStage];
   // PASS 2: per wave, a queue of hits (score bits; entry - split start | wave row << 12) in
-  // (tile, r, lane) order, and the candidate count of each of the workgroup's rows
+  // (tile, set, r, lane) order, and the candidate count of each of the workgroup's rows
   __shared__ uint2 s_q[4][PASS == 2 ? kQueue : 1];
   __shared__ uint32_t s_rcnt[PASS == 2 ? kGemmRows : 1];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kGemmRows;
-  const int row0 = wg_row0 + wave * 32;
+  const int row0 = wg_row0 + wave * kWaveRows;
   const int split = blockIdx.y;
   const int e_begin = split * kSplitEntries;
   const int e_end = min(e_begin + kSplitEntries, n_entries);
@@ -155,39 +160,47 @@ __global__ __launch_bounds__(kGemmThreads, 3) void k_prefill_gemm(
 
   // entries any row of the workgroup can see, and of this wave's rows
   const int wg_nmax = visible(pos0 + min(wg_row0 + kGemmRows - 1, T - 1), ratio, n_entries);
-  const int wave_nmax = row0 < T ? visible(pos0 + min(row0 + 31, T - 1), ratio, n_entries) : 0;
+  const int wave_nmax = row0 < T ? visible(pos0 + min(row0 + kWaveRows - 1, T - 1), ratio, n_entries) : 0;
   const int wave_nmin = row0 < T ? visible(pos0 + row0, ratio, n_entries) : 0;
   const int e_stop = min(e_end, wg_nmax);
   const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
 
-  // A operand: query row row0 + rl, dims 64*half .. +63
-  bf16x8 a[8];
-  {
-    const int ar = min(row0 + rl, T - 1);
+  // A operands: query row row0 + 32*s + rl, dims 64*half .. +63
+  bf16x8 a[kSets][8];
+#pragma unroll
+  for (int s = 0; s < kSets; ++s) {
+    const int ar = min(row0 + 32 * s + rl, T - 1);
     const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)ar * kDIdx + 64 * half);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) a[kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+    for (int kk = 0; kk < 8; ++kk) a[s][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
   }
-  int nvis[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    nvis[r] = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
-  }
+  // row of accumulator r of set s within the wave
+  auto wrow = [&](int s, int r) { return 32 * s + 8 * (r >> 2) + 4 * half + (r & 3); };
+  // On a tile at the causal frontier, entry col is visible to wave row w once its last
+  // position (col+1)*ratio - 1 is at most pos0 + row0 + w, i.e. once lim <= w - 4*half with
+  // lim the lane's offset below (clamped: far from the frontier only its sign matters).
+  // Rows past T need no mask: their maxima are never published and their thresholds are +inf.
+  auto frontier_lim = [&](int col) {
+    const int64_t d = (int64_t)(col + 1) * ratio - 1 - (pos0 + row0 + 4 * half);
+    return col < n_entries ? (int)max(min(d, (int64_t)1 << 30), -((int64_t)1 << 30)) : (1 << 30);
+  };
+  auto wrow_h = [&](int s, int r) { return 32 * s + 8 * (r >> 2) + (r & 3); };  // wrow - 4*half
   // PASS 2: row thresholds; the hit queue's fill (wave-uniform)
-  float th[16];
+  float th[kSets][16];
   uint32_t qn = 0;
   if (PASS == 2) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      th[r] = t < T ? ws.theta[t] : __builtin_inff();
-    }
-    if (lane < 32) s_rcnt[wave * 32 + lane] = 0u;
+    for (int s = 0; s < kSets; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = row0 + wrow(s, r);
+        th[s][r] = t < T ? ws.theta[t] : __builtin_inff();
+      }
+    s_rcnt[wave * kWaveRows + lane] = 0u;
   }
   // PASS 2: moves queued hits into their rows' slots, 64 at a time (all of them if `all`,
   // else whole batches, the rest moved to the queue's front).  A hit's slot is its row's
-  // count so far plus the hits of the same row in lower lanes (lanes compared on the five
+  // count so far plus the hits of the same row in lower lanes (lanes compared on the six
   // row bits), so every row's slots stay in queue order, i.e. ascending entries.
   auto flush = [&](bool all) {
     uint32_t b = 0;
@@ -197,14 +210,14 @@ __global__ __launch_bounds__(kGemmThreads, 3) void k_prefill_gemm(
       const uint32_t lrow = e.y >> 12;
       uint64_t eq = __ballot(valid);
 #pragma unroll
-      for (int bit = 0; bit < 5; ++bit) {
+      for (int bit = 0; bit < 6; ++bit) {
         const bool set = (lrow >> bit) & 1u;
         const uint64_t bm = __ballot(set);
         eq &= set ? bm : ~bm;
       }
       const uint32_t rank = lanes_below(eq);
       const bool last = ((eq >> lane) >> 1) == 0ull;  // no higher lane holds this row
-      const uint32_t gr = wave * 32 + lrow;
+      const uint32_t gr = wave * kWaveRows + lrow;
       const uint32_t slot = (valid ? s_rcnt[gr] : 0u) + rank;
       if (valid && slot < (uint32_t)kSlots)
         ws.cand[((size_t)(row0 + lrow) * ws.n_splits + split) * kSlots + slot] =
@@ -235,9 +248,11 @@ __global__ __launch_bounds__(kGemmThreads, 3) void k_prefill_gemm(
   } while (0)
   if (n_active > 0) CSA2_LOAD_STAGE(0);
 
-  float rm[16];
+  float rm[kSets][16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) rm[r] = -__builtin_inff();
+  for (int s = 0; s < kSets; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rm[s][r] = -__builtin_inff();
 
   for (int st = 0; st < kStages; ++st) {
     if (st < n_active) {
@@ -258,49 +273,61 @@ __global__ __launch_bounds__(kGemmThreads, 3) void k_prefill_gemm(
         const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
         const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
         const float sc = s_sc[buf][i];
-        f32x16 acc = {};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], fp4x8_bf16(c0.x), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], fp4x8_bf16(c0.y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], fp4x8_bf16(c0.z), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], fp4x8_bf16(c0.w), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[4], fp4x8_bf16(c1.x), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[5], fp4x8_bf16(c1.y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[6], fp4x8_bf16(c1.z), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[7], fp4x8_bf16(c1.w), acc, 0, 0, 0);
+        f32x16 acc[kSets];
+#pragma unroll
+        for (int s = 0; s < kSets; ++s) acc[s] = f32x16{};
+        const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 bv = fp4x8_bf16(cw[kk]);
+#pragma unroll
+          for (int s = 0; s < kSets; ++s)
+            acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][kk], bv, acc[s], 0, 0, 0);
+        }
         const int col = e0 + rl;
         const bool full = e0 + 32 <= wave_nmin;  // wave-uniform: every row sees the tile
         if (PASS == 1) {
           if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) rm[r] = vmax(acc[r] * sc, rm[r]);
-          } else {
+            for (int s = 0; s < kSets; ++s)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float s = acc[r] * sc;
-              rm[r] = col < nvis[r] ? vmax(s, rm[r]) : rm[r];
-            }
+              for (int r = 0; r < 16; ++r) rm[s][r] = vmax(acc[s][r] * sc, rm[s][r]);
+          } else {
+            const int lim = frontier_lim(col);
+#pragma unroll
+            for (int s = 0; s < kSets; ++s)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float v = acc[s][r] * sc;
+                rm[s][r] = lim <= wrow_h(s, r) ? vmax(v, rm[s][r]) : rm[s][r];
+              }
           }
         } else {
-          const uint32_t tag = (uint32_t)(col - e_begin) | ((uint32_t)half << 14);  // row bit 2 = half
-          auto push = [&](int r, float s, bool hit, uint64_t m) {  // m: the wave's hits
+          const uint32_t tag = (uint32_t)(col - e_begin);
+          auto push = [&](int s, int r, float v, bool hit, uint64_t m) {  // m: the wave's hits
             if (m == 0ull) return;
             const uint32_t pos = qn + lanes_below(m);
-            if (hit) s_q[wave][pos] = make_uint2(__float_as_uint(s), tag | ((uint32_t)(8 * (r >> 2) + (r & 3)) << 12));
+            if (hit) s_q[wave][pos] = make_uint2(__float_as_uint(v), tag | ((uint32_t)wrow(s, r) << 12));
             qn += (uint32_t)__builtin_popcountll(m);
           };
-          if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float s = acc[r] * sc;
-              push(r, s, s >= th[r], mask_ge(s, th[r]));
-              if ((r & 3) == 3 && qn >= 64u) flush(false);
-            }
-          } else {
+          for (int s = 0; s < kSets; ++s) {
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float s = acc[r] * sc;
-              push(r, s, s >= th[r] && col < nvis[r], mask_ge(s, th[r]) & mask_lt(col, nvis[r]));
-              if ((r & 3) == 3 && qn >= 64u) flush(false);
+              for (int r = 0; r < 16; ++r) {
+                const float v = acc[s][r] * sc;
+                push(s, r, v, v >= th[s][r], mask_ge(v, th[s][r]));
+                if ((r & 3) == 3 && qn >= 64u) flush(false);
+              }
+            } else {
+              const int lim = frontier_lim(col);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float v = acc[s][r] * sc;
+                const int w = wrow_h(s, r);
+                push(s, r, v, v >= th[s][r] && lim <= w, mask_ge(v, th[s][r]) & mask_le(lim, w));
+                if ((r & 3) == 3 && qn >= 64u) flush(false);
+              }
             }
           }
         }
@@ -309,22 +336,24 @@ __global__ __launch_bounds__(kGemmThreads, 3) void k_prefill_gemm(
     if (PASS == 1 && (st + 1) % kRunStages == 0) {  // end of a run: publish the group maxima
       const int g = split * kGroupsPerSplit + (st / kRunStages) * 32 + rl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (t < T) {
-          const uint16_t key16 =
-              rm[r] == -__builtin_inff() ? (uint16_t)0 : (uint16_t)(score_key(rm[r]) >> 16);
-          ws.gmax[(size_t)t * ws.G + g] = key16;
+      for (int s = 0; s < kSets; ++s)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = row0 + wrow(s, r);
+          if (t < T) {
+            const uint16_t key16 =
+                rm[s][r] == -__builtin_inff() ? (uint16_t)0 : (uint16_t)(score_key(rm[s][r]) >> 16);
+            ws.gmax[(size_t)t * ws.G + g] = key16;
+          }
+          rm[s][r] = -__builtin_inff();
         }
-        rm[r] = -__builtin_inff();
-      }
     }
   }
 #undef CSA2_LOAD_STAGE
   if (PASS == 2) {
     flush(true);
-    if (lane < 32 && row0 + lane < T)
-      ws.ccount[(size_t)(row0 + lane) * ws.n_splits + split] = s_rcnt[wave * 32 + lane];
+    if (row0 + lane < T)
+      ws.ccount[(size_t)(row0 + lane) * ws.n_splits + split] = s_rcnt[wave * kWaveRows + lane];
   }
 }
 
