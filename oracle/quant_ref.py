@@ -52,7 +52,9 @@ def _nearest_code(a: np.ndarray, table: np.ndarray) -> np.ndarray:
     d_lo = np.abs(a - table[lo])
     d_hi = np.abs(table[hi] - a)
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    return np.where(pick_hi, hi, lo)
+    # at or past the largest value: saturate (for huge values the two fp64 distances are
+    # equal and the tie rule above would pick the lower neighbour)
+    return np.where(a >= table[-1], len(table) - 1, np.where(pick_hi, hi, lo))
 
 
 _E2M1_MAG = e2m1_decode(np.arange(8))                    # 0, .5, 1, 1.5, 2, 3, 4, 6

@@ -37,8 +37,8 @@ def test_e4m3_encode_matches_torch_cast():
 def test_e4m3_encode_roundtrip_and_saturation():
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
     assert np.array_equal(oracle.e4m3_encode(formats.e4m3_decode(codes)), codes)
-    big = np.array([449.0, 463.9, 464.0, 480.0, 1e6, -500.0])
-    assert list(oracle.e4m3_encode(big)) == [0x7E] * 5 + [0xFE]
+    big = np.array([449.0, 463.9, 464.0, 480.0, 1e6, 1e30, 3e38, -500.0])
+    assert list(oracle.e4m3_encode(big)) == [0x7E] * 7 + [0xFE]
 
 
 def test_e2m1_encode_table_ties_and_saturation():
@@ -50,7 +50,7 @@ def test_e2m1_encode_table_ties_and_saturation():
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
     assert list(oracle.e2m1_encode(mids)) == [0, 2, 2, 4, 4, 6, 6]
     assert list(oracle.e2m1_encode(-mids)) == [8, 10, 10, 12, 12, 14, 14]
-    assert list(oracle.e2m1_encode(np.array([6.5, 100.0, -7.0], np.float32))) == [7, 7, 15]
+    assert list(oracle.e2m1_encode(np.array([6.5, 100.0, -7.0, 1e30, -3e38], np.float32))) == [7, 7, 15, 7, 15]
     assert list(oracle.e2m1_encode(np.array([-0.0, -1e-30, 0.2499], np.float32))) == [8, 8, 0]
 
 
