@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5"])
+    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5", "append"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: the "
                    "workload's default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -431,6 +431,79 @@ class Prefill:
                           f"calls on {bt} threads, element-wise decoding on one; {dt:.1f} s"}
 
 
+class Append:
+    """The KV write path: one layer's new entries for a 262,144-token prompt at 1:2
+    (131,072 entries quantised into the 68 B + 288 B formats, written contiguously), and, as
+    a separate phase, one new window row for each of 32 sequences."""
+
+    N = 131072
+    B_SWA = 32
+
+    def __init__(self, args, torch, synth, csa2, dev):
+        self.torch, self.csa2 = torch, csa2
+        n_sets = args.sets or 2
+        print(f"generating {n_sets} append sets ({self.N} entries)", file=sys.stderr, flush=True)
+        self.sets = [synth.make_append_vectors(self.N, seed=50 + s, device=dev) for s in range(n_sets)]
+        self.rows = synth.make_window_rows(self.B_SWA, seed=50, device=dev)
+        self.pos = torch.arange(1000, 1000 + self.B_SWA, dtype=torch.int64, device=dev)
+        self.swa = torch.zeros((self.B_SWA, SWA, D_KV), dtype=torch.uint8, device=dev)
+        self.dst = torch.arange(self.N, dtype=torch.int64, device=dev)
+        self.planes = (torch.zeros((self.N, 64), dtype=torch.uint8, device=dev),
+                       torch.zeros((self.N,), dtype=torch.float32, device=dev),
+                       torch.zeros((self.N, 256), dtype=torch.uint8, device=dev),
+                       torch.zeros((self.N, 32), dtype=torch.uint8, device=dev))
+        self.stream = torch.cuda.current_stream()
+        self.queries_per_step = self.N
+        self.n_marks = 3
+        self.phase_names = ["kv_append_us", "swa_append_us"]
+
+    def step(self, i, marks=None):
+        xi, xk = self.sets[i % len(self.sets)]
+        s = self.stream
+        m = marks if marks is not None else Marks([None] * 3)
+        m[0].record(s)
+        self.csa2.csa2_kv_append(xi, xk, self.dst, *self.planes, stream=s)
+        m[1].record(s)
+        self.csa2.csa2_swa_append(self.rows, self.pos, self.swa, stream=s)
+        m[2].record(s)
+
+    def entry_bytes(self):
+        # read: 128 + 512 bf16 values and the 8-byte id; write: the 68 + 288-byte entry
+        return D_IDX * 2 + D_KV * 2 + 8 + IDX_ENTRY_BYTES + MAIN_ENTRY_BYTES
+
+    def dominant(self):
+        return {"kernel": "k_kv_append (quantise 131,072 entries into the 68 B + 288 B formats)",
+                "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                "work": self.N * self.entry_bytes(), "scale": 1e9, "marks": (0, 1)}
+
+    def step_bytes(self):
+        return self.N * self.entry_bytes() + self.B_SWA * (D_KV * 2 + 8 + D_KV)
+
+    def valid(self):
+        return bool((self.planes[1] > 0).all().item())
+
+    def config(self, n_sets):
+        return {"workload": "kv_append: 131,072 new entries (one layer of a 262,144-token prompt "
+                            "at 1:2) quantised and written contiguously, plus one window row for "
+                            "each of 32 sequences",
+                "entries": self.N, "window_rows": self.B_SWA, "input_sets_rotated": n_sets}
+
+    def cpu_baseline(self, rows):
+        import numpy as np
+        import oracle
+        xi, xk = self.sets[0]
+        rows = rows or 16384
+        hi, hk = host(xi[:rows]), host(xk[:rows])
+        z = (np.zeros((rows, 64), np.uint8), np.zeros(rows, np.float32),
+             np.zeros((rows, 256), np.uint8), np.zeros((rows, 32), np.uint8))
+        t0 = time.perf_counter()
+        oracle.kv_append(*z, hi, hk, np.arange(rows))
+        dt = time.perf_counter() - t0
+        return {"value": round(rows / dt, 1), "unit": "entries/s", "cores": 1, "kind": "oracle",
+                "sample": f"the first {rows} of the {self.N} entries, fp64/fp32 numpy on one "
+                          f"thread; {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -453,8 +526,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wl = Prefill(args, torch, synth, csa2, dev) if args.workload == "c5" else \
-        Decode(args.workload, args, torch, synth, csa2, dev)
+    if args.workload == "c5":
+        wl = Prefill(args, torch, synth, csa2, dev)
+    elif args.workload == "append":
+        wl = Append(args, torch, synth, csa2, dev)
+    else:
+        wl = Decode(args.workload, args, torch, synth, csa2, dev)
     torch.cuda.synchronize()
     print("inputs ready", file=sys.stderr, flush=True)
 
@@ -501,9 +578,10 @@ def main():
         "metric": METRIC if headline else
         {"c2": "CSA2 batched Full decode query-tokens/s (32 x 32,768 entries)",
          "c3": "CSA2 decoder-chain query-tokens/s (20 layers, 16 x 131,072 entries)",
-         "c5": "CSA2 prefill query-tokens/s (4,096-query chunk, 131,072 entries)"}[args.workload],
+         "c5": "CSA2 prefill query-tokens/s (4,096-query chunk, 131,072 entries)",
+         "append": "CSA2 KV append entries/s (131,072 entries)"}[args.workload],
         "value": round(value, 1),
-        "unit": "query-tokens/s",
+        "unit": "entries/s" if args.workload == "append" else "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

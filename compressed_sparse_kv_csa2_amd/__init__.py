@@ -21,7 +21,7 @@ __all__ = [
     "csa2_sparse_attn_decode", "csa2_prefill_chunk", "csa2_topk_workspace_size",
     "csa2_index_topk_workspace_size", "csa2_select_chain_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
     "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
-    "CSA2_TOPK_HIST_FUSED", "Csa2Error",
+    "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +54,8 @@ _SIGS = {
     "csa2_prefill_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "csa2_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
                                           _F32, _P, _P, _P, _SZ, _P]),
+    "csa2_kv_append": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P, _P, _I64, _P, _P]),
+    "csa2_swa_append": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
 }
 
 
@@ -300,3 +302,32 @@ def csa2_prefill_chunk(q_idx, q, idx_codes, idx_scale, kv_codes, kv_scale, n_ent
                                   int(pos0), T, int(k), _ptr(swa), float(softmax_scale),
                                   _ptr(idx_out), _ptr(out), _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
+
+
+def csa2_kv_append(x_idx, x_kv, dst, idx_codes, idx_scale, kv_codes, kv_scale, bad=None,
+                   stream=None):
+    """Quantise rows of x_idx [n,128] / x_kv [n,512] (bf16) into entries dst [n] (int64) of the
+    four planes; rows whose dst is outside the planes are skipped and counted into bad [1]."""
+    n = x_idx.shape[0]
+    _need(x_idx, "x_idx", _BF16, (n, 128))
+    _need(x_kv, "x_kv", _BF16, (n, 512))
+    _need(dst, "dst", (torch.int64,), (n,))
+    _need(idx_codes, "idx_codes", _U8, (None, 64))
+    cap = idx_codes.shape[0]
+    _need(idx_scale, "idx_scale", (torch.float32,), (cap,))
+    _need(kv_codes, "kv_codes", _U8, (cap, 256))
+    _need(kv_scale, "kv_scale", _U8, (cap, 32))
+    if bad is not None:
+        _need(bad, "bad", (torch.int32,), (1,))
+    _check(load_library().csa2_kv_append(_ptr(x_idx), _ptr(x_kv), _ptr(dst), n, _ptr(idx_codes),
+                                         _ptr(idx_scale), _ptr(kv_codes), _ptr(kv_scale), cap,
+                                         _ptr(bad), _stream(stream)))
+
+
+def csa2_swa_append(x, pos, swa, stream=None):
+    """swa[b][pos[b] % 128] = E4M3(x[b]) for every sequence with pos[b] >= 0."""
+    B = x.shape[0]
+    _need(x, "x", _BF16, (B, 512))
+    _need(pos, "pos", (torch.int64,), (B,))
+    _need(swa, "swa", _U8, (B, 128, 512))
+    _check(load_library().csa2_swa_append(_ptr(x), _ptr(pos), B, _ptr(swa), _stream(stream)))

@@ -185,4 +185,27 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
                                  static_cast<hipStream_t>(stream)));
 }
 
+int csa2_kv_append(const uint16_t* x_idx, const uint16_t* x_kv, const int64_t* dst, int32_t n,
+                   uint8_t* idx_codes, float* idx_scale, uint8_t* kv_codes, uint8_t* kv_scale,
+                   int64_t capacity, int32_t* bad, void* stream) {
+  if (n < 0 || capacity < 1) return CSA2_ERR_INVALID_ARG;
+  if (n == 0) return CSA2_OK;
+  if (!x_idx || !x_kv || !dst || !idx_codes || !idx_scale || !kv_codes || !kv_scale)
+    return CSA2_ERR_INVALID_ARG;
+  if (!aligned(x_idx, 16) || !aligned(x_kv, 16) || !aligned(dst, 8) || !aligned(idx_codes, 16) ||
+      !aligned(idx_scale, 4) || !aligned(kv_codes, 16) || (bad && !aligned(bad, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_kv_append(x_idx, x_kv, dst, n, capacity, idx_codes, idx_scale, kv_codes,
+                                   kv_scale, bad, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_swa_append(const uint16_t* x, const int64_t* pos, int32_t batch, uint8_t* swa,
+                    void* stream) {
+  if (batch < 0) return CSA2_ERR_INVALID_ARG;
+  if (batch == 0) return CSA2_OK;
+  if (!x || !pos || !swa) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(pos, 8) || !aligned(swa, 16)) return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_swa_append(x, pos, batch, swa, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -83,6 +83,13 @@ hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_
                           float softmax_scale, int32_t* idx_out, float* out, void* ws,
                           hipStream_t stream);
 
+// ---- KV write path (append.hip) ----
+hipError_t launch_kv_append(const uint16_t* x_idx, const uint16_t* x_kv, const int64_t* dst, int n,
+                            int64_t capacity, uint8_t* idx_codes, float* idx_scale, uint8_t* kv_codes,
+                            uint8_t* kv_scale, int32_t* bad, hipStream_t stream);
+hipError_t launch_swa_append(const uint16_t* x, const int64_t* pos, int batch, uint8_t* swa,
+                             hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace csa2

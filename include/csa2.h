@@ -265,6 +265,49 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
                        int32_t* idx_out, float* out, void* workspace, size_t ws_bytes,
                        void* stream);
 
+/*
+ * csa2_kv_append -- the write path in front of the hot path: quantise n new global-KV
+ * entries into entry ids dst[i] of the four planes.
+ *   [STRUCT] Q&A on the 890-byte count (indexer entry = 128 x 4 bit + 4-byte scale = 68 B,
+ *   main entry = 512 x 4 bit + 32 B of scale = 288 B); [DEEP] part-4 entry on FP4 in the KV
+ *   cache (main KV and indexer in different 4-bit formats).  Encoders (this library's
+ *   reading; csa2_index_score and csa2_sparse_attn_decode decode exactly these):
+ *     indexer  scale = fp32(amax/6) over the 128 values (1 if below 2^-126),
+ *              code_d = E2M1(fp32(x_d / scale));
+ *     main     per 16 values scale = E4M3(fp32(amax/6)) (code 0 becomes 1, i.e. 2^-9),
+ *              code_d = E2M1(fp32(x_d / scale));
+ *     E2M1 / E4M3  nearest, ties to even, saturating (6 / 448); the sign bit is the
+ *              value's; element 2i in the low nibble.  Inputs must be finite.
+ *
+ *   x_idx      bf16 [n][128]      new indexer vectors
+ *   x_kv       bf16 [n][512]      new main vectors
+ *   dst        i64  [n]           entry id of each row; ids must be distinct.  A row whose
+ *                                 id is outside [0, capacity) is not written.
+ *   idx_codes  u8 [capacity][64], idx_scale f32 [capacity], kv_codes u8 [capacity][256],
+ *   kv_scale   u8 [capacity][32]  (in/out) the planes; only rows dst[i] are written
+ *   bad        i32 [1] or NULL    (in/out) if given, the number of rows not written
+ *                                 (dst out of range) is added to *bad
+ * n = 0 launches nothing.  Errors: INVALID_ARG (n < 0, capacity < 1, null planes),
+ * ALIGNMENT (x_idx, x_kv, kv_codes, idx_codes 16 B; idx_scale, bad 4 B; dst 8 B).
+ */
+int csa2_kv_append(const uint16_t* x_idx, const uint16_t* x_kv, const int64_t* dst, int32_t n,
+                   uint8_t* idx_codes, float* idx_scale, uint8_t* kv_codes, uint8_t* kv_scale,
+                   int64_t capacity, int32_t* bad, void* stream);
+
+/*
+ * csa2_swa_append -- write one new window row per sequence as E4M3 into its ring:
+ * swa[b][pos[b] mod 128] = E4M3(x[b]) (nearest, ties to even, saturating at 448).
+ *   [DEEP] part-4 entry on FP4 in the KV cache (the sliding window stays FP8); [V4TO41]
+ *   section on global KV sharing with per-layer windows (128 tokens per layer).
+ *   x      bf16 [batch][512]
+ *   pos    i64  [batch]   position of the new token; a sequence with pos < 0 is skipped
+ *   swa    u8   [batch][128][512] (in/out) the layer's rings; csa2_sparse_attn_decode
+ *          attends rows 0..swa_len-1 with swa_len = min(pos + 1, 128)
+ * Errors: INVALID_ARG (batch < 0, null pointers), ALIGNMENT (x, swa 16 B; pos 8 B).
+ */
+int csa2_swa_append(const uint16_t* x, const int64_t* pos, int32_t batch, uint8_t* swa,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

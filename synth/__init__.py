@@ -191,6 +191,27 @@ def make_swa(B: int, rows: int, seed: int, device="cpu", sub: int = 0) -> torch.
     return e4m3_bytes(_randn((B, rows, D_KV), _gen(device, seed, F_SWA, sub), device))
 
 
+F_APPEND_IDX, F_APPEND_KV, F_APPEND_SWA = 5, 6, 7
+
+
+def make_append_vectors(n: int, seed: int, device="cpu"):
+    """New global-KV vectors before quantisation: bf16 bits (int16 storage) [n, 128] and
+    [n, 512], N(0,1) times a per-row magnitude drawn log-uniformly from 2^-8 .. 2^8 (the
+    magnitude only spreads the scales; both sides read the same bits)."""
+    device = torch.device(device)
+    g_i, g_k = _gen(device, seed, F_APPEND_IDX), _gen(device, seed, F_APPEND_KV)
+    mi = torch.exp2(torch.rand((n, 1), generator=g_i, device=device) * 16 - 8)
+    mk = torch.exp2(torch.rand((n, 1), generator=g_k, device=device) * 16 - 8)
+    return (bf16_bits(_randn((n, D_IDX), g_i, device) * mi),
+            bf16_bits(_randn((n, D_KV), g_k, device) * mk))
+
+
+def make_window_rows(B: int, seed: int, device="cpu") -> torch.Tensor:
+    """New window rows before quantisation: bf16 bits (int16 storage) [B, 512], N(0,1)."""
+    device = torch.device(device)
+    return bf16_bits(_randn((B, D_KV), _gen(device, seed, F_APPEND_SWA), device))
+
+
 # ----------------------------------------------------------------------------
 # The five workloads (sizes as the path's configurations state them).
 # ----------------------------------------------------------------------------

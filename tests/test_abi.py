@@ -125,3 +125,22 @@ def test_select_chain_validation(lib):
     assert f(*a[:17] + [100, None]) == -3  # no Reindex layer: still needs its workspace
     assert lib.csa2_select_chain_workspace_size(4, 1 << 20, 0) == 0
     assert lib.csa2_select_chain_workspace_size(4, 1 << 20, 16384) > 0
+
+
+def test_kv_append_validation(lib):
+    f = lib.csa2_kv_append
+    base = [FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, FAKE, 1000, None, None]
+    for pos, val, want in [(3, -1, -1), (8, 0, -1), (0, None, -1), (6, None, -1), (1, ODD, -2),
+                           (4, ODD, -2)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
+    a = list(base); a[3] = 0; a[0] = None
+    assert f(*a) == 0  # n = 0 launches nothing
+
+
+def test_swa_append_validation(lib):
+    f = lib.csa2_swa_append
+    base = [FAKE, FAKE, 4, FAKE, None]
+    for pos, val, want in [(2, -1, -1), (0, None, -1), (3, None, -1), (0, ODD, -2), (3, ODD, -2)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
