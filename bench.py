@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5", "append"])
+    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5", "append", "model"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: the "
                    "workload's default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -65,6 +65,8 @@ def parse():
                         "layer, or csa2_index_score + csa2_topk per layer")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="queries of the first input set the CPU oracle runs (0: default)")
+    p.add_argument("--graph", action="store_true",
+                   help="model workload: capture the 40-layer step into a HIP graph and replay it")
     p.add_argument("--no-phases", action="store_true",
                    help="skip the separate, untimed per-phase timing pass")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -431,6 +433,134 @@ class Prefill:
                           f"calls on {bt} threads, element-wise decoding on one; {dt:.1f} s"}
 
 
+class Model:
+    """A whole 40-layer decode step at a 2^20-token context, batch 4: three encoder Full
+    layers each scanning its own 524,288-entry pool (1:2), the decoder's Full layer scanning
+    1,048,576 entries (ratio 1) into the 16,384 pool and its own top-512, four Reindex
+    layers, and 40 attentions (two window-only, 38 over their lists), each with its own
+    query and window (compressed_sparse_kv_csa2_amd.model).  With --graph the step is
+    captured once into a HIP graph and replayed."""
+
+    B, N_ENC, N_DEC, POOL, K = 4, 1 << 19, 1 << 20, 16384, 512
+
+    def __init__(self, args, torch, synth, csa2, dev):
+        from compressed_sparse_kv_csa2_amd import model
+        self.torch, self.model = torch, model
+        seed = 3
+        B = self.B
+        print(f"generating the 2^20 model inputs (3 x {B} x {self.N_ENC} + {B} x {self.N_DEC} "
+              "entries)", file=sys.stderr, flush=True)
+        self.enc = [synth.make_entries([self.N_ENC] * B, seed=seed, device=dev, field_base=10 * (i + 1))
+                    for i in range(3)]
+        self.dec = synth.make_entries([self.N_DEC] * B, seed=seed, device=dev)
+        self.q_idx = {l: synth.make_index_queries(B, seed, device=dev, sub=l) for l in model.SELECTING}
+        self.q = torch.stack([synth.make_queries(B, seed, device=dev, sub=l) for l in range(40)]).contiguous()
+        self.swa = torch.stack([synth.make_swa(B, SWA, seed, device=dev, sub=l) for l in range(40)]).contiguous()
+        self.swa_len = torch.full((B,), SWA, dtype=torch.int32, device=dev)
+        self.run = model.DecodePass(B, self.N_ENC, self.N_DEC, self.POOL, self.K, device=dev)
+        self.sets = [None]
+        self.stream = torch.cuda.current_stream()
+        self.queries_per_step = B
+        self.n_marks = 4
+        self.phase_names = ["encoder_layers_us", "decoder_full_select_us", "decoder_rest_us"]
+        self.graph = None
+        if args.graph:
+            self.run.step(self.enc, self.dec, self.q_idx, self.q, self.swa, self.swa_len, stream=self.stream)
+            torch.cuda.synchronize()
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph):
+                self.run.step(self.enc, self.dec, self.q_idx, self.q, self.swa, self.swa_len,
+                              stream=torch.cuda.current_stream())
+            torch.cuda.synchronize()
+
+    def step(self, i, marks=None):
+        self.run.step(self.enc, self.dec, self.q_idx, self.q, self.swa, self.swa_len,
+                      stream=self.stream, marks=marks)
+
+    def graph_timing(self, steps):
+        """ms per step of `steps` back-to-back replays of the captured step, and whether the
+        last replay's lists and outputs equal an eager step's."""
+        t = self.torch
+        self.step(0)
+        t.cuda.synchronize()
+        ref = [self.run.out.clone()] + [v.clone() for v in self.run.lists.values()]
+        t.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.graph.replay()
+        t.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        got = [self.run.out] + list(self.run.lists.values())
+        same = all(bool(t.equal(a, b)) for a, b in zip(ref, got))
+        return ms, same
+
+    def dominant(self):
+        return {"kernel": "k_index_topk<false> (decoder Full scan of 1,048,576 entries, pool 16,384 "
+                          "and its own top-512 in one launch)",
+                "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                "work": self.B * self.N_DEC * IDX_ENTRY_BYTES, "scale": 1e9, "marks": (1, 2)}
+
+    def step_bytes(self):
+        per_q = (3 * self.N_ENC + self.N_DEC) * IDX_ENTRY_BYTES + 8 * D_IDX * 2
+        per_q += self.POOL * 4 + 4 * self.POOL * (IDX_ENTRY_BYTES + 4)
+        per_q += 38 * self.K * (MAIN_ENTRY_BYTES + 4) + 40 * (SWA * D_KV + HEADS * D_KV * 2 + HEADS * D_KV * 4)
+        return self.B * per_q
+
+    def valid(self):
+        t = self.torch
+        ok = bool(t.isfinite(self.run.out).all().item())
+        for lst in self.run.lists.values():
+            ok = ok and bool(((lst[:, 1:] > lst[:, :-1]).all() & (lst >= 0).all()).item())
+        return ok
+
+    def config(self, n_sets):
+        return {"workload": "model_decode: one decode step of all 40 layers at a 2^20-token context, "
+                            "batch 4 (3 encoder Full scans of 524,288 entries, decoder Full scan of "
+                            "1,048,576 -> pool 16,384, 4 Reindex, 40 attentions 16x512 + SWA 128)",
+                "batch": self.B, "context_tokens": 1 << 20, "encoder_entries": self.N_ENC,
+                "decoder_entries": self.N_DEC, "pool": self.POOL, "top_k": self.K, "layers": 40,
+                "hip_graph": self.graph is not None}
+
+    def cpu_baseline(self, rows):
+        import numpy as np
+        import oracle
+        model = self.model
+        t0 = time.perf_counter()
+        b = 0
+        lists = {}
+        for i, l in enumerate(model.ENCODER_FULL):
+            c = self.enc[i]
+            sl = slice(b * self.N_ENC, (b + 1) * self.N_ENC)
+            lists[l] = oracle.topk(oracle.index_scores(host(self.q_idx[l])[b], host(c.idx_codes[sl]),
+                                                       host(c.idx_scale[sl])), self.K)
+        sl = slice(b * self.N_DEC, (b + 1) * self.N_DEC)
+        codes, scale = host(self.dec.idx_codes[sl]), host(self.dec.idx_scale[sl])
+        s = oracle.index_scores(host(self.q_idx[20])[b], codes, scale)
+        pool = oracle.topk(s, self.POOL)
+        lists[20] = pool[oracle.topk(s[pool], self.K)]
+        for l in model.REINDEX:
+            lists[l], _ = oracle.reindex_layer(host(self.q_idx[l])[b], codes, scale, pool)
+        hosts = [(host(c.kv_codes), host(c.kv_scale)) for c in self.enc + [self.dec]]
+        q, sw = host(self.q), host(self.swa)
+        for l in range(40):
+            src = None if l in model.WINDOW_ONLY else model.list_source(l)
+            if src is None or src >= model.DECODER_FULL:
+                kc, ks = hosts[3]
+                base = b * self.N_DEC
+            else:
+                kc, ks = hosts[model.ENCODER_FULL.index(src)]
+                base = b * self.N_ENC
+            idx = np.zeros(0, np.int32) if src is None else lists[src]
+            oracle.decode_attention(q[l, b], kc, ks, base, idx, sw[l, b], SWA)
+        dt = time.perf_counter() - t0
+        bt = blas_threads()
+        return {"value": round(1 / dt, 4), "unit": "query-tokens/s", "cores": bt, "kind": "oracle",
+                "sample": f"1 of the {self.B} sequences through all 40 layers (3 encoder scans of "
+                          f"{self.N_ENC} and the decoder scan of {self.N_DEC} entries, pool, 4 "
+                          f"Reindex, 40 attentions), fp64 numpy; BLAS calls on {bt} threads, "
+                          f"element-wise decoding on one; {dt:.1f} s"}
+
+
 class Append:
     """The KV write path: one layer's new entries for a 262,144-token prompt at 1:2
     (131,072 entries quantised into the 68 B + 288 B formats, written contiguously), and, as
@@ -530,6 +660,8 @@ def main():
         wl = Prefill(args, torch, synth, csa2, dev)
     elif args.workload == "append":
         wl = Append(args, torch, synth, csa2, dev)
+    elif args.workload == "model":
+        wl = Model(args, torch, synth, csa2, dev)
     else:
         wl = Decode(args.workload, args, torch, synth, csa2, dev)
     torch.cuda.synchronize()
@@ -579,7 +711,8 @@ def main():
         {"c2": "CSA2 batched Full decode query-tokens/s (32 x 32,768 entries)",
          "c3": "CSA2 decoder-chain query-tokens/s (20 layers, 16 x 131,072 entries)",
          "c5": "CSA2 prefill query-tokens/s (4,096-query chunk, 131,072 entries)",
-         "append": "CSA2 KV append entries/s (131,072 entries)"}[args.workload],
+         "append": "CSA2 KV append entries/s (131,072 entries)",
+         "model": "CSA2 whole-model decode query-tokens/s (40 layers, 2^20 ctx, batch 4)"}[args.workload],
         "value": round(value, 1),
         "unit": "entries/s" if args.workload == "append" else "query-tokens/s",
         "n_gpus": 1,
@@ -604,6 +737,12 @@ def main():
         "selection_valid": ok,
         "cpu_baseline": cpu,
     }
+    if getattr(wl, "graph", None) is not None:
+        g_ms, g_same = wl.graph_timing(args.steps)
+        line["hip_graph"] = {"ms_per_step": round(g_ms, 5),
+                             "value": round(wl.queries_per_step / (g_ms * 1e-3), 1),
+                             "replays_equal_eager": g_same}
+        ok = ok and g_same
     print(json.dumps(line), flush=True)
     if not ok:
         sys.exit(3)

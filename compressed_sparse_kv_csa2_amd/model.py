@@ -1,0 +1,97 @@
+"""One decode step of the 40-layer CSA2 backbone, sequenced through the C ABI.
+
+Sequencing only: every step runs in the library's kernels (csa2_index_topk,
+csa2_select_chain, csa2_sparse_attn_decode); this module holds workspaces and output
+buffers and issues the calls in layer order on one stream.
+
+Layer layout ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash", Q&A on how the
+40 layers are laid out, and commentary on the four layer modes; "从V4到V4.1 Flash：架构的
+激进进化", CSA2 architecture, encoder and decoder sections):
+  * layers 0-1 attend their sliding window only;
+  * Full at 2, 8 and 14 (encoder: each scans its own 1:2 pool and takes its top-512) and at
+    20 (decoder: scans the ratio-1 pool, keeps the top-16,384 as the candidate pool and its
+    own top-512 inside it);
+  * Reindex at 24, 28, 32, 36: the layer's own indexer query re-scores the pool only;
+  * every other layer is Reuse: the list of the most recent Full/Reindex layer at or below
+    it;
+  * every layer attends with its own 16 x 512 query over its list plus its own 128-row
+    window.
+Each Reindex layer's query arrives at its own layer (it depends on the layers before it in
+a real decoder), so the Reindex selections run one call per layer.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (attn_workspace, csa2_index_topk, csa2_select_chain, csa2_sparse_attn_decode,
+               index_topk_workspace, select_chain_workspace)
+
+N_LAYERS = 40
+WINDOW_ONLY = (0, 1)
+ENCODER_FULL = (2, 8, 14)
+DECODER_FULL = 20
+REINDEX = (24, 28, 32, 36)
+SELECTING = ENCODER_FULL + (DECODER_FULL,) + REINDEX
+
+
+def list_source(layer: int) -> int:
+    """The layer whose selection `layer` attends over (itself for Full/Reindex layers)."""
+    return max(l for l in SELECTING if l <= layer)
+
+
+class DecodePass:
+    """Buffers for one 40-layer decode step of `batch` sequences.
+
+    enc_entries / dec_entries: entries per sequence in each encoder pool / the decoder pool.
+    After step(): lists[l] (int32 [batch, k]) for every selecting layer, pool (int32
+    [batch, pool]) and out[l] (f32 [batch, 16, 512]) for every layer."""
+
+    def __init__(self, batch: int, enc_entries: int, dec_entries: int, pool: int = 16384,
+                 k: int = 512, device="cuda"):
+        self.B, self.n_enc, self.n_dec, self.P, self.K = batch, enc_entries, dec_entries, pool, k
+        dev = torch.device(device)
+        self.enc_ws = index_topk_workspace(batch, enc_entries, k, device=dev)
+        self.dec_ws = select_chain_workspace(batch, dec_entries, pool, device=dev)
+        self.re_ws = index_topk_workspace(batch, pool, k, device=dev)
+        self.attn_ws = attn_workspace(batch, k, device=dev)
+        self.pool = torch.empty((batch, pool), dtype=torch.int32, device=dev)
+        self.pool_valid = torch.full((batch,), pool, dtype=torch.int32, device=dev)
+        self.lists = {l: torch.empty((batch, k), dtype=torch.int32, device=dev) for l in SELECTING}
+        self.out = torch.empty((N_LAYERS, batch, 16, 512), dtype=torch.float32, device=dev)
+
+    def step(self, enc_caches, dec_cache, q_idx, q, swa, swa_len, stream=None, marks=None):
+        """enc_caches: three entry caches (layers 2, 8, 14); dec_cache: the decoder's.
+        q_idx: {selecting layer: bf16 [batch, 128]}; q: bf16 [40, batch, 16, 512];
+        swa: E4M3 [40, batch, 128, 512]; swa_len: int32 [batch].  marks (optional): four
+        events recorded before layer 0, around the decoder's Full selection and at the end."""
+        if marks is not None:
+            marks[0].record(stream)
+        for l in range(N_LAYERS):
+            if l in ENCODER_FULL:
+                c = enc_caches[ENCODER_FULL.index(l)]
+                csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries, self.K,
+                                self.lists[l], self.enc_ws, self.n_enc, stream=stream)
+            elif l == DECODER_FULL:
+                c = dec_cache
+                if marks is not None:
+                    marks[1].record(stream)
+                csa2_select_chain(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                                  self.n_dec, self.pool, self.dec_ws, k=self.K,
+                                  own_out=self.lists[l], stream=stream)
+                if marks is not None:
+                    marks[2].record(stream)
+            elif l in REINDEX:
+                c = dec_cache
+                csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid,
+                                self.K, self.lists[l], self.re_ws, self.P, cand=self.pool,
+                                stream=stream)
+            if l in WINDOW_ONLY:
+                c, idx = dec_cache, None
+            else:
+                src = list_source(l)
+                c = dec_cache if src >= DECODER_FULL else enc_caches[ENCODER_FULL.index(src)]
+                idx = self.lists[src]
+            csa2_sparse_attn_decode(q[l], c.kv_codes, c.kv_scale, c.seq_base, idx, swa[l], swa_len,
+                                    self.out[l], self.attn_ws, stream=stream)
+        if marks is not None:
+            marks[3].record(stream)
