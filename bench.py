@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5", "append", "model"])
+    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5", "c5r4", "append", "model"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: the "
                    "workload's default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -354,11 +354,16 @@ class Decode:
 
 # ------------------------------------------------------------------------------------ prefill
 class Prefill:
-    """c5: T = 4,096 queries at the tail of a 262,144-token context (131,072 entries at 1:2)."""
+    """c5: T = 4,096 queries at the tail of a 262,144-token context (131,072 entries at 1:2).
+    c5r4 (ratio=4): the same 131,072 entries at the predecessor's 4:1 compression, i.e. the
+    tail of a 524,288-token context."""
 
-    def __init__(self, args, torch, synth, csa2, dev):
-        self.name, self.torch, self.csa2, self.dev = "c5", torch, csa2, dev
-        self.cfg = cfg = synth.CONFIGS["c5_prefill"]
+    def __init__(self, args, torch, synth, csa2, dev, ratio=None):
+        self.name, self.torch, self.csa2, self.dev = "c5" if ratio is None else "c5r4", torch, csa2, dev
+        self.cfg = cfg = dict(synth.CONFIGS["c5_prefill"])
+        if ratio is not None:
+            cfg["ctx"] = cfg["ctx"] // cfg["ratio"] * ratio
+            cfg["ratio"] = ratio
         self.T, self.ratio, self.K = cfg["T"], cfg["ratio"], cfg["k"]
         self.N = cfg["ctx"] // self.ratio
         self.pos0 = cfg["ctx"] - self.T
@@ -410,9 +415,10 @@ class Prefill:
             bool(self.torch.isfinite(self.out).all().item())
 
     def config(self, n_sets):
-        return {"workload": "c5_prefill: 4,096 queries at positions 258,048..262,143 of a "
-                            "262,144-token context (131,072 entries at 1:2), causal indexer, "
-                            "top-512 per query, attention 16x512 + causal SWA 128",
+        ctx = self.cfg["ctx"]
+        return {"workload": f"{self.name}_prefill: 4,096 queries at positions {self.pos0:,}..{ctx - 1:,} "
+                            f"of a {ctx:,}-token context ({self.N:,} entries at 1:{self.ratio}), causal "
+                            "indexer, top-512 per query, attention 16x512 + causal SWA 128",
                 "queries": self.T, "context_tokens": self.cfg["ctx"], "entries": self.N,
                 "top_k": self.K, "heads": HEADS, "head_dim": D_KV, "swa": SWA,
                 "input_sets_rotated": n_sets}
@@ -656,8 +662,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    if args.workload == "c5":
-        wl = Prefill(args, torch, synth, csa2, dev)
+    if args.workload in ("c5", "c5r4"):
+        wl = Prefill(args, torch, synth, csa2, dev, ratio=4 if args.workload == "c5r4" else None)
     elif args.workload == "append":
         wl = Append(args, torch, synth, csa2, dev)
     elif args.workload == "model":
@@ -711,6 +717,7 @@ def main():
         {"c2": "CSA2 batched Full decode query-tokens/s (32 x 32,768 entries)",
          "c3": "CSA2 decoder-chain query-tokens/s (20 layers, 16 x 131,072 entries)",
          "c5": "CSA2 prefill query-tokens/s (4,096-query chunk, 131,072 entries)",
+         "c5r4": "CSA2 prefill query-tokens/s at 4:1 compression (4,096-query chunk, 131,072 entries)",
          "append": "CSA2 KV append entries/s (131,072 entries)",
          "model": "CSA2 whole-model decode query-tokens/s (40 layers, 2^20 ctx, batch 4)"}[args.workload],
         "value": round(value, 1),
