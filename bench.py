@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5", "c5r4", "append", "model"])
+    p.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c5", "c5r4", "append", "model", "replay"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated per step (0: the "
                    "workload's default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -567,6 +567,89 @@ class Model:
                           f"element-wise decoding on one; {dt:.1f} s"}
 
 
+class Replay:
+    """The decoder's bounded replay at a 2^20-token context: the last 128 tokens of one
+    sequence through the decoder's 20 layers (compressed_sparse_kv_csa2_amd.model.
+    ReplayChunk): per query a Full scan of its visible entries (up to 1,048,576, ratio 1)
+    into its own pool of 16,384 and top-512, four Reindex top-512s in its pool, 20
+    attentions with causal windows."""
+
+    T, N, POOL, K = 128, 1 << 20, 16384, 512
+
+    def __init__(self, args, torch, synth, csa2, dev):
+        from compressed_sparse_kv_csa2_amd import model
+        self.torch, self.model = torch, model
+        seed = 12
+        self.pos0 = self.N - self.T
+        print(f"generating the replay inputs ({self.N} entries, {self.T} queries)", file=sys.stderr,
+              flush=True)
+        self.cache = synth.make_entries([self.N], seed=seed, device=dev)
+        self.q_idx = {l: synth.make_index_queries(self.T, seed, device=dev, sub=l)
+                      for l in (20,) + model.REINDEX}
+        self.q = torch.stack([synth.make_queries(self.T, seed, device=dev, sub=l)
+                              for l in range(20, 40)]).contiguous()
+        self.swa = torch.stack([synth.make_swa(1, self.T + SWA - 1, seed, device=dev, sub=l)[0]
+                                for l in range(20, 40)]).contiguous()
+        self.run = model.ReplayChunk(self.T, self.N, self.pos0, self.POOL, self.K, device=dev)
+        self.sets = [None]
+        self.stream = torch.cuda.current_stream()
+        self.queries_per_step = self.T
+        self.n_marks = 3
+        self.phase_names = ["full_select_us", "reindex_and_attention_us"]
+
+    def step(self, i, marks=None):
+        self.run.step(self.cache, self.q_idx, self.q, self.swa, stream=self.stream, marks=marks)
+
+    def dominant(self):
+        return {"kernel": "k_index_topk<false> launches of the per-query Full scans (pool 16,384 "
+                          "and own top-512; 4 queries per launch, each scanning its visible keys)",
+                "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                "work": sum(min(self.pos0 + t + 1, self.N) for t in range(self.T)) * IDX_ENTRY_BYTES,
+                "scale": 1e9, "marks": (0, 1)}
+
+    def step_bytes(self):
+        scan = sum(min(self.pos0 + t + 1, self.N) for t in range(self.T)) * IDX_ENTRY_BYTES
+        per_q = self.POOL * 4 + 4 * self.POOL * (IDX_ENTRY_BYTES + 4) + 5 * D_IDX * 2
+        per_q += 20 * (self.K * (MAIN_ENTRY_BYTES + 4) + SWA * D_KV + HEADS * D_KV * 6)
+        return scan + self.T * per_q
+
+    def valid(self):
+        t = self.torch
+        ok = bool(t.isfinite(self.run.out).all().item())
+        for lst in self.run.lists.values():
+            ok = ok and bool(((lst[:, 1:] > lst[:, :-1]).all() & (lst >= 0).all()).item())
+        return ok
+
+    def config(self, n_sets):
+        return {"workload": "replay: the last 128 tokens of a 2^20-token sequence through the 20 "
+                            "decoder layers (per-query Full scan of up to 1,048,576 entries -> pool "
+                            "16,384 + own top-512, 4 Reindex, 20 attentions 16x512 + causal SWA 128)",
+                "queries": self.T, "context_tokens": self.N, "entries": self.N, "pool": self.POOL,
+                "top_k": self.K, "layers": 20}
+
+    def cpu_baseline(self, rows):
+        import numpy as np
+        import oracle
+        t = self.T - 1
+        t0 = time.perf_counter()
+        codes, scale = host(self.cache.idx_codes), host(self.cache.idx_scale)
+        s = oracle.index_scores(host(self.q_idx[20])[t], codes, scale)
+        pool = oracle.topk(s, self.POOL)
+        lists = {20: pool[oracle.topk(s[pool], self.K)]}
+        for l in self.model.REINDEX:
+            lists[l], _ = oracle.reindex_layer(host(self.q_idx[l])[t], codes, scale, pool)
+        kc, ks, q, sw = host(self.cache.kv_codes), host(self.cache.kv_scale), host(self.q), host(self.swa)
+        for l in range(20, 40):
+            win = sw[l - 20][t: t + SWA]
+            oracle.decode_attention(q[l - 20][t], kc, ks, 0, lists[self.model.list_source(l)], win, SWA)
+        dt = time.perf_counter() - t0
+        bt = blas_threads()
+        return {"value": round(1 / dt, 4), "unit": "query-tokens/s", "cores": bt, "kind": "oracle",
+                "sample": f"the last of the {self.T} queries through the 20 decoder layers (scan of "
+                          f"{self.N} entries, pool, 4 Reindex, 20 attentions), fp64 numpy; BLAS calls "
+                          f"on {bt} threads, element-wise decoding on one; {dt:.1f} s"}
+
+
 class Append:
     """The KV write path: one layer's new entries for a 262,144-token prompt at 1:2
     (131,072 entries quantised into the 68 B + 288 B formats, written contiguously), and, as
@@ -668,6 +751,8 @@ def main():
         wl = Append(args, torch, synth, csa2, dev)
     elif args.workload == "model":
         wl = Model(args, torch, synth, csa2, dev)
+    elif args.workload == "replay":
+        wl = Replay(args, torch, synth, csa2, dev)
     else:
         wl = Decode(args.workload, args, torch, synth, csa2, dev)
     torch.cuda.synchronize()
@@ -719,7 +804,8 @@ def main():
          "c5": "CSA2 prefill query-tokens/s (4,096-query chunk, 131,072 entries)",
          "c5r4": "CSA2 prefill query-tokens/s at 4:1 compression (4,096-query chunk, 131,072 entries)",
          "append": "CSA2 KV append entries/s (131,072 entries)",
-         "model": "CSA2 whole-model decode query-tokens/s (40 layers, 2^20 ctx, batch 4)"}[args.workload],
+         "model": "CSA2 whole-model decode query-tokens/s (40 layers, 2^20 ctx, batch 4)",
+         "replay": "CSA2 decoder replay query-tokens/s (128 tokens, 20 layers, 2^20 ctx)"}[args.workload],
         "value": round(value, 1),
         "unit": "entries/s" if args.workload == "append" else "query-tokens/s",
         "n_gpus": 1,

@@ -24,7 +24,7 @@ from __future__ import annotations
 import torch
 
 from . import (attn_workspace, csa2_index_topk, csa2_select_chain, csa2_sparse_attn_decode,
-               index_topk_workspace, select_chain_workspace)
+               csa2_sparse_attn_prefill, index_topk_workspace, select_chain_workspace)
 
 N_LAYERS = 40
 WINDOW_ONLY = (0, 1)
@@ -95,3 +95,56 @@ class DecodePass:
                                     self.out[l], self.attn_ws, stream=stream)
         if marks is not None:
             marks[3].record(stream)
+
+
+class ReplayChunk:
+    """The decoder's bounded replay: T consecutive tokens of one sequence (positions pos0 ..
+    pos0 + T - 1) through the decoder's 20 layers ("DeepSeek-V4.1 模型结构（0）：一张图看懂
+    DeepSeek-V4.1-Flash", content summary and Q&A on prefill: on eviction or restore only the
+    last 128 tokens of the decoder are replayed; "从V4到V4.1 Flash：架构的激进进化", decoder
+    section).  The decoder's global KV has ratio 1, so entry j is token j and query t sees
+    entries 0 .. pos0 + t.  Per query, as in decode: the Full layer (20) scans every visible
+    entry, keeps its top-16,384 as the query's pool and its own top-512 inside it; each
+    Reindex layer re-scores that query's pool; every layer attends over its list and its own
+    causal window.
+
+    After step(): pool (int32 [T, pool]), lists[l] (int32 [T, k]) for 20, 24, 28, 32, 36 and
+    out[l - 20] (f32 [T, 16, 512]) for layers 20..39."""
+
+    def __init__(self, T: int, n_entries: int, pos0: int, pool: int = 16384, k: int = 512,
+                 device="cuda"):
+        self.T, self.n, self.pos0, self.P, self.K = T, n_entries, pos0, pool, k
+        dev = torch.device(device)
+        self.sel_ws = select_chain_workspace(T, n_entries, pool, device=dev)
+        self.re_ws = index_topk_workspace(T, pool, k, device=dev)
+        self.seq_base = torch.zeros((T,), dtype=torch.int64, device=dev)
+        vis = torch.arange(pos0 + 1, pos0 + T + 1, dtype=torch.int64).clamp(max=n_entries)
+        self.n_visible = vis.to(torch.int32).to(dev)
+        self.pool = torch.empty((T, pool), dtype=torch.int32, device=dev)
+        self.pool_valid = self.n_visible.clamp(max=pool).contiguous()
+        self.lists = {l: torch.empty((T, k), dtype=torch.int32, device=dev)
+                      for l in (DECODER_FULL,) + REINDEX}
+        self.out = torch.empty((N_LAYERS - DECODER_FULL, T, 16, 512), dtype=torch.float32, device=dev)
+
+    def step(self, cache, q_idx, q, swa, stream=None, marks=None):
+        """cache: the sequence's decoder entries (planes from entry 0); q_idx: {20, 24, 28,
+        32, 36: bf16 [T, 128]}; q: bf16 [20, T, 16, 512] (layers 20..39); swa: E4M3
+        [20, T + 127, 512] (row r = position pos0 - 127 + r).  marks (optional): three events,
+        before the Full selection, after it, at the end."""
+        if marks is not None:
+            marks[0].record(stream)
+        csa2_select_chain(q_idx[DECODER_FULL], cache.idx_codes, cache.idx_scale, self.seq_base,
+                          self.n_visible, self.n, self.pool, self.sel_ws, k=self.K,
+                          own_out=self.lists[DECODER_FULL], stream=stream)
+        if marks is not None:
+            marks[1].record(stream)
+        for l in range(DECODER_FULL, N_LAYERS):
+            if l in REINDEX:
+                csa2_index_topk(q_idx[l], cache.idx_codes, cache.idx_scale, self.seq_base,
+                                self.pool_valid, self.K, self.lists[l], self.re_ws, self.P,
+                                cand=self.pool, stream=stream)
+            csa2_sparse_attn_prefill(q[l - DECODER_FULL], cache.kv_codes, cache.kv_scale,
+                                     self.lists[list_source(l)], swa[l - DECODER_FULL], self.pos0,
+                                     self.out[l - DECODER_FULL], stream=stream)
+        if marks is not None:
+            marks[2].record(stream)

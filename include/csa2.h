@@ -266,6 +266,25 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
                        void* stream);
 
 /*
+ * csa2_sparse_attn_prefill -- a5 + a6 for T consecutive query positions of one sequence,
+ * each over its own list and its own causal window: the attention half of
+ * csa2_prefill_chunk, for lists made elsewhere (a Reuse layer of a prefill or replay chunk
+ * attends over the list of the layer it reuses).
+ *   [V4TO41] CSA2 architecture (Reuse attends over an earlier layer's selection) and
+ *   section on global KV sharing with per-layer windows; [STRUCT] Q&A on prefill.
+ *   q          bf16 [T][16][512]     query t at position pos0 + t
+ *   kv_codes, kv_scale               entries of the sequence from 0 (as csa2_prefill_chunk)
+ *   idx        i32 [T][k] or NULL when k == 0; entry ids, -1 = skip
+ *   swa        u8 [T+127][512]       E4M3 window rows; row r holds position pos0-127+r;
+ *              query t attends the rows for positions max(0,p-127)..p
+ *   out        f32 [T][16][512] (out)
+ * Errors: INVALID_ARG (T < 1, k < 0 or > 16384, pos0 < 0, null pointers), ALIGNMENT.
+ */
+int csa2_sparse_attn_prefill(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                             const int32_t* idx, int32_t k, const uint8_t* swa, int64_t pos0,
+                             int32_t T, float softmax_scale, float* out, void* stream);
+
+/*
  * csa2_kv_append -- the write path in front of the hot path: quantise n new global-KV
  * entries into entry ids dst[i] of the four planes.
  *   [STRUCT] Q&A on the 890-byte count (indexer entry = 128 x 4 bit + 4-byte scale = 68 B,
