@@ -53,6 +53,13 @@ constexpr int kCandLds = 4096;              // candidates a row may gather into 
 constexpr int kSelThreads = 256;
 static_assert(kSelThreads == 256, "the theta and select kernels give each of 256 bins a thread");
 constexpr int kSelMaxSplits = 512;          // splits a row's fast path can gather (N <= 2M)
+// Sampled threshold: pass 1 over every kSampleStride-th entry.  Used when kq = 3k/8 is at
+// least kSampleMinQ and the first row sees at least kSampleMinGroupsPerQ * kq sample groups
+// (each of 32 samples); with i.i.d. scores the candidates then number about 1.5 k per row
+// (relative spread about 1 / sqrt(kq)), so fewer than k is a ~5 sigma event.
+constexpr int kSampleStride = 4;
+constexpr int kSampleMinQ = 128;
+constexpr int kSampleMinGroupsPerQ = 4;
 
 struct PrefillWs {
   uint16_t* gmax;               // [T][G] group maxima as key >> 16 (0 = empty group)
@@ -60,7 +67,8 @@ struct PrefillWs {
   uint32_t* ccount;             // [T][n_splits] candidates found per split
   unsigned long long* cand;     // [T][n_splits][kSlots] (key << 32 | entry)
   void* attn;                   // attention workspace (unused by the prefill attention)
-  int G, n_splits;
+  int G, n_splits;              // G: row stride of gmax (groups of the full pass 1)
+  int G_used;                   // groups the current pass 1 wrote per row (<= G)
 };
 
 static int prefill_splits(int n_entries) {
@@ -83,6 +91,7 @@ static PrefillWs prefill_ws_carve(void* base, int T, int n_entries) {
   PrefillWs w;
   w.n_splits = prefill_splits(n_entries);
   w.G = w.n_splits * kGroupsPerSplit;
+  w.G_used = w.G;
   char* p = static_cast<char*>(base);
   w.gmax = reinterpret_cast<uint16_t*>(p);
   p += align_up((size_t)T * w.G * 2, 256);
@@ -94,6 +103,11 @@ static PrefillWs prefill_ws_carve(void* base, int T, int n_entries) {
   p += align_up((size_t)T * w.n_splits * kSlots * 8, 256);
   w.attn = p;
   return w;
+}
+
+static int visible_host(int64_t pos, int ratio, int n_entries) {
+  const int64_t v = (pos + 1) / ratio;
+  return (int)(v < n_entries ? v : n_entries);
 }
 
 __device__ __forceinline__ int visible(int64_t pos, int ratio, int n_entries) {
@@ -140,7 +154,10 @@ __device__ __forceinline__ int stage_blk(int i, int b) { return i * 4 + (b ^ ((i
 // k-slice 8*(l/32)..+7; the dims behind k-step kk for half h are 64h + 8kk .. +7.
 // A wave owns 64 rows as two sets of 32 (set s: rows 32s ..); each expanded B operand
 // feeds one MFMA per set.
-template <int PASS>
+// STRIDE > 1 (pass 1 only): the contraction runs over every STRIDE-th entry (columns are
+// sample indices, column c = entry STRIDE * c), for the sampled threshold.  A workgroup
+// covers SPLIT columns (a multiple of one run of 1,024), SPLIT / 1,024 * 32 groups.
+template <int PASS, int STRIDE, int SPLIT>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
@@ -153,15 +170,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kGemmRows;
   const int row0 = wg_row0 + wave * kWaveRows;
+  static_assert(PASS == 1 || (STRIDE == 1 && SPLIT == kSplitEntries), "pass 2 scans every entry");
+  static_assert(SPLIT % (kRunStages * kStage) == 0 && SPLIT <= kSplitEntries, "whole runs");
+  constexpr int n_stages = SPLIT / kStage;
+  constexpr int groups_per_split = n_stages / kRunStages * 32;
   const int split = blockIdx.y;
-  const int e_begin = split * kSplitEntries;
-  const int e_end = min(e_begin + kSplitEntries, n_entries);
+  const int n_cols = (n_entries + STRIDE - 1) / STRIDE;
+  const int e_begin = split * SPLIT;  // columns
+  const int e_end = min(e_begin + SPLIT, n_cols);
   const int rl = lane & 31, half = lane >> 5;
+  // columns a row sees: the entries it sees, in columns
+  auto vis_cols = [&](int64_t pos) { return (visible(pos, ratio, n_entries) + STRIDE - 1) / STRIDE; };
 
-  // entries any row of the workgroup can see, and of this wave's rows
-  const int wg_nmax = visible(pos0 + min(wg_row0 + kGemmRows - 1, T - 1), ratio, n_entries);
-  const int wave_nmax = row0 < T ? visible(pos0 + min(row0 + kWaveRows - 1, T - 1), ratio, n_entries) : 0;
-  const int wave_nmin = row0 < T ? visible(pos0 + row0, ratio, n_entries) : 0;
+  // columns any row of the workgroup can see, and of this wave's rows
+  const int wg_nmax = vis_cols(pos0 + min(wg_row0 + kGemmRows - 1, T - 1));
+  const int wave_nmax = row0 < T ? vis_cols(pos0 + min(row0 + kWaveRows - 1, T - 1)) : 0;
+  const int wave_nmin = row0 < T ? vis_cols(pos0 + row0) : 0;
   const int e_stop = min(e_end, wg_nmax);
   const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
 
@@ -176,13 +200,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
   }
   // row of accumulator r of set s within the wave
   auto wrow = [&](int s, int r) { return 32 * s + 8 * (r >> 2) + 4 * half + (r & 3); };
-  // On a tile at the causal frontier, entry col is visible to wave row w once its last
-  // position (col+1)*ratio - 1 is at most pos0 + row0 + w, i.e. once lim <= w - 4*half with
-  // lim the lane's offset below (clamped: far from the frontier only its sign matters).
+  // On a tile at the causal frontier, column col (entry STRIDE*col) is visible to wave row w
+  // once the entry's last position (STRIDE*col+1)*ratio - 1 is at most pos0 + row0 + w, i.e.
+  // once lim <= w - 4*half with lim the lane's offset below (clamped: far from the frontier
+  // only its sign matters).
   // Rows past T need no mask: their maxima are never published and their thresholds are +inf.
   auto frontier_lim = [&](int col) {
-    const int64_t d = (int64_t)(col + 1) * ratio - 1 - (pos0 + row0 + 4 * half);
-    return col < n_entries ? (int)max(min(d, (int64_t)1 << 30), -((int64_t)1 << 30)) : (1 << 30);
+    const int64_t d = ((int64_t)col * STRIDE + 1) * ratio - 1 - (pos0 + row0 + 4 * half);
+    return col < n_cols ? (int)max(min(d, (int64_t)1 << 30), -((int64_t)1 << 30)) : (1 << 30);
   };
   auto wrow_h = [&](int s, int r) { return 32 * s + 8 * (r >> 2) + (r & 3); };  // wrow - 4*half
   // PASS 2: row thresholds; the hit queue's fill (wave-uniform)
@@ -238,7 +263,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
   float psc = 0.f;
 #define CSA2_LOAD_STAGE(st)                                                                   \
   do {                                                                                        \
-    const int e_ = min(e_begin + (st) * kStage + tid, n_entries - 1);                         \
+    const int e_ = min(e_begin + (st) * kStage + tid, n_cols - 1) * STRIDE;                   \
     const uint4* cp_ = reinterpret_cast<const uint4*>(codes + (size_t)e_ * kIdxCodeBytes);    \
     pc0 = cp_[0];                                                                             \
     pc1 = cp_[1];                                                                             \
@@ -254,7 +279,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
 #pragma unroll
     for (int r = 0; r < 16; ++r) rm[s][r] = -__builtin_inff();
 
-  for (int st = 0; st < kStages; ++st) {
+  for (int st = 0; st < n_stages; ++st) {
     if (st < n_active) {
       const int buf = st & 1;
       s_code[buf][stage_blk(tid, 0)] = pc0;
@@ -313,10 +338,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
 #pragma unroll
           for (int s = 0; s < kSets; ++s) {
             if (full) {
+              // every compare of the set first: the scalar tests that follow then wait for
+              // the vector unit once, not once per row
+              float v[16];
+              uint64_t mk[16];
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                const float v = acc[s][r] * sc;
-                push(s, r, v, v >= th[s][r], mask_ge(v, th[s][r]));
+                v[r] = acc[s][r] * sc;
+                mk[r] = mask_ge(v[r], th[s][r]);
+              }
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                push(s, r, v[r], v[r] >= th[s][r], mk[r]);
                 if ((r & 3) == 3 && qn >= 64u) flush(false);
               }
             } else {
@@ -334,7 +367,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
       }
     }
     if (PASS == 1 && (st + 1) % kRunStages == 0) {  // end of a run: publish the group maxima
-      const int g = split * kGroupsPerSplit + (st / kRunStages) * 32 + rl;
+      const int g = split * groups_per_split + (st / kRunStages) * 32 + rl;
 #pragma unroll
       for (int s = 0; s < kSets; ++s)
 #pragma unroll
@@ -417,10 +450,12 @@ __device__ uint32_t block_scan_excl(uint32_t v, uint32_t* scratch, uint32_t* tot
 }
 
 // theta_t: +inf for a row that takes all its (at most k) visible entries; otherwise the
-// k-th largest group maximum of row t as a float lower bound, or -inf when the row has
-// fewer than k non-empty groups.
+// kq-th largest of the row's group maxima (G_used of them), or -inf when the row has fewer
+// than kq non-empty groups.  With groups over every entry and kq = k this is a rigorous
+// lower bound on the row's k-th score; over a sample it is an estimate, which the select
+// checks (it needs at least k candidates).
 __global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, int ratio,
-                                                               int64_t pos0, int T, int k,
+                                                               int64_t pos0, int T, int k, int kq,
                                                                PrefillWs ws) {
   // 256 bins, each spread over 16 copies (copy = lane % 16) so that the many lanes whose
   // maxima share a bin do not serialise on one LDS word
@@ -438,7 +473,7 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, in
   // in registers, a longer row is read again from memory at each level
   constexpr int kRegChunks = 4;
   const uint4* g4 = reinterpret_cast<const uint4*>(ws.gmax + (size_t)t * ws.G);
-  const int nch = ws.G / 8;
+  const int nch = ws.G_used / 8;
   const bool cached = nch <= kRegChunks * kSelThreads;
   uint4 w[kRegChunks];
 #pragma unroll
@@ -455,7 +490,7 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, in
         atomicAdd(&s_hist[((m >> shift) & 255u) * 16 + (lane & 15)], 1u);
     }
   };
-  uint32_t need = (uint32_t)k, prefix = 0;
+  uint32_t need = (uint32_t)kq, prefix = 0;
   for (int level = 0; level < 2; ++level) {
     const int shift = 8 - 8 * level;
 #pragma unroll
@@ -488,7 +523,7 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, in
       }
     }
     __syncthreads();
-    if (level == 0 && s_res[2] < (uint32_t)k) {  // fewer than k non-empty groups
+    if (level == 0 && s_res[2] < (uint32_t)kq) {  // fewer than kq non-empty groups
       if (tid == 0) ws.theta[t] = -__builtin_inff();
       return;
     }
@@ -570,7 +605,9 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     }
     if (lane == 0) {
       s_total = carry;
-      s_over = over | (carry > (uint32_t)kCandLds ? 1u : 0u);
+      // too many candidates for LDS, or (a sampled threshold) too few to hold the top k:
+      // the row is recomputed
+      s_over = over | (carry > (uint32_t)kCandLds ? 1u : 0u) | (carry < k_eff ? 1u : 0u);
     }
   }
   __syncthreads();
@@ -727,16 +764,33 @@ hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_
                           float softmax_scale, int32_t* idx_out, float* out, void* ws_base,
                           hipStream_t stream) {
   PrefillWs ws = prefill_ws_carve(ws_base, T, n_entries);
-  const dim3 ggrid((T + kGemmRows - 1) / kGemmRows, ws.n_splits);
-  if (n_entries > 0) {
-    hipLaunchKernelGGL(k_prefill_gemm<1>, ggrid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
-                       idx_scale, n_entries, ratio, pos0, T, ws);
+  const int row_blocks = (T + kGemmRows - 1) / kGemmRows;
+  // Threshold: from a 1-in-kSampleStride sample of the entries when every row sees enough of
+  // them for the estimate to be sharp (the kq-th of ~n/128 sample group maxima, kq = 3k/8,
+  // aims at about 1.5 k candidates per row), else the rigorous bound from every entry.
+  const int kq = (3 * k + 7) / 8;
+  const bool sampled = kq >= kSampleMinQ && n_entries > 0 &&
+                       (int64_t)visible_host(pos0, ratio, n_entries) >= (int64_t)kSampleMinGroupsPerQ * kq * 32 * kSampleStride;
+  if (sampled) {
+    // a quarter of the columns: quarter-size splits keep the grid as wide as pass 2's
+    constexpr int split = kSplitEntries / kSampleStride;
+    const int n_cols = (n_entries + kSampleStride - 1) / kSampleStride;
+    const int splits = (n_cols + split - 1) / split;
+    ws.G_used = splits * (split / (kRunStages * kStage) * 32);
+    hipLaunchKernelGGL((k_prefill_gemm<1, kSampleStride, split>), dim3(row_blocks, splits),
+                       dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
+                       pos0, T, ws);
+  } else if (n_entries > 0) {
+    hipLaunchKernelGGL((k_prefill_gemm<1, 1, kSplitEntries>), dim3(row_blocks, ws.n_splits),
+                       dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
+                       pos0, T, ws);
   }
   hipLaunchKernelGGL(k_prefill_theta, dim3(T), dim3(kSelThreads), 0, stream, n_entries, ratio, pos0, T,
-                     k, ws);
+                     k, sampled ? kq : k, ws);
   if (n_entries > 0) {
-    hipLaunchKernelGGL(k_prefill_gemm<2>, ggrid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
-                       idx_scale, n_entries, ratio, pos0, T, ws);
+    hipLaunchKernelGGL((k_prefill_gemm<2, 1, kSplitEntries>), dim3(row_blocks, ws.n_splits),
+                       dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
+                       pos0, T, ws);
   }
   hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), 0, stream, q_idx, idx_codes,
                      idx_scale, n_entries, ratio, pos0, T, k, idx_out, ws);

@@ -89,6 +89,34 @@ def test_prefill_all_rows(N, ratio, T, pos0, k):
     check_rows(cache, q_idx, q, swa, N, ratio, pos0, k, idx, out, range(T))
 
 
+def test_prefill_sampled_threshold_rows():
+    # every row sees >= 98,304 entries and k = 512: the threshold comes from a 1-in-4 sample
+    log("prefill sampled threshold")
+    N, T, pos0, k = 100000, 64, 99000, 512
+    cache, q_idx, q, swa, idx, out = _case(N, 1, T, pos0, k, seed=77)
+    check_rows(cache, q_idx, q, swa, N, 1, pos0, k, idx, out, range(T))
+
+
+def test_prefill_sampled_threshold_too_high_falls_back():
+    # the sampled entries (every 4th) score far above the rest, so the sampled threshold
+    # admits fewer than k candidates: rows must be resolved exactly by recomputation
+    log("prefill sampled threshold fallback")
+    N, T, pos0, k = 100000, 8, 99000, 512
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(N, 128, generator=g)
+    x[::4] += 0.3
+    codes, scale, _ = synth.quantize_index_keys(x)
+    base = synth.make_entries([N], seed=5, device=DEV)
+    cache = synth.EntryCache(codes.to(DEV), scale.to(DEV), base.kv_codes, base.kv_scale,
+                             base.seq_base, base.n_entries)
+    q_idx = synth.bf16_bits(torch.ones(T, 128)).to(DEV)
+    q = synth.make_queries(T, 5, device=DEV)
+    swa = synth.make_swa(1, T + 127, 5, device=DEV)[0]
+    idx, out = run_prefill(cache, q_idx, q, swa, N, 1, pos0, k)
+    torch.cuda.synchronize()
+    check_rows(cache, q_idx, q, swa, N, 1, pos0, k, idx, out, range(T))
+
+
 def test_prefill_overflow_path_all_ties():
     # every score is 0: the candidate list overflows and rows are resolved by recomputation;
     # ties go to the lowest entries
