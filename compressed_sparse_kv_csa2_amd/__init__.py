@@ -54,7 +54,8 @@ _SIGS = {
     "csa2_prefill_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "csa2_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
                                           _F32, _P, _P, _P, _SZ, _P]),
-    "csa2_sparse_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I64, _I32, _F32, _P, _P]),
+    "csa2_sparse_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I64, _I32, _F32, _P, _P,
+                                                _SZ, _P]),
     "csa2_kv_append": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P, _P, _I64, _P, _P]),
     "csa2_swa_append": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
 }
@@ -334,10 +335,11 @@ def csa2_swa_append(x, pos, swa, stream=None):
     _check(load_library().csa2_swa_append(_ptr(x), _ptr(pos), B, _ptr(swa), _stream(stream)))
 
 
-def csa2_sparse_attn_prefill(q, kv_codes, kv_scale, idx, swa, pos0, out, softmax_scale=512 ** -0.5,
-                             stream=None):
+def csa2_sparse_attn_prefill(q, kv_codes, kv_scale, idx, swa, pos0, out, workspace,
+                             softmax_scale=512 ** -0.5, stream=None):
     """out [T, 16, 512]: query t (position pos0 + t) over its list idx[t] (entry ids from 0;
-    None for none) and its causal window from swa [T + 127, 512] (row r = position pos0-127+r)."""
+    None for none) and its causal window from swa [T + 127, 512] (row r = position pos0-127+r).
+    workspace: attn_workspace(T, k)."""
     T = q.shape[0]
     _need(q, "q", _BF16, (T, 16, 512))
     _need(kv_codes, "kv_codes", _U8, (None, 256))
@@ -348,7 +350,9 @@ def csa2_sparse_attn_prefill(q, kv_codes, kv_scale, idx, swa, pos0, out, softmax
         k = idx.shape[1]
     _need(swa, "swa", _U8, (T + 127, 512))
     _need(out, "out", (torch.float32,), (T, 16, 512))
+    _need(workspace, "workspace", _U8)
     _check(load_library().csa2_sparse_attn_prefill(_ptr(q), _ptr(kv_codes), _ptr(kv_scale),
                                                    _ptr(idx) if k > 0 else None, k, _ptr(swa),
                                                    int(pos0), T, float(softmax_scale), _ptr(out),
+                                                   _ptr(workspace), workspace.numel(),
                                                    _stream(stream)))

@@ -187,14 +187,17 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
 
 int csa2_sparse_attn_prefill(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
                              const int32_t* idx, int32_t k, const uint8_t* swa, int64_t pos0,
-                             int32_t T, float softmax_scale, float* out, void* stream) {
+                             int32_t T, float softmax_scale, float* out, void* workspace,
+                             size_t ws_bytes, void* stream) {
   if (!q || !swa || !out || !kv_codes || !kv_scale) return CSA2_ERR_INVALID_ARG;
   if (T < 1 || k < 0 || k > CSA2_MAX_K || pos0 < 0 || (k > 0 && !idx)) return CSA2_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(swa, 16) || !aligned(out, 16) || !aligned(kv_codes, 16) ||
       !aligned(kv_scale, 4) || (idx && !aligned(idx, 4)))
     return CSA2_ERR_ALIGNMENT;
+  if (!workspace || ws_bytes < attn_ws_bytes(T, k)) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
   return from_hip(launch_attn(1, q, kv_codes, kv_scale, nullptr, k > 0 ? idx : nullptr, k, swa,
-                              nullptr, pos0, softmax_scale, T, out, nullptr,
+                              nullptr, pos0, softmax_scale, T, out, workspace,
                               static_cast<hipStream_t>(stream)));
 }
 

@@ -80,8 +80,16 @@ static int attn_segs_per_split(int rows, int k) {
   return min(sps, segs);
 }
 
+// Splits a row of k entries + its window is cut into for `rows` rows.
+static int attn_used_splits(int rows, int k) {
+  const int sps = attn_segs_per_split(rows, k);
+  return (attn_segments(k) + sps - 1) / sps;
+}
+
+// Partials of the split rows; a launch whose rows are not split needs none.
 size_t attn_ws_bytes(int rows, int k) {
-  return align_up((size_t)rows * attn_splits(k) * kPart * sizeof(float), 256);
+  const int used = attn_used_splits(rows, k);
+  return used > 1 ? align_up((size_t)rows * used * kPart * sizeof(float), 256) : 256;
 }
 
 // ---- LDS tiles
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     }
   }
   __syncthreads();
-  if (MODE == 1 || n_splits == 1) {
+  if (n_splits == 1) {
     float* O = out + (size_t)b * kHeads * kDKv + kHalf * w;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -499,16 +507,22 @@ hipError_t launch_attn(int mode, const uint16_t* q, const uint8_t* kv_codes, con
                        float* out, void* ws, hipStream_t stream) {
   const float qscale = softmax_scale * 1.4426950408889634f;  // log2(e)
   const int segs = attn_segments(k);
-  if (mode == 1) {
-    hipLaunchKernelGGL(k_attn<1>, dim3(1, rows), dim3(kAThreads), 0, stream, q, kv_codes,
-                       kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, nullptr, segs, 1);
-    return hipGetLastError();
+  // rows are split over workgroups when they are few (decode batches, short prefill or
+  // replay chunks); a prefill row's causal window may be shorter than 128, so its last
+  // splits can be empty (they leave an empty partial)
+  int sps = attn_segs_per_split(rows, k);
+  int used = (segs + sps - 1) / sps;  // splits, each with at least one segment
+  if (ws == nullptr) {                // no room for partials: one split per row
+    sps = segs;
+    used = 1;
   }
-  const int sps = attn_segs_per_split(rows, k);
-  const int used = (segs + sps - 1) / sps;  // splits, each with at least one segment
   float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL(k_attn<0>, dim3(used, rows), dim3(kAThreads), 0, stream, q, kv_codes,
-                     kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, part, sps, used);
+  if (mode == 1)
+    hipLaunchKernelGGL(k_attn<1>, dim3(used, rows), dim3(kAThreads), 0, stream, q, kv_codes,
+                       kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, part, sps, used);
+  else
+    hipLaunchKernelGGL(k_attn<0>, dim3(used, rows), dim3(kAThreads), 0, stream, q, kv_codes,
+                       kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, part, sps, used);
   if (used > 1)
     hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, rows), dim3(kMergeThreads), 0, stream, part, used,
                        out);

@@ -66,7 +66,7 @@ struct PrefillWs {
   float* theta;                 // [T]
   uint32_t* ccount;             // [T][n_splits] candidates found per split
   unsigned long long* cand;     // [T][n_splits][kSlots] (key << 32 | entry)
-  void* attn;                   // attention workspace (unused by the prefill attention)
+  void* attn;                   // attention partials (rows split over workgroups)
   int G, n_splits;              // G: row stride of gmax (groups of the full pass 1)
   int G_used;                   // groups the current pass 1 wrote per row (<= G)
 };
@@ -76,7 +76,6 @@ static int prefill_splits(int n_entries) {
 }
 
 size_t prefill_ws_bytes(int T, int n_entries, int k) {
-  (void)k;
   const size_t S = (size_t)prefill_splits(n_entries);
   const size_t G = S * kGroupsPerSplit;
   size_t s = 0;
@@ -84,6 +83,7 @@ size_t prefill_ws_bytes(int T, int n_entries, int k) {
   s += align_up((size_t)T * 4, 256);
   s += align_up((size_t)T * S * 4, 256);
   s += align_up((size_t)T * S * kSlots * 8, 256);
+  s += attn_ws_bytes(T, k);  // partials when the attention splits its rows (short chunks)
   return s;
 }
 

@@ -116,6 +116,7 @@ class ReplayChunk:
         self.T, self.n, self.pos0, self.P, self.K = T, n_entries, pos0, pool, k
         dev = torch.device(device)
         self.sel_ws = select_chain_workspace(T, n_entries, pool, device=dev)
+        self.attn_ws = attn_workspace(T, k, device=dev)
         self.re_ws = index_topk_workspace(T, pool, k, device=dev)
         self.seq_base = torch.zeros((T,), dtype=torch.int64, device=dev)
         vis = torch.arange(pos0 + 1, pos0 + T + 1, dtype=torch.int64).clamp(max=n_entries)
@@ -145,6 +146,6 @@ class ReplayChunk:
                                 cand=self.pool, stream=stream)
             csa2_sparse_attn_prefill(q[l - DECODER_FULL], cache.kv_codes, cache.kv_scale,
                                      self.lists[list_source(l)], swa[l - DECODER_FULL], self.pos0,
-                                     self.out[l - DECODER_FULL], stream=stream)
+                                     self.out[l - DECODER_FULL], self.attn_ws, stream=stream)
         if marks is not None:
             marks[2].record(stream)

@@ -278,11 +278,15 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
  *   swa        u8 [T+127][512]       E4M3 window rows; row r holds position pos0-127+r;
  *              query t attends the rows for positions max(0,p-127)..p
  *   out        f32 [T][16][512] (out)
- * Errors: INVALID_ARG (T < 1, k < 0 or > 16384, pos0 < 0, null pointers), ALIGNMENT.
+ *   workspace  device, 256-byte aligned, csa2_attn_workspace_size(T, k) bytes (partials when
+ *              few rows are split over workgroups); no zero-filling needed
+ * Errors: INVALID_ARG (T < 1, k < 0 or > 16384, pos0 < 0, null pointers), ALIGNMENT,
+ * WORKSPACE.
  */
 int csa2_sparse_attn_prefill(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
                              const int32_t* idx, int32_t k, const uint8_t* swa, int64_t pos0,
-                             int32_t T, float softmax_scale, float* out, void* stream);
+                             int32_t T, float softmax_scale, float* out, void* workspace,
+                             size_t ws_bytes, void* stream);
 
 /*
  * csa2_kv_append -- the write path in front of the hot path: quantise n new global-KV

@@ -148,8 +148,8 @@ def test_swa_append_validation(lib):
 
 def test_attn_prefill_validation(lib):
     f = lib.csa2_sparse_attn_prefill
-    base = [FAKE, FAKE, FAKE, FAKE, 512, FAKE, 1000, 64, 0.04, FAKE, None]
+    base = [FAKE, FAKE, FAKE, FAKE, 512, FAKE, 1000, 64, 0.04, FAKE, FAKE, 1 << 40, None]
     for pos, val, want in [(7, 0, -1), (4, -1, -1), (6, -1, -1), (3, None, -1), (0, ODD, -2),
-                           (9, ODD, -2)]:
+                           (9, ODD, -2), (11, 10, -3), (10, None, -3)]:
         a = list(base); a[pos] = val
         assert f(*a) == want, (pos, val)

@@ -79,7 +79,8 @@ def test_attn_prefill_without_list():
     q = synth.make_queries(T, 3, device=DEV)
     swa = synth.make_swa(1, T + 127, 3, device=DEV)[0]
     out = torch.empty((T, 16, 512), dtype=torch.float32, device=DEV)
-    csa2.csa2_sparse_attn_prefill(q, cache.kv_codes, cache.kv_scale, None, swa, pos0, out)
+    csa2.csa2_sparse_attn_prefill(q, cache.kv_codes, cache.kv_scale, None, swa, pos0, out,
+                                  csa2.attn_workspace(T, 0))
     torch.cuda.synchronize()
     qq, sw, g = h(q), h(swa), h(out)
     for t in (0, 17, T - 1):
