@@ -10,7 +10,11 @@
  *                      gathered, dequantised and attended by 16 query heads, merged in one
  *                      softmax with the layer's own 128-row E4M3 sliding window;
  *   4. prefill      -- a chunk of queries, each scoring its causally visible keys (a BF16
- *                      MFMA contraction), taking its own top-k and attending.
+ *                      MFMA contraction), taking its own top-k and attending;
+ *   5. write path   -- new entries quantised into the two formats, new window rows into
+ *                      their E4M3 rings (csa2_kv_append, csa2_swa_append).
+ * Compositions (a decoder's layer chain in one call, a prefill or replay chunk's attention
+ * over lists made elsewhere) are entry points of their own below.
  *
  * Pages this interface follows (cited by title and section):
  *   [STRUCT] "DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash" (xhh.club):
