@@ -83,3 +83,49 @@ def test_whole_model_decode_step():
             ref = oracle.decode_attention(h(q[l])[b], *host[id(c)], base, idx,
                                           h(swa[l])[b], int(h(swa_len)[b]), SCALE)
             assert attn_rel_err(out1[l, b], ref) <= ATTN_TOL, f"layer {l} row {b}"
+
+
+def test_whole_model_decode_step_full_size():
+    # the benchmark's shape (2^20 context, batch 4) in its launch configuration; sampled
+    # checks: sequence 3 through every selecting layer and a spread of attention layers
+    B, n_enc, n_dec, seed = 4, 1 << 19, 1 << 20, 3
+    log(f"model pass full size B={B} enc={n_enc} dec={n_dec}")
+    enc = [synth.make_entries([n_enc] * B, seed=seed, device=DEV, field_base=10 * (i + 1))
+           for i in range(3)]
+    dec = synth.make_entries([n_dec] * B, seed=seed, device=DEV)
+    q_idx = {l: synth.make_index_queries(B, seed, device=DEV, sub=l) for l in model.SELECTING}
+    q = torch.stack([synth.make_queries(B, seed, device=DEV, sub=l) for l in range(40)]).contiguous()
+    swa = torch.stack([synth.make_swa(B, 128, seed, device=DEV, sub=l) for l in range(40)]).contiguous()
+    swa_len = torch.full((B,), 128, dtype=torch.int32, device=DEV)
+    run = model.DecodePass(B, n_enc, n_dec, device=DEV)
+    run.step(enc, dec, q_idx, q, swa, swa_len)
+    torch.cuda.synchronize()
+    b = 3
+    lists = {l: h(t)[b] for l, t in run.lists.items()}
+    out = h(run.out[:, b])
+    caches = {l: enc[i] for i, l in enumerate(model.ENCODER_FULL)}
+    for l in model.ENCODER_FULL:
+        c = caches[l]
+        sl = slice(b * n_enc, (b + 1) * n_enc)
+        s = oracle.index_scores(h(q_idx[l])[b], h(c.idx_codes[sl]), h(c.idx_scale[sl]))
+        check_topk(lists[l], s, 512, label=f"encoder Full {l}")
+    sl = slice(b * n_dec, (b + 1) * n_dec)
+    codes, scale = h(dec.idx_codes[sl]), h(dec.idx_scale[sl])
+    s = oracle.index_scores(h(q_idx[20])[b], codes, scale)
+    p = h(run.pool)[b]
+    check_topk(p, s, 16384, label="decoder pool")
+    check_topk(lists[20], s[p], 512, ids=p, label="decoder own")
+    for l in model.REINDEX:
+        _, r = oracle.reindex_layer(h(q_idx[l])[b], codes, scale, p)
+        check_topk(lists[l], r, 512, ids=p, label=f"Reindex {l}")
+    for l in (0, 2, 7, 14, 19, 20, 23, 28, 39):
+        src = None if l in model.WINDOW_ONLY else model.list_source(l)
+        if src is None:
+            c, n, idx = dec, n_dec, np.zeros(0, np.int32)
+        else:
+            c, n = (dec, n_dec) if src >= model.DECODER_FULL else (caches[src], n_enc)
+            idx = lists[src]
+        sl = slice(b * n, (b + 1) * n)
+        ref = oracle.decode_attention(h(q[l])[b], h(c.kv_codes[sl]), h(c.kv_scale[sl]), 0, idx,
+                                      h(swa[l])[b], 128, SCALE)
+        assert attn_rel_err(out[l], ref) <= ATTN_TOL, f"layer {l}"

@@ -90,3 +90,37 @@ def test_attn_prefill_without_list():
         ref = oracle.decode_attention(qq[t], h(cache.kv_codes), h(cache.kv_scale), 0,
                                       np.zeros(0, np.int32), win, win.shape[0], SCALE)
         assert attn_rel_err(g[t], ref) <= ATTN_TOL
+
+
+def test_replay_chunk_full_size():
+    # the benchmark's shape: the last 128 tokens of a 2^20-token sequence; sampled queries
+    n, T = 1 << 20, 128
+    pos0 = n - T
+    log(f"replay full size n={n} T={T}")
+    seed = 12
+    cache = synth.make_entries([n], seed=seed, device=DEV)
+    q_idx = {l: synth.make_index_queries(T, seed, device=DEV, sub=l) for l in (20,) + model.REINDEX}
+    q = torch.stack([synth.make_queries(T, seed, device=DEV, sub=l) for l in range(20, 40)]).contiguous()
+    swa = torch.stack([synth.make_swa(1, T + 127, seed, device=DEV, sub=l)[0] for l in range(20, 40)]).contiguous()
+    run = model.ReplayChunk(T, n, pos0, device=DEV)
+    run.step(cache, q_idx, q, swa)
+    torch.cuda.synchronize()
+    codes, scale = h(cache.idx_codes), h(cache.idx_scale)
+    kc, ks = h(cache.kv_codes), h(cache.kv_scale)
+    pool = h(run.pool)
+    lists = {l: h(v) for l, v in run.lists.items()}
+    out, qq, sw = h(run.out), h(q), h(swa)
+    for t in (0, T - 1):
+        vis = pos0 + t + 1
+        s = oracle.index_scores(h(q_idx[20])[t], codes[:vis], scale[:vis])
+        check_topk(pool[t], s, 16384, label=f"pool row {t}")
+        p = pool[t]
+        check_topk(lists[20][t], s[p], 512, ids=p, label=f"own row {t}")
+        _, r = oracle.reindex_layer(h(q_idx[32])[t], codes, scale, p)
+        check_topk(lists[32][t], r, 512, ids=p, label=f"Reindex 32 row {t}")
+        pos = pos0 + t
+        for l in (20, 27, 32, 39):
+            win = sw[l - 20][pos - 127 - (pos0 - 127): pos - (pos0 - 127) + 1]
+            ref = oracle.decode_attention(qq[l - 20][t], kc, ks, 0, lists[model.list_source(l)][t],
+                                          win, win.shape[0], SCALE)
+            assert attn_rel_err(out[l - 20][t], ref) <= ATTN_TOL, f"layer {l} row {t}"
