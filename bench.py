@@ -380,29 +380,35 @@ class Prefill:
         self.idx = torch.empty((self.T, self.K), dtype=torch.int32, device=dev)
         self.out = torch.empty((self.T, HEADS, D_KV), dtype=torch.float32, device=dev)
         self.ws = csa2.prefill_workspace(self.T, self.N, self.K, device=dev)
+        self.attn_ws = csa2.attn_workspace(self.T, self.K, device=dev)
         self.stream = torch.cuda.current_stream()
         self.queries_per_step = self.T
-        self.n_marks = 2
-        self.phase_names = ["chunk_us"]
+        self.n_marks = 3
+        self.phase_names = ["indexer_select_us", "attention_us"]
         # visible entry-pairs of the causal contraction: query t sees (pos0 + t + 1) // ratio
         self.pairs = sum(min(self.N, (self.pos0 + t + 1) // self.ratio) for t in range(self.T))
 
     def step(self, i, marks=None):
+        """The chunk as its two halves (the same kernels csa2_prefill_chunk runs): the causal
+        indexer and per-query selection, then the attention over the lists."""
         c, qi, q, sw = self.sets[i % len(self.sets)]
         s = self.stream
-        m = marks if marks is not None else Marks([None] * 2)
+        m = marks if marks is not None else Marks([None] * 3)
         m[0].record(s)
-        self.csa2.csa2_prefill_chunk(qi, q, c.idx_codes, c.idx_scale, c.kv_codes, c.kv_scale, self.N,
-                                     self.ratio, self.pos0, self.K, sw, self.idx, self.out, self.ws,
-                                     stream=s)
+        self.csa2.csa2_prefill_select(qi, c.idx_codes, c.idx_scale, self.N, self.ratio, self.pos0,
+                                      self.K, self.idx, self.ws, stream=s)
         m[1].record(s)
+        self.csa2.csa2_sparse_attn_prefill(q, c.kv_codes, c.kv_scale, self.idx, sw, self.pos0,
+                                           self.out, self.attn_ws, stream=s)
+        m[2].record(s)
 
     def dominant(self):
         # the causal indexer contraction counted once (2 flops per multiply-add; the library
-        # runs it twice, the second time to collect candidates), timed as the whole chunk
-        # call: a lower bound on the contraction's own rate (per-kernel times: rocprofv3)
-        return {"kernel": "csa2_prefill_chunk (causal BF16 MFMA indexer contraction; whole call "
-                          "timed)",
+        # runs a quarter of it again for the sampled threshold), timed over the whole indexer
+        # and selection call: a lower bound on the contraction's own rate (per kernel:
+        # rocprofv3)
+        return {"kernel": "csa2_prefill_select (causal BF16 MFMA indexer contraction, sampled "
+                          "threshold and per-query top-512; the call timed)",
                 "bound": "mfma", "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
                 "work": 2 * D_IDX * self.pairs, "scale": 1e12, "marks": (0, 1)}
 

@@ -21,7 +21,7 @@ __all__ = [
     "csa2_sparse_attn_decode", "csa2_prefill_chunk", "csa2_topk_workspace_size",
     "csa2_index_topk_workspace_size", "csa2_select_chain_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
     "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
-    "csa2_sparse_attn_prefill", "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
+    "csa2_prefill_select", "csa2_sparse_attn_prefill", "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +54,8 @@ _SIGS = {
     "csa2_prefill_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "csa2_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
                                           _F32, _P, _P, _P, _SZ, _P]),
+    "csa2_prefill_select": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P, _P, _SZ,
+                                           _P]),
     "csa2_sparse_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I64, _I32, _F32, _P, _P,
                                                 _SZ, _P]),
     "csa2_kv_append": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P, _P, _I64, _P, _P]),
@@ -356,3 +358,20 @@ def csa2_sparse_attn_prefill(q, kv_codes, kv_scale, idx, swa, pos0, out, workspa
                                                    int(pos0), T, float(softmax_scale), _ptr(out),
                                                    _ptr(workspace), workspace.numel(),
                                                    _stream(stream)))
+
+
+def csa2_prefill_select(q_idx, idx_codes, idx_scale, n_entries, ratio, pos0, k, idx_out, workspace,
+                        stream=None):
+    """idx_out [T, k]: the per-query top-k of csa2_prefill_chunk, without its attention."""
+    T = q_idx.shape[0]
+    _need(q_idx, "q_idx", _BF16, (T, 128))
+    _need(idx_codes, "idx_codes", _U8, (None, 64))
+    _need(idx_scale, "idx_scale", (torch.float32,), (idx_codes.shape[0],))
+    if idx_codes.shape[0] < n_entries:
+        raise ValueError("fewer cache entries than n_entries")
+    _need(idx_out, "idx_out", (torch.int32,), (T, k))
+    _need(workspace, "workspace", _U8)
+    _check(load_library().csa2_prefill_select(_ptr(q_idx), _ptr(idx_codes), _ptr(idx_scale),
+                                              int(n_entries), int(ratio), int(pos0), T, int(k),
+                                              _ptr(idx_out), _ptr(workspace), workspace.numel(),
+                                              _stream(stream)))

@@ -185,6 +185,22 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
                                  static_cast<hipStream_t>(stream)));
 }
 
+int csa2_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                        int32_t n_entries, int32_t ratio, int64_t pos0, int32_t T, int32_t k,
+                        int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!q_idx || !idx_out) return CSA2_ERR_INVALID_ARG;
+  if (n_entries > 0 && (!idx_codes || !idx_scale)) return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || n_entries < 0 || ratio < 1 || pos0 < 0 || k < 1 || k > CSA2_MAX_K)
+    return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(idx_out, 4) || (idx_codes && !aligned(idx_codes, 16)) ||
+      (idx_scale && !aligned(idx_scale, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  if (!workspace || ws_bytes < prefill_ws_bytes(T, n_entries, k)) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_prefill_select(q_idx, idx_codes, idx_scale, n_entries, ratio, pos0, T, k,
+                                        idx_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int csa2_sparse_attn_prefill(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
                              const int32_t* idx, int32_t k, const uint8_t* swa, int64_t pos0,
                              int32_t T, float softmax_scale, float* out, void* workspace,

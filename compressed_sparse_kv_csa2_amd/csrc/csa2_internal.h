@@ -77,6 +77,9 @@ hipError_t launch_attn(int mode, const uint16_t* q, const uint8_t* kv_codes, con
 
 // ---- prefill ----
 size_t prefill_ws_bytes(int T, int n_entries, int k);
+hipError_t launch_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes,
+                                 const float* idx_scale, int n_entries, int ratio, int64_t pos0,
+                                 int T, int k, int32_t* idx_out, void* ws, hipStream_t stream);
 hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_t* idx_codes,
                           const float* idx_scale, const uint8_t* kv_codes, const uint8_t* kv_scale,
                           int n_entries, int ratio, int64_t pos0, int T, int k, const uint8_t* swa,

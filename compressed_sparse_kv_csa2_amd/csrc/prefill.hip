@@ -758,11 +758,9 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
   for (int i = (int)written + tid; i < k; i += kSelThreads) orow[i] = -1;
 }
 
-hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_t* idx_codes,
-                          const float* idx_scale, const uint8_t* kv_codes, const uint8_t* kv_scale,
-                          int n_entries, int ratio, int64_t pos0, int T, int k, const uint8_t* swa,
-                          float softmax_scale, int32_t* idx_out, float* out, void* ws_base,
-                          hipStream_t stream) {
+hipError_t launch_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes,
+                                 const float* idx_scale, int n_entries, int ratio, int64_t pos0,
+                                 int T, int k, int32_t* idx_out, void* ws_base, hipStream_t stream) {
   PrefillWs ws = prefill_ws_carve(ws_base, T, n_entries);
   const int row_blocks = (T + kGemmRows - 1) / kGemmRows;
   // Threshold: from a 1-in-kSampleStride sample of the entries when every row sees enough of
@@ -794,8 +792,18 @@ hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_
   }
   hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), 0, stream, q_idx, idx_codes,
                      idx_scale, n_entries, ratio, pos0, T, k, idx_out, ws);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const uint16_t* q_idx, const uint16_t* q, const uint8_t* idx_codes,
+                          const float* idx_scale, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                          int n_entries, int ratio, int64_t pos0, int T, int k, const uint8_t* swa,
+                          float softmax_scale, int32_t* idx_out, float* out, void* ws_base,
+                          hipStream_t stream) {
+  const hipError_t e = launch_prefill_select(q_idx, idx_codes, idx_scale, n_entries, ratio, pos0, T, k,
+                                             idx_out, ws_base, stream);
   if (e != hipSuccess) return e;
+  const PrefillWs ws = prefill_ws_carve(ws_base, T, n_entries);
   return launch_attn(1, q, kv_codes, kv_scale, nullptr, idx_out, k, swa, nullptr, pos0, softmax_scale,
                      T, out, ws.attn, stream);
 }

@@ -270,6 +270,20 @@ int csa2_prefill_chunk(const uint16_t* q_idx, const uint16_t* q, const uint8_t* 
                        void* stream);
 
 /*
+ * csa2_prefill_select -- a7 and the per-query top-k of csa2_prefill_chunk without the
+ * attention: idx_out is exactly what csa2_prefill_chunk writes for the same arguments.  For
+ * a layer group whose Full layer selects once and whose Reuse layers attend over the same
+ * lists (csa2_sparse_attn_prefill per layer).
+ *   [STRUCT] content summary and Q&A on prefill; [V4TO41] CSA2 architecture (Reuse).
+ *   Arguments as csa2_prefill_chunk; the workspace is csa2_prefill_workspace_size(T,
+ *   n_entries, k) bytes, 256-byte aligned, no zero-filling needed.
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE.
+ */
+int csa2_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                        int32_t n_entries, int32_t ratio, int64_t pos0, int32_t T, int32_t k,
+                        int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * csa2_sparse_attn_prefill -- a5 + a6 for T consecutive query positions of one sequence,
  * each over its own list and its own causal window: the attention half of
  * csa2_prefill_chunk, for lists made elsewhere (a Reuse layer of a prefill or replay chunk

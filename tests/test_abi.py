@@ -153,3 +153,12 @@ def test_attn_prefill_validation(lib):
                            (9, ODD, -2), (11, 10, -3), (10, None, -3)]:
         a = list(base); a[pos] = val
         assert f(*a) == want, (pos, val)
+
+
+def test_prefill_select_validation(lib):
+    f = lib.csa2_prefill_select
+    base = [FAKE, FAKE, FAKE, 131072, 2, 258048, 4096, 512, FAKE, FAKE, 1 << 40, None]
+    for pos, val, want in [(4, 0, -1), (5, -1, -1), (7, 0, -1), (6, 0, -1), (0, ODD, -2),
+                           (10, 10, -3), (9, None, -3)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)

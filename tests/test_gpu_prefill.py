@@ -117,6 +117,35 @@ def test_prefill_sampled_threshold_too_high_falls_back():
     check_rows(cache, q_idx, q, swa, N, 1, pos0, k, idx, out, range(T))
 
 
+def test_prefill_select_and_reuse_attention_match_chunk():
+    # csa2_prefill_select writes the chunk's lists; csa2_sparse_attn_prefill over them with the
+    # same queries and window reproduces the chunk's output bit for bit, and a Reuse layer's
+    # own queries and window over the same lists match the oracle
+    log("prefill select + reuse attention")
+    N, ratio, T, pos0, k = 20000, 2, 200, 39800, 512
+    cache, q_idx, q, swa, idx, out = _case(N, ratio, T, pos0, k, seed=31)
+    ws = csa2.prefill_workspace(T, N, k)
+    idx2 = torch.empty_like(idx)
+    csa2.csa2_prefill_select(q_idx, cache.idx_codes, cache.idx_scale, N, ratio, pos0, k, idx2, ws)
+    out2 = torch.empty_like(out)
+    aws = csa2.attn_workspace(T, k)
+    csa2.csa2_sparse_attn_prefill(q, cache.kv_codes, cache.kv_scale, idx2, swa, pos0, out2, aws, SCALE)
+    q_r = synth.make_queries(T, 32, device=DEV)
+    swa_r = synth.make_swa(1, T + 127, 32, device=DEV)[0]
+    out_r = torch.empty_like(out)
+    csa2.csa2_sparse_attn_prefill(q_r, cache.kv_codes, cache.kv_scale, idx2, swa_r, pos0, out_r, aws, SCALE)
+    torch.cuda.synchronize()
+    assert np.array_equal(h(idx2), h(idx))
+    assert np.array_equal(h(out2), h(out))
+    kc, ks, g = h(cache.kv_codes), h(cache.kv_scale), h(idx2)
+    for t in (0, 99, T - 1):
+        p = pos0 + t
+        lo = max(0, p - 127)
+        win = h(swa_r)[lo - (pos0 - 127): p - (pos0 - 127) + 1]
+        ref = oracle.decode_attention(h(q_r)[t], kc, ks, 0, g[t], win, win.shape[0], SCALE)
+        assert attn_rel_err(h(out_r)[t], ref) <= ATTN_TOL, f"row {t}"
+
+
 def test_prefill_overflow_path_all_ties():
     # every score is 0: the candidate list overflows and rows are resolved by recomputation;
     # ties go to the lowest entries
