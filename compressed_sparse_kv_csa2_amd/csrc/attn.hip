@@ -166,6 +166,10 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
 
   const int split = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // the row's base and window length first: the first gather's addresses need them, so
+  // their latency overlaps the ids' and q's instead of following them
+  const int64_t base = MODE == 0 ? seq_base[b] : 0;
+  const int row_swa_len = MODE == 0 ? swa_len[b] : 0;
   const int n16 = lane & 15, g16 = lane >> 4;
   const int d0 = kHalf * w + 64 * g16;  // this lane's first dim in the q . v steps
   const int32_t* irow = k > 0 ? idx + (size_t)b * k : nullptr;
@@ -229,12 +233,11 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     for (int j = 0; j < 2; ++j) qs[j] = qscale * ldexpf(1.0f, __shfl(e, 8 * w + 2 * g16 + j));
   }
 
-  const int64_t base = MODE == 0 ? seq_base[b] : 0;
   const uint8_t* rows;
   int nrows;
   if (MODE == 0) {
     rows = swa + (size_t)b * kSwa * kDKv;
-    nrows = min(max(swa_len[b], 0), kSwa);
+    nrows = min(max(row_swa_len, 0), kSwa);
   } else {
     const int64_t p = pos0 + b;
     const int64_t lo = p - (kSwa - 1) > 0 ? p - (kSwa - 1) : 0;
