@@ -460,6 +460,13 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __res
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int par = tid >> 7, d = 4 * (tid & 127);
   const float* P0 = part + (size_t)b * n_splits * kPart;
+  // each split's (max, sum) first: loads return in order, so the weights can be computed
+  // while the accumulators are still on their way
+  float ms = -__builtin_inff(), ls = 0.f;
+  if (tid < 64 && lane < n_splits) {
+    ms = P0[(size_t)lane * kPart + h];
+    ls = P0[(size_t)lane * kPart + kHeads + h];
+  }
   float4 a[kMaxSplits / 2];
 #pragma unroll
   for (int i = 0; i < kMaxSplits / 2; ++i) {
@@ -468,8 +475,6 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __res
                          : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (tid < 64) {
-    const float ms = lane < n_splits ? P0[(size_t)lane * kPart + h] : -__builtin_inff();
-    const float ls = lane < n_splits ? P0[(size_t)lane * kPart + kHeads + h] : 0.f;
     float M = ms;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
