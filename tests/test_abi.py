@@ -162,3 +162,16 @@ def test_prefill_select_validation(lib):
                            (10, 10, -3), (9, None, -3)]:
         a = list(base); a[pos] = val
         assert f(*a) == want, (pos, val)
+
+
+def test_binding_rejects_host_tensors():
+    # no CPU fallback: the binding refuses tensors that are not on the GPU before any call
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.int16)
+    y = torch.zeros((4, 512), dtype=torch.int16)
+    planes = (torch.zeros((8, 64), dtype=torch.uint8), torch.zeros(8), torch.zeros((8, 256), dtype=torch.uint8),
+              torch.zeros((8, 32), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU"):
+        csa2.csa2_kv_append(x, y, torch.arange(4), *planes)
+    with pytest.raises(ValueError, match="GPU"):
+        csa2.csa2_swa_append(y, torch.arange(4), torch.zeros((4, 128, 512), dtype=torch.uint8))
