@@ -1,8 +1,9 @@
 """One decode step of the 40-layer CSA2 backbone, sequenced through the C ABI.
 
 Sequencing only: every step runs in the library's kernels (csa2_index_topk,
-csa2_select_chain, csa2_sparse_attn_decode); this module holds workspaces and output
-buffers and issues the calls in layer order on one stream.
+csa2_select_chain, csa2_index_score + csa2_topk, csa2_sparse_attn_decode,
+csa2_sparse_attn_prefill); this module holds workspaces and output buffers and issues the
+calls in layer order on one stream.
 
 Layer layout ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash", Q&A on how the
 40 layers are laid out, and commentary on the four layer modes; "从V4到V4.1 Flash：架构的
@@ -17,14 +18,16 @@ Layer layout ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1
   * every layer attends with its own 16 x 512 query over its list plus its own 128-row
     window.
 Each Reindex layer's query arrives at its own layer (it depends on the layers before it in
-a real decoder), so the Reindex selections run one call per layer.
+a real decoder), so the Reindex selections run per layer: the pool re-scored, then its
+top-k (two launches; for pools of 16,384 this is faster than the single fused launch).
 """
 from __future__ import annotations
 
 import torch
 
-from . import (attn_workspace, csa2_index_topk, csa2_select_chain, csa2_sparse_attn_decode,
-               csa2_sparse_attn_prefill, index_topk_workspace, select_chain_workspace)
+from . import (attn_workspace, csa2_index_score, csa2_index_topk, csa2_select_chain,
+               csa2_sparse_attn_decode, csa2_sparse_attn_prefill, csa2_topk, index_topk_workspace,
+               select_chain_workspace, topk_workspace)
 
 N_LAYERS = 40
 WINDOW_ONLY = (0, 1)
@@ -52,7 +55,10 @@ class DecodePass:
         dev = torch.device(device)
         self.enc_ws = index_topk_workspace(batch, enc_entries, k, device=dev)
         self.dec_ws = select_chain_workspace(batch, dec_entries, pool, device=dev)
-        self.re_ws = index_topk_workspace(batch, pool, k, device=dev)
+        # a Reindex layer re-scores the pool and selects in two launches (measured faster than
+        # the single fused launch for pools of this size: 21 against 28 us at batch 4)
+        self.re_ws = topk_workspace(batch, pool, k, device=dev)
+        self.re_scores = torch.empty((batch, pool), dtype=torch.float32, device=dev)
         self.attn_ws = attn_workspace(batch, k, device=dev)
         self.pool = torch.empty((batch, pool), dtype=torch.int32, device=dev)
         self.pool_valid = torch.full((batch,), pool, dtype=torch.int32, device=dev)
@@ -82,9 +88,10 @@ class DecodePass:
                     marks[2].record(stream)
             elif l in REINDEX:
                 c = dec_cache
-                csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid,
-                                self.K, self.lists[l], self.re_ws, self.P, cand=self.pool,
-                                stream=stream)
+                csa2_index_score(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid,
+                                 self.re_scores, cand=self.pool, topk_ws=self.re_ws, stream=stream)
+                csa2_topk(self.re_scores, self.pool_valid, self.K, self.lists[l], cand=self.pool,
+                          hist_fused=True, workspace=self.re_ws, stream=stream)
             if l in WINDOW_ONLY:
                 c, idx = dec_cache, None
             else:
@@ -117,7 +124,8 @@ class ReplayChunk:
         dev = torch.device(device)
         self.sel_ws = select_chain_workspace(T, n_entries, pool, device=dev)
         self.attn_ws = attn_workspace(T, k, device=dev)
-        self.re_ws = index_topk_workspace(T, pool, k, device=dev)
+        self.re_ws = topk_workspace(T, pool, k, device=dev)  # Reindex: re-score, then select
+        self.re_scores = torch.empty((T, pool), dtype=torch.float32, device=dev)
         self.seq_base = torch.zeros((T,), dtype=torch.int64, device=dev)
         vis = torch.arange(pos0 + 1, pos0 + T + 1, dtype=torch.int64).clamp(max=n_entries)
         self.n_visible = vis.to(torch.int32).to(dev)
@@ -141,9 +149,11 @@ class ReplayChunk:
             marks[1].record(stream)
         for l in range(DECODER_FULL, N_LAYERS):
             if l in REINDEX:
-                csa2_index_topk(q_idx[l], cache.idx_codes, cache.idx_scale, self.seq_base,
-                                self.pool_valid, self.K, self.lists[l], self.re_ws, self.P,
-                                cand=self.pool, stream=stream)
+                csa2_index_score(q_idx[l], cache.idx_codes, cache.idx_scale, self.seq_base,
+                                 self.pool_valid, self.re_scores, cand=self.pool, topk_ws=self.re_ws,
+                                 stream=stream)
+                csa2_topk(self.re_scores, self.pool_valid, self.K, self.lists[l], cand=self.pool,
+                          hist_fused=True, workspace=self.re_ws, stream=stream)
             csa2_sparse_attn_prefill(q[l - DECODER_FULL], cache.kv_codes, cache.kv_scale,
                                      self.lists[list_source(l)], swa[l - DECODER_FULL], self.pos0,
                                      self.out[l - DECODER_FULL], self.attn_ws, stream=stream)
