@@ -316,8 +316,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       }
       f32x4v z = {0.f, 0.f, 0.f, 0.f};
       f16* vrow = vt + n16 * kHalf;
-      int sw = vswz(n16);
-      asm volatile("" : "+v"(sw));  // recomputed per segment: no 8 addresses held live
+      const int sw = vswz(n16);  // loop-invariant: the 8 write addresses stay in registers
       auto step = [&](int s, const f16x8& bv) {
         *reinterpret_cast<f16x8*>(vrow + 8 * ((8 * g16 + s) ^ sw)) = bv;
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], bv, z, 0, 0, 0);
@@ -386,9 +385,9 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       // ---- acc += p . v over this wave's half: A = p (head, 4 positions), B = v, transposed
       const f16x4 a_hi = tr_read(s_p[0] + tr_row * kHeads + 4 * tr_q);
       const f16x4 a_lo = tr_read(s_p[1] + tr_row * kHeads + 4 * tr_q);
-      int tsw = vswz(tr_row);
-      asm volatile("" : "+v"(tsw));
-      // tiles t and t + 8 share the swizzled block's low bits: 8 bases, immediate offsets
+      const int tsw = vswz(tr_row);
+      // tiles t and t + 8 share the swizzled block's low bits: 8 loop-invariant bases,
+      // immediate offsets
       const f16* vr[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t)
