@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       return r;
     };
 
-    auto compute = [&](const Raw& r) {
+    auto compute = [&](Raw& r, int next) {
       // ---- dequantise this wave's half into B operands, stage it for p . v, and q . v.
       // The segment's kinds pick one of three straight-line paths (wave-uniform): main
       // entries (a lane with nothing dequantises with scale 0), window rows, or both.
@@ -340,6 +340,10 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
           step(s, win ? bw : bm);
         }
       }
+      // the raw bytes are dead: the next segment's loads go into the same registers and
+      // stay in flight through the softmax and p . v (no second register set to copy from)
+      const bool valid = r.kind != 0;
+      r = issue(next);
       // ---- the two halves' scores, added in the same order in both waves
       s_z[w][lane] = z;
       __syncthreads();
@@ -348,7 +352,6 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       const float2 za = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&s_z[0][zl]) + 2 * (g16 & 1));
       const float2 zb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&s_z[1][zl]) + 2 * (g16 & 1));
       const float zsum[2] = {za.x + zb.x, za.y + zb.y};
-      const bool valid = r.kind != 0;
       float p[2], alpha[2];
       bool moved = false;
 #pragma unroll
@@ -405,11 +408,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
 
     // the next segment's loads are in flight while one is computed
     Raw r0 = issue(0);
-    for (int i = 0; i < n_i; ++i) {
-      const Raw nx = issue(i + 1);
-      compute(r0);
-      r0 = nx;
-    }
+    for (int i = 0; i < n_i; ++i) compute(r0, i + 1);
   }
 
   // ---- each head's max and sum (over its 16 lanes' shares), then out (one split) or this
