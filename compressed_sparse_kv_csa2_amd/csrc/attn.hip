@@ -352,32 +352,28 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       const float2 za = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&s_z[0][zl]) + 2 * (g16 & 1));
       const float2 zb = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&s_z[1][zl]) + 2 * (g16 & 1));
       const float zsum[2] = {za.x + zb.x, za.y + zb.y};
-      float zs[2], mu[2];
+      float zs[2], alpha[2] = {1.0f, 1.0f};
+      bool moved = false;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        zs[j] = valid ? zsum[j] * qs[j] : -__builtin_inff();
-        mu[j] = m[j];
-      }
+      for (int j = 0; j < 2; ++j) zs[j] = valid ? zsum[j] * qs[j] : -__builtin_inff();
       // a head's running max moves only to a segment maximum above it by more than
       // kRescale, so one compare per lane tells whether any head of the wave needs its
-      // segment maximum (the first segment, then rarely); the result is the same as always
-      // reducing
+      // segment maximum and rescale factor (the first segment, then rarely); otherwise
+      // both stay as they are (factor 1), the same result as always reducing
       if (__ballot(zs[0] > m[0] + kRescale || zs[1] > m[1] + kRescale) != 0ull) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const float cm = row16<true>(zs[j]);
-          mu[j] = cm > m[j] + kRescale ? cm : m[j];
+          const float mu = cm > m[j] + kRescale ? cm : m[j];
+          alpha[j] = mu == m[j] ? 1.0f : (m[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[j] - mu));
+          moved |= mu != m[j];
+          m[j] = mu;
         }
       }
-      float p[2], alpha[2];
-      bool moved = false;
+      float p[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        alpha[j] = mu[j] == m[j] ? 1.0f
-                                 : (m[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m[j] - mu[j]));
-        moved |= mu[j] != m[j];
-        m[j] = mu[j];
-        p[j] = zs[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(zs[j] - mu[j]);
+        p[j] = zs[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(zs[j] - m[j]);
         lp[j] = lp[j] * alpha[j] + p[j];
       }
       // p = hi + lo in fp16, staged as [position][head]; each head's rescale and whether a
