@@ -175,6 +175,11 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
   const int32_t* irow = k > 0 ? idx + (size_t)b * k : nullptr;
   const int seg_begin = split * segs_per_split;
 
+  // this lane's position in the split's first segment and its entry id, loaded first: the
+  // first gather depends on nothing else, so it is issued before q's prologue
+  const int p_first = seg_begin * kSeg + n16;
+  const int j_first = p_first < k ? irow[p_first] : -1;
+
   // the first stage's entry ids, loaded before q so that both latencies overlap
   constexpr int kIdPer = kIdxStage / kAThreads;
   int32_t ids[kIdPer];
@@ -190,12 +195,53 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
   // ---- q as A operands (head n16, dims d0 + 8 s .. + 7 for k-step s), scaled per head by
   // a power of two into fp16's range
   const uint16_t* qrow = q + ((size_t)b * kHeads + n16) * kDKv;
+  uint4 raw[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) raw[s] = reinterpret_cast<const uint4*>(qrow + d0)[s];
+
+  const uint8_t* rows;
+  int nrows;
+  if (MODE == 0) {
+    rows = swa + (size_t)b * kSwa * kDKv;
+    nrows = min(max(row_swa_len, 0), kSwa);
+  } else {
+    const int64_t p = pos0 + b;
+    const int64_t lo = p - (kSwa - 1) > 0 ? p - (kSwa - 1) : 0;
+    rows = swa + (size_t)(lo - (pos0 - (kSwa - 1))) * kDKv;
+    nrows = (int)(p - lo + 1);
+  }
+  const int n_pos = k + nrows;
+  const int n_seg = (n_pos + kSeg - 1) / kSeg;
+  const int seg_end = min(seg_begin + segs_per_split, n_seg);
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(qrow);  // any valid 64 bytes
+
+  // Raw bytes of segment `seg` for this lane (entry id j if its position holds a main
+  // entry); nothing at or past segment `stop`
+  auto gather = [&](int seg, int j, int stop) {
+    Raw r;
+    const int p = seg * kSeg + n16;
+    const int kind = (seg < stop && p < n_pos) ? (p < k ? (j >= 0 ? 1 : 0) : 2) : 0;
+    const int64_t e = base + (kind == 1 ? j : 0);
+    const uint8_t* am = kv_codes + e * kKvCodeBytes + d0 / 2;
+    const uint8_t* aw = rows + (size_t)(kind == 2 ? p - k : 0) * kDKv + d0;
+    const uint8_t* a = kind == 1 ? am : kind == 2 ? aw : dummy;
+    const uint8_t* a2 = kind == 2 ? aw + 32 : a;
+    const uint8_t* asc = kind == 1 ? kv_scale + e * kKvScaleBytes + d0 / 16 : a;
+    r.u[0] = reinterpret_cast<const uint4*>(a)[0];
+    r.u[1] = reinterpret_cast<const uint4*>(a)[1];
+    r.u[2] = reinterpret_cast<const uint4*>(a2)[0];
+    r.u[3] = reinterpret_cast<const uint4*>(a2)[1];
+    r.sc = *reinterpret_cast<const uint32_t*>(asc);
+    r.kind = kind;
+    return r;
+  };
+  // the split's first segment is in flight through q's prologue and the ids' staging
+  Raw r0 = gather(seg_begin, j_first, min(seg_begin + kIdxStage / kSeg, seg_end));
+  __builtin_amdgcn_sched_barrier(0);  // issued before the prologue's first wait on q
+
   f16x8 qa[8];
   float qs[2];  // softmax scale of heads 8 w + 2 g16 + j (log2 units), with the head's power of two
   {
-    uint4 raw[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) raw[s] = reinterpret_cast<const uint4*>(qrow + d0)[s];
     float amax = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -233,22 +279,6 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     for (int j = 0; j < 2; ++j) qs[j] = qscale * ldexpf(1.0f, __shfl(e, 8 * w + 2 * g16 + j));
   }
 
-  const uint8_t* rows;
-  int nrows;
-  if (MODE == 0) {
-    rows = swa + (size_t)b * kSwa * kDKv;
-    nrows = min(max(row_swa_len, 0), kSwa);
-  } else {
-    const int64_t p = pos0 + b;
-    const int64_t lo = p - (kSwa - 1) > 0 ? p - (kSwa - 1) : 0;
-    rows = swa + (size_t)(lo - (pos0 - (kSwa - 1))) * kDKv;
-    nrows = (int)(p - lo + 1);
-  }
-  const int n_pos = k + nrows;
-  const int n_seg = (n_pos + kSeg - 1) / kSeg;
-  const int seg_end = min(seg_begin + segs_per_split, n_seg);
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(qrow);  // any valid 64 bytes
-
   // running softmax state: wave w, lane (position n16, g16) runs heads 8 w + 2 g16 + j
   // (j = 0, 1): the running max (the same in the head's 16 lanes) and this lane's share of
   // the sum (its position's terms, added over the lanes at the end).  Accumulators of this
@@ -281,24 +311,10 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     __syncthreads();
     const int n_i = stage1 - stage0;
 
+    // segment stage0 + i with its id from the stage's LDS copy (read whatever the kind)
     auto issue = [&](int i) {
-      Raw r;
       const int p = (stage0 + i) * kSeg + n16;
-      const int j = s_idx[min(max(p - idx_base, 0), kIdxStage - 1)];  // read whatever the kind
-      const int kind = (i < n_i && p < n_pos) ? (p < k ? (j >= 0 ? 1 : 0) : 2) : 0;
-      const int64_t e = base + (kind == 1 ? j : 0);
-      const uint8_t* am = kv_codes + e * kKvCodeBytes + d0 / 2;
-      const uint8_t* aw = rows + (size_t)(kind == 2 ? p - k : 0) * kDKv + d0;
-      const uint8_t* a = kind == 1 ? am : kind == 2 ? aw : dummy;
-      const uint8_t* a2 = kind == 2 ? aw + 32 : a;
-      const uint8_t* asc = kind == 1 ? kv_scale + e * kKvScaleBytes + d0 / 16 : a;
-      r.u[0] = reinterpret_cast<const uint4*>(a)[0];
-      r.u[1] = reinterpret_cast<const uint4*>(a)[1];
-      r.u[2] = reinterpret_cast<const uint4*>(a2)[0];
-      r.u[3] = reinterpret_cast<const uint4*>(a2)[1];
-      r.sc = *reinterpret_cast<const uint32_t*>(asc);
-      r.kind = kind;
-      return r;
+      return gather(stage0 + i, s_idx[min(max(p - idx_base, 0), kIdxStage - 1)], stage1);
     };
 
     auto compute = [&](Raw& r, int next) {
@@ -418,7 +434,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     };
 
     // the next segment's loads are in flight while one is computed
-    Raw r0 = issue(0);
+    if (stage0 != seg_begin) r0 = issue(0);
     for (int i = 0; i < n_i; ++i) compute(r0, i + 1);
   }
 
