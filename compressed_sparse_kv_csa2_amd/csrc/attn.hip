@@ -472,18 +472,25 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       P[2 * kHeads + (4 * g16 + r) * kDKv + kHalf * w + 16 * t + n16] = acc[t][r];
 }
 
-// Log-sum-exp merge of a decode row's splits for one head: 256 threads; thread t sums dims
-// 4 (t % 128) .. + 3 over the splits of parity t / 128, with every load issued before the
-// first is used, and the two parities meet in LDS.  The first wave turns each split's
-// (max, sum) into its weight meanwhile (two wave reductions).
+// Log-sum-exp merge of a decode row's splits for one quarter of one head's dims: 256
+// threads; thread t sums dims 4 (t % 32) .. + 3 of the quarter over the splits
+// t / 32, t / 32 + 8, .. with every load issued before the first is used, and the eight
+// split groups meet in LDS.  The first wave turns each split's (max, sum) into its weight
+// meanwhile (two wave reductions).
 constexpr int kMergeThreads = 256;
+constexpr int kMergeQuarters = 4;                                       // blocks per head
+constexpr int kMergeDims = kDKv / kMergeQuarters;                       // 128
+constexpr int kMergeLanes = kMergeDims / 4;                             // 32 float4 lanes
+constexpr int kMergeGroups = kMergeThreads / kMergeLanes;               // 8 split groups
+constexpr int kMergePer = (kMaxSplits + kMergeGroups - 1) / kMergeGroups;  // 8 loads
 __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __restrict__ part,
                                                               int n_splits, float* __restrict__ out) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_L;
-  __shared__ float4 s_o[kMergeThreads / 2];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  const int par = tid >> 7, d = 4 * (tid & 127);
+  __shared__ float4 s_o[kMergeGroups][kMergeLanes];
+  const int h = blockIdx.x / kMergeQuarters, quarter = blockIdx.x % kMergeQuarters;
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int grp = tid / kMergeLanes, d = quarter * kMergeDims + 4 * (tid % kMergeLanes);
   const float* P0 = part + (size_t)b * n_splits * kPart;
   // each split's (max, sum) first: loads return in order, so the weights can be computed
   // while the accumulators are still on their way
@@ -492,10 +499,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __res
     ms = P0[(size_t)lane * kPart + h];
     ls = P0[(size_t)lane * kPart + kHeads + h];
   }
-  float4 a[kMaxSplits / 2];
+  float4 a[kMergePer];
 #pragma unroll
-  for (int i = 0; i < kMaxSplits / 2; ++i) {
-    const int sp = 2 * i + par;
+  for (int i = 0; i < kMergePer; ++i) {
+    const int sp = grp + kMergeGroups * i;
     a[i] = sp < n_splits ? *reinterpret_cast<const float4*>(P0 + (size_t)sp * kPart + 2 * kHeads + h * kDKv + d)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -513,8 +520,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __res
   __syncthreads();
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int i = 0; i < kMaxSplits / 2; ++i) {
-    const int sp = 2 * i + par;
+  for (int i = 0; i < kMergePer; ++i) {
+    const int sp = grp + kMergeGroups * i;
     if (sp < n_splits) {
       const float wgt = s_w[sp];
       o.x = fmaf(a[i].x, wgt, o.x);
@@ -523,14 +530,22 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __res
       o.w = fmaf(a[i].w, wgt, o.w);
     }
   }
-  if (par == 1) s_o[tid & 127] = o;
+  s_o[grp][tid % kMergeLanes] = o;
   __syncthreads();
-  if (par == 0) {
-    const float4 o1 = s_o[tid];
+  if (tid < kMergeLanes) {
+    float4 t = s_o[0][tid];
+#pragma unroll
+    for (int g = 1; g < kMergeGroups; ++g) {
+      const float4 u = s_o[g][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
     const float L = s_L;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     *reinterpret_cast<float4*>(&out[((size_t)b * kHeads + h) * kDKv + d]) =
-        make_float4((o.x + o1.x) * inv, (o.y + o1.y) * inv, (o.z + o1.z) * inv, (o.w + o1.w) * inv);
+        make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
   }
 }
 
@@ -557,8 +572,8 @@ hipError_t launch_attn(int mode, const uint16_t* q, const uint8_t* kv_codes, con
     hipLaunchKernelGGL(k_attn<0>, dim3(used, rows), dim3(kAThreads), 0, stream, q, kv_codes,
                        kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, part, sps, used);
   if (used > 1)
-    hipLaunchKernelGGL(k_attn_merge, dim3(kHeads, rows), dim3(kMergeThreads), 0, stream, part, used,
-                       out);
+    hipLaunchKernelGGL(k_attn_merge, dim3(kHeads * kMergeQuarters, rows), dim3(kMergeThreads), 0,
+                       stream, part, used, out);
   return hipGetLastError();
 }
 
