@@ -61,19 +61,27 @@ constexpr int kSeg = 16;                     // list positions per wave step
 constexpr int kIdxStage = 1024;              // list positions whose entry ids sit in LDS
 constexpr int kMaxSplits = 64;               // splits per decode row
 constexpr int kSplitSlots = 1024;            // decode workgroups aimed for (4 per CU)
+constexpr int kSplitCUs = 256;               // compute units (one split each for few rows)
+constexpr int kCuSplitMaxSegs = 5;           // longest split the one-per-CU rule may take
 constexpr int kPart = 2 * kHeads + kHeads * kDKv;  // floats per split: m[16], l[16], acc
 constexpr float kRescale = 8.0f;             // log2 headroom before the running max moves
 
 int attn_segments(int k) { return (k + kSwa + kSeg - 1) / kSeg; }
 int attn_splits(int k) { return min(attn_segments(k), kMaxSplits); }
 
-// Decode segments per split.  Each extra segment in a split adds about one gather latency
-// (~1.6 us: the next segment's loads are issued one segment ahead), while each split's
-// partial (16 x 512 fp32) is written and read back once (~0.5 us of the device's
-// bandwidth per 40 splits and row); the sum is smallest near sqrt(rows x segments / 123)
-// segments per split (1 for 4 rows of 640 positions, 2 for 16, 3 for 32).
+// Decode segments per split.  Few rows: the fewest segments (at most kCuSplitMaxSegs) that
+// put every row's splits on their own compute unit (measured at 640 positions per row: 1
+// segment for 4 rows, 3 for 16, 5 for 32; the split rule below gave 2 and 3, and c3's 20
+// attentions at 16 rows took 338 instead of 297 us).  Otherwise each extra segment in a
+// split adds about one gather latency, while each split's partial (16 x 512 fp32) is
+// written and read back once; the sum is smallest near sqrt(rows x segments / 123)
+// segments per split (6 for 128 rows, measured against 9 and 13).
 static int attn_segs_per_split(int rows, int k) {
   const int segs = attn_segments(k);
+  for (int s = 1; s <= min(kCuSplitMaxSegs, segs); ++s) {
+    const int splits = (segs + s - 1) / s;
+    if (splits <= kMaxSplits && (long long)rows * splits <= kSplitCUs) return s;
+  }
   int sps = max(1, (int)lround(sqrt((double)rows * segs / 123.0)));
   sps = max(sps, (int)(((long long)rows * segs + kSplitSlots - 1) / kSplitSlots));
   sps = max(sps, (segs + kMaxSplits - 1) / kMaxSplits);
