@@ -55,6 +55,30 @@ def test_workspace_sizes(lib):
     assert lib.csa2_prefill_workspace_size(0, 131072, 512) == 0
 
 
+def test_attention_split_counts(lib):
+    # the attention workspace holds one partial (max[16], sum[16], acc[16][512] in fp32) per
+    # split and row, so its size gives the split count the launch uses: few rows get the
+    # fewest segments per split that leave every split its own compute unit, many rows the
+    # square-root rule, and no row is ever cut into more than 64 splits
+    part = (2 * 16 + 16 * 512) * 4
+
+    def splits(rows, k):
+        size = lib.csa2_attn_workspace_size(rows, k)
+        if size == 256:
+            return 1
+        assert size % 256 == 0 and size >= rows * part
+        return size // (rows * part)
+
+    assert [splits(r, 512) for r in (1, 4, 8, 16, 32, 128, 4096)] == [40, 40, 20, 14, 8, 7, 1]
+    for rows in (1, 3, 4, 7, 13, 16, 33, 64, 128, 1000):
+        for k in (0, 16, 100, 512, 2048, 16384):
+            n = splits(rows, k)
+            segs = (k + 128 + 15) // 16
+            assert 1 <= n <= min(64, segs)
+            if rows * segs <= 256 and segs <= 64:
+                assert n == segs  # one segment per split when every split gets a unit
+
+
 FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
 ODD = ctypes.c_void_p((1 << 20) + 2)   # misaligned
 
