@@ -25,19 +25,22 @@
 // 16-position segments of the row's list (the k selected entries, then the window rows);
 // wave w owns dims 256 w .. 256 w + 255 of every segment:
 //   gather   lane (position n, dim group g) loads dims 256 w + 64 g .. + 63 of position n
-//            (32 code bytes + 4 scale bytes, or 64 window bytes), one segment ahead;
+//            (32 code bytes + 4 scale bytes, or 64 window bytes); the next segment's
+//            loads are issued as soon as this one's bytes are dequantised, into the same
+//            registers, and a split's first segment before the query's prologue;
 //   q . v    8 k-steps; k-step s of dim group g covers dims 256 w + 64 g + 8 s .. + 7, so
 //            each lane dequantises exactly its own loaded bytes into the B operand; the two
 //            waves' partial scores meet in LDS and are added in the same order by both;
-//   softmax  per head over the segment's 16 positions (DPP row reductions), computed by
-//            both waves alike; the running max moves only when a score exceeds it by more
-//            than 2^8, so rescaling the accumulators is rare;
+//   softmax  per head over the segment's 16 positions, computed by both waves alike; the
+//            running max moves only when a score exceeds it by more than 2^8, so one
+//            ballot per segment usually shows that neither the segment's maximum (DPP row
+//            reductions) nor a rescale of the accumulators is needed;
 //   p . v    the dequantised half-segment is also written to the wave's LDS tile (positions
 //            x dims, XOR-swizzled) and read back transposed with ds_read_b64_tr_b16 as the
 //            B operand of 16 output tiles of 16 dims; p (hi from wave 0, lo from wave 1)
 //            goes through LDS the same way.  Two workgroup barriers per segment.
-// A decode row with several splits leaves (max, sum, acc[16][512]) per split in the
-// workspace and k_attn_merge combines them by log-sum-exp.  exp2 with log2(e) folded into
+// A row with several splits leaves (max, sum, acc[16][512]) per split in the workspace and
+// k_attn_merge combines them by log-sum-exp.  exp2 with log2(e) folded into
 // the scale.
 #include "csa2_device.h"
 #include "csa2_internal.h"
