@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       // the raw bytes are dead: the next segment's loads go into the same registers and
       // stay in flight through the softmax and p . v (no second register set to copy from)
       const bool valid = r.kind != 0;
-      r = issue(next);
+      if (next < n_i) r = issue(next);  // wave-uniform: nothing to load after the stage's last
       // ---- the two halves' scores, added in the same order in both waves
       s_z[w][lane] = z;
       __syncthreads();
