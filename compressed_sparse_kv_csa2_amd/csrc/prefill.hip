@@ -534,6 +534,51 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_theta(int n_entries, in
   if (tid == 0) ws.theta[t] = key_score(prefix << 16);
 }
 
+// The same threshold for rows of at most kThetaWaveMax group maxima (the sampled pass's
+// 1,024 per row): one wave per row, 16 maxima per lane in registers.  The kq-th largest
+// 16-bit key is found bit by bit from the top, as the largest value that at least kq
+// maxima reach; each count is one ballot and popcount per register, so the wave needs no
+// LDS, atomics or barriers.  Rows and special cases as in k_prefill_theta.
+constexpr int kThetaWaveMax = 1024;
+constexpr int kThetaRowsPerBlock = 4;
+__global__ __launch_bounds__(64 * kThetaRowsPerBlock) void k_prefill_theta_wave(
+    int n_entries, int ratio, int64_t pos0, int T, int k, int kq, PrefillWs ws) {
+  const int t = blockIdx.x * kThetaRowsPerBlock + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;  // wave-uniform
+  if (visible(pos0 + t, ratio, n_entries) <= k) {  // the select takes every visible entry
+    if (lane == 0) ws.theta[t] = __builtin_inff();
+    return;
+  }
+  const uint4* g4 = reinterpret_cast<const uint4*>(ws.gmax + (size_t)t * ws.G);
+  const int nch = ws.G_used / 8;  // 16-byte chunks of 8 maxima, at most 128
+  const uint4 c0 = lane < nch ? g4[lane] : make_uint4(0u, 0u, 0u, 0u);
+  const uint4 c1 = lane + 64 < nch ? g4[lane + 64] : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  uint32_t v[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = w[i] & 0xffffu;
+    v[2 * i + 1] = w[i] >> 16;
+  }
+  auto count_ge = [&](uint32_t c) {  // maxima of the row >= c (c >= 1 leaves out empty groups)
+    uint32_t n = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) n += (uint32_t)__popcll(__ballot(v[i] >= c));
+    return n;
+  };
+  if (count_ge(1u) < (uint32_t)kq) {  // fewer than kq non-empty groups
+    if (lane == 0) ws.theta[t] = -__builtin_inff();
+    return;
+  }
+  uint32_t th = 0;
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = th | (1u << b);
+    if (count_ge(c) >= (uint32_t)kq) th = c;
+  }
+  if (lane == 0) ws.theta[t] = key_score(th << 16);
+}
+
 // Score of entry j for a query held as 64 bf16 pairs (fp32, same rounding class as the
 // MFMA path: exact products, fp32 sums).
 __device__ __forceinline__ float score_row(const bf16x2 (&qq)[64], const uint8_t* codes, const float* scale,
@@ -783,8 +828,13 @@ hipError_t launch_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes
                        dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
                        pos0, T, ws);
   }
-  hipLaunchKernelGGL(k_prefill_theta, dim3(T), dim3(kSelThreads), 0, stream, n_entries, ratio, pos0, T,
-                     k, sampled ? kq : k, ws);
+  if (ws.G_used <= kThetaWaveMax)
+    hipLaunchKernelGGL(k_prefill_theta_wave, dim3((T + kThetaRowsPerBlock - 1) / kThetaRowsPerBlock),
+                       dim3(64 * kThetaRowsPerBlock), 0, stream, n_entries, ratio, pos0, T, k,
+                       sampled ? kq : k, ws);
+  else
+    hipLaunchKernelGGL(k_prefill_theta, dim3(T), dim3(kSelThreads), 0, stream, n_entries, ratio, pos0,
+                       T, k, sampled ? kq : k, ws);
   if (n_entries > 0) {
     hipLaunchKernelGGL((k_prefill_gemm<2, 1, kSplitEntries>), dim3(row_blocks, ws.n_splits),
                        dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
