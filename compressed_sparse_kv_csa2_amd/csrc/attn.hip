@@ -483,19 +483,22 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       P[2 * kHeads + (4 * g16 + r) * kDKv + kHalf * w + 16 * t + n16] = acc[t][r];
 }
 
-// Log-sum-exp merge of a decode row's splits for one quarter of one head's dims: 256
-// threads; thread t sums dims 4 (t % 32) .. + 3 of the quarter over the splits
-// t / 32, t / 32 + 8, .. with every load issued before the first is used, and the eight
-// split groups meet in LDS.  The first wave turns each split's (max, sum) into its weight
-// meanwhile (two wave reductions).
+// Log-sum-exp merge of a row's splits for one of QB equal blocks of one head's dims: 256
+// threads; each sums 4 dims of the block over one group of splits (the groups interleave),
+// with every load issued before the first is used, and the split groups meet in LDS.  The
+// first wave turns each split's (max, sum) into its weight meanwhile (two wave
+// reductions).  Quarters (8 split groups) up to kMergeManyRows rows, halves beyond
+// (measured for 128 rows: 720 against 732 us for the replay's layers; whole heads 753).
 constexpr int kMergeThreads = 256;
-constexpr int kMergeQuarters = 4;                                       // blocks per head
-constexpr int kMergeDims = kDKv / kMergeQuarters;                       // 128
-constexpr int kMergeLanes = kMergeDims / 4;                             // 32 float4 lanes
-constexpr int kMergeGroups = kMergeThreads / kMergeLanes;               // 8 split groups
-constexpr int kMergePer = (kMaxSplits + kMergeGroups - 1) / kMergeGroups;  // 8 loads
+constexpr int kMergeManyRows = 32;  // rows above which a head's dims are merged in fewer blocks
+template <int QB>
 __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(const float* __restrict__ part,
                                                               int n_splits, float* __restrict__ out) {
+  constexpr int kMergeQuarters = QB;                                      // blocks per head
+  constexpr int kMergeDims = kDKv / kMergeQuarters;
+  constexpr int kMergeLanes = kMergeDims / 4;                             // float4 lanes
+  constexpr int kMergeGroups = kMergeThreads / kMergeLanes;               // split groups
+  constexpr int kMergePer = (kMaxSplits + kMergeGroups - 1) / kMergeGroups;
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_L;
   __shared__ float4 s_o[kMergeGroups][kMergeLanes];
@@ -582,9 +585,12 @@ hipError_t launch_attn(int mode, const uint16_t* q, const uint8_t* kv_codes, con
   else
     hipLaunchKernelGGL(k_attn<0>, dim3(used, rows), dim3(kAThreads), 0, stream, q, kv_codes,
                        kv_scale, seq_base, idx, k, swa, swa_len, pos0, qscale, out, part, sps, used);
-  if (used > 1)
-    hipLaunchKernelGGL(k_attn_merge, dim3(kHeads * kMergeQuarters, rows), dim3(kMergeThreads), 0,
-                       stream, part, used, out);
+  if (used > 1 && rows > kMergeManyRows)
+    hipLaunchKernelGGL(k_attn_merge<2>, dim3(kHeads * 2, rows), dim3(kMergeThreads), 0, stream,
+                       part, used, out);
+  else if (used > 1)
+    hipLaunchKernelGGL(k_attn_merge<4>, dim3(kHeads * 4, rows), dim3(kMergeThreads), 0, stream, part,
+                       used, out);
   return hipGetLastError();
 }
 
