@@ -77,15 +77,16 @@ int attn_splits(int k) { return min(attn_segments(k), kMaxSplits); }
 // segment for 4 rows, 3 for 16, 5 for 32; the split rule below gave 2 and 3, and c3's 20
 // attentions at 16 rows took 338 instead of 297 us).  Otherwise each extra segment in a
 // split adds about one gather latency, while each split's partial (16 x 512 fp32) is
-// written and read back once; the sum is smallest near sqrt(rows x segments / 123)
-// segments per split (6 for 128 rows, measured against 9 and 13).
+// written and read back once; the sum is smallest near sqrt(rows x segments / 200)
+// segments per split (5 for 128 rows of 640 positions, i.e. 8 equal splits: 704 us for the
+// replay's layers against 716 at 6, 706 at 7 and more at 9 and 13).
 static int attn_segs_per_split(int rows, int k) {
   const int segs = attn_segments(k);
   for (int s = 1; s <= min(kCuSplitMaxSegs, segs); ++s) {
     const int splits = (segs + s - 1) / s;
     if (splits <= kMaxSplits && (long long)rows * splits <= kSplitCUs) return s;
   }
-  int sps = max(1, (int)lround(sqrt((double)rows * segs / 123.0)));
+  int sps = max(1, (int)lround(sqrt((double)rows * segs / 200.0)));
   sps = max(sps, (int)(((long long)rows * segs + kSplitSlots - 1) / kSplitSlots));
   sps = max(sps, (segs + kMaxSplits - 1) / kMaxSplits);
   return min(sps, segs);
