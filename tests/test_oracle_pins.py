@@ -333,3 +333,170 @@ def test_decoder_chain_shares_lists():
             assert set(res[l][0]) <= set(pool)
     # Reuse layers differ only through their own query and window
     assert not np.allclose(res[21][1], res[22][1])
+
+
+# --------------------------------------------------------------------------- compositions
+# Constructed inputs whose selections and outputs are known by construction, so the
+# compositions decode_step_long and decoder_chain are pinned to closed forms, not to the
+# oracle's own component functions.  Indexer entry j carries its Full-query score in
+# dimension 0 and a Reindex score per Reindex layer in dimensions 1..4; a query that is
+# one-hot on dimension d therefore scores entry j as scale_j * e2m1(code_jd).  Main entry
+# j is the constant vector v_j * ones(512) (all codes equal, every E4M3 scale 1.0), and
+# window row t of layer l is the constant w_l * ones(512).  With q_h = a * ones(512) a
+# head's logits are a * sqrt(512) * (entry value), so each output row is the constant
+# softmax-weighted mean of the attended values: a one-dimensional closed form.
+_E2M1_CODE = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+_E4M3_ONE = 0x38       # 1.0 in E4M3 (exponent 7, mantissa 0)
+_E4M3_CODE = {0.5: 0x30, 1.0: 0x38, 2.0: 0x40, 3.0: 0x44, 4.0: 0x48}
+
+
+def _bf16_bits(x):
+    b = np.asarray(x, dtype=np.float32).view(np.uint32) >> 16
+    assert np.array_equal((b << 16).view(np.float32), np.asarray(x, dtype=np.float32))
+    return b.astype(np.uint16)
+
+
+def _onehot_query(d):
+    v = np.zeros(128, dtype=np.float32)
+    v[d] = 1.0
+    return _bf16_bits(v)
+
+
+def _const_query(a):
+    return _bf16_bits(np.full((16, 512), a, dtype=np.float32))
+
+
+def _pack_index_entries(dims):
+    """dims: [n][5] E2M1 values of dimensions 0..4 (the rest 0) -> codes u8 [n][64]."""
+    n = len(dims)
+    nib = np.zeros((n, 128), dtype=np.uint8)
+    for j, row in enumerate(dims):
+        for d, v in enumerate(row):
+            nib[j, d] = _E2M1_CODE[float(v)]
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _pack_main_entries(vals):
+    """vals[j]: E2M1 value of every one of entry j's 512 elements (scale 1.0)."""
+    n = len(vals)
+    codes = np.zeros((n, 256), dtype=np.uint8)
+    for j, v in enumerate(vals):
+        c = _E2M1_CODE[float(v)]
+        codes[j, :] = c | (c << 4)
+    return codes, np.full((n, 32), _E4M3_ONE, dtype=np.uint8)
+
+
+def _weighted_mean(values, a):
+    """Closed form of one output element when every attended row is c * ones(512)."""
+    v = np.asarray(values, dtype=np.float64)
+    z = a * math.sqrt(512.0) * v  # (q . v) / sqrt(512) with q = a * ones
+    w = np.exp(z - z.max())
+    return float((w * v).sum() / w.sum())
+
+
+def _chain_fixture(n_before=9, n=40, n_after=7, pool=12, k=3):
+    """A sequence of n entries at seq_base = n_before inside a buffer with n_before entries
+    in front and n_after behind (all of which score highest for every query: a wrong slice
+    selects them).  Construction, by the entry's local index j:
+      Full score  (dim 0):  pool members P = {2, 5, ..., 35} (12 entries, every third from 2)
+                            score 4 or 6; the Full layer's own top-k F = {5, 20, 35} score
+                            6 * scale, the rest of P 4 * scale; everything else 0.5 * scale.
+      Reindex score of layer r (dim 1 + r): inside P the layer's own set R_r (3 entries,
+                            disjoint from F and from the other layers' sets) scores 6, the
+                            rest of P 1; OUTSIDE P every entry scores 6 * 2 (scale 2), so a
+                            Reindex that searched beyond the pool picks them instead.
+    Main values: F entries 2.0, R_r entries 3.0 + r (as E2M1: 3, 4, 6, 6), others 0.5."""
+    P = list(range(2, 2 + 3 * pool, 3))
+    F = [5, 20, 35]
+    R = [[2, 8, 11], [14, 17, 23], [26, 29, 32]]
+    dims, scale, main = [], [], []
+    total = n_before + n + n_after
+    for g in range(total):
+        j = g - n_before
+        if j < 0 or j >= n:          # outside the sequence: top score for every query
+            dims.append([6.0] * 5)
+            scale.append(4.0)
+            main.append(0.5)
+            continue
+        row = [0.5, 1.0, 1.0, 1.0, 1.0]
+        sc = 1.0
+        if j in P:
+            row[0] = 6.0 if j in F else 4.0
+            for r, Rr in enumerate(R):
+                row[1 + r] = 6.0 if j in Rr else 1.0
+        else:
+            sc = 2.0                  # off-pool entries: Reindex score 12 > 6 (and Full 1.0)
+            row = [0.5, 6.0, 6.0, 6.0, 6.0]
+        dims.append(row)
+        scale.append(sc)
+        main.append(2.0 if j in F else next((3.0 + r if r < 2 else 6.0 for r, Rr in enumerate(R)
+                                             if j in Rr), 0.5))
+    codes = _pack_index_entries(dims)
+    kvc, kvs = _pack_main_entries(main)
+    fx = dict(codes=codes, scale=np.asarray(scale, np.float32), kvc=kvc, kvs=kvs,
+              base=n_before, n=n, P=P, F=F, R=R, pool=pool, k=k,
+              value=lambda j: main[n_before + j])
+    # with these scales the Full scores of P are 6 or 4 (x1), off-pool 0.5 x 2 = 1: P is the
+    # top-12; off-pool Reindex scores 6 x 2 = 12 beat every pool entry's 6 or 1
+    return fx
+
+
+def _swa_const(w, length=128):
+    return np.full((length, 512), _E4M3_CODE[w], dtype=np.uint8)
+
+
+def test_decode_step_long_constructed():
+    fx = _chain_fixture()
+    a = 2.0 ** -5
+    swa_len = 5
+    pool, idx, out = oracle.decode_step_long(
+        _onehot_query(0), _onehot_query(2), _const_query(a), fx["codes"], fx["scale"], fx["kvc"],
+        fx["kvs"], fx["base"], fx["n"], _swa_const(0.5), swa_len, pool_size=fx["pool"],
+        k=fx["k"])
+    assert list(pool) == fx["P"]                    # local ids of the pool, ascending
+    assert list(idx) == fx["R"][1]                  # Reindex layer 1's set, inside the pool
+    want = _weighted_mean([fx["value"](j) for j in fx["R"][1]] + [0.5] * swa_len, a)
+    np.testing.assert_allclose(out, np.full((16, 512), want), rtol=1e-12)
+    # the window rows beyond swa_len are never attended
+    _, _, out2 = oracle.decode_step_long(
+        _onehot_query(0), _onehot_query(2), _const_query(a), fx["codes"], fx["scale"], fx["kvc"],
+        fx["kvs"], fx["base"], fx["n"], np.concatenate([_swa_const(0.5, swa_len),
+                                                        _swa_const(4.0, 128 - swa_len)]),
+        swa_len, pool_size=fx["pool"], k=fx["k"])
+    np.testing.assert_array_equal(out2, out)
+
+
+def test_decoder_chain_constructed():
+    fx = _chain_fixture()
+    layers = range(20, 32)          # Full 20, Reuse 21-23, Reindex 24, Reuse 25-27, Reindex 28 ...
+    # the Full layer uses dim 0; Reindex layers 24, 28 use dims 1, 2 (sets R[0], R[1])
+    qi = {l: _onehot_query(0) for l in layers}
+    qi[24], qi[28] = _onehot_query(1), _onehot_query(2)
+    wvals = [0.5, 1.0, 2.0, 3.0, 4.0]
+    a_of = {l: 2.0 ** -(4 + (l % 3)) for l in layers}
+    w_of = {l: wvals[l % 5] for l in layers}
+    q = {l: _const_query(a_of[l]) for l in layers}
+    sw = {l: _swa_const(w_of[l]) for l in layers}
+    swa_len = 7
+    res, pool = oracle.decoder_chain(qi, q, sw, swa_len, fx["codes"], fx["scale"], fx["kvc"],
+                                     fx["kvs"], fx["base"], fx["n"], pool_size=fx["pool"],
+                                     k=fx["k"], first=20, last=31)
+    assert list(pool) == fx["P"]
+    want_list = {}
+    for l in layers:
+        want_list[l] = fx["F"] if l < 24 else fx["R"][0] if l < 28 else fx["R"][1]
+        assert list(res[l][0]) == want_list[l], l
+        want = _weighted_mean([fx["value"](j) for j in want_list[l]] + [w_of[l]] * swa_len, a_of[l])
+        np.testing.assert_allclose(res[l][1], np.full((16, 512), want), rtol=1e-12, err_msg=str(l))
+    # swapping two layers' queries and windows swaps their outputs (and nothing else moves)
+    q2, sw2 = dict(q), dict(sw)
+    q2[21], q2[26] = q[26], q[21]
+    sw2[21], sw2[26] = sw[26], sw[21]
+    res2, _ = oracle.decoder_chain(qi, q2, sw2, swa_len, fx["codes"], fx["scale"], fx["kvc"],
+                                   fx["kvs"], fx["base"], fx["n"], pool_size=fx["pool"], k=fx["k"],
+                                   first=20, last=31)
+    got21 = _weighted_mean([fx["value"](j) for j in want_list[21]] + [w_of[26]] * swa_len, a_of[26])
+    np.testing.assert_allclose(res2[21][1], np.full((16, 512), got21), rtol=1e-12)
+    for l in layers:
+        if l not in (21, 26):
+            np.testing.assert_array_equal(res2[l][1], res[l][1])
