@@ -22,6 +22,7 @@ __all__ = [
     "csa2_index_topk_workspace_size", "csa2_select_chain_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
     "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
     "csa2_prefill_select", "csa2_sparse_attn_prefill", "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
+    "csa2_workspace_status", "workspace_status", "check_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,7 @@ _SIGS = {
     "csa2_select_chain_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "csa2_select_chain": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
                                          _I32, _P, _P, _P, _SZ, _P]),
+    "csa2_workspace_status": (ctypes.c_int, [_P, _P, _P]),
     "csa2_attn_workspace_size": (_SZ, [_I32, _I32]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _F32, _I32, _P, _P,
                                                _SZ, _P]),
@@ -157,6 +159,31 @@ def index_topk_workspace(batch, n_cols, k, device="cuda"):
 def select_chain_workspace(batch, n_cols, pool_k, device="cuda"):
     """Zero-filled workspace for csa2_select_chain (its first int32 is the status word)."""
     return _zeros(csa2_select_chain_workspace_size(batch, n_cols, pool_k), device)
+
+
+def csa2_workspace_status(workspace, stream=None):
+    """(error bits, rows re-scanned) from the status block of a csa2_index_topk /
+    csa2_select_chain workspace; synchronizes the stream."""
+    _need(workspace, "workspace", _U8)
+    out = (ctypes.c_uint32 * 2)()
+    _check(load_library().csa2_workspace_status(_ptr(workspace), ctypes.cast(out, ctypes.c_void_p),
+                                                _stream(stream)))
+    return int(out[0]), int(out[1])
+
+
+def workspace_status(workspace, stream=None) -> int:
+    """The sticky error bits of a selection workspace (0 after correct calls)."""
+    return csa2_workspace_status(workspace, stream)[0]
+
+
+def check_workspace(workspace, stream=None):
+    """Raises Csa2Error when a selection workspace reports an error; the workspace is then
+    zero-filled so that it can serve the next call (that call's results were undefined)."""
+    bits = workspace_status(workspace, stream)
+    if bits:
+        workspace.zero_()
+        raise Csa2Error(f"selection workspace reports error bits {bits:#x}: results of the calls "
+                        "since the last check are undefined (workspace re-zeroed)")
 
 
 def attn_workspace(batch, k, device="cuda"):

@@ -138,6 +138,19 @@ int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const fl
                                       static_cast<hipStream_t>(stream)));
 }
 
+int csa2_workspace_status(const void* workspace, uint32_t* out, void* stream) {
+  if (!workspace || !out) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+  uint32_t w[3] = {0, 0, 0};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(w, workspace, sizeof(w), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return CSA2_ERR_HIP;
+  out[0] = w[0];
+  out[1] = w[2];
+  return CSA2_OK;
+}
+
 size_t csa2_attn_workspace_size(int32_t batch, int32_t k) {
   if (batch < 1 || k < 0) return 0;
   return attn_ws_bytes(batch, k);

@@ -64,7 +64,6 @@ constexpr int kSeg = 16;                     // list positions per wave step
 constexpr int kIdxStage = 1024;              // list positions whose entry ids sit in LDS
 constexpr int kMaxSplits = 64;               // splits per decode row
 constexpr int kSplitSlots = 1024;            // decode workgroups aimed for (4 per CU)
-constexpr int kSplitCUs = 256;               // compute units (one split each for few rows)
 constexpr int kCuSplitMaxSegs = 5;           // longest split the one-per-CU rule may take
 constexpr int kPart = 2 * kHeads + kHeads * kDKv;  // floats per split: m[16], l[16], acc
 constexpr float kRescale = 8.0f;             // log2 headroom before the running max moves
@@ -80,11 +79,22 @@ int attn_splits(int k) { return min(attn_segments(k), kMaxSplits); }
 // written and read back once; the sum is smallest near sqrt(rows x segments / 200)
 // segments per split (5 for 128 rows of 640 positions, i.e. 8 equal splits: 704 us for the
 // replay's layers against 716 at 6, 706 at 7 and more at 9 and 13).
+// Compute units of the current device (one split each for few rows); 256, an MI355X's
+// count, when no device answers (workspace sizing on a host without one).
+static int attn_cus() {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+    return 256;
+  return n_cu;
+}
+
 static int attn_segs_per_split(int rows, int k) {
   const int segs = attn_segments(k);
+  const int n_cu = attn_cus();
   for (int s = 1; s <= min(kCuSplitMaxSegs, segs); ++s) {
     const int splits = (segs + s - 1) / s;
-    if (splits <= kMaxSplits && (long long)rows * splits <= kSplitCUs) return s;
+    if (splits <= kMaxSplits && (long long)rows * splits <= n_cu) return s;
   }
   int sps = max(1, (int)lround(sqrt((double)rows * segs / 200.0)));
   sps = max(sps, (int)(((long long)rows * segs + kSplitSlots - 1) / kSplitSlots));

@@ -1,6 +1,7 @@
 // Host-side launchers shared between the C-ABI front end (api.hip) and the kernel files.
 #pragma once
 #include <hip/hip_runtime.h>
+#include "csa2.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -29,13 +30,18 @@ struct TopkWs {
   int n_chunks;
 };
 
-// ---- fused scan + top-k (index_topk.hip) ----
-constexpr int kHist3Bins = 512;       // level-3 digit: key bits 8..0
-constexpr int kFuseMaxWg = 256;       // workgroups per row (one per CU at most)
-constexpr int kPubSlots = 2048;       // published composites per row and selection
-constexpr int kMaxSel = 6;            // selections per row: scan, own top-k, 4 Reindex
-constexpr int kMaxReindex = kMaxSel - 2;
-constexpr int kSyncStride = 32;       // u32 per row of barrier counters (one 128-byte line)
+// ---- scan + top-k in one launch (fsel.hip) and its dispatch (index_topk.hip) ----
+constexpr int kMaxReindex = CSA2_MAX_REINDEX;  // Reindex layers one chained call re-scores
+
+// Rows the single-launch filtered selection handles (longer rows: index_score + topk).
+bool fsel_fits(int n_cols);
+size_t fsel_ws_bytes(int batch, int n_cols, bool chain);
+hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* scale,
+                       const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
+                       int batch, int n_cols, int k, int32_t* out, float* sout, int own_k,
+                       int32_t* own_out, const uint16_t* q_re, int n_re, int re_k,
+                       int32_t* re_out, float* re_sout, bool chain_ws, void* ws,
+                       hipStream_t stream);
 
 size_t index_topk_ws_bytes(int batch, int n_cols);
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint8_t* codes, const float* scale,

@@ -34,8 +34,9 @@
  *
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers unless stated; the caller owns every buffer.  The
- *    library allocates nothing, keeps no mutable global state and is re-entrant, except
- *    that calls sharing one workspace must not overlap in time.
+ *    library allocates nothing and is re-entrant, except that calls sharing one workspace
+ *    must not overlap in time.  Its only global state is a per-device cache of immutable
+ *    device facts (compute units and kernel occupancy), filled on first use.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
  *    asynchronous; kernel faults surface at the caller's next synchronisation.
  *  - Arguments are validated on the host BEFORE anything is enqueued; on error nothing is
@@ -160,12 +161,15 @@ size_t csa2_index_topk_workspace_size(int32_t batch, int32_t n_cols, int32_t k);
  *   idx_out    i32 [batch][k]  (out)          as for csa2_topk
  *   score_out  f32 [batch][k] or NULL (out)   as for csa2_topk
  *   workspace  device, 256-byte aligned, csa2_index_topk_workspace_size bytes, zero-filled
- *              before its first use; each call leaves it ready for the next one.  Its
- *              first 4 bytes are a sticky status word that stays 0 unless a row barrier of
- *              the single-launch kernel gave up waiting (results of that call undefined).
- *              Calls sharing one workspace must not run concurrently.
- * A row whose workgroups all fit on the device at once is scored and selected in one
- * cooperative launch; longer rows run csa2_index_score's and csa2_topk's kernels.
+ *              before its first use; each call leaves it ready for the next call of the
+ *              same shape.  It starts with a status block (csa2_workspace_status).  Calls
+ *              sharing one workspace must not run concurrently.
+ * Rows of up to 3,932,160 columns run as two launches: a filtered scan (any number of
+ * workgroups, no co-residency needed: workgroups claim chunks of columns from a counter
+ * and keep only keys at or above a threshold estimated from a sample of the row) and one
+ * selecting workgroup per row.  The result never depends on the estimate; a row whose
+ * estimate was too high is scanned again by its selecting workgroup (slower, counted in
+ * the status block).  Longer rows run csa2_index_score's and csa2_topk's kernels.
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_cols > 2^26), HIP.
  */
 int csa2_index_topk(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
@@ -196,11 +200,12 @@ size_t csa2_select_chain_workspace_size(int32_t batch, int32_t n_cols, int32_t p
  *   re_out         i32 [n_re][batch][k] (out)  = csa2_index_topk(q_re[r], cand = pool,
  *                  n_valid = pool entries, k) for each layer r
  *   re_score_out   f32 [n_re][batch][k] or NULL (out), their scores
- *   workspace      as csa2_index_topk (zero-filled before first use, left ready; first
- *                  4 bytes: sticky status word)
- * Outputs are bit-identical to the separate calls named above.  When one row's
- * workgroups fit the device at once, everything runs in one launch; otherwise the
- * separate calls run.
+ *   workspace      as csa2_index_topk (zero-filled before first use, left ready; starts
+ *                  with the status block)
+ * Outputs are bit-identical to the separate calls named above.  Rows of up to 3,932,160
+ * columns run the two launches of csa2_index_topk, the Reindex re-scores computed for
+ * the scan's candidates as they are written and every selection made by the row's
+ * selecting workgroup; longer rows run the separate calls.
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_cols > 2^26), HIP.
  */
 int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const float* idx_scale,
@@ -209,6 +214,22 @@ int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const fl
                       int32_t k, int32_t* own_out, const uint16_t* q_re, int32_t n_re,
                       int32_t* re_out, float* re_score_out, void* workspace, size_t ws_bytes,
                       void* stream);
+
+/*
+ * csa2_workspace_status -- reads the status block at the start of a csa2_index_topk or
+ * csa2_select_chain workspace.  Enqueues a 12-byte copy on `stream` and synchronizes the
+ * stream, so it reports on every call enqueued there before it.
+ *   out  host u32 [2] (out):
+ *     out[0]  sticky error bits, 0 after correct calls: bit 0 = a chunk waited too long
+ *             for its row's threshold, bit 1 = a wave waited too long for its workgroup's
+ *             next chunk.  Neither can happen while the calls run to completion; if one
+ *             is set, that call's results are undefined and the workspace must be
+ *             zero-filled again before its next use.
+ *     out[1]  rows whose sampled threshold was too high since the workspace was
+ *             zero-filled (each row so reported was selected exactly, by a second scan).
+ * Errors: INVALID_ARG (null pointers), ALIGNMENT (workspace not 256-byte aligned), HIP.
+ */
+int csa2_workspace_status(const void* workspace, uint32_t* out, void* stream);
 
 /* Bytes of workspace csa2_sparse_attn_decode needs for this shape. */
 size_t csa2_attn_workspace_size(int32_t batch, int32_t k);

@@ -4,7 +4,7 @@ Its selection is compared (1) bit for bit with the oracle's selection rule appli
 GPU's own fp32 scores from csa2_index_score (both calls run the same scan arithmetic),
 (2) with csa2_index_score + csa2_topk, output for output, and (3) against fp64 oracle
 scores under the gap rule.  The workspace must come back ready for the next call: the
-status word stays 0 and the histograms and barrier counters return to zero.
+status block reports no error and the task and per-row counters return to zero.
 """
 import sys
 
@@ -64,29 +64,31 @@ def two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None):
     return sc, idx, so
 
 
-SEL_BYTES = 4096 * 4 + 2048 * 4 + 512 * 4 + 256 * 4 + 2048 * 8  # one selection block
-SEL_HISTS = 4096 * 4 + 2048 * 4 + 512 * 4                       # its three histograms
-MAX_SEL = 6
-FINE_BYTES = 4096 * 16 * 4                                       # fine counts per row
-
-
-def ws_clean(ws, B):
-    """Status word 0; barrier counters, the above-window count, every selection's
-    histograms and the fine window counts back to zero.  Layout: status 256 B | per row
-    32 u32 (arrivals, departures, fine-window hint, keys above the window), 256-aligned |
-    B x 6 selection blocks | B x fine counts."""
+def ws_clean(ws, B, slow=None):
+    """Status block: no error bits, the task counter back to zero (and, when given, the
+    number of rows that took the second scan); the per-row counters that follow it (64
+    bytes per row from byte 256) back to zero."""
+    bits, n_slow = csa2.csa2_workspace_status(ws)
+    assert bits == 0, f"workspace error bits {bits:#x}"
+    if slow is not None:
+        assert n_slow == slow, f"{n_slow} rows re-scanned, expected {slow}"
     w = h(ws)
-    assert w[:4].view(np.uint32)[0] == 0, "a row barrier gave up waiting"
-    sync = -(-B * 32 * 4 // 256) * 256
-    rows = w[256:256 + B * 128].view(np.uint32).reshape(B, 32)
-    assert not rows[:, :2].any(), "barrier counters not reset"
-    assert not rows[:, 3].any(), "above-window count not reset"
-    base = 256 + sync
-    for blk in range(B * MAX_SEL):
-        o = base + blk * SEL_BYTES
-        assert not w[o:o + SEL_HISTS].any(), f"histograms of block {blk} not returned to zero"
-    fine = base + B * MAX_SEL * SEL_BYTES
-    assert not w[fine:fine + B * FINE_BYTES].any(), "fine window counts not cleared"
+    assert w[4:8].view(np.uint32)[0] == 0, "task counter not reset"
+    rows = min(B, 16)
+    assert not w[256:256 + rows * 64].any(), "per-row counters not reset"
+
+
+def sampled_columns(n):
+    """Columns a row of n > 24,576 visible columns samples for its threshold: 16 groups of
+    64 consecutive columns per 32,768 columns (at least 16, at most 512 groups), group g of
+    G centred at column (2g + 1) n / 2G."""
+    ns = min(32, max(1, n // 32768))
+    G = ns * 16
+    cols = []
+    for g in range(G):
+        st = max(0, min(n - 64, (2 * g + 1) * n // (2 * G) - 32))
+        cols.extend(range(st, st + 64))
+    return np.unique(np.asarray(cols))
 
 
 def same_as_two_step(cache, q_idx, n_cols, k, n_valid=None, cand=None, rows=None):
@@ -207,47 +209,38 @@ def test_workspace_reuse_is_deterministic():
     ws_clean(ws, 2)
 
 
-def test_fine_window_hint_hits_and_misses():
-    """Long rows count a fine window around the previous call's level-1 bin.  Calls on one
-    workspace alternate between queries whose k-th score lies in that window and queries
-    scaled by 8 (three octaves away: the window misses); every call stays exact."""
-    log("index_topk fine-window hint")
-    n = 200_000
-    cache = synth.make_entries([n, n - 3], seed=38, device=DEV)
-    q = synth.make_index_queries(2, 38, device=DEV)
-    q8 = (q.view(torch.bfloat16).float() * 8).to(torch.bfloat16).view(torch.int16)
-    ws = csa2.index_topk_workspace(2, n, 16384)
-    for qq in (q, q, q8, q, q8, q8, q):
-        idx, so, _ = fused(cache, qq, n, 16384, ws=ws)
-        _, idx2, so2 = two_step(cache, qq, n, 16384)
-        torch.cuda.synchronize()
-        assert torch.equal(idx, idx2) and torch.equal(so, so2)
-    ws_clean(ws, 2)
-    hint = h(ws)[256:256 + 2 * 128].view(np.uint32).reshape(2, 32)[:, 2]
-    assert np.all(hint > 0), "the hint was not kept"
+def test_threshold_too_high_takes_the_second_scan():
+    """Entries at the sampled columns score far above every other entry, so the sampled
+    threshold keeps fewer than k candidates: the selection scans the row again keeping every
+    key, and the result is still exact (and counted in the status block)."""
+    log("index_topk forced second scan")
+    n, k = 100_000, 16384
+    cache = synth.make_entries([n, n], seed=45, device=DEV)
+    cols = torch.from_numpy(sampled_columns(n)).to(DEV)
+    cache.idx_codes[cols] = 0x77           # every value 6
+    cache.idx_scale[cols] = 1000.0
+    q = torch.ones((2, 128), dtype=torch.float32).to(torch.bfloat16).view(torch.int16).to(DEV)
+    ws = csa2.index_topk_workspace(2, n, k)
+    idx, so, _ = fused(cache, q, n, k, ws=ws)
+    _, idx2, so2 = two_step(cache, q, n, k)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(so, so2)
+    ws_clean(ws, 2, slow=1)                # only row 0 holds the planted entries
+    s0 = oracle.index_scores(h(q)[0], h(cache.idx_codes)[:n], h(cache.idx_scale)[:n])
+    check_topk(h(idx)[0], s0, k, label="row 0")
 
 
-def test_fine_window_fast_path_with_clustered_ties():
-    """Repeated calls on one workspace take the pool's threshold straight from the fine
-    window.  Five hundred copies of the k-th entry inside one workgroup's columns put more
-    tied keys in the threshold sub-bin than a workgroup may publish, so the tie rule runs
-    from the window's bin; every call stays exact."""
-    log("index_topk fine-window fast path, clustered ties")
-    n, k = 300_000, 16384
-    cache = synth.make_entries([n], seed=44, device=DEV)
-    q = synth.make_index_queries(1, 44, device=DEV)
-    s = oracle.index_scores(h(q)[0], h(cache.idx_codes), h(cache.idx_scale))
-    src = int(np.argsort(-s, kind="stable")[k - 1])
-    dst = torch.arange(3 * 2048 + 100, 3 * 2048 + 600, device=DEV)
-    cache.idx_codes[dst] = cache.idx_codes[src].clone()
-    cache.idx_scale[dst] = cache.idx_scale[src].clone()
-    ws = csa2.index_topk_workspace(1, n, k)
-    for _ in range(3):
-        idx, so, _ = fused(cache, q, n, k, ws=ws)
-        _, idx2, so2 = two_step(cache, q, n, k)
-        torch.cuda.synchronize()
-        assert torch.equal(idx, idx2) and torch.equal(so, so2)
-    ws_clean(ws, 1)
+def test_ragged_rows_mix_sampled_and_unsampled():
+    """Rows with every valid key kept (<= 32,768 columns) and sampled rows in one call, with
+    lengths that end inside a chunk, exactly at chunk ends and at zero."""
+    log("index_topk ragged rows")
+    lens = [1, 1920, 1921, 32_768, 32_769, 65_536 + 7, 3 * 1920 * 17, 0]
+    cache = synth.make_entries([max(1, x) for x in lens], seed=46, device=DEV)
+    q = synth.make_index_queries(len(lens), 46, device=DEV)
+    n_cols = max(lens)
+    for k in (512, 16384):
+        _, _, ws = same_as_two_step(cache, q, n_cols, k, n_valid=i32(lens))
+        ws_clean(ws, len(lens))
 
 
 def test_long_decode_pool_and_reindex_at_full_size():
@@ -263,8 +256,8 @@ def test_long_decode_pool_and_reindex_at_full_size():
     same_as_two_step(cache, q_re, 16384, 512, n_valid=i32([16384] * B), cand=pool)
 
 
-def test_rows_split_over_several_launches():
-    """5 x 2^20 columns need more workgroups than fit at once: rows go in several launches."""
+def test_many_rows_of_2_20():
+    """5 x 2^20 columns: more rows than the c4 batch, chunks claimed across all of them."""
     B, N = 5, 1 << 20
     log(f"index_topk split B={B}")
     cache = synth.make_entries([N] * B, seed=36, device=DEV)
@@ -273,9 +266,9 @@ def test_rows_split_over_several_launches():
     ws_clean(ws, B)
 
 
-def test_row_longer_than_one_resident_grid():
-    """A row of more than 256 x 16,384 columns (more workgroups than CUs) takes the two-launch
-    path inside the call."""
+def test_row_longer_than_the_filtered_selection():
+    """A row of more than 2,048 chunks of 1,920 columns takes the scan-then-top-k path
+    inside the call."""
     n = 256 * 16384 + 5000
     log(f"index_topk long row n={n}")
     cache = synth.make_entries([n], seed=37, device=DEV)
@@ -357,8 +350,8 @@ def test_chain_with_ties():
 
 
 def test_chain_long_decode_at_full_size():
-    """4 x 2^20 Full scan -> pool 16,384 -> own top-512 and one Reindex layer; the second
-    and third calls on the workspace use the fine window of the first."""
+    """4 x 2^20 Full scan -> pool 16,384 -> own top-512 and one Reindex layer, three calls
+    on one workspace."""
     cfg = synth.CONFIGS["c4_long_decode"]
     B, N = cfg["B"], 1 << 20
     log(f"select_chain 2^20 B={B}")
