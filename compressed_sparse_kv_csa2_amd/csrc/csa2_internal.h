@@ -34,7 +34,8 @@ struct TopkWs {
 constexpr int kMaxReindex = CSA2_MAX_REINDEX;  // Reindex layers one chained call re-scores
 
 // Rows the single-launch filtered selection handles (longer rows: index_score + topk).
-bool fsel_fits(int n_cols);
+bool fsel_fits(int n_cols, int k);
+bool fsel_len_ok(int n_cols);
 size_t fsel_ws_bytes(int batch, int n_cols, bool chain);
 hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* scale,
                        const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,

@@ -47,6 +47,8 @@
 //     (Reindex), which the writer computed as it stored each candidate.
 // The launch boundary orders the candidate stores before the selection.  The selection
 // returns the scan's counters to zero, so the workspace needs no clearing between calls.
+#include <cmath>
+
 #include "csa2_internal.h"
 #include "scan_device.h"
 #include "select_device.h"
@@ -68,24 +70,18 @@ namespace {
 
 constexpr int kT = 1024;                  // threads per workgroup
 constexpr int kNW = kT / 64;              // waves
-constexpr int kSW = 15;                   // streaming waves of the scan
+constexpr int kSeg = 16384;               // columns per scan segment (one workgroup, keys in LDS)
+constexpr int kSegU = kSeg / kT;          // segment keys per thread
 constexpr int kMaxCand = 24576;           // candidates the selection holds (LDS + registers)
 constexpr int kU = kMaxCand / kT;         // candidates per thread
 constexpr int kPU = CSA2_MAX_K / kT;      // pool entries per thread
-constexpr int kSampTask = 1024;           // sampled keys per sample task (16 waves x 64)
-constexpr int kSampEvery = 32;            // one column in 32 is sampled
-constexpr int kMaxSampTasks = 32;
-constexpr int kSampRow = kSampTask * kMaxSampTasks;
 constexpr int kMaxRows = 256;             // rows per launch
-constexpr int kMaxRuns = 2048;            // chunks per row
+constexpr int kMaxRuns = 2048;            // segments per row
 constexpr int kBins = 4096;
-constexpr int kG = 2;                     // groups of 64 columns per streaming wave and chunk
-constexpr int kChunk = kSW * 64 * kG;     // 1,920 columns
-constexpr int kCW = kChunk / 64;          // 64-column words of a chunk
 constexpr int kRowWords = 16;             // per-row counters (64 bytes)
-constexpr int kRwSamp = 0, kRwTheta = 1, kRwDone = 2, kRwShift = 3;
-constexpr int kCtStatus = 0, kCtTask = 1, kCtSlow = 2;
-constexpr uint32_t kSpin = 1u << 22;
+constexpr int kRwDone = 0;
+constexpr int kCtStatus = 0, kCtSlow = 2;
+constexpr uint32_t kTrunc = 0x80000000u;  // segment count flag: the segment kept only its top keys
 constexpr int kChainRows = 16;            // rows per launch of a chained selection
 
 __device__ __forceinline__ uint32_t ld_ag(const uint32_t* p) {
@@ -97,6 +93,9 @@ __device__ __forceinline__ void st_ag(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t add_ag(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A value every lane of the wave holds alike, moved to a scalar register.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
 // Waits until every vector memory operation this wave issued has completed; its
 // agent-scope stores are then visible to every workgroup.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -108,7 +107,7 @@ struct FsArgs {
   const int64_t* seq_base;
   const int32_t* n_valid;
   const int32_t* cand;        // [batch][n_cols] (Reindex) or null
-  int n_cols, runs;           // columns, chunks per row at most
+  int n_cols, runs;           // columns, segments per row at most
   int row0, rows, batch;
   int k;
   int32_t* out;               // [batch][k]
@@ -119,16 +118,14 @@ struct FsArgs {
   const uint16_t* q_re;       // [n_re][batch][128]
   int32_t* re_out;            // [n_re][batch][re_k]
   float* re_sout;             // or null
-  uint32_t* ctrl;             // status, task counter, slow rows
-  uint32_t* roww;             // [rows][16]: sample tasks done, theta, picking workgroups done, shift
-  uint32_t* samp;             // [rows][kSampRow]
-  uint32_t* ccnt;             // [rows][runs] how many candidates each chunk has
-  uint32_t* ckey;             // [rows][cap] candidate keys: chunk j's run (column order) at j * 1920
+  uint32_t* ctrl;             // status, -, rows re-scanned
+  uint32_t* roww;             // [rows][16]: picking workgroups done
+  uint32_t* ccnt;             // [rows][runs] candidates of each segment (| kTrunc when truncated)
+  uint32_t* ckey;             // [rows][cap] candidate keys: segment j's run (column order) at j * 16384
   uint32_t* ccol;             // [rows][cap] their columns
   uint32_t* rekey;            // [4][rows][cap] their Reindex re-scores (chain)
   uint32_t* pmap;             // [rows][16384] store index of each pool entry (chain, slow path)
-  uint32_t* rhist;            // [rows][4096] candidates per bin of (key - theta) >> shift
-  size_t cap;                 // per-row store: runs * 1920
+  size_t cap;                 // per-row store: runs * 16384
 };
 
 // LDS the exact-threshold search and the ordered emission share.
@@ -140,44 +137,6 @@ struct Core {
   uint32_t res[4];
   uint32_t misc[8];
 };
-
-// ------------------------------------------------------------------ workgroup reductions
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o));
-  return v;
-}
-
-// Sum, max and min over the workgroup in one exchange.  Ends with a barrier.
-__device__ __forceinline__ void block_smm(uint32_t& s, uint32_t& mx, uint32_t& mn, Core& L) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  s = wave_sum(s);
-  mx = wave_max(mx);
-  mn = wave_min(mn);
-  if (lane == 0) {
-    L.red[wave] = s;
-    L.red[kNW + wave] = mx;
-    L.red[2 * kNW + wave] = mn;
-  }
-  __syncthreads();
-  uint32_t a = 0, b = 0, c = 0xffffffffu;
-  for (int w = 0; w < kNW; ++w) {
-    a += L.red[w];
-    b = max(b, L.red[kNW + w]);
-    c = min(c, L.red[2 * kNW + w]);
-  }
-  s = a;
-  mx = b;
-  mn = c;
-  __syncthreads();
-}
 
 // Calls f(u, i) for the elements i < m this thread owns, i = threadIdx.x + kT * u: with
 // U > 0 the loop is unrolled U times (u is a constant, so per-thread register arrays may
@@ -191,6 +150,7 @@ __device__ __forceinline__ void for_mine(int m, F f) {
       if (i < m) f(u, i);
     }
   } else {
+#pragma unroll 4
     for (int i = threadIdx.x; i < m; i += kT) f(0, i);
   }
 }
@@ -206,106 +166,163 @@ __device__ __forceinline__ bool selected(const Thr& t, uint32_t key, uint32_t x)
   return key != 0u && (key > t.tkey || (key == t.tkey && x <= t.tx));
 }
 
+// Bin of the need-th largest element of h[0 .. 4 kT) (thread t owns the 4 bins just below
+// 4 (kT - t); one block scan orders them from the top).  With clamp, need becomes
+// min(need, total) first.  res[0] = bin, res[1] = elements in higher bins, res[2] = total,
+// res[3] = need (after the clamp).  Ends with a barrier.
+__device__ __forceinline__ void find_bin4(const uint32_t* h, uint32_t need, bool clamp, Core& C) {
+  const int tid = threadIdx.x;
+  const int top = 4 * (kT - tid);
+  uint32_t c[4];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = h[top - 1 - i];
+    sum += c[i];
+  }
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan(sum, C.scan, &total);
+  if (clamp) need = min(need, total);
+  if (tid == 0) {
+    C.res[0] = 0u;
+    C.res[1] = 0u;
+    C.res[2] = total;
+    C.res[3] = need;
+  }
+  __syncthreads();
+  if (need > 0u && excl < need && need <= excl + sum) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (acc + c[i] >= need) {
+        C.res[0] = (uint32_t)(top - 1 - i);
+        C.res[1] = acc;
+        break;
+      }
+      acc += c[i];
+    }
+  }
+  __syncthreads();
+}
+
+// Largest of v over a wave (DPP row shifts and broadcasts; lane 63 ends with it).
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  int x = (int)v;
+  x = (int)max((unsigned)x, (unsigned)__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = (int)max((unsigned)x, (unsigned)__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = (int)max((unsigned)x, (unsigned)__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = (int)max((unsigned)x, (unsigned)__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = (int)max((unsigned)x, (unsigned)__builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = (int)max((unsigned)x, (unsigned)__builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
+// Sum and largest of (s, mx) over the workgroup.  Ends with a barrier.
+__device__ __forceinline__ void block_sum_max(uint32_t& s, uint32_t& mx, Core& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t ws = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(s), 63);
+  const uint32_t wm = wave_max_dpp(mx);
+  if (lane == 0) {
+    L.red[wave] = ws;
+    L.red[kNW + wave] = wm;
+  }
+  __syncthreads();
+  uint32_t a = 0u, b = 0u;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) {
+    a += L.red[w];
+    b = max(b, L.red[kNW + w]);
+  }
+  s = uni(a);
+  mx = uni(b);
+  __syncthreads();
+}
+
 // The need-th largest composite (key, then lower x first) among elements i < m with a
-// non-zero key K(u, i) and unique tie index X(u, i), need = min(k, #non-zero).  The value
-// range is narrowed with 4,096-bin histograms over the range actually present (keys
-// first, then, for equal keys, ~x) until at most 64 elements remain in the chosen bin;
-// those are ranked directly by wave 0.  Whole workgroup; ends with a barrier.
+// non-zero key K(u, i) and unique tie index X(u, i), need = min(k, #non-zero).  One sweep
+// finds the count and the largest key; then 4,096-bin histograms of windows [lo, hi]: the
+// first holds the 2^24 key values up to the largest, so a top-k's threshold bin usually
+// holds a few keys; a window with fewer than need members hands them all over as above the
+// threshold and the next window is everything below it; otherwise the next window is the
+// threshold's bin, until at most 64 members remain and wave 0 ranks them directly.  More
+// than 64 equal keys are ranked by ~x the same way.  Whole workgroup; ends with a barrier.
 template <int U, class KF, class XF>
-__device__ __forceinline__ Thr find_thr(KF K, XF X, int m, uint32_t k, Core& L, int tr = -1) {
+__device__ __forceinline__ Thr find_thr_any(KF K, XF X, int m, uint32_t k, Core& L, int tr = -1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int npass = 0;
-  if (tr >= 0 && tid == 0) FS_TR(tr, FS_NOW() | ((unsigned long long)m << 44));
-  uint32_t c = 0, mx = 0, mn = 0xffffffffu;
+  Thr t;
+  t.tkey = 0u;
+  t.tx = 0u;
+  if (tr >= 0 && tid == 0) FS_TR(tr, FS_NOW());
+  uint32_t c = 0, mx = 0;
   for_mine<U>(m, [&](int u, int i) {
     const uint32_t v = K(u, i);
     if (v) {
       ++c;
       mx = max(mx, v);
-      mn = min(mn, v);
     }
   });
-  block_smm(c, mx, mn, L);
-  Thr t;
+  block_sum_max(c, mx, L);
   t.total = c;
   uint32_t need = min(k, c);
   t.nsel = need;
-  t.tkey = 0u;
-  t.tx = 0u;
   if (need == c) return t;  // every non-zero key (or none)
-
-  uint32_t lo = mn, hi = mx, cnt_in = c, tkey = 0u;
+  uint32_t hi = mx, lo = mx >= (1u << 24) ? mx - ((1u << 24) - 1u) : 1u, tkey = 0u;
   bool xphase = false;
-  // member in the key phase: lo <= K <= hi; in the x phase: K == tkey and lo <= ~X <= hi
-  while (cnt_in > 64u) {
-    if (!xphase && lo == hi) {  // more than 64 equal keys: rank them by the tie index
+  uint32_t cnt_in = 0xffffffffu;
+  auto member = [&](int u, int i, uint32_t& v) -> bool {
+    const uint32_t key = K(u, i);
+    if (!xphase) {
+      v = key;
+      return key != 0u && key >= lo && key <= hi;
+    }
+    if (key != tkey) return false;
+    v = ~X(u, i);
+    return v >= lo && v <= hi;
+  };
+  for (int pass = 0; pass < 12; ++pass) {
+    if (!xphase && lo == hi && cnt_in > 64u) {  // more than 64 equal keys: rank them by ~x
       xphase = true;
       tkey = lo;
-      uint32_t s2 = 0, xmx = 0, xmn = 0xffffffffu;
-      for_mine<U>(m, [&](int u, int i) {
-        if (K(u, i) == tkey) {
-          const uint32_t v = ~X(u, i);
-          ++s2;
-          xmx = max(xmx, v);
-          xmn = min(xmn, v);
-        }
-      });
-      block_smm(s2, xmx, xmn, L);
-      lo = xmn;
-      hi = xmx;
-      continue;
+      lo = 0u;
+      hi = 0xffffffffu;
     }
     const uint32_t range = hi - lo;
     const int sh = range == 0u ? 0 : max(0, 32 - __clz((int)range) - 12);
-    if (tr >= 0 && tid == 0 && npass < 8) FS_TR(tr + 1 + npass, FS_NOW() | ((unsigned long long)cnt_in << 44));
-    ++npass;
     for (int i = tid; i < kBins; i += kT) L.hist[i] = 0u;
     __syncthreads();
     for_mine<U>(m, [&](int u, int i) {
-      const uint32_t key = K(u, i);
       uint32_t v;
-      bool mem;
-      if (!xphase) {
-        v = key;
-        mem = key != 0u && key >= lo && key <= hi;
-      } else {
-        mem = key == tkey;
-        v = mem ? ~X(u, i) : 0u;
-        mem = mem && v >= lo && v <= hi;
-      }
-      if (mem) atomicAdd(&L.hist[(v - lo) >> sh], 1u);
+      if (member(u, i, v)) atomicAdd(&L.hist[(v - lo) >> sh], 1u);
     });
     __syncthreads();
-    find_bin_block<kBins / kT>(L.hist, need, L.scan, L.res);  // ends with a barrier
-    const uint32_t d = L.res[0];
-    need -= L.res[1];
-    cnt_in = L.hist[d];
+    find_bin4(L.hist, need, false, L);  // ends with a barrier
+    const uint32_t in_window = uni(L.res[2]);
+    if (tr >= 0 && tid == 0 && pass < 8) FS_TR(tr + 1 + pass, FS_NOW() | ((unsigned long long)in_window << 44));
+    if (in_window < need) {  // the threshold lies below this window
+      need -= in_window;
+      hi = lo - 1u;
+      lo = xphase ? 0u : 1u;
+      cnt_in = 0xffffffffu;
+      __syncthreads();
+      continue;
+    }
+    const uint32_t d = uni(L.res[0]);
+    need -= uni(L.res[1]);
+    cnt_in = uni(L.hist[d]);
     const uint32_t nlo = lo + (d << sh);
     hi = (uint32_t)min((unsigned long long)hi, (unsigned long long)nlo + (1ull << sh) - 1ull);
     lo = nlo;
     __syncthreads();  // L.hist and L.res are read before they are rewritten
+    if (cnt_in <= 64u) break;
   }
   // rank the <= 64 remaining members directly
-  if (tr >= 0 && tid == 0) FS_TR(tr + 10, FS_NOW() | ((unsigned long long)npass << 44));
   if (tid == 0) L.misc[0] = 0u;
   __syncthreads();
   for_mine<U>(m, [&](int u, int i) {
-    const uint32_t key = K(u, i);
-    bool mem;
-    uint32_t x = 0u;
-    if (!xphase) {
-      mem = key != 0u && key >= lo && key <= hi;
-      if (mem) x = X(u, i);
-    } else {
-      mem = key == tkey;
-      if (mem) {
-        x = X(u, i);
-        mem = ~x >= lo && ~x <= hi;
-      }
-    }
-    if (mem) {
+    uint32_t v;
+    if (member(u, i, v)) {
       const uint32_t slot = atomicAdd(&L.misc[0], 1u);
-      if (slot < 64u) L.pub[slot] = ((unsigned long long)key << 32) | (uint32_t)~x;
+      if (slot < 64u) L.pub[slot] = ((unsigned long long)K(u, i) << 32) | (uint32_t)~X(u, i);
     }
   });
   __syncthreads();
@@ -325,10 +342,223 @@ __device__ __forceinline__ Thr find_thr(KF K, XF X, int m, uint32_t k, Core& L, 
     }
   }
   __syncthreads();
-  t.tkey = L.res[2];
-  t.tx = L.res[3];
+  t.tkey = uni(L.res[2]);
+  t.tx = uni(L.res[3]);
+  if (tr >= 0 && tid == 0) FS_TR(tr + 10, FS_NOW());
   __syncthreads();
   return t;
+}
+
+// Register form of the same search for U > 0: each thread's U keys (element i = tid + kT * u)
+// are read once into registers, and every sweep is straight-line code over them.  K must
+// return 0 for i >= m.
+template <int U, class KF, class XF>
+__device__ __forceinline__ Thr find_thr(KF K, XF X, int m, uint32_t k, Core& L, int tr = -1) {
+  if constexpr (U == 0) {
+    return find_thr_any<0>(K, X, m, k, L, tr);
+  } else {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    Thr t;
+    t.tkey = 0u;
+    t.tx = 0u;
+    if (tr >= 0 && tid == 0) FS_TR(tr, FS_NOW());
+    uint32_t kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kk[u] = K(u, tid + kT * u);
+    uint32_t c = 0, mx = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      c += kk[u] != 0u ? 1u : 0u;
+      mx = max(mx, kk[u]);
+    }
+    block_sum_max(c, mx, L);
+    t.total = c;
+    uint32_t need = min(k, c);
+    t.nsel = need;
+    if (need == c) return t;  // every non-zero key (or none)
+    uint32_t hi = mx, lo = mx >= (1u << 24) ? mx - ((1u << 24) - 1u) : 1u, tkey = 0u;
+    bool xphase = false;
+    uint32_t cnt_in = 0xffffffffu;
+    for (int pass = 0; pass < 12; ++pass) {
+      if (!xphase && lo == hi && cnt_in > 64u) {  // more than 64 equal keys: rank them by ~x
+        xphase = true;
+        tkey = lo;
+        lo = 0u;
+        hi = 0xffffffffu;
+      }
+      const uint32_t range = hi - lo;
+      const int sh = range == 0u ? 0 : max(0, 32 - __clz((int)range) - 12);
+#pragma unroll
+      for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
+      __syncthreads();
+      if (!xphase) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t v = kk[u];
+          if (v != 0u && v >= lo && v <= hi) atomicAdd(&L.hist[(v - lo) >> sh], 1u);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t v = ~X(u, tid + kT * u);
+          if (kk[u] == tkey && v >= lo && v <= hi) atomicAdd(&L.hist[(v - lo) >> sh], 1u);
+        }
+      }
+      __syncthreads();
+      find_bin4(L.hist, need, false, L);  // ends with a barrier
+      const uint32_t in_window = L.res[2];
+      if (tr >= 0 && tid == 0 && pass < 8) FS_TR(tr + 1 + pass, FS_NOW() | ((unsigned long long)in_window << 44));
+      if (in_window < need) {  // the threshold lies below this window
+        need -= in_window;
+        hi = lo - 1u;
+        lo = xphase ? 0u : 1u;
+        cnt_in = 0xffffffffu;
+        __syncthreads();
+        continue;
+      }
+      const uint32_t d = uni(L.res[0]);
+      need -= uni(L.res[1]);
+      cnt_in = uni(L.hist[d]);
+      const uint32_t nlo = lo + (d << sh);
+      hi = (uint32_t)min((unsigned long long)hi, (unsigned long long)nlo + (1ull << sh) - 1ull);
+      lo = nlo;
+      __syncthreads();  // L.hist and L.res are read before they are rewritten
+      if (cnt_in <= 64u) break;
+    }
+    // rank the <= 64 remaining members directly
+    if (tid == 0) L.misc[0] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t key = kk[u];
+      const uint32_t x = X(u, tid + kT * u);
+      const uint32_t v = xphase ? ~x : key;
+      const bool mem = (xphase ? key == tkey : key != 0u) && v >= lo && v <= hi;
+      if (mem) {
+        const uint32_t slot = atomicAdd(&L.misc[0], 1u);
+        if (slot < 64u) L.pub[slot] = ((unsigned long long)key << 32) | (uint32_t)~x;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t nt = min(L.misc[0], 64u);
+      const unsigned long long cc = (uint32_t)lane < nt ? L.pub[lane] : 0ull;
+      const uint32_t chi = (uint32_t)(cc >> 32), clo = (uint32_t)cc;
+      uint32_t r = 0;
+      for (uint32_t j = 0; j < nt; ++j) {
+        const uint32_t ohi = __builtin_amdgcn_readlane(chi, j);
+        const uint32_t olo = __builtin_amdgcn_readlane(clo, j);
+        r += (ohi > chi || (ohi == chi && olo > clo)) ? 1u : 0u;
+      }
+      if ((uint32_t)lane < nt && r == need - 1u) {
+        L.res[2] = chi;
+        L.res[3] = ~clo;
+      }
+    }
+    __syncthreads();
+    t.tkey = uni(L.res[2]);
+    t.tx = uni(L.res[3]);
+    if (tr >= 0 && tid == 0) FS_TR(tr + 10, FS_NOW());
+    __syncthreads();
+    return t;
+  }
+}
+
+// The same threshold for the common case, from registers, with the count c of non-zero
+// keys and the largest key mx given: one 4,096-bin histogram of the 2^24 key values up to
+// mx (bins of 4,096 values), one of the exact values inside the threshold's bin, done.  The
+// general search runs instead when the threshold lies below that window, or when keys
+// equal to the threshold key must be split by the tie index.  kk[u] = 0 for i >= m.
+template <int U, class XF>
+__device__ __forceinline__ Thr find_thr_lean(const uint32_t (&kk)[U], XF X, int m, uint32_t k, uint32_t c,
+                                             uint32_t mx, Core& L) {
+  const int tid = threadIdx.x;
+  Thr t;
+  t.total = c;
+  t.nsel = min(k, c);
+  t.tkey = 0u;
+  t.tx = 0xffffffffu;
+  if (t.nsel == c) return t;  // every non-zero key (or none)
+  uint32_t need = t.nsel;
+  const uint32_t lo = mx >= (1u << 24) ? mx - ((1u << 24) - 1u) : 1u;
+#pragma unroll
+  for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t v = kk[u];
+    if (v >= lo) atomicAdd(&L.hist[(v - lo) >> 12], 1u);
+  }
+  __syncthreads();
+  find_bin4(L.hist, need, false, L);  // ends with a barrier
+  bool general = uni(L.res[2]) < need;  // the threshold lies below the window
+  uint32_t tkey = 0u;
+  if (!general) {
+    const uint32_t lo2 = lo + (uni(L.res[0]) << 12);
+    need -= uni(L.res[1]);
+    __syncthreads();  // L.res is read before it is rewritten
+#pragma unroll
+    for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t e = kk[u] - lo2;
+      if (e < 4096u) atomicAdd(&L.hist[e], 1u);
+    }
+    __syncthreads();
+    find_bin4(L.hist, need, false, L);
+    const uint32_t d = uni(L.res[0]);
+    tkey = lo2 + d;
+    need -= uni(L.res[1]);
+    general = need != uni(L.hist[d]);  // equal keys to split by the tie index
+    __syncthreads();
+  }
+  if (general) return find_thr<U>([&](int u, int) { return kk[u]; }, X, m, k, L);
+  t.tkey = tkey;  // every key == tkey is taken (tx = all)
+  return t;
+}
+
+// Calls emit(rank, u, i) for every element i = threadIdx.x + kT * u (u < U, i < m) whose
+// bit u of `mine` is set, rank = its position among them in index order (U * kT <= 64 kT);
+// returns how many there are.  Ballots, one scan of the per-(u, wave) counts by wave 0.
+// Whole workgroup; ends with a barrier.
+template <int U, class EmitF>
+__device__ __forceinline__ uint32_t emit_reg(uint32_t mine, EmitF emit, Core& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  static_assert(U * kNW <= 1024, "counts fit the scan");
+  uint32_t below[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const unsigned long long msk = __ballot((mine >> u) & 1u);
+    below[u] = lanes_below(msk);
+    if (lane == 0) L.hist[u * kNW + wave] = (uint32_t)__popcll(msk);
+  }
+  __syncthreads();
+  if (wave == 0) {  // U * kNW counts in (u, wave) order = index order
+    constexpr int PER = (U * kNW + 63) / 64;
+    uint32_t c[PER];
+    uint32_t part = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      c[q] = PER * lane + q < U * kNW ? L.hist[PER * lane + q] : 0u;
+      part += c[q];
+    }
+    const uint32_t incl = wave_incl_scan(part);
+    uint32_t run = incl - part;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (PER * lane + q < U * kNW) L.hist[PER * lane + q] = run;
+      run += c[q];
+    }
+    if (lane == 63) L.misc[5] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if ((mine >> u) & 1u) emit(L.hist[u * kNW + wave] + below[u], u, tid + kT * u);
+  const uint32_t total = uni(L.misc[5]);
+  __syncthreads();
+  return total;
 }
 
 // Calls emit(rank, i) for every element i < m with sel(i), rank = its position among them
@@ -379,19 +609,18 @@ __device__ __forceinline__ void emit_ordered(int m, SelF sel, EmitF emit, Core& 
 }
 
 // ------------------------------------------------------------------ shared helpers
-// Sample tasks and chunk tasks of a row with n visible columns.
-__device__ __forceinline__ int row_samples(int n) {
-  return n > kMaxCand ? min(kMaxSampTasks, max(1, n / (kSampTask * kSampEvery))) : 0;
-}
-__device__ __forceinline__ int row_chunks(int n) { return max(1, (n + kChunk - 1) / kChunk); }
+// Segments of a row with n visible columns (one, possibly empty, for n = 0).
+__device__ __forceinline__ int row_segs(int n) { return max(1, (n + kSeg - 1) / kSeg); }
 
-// Sample rank whose key serves as theta: about k * s / n sampled keys lie above the row's
-// k-th key; four standard deviations and four keys more keep theta below it unless the
-// sample is far from typical.  0: no useful threshold (theta = 1).
-__device__ __forceinline__ uint32_t sample_rank(int k, int s, int n) {
-  const float mu = (float)k * (float)s / (float)n;
-  const float r = ceilf(mu + 4.0f * sqrtf(mu) + 4.0f);
-  return r >= (float)s ? 0u : (uint32_t)r;
+// Keys a segment of len columns keeps, of a row of n visible columns whose top-k is
+// wanted: every key when the row is short enough for the selection to hold it whole;
+// otherwise about e = k len / n of the row's top-k are expected in the segment, and six
+// standard deviations and four more keep every one of them unless the row is far from
+// typical (the selection detects that case and scans the row again).
+__device__ __forceinline__ uint32_t seg_keep(int k, int len, int n) {
+  if (n <= kMaxCand) return (uint32_t)len;
+  const float e = (float)k * (float)len / (float)n;
+  return (uint32_t)ceilf(e + 6.0f * sqrtf(e) + 4.0f);
 }
 
 __device__ __forceinline__ void unpack_q(const uint4* qp, bf16x2 (&q)[16]) {
@@ -436,388 +665,131 @@ __device__ __forceinline__ int upper_index(const uint32_t* pre, int n, uint32_t 
   return lo;
 }
 
-// ------------------------------------------------------------------ k_fscan
-struct ScanLds {
-  union {
-    uint32_t key[kSampRow];               // a row's sample (theta), before any chunk
-    struct {                              // per phase parity, per group of 64 columns:
-      uint32_t skey[2][kCW][64];          //   its candidates' keys, in column order
-      uint16_t soff[2][kCW][64];          //   their columns within the chunk
-      uint32_t scnt[2][kCW];              //   how many
-      uint32_t gpre[kCW + 1];             // writer: candidates before each group
-    };
-  };
-  uint32_t spre[kMaxRows + 1];            // sample-task prefix per row
-  uint32_t cpre[kMaxRows + 1];            // chunk-task prefix per row
-  int64_t rbase[kMaxRows];                // seq_base of each row
-  int32_t rn[kMaxRows];                   // visible columns of each row
-  uint32_t rth[kMaxRows];                 // theta of each row, as the streaming waves read it
-  uint32_t rsh[kMaxRows];                 // and its histogram shift
-  uint32_t task[4];                       // the chunk task streamed in phase P, at P & 3
-  unsigned long long claim;               // (phase << 32) | task, published by streaming wave 0
+// ------------------------------------------------------------------ k_fseg
+struct SegLds {
+  uint32_t key[kSeg];                     // the segment's keys (0 = not selectable)
+  uint16_t pick[kSeg];                    // local columns of the kept keys, in column order
   __align__(16) uint16_t qre[kMaxReindex * kDIdx];
   Core c;
 };
 
-// Histogram shift of a row: candidate bins (key - theta) >> shift over [theta, top key of
-// the sample], keys above it in the last bin.  kNoHist: rows without a sampled theta.
-constexpr uint32_t kNoHist = 32u;
+// The segment's cut: the lower edge of the 4,096-value bin (of the 2^24 key values up to the
+// largest, mx) that holds its keep-th largest key, so that every key >= cut (at least keep
+// of them, all of them when fewer than keep are non-zero) is kept.  Keeping whole bins keeps
+// equal keys together: what is left out is below everything kept.  Whole workgroup; ends
+// with a barrier.
+template <int U>
+__device__ __forceinline__ uint32_t seg_cut(const uint32_t (&kv)[U], uint32_t keep, uint32_t cnt, uint32_t mx,
+                                            Core& L) {
+  const int tid = threadIdx.x;
+  if (keep >= cnt) return 1u;  // every non-zero key
+  const uint32_t lo = mx >= (1u << 24) ? mx - ((1u << 24) - 1u) : 1u;
+#pragma unroll
+  for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t v = kv[u];
+    if (v >= lo) atomicAdd(&L.hist[(v - lo) >> 12], 1u);
+  }
+  __syncthreads();
+  find_bin4(L.hist, keep, false, L);  // ends with a barrier
+  uint32_t cut = lo + (uni(L.res[0]) << 12);
+  const uint32_t in_window = uni(L.res[2]);
+  __syncthreads();
+  if (in_window < keep && lo > 1u) {  // the cut lies below the window: bins over [1, lo)
+    const uint32_t range = lo - 2u;
+    const int sh = range == 0u ? 0 : max(0, 32 - __clz((int)range) - 12);
+#pragma unroll
+    for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t v = kv[u];
+      if (v != 0u && v < lo) atomicAdd(&L.hist[(v - 1u) >> sh], 1u);
+    }
+    __syncthreads();
+    find_bin4(L.hist, keep - in_window, false, L);
+    cut = 1u + (uni(L.res[0]) << sh);
+    __syncthreads();
+  }
+  return cut;
+}
 
-// One sample task: 16 waves score one group of 64 columns each (stratified over the row)
-// into the row's sample; the last task of the row turns the sample into theta (and the
-// bin width of the row's candidate histogram).
+// Grid: rows x runs.  Workgroup (r, j) scores columns [16384 j, 16384 (j + 1)) of row r into
+// LDS, keeps every key at or above its cut (at least seg_keep of them), and writes them in
+// column order to segment j's run of the row's store, with their count (flagged when keys were
+// left out) and, when chained, their Reindex re-scores (the scan's arithmetic).
 template <bool CAND>
-__device__ __forceinline__ void sample_task(const FsArgs& a, ScanLds& L, int r, int si) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int quarter = lane & 3, ent = lane >> 2;
-  const int n = L.rn[r], ns = row_samples(n);
+__global__ __launch_bounds__(kT) void k_fseg(FsArgs a) {
+  __shared__ SegLds L;
+  const int tid = threadIdx.x, quarter = tid & 3;
+  const int r = (int)blockIdx.x / a.runs, j = (int)blockIdx.x % a.runs;
   const int b = a.row0 + r;
-  const int g = si * kNW + wave;
-  long long st = ((2LL * g + 1) * n) / (2LL * ns * kNW) - 32;
-  st = st < 0 ? 0 : (st > n - 64 ? n - 64 : st);
+  const int n = max(0, min(a.n_valid[b], a.n_cols));
+  if (j >= row_segs(n)) return;
+  const int c0 = j * kSeg, len = max(0, min(n - c0, kSeg));
+  const int64_t base = a.seq_base[b];
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
-  bf16x2 q[16];
-  load_q(a.q + (size_t)b * kDIdx, quarter, q);
-  const ScanGroup s = load_group<CAND>(a.codes, a.scale, cand_row, L.rbase[r], (int)st, n - 1, ent, quarter);
-  const float score = group_score(s, q, quarter);
-  st_ag(&a.samp[(size_t)r * kSampRow + g * 64 + 16 * quarter + ent], s.own_ok ? score_key(score) : 0u);
-  wait_vm();
-  __syncthreads();
-  if (tid == 0) FS_TR(blockIdx.x * 2048 + 2, FS_NOW());
-  if (tid == 0)
-    L.c.misc[2] = add_ag(&a.roww[r * kRowWords + kRwSamp], 1u) == (uint32_t)(ns - 1) ? 1u : 0u;
-  __syncthreads();
-  if (L.c.misc[2] == 0u) return;
-  if (tid == 0) FS_TR(blockIdx.x * 2048 + 3, FS_NOW() | ((unsigned long long)(r + 1) << 52));
-  // the last sample task of the row: theta = the sample key of rank sample_rank; every
-  // load of the sample is issued before the first is stored
-  const int m = ns * kSampTask;
-  uint32_t top = 0u;
-  {
-    uint32_t v[kSampRow / kT];
+  if (tid == 0) FS_TR(blockIdx.x * 8, FS_NOW());
+  uint32_t cnt = 0u, mx = 0u;  // this thread's valid columns and their largest key
+  if (len > 0)
+    scan_columns<CAND, kT>(a.q + (size_t)b * kDIdx, a.codes, a.scale, cand_row, base, n, c0, c0 + len,
+                           [] {},
+                           [&](int col, float score, bool valid) {
+                             const uint32_t key = valid ? score_key(score) : 0u;
+                             L.key[col - c0] = key;
+                             cnt += valid ? 1u : 0u;
+                             mx = max(mx, key);
+                           });
+  block_sum_max(cnt, mx, L.c);  // ends with a barrier
+  if (tid == 0) FS_TR(blockIdx.x * 8 + 1, FS_NOW());
+  // keys of column c0 + tid + kT u, u < 16, in registers
+  uint32_t kv[kSegU];
 #pragma unroll
-    for (int u = 0; u < kSampRow / kT; ++u) {
-      const int i = tid + kT * u;
-      v[u] = i < m ? ld_ag(&a.samp[(size_t)r * kSampRow + i]) : 0u;
-    }
+  for (int u = 0; u < kSegU; ++u) kv[u] = tid + kT * u < len ? L.key[tid + kT * u] : 0u;
+  const uint32_t cut = seg_cut(kv, seg_keep(a.k, len, n), cnt, mx, L.c);
+  if (tid == 0) FS_TR(blockIdx.x * 8 + 2, FS_NOW());
+  const size_t rb = (size_t)r * a.cap + (size_t)j * kSeg;
+  uint32_t mine = 0u;
 #pragma unroll
-    for (int u = 0; u < kSampRow / kT; ++u) {
-      L.key[tid + kT * u] = v[u];
-      top = max(top, v[u]);
+  for (int u = 0; u < kSegU; ++u) mine |= (kv[u] != 0u && kv[u] >= cut ? 1u : 0u) << u;
+  const uint32_t kept = emit_reg<kSegU>(
+      mine,
+      [&](uint32_t rank, int u, int i) {
+        a.ckey[rb + rank] = kv[u];
+        a.ccol[rb + rank] = (uint32_t)(c0 + i);
+        L.pick[rank] = (uint16_t)i;
+      },
+      L.c);
+  if (tid == 0) a.ccnt[(size_t)r * a.runs + j] = kept | (kept < cnt ? kTrunc : 0u);
+  if (tid == 0) FS_TR(blockIdx.x * 8 + 3, FS_NOW());
+  if (!CAND && a.n_re > 0 && kept > 0u) {
+    // the Reindex layers' re-scores of the kept entries: 4 lanes (quarters) per entry
+    for (int i = tid; i < a.n_re * (kDIdx / 8); i += kT) {
+      const int l = i / (kDIdx / 8), part = i % (kDIdx / 8);
+      reinterpret_cast<uint4*>(L.qre)[i] =
+          reinterpret_cast<const uint4*>(a.q_re + ((size_t)l * a.batch + b) * kDIdx)[part];
     }
-  }
-  uint32_t dummy_s = 0, dummy_mn = 0xffffffffu;
-  block_smm(dummy_s, top, dummy_mn, L.c);  // top: the largest sampled key
-  if (tid == 0) FS_TR(blockIdx.x * 2048 + 4, FS_NOW());
-  const uint32_t rk = sample_rank(a.k, m, n);
-  uint32_t th = 1u;
-  if (rk > 0u) {
-    const Thr t = find_thr<0>([&](int, int i) { return L.key[i]; },
-                              [&](int, int i) { return (uint32_t)i; }, m, rk, L.c, blockIdx.x * 2048 + 1500);
-    th = (t.nsel == rk && t.tkey > 0u) ? t.tkey : 1u;
-  }
-  if (tid == 0) FS_TR(blockIdx.x * 2048 + 5, FS_NOW());
-  if (tid == 0) {
-    uint32_t sh = kNoHist;
-    if (th > 1u) {
-      const uint32_t range = top - th;
-      sh = range == 0u ? 0u : (uint32_t)max(0, 32 - __clz((int)range) - 12);
-    }
-    st_ag(&a.roww[r * kRowWords + kRwShift], sh);
-    wait_vm();  // the shift is visible before theta: whoever sees theta sees the shift
-    st_ag(&a.roww[r * kRowWords + kRwTheta], th);
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void decode_task(const ScanLds& L, int rows, uint32_t n_samp,
-                                            uint32_t n_tasks, uint32_t task, int& row, int& j) {
-  row = -1;
-  j = 0;
-  if (task < n_tasks) {
-    const uint32_t c = task - n_samp;
-    row = upper_index(L.cpre, rows, c);
-    j = (int)(c - L.cpre[row]);
-  }
-}
-
-// The claim of phase P + 1, written by the writer in phase P; false if it never arrived
-// (status bit 2; cannot happen while the writer runs).
-__device__ __forceinline__ bool wait_claim(const FsArgs& a, const ScanLds& L, uint32_t phase,
-                                           uint32_t& task) {
-  unsigned long long cl;
-  uint32_t spins = 0;
-  while ((uint32_t)((cl = __hip_atomic_load(&L.claim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >> 32) !=
-         phase + 1u) {
-    if (++spins > kSpin) {
-      if ((threadIdx.x & 63) == 0) atomicOr(&a.ctrl[kCtStatus], 2u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  task = (uint32_t)cl;
-  return true;
-}
-
-// theta of row r and its histogram shift (sampled rows wait until the row's last sample
-// task has set them; the shift is stored before theta).
-__device__ __forceinline__ uint32_t row_theta(const FsArgs& a, const ScanLds& L, int r, uint32_t& sh) {
-  sh = kNoHist;
-  if (row_samples(L.rn[r]) == 0) return 1u;
-  uint32_t th, spins = 0;
-  while ((th = ld_ag(&a.roww[r * kRowWords + kRwTheta])) == 0u) {
-    if (++spins > kSpin) {
-      if ((threadIdx.x & 63) == 0) atomicOr(&a.ctrl[kCtStatus], 1u);
-      return 1u;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  sh = ld_ag(&a.roww[r * kRowWords + kRwShift]);
-  return th;
-}
-
-// The 15 streaming waves: score each chunk's columns and keep, per group of 64 columns,
-// the keys >= theta in column order in the stage, issuing the next chunk's loads into each
-// buffer as soon as it is processed.  Wave 0 claims chunks two phases ahead: the claim of
-// phase P + 2 is issued in phase P just before that wave's loads of phase P + 1, so by
-// the time it is read (after those loads' first buffer has been waited for) it has
-// returned, and only loads precede it in the wave's memory counter.
-template <bool CAND>
-__device__ __forceinline__ void stream_loop(const FsArgs& a, ScanLds& L, uint32_t t,
-                                            uint32_t n_samp, uint32_t n_tasks) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int quarter = lane & 3, ent = lane >> 2;
-  const int cg = 16 * quarter + ent;               // column of this lane inside a group
-  const int src = 4 * (lane & 15) + (lane >> 4);   // lane owning column `lane` of a group
-  int cur_row, cur_j;
-  decode_task(L, a.rows, n_samp, n_tasks, t, cur_row, cur_j);
-  ScanGroup buf[kG];
-  int q_row = -1;
-  uint32_t th = 1u;
-  bf16x2 q[16];
-  auto issue = [&](int u, int row, int j) {
-    const int n = L.rn[row];
-    if (n == 0) return;
-    const int b = a.row0 + row;
-    const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
-    const int g = j * kChunk + (u * kSW + wave) * 64;
-    buf[u] = load_group<CAND>(a.codes, a.scale, cand_row, L.rbase[row], min(g, n - 1), n - 1, ent,
-                              quarter);
-  };
-  uint32_t nxt = 0xffffffffu;  // wave 0, lane 0: the claim in flight (the task after next)
-  if (cur_row >= 0) {
-    if (wave == 0 && lane == 0) nxt = add_ag(&a.ctrl[kCtTask], 1u);
-    asm volatile("" ::: "memory");  // the claim is issued before the loads
-#pragma unroll
-    for (int u = 0; u < kG; ++u) issue(u, cur_row, cur_j);
-  }
-  uint32_t phase = 0;
-  bool pending = false;  // the writer still has the last chunk to write
-  while (cur_row >= 0 || pending) {
-    int next_row = -1, next_j = 0;
-    pending = cur_row >= 0;
-    if (cur_row >= 0) {
-      const int n = L.rn[cur_row];
-      if (q_row != cur_row) {
-        load_q(a.q + (size_t)(a.row0 + cur_row) * kDIdx, quarter, q);
-        uint32_t sh;
-        th = row_theta(a, L, cur_row, sh);
-        if (wave == 0 && lane == 0) {
-          L.rth[cur_row] = th;
-          L.rsh[cur_row] = sh;
-        }
-        q_row = cur_row;
-      }
-      const int par = (int)(phase & 1u);
-#pragma unroll
-      for (int u = 0; u < kG; ++u) {
-        const int g = u * kSW + wave;                  // group index inside the chunk
-        const int col = cur_j * kChunk + g * 64 + cg;
-        bool cand = false;
-        uint32_t key = 0u;
-        if (n > 0) {
-          const float score = group_score(buf[u], q, quarter);
-          key = score_key(score);
-          cand = col < n && buf[u].own_ok && key >= th;
-        }
-        // the candidates of this group in column order
-        const bool by_col = __shfl(cand ? 1 : 0, src) != 0;
-        const unsigned long long cmask = __ballot(by_col);
-        if (cand) {
-          const uint32_t rank = (uint32_t)__popcll(cmask & ((1ull << cg) - 1ull));
-          L.skey[par][g][rank] = key;
-          L.soff[par][g][rank] = (uint16_t)(g * 64 + cg);
-        }
-        if (lane == 0) L.scnt[par][g] = (uint32_t)__popcll(cmask);
-        if (u == 0) {
-          if (wave == 0 && lane == 0) FS_TR(blockIdx.x * 2048 + 600 + 3 * (int)min(phase, 99u), FS_NOW());
-          uint32_t tn = 0xffffffffu;
-          if (wave == 0) {
-            if (lane == 0) {  // publish the next task, then claim the one after it
-              L.task[(phase + 1u) & 3u] = nxt;
-              __hip_atomic_store(&L.claim, ((unsigned long long)(phase + 1u) << 32) | nxt, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-              tn = nxt;
-              nxt = nxt < n_tasks ? add_ag(&a.ctrl[kCtTask], 1u) : 0xffffffffu;
-            }
-            asm volatile("" ::: "memory");  // the claim is issued before the loads below
-            tn = __builtin_amdgcn_readfirstlane(tn);
-            decode_task(L, a.rows, n_samp, n_tasks, tn, next_row, next_j);
-          } else if (wait_claim(a, L, phase, tn)) {
-            decode_task(L, a.rows, n_samp, n_tasks, tn, next_row, next_j);
-          }
-          if (wave == 0 && lane == 0) FS_TR(blockIdx.x * 2048 + 601 + 3 * (int)min(phase, 99u), FS_NOW());
-        }
-        if (next_row >= 0) issue(u, next_row, next_j);  // this buffer is free again
-      }
-    }
-    if (wave == 0 && lane == 0) FS_TR(blockIdx.x * 2048 + 602 + 3 * (int)min(phase, 99u), FS_NOW());
-    ++phase;
-    cur_row = next_row;
-    cur_j = next_j;
     __syncthreads();
-  }
-}
-
-// The writer wave: writes the candidates of the chunk streamed in the previous phase (the
-// stage, in column order) to that chunk's own region of the row's store (chunk j at
-// j * 1920: no reservation), its count, each candidate into the row's histogram and, when
-// chained, its Reindex re-scores.  Nothing it issues returns a value, so its stores never
-// hold up anything.
-template <bool CAND>
-__device__ __forceinline__ void writer_loop(const FsArgs& a, ScanLds& L, uint32_t t,
-                                            uint32_t n_samp, uint32_t n_tasks) {
-  const int lane = threadIdx.x & 63;
-  const int quarter = lane & 3, ent = lane >> 2;
-  int cur_row, cur_j;
-  decode_task(L, a.rows, n_samp, n_tasks, t, cur_row, cur_j);
-  int w_row = -1, w_j = 0, w_par = 0;   // chunk whose candidates wait in the stage w_par
-  int re_row = -1;
-  uint32_t phase = 0;
-  while (cur_row >= 0 || w_row >= 0) {
-    const int tb = blockIdx.x * 2048 + 16 + 5 * (int)min(phase, 99u);
-    if (lane == 0) FS_TR(tb, FS_NOW() | ((unsigned long long)(w_row + 1) << 52));
-    if (w_row >= 0) {
-      const int b = a.row0 + w_row;
-      // candidates of the chunk per group -> their places in the chunk's region
-      const uint32_t cnt = lane < kCW ? L.scnt[w_par][lane] : 0u;
-      const uint32_t incl = wave_incl_scan(cnt);
-      const uint32_t n = __builtin_amdgcn_readlane(incl, 63);
-      if (lane < kCW) L.gpre[lane] = incl - cnt;
-      if (lane == 0) L.gpre[kCW] = n;
-      const uint32_t th = L.rth[w_row], sh = L.rsh[w_row];
-      const size_t rb = (size_t)w_row * a.cap + (size_t)w_j * kChunk;
-      uint32_t* hist = a.rhist + (size_t)w_row * kBins;
-      for (uint32_t e = lane; e < n; e += 64) {
-        const int g = upper_index(L.gpre, kCW, e);
-        const uint32_t key = L.skey[w_par][g][e - L.gpre[g]];
-        const uint32_t off = L.soff[w_par][g][e - L.gpre[g]];
-        a.ckey[rb + e] = key;
-        a.ccol[rb + e] = (uint32_t)(w_j * kChunk) + off;
-        if (sh != kNoHist) atomicAdd(&hist[min((key - th) >> sh, (uint32_t)(kBins - 1))], 1u);
-      }
-      if (lane == 0) {
-        a.ccnt[(size_t)w_row * a.runs + w_j] = n;
-        FS_TR(tb + 3, FS_NOW() | ((unsigned long long)n << 48));
-      }
-      if (!CAND && a.n_re > 0 && n > 0u) {
-        // the Reindex layers' re-scores of this chunk's candidates (the scan's arithmetic)
-        if (re_row != w_row) {
-          for (int i = lane; i < a.n_re * (kDIdx / 8); i += 64) {
-            const int l = i / (kDIdx / 8), part = i % (kDIdx / 8);
-            reinterpret_cast<uint4*>(L.qre)[i] =
-                reinterpret_cast<const uint4*>(a.q_re + ((size_t)l * a.batch + b) * kDIdx)[part];
-          }
-          re_row = w_row;
-        }
-        const int64_t sbase = L.rbase[w_row];
-        for (uint32_t e0 = 0; e0 < n; e0 += 64) {
-          uint4 w4[4];
-          float sc4[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t e = min(e0 + 16u * u + (uint32_t)ent, n - 1u);
-            const int g = upper_index(L.gpre, kCW, e);
-            const int64_t entry = sbase + (int64_t)(w_j * kChunk + L.soff[w_par][g][e - L.gpre[g]]);
-            w4[u] = *reinterpret_cast<const uint4*>(a.codes + entry * kIdxCodeBytes + quarter * 16);
-            sc4[u] = a.scale[entry];
-          }
-          for (int l = 0; l < a.n_re; ++l) {
-            bf16x2 qr[16];
-            unpack_q(reinterpret_cast<const uint4*>(L.qre + l * kDIdx) + quarter * 4, qr);
-            uint32_t* rk = a.rekey + ((size_t)l * a.rows + w_row) * a.cap + (size_t)w_j * kChunk;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              float v = dot32(w4[u], qr);
-              v += __shfl_xor(v, 1);
-              v += __shfl_xor(v, 2);
-              const uint32_t e = e0 + 16u * u + (uint32_t)ent;
-              if (quarter == 0 && e < n) rk[e] = score_key(v * sc4[u]);
-            }
-          }
-        }
+    const uint32_t m = kept;
+    for (uint32_t p0 = 0; p0 < m; p0 += kT / 4) {
+      const uint32_t p = p0 + (uint32_t)(tid >> 2);
+      const uint32_t pc = min(p, m - 1u);
+      const int64_t entry = base + (int64_t)(c0 + L.pick[pc]);
+      const uint4 w = *reinterpret_cast<const uint4*>(a.codes + entry * kIdxCodeBytes + quarter * 16);
+      const float sc = a.scale[entry];
+      for (int l = 0; l < a.n_re; ++l) {
+        bf16x2 qr[16];
+        unpack_q(reinterpret_cast<const uint4*>(L.qre + l * kDIdx) + quarter * 4, qr);
+        float v = dot32(w, qr);
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        if (quarter == 0 && p < m) a.rekey[(size_t)l * a.rows * a.cap + rb + p] = score_key(v * sc);
       }
     }
-    if (lane == 0) FS_TR(tb + 4, FS_NOW());
-    // the chunk streamed in this phase is written out in the next one
-    w_row = cur_row;
-    w_j = cur_j;
-    w_par = (int)(phase & 1u);
-    ++phase;
-    __syncthreads();
-    // the next phase's chunk: published by streaming wave 0 during the phase just ended
-    if (cur_row >= 0) decode_task(L, a.rows, n_samp, n_tasks, L.task[phase & 3u], cur_row, cur_j);
   }
-}
-
-template <bool CAND>
-__global__ __launch_bounds__(kT) void k_fscan(FsArgs a) {
-  __shared__ ScanLds L;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  if (tid == 0) FS_TR(blockIdx.x * 2048, FS_NOW());
-  // per-row facts and the task layout: every row's sample tasks, then its chunks
-  if (tid == 0) L.claim = add_ag(&a.ctrl[kCtTask], 1u);
-  {
-    uint32_t ns = 0, nc = 0;
-    if (tid < a.rows) {
-      const int b = a.row0 + tid;
-      const int n = max(0, min(a.n_valid[b], a.n_cols));
-      L.rn[tid] = n;
-      L.rbase[tid] = a.seq_base[b];
-      ns = (uint32_t)row_samples(n);
-      nc = (uint32_t)row_chunks(n);
-    }
-    uint32_t tns, tnc;
-    const uint32_t ps = block_exclusive_scan(ns, L.c.scan, &tns);
-    const uint32_t pc = block_exclusive_scan(nc, L.c.scan, &tnc);
-    if (tid < a.rows) {
-      L.spre[tid] = ps;
-      L.cpre[tid] = pc;
-    }
-    if (tid == 0) {
-      L.spre[a.rows] = tns;
-      L.cpre[a.rows] = tnc;
-    }
-  }
-  __syncthreads();
-  const uint32_t n_samp = L.spre[a.rows], n_tasks = n_samp + L.cpre[a.rows];
-  uint32_t t = (uint32_t)L.claim;
-  // sample tasks (whole workgroup, one at a time)
-  while (t < n_samp) {
-    const int r = upper_index(L.spre, a.rows, t);
-    __syncthreads();
-    if (tid == 0) L.claim = add_ag(&a.ctrl[kCtTask], 1u);
-    sample_task<CAND>(a, L, r, (int)(t - L.spre[r]));
-    __syncthreads();
-    t = (uint32_t)L.claim;
-  }
-  if (tid == 0) FS_TR(blockIdx.x * 2048 + 1, FS_NOW());
-  // chunk tasks: in phase P the streaming waves score chunk t_P into the stage P & 1
-  // while the writer wave claims t_{P+1} (published in L.claim with tag P + 1) and writes
-  // out the candidates of t_{P-1}; each kind of wave runs a loop of its own (keeping only
-  // its own registers) and both meet at one barrier per phase.
-  if (wave < kSW) stream_loop<CAND>(a, L, t, n_samp, n_tasks);
-  else writer_loop<CAND>(a, L, t, n_samp, n_tasks);
+  if (tid == 0) FS_TR(blockIdx.x * 8 + 4, FS_NOW());
 }
 
 // ------------------------------------------------------------------ k_fpick
@@ -827,7 +799,7 @@ __global__ __launch_bounds__(kT) void k_fscan(FsArgs a) {
 // a bitmap whose prefix gives each winner's output position, and writes the winners of
 // its own slice of chunks.  The chained selections each go to one workgroup of the row.
 struct PickLds {
-  uint32_t key[kMaxCand];                 // slow path: scratch; Reindex: pool re-scores
+  uint32_t key[kMaxCand];                 // each candidate's store slot; Reindex: pool re-scores
   uint32_t off[kMaxRuns + 1];             // first candidate of each chunk (dense, col order)
   uint16_t blk[kMaxCand / 32];            // chunk of the first candidate of each 32-block
   uint32_t bm[kMaxCand / 32 + 1];         // winners, one bit per candidate
@@ -866,63 +838,16 @@ __device__ __forceinline__ void bitmap_prefix(const uint32_t* bm, uint32_t* wp, 
 }
 
 // Marks in L.bm the top-k of the m candidates (key kv[u] of candidate i = threadIdx.x +
-// kT * u, ties to the lower index, i.e. the lower column).  With the row's histogram in
-// L.c.hist (candidates per bin of (key - theta) >> sh, the last bin open-ended) the bin
-// of the k-th key is read off it: keys above the bin win by ballot and the <= 64 keys in
-// it are ranked directly.  Otherwise (no histogram, the last bin or a crowded one) the
-// general search runs.  Returns the number selected.  Whole workgroup; ends with a barrier.
-__device__ __forceinline__ uint32_t pick_marked(const uint32_t (&kv)[kU], int m, uint32_t k,
-                                                uint32_t theta, uint32_t sh, PickLds& L) {
+// kT * u, ties to the lower index, i.e. the lower column).  Returns the number selected and
+// the threshold.  Whole workgroup; ends with a barrier.
+__device__ __forceinline__ Thr pick_marked(const uint32_t (&kv)[kU], int m, uint32_t k, PickLds& L,
+                                          int tr = -1) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t need = min(k, (uint32_t)m);
-  if (sh != kNoHist && need < (uint32_t)m) {
-    find_bin_block<kBins / kT>(L.c.hist, need, L.c.scan, L.c.res);  // ends with a barrier
-    const uint32_t d = L.c.res[0], above = L.c.res[1], in_bin = L.c.hist[d];
-    if (d < (uint32_t)(kBins - 1) && in_bin <= 64u) {
-      const uint32_t lo = theta + (d << sh);
-      const uint32_t hi = lo + ((1u << sh) - 1u);
-      if (tid == 0) L.c.misc[0] = 0u;
-      __syncthreads();
+  uint32_t c = 0u, mx = 0u;  // every candidate key is non-zero: the count is m
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i = tid + kT * u;
-        const uint32_t key = i < m ? kv[u] : 0u;
-        const unsigned long long msk = __ballot(key > hi);
-        if (lane == 0) {
-          L.bm[(kT * u + 64 * wave) >> 5] = (uint32_t)msk;
-          L.bm[((kT * u + 64 * wave) >> 5) + 1] = (uint32_t)(msk >> 32);
-        }
-        if (key >= lo && key <= hi) {
-          const uint32_t slot = atomicAdd(&L.c.misc[0], 1u);
-          if (slot < 64u) {
-            L.c.pub[slot] = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)i;
-            L.pidx[slot] = (uint32_t)i;
-          }
-        }
-      }
-      if (tid == 0) L.bm[kMaxCand / 32] = 0u;
-      __syncthreads();
-      if (wave == 0) {  // the (need - above) best members of the bin win
-        const uint32_t nt = min(L.c.misc[0], 64u);
-        const unsigned long long cc = (uint32_t)lane < nt ? L.c.pub[lane] : 0ull;
-        const uint32_t chi = (uint32_t)(cc >> 32), clo = (uint32_t)cc;
-        uint32_t rk = 0;
-        for (uint32_t j = 0; j < nt; ++j) {
-          const uint32_t ohi = __builtin_amdgcn_readlane(chi, j);
-          const uint32_t olo = __builtin_amdgcn_readlane(clo, j);
-          rk += (ohi > chi || (ohi == chi && olo > clo)) ? 1u : 0u;
-        }
-        if ((uint32_t)lane < nt && rk < need - above) {
-          const uint32_t i = L.pidx[lane];
-          atomicOr(&L.bm[i >> 5], 1u << (i & 31));
-        }
-      }
-      __syncthreads();
-      return need;
-    }
-  }
-  const Thr t = find_thr<kU>([&](int u, int) { return kv[u]; }, [&](int, int i) { return (uint32_t)i; },
-                             m, k, L.c);
+  for (int u = 0; u < kU; ++u) mx = max(mx, kv[u]);
+  block_sum_max(c, mx, L.c);
+  const Thr t = find_thr_lean<kU>(kv, [&](int, int i) { return (uint32_t)i; }, m, k, (uint32_t)m, mx, L.c);
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int i = tid + kT * u;
@@ -934,7 +859,7 @@ __device__ __forceinline__ uint32_t pick_marked(const uint32_t (&kv)[kU], int m,
   }
   if (tid == 0) L.bm[kMaxCand / 32] = 0u;
   __syncthreads();
-  return t.nsel;
+  return t;
 }
 
 // Entries p < n of `row` hold pool positions (written by this workgroup); replaces each by
@@ -957,8 +882,8 @@ __device__ __forceinline__ void deref_pool(int32_t* row, int n, const int32_t* p
     if (tid + u * kT < n) row[tid + u * kT] = (int32_t)v[u];
 }
 
-// Slow path of a row whose theta turned out too high or too low: this workgroup alone
-// scores every column again and stores every key at store index = column (0 for a
+// Slow path of a row whose segments left out a key of its top-k (or whose candidates
+// exceed what the selection holds): this workgroup alone scores every column again and stores every key at store index = column (0 for a
 // candidate hole), with the Reindex re-scores when chained.
 template <bool CAND>
 __device__ __forceinline__ void rescan_row(const FsArgs& a, int r, int n) {
@@ -990,8 +915,8 @@ __device__ __forceinline__ void rescan_row(const FsArgs& a, int r, int n) {
   __syncthreads();
 }
 
-// The slow path of a row (its theta was too high, or too many keys passed it): every key
-// of the row again, the store then in column order (store index = column), and every
+// The slow path of a row (a segment left out one of its top-k, or too many candidates):
+// every key of the row again, the store then in column order (store index = column), and every
 // selection of the row from global memory by this one workgroup.  Out of line, with the
 // arguments by value, so the fast path keeps its registers.
 template <bool CAND>
@@ -1074,25 +999,39 @@ __device__ __noinline__ void slow_select(FsArgs a, PickLds* Lp, int r) {
 // position = winner rank among the candidates; ties to the lower position), written as
 // pool entries in pool order.  L.bm / L.wp mark the pool; gs[u] is candidate i's place in
 // the store.
-// Store slot of candidate i (chunk j's run starts at j * 1920).
+// Index of the set bit of rank r (from 0) of a bitmap whose word prefix wp has words + 1
+// entries (r < wp[words]).
+__device__ __forceinline__ uint32_t nth_bit(const uint32_t* bm, const uint32_t* wp, int words, uint32_t r) {
+  const int w = upper_index(wp, words, r);
+  uint32_t x = bm[w];
+  for (uint32_t q = r - wp[w]; q > 0u; --q) x &= x - 1u;  // drop the lower set bits
+  return (uint32_t)w * 32u + (uint32_t)__builtin_ctz(x);
+}
+
+// Store slot of candidate i (segment j's run starts at j * 16384).
 __device__ __forceinline__ uint32_t slot_of(const PickLds& L, uint32_t i) {
   const int j = chunk_of(L, i);
-  return (uint32_t)j * kChunk + (i - L.off[j]);
+  return (uint32_t)j * kSeg + (i - L.off[j]);
 }
 
 template <bool CAND>
 __device__ __forceinline__ void pick_reindex(const FsArgs& a, PickLds& L, int r, int l, int m, uint32_t P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int trb = (1 << 20) - 262144 + (int)blockIdx.x * 16;
+  if (tid == 0) FS_TR(trb + 4, FS_NOW());
   const int b = a.row0 + r;
   const uint32_t* rk = a.rekey + ((size_t)l * a.rows + r) * a.cap;
   const uint32_t* cc = a.ccol + (size_t)r * a.cap;
-  {
+  {  // L.key holds each candidate's store slot: read them all before the pool order overwrites it
     uint32_t v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = tid + kT * u;
-      v[u] = (i < m && bit_at(L.bm, (uint32_t)i)) ? rk[slot_of(L, (uint32_t)i)] : 0u;
+      v[u] = (i < m && bit_at(L.bm, (uint32_t)i)) ? L.key[i] : 0xffffffffu;
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = v[u] != 0xffffffffu ? rk[v[u]] : 0u;
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = tid + kT * u;
@@ -1100,12 +1039,22 @@ __device__ __forceinline__ void pick_reindex(const FsArgs& a, PickLds& L, int r,
     }
   }
   __syncthreads();
-  const Thr tr = find_thr<kPU>([&](int, int p) { return L.key[p]; }, [&](int, int p) { return (uint32_t)p; },
-                               (int)P, (uint32_t)a.re_k, L.c, (1 << 20) - 131072 + (int)blockIdx.x * 16);
+  if (tid == 0) FS_TR(trb, FS_NOW());
+  uint32_t kk[kPU], c = 0u, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < kPU; ++u) {
+    kk[u] = tid + kT * u < (int)P ? L.key[tid + kT * u] : 0u;
+    c += kk[u] != 0u ? 1u : 0u;
+    mx = max(mx, kk[u]);
+  }
+  block_sum_max(c, mx, L.c);
+  const Thr tr = find_thr_lean<kPU>(kk, [&](int, int p) { return (uint32_t)p; }, (int)P, (uint32_t)a.re_k, c,
+                                    mx, L.c);
+  if (tid == 0) FS_TR(trb + 1, FS_NOW());
 #pragma unroll
   for (int u = 0; u < kPU; ++u) {
     const int p = tid + kT * u;
-    const unsigned long long msk = __ballot(p < (int)P && selected(tr, L.key[p], (uint32_t)p));
+    const unsigned long long msk = __ballot(p < (int)P && selected(tr, kk[u], (uint32_t)p));
     if (lane == 0) {
       L.rbm[(kT * u + 64 * wave) >> 5] = (uint32_t)msk;
       L.rbm[((kT * u + 64 * wave) >> 5) + 1] = (uint32_t)(msk >> 32);
@@ -1117,174 +1066,164 @@ __device__ __forceinline__ void pick_reindex(const FsArgs& a, PickLds& L, int r,
   int32_t* orr = a.re_out + ((size_t)l * a.batch + b) * a.re_k;
   float* srr = a.re_sout ? a.re_sout + ((size_t)l * a.batch + b) * a.re_k : nullptr;
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
-  for (uint32_t i = tid; i < (uint32_t)m; i += kT) {  // few winners: one load each at most
-    if (!bit_at(L.bm, i)) continue;
-    const uint32_t p = bits_before(L.bm, L.wp, i);
-    if (!bit_at(L.rbm, p)) continue;
-    const uint32_t rank = bits_before(L.rbm, L.rwp, p);
+  if (tid == 0) FS_TR(trb + 2, FS_NOW());
+  // a thread per output rank: its pool position, that winner's candidate index, its column
+  for (uint32_t q = tid; q < tr.nsel; q += kT) {
+    const uint32_t p = nth_bit(L.rbm, L.rwp, ((int)P + 31) / 32, q);
+    const uint32_t i = nth_bit(L.bm, L.wp, (m + 31) / 32, p);
     const uint32_t col = cc[slot_of(L, i)];
-    orr[rank] = CAND ? cand_row[col] : (int32_t)col;
-    if (srr) srr[rank] = key_score(L.key[p]);
+    orr[q] = CAND ? cand_row[col] : (int32_t)col;
+    if (srr) srr[q] = key_score(L.key[p]);
   }
   for (int p = (int)tr.nsel + tid; p < a.re_k; p += kT) {
     orr[p] = -1;
     if (srr) srr[p] = -__builtin_inff();
   }
+  if (tid == 0) FS_TR(trb + 3, FS_NOW());
   __syncthreads();
 }
 
 // The Full layer's own top-own_k of the m candidates of row r (ties to the lower column), in
 // column order.
 template <bool CAND>
-__device__ __forceinline__ void pick_own(const FsArgs& a, PickLds& L, int r, int m, uint32_t theta,
-                                         uint32_t sh) {
+__device__ __forceinline__ void pick_own(const FsArgs& a, PickLds& L, int r, int m) {
   const int tid = threadIdx.x;
   const int b = a.row0 + r;
   const uint32_t* ck = a.ckey + (size_t)r * a.cap;
   const uint32_t* cc = a.ccol + (size_t)r * a.cap;
-  const uint32_t* hist = a.rhist + (size_t)r * kBins;
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
-  uint32_t kv[kU];
+  uint32_t kv[kU];  // L.key holds each candidate's store slot
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int i = tid + kT * u;
-    kv[u] = i < m ? ck[slot_of(L, (uint32_t)i)] : 0u;
-  }
+  for (int u = 0; u < kU; ++u) kv[u] = tid + kT * u < m ? L.key[tid + kT * u] : 0u;
 #pragma unroll
-  for (int u = 0; u < kBins / kT; ++u) L.c.hist[tid + kT * u] = sh != kNoHist ? hist[tid + kT * u] : 0u;
-  __syncthreads();
-  const uint32_t n_own = pick_marked(kv, m, (uint32_t)a.own_k, theta, sh, L);
+  for (int u = 0; u < kU; ++u) kv[u] = tid + kT * u < m ? ck[kv[u]] : 0u;
+  const uint32_t n_own = pick_marked(kv, m, (uint32_t)a.own_k, L).nsel;
   bitmap_prefix(L.bm, L.wp, m, L.c);
   int32_t* own = a.own_out + (size_t)b * a.own_k;
-  for (uint32_t i = tid; i < (uint32_t)m; i += kT) {
-    if (!bit_at(L.bm, i)) continue;
-    const uint32_t col = cc[slot_of(L, i)];
-    own[bits_before(L.bm, L.wp, i)] = CAND ? cand_row[col] : (int32_t)col;
+  for (uint32_t q = tid; q < n_own; q += kT) {  // a thread per output rank
+    const uint32_t col = cc[slot_of(L, nth_bit(L.bm, L.wp, (m + 31) / 32, q))];
+    own[q] = CAND ? cand_row[col] : (int32_t)col;
   }
   for (int p = (int)n_own + tid; p < a.own_k; p += kT) own[p] = -1;
 }
 
 // Grid: rows x (S + R): per row, S workgroups that each write a slice of the pool, then R
 // workgroups with one chained selection each (Reindex layer 0 .. n_re - 1, then the Full
-// layer's own top-k).
+// layer's own top-k).  The candidates are exact when no segment that left keys out had all
+// of its kept keys selected (then its best left-out key is below the threshold); otherwise,
+// or when they exceed what the selection holds, the row takes the slow path.
 template <bool CAND>
 __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
   __shared__ PickLds L;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = a.n_re + (a.own_k > 0 ? 1 : 0);
   const int r = (int)blockIdx.x / (S + R), s = (int)blockIdx.x % (S + R);
   const int tb = (1 << 20) - 65536 + (int)blockIdx.x * 8;
   if (tid == 0) FS_TR(tb, FS_NOW());
   const int b = a.row0 + r;
   const int n_row = max(0, min(a.n_valid[b], a.n_cols));
-  const int nch = row_chunks(n_row);
+  const int nsg = row_segs(n_row);
   const uint32_t* ck = a.ckey + (size_t)r * a.cap;
   const uint32_t* cc = a.ccol + (size_t)r * a.cap;
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
   int32_t* orow = a.out + (size_t)b * a.k;
   float* srow = a.sout ? a.sout + (size_t)b * a.k : nullptr;
-  uint32_t* hist = a.rhist + (size_t)r * kBins;
-  if (blockIdx.x == 0 && tid == 0) a.ctrl[kCtTask] = 0u;  // the scan that counted on it has ended
-  // one round of loads: theta, the shift, the histogram and each chunk's count
-  const bool sampled = row_samples(n_row) > 0;
-  const uint32_t theta = sampled ? a.roww[r * kRowWords + kRwTheta] : 1u;
-  const uint32_t sh = sampled ? a.roww[r * kRowWords + kRwShift] : kNoHist;
-  uint32_t h[kBins / kT];
-#pragma unroll
-  for (int u = 0; u < kBins / kT; ++u) h[u] = sampled ? hist[tid + kT * u] : 0u;  // read again by the own-top-k workgroup
-  const uint32_t c0 = 2 * tid < nch ? a.ccnt[(size_t)r * a.runs + 2 * tid] : 0u;
-  const uint32_t c1 = 2 * tid + 1 < nch ? a.ccnt[(size_t)r * a.runs + 2 * tid + 1] : 0u;
-#pragma unroll
-  for (int u = 0; u < kBins / kT; ++u) L.c.hist[tid + kT * u] = h[u];
+  // each segment's count (thread t: segments 2t, 2t + 1), their prefix = dense offsets
+  const uint32_t r0 = 2 * tid < nsg ? a.ccnt[(size_t)r * a.runs + 2 * tid] : 0u;
+  const uint32_t r1 = 2 * tid + 1 < nsg ? a.ccnt[(size_t)r * a.runs + 2 * tid + 1] : 0u;
+  const uint32_t c0 = r0 & ~kTrunc, c1 = r1 & ~kTrunc;
   uint32_t m_all;
   {
     const uint32_t e = block_exclusive_scan(c0 + c1, L.c.scan, &m_all);
-    if (2 * tid < nch) L.off[2 * tid] = e;
-    if (2 * tid + 1 < nch) L.off[2 * tid + 1] = e + c0;
-    if (tid == 0) L.off[nch] = m_all;
+    m_all = uni(m_all);
+    if (2 * tid < nsg) L.off[2 * tid] = e;
+    if (2 * tid + 1 < nsg) L.off[2 * tid + 1] = e + c0;
+    if (tid == 0) L.off[nsg] = m_all;
   }
   __syncthreads();
   if (tid == 0) FS_TR(tb + 5, FS_NOW());
-  const bool fast =
-      m_all <= (uint32_t)kMaxCand && !(theta > 1u && m_all < (uint32_t)min(a.k, n_row));
+  bool fast = m_all <= (uint32_t)kMaxCand;
   if (fast) {
     const int m = (int)m_all;
-    for (int w = tid; w < (m + 31) / 32; w += kT) L.blk[w] = (uint16_t)upper_index(L.off, nch, 32u * w);
+    for (int w = tid; w < (m + 31) / 32; w += kT) L.blk[w] = (uint16_t)upper_index(L.off, nsg, 32u * w);
+    // each candidate's store slot (a wave per segment)
+    for (int j = wave; j < nsg; j += kNW) {
+      const uint32_t o = L.off[j], c = L.off[j + 1] - o;
+      for (uint32_t e = lane; e < c; e += 64) L.key[o + e] = (uint32_t)j * kSeg + e;
+    }
     __syncthreads();
     if (tid == 0) FS_TR(tb + 6, FS_NOW());
-    // every candidate key of the row (candidate i = tid + kT * u), then the pool (or the only
-    // selection) marked in L.bm
+    // every candidate key of the row (candidate i = tid + kT * u, all loads in flight at
+    // once), then the pool (or the only selection) marked in L.bm
     uint32_t n_pool;
     {
       uint32_t kv[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int i = tid + kT * u;
-        kv[u] = i < m ? ck[slot_of(L, (uint32_t)i)] : 0u;
+        kv[u] = i < m ? L.key[i] : 0u;
       }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) kv[u] = tid + kT * u < m ? ck[kv[u]] : 0u;
       if (tid == 0) FS_TR(tb + 1, FS_NOW());
-      n_pool = pick_marked(kv, m, (uint32_t)a.k, theta, sh, L);
+      n_pool = pick_marked(kv, m, (uint32_t)a.k, L, (1 << 20) - 131072 + (int)blockIdx.x * 16).nsel;
     }
     bitmap_prefix(L.bm, L.wp, m, L.c);
+    // a truncated segment whose kept keys all won may have left out a winner
+    bool bad = false;
+    if (2 * tid < nsg && (r0 & kTrunc) &&
+        bits_before(L.bm, L.wp, L.off[2 * tid + 1]) - bits_before(L.bm, L.wp, L.off[2 * tid]) == c0)
+      bad = true;
+    if (2 * tid + 1 < nsg && (r1 & kTrunc) &&
+        bits_before(L.bm, L.wp, L.off[2 * tid + 2]) - bits_before(L.bm, L.wp, L.off[2 * tid + 1]) == c1)
+      bad = true;
+    fast = !__syncthreads_or(bad);
     if (tid == 0) FS_TR(tb + 2, FS_NOW());
-    if (s < S) {  // this workgroup's slice of chunks
-      const int j0 = (int)((long long)s * nch / S), j1 = (int)((long long)(s + 1) * nch / S);
-      const uint32_t i1 = L.off[j1];
-      for (uint32_t i = L.off[j0] + tid; i < i1; i += kT) {
-        if (!bit_at(L.bm, i)) continue;
-        const uint32_t slot = slot_of(L, i);
-        const uint32_t col = cc[slot];
-        const uint32_t pos = bits_before(L.bm, L.wp, i);
-        orow[pos] = CAND ? cand_row[col] : (int32_t)col;
-        if (srow) srow[pos] = key_score(ck[slot]);
-      }
-      if (s == 0)
-        for (int p = (int)n_pool + tid; p < a.k; p += kT) {
-          orow[p] = -1;
-          if (srow) srow[p] = -__builtin_inff();
+    if (fast) {
+      if (s < S) {  // this workgroup's slice of the candidates
+        const uint32_t i0 = (uint32_t)((long long)s * m / S), i1 = (uint32_t)((long long)(s + 1) * m / S);
+        for (uint32_t i = i0 + tid; i < i1; i += kT) {
+          if (!bit_at(L.bm, i)) continue;
+          const uint32_t slot = slot_of(L, i);
+          const uint32_t col = cc[slot];
+          const uint32_t pos = bits_before(L.bm, L.wp, i);
+          orow[pos] = CAND ? cand_row[col] : (int32_t)col;
+          if (srow) srow[pos] = key_score(ck[slot]);
         }
-      if (tid == 0) FS_TR(tb + 3, FS_NOW());
-    } else if (s - S < a.n_re) {
-      pick_reindex<CAND>(a, L, r, s - S, m, n_pool);
-    } else {
-      pick_own<CAND>(a, L, r, m, theta, sh);
+        if (s == 0)
+          for (int p = (int)n_pool + tid; p < a.k; p += kT) {
+            orow[p] = -1;
+            if (srow) srow[p] = -__builtin_inff();
+          }
+        if (tid == 0) FS_TR(tb + 3, FS_NOW());
+      } else if (s - S < a.n_re) {
+        pick_reindex<CAND>(a, L, r, s - S, m, n_pool);
+      } else {
+        pick_own<CAND>(a, L, r, m);
+      }
     }
-  } else if (s == 0) {
-    slow_select<CAND>(a, &L, r);
   }
+  if (!fast && s == 0) slow_select<CAND>(a, &L, r);
   if (tid == 0) FS_TR(tb + 4, FS_NOW());
-  // the last workgroup of the row returns the row's counters and histogram to zero (every
-  // workgroup of the row has read them by then)
+  // the last workgroup of the row returns the row's counter to zero
   wait_vm();
   __syncthreads();
   if (tid == 0) L.c.misc[4] = add_ag(&a.roww[r * kRowWords + kRwDone], 1u) == (uint32_t)(S + R - 1) ? 1u : 0u;
   __syncthreads();
-  if (L.c.misc[4] != 0u) {
-    if (sampled)
-      for (int i = tid; i < kBins; i += kT) hist[i] = 0u;
-    if (tid < kRowWords) a.roww[r * kRowWords + tid] = 0u;
-  }
+  if (L.c.misc[4] != 0u && tid < kRowWords) a.roww[r * kRowWords + tid] = 0u;
 }
 
 // ---------------------------------------------------------------------------- host side
 constexpr int kMaxDevices = 64;
 
-// Scan workgroups resident per device at once: the persistent grid's size (correctness
-// does not depend on it).  Immutable device properties, cached once per device.
+// Compute units of the current device (the picking grid's size aims at one workgroup
+// each; correctness does not depend on it).
 int fs_capacity() {
-  static int cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  if (cache[dev] > 0) return cache[dev];
-  int per_cu_a = 0, per_cu_b = 0, n_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_a, reinterpret_cast<const void*>(k_fscan<false>),
-                                                   kT, 0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_b, reinterpret_cast<const void*>(k_fscan<true>),
-                                                   kT, 0) != hipSuccess ||
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  cache[dev] = max(1, min(per_cu_a, per_cu_b)) * n_cu;
-  return cache[dev];
+  return n_cu;
 }
 
 struct FsShape {
@@ -1294,19 +1233,19 @@ struct FsShape {
 
 FsShape fs_shape(int batch, int n_cols, bool chain) {
   FsShape s;
-  s.runs = (n_cols + kChunk - 1) / kChunk;
-  s.cap = (size_t)s.runs * kChunk;
+  s.runs = (n_cols + kSeg - 1) / kSeg;
+  s.cap = (size_t)s.runs * kSeg;
   s.rows_ws = min(batch, chain ? kChainRows : kMaxRows);
   return s;
 }
 
 struct FsParts {
-  uint32_t *ctrl, *roww, *samp, *ccnt, *ckey, *ccol, *rekey, *pmap, *rhist;
+  uint32_t *ctrl, *roww, *ccnt, *ckey, *ccol, *rekey, *pmap;
   size_t bytes;
 };
 
-// Workspace: [ctrl 256 B][per row 64 B][samples][histograms][chunk counts][candidate keys][their
-// columns] and, for a chain, [their Reindex re-scores][pool -> store index].
+// Workspace: [ctrl 256 B][per row 64 B][segment counts][candidate keys][their columns] and,
+// for a chain, [their Reindex re-scores][pool -> store index].
 FsParts fs_carve(char* p, const FsShape& s, bool chain) {
   FsParts f{};
   size_t off = 0;
@@ -1318,8 +1257,6 @@ FsParts fs_carve(char* p, const FsShape& s, bool chain) {
   const size_t R = (size_t)s.rows_ws;
   f.ctrl = take(256);
   f.roww = take(R * kRowWords * 4);
-  f.samp = take(R * kSampRow * 4);
-  f.rhist = take(R * kBins * 4);
   f.ccnt = take(R * s.runs * 4);
   f.ckey = take(R * s.cap * 4);
   f.ccol = take(R * s.cap * 4);
@@ -1344,7 +1281,17 @@ extern "C" int csa2_fs_trace_zero() {
 }
 #endif
 
-bool fsel_fits(int n_cols) { return n_cols >= 1 && n_cols <= kMaxRuns * kChunk; }
+// Rows up to n_cols long whose top-k the filtered selection takes: at most kMaxRuns
+// segments, and the segments' kept keys of the longest such row, at most
+// k + 6 sqrt(k segs) + 5 segs (the sum of seg_keep over its segments), fit the selection.
+bool fsel_fits(int n_cols, int k) {
+  if (n_cols < 1 || n_cols > kMaxRuns * kSeg) return false;
+  if (n_cols <= kMaxCand) return true;
+  const double segs = (double)((n_cols + kSeg - 1) / kSeg);
+  return (double)k + 6.0 * std::sqrt((double)k * segs) + 5.0 * segs <= (double)kMaxCand;
+}
+
+bool fsel_len_ok(int n_cols) { return n_cols >= 1 && n_cols <= kMaxRuns * kSeg; }
 
 size_t fsel_ws_bytes(int batch, int n_cols, bool chain) {
   return fs_carve(nullptr, fs_shape(batch, n_cols, chain), chain).bytes;
@@ -1382,28 +1329,26 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
   a.re_sout = re_sout;
   a.ctrl = f.ctrl;
   a.roww = f.roww;
-  a.samp = f.samp;
   a.ccnt = f.ccnt;
   a.ckey = f.ckey;
   a.ccol = f.ccol;
   a.rekey = f.rekey;
   a.pmap = f.pmap;
-  a.rhist = f.rhist;
   a.cap = s.cap;
   for (int r0 = 0; r0 < batch; r0 += s.rows_ws) {
     a.row0 = r0;
     a.rows = min(s.rows_ws, batch - r0);
-    const long long tasks = (long long)a.rows * (s.runs + kMaxSampTasks);
-    const int grid = (int)min((long long)cap_wg, tasks);
-    // picking workgroups per row: about one per compute unit in all, at most one per chunk
-    const int S = max(1, min(s.runs, cap_wg / a.rows));
+    // picking workgroups per row: about one per compute unit in all, none with fewer than
+    // 256 of the k winners to write
     const int R = a.n_re + (a.own_k > 0 ? 1 : 0);
+    const int S = max(1, min(cap_wg / a.rows - R, (k + 255) / 256));
+    const dim3 g_seg((unsigned)(a.rows * s.runs)), g_pick((unsigned)(a.rows * (S + R)));
     if (cand) {
-      hipLaunchKernelGGL(k_fscan<true>, dim3(grid), dim3(kT), 0, stream, a);
-      hipLaunchKernelGGL(k_fpick<true>, dim3(a.rows * (S + R)), dim3(kT), 0, stream, a, S);
+      hipLaunchKernelGGL(k_fseg<true>, g_seg, dim3(kT), 0, stream, a);
+      hipLaunchKernelGGL(k_fpick<true>, g_pick, dim3(kT), 0, stream, a, S);
     } else {
-      hipLaunchKernelGGL(k_fscan<false>, dim3(grid), dim3(kT), 0, stream, a);
-      hipLaunchKernelGGL(k_fpick<false>, dim3(a.rows * (S + R)), dim3(kT), 0, stream, a, S);
+      hipLaunchKernelGGL(k_fseg<false>, g_seg, dim3(kT), 0, stream, a);
+      hipLaunchKernelGGL(k_fpick<false>, g_pick, dim3(kT), 0, stream, a, S);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -43,16 +43,19 @@ hipError_t two_step(const uint16_t* q_idx, const uint8_t* codes, const float* sc
 // Every layout starts with the 256-byte status block (zero on the long-row path).
 constexpr size_t kStatusBlock = 256;
 
+// Rows the filtered selection may take hold room for either path (which one runs depends
+// on k as well).
 size_t index_topk_ws_bytes(int batch, int n_cols) {
-  if (fsel_fits(n_cols)) return fsel_ws_bytes(batch, n_cols, false);
-  return kStatusBlock + two_step_bytes(batch, n_cols);
+  const size_t two = kStatusBlock + two_step_bytes(batch, n_cols);
+  if (fsel_len_ok(n_cols)) return max(fsel_ws_bytes(batch, n_cols, false), two);
+  return two;
 }
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
                              const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
                              int batch, int n_cols, int k, int32_t* idx_out, float* score_out,
                              void* ws, hipStream_t stream) {
-  if (fsel_fits(n_cols))
+  if (fsel_fits(n_cols, k))
     return launch_fsel(q_idx, codes, scale, seq_base, n_valid, cand, batch, n_cols, k, idx_out,
                        score_out, 0, nullptr, nullptr, 0, 0, nullptr, nullptr, false, ws, stream);
   return two_step(q_idx, codes, scale, seq_base, n_valid, cand, batch, n_cols, k, idx_out,
@@ -62,9 +65,10 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const uint8_t* codes, const 
 // Long rows: [status][two-step part][pool scores f32 batch x pool_k][pool sizes][Reindex
 // part].
 size_t select_chain_ws_bytes(int batch, int n_cols, int pool_k) {
-  if (fsel_fits(n_cols)) return fsel_ws_bytes(batch, n_cols, true);
-  return kStatusBlock + two_step_bytes(batch, n_cols) + align_up((size_t)batch * pool_k * 4, 256) +
-         align_up((size_t)batch * 4, 256) + index_topk_ws_bytes(batch, pool_k);
+  const size_t sep = kStatusBlock + two_step_bytes(batch, n_cols) + align_up((size_t)batch * pool_k * 4, 256) +
+                     align_up((size_t)batch * 4, 256) + index_topk_ws_bytes(batch, pool_k);
+  if (fsel_len_ok(n_cols)) return max(fsel_ws_bytes(batch, n_cols, true), sep);
+  return sep;
 }
 
 hipError_t launch_select_chain(const uint16_t* q_full, const uint8_t* codes, const float* scale,
@@ -73,7 +77,7 @@ hipError_t launch_select_chain(const uint16_t* q_full, const uint8_t* codes, con
                                int k, int32_t* own_out, const uint16_t* q_re, int n_re,
                                int32_t* re_out, float* re_score_out, void* ws,
                                hipStream_t stream) {
-  if (fsel_fits(n_cols))
+  if (fsel_fits(n_cols, pool_k))
     return launch_fsel(q_full, codes, scale, seq_base, n_valid, nullptr, batch, n_cols, pool_k,
                        pool_out, pool_score_out, k, own_out, q_re, n_re, k, re_out, re_score_out,
                        true, ws, stream);
