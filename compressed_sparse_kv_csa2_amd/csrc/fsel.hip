@@ -70,7 +70,8 @@ namespace {
 
 constexpr int kT = 1024;                  // threads per workgroup
 constexpr int kNW = kT / 64;              // waves
-constexpr int kSeg = 16384;               // columns per scan segment (one workgroup, keys in LDS)
+constexpr int kSeg = 16384;               // columns per scan segment at most (keys in LDS)
+constexpr int kSegMin = 1024;             // and at least
 constexpr int kSegU = kSeg / kT;          // segment keys per thread
 constexpr int kMaxCand = 24576;           // candidates the selection holds (LDS + registers)
 constexpr int kU = kMaxCand / kT;         // candidates per thread
@@ -108,6 +109,7 @@ struct FsArgs {
   const int32_t* n_valid;
   const int32_t* cand;        // [batch][n_cols] (Reindex) or null
   int n_cols, runs;           // columns, segments per row at most
+  int seg;                    // columns per segment (a power of two in [1024, 16384])
   int row0, rows, batch;
   int k;
   int32_t* out;               // [batch][k]
@@ -121,11 +123,11 @@ struct FsArgs {
   uint32_t* ctrl;             // status, -, rows re-scanned
   uint32_t* roww;             // [rows][16]: picking workgroups done
   uint32_t* ccnt;             // [rows][runs] candidates of each segment (| kTrunc when truncated)
-  uint32_t* ckey;             // [rows][cap] candidate keys: segment j's run (column order) at j * 16384
+  uint32_t* ckey;             // [rows][cap] candidate keys: segment j's run (column order) at j * seg
   uint32_t* ccol;             // [rows][cap] their columns
   uint32_t* rekey;            // [4][rows][cap] their Reindex re-scores (chain)
   uint32_t* pmap;             // [rows][16384] store index of each pool entry (chain, slow path)
-  size_t cap;                 // per-row store: runs * 16384
+  size_t cap;                 // per-row store: runs * seg
 };
 
 // LDS the exact-threshold search and the ordered emission share.
@@ -610,7 +612,7 @@ __device__ __forceinline__ void emit_ordered(int m, SelF sel, EmitF emit, Core& 
 
 // ------------------------------------------------------------------ shared helpers
 // Segments of a row with n visible columns (one, possibly empty, for n = 0).
-__device__ __forceinline__ int row_segs(int n) { return max(1, (n + kSeg - 1) / kSeg); }
+__device__ __forceinline__ int row_segs(int n, int seg) { return max(1, (n + seg - 1) / seg); }
 
 // Keys a segment of len columns keeps, of a row of n visible columns whose top-k is
 // wanted: every key when the row is short enough for the selection to hold it whole;
@@ -727,8 +729,8 @@ __global__ __launch_bounds__(kT) void k_fseg(FsArgs a) {
   const int r = (int)blockIdx.x / a.runs, j = (int)blockIdx.x % a.runs;
   const int b = a.row0 + r;
   const int n = max(0, min(a.n_valid[b], a.n_cols));
-  if (j >= row_segs(n)) return;
-  const int c0 = j * kSeg, len = max(0, min(n - c0, kSeg));
+  if (j >= row_segs(n, a.seg)) return;
+  const int c0 = j * a.seg, len = max(0, min(n - c0, a.seg));
   const int64_t base = a.seq_base[b];
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
   if (tid == 0) FS_TR(blockIdx.x * 8, FS_NOW());
@@ -750,7 +752,7 @@ __global__ __launch_bounds__(kT) void k_fseg(FsArgs a) {
   for (int u = 0; u < kSegU; ++u) kv[u] = tid + kT * u < len ? L.key[tid + kT * u] : 0u;
   const uint32_t cut = seg_cut(kv, seg_keep(a.k, len, n), cnt, mx, L.c);
   if (tid == 0) FS_TR(blockIdx.x * 8 + 2, FS_NOW());
-  const size_t rb = (size_t)r * a.cap + (size_t)j * kSeg;
+  const size_t rb = (size_t)r * a.cap + (size_t)j * a.seg;
   uint32_t mine = 0u;
 #pragma unroll
   for (int u = 0; u < kSegU; ++u) mine |= (kv[u] != 0u && kv[u] >= cut ? 1u : 0u) << u;
@@ -804,8 +806,8 @@ struct PickLds {
   uint16_t blk[kMaxCand / 32];            // chunk of the first candidate of each 32-block
   uint32_t bm[kMaxCand / 32 + 1];         // winners, one bit per candidate
   uint32_t wp[kMaxCand / 32 + 1];         // winners before each bitmap word (and the total)
-  uint32_t rbm[CSA2_MAX_K / 32 + 1];      // Reindex winners over pool positions
-  uint32_t rwp[CSA2_MAX_K / 32 + 1];
+  uint32_t rbm[kMaxCand / 32 + 1];        // Reindex winners over the candidates
+  uint32_t rwp[kMaxCand / 32 + 1];
   uint32_t pidx[64];                      // candidate index of each directly ranked key
   Core c;
 };
@@ -995,10 +997,6 @@ __device__ __noinline__ void slow_select(FsArgs a, PickLds* Lp, int r) {
   }
 }
 
-// Reindex layer l of row r on the fast path: the top-re_k of the pool's re-scores (pool
-// position = winner rank among the candidates; ties to the lower position), written as
-// pool entries in pool order.  L.bm / L.wp mark the pool; gs[u] is candidate i's place in
-// the store.
 // Index of the set bit of rank r (from 0) of a bitmap whose word prefix wp has words + 1
 // entries (r < wp[words]).
 __device__ __forceinline__ uint32_t nth_bit(const uint32_t* bm, const uint32_t* wp, int words, uint32_t r) {
@@ -1008,72 +1006,57 @@ __device__ __forceinline__ uint32_t nth_bit(const uint32_t* bm, const uint32_t* 
   return (uint32_t)w * 32u + (uint32_t)__builtin_ctz(x);
 }
 
-// Store slot of candidate i (segment j's run starts at j * 16384).
-__device__ __forceinline__ uint32_t slot_of(const PickLds& L, uint32_t i) {
+// Store slot of candidate i (segment j's run starts at j * seg).
+__device__ __forceinline__ uint32_t slot_of(const PickLds& L, uint32_t i, int seg) {
   const int j = chunk_of(L, i);
-  return (uint32_t)j * kSeg + (i - L.off[j]);
+  return (uint32_t)j * (uint32_t)seg + (i - L.off[j]);
 }
 
+// Reindex layer l of row r on the fast path: the top-re_k of the pool's re-scores (ties to
+// the lower pool position), written as pool entries in pool order.  The pool's winners in
+// candidate order are in pool order, so the selection runs over the candidates with every
+// non-winner's re-score taken as 0 (not selectable).  L.key holds each candidate's re-score.
 template <bool CAND>
 __device__ __forceinline__ void pick_reindex(const FsArgs& a, PickLds& L, int r, int l, int m, uint32_t P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int trb = (1 << 20) - 262144 + (int)blockIdx.x * 16;
   if (tid == 0) FS_TR(trb + 4, FS_NOW());
   const int b = a.row0 + r;
-  const uint32_t* rk = a.rekey + ((size_t)l * a.rows + r) * a.cap;
   const uint32_t* cc = a.ccol + (size_t)r * a.cap;
-  {  // L.key holds each candidate's store slot: read them all before the pool order overwrites it
-    uint32_t v[kU];
+  uint32_t kk[kU], c = 0u, mx = 0u;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = tid + kT * u;
-      v[u] = (i < m && bit_at(L.bm, (uint32_t)i)) ? L.key[i] : 0xffffffffu;
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = v[u] != 0xffffffffu ? rk[v[u]] : 0u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = tid + kT * u;
-      if (i < m && bit_at(L.bm, (uint32_t)i)) L.key[bits_before(L.bm, L.wp, (uint32_t)i)] = v[u];
-    }
-  }
-  __syncthreads();
-  if (tid == 0) FS_TR(trb, FS_NOW());
-  uint32_t kk[kPU], c = 0u, mx = 0u;
-#pragma unroll
-  for (int u = 0; u < kPU; ++u) {
-    kk[u] = tid + kT * u < (int)P ? L.key[tid + kT * u] : 0u;
+  for (int u = 0; u < kU; ++u) {
+    const int i = tid + kT * u;
+    kk[u] = (i < m && bit_at(L.bm, (uint32_t)i)) ? L.key[i] : 0u;
     c += kk[u] != 0u ? 1u : 0u;
     mx = max(mx, kk[u]);
   }
   block_sum_max(c, mx, L.c);
-  const Thr tr = find_thr_lean<kPU>(kk, [&](int, int p) { return (uint32_t)p; }, (int)P, (uint32_t)a.re_k, c,
-                                    mx, L.c);
+  if (tid == 0) FS_TR(trb, FS_NOW());
+  const Thr tr = find_thr_lean<kU>(kk, [&](int, int i) { return (uint32_t)i; }, m, (uint32_t)a.re_k, c, mx, L.c);
   if (tid == 0) FS_TR(trb + 1, FS_NOW());
 #pragma unroll
-  for (int u = 0; u < kPU; ++u) {
-    const int p = tid + kT * u;
-    const unsigned long long msk = __ballot(p < (int)P && selected(tr, kk[u], (uint32_t)p));
+  for (int u = 0; u < kU; ++u) {
+    const int i = tid + kT * u;
+    const unsigned long long msk = __ballot(i < m && selected(tr, kk[u], (uint32_t)i));
     if (lane == 0) {
       L.rbm[(kT * u + 64 * wave) >> 5] = (uint32_t)msk;
       L.rbm[((kT * u + 64 * wave) >> 5) + 1] = (uint32_t)(msk >> 32);
     }
   }
-  if (tid == 0) L.rbm[CSA2_MAX_K / 32] = 0u;
+  if (tid == 0) L.rbm[kMaxCand / 32] = 0u;
   __syncthreads();
-  bitmap_prefix(L.rbm, L.rwp, (int)P, L.c);
+  bitmap_prefix(L.rbm, L.rwp, m, L.c);
   int32_t* orr = a.re_out + ((size_t)l * a.batch + b) * a.re_k;
   float* srr = a.re_sout ? a.re_sout + ((size_t)l * a.batch + b) * a.re_k : nullptr;
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
   if (tid == 0) FS_TR(trb + 2, FS_NOW());
-  // a thread per output rank: its pool position, that winner's candidate index, its column
+  // a thread per output rank: its candidate index, its column
   for (uint32_t q = tid; q < tr.nsel; q += kT) {
-    const uint32_t p = nth_bit(L.rbm, L.rwp, ((int)P + 31) / 32, q);
-    const uint32_t i = nth_bit(L.bm, L.wp, (m + 31) / 32, p);
-    const uint32_t col = cc[slot_of(L, i)];
+    const uint32_t i = nth_bit(L.rbm, L.rwp, (m + 31) / 32, q);
+    const uint32_t col = cc[slot_of(L, i, a.seg)];
     orr[q] = CAND ? cand_row[col] : (int32_t)col;
-    if (srr) srr[q] = key_score(L.key[p]);
+    if (srr) srr[q] = key_score(L.key[i]);
   }
   for (int p = (int)tr.nsel + tid; p < a.re_k; p += kT) {
     orr[p] = -1;
@@ -1101,7 +1084,7 @@ __device__ __forceinline__ void pick_own(const FsArgs& a, PickLds& L, int r, int
   bitmap_prefix(L.bm, L.wp, m, L.c);
   int32_t* own = a.own_out + (size_t)b * a.own_k;
   for (uint32_t q = tid; q < n_own; q += kT) {  // a thread per output rank
-    const uint32_t col = cc[slot_of(L, nth_bit(L.bm, L.wp, (m + 31) / 32, q))];
+    const uint32_t col = cc[slot_of(L, nth_bit(L.bm, L.wp, (m + 31) / 32, q), a.seg)];
     own[q] = CAND ? cand_row[col] : (int32_t)col;
   }
   for (int p = (int)n_own + tid; p < a.own_k; p += kT) own[p] = -1;
@@ -1122,7 +1105,7 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
   if (tid == 0) FS_TR(tb, FS_NOW());
   const int b = a.row0 + r;
   const int n_row = max(0, min(a.n_valid[b], a.n_cols));
-  const int nsg = row_segs(n_row);
+  const int nsg = row_segs(n_row, a.seg);
   const uint32_t* ck = a.ckey + (size_t)r * a.cap;
   const uint32_t* cc = a.ccol + (size_t)r * a.cap;
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
@@ -1149,7 +1132,7 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
     // each candidate's store slot (a wave per segment)
     for (int j = wave; j < nsg; j += kNW) {
       const uint32_t o = L.off[j], c = L.off[j + 1] - o;
-      for (uint32_t e = lane; e < c; e += 64) L.key[o + e] = (uint32_t)j * kSeg + e;
+      for (uint32_t e = lane; e < c; e += 64) L.key[o + e] = (uint32_t)j * (uint32_t)a.seg + e;
     }
     __syncthreads();
     if (tid == 0) FS_TR(tb + 6, FS_NOW());
@@ -1163,8 +1146,24 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
         const int i = tid + kT * u;
         kv[u] = i < m ? L.key[i] : 0u;
       }
+      if (s >= S && s - S < a.n_re) {
+        // a Reindex workgroup loads its layer's re-scores with the keys, into L.key (each
+        // candidate's slot is read before it is overwritten: same thread, same index)
+        const uint32_t* rk = a.rekey + ((size_t)(s - S) * a.rows + r) * a.cap;
+        uint32_t rv[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) kv[u] = tid + kT * u < m ? ck[kv[u]] : 0u;
+        for (int u = 0; u < kU; ++u) {
+          const bool in = tid + kT * u < m;
+          rv[u] = in ? rk[kv[u]] : 0u;
+          kv[u] = in ? ck[kv[u]] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (tid + kT * u < m) L.key[tid + kT * u] = rv[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) kv[u] = tid + kT * u < m ? ck[kv[u]] : 0u;
+      }
       if (tid == 0) FS_TR(tb + 1, FS_NOW());
       n_pool = pick_marked(kv, m, (uint32_t)a.k, L, (1 << 20) - 131072 + (int)blockIdx.x * 16).nsel;
     }
@@ -1184,7 +1183,7 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
         const uint32_t i0 = (uint32_t)((long long)s * m / S), i1 = (uint32_t)((long long)(s + 1) * m / S);
         for (uint32_t i = i0 + tid; i < i1; i += kT) {
           if (!bit_at(L.bm, i)) continue;
-          const uint32_t slot = slot_of(L, i);
+          const uint32_t slot = slot_of(L, i, a.seg);
           const uint32_t col = cc[slot];
           const uint32_t pos = bits_before(L.bm, L.wp, i);
           orow[pos] = CAND ? cand_row[col] : (int32_t)col;
@@ -1231,12 +1230,36 @@ struct FsShape {
   size_t cap;
 };
 
+// Workspace shape covering every segment length a launch may choose: the store holds
+// n_cols rounded up to the longest segment, the counts one per shortest segment.
 FsShape fs_shape(int batch, int n_cols, bool chain) {
   FsShape s;
-  s.runs = (n_cols + kSeg - 1) / kSeg;
-  s.cap = (size_t)s.runs * kSeg;
+  s.runs = (n_cols + kSegMin - 1) / kSegMin;
+  s.cap = (size_t)((n_cols + kSeg - 1) / kSeg) * kSeg;
   s.rows_ws = min(batch, chain ? kChainRows : kMaxRows);
   return s;
+}
+
+// The kept keys of a row of n_cols columns cut into segs segments fit the selection: every
+// key when the row is short enough, else at most k + 6 sqrt(k segs) + 5 segs (the sum of
+// seg_keep over its segments) plus 2 per segment for the keys sharing the cut's bin.
+bool fs_capacity_ok(int n_cols, int k, int segs) {
+  if (n_cols <= kMaxCand) return true;
+  return (double)k + 6.0 * std::sqrt((double)k * segs) + 7.0 * segs <= (double)kMaxCand;
+}
+
+// Segment length of a launch of `rows` rows: the longest that still gives every compute
+// unit a workgroup (shorter segments, more workgroups), within the selection's capacity
+// and at most kMaxRuns segments per row; 0 when none fits.
+int fs_seg(int rows, int n_cols, int k, int n_cu) {
+  int best = 0;
+  for (int seg = kSeg; seg >= kSegMin; seg /= 2) {
+    const int segs = (n_cols + seg - 1) / seg;
+    if (segs > kMaxRuns || !fs_capacity_ok(n_cols, k, segs)) break;
+    best = seg;
+    if ((long long)rows * segs >= n_cu) break;
+  }
+  return best;
 }
 
 struct FsParts {
@@ -1281,14 +1304,10 @@ extern "C" int csa2_fs_trace_zero() {
 }
 #endif
 
-// Rows up to n_cols long whose top-k the filtered selection takes: at most kMaxRuns
-// segments, and the segments' kept keys of the longest such row, at most
-// k + 6 sqrt(k segs) + 5 segs (the sum of seg_keep over its segments), fit the selection.
+// Rows up to n_cols long whose top-k the filtered selection takes (with its longest
+// segments, the fewest kept keys).
 bool fsel_fits(int n_cols, int k) {
-  if (n_cols < 1 || n_cols > kMaxRuns * kSeg) return false;
-  if (n_cols <= kMaxCand) return true;
-  const double segs = (double)((n_cols + kSeg - 1) / kSeg);
-  return (double)k + 6.0 * std::sqrt((double)k * segs) + 5.0 * segs <= (double)kMaxCand;
+  return n_cols >= 1 && n_cols <= kMaxRuns * kSeg && fs_capacity_ok(n_cols, k, (n_cols + kSeg - 1) / kSeg);
 }
 
 bool fsel_len_ok(int n_cols) { return n_cols >= 1 && n_cols <= kMaxRuns * kSeg; }
@@ -1338,11 +1357,15 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
   for (int r0 = 0; r0 < batch; r0 += s.rows_ws) {
     a.row0 = r0;
     a.rows = min(s.rows_ws, batch - r0);
+    a.seg = fs_seg(a.rows, n_cols, k, cap_wg);
+    if (a.seg == 0) return hipErrorInvalidValue;  // excluded by fsel_fits
+    a.runs = (n_cols + a.seg - 1) / a.seg;
+    a.cap = (size_t)a.runs * a.seg;
     // picking workgroups per row: about one per compute unit in all, none with fewer than
     // 256 of the k winners to write
     const int R = a.n_re + (a.own_k > 0 ? 1 : 0);
     const int S = max(1, min(cap_wg / a.rows - R, (k + 255) / 256));
-    const dim3 g_seg((unsigned)(a.rows * s.runs)), g_pick((unsigned)(a.rows * (S + R)));
+    const dim3 g_seg((unsigned)(a.rows * a.runs)), g_pick((unsigned)(a.rows * (S + R)));
     if (cand) {
       hipLaunchKernelGGL(k_fseg<true>, g_seg, dim3(kT), 0, stream, a);
       hipLaunchKernelGGL(k_fpick<true>, g_pick, dim3(kT), 0, stream, a, S);
