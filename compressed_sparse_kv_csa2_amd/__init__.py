@@ -22,7 +22,7 @@ __all__ = [
     "csa2_index_topk_workspace_size", "csa2_select_chain_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
     "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
     "csa2_prefill_select", "csa2_sparse_attn_prefill", "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
-    "csa2_workspace_status", "workspace_status", "check_workspace",
+    "csa2_workspace_status", "workspace_status", "check_workspace", "csa2_sparse_attn_decode_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,9 @@ _SIGS = {
     "csa2_attn_workspace_size": (_SZ, [_I32, _I32]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _F32, _I32, _P, _P,
                                                _SZ, _P]),
+    "csa2_sparse_attn_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _F32, _I32,
+                                                       _P, _P]),
+    "csa2_attn_noalloc_max_bytes": (_SZ, []),
     "csa2_prefill_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "csa2_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P,
                                           _F32, _P, _P, _P, _SZ, _P]),
@@ -309,6 +312,27 @@ def csa2_sparse_attn_decode(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, 
                                        _ptr(idx) if k > 0 else None, k, _ptr(swa), _ptr(swa_len),
                                        float(softmax_scale), B, _ptr(out), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
+
+
+def csa2_sparse_attn_decode_noalloc(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, out,
+                                    softmax_scale=512 ** -0.5, stream=None):
+    """csa2_sparse_attn_decode with the library's static scratch instead of a workspace."""
+    B = q.shape[0]
+    _need(q, "q", _BF16, (B, 16, 512))
+    _need(kv_codes, "kv_codes", _U8, (None, 256))
+    _need(kv_scale, "kv_scale", _U8, (kv_codes.shape[0], 32))
+    _need(seq_base, "seq_base", (torch.int64,), (B,))
+    k = 0
+    if idx is not None:
+        _need(idx, "idx", (torch.int32,), (B, None))
+        k = idx.shape[1]
+    _need(swa, "swa", _U8, (B, 128, 512))
+    _need(swa_len, "swa_len", (torch.int32,), (B,))
+    _need(out, "out", (torch.float32,), (B, 16, 512))
+    lib = load_library()
+    _check(lib.csa2_sparse_attn_decode_noalloc(_ptr(q), _ptr(kv_codes), _ptr(kv_scale), _ptr(seq_base),
+                                               _ptr(idx) if k > 0 else None, k, _ptr(swa), _ptr(swa_len),
+                                               float(softmax_scale), B, _ptr(out), _stream(stream)))
 
 
 def csa2_prefill_chunk(q_idx, q, idx_codes, idx_scale, kv_codes, kv_scale, n_entries, ratio, pos0,

@@ -5,13 +5,38 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 using namespace csa2;
+
+// Split partials of csa2_sparse_attn_decode_noalloc: a file-scope device array, so that
+// entry point allocates nothing.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never passes this name to a kernel (on the host it is a
+// stand-in, not a device address): it uses the address hipGetSymbolAddress returns for
+// the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+// Device address of `scratch` on the current device, looked up on that device's first call
+// and kept per device; null when the lookup fails.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+
+void* scratch_addr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  g_scratch_addr[dev].store(p, std::memory_order_release);
+  return p;
+}
 
 }  // namespace
 
@@ -25,6 +50,7 @@ const char* csa2_status_string(int status) {
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_UNSUPPORTED: return "unsupported shape";
     case CSA2_ERR_HIP: return "HIP runtime error";
+    case CSA2_ERR_SCRATCH: return "shape needs more than the library's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -170,6 +196,25 @@ int csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_codes, const ui
   if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
   return from_hip(launch_attn(0, q, kv_codes, kv_scale, seq_base, idx, k, swa, swa_len, 0,
                               softmax_scale, batch, out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_attn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int csa2_sparse_attn_decode_noalloc(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                                    const int64_t* seq_base, const int32_t* idx, int32_t k,
+                                    const uint8_t* swa, const int32_t* swa_len, float softmax_scale,
+                                    int32_t batch, float* out, void* stream) {
+  if (!q || !kv_codes || !kv_scale || !seq_base || !swa || !swa_len || !out) return CSA2_ERR_INVALID_ARG;
+  if (batch < 1 || k < 0 || k > CSA2_MAX_K || (k > 0 && !idx)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv_codes, 16) || !aligned(kv_scale, 4) || !aligned(swa, 16) ||
+      !aligned(seq_base, 8) || !aligned(swa_len, 4) || !aligned(out, 16) ||
+      (idx && !aligned(idx, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  if (attn_ws_bytes(batch, k) > kNoAllocScratchBytes) return CSA2_ERR_SCRATCH;
+  void* ws = scratch_addr();
+  if (ws == nullptr) return CSA2_ERR_HIP;
+  return from_hip(launch_attn(0, q, kv_codes, kv_scale, seq_base, idx, k, swa, swa_len, 0,
+                              softmax_scale, batch, out, ws, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa2_prefill_workspace_size(int32_t T, int32_t n_entries, int32_t k) {

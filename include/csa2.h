@@ -35,8 +35,8 @@
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers unless stated; the caller owns every buffer.  The
  *    library allocates nothing and is re-entrant, except that calls sharing one workspace
- *    must not overlap in time.  Its only global state is a per-device cache of immutable
- *    device facts (compute units and kernel occupancy), filled on first use.
+ *    must not overlap in time.  Its only global state is the static scratch array of
+ *    csa2_sparse_attn_decode_noalloc and that array's per-device address.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
  *    asynchronous; kernel faults surface at the caller's next synchronisation.
  *  - Arguments are validated on the host BEFORE anything is enqueued; on error nothing is
@@ -74,7 +74,8 @@ enum csa2_status {
   CSA2_ERR_ALIGNMENT = -2,   /* a plane is not aligned as stated above */
   CSA2_ERR_WORKSPACE = -3,   /* workspace pointer missing or smaller than the query says */
   CSA2_ERR_UNSUPPORTED = -4, /* a shape the kernels do not handle */
-  CSA2_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+  CSA2_ERR_HIP = -5,         /* a HIP launch or runtime call failed */
+  CSA2_ERR_SCRATCH = -6      /* the shape needs more than the static scratch holds */
 };
 
 /* flags for csa2_topk */
@@ -258,6 +259,28 @@ int csa2_sparse_attn_decode(const uint16_t* q, const uint8_t* kv_codes, const ui
                             const uint8_t* swa, const int32_t* swa_len, float softmax_scale,
                             int32_t batch, float* out, void* workspace, size_t ws_bytes,
                             void* stream);
+
+/*
+ * csa2_sparse_attn_decode_noalloc -- csa2_sparse_attn_decode for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels and results.
+ * The split partials live in a static device array of csa2_attn_noalloc_max_bytes()
+ * (16 MiB) that the library holds on each GPU it runs on until the process ends; its
+ * device address is looked up on each device's first call (hipGetSymbolAddress) and kept.
+ * The call allocates and frees nothing.  Every call on one GPU shares that GPU's array,
+ * so calls that overlap in time on one GPU (different streams or threads) race; nothing
+ * in the array needs to start at zero (each split writes its partial before the merge
+ * reads it).
+ * Errors: as csa2_sparse_attn_decode, and SCRATCH when csa2_attn_workspace_size(batch, k)
+ * exceeds csa2_attn_noalloc_max_bytes(); HIP if the address lookup fails.
+ */
+int csa2_sparse_attn_decode_noalloc(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scale,
+                                    const int64_t* seq_base, const int32_t* idx, int32_t k,
+                                    const uint8_t* swa, const int32_t* swa_len, float softmax_scale,
+                                    int32_t batch, float* out, void* stream);
+
+/* Bytes of the static scratch csa2_sparse_attn_decode_noalloc uses (16 MiB). */
+size_t csa2_attn_noalloc_max_bytes(void);
 
 /* Bytes of workspace csa2_prefill_chunk needs for this shape. */
 size_t csa2_prefill_workspace_size(int32_t T, int32_t n_entries, int32_t k);

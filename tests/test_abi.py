@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.csa2_status_string(0) == b"ok"
-    for s in range(-5, 0):
+    for s in range(-6, 0):
         assert lib.csa2_status_string(s) not in (b"ok", b"unknown status")
     assert lib.csa2_status_string(-99) == b"unknown status"
     assert lib.csa2_version() >= 100
@@ -111,6 +111,18 @@ def test_attn_validation(lib):
     f = lib.csa2_sparse_attn_decode
     base = [FAKE, FAKE, FAKE, FAKE, FAKE, 512, FAKE, FAKE, 0.04, 4, FAKE, FAKE, 1 << 40, None]
     for pos, val, want in [(5, -1, -1), (4, None, -1), (9, 0, -1), (0, ODD, -2), (12, 10, -3)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
+
+
+def test_attn_noalloc_validation(lib):
+    # the same checks as csa2_sparse_attn_decode, and SCRATCH (-6) for a shape whose split
+    # partials (64 rows x 16,384 entries: about 34 MB) exceed the static scratch
+    f = lib.csa2_sparse_attn_decode_noalloc
+    assert lib.csa2_attn_noalloc_max_bytes() == 16 << 20
+    assert lib.csa2_attn_workspace_size(64, 16384) > lib.csa2_attn_noalloc_max_bytes()
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 16384, FAKE, FAKE, 0.04, 64, FAKE, None]
+    for pos, val, want in [(5, -1, -1), (4, None, -1), (9, 0, -1), (0, ODD, -2), (9, 64, -6)]:
         a = list(base); a[pos] = val
         assert f(*a) == want, (pos, val)
 
