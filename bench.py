@@ -46,9 +46,9 @@ IDX_ENTRY_BYTES = 68         # 128 x 4 bit + 4-byte scale
 MAIN_ENTRY_BYTES = 288       # 512 x 4 bit + 32 E4M3 scale bytes
 D_KV, HEADS, SWA, D_IDX = 512, 16, 128, 128
 SCAN_SOURCES = tuple("compressed_sparse_kv_csa2_amd/csrc/" + f for f in
-                     ("index_topk.hip", "scan_device.h", "select_device.h", "csa2_device.h",
-                      "csa2_internal.h"))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_topk_c4_long_decode_traffic.md")
+                     ("fsel.hip", "index_topk.hip", "scan_device.h", "select_device.h",
+                      "csa2_device.h", "csa2_internal.h"))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fseg_k_fpick_c4_long_decode_traffic.md")
 
 
 def parse():
@@ -69,6 +69,9 @@ def parse():
                    help="model workload: capture the 40-layer step into a HIP graph and replay it")
     p.add_argument("--no-phases", action="store_true",
                    help="skip the separate, untimed per-phase timing pass")
+    p.add_argument("--read-probe", type=int, default=0, metavar="MIB",
+                   help="instead of a workload, time a plain streaming read (a float32 sum) of "
+                        "MIB MiB, the practical HBM read ceiling the scan is compared with")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of a workload, run 5 plain device copies of MIB MiB (the "
                         "known-size reference for scaling the HBM counters) and exit")
@@ -88,6 +91,53 @@ def copy_calibration(mib):
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
     print(json.dumps({"copy_calibration_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
+
+
+def read_probe(mib):
+    """A plain streaming read: torch's float32 sum over `mib` MiB, 20 timed repetitions."""
+    import torch
+    x = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda:0")
+    for _ in range(3):
+        x.sum()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(20):
+        r = x.sum()
+    ev[1].record()
+    torch.cuda.synchronize()
+    assert float(r.item()) == float(x.numel())
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / 20
+    print(json.dumps({"read_probe_bytes": x.numel() * 4, "avg_us": round(us, 2),
+                      "read_gbs": round(x.numel() * 4 / (us * 1e-6) / 1e9, 1)}), flush=True)
+
+
+def cpu_info():
+    """Logical CPUs of the host and its model name (from /proc/cpuinfo when present)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def timed_oracle(fn, threads):
+    """Runs fn() with the BLAS pool limited to `threads` (None: as configured); seconds."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # threadpoolctl missing: no limit can be set
+        threadpool_limits = None
+    t0 = time.perf_counter()
+    if threads is not None and threadpool_limits is not None:
+        with threadpool_limits(limits=threads, user_api="blas"):
+            fn()
+    else:
+        fn()
+    return time.perf_counter() - t0
 
 
 def scan_source_digest() -> str:
@@ -277,10 +327,13 @@ class Decode:
         self.last_lists, self.last_out = lists, [self.out[l] for l in att_layers]
 
     def dominant(self):
+        sel = "pool, own and Reindex top-512s" if self.name == "c3" else "pool and Reindex top-512"
         kernel = {"unfused": "Full scan + top-k as separate launches (k_index_score, k_topk_*)",
-                  "fused": "k_index_topk<false> (Full scan + top-k in one launch)",
-                  "chain": "k_index_topk<false> (Full scan, pool, own and Reindex top-512s in one "
-                           "launch)"}[self.mode if self.POOL else "fused"]
+                  "fused": "csa2_index_topk: k_fseg<false> (segment scans and cuts) + k_fpick<false> "
+                           "(exact top-k); the call timed",
+                  "chain": f"csa2_select_chain: k_fseg<false> (segment scans and cuts, Reindex "
+                           f"re-scores) + k_fpick<false> ({sel}); the call timed"
+                  }[self.mode if self.POOL else "fused"]
         return {"kernel": kernel, "bound": "hbm", "unit": "GB/s",
                 "peak": HBM_PEAK_GBS, "work": self.B * self.N * IDX_ENTRY_BYTES,
                 "scale": 1e9, "marks": (0, 1)}
@@ -297,13 +350,79 @@ class Decode:
         per_q += n_att * (K * (MAIN_ENTRY_BYTES + 4) + SWA * D_KV + HEADS * D_KV * 2 + HEADS * D_KV * 4)
         return B * per_q
 
+    def workspaces(self):
+        """The selection workspaces that start with a status block (not the two-launch top-k's)."""
+        return [w for w in (getattr(self, "cws", None), getattr(self, "fws", None),
+                            getattr(self, "rws", None)) if w is not None]
+
     def valid(self):
+        """Every list strictly ascending and non-negative, every output finite, and every
+        selection workspace's status block free of error bits."""
         ok = True
         for lst in self.last_lists.values():
             ok &= bool(((lst[:, 1:] > lst[:, :-1]).all() & (lst >= 0).all()).item())
         for o in self.last_out:
             ok &= bool(self.torch.isfinite(o).all().item())
+        self.status = [self.csa2.csa2_workspace_status(w) for w in self.workspaces()]
+        ok &= all(bits == 0 for bits, _ in self.status)
         return ok
+
+    def per_layer(self, steps):
+        """c4 as a decoder runs it layer by layer: the Full layer's scan and pool
+        (csa2_index_topk), then the Reindex layer's own call on that pool with its own query
+        (csa2_index_topk over the pool), then its attention.  Returns the timing, the
+        phases, and whether the lists equal the chained call's."""
+        torch, csa2, B, s = self.torch, self.csa2, self.B, self.stream
+        fws = csa2.index_topk_workspace(B, self.N, self.POOL, device=self.dev)
+        rws = csa2.index_topk_workspace(B, self.POOL, self.K, device=self.dev)
+        pool = torch.empty((B, self.POOL), dtype=torch.int32, device=self.dev)
+        idx = torch.empty((B, self.K), dtype=torch.int32, device=self.dev)
+        out = torch.empty((B, HEADS, D_KV), dtype=torch.float32, device=self.dev)
+        full, re = self.layers[0], self.re_layers[0]
+
+        def step(i, ev=None):
+            w = self.sets[i % len(self.sets)]
+            c = w.cache
+            if ev: ev[0].record(s)
+            csa2.csa2_index_topk(w.q_idx[full], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                                 self.POOL, pool, fws, self.N, stream=s)
+            if ev: ev[1].record(s)
+            csa2.csa2_index_topk(w.q_idx[re], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid,
+                                 self.K, idx, rws, self.POOL, cand=pool, stream=s)
+            if ev: ev[2].record(s)
+            csa2.csa2_sparse_attn_decode(w.q[re], c.kv_codes, c.kv_scale, c.seq_base, idx, w.swa[re],
+                                         w.swa_len, out, self.attn_ws, stream=s)
+            if ev: ev[3].record(s)
+
+        for i in range(5):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        reps = max(20, min(100, steps))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        for i in range(reps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        ph = [round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3 / reps, 2) for j in range(3)]
+        # the same input set through both paths: the Reindex list must be the chain's
+        self.step(0)
+        step(0)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(idx, self.re_out[0]))
+        st = [csa2.csa2_workspace_status(w) for w in (fws, rws)]
+        ok = same and all(bits == 0 for bits, _ in st) and \
+            bool(((idx[:, 1:] > idx[:, :-1]).all() & (idx >= 0).all()).item()) and \
+            bool(torch.isfinite(out).all().item())
+        return {"ms_per_step": round(ms, 5), "value": round(B / (ms * 1e-3), 1),
+                "phases_us": {"full_scan_pool_us": ph[0], "reindex_select_us": ph[1],
+                              "attention_us": ph[2]},
+                "reindex_equals_chain": same, "valid": ok,
+                "calls": "csa2_index_topk (pool) -> csa2_index_topk over the pool (Reindex) -> "
+                         "csa2_sparse_attn_decode"}
 
     def config(self, n_sets):
         desc = {"c4": "c4_long_decode: decoder step at 2^20 ctx, batch 4, Full scan of 1,048,576 "
@@ -327,8 +446,7 @@ class Decode:
         qi = {l: host(v) for l, v in w.q_idx.items()}
         q = {l: host(v) for l, v in w.q.items()}
         sw = {l: host(v) for l, v in w.swa.items()}
-        t0 = time.perf_counter()
-        for b in range(rows):
+        def one(b):
             base = b * N
             if self.name == "c4":
                 oracle.decode_step_long(qi[20][b], qi[24][b], q[24][b], codes, scale, kvc, kvs, base,
@@ -341,15 +459,20 @@ class Decode:
                 oracle.decoder_chain({l: v[b] for l, v in qi.items()}, {l: v[b] for l, v in q.items()},
                                      {l: v[b] for l, v in sw.items()}, SWA, codes, scale, kvc, kvs,
                                      base, N, self.POOL, self.K)
-        dt = time.perf_counter() - t0
+
+        dt = timed_oracle(lambda: [one(b) for b in range(rows)], None)
+        dt1 = timed_oracle(lambda: one(0), 1)
         what = {"c4": "full 1,048,576-entry scan, pool, Reindex, attention each",
                 "c2": "full 32,768-entry scan, top-512, attention each",
                 "c3": "the 20-layer chain over 131,072 entries each"}[self.name]
         bt = blas_threads()
+        n_cpu, model = cpu_info()
         return {"value": round(rows / dt, 4), "unit": "query-tokens/s", "cores": bt,
-                "kind": "oracle",
-                "sample": f"{rows} of the {B} sequences of one step ({what}), fp64 numpy; BLAS calls "
-                          f"on {bt} threads, element-wise decoding on one; {dt:.1f} s"}
+                "kind": "oracle", "os_cpu_count": n_cpu, "cpu_model": model,
+                "value_1thread": round(1 / dt1, 4),
+                "sample": f"{rows} of the {B} sequences of one step ({what}), fp64 numpy with BLAS "
+                          f"calls on {bt} threads (element-wise decoding on one): {dt:.1f} s; one "
+                          f"sequence with BLAS limited to 1 thread: {dt1:.1f} s"}
 
 
 # ------------------------------------------------------------------------------------ prefill
@@ -436,13 +559,15 @@ class Prefill:
         sample = [self.T - 1 - r * (self.T // rows) for r in range(rows)]
         args = (host(qi), host(q), host(c.idx_codes), host(c.idx_scale), host(c.kv_codes),
                 host(c.kv_scale), self.N, self.ratio, self.pos0, self.K, host(sw))
-        t0 = time.perf_counter()
-        oracle.prefill_chunk(*args, rows=sample)
-        dt = time.perf_counter() - t0
+        dt = timed_oracle(lambda: oracle.prefill_chunk(*args, rows=sample), None)
+        dt1 = timed_oracle(lambda: oracle.prefill_chunk(*args, rows=sample[:1]), 1)
         bt = blas_threads()
+        n_cpu, model = cpu_info()
         return {"value": round(rows / dt, 4), "unit": "query-tokens/s", "cores": bt, "kind": "oracle",
-                "sample": f"{rows} of the {self.T} queries (spread over the chunk), fp64 numpy; BLAS "
-                          f"calls on {bt} threads, element-wise decoding on one; {dt:.1f} s"}
+                "os_cpu_count": n_cpu, "cpu_model": model, "value_1thread": round(1 / dt1, 4),
+                "sample": f"{rows} of the {self.T} queries (spread over the chunk), fp64 numpy with "
+                          f"BLAS calls on {bt} threads (element-wise decoding on one): {dt:.1f} s; one "
+                          f"query with BLAS limited to 1 thread: {dt1:.1f} s"}
 
 
 class Model:
@@ -739,6 +864,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.read_probe:
+        read_probe(args.read_probe)
+        return
 
     import torch
     import synth
@@ -836,6 +964,12 @@ def main():
         "selection_valid": ok,
         "cpu_baseline": cpu,
     }
+    if getattr(wl, "status", None) is not None:
+        line["workspace_status"] = [{"error_bits": b, "rows_rescanned": n} for b, n in wl.status]
+    if headline and args.select == "chain":
+        pl = wl.per_layer(args.steps)
+        line["per_layer_path"] = pl
+        ok = ok and pl["valid"]
     if getattr(wl, "graph", None) is not None:
         g_ms, g_same = wl.graph_timing(args.steps)
         line["hip_graph"] = {"ms_per_step": round(g_ms, 5),

@@ -1179,7 +1179,9 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
     fast = !__syncthreads_or(bad);
     if (tid == 0) FS_TR(tb + 2, FS_NOW());
     if (fast) {
-      if (s < S) {  // this workgroup's slice of the candidates
+      if (s < S && (long long)m <= 2LL * kT * S) {
+        // this workgroup's slice of the candidates (at most two per thread): each winner's
+        // output position from the bitmap's prefix
         const uint32_t i0 = (uint32_t)((long long)s * m / S), i1 = (uint32_t)((long long)(s + 1) * m / S);
         for (uint32_t i = i0 + tid; i < i1; i += kT) {
           if (!bit_at(L.bm, i)) continue;
@@ -1189,6 +1191,17 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
           orow[pos] = CAND ? cand_row[col] : (int32_t)col;
           if (srow) srow[pos] = key_score(ck[slot]);
         }
+      } else if (s < S) {
+        // this workgroup's slice of the output, a thread per rank: its winner by bitmap rank
+        const uint32_t q0 = (uint32_t)((long long)s * n_pool / S), q1 = (uint32_t)((long long)(s + 1) * n_pool / S);
+        for (uint32_t q = q0 + tid; q < q1; q += kT) {
+          const uint32_t slot = slot_of(L, nth_bit(L.bm, L.wp, (m + 31) / 32, q), a.seg);
+          const uint32_t col = cc[slot];
+          orow[q] = CAND ? cand_row[col] : (int32_t)col;
+          if (srow) srow[q] = key_score(ck[slot]);
+        }
+      }
+      if (s < S) {
         if (s == 0)
           for (int p = (int)n_pool + tid; p < a.k; p += kT) {
             orow[p] = -1;
@@ -1362,9 +1375,9 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
     a.runs = (n_cols + a.seg - 1) / a.seg;
     a.cap = (size_t)a.runs * a.seg;
     // picking workgroups per row: about one per compute unit in all, none with fewer than
-    // 256 of the k winners to write
+    // 128 of the k winners to write
     const int R = a.n_re + (a.own_k > 0 ? 1 : 0);
-    const int S = max(1, min(cap_wg / a.rows - R, (k + 255) / 256));
+    const int S = max(1, min(cap_wg / a.rows - R, (k + 127) / 128));
     const dim3 g_seg((unsigned)(a.rows * a.runs)), g_pick((unsigned)(a.rows * (S + R)));
     if (cand) {
       hipLaunchKernelGGL(k_fseg<true>, g_seg, dim3(kT), 0, stream, a);
