@@ -65,6 +65,10 @@ class DecodePass:
         self.lists = {l: torch.empty((batch, k), dtype=torch.int32, device=dev) for l in SELECTING}
         self.out = torch.empty((N_LAYERS, batch, 16, 512), dtype=torch.float32, device=dev)
 
+    def workspaces(self):
+        """The selection workspaces whose status block (csa2_workspace_status) reports errors."""
+        return [self.enc_ws, self.dec_ws]
+
     def step(self, enc_caches, dec_cache, q_idx, q, swa, swa_len, stream=None, marks=None):
         """enc_caches: three entry caches (layers 2, 8, 14); dec_cache: the decoder's.
         q_idx: {selecting layer: bf16 [batch, 128]}; q: bf16 [40, batch, 16, 512];
@@ -134,6 +138,10 @@ class ReplayChunk:
         self.lists = {l: torch.empty((T, k), dtype=torch.int32, device=dev)
                       for l in (DECODER_FULL,) + REINDEX}
         self.out = torch.empty((N_LAYERS - DECODER_FULL, T, 16, 512), dtype=torch.float32, device=dev)
+
+    def workspaces(self):
+        """The selection workspace whose status block (csa2_workspace_status) reports errors."""
+        return [self.sel_ws]
 
     def step(self, cache, q_idx, q, swa, stream=None, marks=None):
         """cache: the sequence's decoder entries (planes from entry 0); q_idx: {20, 24, 28,

@@ -79,3 +79,11 @@ def score_error_bound(q_bits, codes, scale):
     sc = np.asarray(scale, np.float32).astype(np.float64)
     exact = sc * (v @ q)
     return 130 * 2.0 ** -24 * sc * mag + 2.0 ** -23 * np.abs(exact)
+
+
+def assert_ws_ok(*workspaces):
+    """Every selection workspace's status block reports no error bits."""
+    import compressed_sparse_kv_csa2_amd as csa2
+    for ws in workspaces:
+        bits, _ = csa2.csa2_workspace_status(ws)
+        assert bits == 0, f"selection workspace error bits {bits:#x}"

@@ -17,7 +17,7 @@ import torch
 import compressed_sparse_kv_csa2_amd as csa2
 import oracle
 import synth
-from _util import ATTN_TOL, attn_rel_err, check_topk, score_error_bound
+from _util import ATTN_TOL, assert_ws_ok, attn_rel_err, check_topk, score_error_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -337,6 +337,57 @@ def test_c4_long_decode_step():
         ref = oracle.decode_attention(h(q)[b], h(cache.kv_codes), h(cache.kv_scale), base, h(idx)[b],
                                       h(swa)[b], 128, SCALE)
         assert attn_rel_err(h(out)[b], ref) <= ATTN_TOL
+
+
+def test_c4_bench_call_sequence():
+    """The benchmark's c4 step exactly: input set 0 of its rotation (layer 20's index query,
+    layer 24's index query, layer 24's query and window), csa2_select_chain (Full scan of
+    4 x 2^20 entries, pool 16,384, one Reindex layer's top-512, no own list) on the chain
+    workspace, then csa2_sparse_attn_decode over the Reindex list.  The pool and the Reindex
+    list against fp64 oracle scores, rows 0 and 3's attention against the oracle, and the
+    per-layer calls (csa2_index_topk for the pool, then over the pool) give the same lists."""
+    cfg = synth.CONFIGS["c4_long_decode"]
+    B, N, seed = cfg["B"], cfg["ctx"] // cfg["ratio"], cfg["seed"]
+    log(f"c4 bench sequence B={B} N={N}")
+    cache = synth.make_entries([N] * B, seed=seed, device=DEV)
+    q_full = synth.make_index_queries(B, seed, device=DEV, sub=20)
+    q_re = synth.make_index_queries(B, seed, device=DEV, sub=24)
+    q = synth.make_queries(B, seed, device=DEV, sub=24)
+    swa = synth.make_swa(B, 128, seed, device=DEV, sub=24)
+    swa_len = i32([128] * B)
+    cws = csa2.select_chain_workspace(B, N, 16384)
+    pool = torch.empty((B, 16384), dtype=torch.int32, device=DEV)
+    re_out = torch.empty((1, B, 512), dtype=torch.int32, device=DEV)
+    csa2.csa2_select_chain(q_full, cache.idx_codes, cache.idx_scale, cache.seq_base, cache.n_entries, N,
+                           pool, cws, k=512, q_re=q_re[None].contiguous(), re_out=re_out)
+    out = torch.empty((B, 16, 512), dtype=torch.float32, device=DEV)
+    aws = csa2.attn_workspace(B, 512)
+    csa2.csa2_sparse_attn_decode(q, cache.kv_codes, cache.kv_scale, cache.seq_base, re_out[0], swa,
+                                 swa_len, out, aws, softmax_scale=SCALE)
+    # the per-layer calls on the same inputs
+    fws = csa2.index_topk_workspace(B, N, 16384)
+    rws = csa2.index_topk_workspace(B, 16384, 512)
+    pool2 = torch.empty_like(pool)
+    idx2 = torch.empty((B, 512), dtype=torch.int32, device=DEV)
+    csa2.csa2_index_topk(q_full, cache.idx_codes, cache.idx_scale, cache.seq_base, cache.n_entries, 16384,
+                         pool2, fws, N)
+    csa2.csa2_index_topk(q_re, cache.idx_codes, cache.idx_scale, cache.seq_base, i32([16384] * B), 512,
+                         idx2, rws, 16384, cand=pool2)
+    torch.cuda.synchronize()
+    assert_ws_ok(cws, fws, rws)
+    assert torch.equal(pool, pool2) and torch.equal(re_out[0], idx2), "per-layer calls differ"
+    codes, scale = h(cache.idx_codes), h(cache.idx_scale)
+    for b in (0, B - 1):
+        base = b * N
+        log(f"c4 bench sequence oracle row {b}")
+        s = oracle.index_scores(h(q_full)[b], codes[base:base + N], scale[base:base + N])
+        check_topk(h(pool)[b], s, 16384, label=f"pool {b}")
+        p = h(pool)[b]
+        _, ref_r = oracle.reindex_layer(h(q_re)[b], codes[base:base + N], scale[base:base + N], p)
+        check_topk(h(re_out)[0][b], ref_r, 512, ids=p, label=f"reindex {b}")
+        ref = oracle.decode_attention(h(q)[b], h(cache.kv_codes), h(cache.kv_scale), base, h(re_out)[0][b],
+                                      h(swa)[b], 128, SCALE)
+        assert attn_rel_err(h(out)[b], ref) <= ATTN_TOL, f"attention row {b}"
 
 
 def test_decode_is_deterministic():

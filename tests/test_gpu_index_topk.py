@@ -337,6 +337,26 @@ def test_chain_with_ties():
     assert np.array_equal(h(re_out)[1][0], np.arange(512))
 
 
+def check_chain_fp64(cache, q_full, q_re, pool, own, re_out, rows, pool_k=16384, k=512):
+    """The chain's pool, own top-k and every Reindex list against fp64 oracle scores (gap
+    rule): the pool and own top-k over the row's scores, each Reindex list over the re-scores
+    of the pool's entries."""
+    codes, scale = h(cache.idx_codes), h(cache.idx_scale)
+    bases, lens = h(cache.seq_base), h(cache.n_entries)
+    P, R = h(pool), None if re_out is None else h(re_out)
+    for b in rows:
+        base, n = int(bases[b]), int(lens[b])
+        log(f"chain fp64 row {b}")
+        s = oracle.index_scores(h(q_full)[b], codes[base:base + n], scale[base:base + n])
+        check_topk(P[b], s, pool_k, label=f"pool row {b}")
+        if own is not None:
+            check_topk(h(own)[b], s, k, label=f"own row {b}")
+        pv = P[b][P[b] >= 0]
+        for r in range(0 if q_re is None else q_re.shape[0]):
+            sr = oracle.index_scores(h(q_re)[r][b], codes[base + pv], scale[base + pv])
+            check_topk(R[r][b], sr, k, ids=pv, label=f"Reindex {r} row {b}")
+
+
 def test_chain_long_decode_at_full_size():
     """4 x 2^20 Full scan -> pool 16,384 -> own top-512 and one Reindex layer, three calls
     on one workspace."""
@@ -348,7 +368,8 @@ def test_chain_long_decode_at_full_size():
     for rep in range(3):
         q = synth.make_index_queries(B, cfg["seed"] + rep, device=DEV)
         q_re = synth.make_index_queries(B, cfg["seed"] + 1000 + rep, device=DEV)[None].contiguous()
-        check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 3], ws=ws)
+        pool, own, re_out = check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 3], ws=ws)
+    check_chain_fp64(cache, q, q_re, pool, own, re_out, rows=[0, 3])
 
 
 def test_chain_decoder_layer_chain_at_full_size():
@@ -360,4 +381,5 @@ def test_chain_decoder_layer_chain_at_full_size():
     q = synth.make_index_queries(B, cfg["seed"], device=DEV)
     q_re = torch.stack([synth.make_index_queries(B, cfg["seed"] + 10 + r, device=DEV)
                         for r in range(4)]).contiguous()
-    check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 15])
+    pool, own, re_out = check_chain(cache, q, N, 16384, 512, q_re, rows=[0, 15])
+    check_chain_fp64(cache, q, q_re, pool, own, re_out, rows=[0, 15])

@@ -16,7 +16,7 @@ import compressed_sparse_kv_csa2_amd as csa2
 from compressed_sparse_kv_csa2_amd import model
 import oracle
 import synth
-from _util import ATTN_TOL, attn_rel_err, check_topk
+from _util import ATTN_TOL, assert_ws_ok, attn_rel_err, check_topk
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -50,6 +50,7 @@ def test_whole_model_decode_step():
     out1 = h(run.out).copy()
     run.step(enc, dec, q_idx, q, swa, swa_len)  # a second step on the same buffers
     torch.cuda.synchronize()
+    assert_ws_ok(*run.workspaces())
     assert all(np.array_equal(first[l], h(run.lists[l])) for l in first)
     assert np.array_equal(out1, h(run.out))
 
@@ -100,6 +101,7 @@ def test_whole_model_decode_step_full_size():
     run = model.DecodePass(B, n_enc, n_dec, device=DEV)
     run.step(enc, dec, q_idx, q, swa, swa_len)
     torch.cuda.synchronize()
+    assert_ws_ok(*run.workspaces())
     b = 3
     lists = {l: h(t)[b] for l, t in run.lists.items()}
     out = h(run.out[:, b])
@@ -129,3 +131,40 @@ def test_whole_model_decode_step_full_size():
         ref = oracle.decode_attention(h(q[l])[b], h(c.kv_codes[sl]), h(c.kv_scale[sl]), 0, idx,
                                       h(swa[l])[b], 128, SCALE)
         assert attn_rel_err(out[l], ref) <= ATTN_TOL, f"layer {l}"
+
+
+def test_graph_replay_equals_eager():
+    """The 40-layer step captured once into a HIP graph (as the benchmark's --graph does)
+    and replayed five times, with eager steps on other inputs and synchronisations between
+    the replays: every replay's lists and outputs equal an eager step's on the captured
+    inputs, bit for bit."""
+    B, n_enc, n_dec, seed = 2, 32768, 65536, 11
+    log(f"graph replay B={B} enc={n_enc} dec={n_dec}")
+
+    def inputs(sd):
+        enc = [synth.make_entries([n_enc] * B, seed=sd, device=DEV, field_base=10 * (i + 1))
+               for i in range(3)]
+        dec = synth.make_entries([n_dec] * B, seed=sd, device=DEV)
+        q_idx = {l: synth.make_index_queries(B, sd, device=DEV, sub=l) for l in model.SELECTING}
+        q = torch.stack([synth.make_queries(B, sd, device=DEV, sub=l) for l in range(40)]).contiguous()
+        swa = torch.stack([synth.make_swa(B, 128, sd, device=DEV, sub=l) for l in range(40)]).contiguous()
+        return enc, dec, q_idx, q, swa
+
+    a, other = inputs(seed), inputs(seed + 1)
+    swa_len = torch.tensor([128, 90], dtype=torch.int32, device=DEV)
+    run = model.DecodePass(B, n_enc, n_dec, device=DEV)
+    run.step(*a, swa_len)
+    torch.cuda.synchronize()
+    ref = [run.out.clone()] + [v.clone() for v in run.lists.values()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.step(*a, swa_len, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(5):
+        run.step(*other, swa_len)  # eager work on other inputs between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [run.out] + list(run.lists.values())
+        assert all(torch.equal(x, y) for x, y in zip(ref, got)), f"replay {rep} differs from eager"
+    assert_ws_ok(*run.workspaces())

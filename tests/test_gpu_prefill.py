@@ -176,8 +176,19 @@ def test_prefill_matches_decode_per_row():
     # same selection rule on scores of the same precision class; compare as sets within the rule
     keys = oracle.dequant_index_keys(h(cache.idx_codes)[:n_t])
     s = h(cache.idx_scale)[:n_t].astype(np.float64) * (keys @ oracle.formats.bf16_decode(h(q_idx)[t]))
-    check_topk(h(didx)[0], s, k, label="decode row")
+    gap = check_topk(h(didx)[0], s, k, label="decode row")
     check_topk(h(idx)[t], s, k, label="prefill row")
+    if gap > 1e-4:  # a clear threshold: the two selections are the same set
+        assert np.array_equal(h(didx)[0], h(idx)[t]), "prefill and decode lists differ"
+    # the decode attention over the prefill row's list and its causal window equals the row
+    win = swa[p - (pos0 - 127) - 127: p - (pos0 - 127) + 1][None].contiguous()
+    dout = torch.empty((1, 16, 512), dtype=torch.float32, device=DEV)
+    csa2.csa2_sparse_attn_decode(q[t:t + 1].contiguous(), cache.kv_codes, cache.kv_scale,
+                                 torch.zeros(1, dtype=torch.int64, device=DEV), idx[t:t + 1].contiguous(),
+                                 win, torch.tensor([128], dtype=torch.int32, device=DEV), dout,
+                                 csa2.attn_workspace(1, k), softmax_scale=SCALE)
+    torch.cuda.synchronize()
+    assert attn_rel_err(h(dout)[0], h(out)[t]) <= 1e-5, "prefill and decode attention differ"
 
 
 def test_c5_prefill_chunk_sampled_rows():
@@ -193,5 +204,15 @@ def test_c5_prefill_chunk_sampled_rows():
         n_t = (pos0 + t + 1) // ratio
         row = g[t]
         assert np.all(row >= 0) and np.all(np.diff(row) > 0) and row[-1] < n_t
-    rows = [0, 1, 127, 128, 2047, 2048, 4094, 4095]
+    # 68 rows: both ends of the chunk, both sides of every 256-row block edge, around the
+    # middle, and the rows whose visible count reaches the last multiple of 4,096 entries
+    # (the contraction's entry splits), plus a seeded spread
+    rows = {0, 1, 2, 3, 127, 128, 129, 2047, 2048, 2049, T - 4, T - 3, T - 2, T - 1}
+    rows |= {256 * j - 1 for j in range(1, T // 256)} | {256 * j for j in range(1, T // 256)}
+    rows |= {t for t in range(T) if ((pos0 + t + 1) // ratio) % 4096 in (0, 4095, 1)}
+    rng = np.random.default_rng(cfg["seed"])
+    rows |= set(rng.choice(T, 68 - len(rows), replace=False).tolist()) if len(rows) < 68 else set()
+    rows = sorted(rows)
+    assert len(rows) >= 64
+    log(f"c5 oracle rows: {len(rows)}")
     check_rows(cache, q_idx, q, swa, N, ratio, pos0, k, idx, out, rows)

@@ -16,7 +16,7 @@ import compressed_sparse_kv_csa2_amd as csa2
 from compressed_sparse_kv_csa2_amd import model
 import oracle
 import synth
-from _util import ATTN_TOL, attn_rel_err, check_topk
+from _util import ATTN_TOL, assert_ws_ok, attn_rel_err, check_topk
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -47,6 +47,7 @@ def test_replay_chunk(n, T, pos0, rows):
     run = model.ReplayChunk(T, n, pos0, device=DEV)
     run.step(cache, q_idx, q, swa)
     torch.cuda.synchronize()
+    assert_ws_ok(*run.workspaces())
     codes, scale = h(cache.idx_codes), h(cache.idx_scale)
     kc, ks = h(cache.kv_codes), h(cache.kv_scale)
     pool = h(run.pool)
@@ -105,6 +106,7 @@ def test_replay_chunk_full_size():
     run = model.ReplayChunk(T, n, pos0, device=DEV)
     run.step(cache, q_idx, q, swa)
     torch.cuda.synchronize()
+    assert_ws_ok(*run.workspaces())
     codes, scale = h(cache.idx_codes), h(cache.idx_scale)
     kc, ks = h(cache.kv_codes), h(cache.kv_scale)
     pool = h(run.pool)
