@@ -23,6 +23,7 @@ __all__ = [
     "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
     "csa2_prefill_select", "csa2_sparse_attn_prefill", "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
     "csa2_workspace_status", "workspace_status", "check_workspace", "csa2_sparse_attn_decode_noalloc",
+    "check_attention_ids",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -291,9 +292,36 @@ def csa2_select_chain(q_full, idx_codes, idx_scale, seq_base, n_valid, n_cols, p
                                  workspace.numel(), _stream(stream)))
 
 
+def check_attention_ids(idx, n_entries):
+    """Host-side range check of attention lists: every id of row b must be -1 (skip) or in
+    [0, n_entries[b]).  idx: int32 [B, k] and n_entries: [B] (either device), copied to the
+    host; raises Csa2Error naming the first bad row and id.  The library cannot check this
+    itself: its attention call takes no per-sequence entry count, so an id out of range
+    would read outside the sequence's entries."""
+    import numpy as np
+    ids = idx.detach().to("cpu").numpy()
+    n = np.asarray(n_entries.detach().to("cpu").numpy() if hasattr(n_entries, "detach") else n_entries,
+                   dtype=np.int64).reshape(-1)
+    if ids.ndim != 2 or n.shape[0] != ids.shape[0]:
+        raise Csa2Error(f"id check: idx {tuple(ids.shape)} and n_entries {tuple(n.shape)} disagree")
+    bad = (ids < -1) | (ids >= n[:, None])
+    if bad.any():
+        b, j = map(int, np.argwhere(bad)[0])
+        raise Csa2Error(f"attention list row {b} position {j}: id {int(ids[b, j])} outside "
+                        f"[-1, {int(n[b])})")
+
+
+def _ids_checked() -> bool:
+    return os.environ.get("CSA2_CHECK_IDS", "") not in ("", "0")
+
+
 def csa2_sparse_attn_decode(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, out, workspace,
-                            softmax_scale=512 ** -0.5, stream=None):
-    """out [B, 16, 512] f32: one softmax over the selected entries and the window rows."""
+                            softmax_scale=512 ** -0.5, stream=None, n_entries=None):
+    """out [B, 16, 512] f32: one softmax over the selected entries and the window rows.
+    When n_entries (int32 [B]) is given and the environment sets CSA2_CHECK_IDS=1, the list
+    is range-checked on the host first (check_attention_ids)."""
+    if idx is not None and n_entries is not None and _ids_checked():
+        check_attention_ids(idx, n_entries)
     B = q.shape[0]
     _need(q, "q", _BF16, (B, 16, 512))
     _need(kv_codes, "kv_codes", _U8, (None, 256))

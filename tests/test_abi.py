@@ -211,3 +211,22 @@ def test_binding_rejects_host_tensors():
         csa2.csa2_kv_append(x, y, torch.arange(4), *planes)
     with pytest.raises(ValueError, match="GPU"):
         csa2.csa2_swa_append(y, torch.arange(4), torch.zeros((4, 128, 512), dtype=torch.uint8))
+
+
+def test_attention_id_range_check_on_the_host(monkeypatch):
+    """The host-side id check (CPU only, no launch): -1 and ids below the row's entry count
+    pass; an id at or past it, or below -1, raises before any call."""
+    import torch
+    n = torch.tensor([10, 3], dtype=torch.int32)
+    ok = torch.tensor([[0, 4, 9, -1], [-1, 0, 1, 2]], dtype=torch.int32)
+    csa2.check_attention_ids(ok, n)
+    for bad, where in [([[0, 4, 10, -1], [-1, 0, 1, 2]], "row 0 position 2"),
+                       ([[0, 4, 9, -1], [-1, 0, 3, 2]], "row 1 position 2"),
+                       ([[0, -2, 9, -1], [-1, 0, 1, 2]], "row 0 position 1")]:
+        with pytest.raises(csa2.Csa2Error, match=where):
+            csa2.check_attention_ids(torch.tensor(bad, dtype=torch.int32), n)
+    # the attention binding runs it when asked, before anything reaches the library
+    monkeypatch.setenv("CSA2_CHECK_IDS", "1")
+    bad = torch.tensor([[0, 4, 10, -1], [-1, 0, 1, 2]], dtype=torch.int32)
+    with pytest.raises(csa2.Csa2Error, match="outside"):
+        csa2.csa2_sparse_attn_decode(None, None, None, None, bad, None, None, None, None, n_entries=n)
