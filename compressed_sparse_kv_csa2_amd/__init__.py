@@ -23,7 +23,8 @@ __all__ = [
     "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
     "csa2_prefill_select", "csa2_sparse_attn_prefill", "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
     "csa2_workspace_status", "workspace_status", "check_workspace", "csa2_sparse_attn_decode_noalloc",
-    "check_attention_ids",
+    "check_attention_ids", "csa2_replay_select", "csa2_replay_select_workspace_size",
+    "replay_select_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +52,9 @@ _SIGS = {
     "csa2_select_chain": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
                                          _I32, _P, _P, _P, _SZ, _P]),
     "csa2_workspace_status": (ctypes.c_int, [_P, _P, _P]),
+    "csa2_replay_select_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "csa2_replay_select": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P, _P, _I32, _P,
+                                          _P, _SZ, _P]),
     "csa2_attn_workspace_size": (_SZ, [_I32, _I32]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _F32, _I32, _P, _P,
                                                _SZ, _P]),
@@ -138,6 +142,10 @@ def csa2_select_chain_workspace_size(batch: int, n_cols: int, pool_k: int) -> in
     return int(load_library().csa2_select_chain_workspace_size(batch, n_cols, pool_k))
 
 
+def csa2_replay_select_workspace_size(T: int, n_entries: int, pool_k: int) -> int:
+    return int(load_library().csa2_replay_select_workspace_size(T, n_entries, pool_k))
+
+
 def csa2_attn_workspace_size(batch: int, k: int) -> int:
     return int(load_library().csa2_attn_workspace_size(batch, k))
 
@@ -165,9 +173,14 @@ def select_chain_workspace(batch, n_cols, pool_k, device="cuda"):
     return _zeros(csa2_select_chain_workspace_size(batch, n_cols, pool_k), device)
 
 
+def replay_select_workspace(T, n_entries, pool_k, device="cuda"):
+    """Zero-filled workspace for csa2_replay_select (its first int32 is the status word)."""
+    return _zeros(csa2_replay_select_workspace_size(T, n_entries, pool_k), device)
+
+
 def csa2_workspace_status(workspace, stream=None):
     """(error bits, rows re-scanned) from the status block of a csa2_index_topk /
-    csa2_select_chain workspace; synchronizes the stream."""
+    csa2_select_chain / csa2_replay_select workspace; synchronizes the stream."""
     _need(workspace, "workspace", _U8)
     out = (ctypes.c_uint32 * 2)()
     _check(load_library().csa2_workspace_status(_ptr(workspace), ctypes.cast(out, ctypes.c_void_p),
@@ -290,6 +303,29 @@ def csa2_select_chain(q_full, idx_codes, idx_scale, seq_base, n_valid, n_cols, p
                                  _ptr(pool_score_out), k, _ptr(own_out), _ptr(q_re), n_re,
                                  _ptr(re_out), _ptr(re_score_out), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
+
+
+def csa2_replay_select(q_idx, idx_codes, idx_scale, n_entries, ratio, pos0, pool_out, workspace,
+                       k=512, own_out=None, pool_n_out=None, stream=None):
+    """Per query t of q_idx [T, 128] (position pos0 + t): pool_out [T, pool_k], the pool of its
+    best visible entries; own_out [T, k] (optional), its top-k inside the pool; pool_n_out
+    [T] (optional), the valid entries of each pool."""
+    T, pool_k = pool_out.shape
+    _need(q_idx, "q_idx", _BF16, (T, 128))
+    _need(idx_codes, "idx_codes", _U8, (None, 64))
+    _need(idx_scale, "idx_scale", (torch.float32,), (idx_codes.shape[0],))
+    if idx_codes.shape[0] < n_entries:
+        raise ValueError("fewer cache entries than n_entries")
+    _need(pool_out, "pool_out", (torch.int32,), (T, pool_k))
+    if own_out is not None:
+        _need(own_out, "own_out", (torch.int32,), (T, k))
+    if pool_n_out is not None:
+        _need(pool_n_out, "pool_n_out", (torch.int32,), (T,))
+    _need(workspace, "workspace", _U8)
+    _check(load_library().csa2_replay_select(_ptr(q_idx), _ptr(idx_codes), _ptr(idx_scale),
+                                             int(n_entries), int(ratio), int(pos0), T, pool_k,
+                                             _ptr(pool_out), _ptr(pool_n_out), int(k), _ptr(own_out),
+                                             _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def check_attention_ids(idx, n_entries):

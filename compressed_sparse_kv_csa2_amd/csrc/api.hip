@@ -164,6 +164,32 @@ int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const fl
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t csa2_replay_select_workspace_size(int32_t T, int32_t n_entries, int32_t pool_k) {
+  if (T < 1 || n_entries < 0 || n_entries > kTopkMaxCols || pool_k < 1 || pool_k > CSA2_MAX_K) return 0;
+  return replay_select_ws_bytes(T, n_entries, pool_k);
+}
+
+int csa2_replay_select(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                       int32_t n_entries, int32_t ratio, int64_t pos0, int32_t T, int32_t pool_k,
+                       int32_t* pool_out, int32_t* pool_n_out, int32_t k, int32_t* own_out,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (!q_idx || !pool_out) return CSA2_ERR_INVALID_ARG;
+  if (n_entries > 0 && (!idx_codes || !idx_scale)) return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || n_entries < 0 || ratio < 1 || pos0 < 0 || pool_k < 1 || pool_k > CSA2_MAX_K)
+    return CSA2_ERR_INVALID_ARG;
+  if (own_out && (k < 1 || k > CSA2_MAX_K)) return CSA2_ERR_INVALID_ARG;
+  if (n_entries > kTopkMaxCols) return CSA2_ERR_UNSUPPORTED;
+  if (!aligned(q_idx, 16) || (idx_codes && !aligned(idx_codes, 16)) ||
+      (idx_scale && !aligned(idx_scale, 4)) || !aligned(pool_out, 4) ||
+      (pool_n_out && !aligned(pool_n_out, 4)) || (own_out && !aligned(own_out, 4)))
+    return CSA2_ERR_ALIGNMENT;
+  if (!workspace || ws_bytes < replay_select_ws_bytes(T, n_entries, pool_k)) return CSA2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;
+  return from_hip(launch_replay_select(q_idx, idx_codes, idx_scale, n_entries, ratio, pos0, T, pool_k,
+                                       pool_out, pool_n_out, own_out ? k : 0, own_out, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int csa2_workspace_status(const void* workspace, uint32_t* out, void* stream) {
   if (!workspace || !out) return CSA2_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return CSA2_ERR_ALIGNMENT;

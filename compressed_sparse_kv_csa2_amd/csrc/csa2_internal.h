@@ -42,7 +42,7 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
                        int batch, int n_cols, int k, int32_t* out, float* sout, int own_k,
                        int32_t* own_out, const uint16_t* q_re, int n_re, int re_k,
                        int32_t* re_out, float* re_sout, bool chain_ws, void* ws,
-                       hipStream_t stream);
+                       hipStream_t stream, const float* smat = nullptr);
 
 size_t index_topk_ws_bytes(int batch, int n_cols);
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
@@ -55,6 +55,12 @@ hipError_t launch_select_chain(const uint16_t* q_full, const uint8_t* codes, con
                                int n_cols, int pool_k, int32_t* pool_out, float* pool_score_out,
                                int k, int32_t* own_out, const uint16_t* q_re, int n_re,
                                int32_t* re_out, float* re_score_out, void* ws, hipStream_t stream);
+
+size_t replay_select_ws_bytes(int T, int n_entries, int pool_k);
+hipError_t launch_replay_select(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
+                                int n_entries, int ratio, int64_t pos0, int T, int pool_k,
+                                int32_t* pool_out, int32_t* pool_n_out, int k, int32_t* own_out,
+                                void* ws, hipStream_t stream);
 
 int topk_chunk_iters(int n_cols);
 int topk_n_chunks(int n_cols);
@@ -84,6 +90,13 @@ hipError_t launch_attn(int mode, const uint16_t* q, const uint8_t* kv_codes, con
 
 // ---- prefill ----
 size_t prefill_ws_bytes(int T, int n_entries, int k);
+// S[t][j] for the entries j that position pos0 + t sees (blocked: at (j / 1024 * T + t) *
+// 1024 + j % 1024, T * round_up(n_entries, 1024) floats; else row-major), each row's visible
+// count and, when pool_n is given, min(visible, pool_k)
+hipError_t launch_causal_scores(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                                int n_entries, int ratio, int64_t pos0, int T, bool blocked,
+                                float* scores, int32_t* n_vis, int pool_k, int32_t* pool_n,
+                                hipStream_t stream);
 hipError_t launch_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes,
                                  const float* idx_scale, int n_entries, int ratio, int64_t pos0,
                                  int T, int k, int32_t* idx_out, void* ws, hipStream_t stream);

@@ -11,42 +11,37 @@
 // padded.  Inside the pool, "column" means the pool position, which ascends with the
 // entry id, so ties again go to the lowest entry.
 //
-// Design: a filtered scan, then a selection over the survivors.  The pool is 1.6 % of a
-// 2^20-entry row, so the scan need not keep every key until the row's threshold is
-// known: given a lower bound theta of the k-th key, each chunk of columns writes out only
-// its keys >= theta (the candidates), and a second launch selects the exact top-k of each
-// row among its candidates.
-//   k_fscan, one persistent workgroup per compute unit:
-//   * Work is a list of tasks claimed from one atomic counter: first each long row's
-//     sample tasks (1,024 keys each: one column in 32, in groups of 64 spread evenly over
-//     the row), then every row's chunks of 15 x 64 x 2 columns, row after row.  Chunks go
-//     to whichever workgroup is free, so compute units that stream faster take more.
-//   * theta of a row is an order statistic of its sample, chosen so that about
-//     k + 4 sqrt(k) keys of the row are expected above it; the last sample task of the
-//     row computes it.  Exactness never rests on it: when fewer than k keys of the row
-//     turn out to be >= theta, or more than the selection holds, the selection scans the
-//     row again keeping every key (slow, counted in the workspace).  Rows short enough
-//     for the selection to hold whole use theta = 1 (every valid key).
-//   * A workgroup is 15 streaming waves and one writer wave.  The streaming waves score a
-//     chunk's columns into LDS with the next chunk's loads already in flight; meanwhile the
-//     writer wave claims the next chunk and appends the previous chunk's keys >= theta
-//     (in column order) to the row's candidate store, at a place it reserves with one
-//     atomic add.  Stores never sit in a streaming wave's memory counter, so they never
-//     hold up its loads.
-//   * Only the writer of a chunk waits on other workgroups (for its row's theta), and the
-//     sample tasks it waits for were claimed earlier by running workgroups that wait on
-//     nothing: the launch needs no co-residency.
-//   k_fselect, one workgroup per row:
-//   * one round of coalesced loads brings the row's candidates (keys to LDS, columns to
-//     registers) and each chunk's place in the store; the k-th composite (key, lower
-//     column first) is found by narrowing 4,096-bin histograms over the range the keys
-//     actually span until at most 64 remain, which are ranked directly.  A winner's output
-//     position is the number of winners in the chunks before its own (column order) plus
-//     those before it in its chunk's run, from a bitmap over the store.  The chained
-//     selections run on the same candidates (own top-k) or on the pool's re-scores
-//     (Reindex), which the writer computed as it stored each candidate.
-// The launch boundary orders the candidate stores before the selection.  The selection
-// returns the scan's counters to zero, so the workspace needs no clearing between calls.
+// Design: a segmented scan, then a selection over the survivors.  The pool is 1.6 % of a
+// 2^20-entry row, so the scan need not keep every key until the row's threshold is known:
+// each segment of a row keeps only as many of its best keys as the row's top-k can
+// plausibly hold there, and a second launch selects the exact top-k among them.
+//   k_fseg, one workgroup per (row, segment of `seg` columns; seg a power of two in
+//   [1024, 16384], the longest that still gives every compute unit a workgroup):
+//   * scores its columns into LDS (the Full scan's arithmetic), counting the valid ones
+//     and their largest key;
+//   * keeps every key at or above the lower edge of the 4,096-value bin holding its
+//     seg_keep-th key (bins over the 2^24 key values below the largest, then over the rest
+//     when that window holds too few): whole bins, so equal keys stay together and every
+//     key left out is below every key kept;
+//   * writes the kept keys and columns in column order to its own run of the row's store
+//     (ranks from wave ballots, no atomics), and their count, flagged when keys were left
+//     out; when chained, the kept entries' Reindex re-scores follow.
+//   k_fpick, rows x (S + R) workgroups, S slices of the output and R chained selections:
+//   * every workgroup loads the row's segment counts, their prefix (the dense index of the
+//     candidates in column order), each candidate's store slot, then all of its keys;
+//   * the k-th composite (key, lower column first) comes from a histogram of the 2^24 key
+//     values below the largest and one of the exact values in the bin that holds it (the
+//     general digit-by-digit search when the window does not hold it); one ballot pass
+//     marks the winners in a bitmap whose prefix is each winner's output position;
+//   * exactness: a flagged segment whose kept keys all won may have left a winner out;
+//     then (or when the candidates exceed what the selection holds) the row is scored
+//     again keeping every key (slow, counted in the workspace's status block);
+//   * slices write their share of the output; a chained selection (own top-k, or a
+//     Reindex layer's top-k over the pool's re-scores, in pool order) runs in one
+//     workgroup of its own.
+// The launch boundary orders the candidate stores before the selection, and no workgroup
+// waits on another.  The last workgroup of a row returns its counter to zero, so the
+// workspace needs no clearing between calls.
 #include <cmath>
 
 #include "csa2_internal.h"
@@ -108,6 +103,8 @@ struct FsArgs {
   const int64_t* seq_base;
   const int32_t* n_valid;
   const int32_t* cand;        // [batch][n_cols] (Reindex) or null
+  const float* smat;          // scores already computed (see smat_at) or null
+  int smat_rows;              // rows of the score matrix
   int n_cols, runs;           // columns, segments per row at most
   int seg;                    // columns per segment (a power of two in [1024, 16384])
   int row0, rows, batch;
@@ -794,6 +791,50 @@ __global__ __launch_bounds__(kT) void k_fseg(FsArgs a) {
   if (tid == 0) FS_TR(blockIdx.x * 8 + 4, FS_NOW());
 }
 
+// Score-matrix variant (a chunk of queries scored by one contraction): column c of row b is
+// at smat_at(a, b, c), in blocks of 1,024 columns that each hold every row.  The keys go
+// straight to registers and only the cut needs LDS, so two workgroups share a compute unit
+// and one's loads overlap the other's cut.
+__device__ __forceinline__ size_t smat_at(const FsArgs& a, int b, int c) {
+  return ((size_t)(c >> 10) * (size_t)a.smat_rows + (size_t)b) * 1024u + (size_t)(c & 1023);
+}
+
+__global__ __launch_bounds__(kT) void k_fseg_mat(FsArgs a) {
+  __shared__ Core L;
+  const int tid = threadIdx.x;
+  const int r = (int)blockIdx.x / a.runs, j = (int)blockIdx.x % a.runs;
+  const int b = a.row0 + r;
+  const int n = max(0, min(a.n_valid[b], a.n_cols));
+  if (j >= row_segs(n, a.seg)) return;
+  const int c0 = j * a.seg, len = max(0, min(n - c0, a.seg));
+  float v[kSegU];
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u)
+    v[u] = tid + kT * u < len ? __builtin_nontemporal_load(a.smat + smat_at(a, b, c0 + tid + kT * u)) : 0.f;
+  uint32_t kv[kSegU], cnt = 0u, mx = 0u;  // every column < n is valid
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    const bool in = tid + kT * u < len;
+    kv[u] = in ? score_key(v[u]) : 0u;
+    cnt += in ? 1u : 0u;
+    mx = max(mx, kv[u]);
+  }
+  block_sum_max(cnt, mx, L);  // ends with a barrier
+  const uint32_t cut = seg_cut(kv, seg_keep(a.k, len, n), cnt, mx, L);
+  const size_t rb = (size_t)r * a.cap + (size_t)j * a.seg;
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) mine |= (kv[u] != 0u && kv[u] >= cut ? 1u : 0u) << u;
+  const uint32_t kept = emit_reg<kSegU>(
+      mine,
+      [&](uint32_t rank, int u, int i) {
+        a.ckey[rb + rank] = kv[u];
+        a.ccol[rb + rank] = (uint32_t)(c0 + i);
+      },
+      L);
+  if (tid == 0) a.ccnt[(size_t)r * a.runs + j] = kept | (kept < cnt ? kTrunc : 0u);
+}
+
 // ------------------------------------------------------------------ k_fpick
 // Grid: rows x S workgroups; workgroup (r, s) loads every candidate key of row r (in
 // column order: chunk after chunk, each chunk's run in column order), finds the row's
@@ -892,10 +933,19 @@ __device__ __forceinline__ void rescan_row(const FsArgs& a, int r, int n) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int quarter = lane & 3, ent = lane >> 2;
   const int b = a.row0 + r;
-  const int64_t base = a.seq_base[b];
   const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
   uint32_t* ck = a.ckey + (size_t)r * a.cap;
   uint32_t* cc = a.ccol + (size_t)r * a.cap;
+  if (a.smat) {  // the scores are given
+    for (int col = tid; col < n; col += kT) {
+      st_ag(&ck[col], score_key(a.smat[smat_at(a, b, col)]));
+      st_ag(&cc[col], (uint32_t)col);
+    }
+    wait_vm();
+    __syncthreads();
+    return;
+  }
+  const int64_t base = a.seq_base[b];
   bf16x2 q[16];
   load_q(a.q + (size_t)b * kDIdx, quarter, q);
   for (int g = wave * 64; g < n; g += kT) {
@@ -1191,14 +1241,40 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
           orow[pos] = CAND ? cand_row[col] : (int32_t)col;
           if (srow) srow[pos] = key_score(ck[slot]);
         }
-      } else if (s < S) {
-        // this workgroup's slice of the output, a thread per rank: its winner by bitmap rank
+      } else if (s < S && n_pool <= (uint32_t)kT * (uint32_t)S) {
+        // this workgroup's slice of the output, one rank per thread: its winner by bitmap rank
         const uint32_t q0 = (uint32_t)((long long)s * n_pool / S), q1 = (uint32_t)((long long)(s + 1) * n_pool / S);
-        for (uint32_t q = q0 + tid; q < q1; q += kT) {
+        const uint32_t q = q0 + (uint32_t)tid;
+        if (q < q1) {
           const uint32_t slot = slot_of(L, nth_bit(L.bm, L.wp, (m + 31) / 32, q), a.seg);
           const uint32_t col = cc[slot];
           orow[q] = CAND ? cand_row[col] : (int32_t)col;
           if (srow) srow[q] = key_score(ck[slot]);
+        }
+      } else if (s < S) {
+        // few slices for many winners: this workgroup's candidates in blocks of eight per
+        // thread (candidate i = tid + kT u), each block's slots first, then all of its loads
+        // in flight, then each winner written at its bitmap position
+        const uint32_t i0 = (uint32_t)((long long)s * m / S), i1 = (uint32_t)((long long)(s + 1) * m / S);
+        constexpr int kB = 8;
+        static_assert(kU % kB == 0, "whole blocks");
+        for (int u0 = 0; u0 < kU; u0 += kB) {
+          if (kT * u0 >= (int)i1) break;  // uniform: the rest is past the slice
+          uint32_t sl[kB], col[kB];
+#pragma unroll
+          for (int v = 0; v < kB; ++v) {
+            const uint32_t i = (uint32_t)(tid + kT * (u0 + v));
+            sl[v] = i >= i0 && i < i1 && bit_at(L.bm, i) ? slot_of(L, i, a.seg) : ~0u;
+          }
+#pragma unroll
+          for (int v = 0; v < kB; ++v) col[v] = sl[v] != ~0u ? cc[sl[v]] : 0u;
+#pragma unroll
+          for (int v = 0; v < kB; ++v)
+            if (sl[v] != ~0u) {
+              const uint32_t pos = bits_before(L.bm, L.wp, (uint32_t)(tid + kT * (u0 + v)));
+              orow[pos] = CAND ? cand_row[col[v]] : (int32_t)col[v];
+              if (srow) srow[pos] = key_score(ck[sl[v]]);
+            }
         }
       }
       if (s < S) {
@@ -1334,7 +1410,7 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
                        int batch, int n_cols, int k, int32_t* out, float* sout, int own_k,
                        int32_t* own_out, const uint16_t* q_re, int n_re, int re_k,
                        int32_t* re_out, float* re_sout, bool chain_ws, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, const float* smat) {
   const FsShape s = fs_shape(batch, n_cols, chain_ws);
   const FsParts f = fs_carve(static_cast<char*>(ws), s, chain_ws);
   const int cap_wg = fs_capacity();
@@ -1346,6 +1422,8 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
   a.seq_base = seq_base;
   a.n_valid = n_valid;
   a.cand = cand;
+  a.smat = smat;
+  a.smat_rows = batch;
   a.n_cols = n_cols;
   a.runs = s.runs;
   a.batch = batch;
@@ -1382,6 +1460,9 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
     if (cand) {
       hipLaunchKernelGGL(k_fseg<true>, g_seg, dim3(kT), 0, stream, a);
       hipLaunchKernelGGL(k_fpick<true>, g_pick, dim3(kT), 0, stream, a, S);
+    } else if (smat) {
+      hipLaunchKernelGGL(k_fseg_mat, g_seg, dim3(kT), 0, stream, a);
+      hipLaunchKernelGGL(k_fpick<false>, g_pick, dim3(kT), 0, stream, a, S);
     } else {
       hipLaunchKernelGGL(k_fseg<false>, g_seg, dim3(kT), 0, stream, a);
       hipLaunchKernelGGL(k_fpick<false>, g_pick, dim3(kT), 0, stream, a, S);

@@ -1,7 +1,8 @@
-// csa2_index_topk and csa2_select_chain: the scan and its selections in one launch of the
-// filtered selection (fsel.hip) for rows up to its length limit; longer rows take the
-// separate scan (index_score.hip, scores written out) and top-k (topk.hip) launches inside
-// the same call, with the same results.
+// csa2_index_topk and csa2_select_chain: the scan and its selections in the two launches of
+// the filtered selection (fsel.hip) for rows whose candidates it can hold; longer rows take
+// the separate scan (index_score.hip, scores written out) and top-k (topk.hip) launches
+// inside the same call, with the same results.  csa2_replay_select: the causal score matrix
+// of a chunk of queries (prefill.hip's contraction), then the same selections on it.
 #include "csa2_internal.h"
 #include "select_device.h"
 
@@ -108,6 +109,60 @@ hipError_t launch_select_chain(const uint16_t* q_full, const uint8_t* codes, con
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// csa2_replay_select: [selection part][score matrix f32][visible counts i32 T].  The
+// selection part is the filtered selection's workspace (rows it takes; the matrix blocked)
+// or, for longer rows, [status][top-k workspace][pool scores f32 T x pool_k][pool sizes i32
+// T] (the matrix row-major, as csa2_topk reads it).
+// A sequence with no entries runs the longer-row path on one column that no row sees.
+static size_t replay_sel_bytes(int T, int n_entries, int pool_k) {
+  if (fsel_fits(n_entries, pool_k)) return fsel_ws_bytes(T, n_entries, false);
+  const int n_cols = max(n_entries, 1);
+  return kStatusBlock + topk_ws_bytes(T, n_cols) + align_up((size_t)T * pool_k * 4, 256) +
+         align_up((size_t)T * 4, 256);
+}
+
+// the matrix, blocked (whole blocks of 1,024 columns) or row-major
+static size_t replay_scores_bytes(int T, int n_entries) {
+  return align_up((size_t)T * align_up((size_t)max(n_entries, 1), 1024) * 4, 256);
+}
+
+size_t replay_select_ws_bytes(int T, int n_entries, int pool_k) {
+  return replay_sel_bytes(T, n_entries, pool_k) + replay_scores_bytes(T, n_entries) +
+         align_up((size_t)T * 4, 256);
+}
+
+hipError_t launch_replay_select(const uint16_t* q_idx, const uint8_t* codes, const float* scale,
+                                int n_entries, int ratio, int64_t pos0, int T, int pool_k,
+                                int32_t* pool_out, int32_t* pool_n_out, int k, int32_t* own_out,
+                                void* ws, hipStream_t stream) {
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + replay_sel_bytes(T, n_entries, pool_k));
+  int32_t* vis = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scores) + replay_scores_bytes(T, n_entries));
+  const bool fits = n_entries > 0 && fsel_fits(n_entries, pool_k);
+  if (fits) {
+    hipError_t e = launch_causal_scores(q_idx, codes, scale, n_entries, ratio, pos0, T, true, scores, vis,
+                                        pool_k, pool_n_out, stream);
+    if (e != hipSuccess) return e;
+    return launch_fsel(nullptr, nullptr, nullptr, nullptr, vis, nullptr, T, n_entries, pool_k, pool_out,
+                       nullptr, k, own_out, nullptr, 0, 0, nullptr, nullptr, false, ws, stream, scores);
+  }
+  // longer rows (or no entries): a row-major matrix and csa2_topk's kernels
+  const int n_cols = n_entries > 0 ? n_entries : 1;  // a row of nothing visible
+  char* p = base + kStatusBlock;
+  const TopkWs tw = topk_ws_carve(p, T, n_cols);
+  float* pool_scores = reinterpret_cast<float*>(p + topk_ws_bytes(T, n_cols));
+  int32_t* pool_n = pool_n_out ? pool_n_out
+                               : reinterpret_cast<int32_t*>(reinterpret_cast<char*>(pool_scores) +
+                                                            align_up((size_t)T * pool_k * 4, 256));
+  hipError_t e = launch_causal_scores(q_idx, codes, scale, n_entries, ratio, pos0, T, false, scores, vis,
+                                      pool_k, pool_n, stream);
+  if (e == hipSuccess)
+    e = launch_topk(scores, T, n_cols, vis, nullptr, pool_k, pool_out, pool_scores, false, tw, stream);
+  if (e == hipSuccess && own_out)
+    e = launch_topk(pool_scores, T, pool_k, pool_n, pool_out, k, own_out, nullptr, false, TopkWs{}, stream);
+  return e;
 }
 
 }  // namespace csa2

@@ -1,9 +1,9 @@
 """One decode step of the 40-layer CSA2 backbone, sequenced through the C ABI.
 
 Sequencing only: every step runs in the library's kernels (csa2_index_topk,
-csa2_select_chain, csa2_index_score + csa2_topk, csa2_sparse_attn_decode,
-csa2_sparse_attn_prefill); this module holds workspaces and output buffers and issues the
-calls in layer order on one stream.
+csa2_select_chain, csa2_replay_select, csa2_index_score + csa2_topk,
+csa2_sparse_attn_decode, csa2_sparse_attn_prefill); this module holds workspaces and output
+buffers and issues the calls in layer order on one stream.
 
 Layer layout ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash", Q&A on how the
 40 layers are laid out, and commentary on the four layer modes; "从V4到V4.1 Flash：架构的
@@ -25,9 +25,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (attn_workspace, csa2_index_score, csa2_index_topk, csa2_select_chain,
-               csa2_sparse_attn_decode, csa2_sparse_attn_prefill, csa2_topk, index_topk_workspace,
-               select_chain_workspace, topk_workspace)
+from . import (attn_workspace, csa2_index_score, csa2_index_topk, csa2_replay_select,
+               csa2_select_chain, csa2_sparse_attn_decode, csa2_sparse_attn_prefill, csa2_topk,
+               index_topk_workspace, replay_select_workspace, select_chain_workspace,
+               topk_workspace)
 
 N_LAYERS = 40
 WINDOW_ONLY = (0, 1)
@@ -114,10 +115,11 @@ class ReplayChunk:
     DeepSeek-V4.1-Flash", content summary and Q&A on prefill: on eviction or restore only the
     last 128 tokens of the decoder are replayed; "从V4到V4.1 Flash：架构的激进进化", decoder
     section).  The decoder's global KV has ratio 1, so entry j is token j and query t sees
-    entries 0 .. pos0 + t.  Per query, as in decode: the Full layer (20) scans every visible
-    entry, keeps its top-16,384 as the query's pool and its own top-512 inside it; each
-    Reindex layer re-scores that query's pool; every layer attends over its list and its own
-    causal window.
+    entries 0 .. pos0 + t.  Per query, as in decode: the Full layer (20) scores every visible
+    entry, keeps its top-16,384 as the query's pool and its own top-512 inside it
+    (csa2_replay_select: one MFMA contraction reads the keys once for all T queries, and the
+    library derives each query's visible entries from pos0); each Reindex layer re-scores
+    that query's pool; every layer attends over its list and its own causal window.
 
     After step(): pool (int32 [T, pool]), lists[l] (int32 [T, k]) for 20, 24, 28, 32, 36 and
     out[l - 20] (f32 [T, 16, 512]) for layers 20..39."""
@@ -126,15 +128,13 @@ class ReplayChunk:
                  device="cuda"):
         self.T, self.n, self.pos0, self.P, self.K = T, n_entries, pos0, pool, k
         dev = torch.device(device)
-        self.sel_ws = select_chain_workspace(T, n_entries, pool, device=dev)
+        self.sel_ws = replay_select_workspace(T, n_entries, pool, device=dev)
         self.attn_ws = attn_workspace(T, k, device=dev)
         self.re_ws = topk_workspace(T, pool, k, device=dev)  # Reindex: re-score, then select
         self.re_scores = torch.empty((T, pool), dtype=torch.float32, device=dev)
         self.seq_base = torch.zeros((T,), dtype=torch.int64, device=dev)
-        vis = torch.arange(pos0 + 1, pos0 + T + 1, dtype=torch.int64).clamp(max=n_entries)
-        self.n_visible = vis.to(torch.int32).to(dev)
         self.pool = torch.empty((T, pool), dtype=torch.int32, device=dev)
-        self.pool_valid = self.n_visible.clamp(max=pool).contiguous()
+        self.pool_valid = torch.empty((T,), dtype=torch.int32, device=dev)  # written by the selection
         self.lists = {l: torch.empty((T, k), dtype=torch.int32, device=dev)
                       for l in (DECODER_FULL,) + REINDEX}
         self.out = torch.empty((N_LAYERS - DECODER_FULL, T, 16, 512), dtype=torch.float32, device=dev)
@@ -150,9 +150,9 @@ class ReplayChunk:
         before the Full selection, after it, at the end."""
         if marks is not None:
             marks[0].record(stream)
-        csa2_select_chain(q_idx[DECODER_FULL], cache.idx_codes, cache.idx_scale, self.seq_base,
-                          self.n_visible, self.n, self.pool, self.sel_ws, k=self.K,
-                          own_out=self.lists[DECODER_FULL], stream=stream)
+        csa2_replay_select(q_idx[DECODER_FULL], cache.idx_codes, cache.idx_scale, self.n, 1, self.pos0,
+                           self.pool, self.sel_ws, k=self.K, own_out=self.lists[DECODER_FULL],
+                           pool_n_out=self.pool_valid, stream=stream)
         if marks is not None:
             marks[1].record(stream)
         for l in range(DECODER_FULL, N_LAYERS):

@@ -165,12 +165,14 @@ size_t csa2_index_topk_workspace_size(int32_t batch, int32_t n_cols, int32_t k);
  *              before its first use; each call leaves it ready for the next call of the
  *              same shape.  It starts with a status block (csa2_workspace_status).  Calls
  *              sharing one workspace must not run concurrently.
- * Rows of up to 3,932,160 columns run as two launches: a filtered scan (any number of
- * workgroups, no co-residency needed: workgroups claim chunks of columns from a counter
- * and keep only keys at or above a threshold estimated from a sample of the row) and one
- * selecting workgroup per row.  The result never depends on the estimate; a row whose
- * estimate was too high is scanned again by its selecting workgroup (slower, counted in
- * the status block).  Longer rows run csa2_index_score's and csa2_topk's kernels.
+ * Two launches when the selection can hold the row's candidates: one workgroup per
+ * segment of the row keeps the segment's best keys (enough of them for every key of the
+ * row's top-k unless the row is far from typical), then each row's exact top-k is taken
+ * among them.  No workgroup waits on another, so no co-residency is needed.  A row whose
+ * segments left out a key of its top-k is detected and scored again by one workgroup
+ * (slower, counted in the status block); the result never depends on the cut.  Rows
+ * where k + 6 sqrt(k s) + 7 s > 24,576 for s segments of 16,384 columns (a pool of 16,384
+ * beyond 1,556,480 columns) run csa2_index_score's and csa2_topk's kernels.
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_cols > 2^26), HIP.
  */
 int csa2_index_topk(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
@@ -203,10 +205,10 @@ size_t csa2_select_chain_workspace_size(int32_t batch, int32_t n_cols, int32_t p
  *   re_score_out   f32 [n_re][batch][k] or NULL (out), their scores
  *   workspace      as csa2_index_topk (zero-filled before first use, left ready; starts
  *                  with the status block)
- * Outputs are bit-identical to the separate calls named above.  Rows of up to 3,932,160
- * columns run the two launches of csa2_index_topk, the Reindex re-scores computed for
- * the scan's candidates as they are written and every selection made by the row's
- * selecting workgroup; longer rows run the separate calls.
+ * Outputs are bit-identical to the separate calls named above.  Rows that csa2_index_topk
+ * runs as two launches do so here too: the segments compute the Reindex re-scores of the
+ * keys they keep as they write them, and each chained selection takes one workgroup of
+ * the second launch.  Other rows run the separate calls.
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_cols > 2^26), HIP.
  */
 int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const float* idx_scale,
@@ -216,18 +218,56 @@ int csa2_select_chain(const uint16_t* q_full, const uint8_t* idx_codes, const fl
                       int32_t* re_out, float* re_score_out, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* Bytes of workspace csa2_replay_select needs for this shape. */
+size_t csa2_replay_select_workspace_size(int32_t T, int32_t n_entries, int32_t pool_k);
+
 /*
- * csa2_workspace_status -- reads the status block at the start of a csa2_index_topk or
- * csa2_select_chain workspace.  Enqueues a 12-byte copy on `stream` and synchronizes the
+ * csa2_replay_select -- the Full layer's selections for T consecutive query positions of
+ * one sequence (the decoder's bounded replay): per query, the pool of its pool_k best
+ * visible entries and its own top-k inside that pool, by the rule csa2_select_chain
+ * applies to one decode query.
+ *   [STRUCT] content summary and Q&A on prefill (on eviction or restore the decoder replays
+ *   only its last 128 tokens); [V4TO41] decoder section (a full scan yields a pool of about
+ *   16K positions, later layers pick their top-512 inside it) and the section on the
+ *   bounded window replay.
+ *
+ *   q_idx, idx_codes, idx_scale, n_entries, ratio, pos0, T   as csa2_prefill_chunk (query t
+ *              at position pos0 + t sees entries j < min(n_entries, (pos0 + t + 1) / ratio))
+ *   pool_k     1..16384
+ *   pool_out   i32 [T][pool_k] (out)   the query's pool_k best visible entries (ties to the
+ *              lower entry), ascending entry ids, -1 padded
+ *   pool_n_out i32 [T] or NULL (out)   valid entries of each pool, min(visible, pool_k): the
+ *              n_valid of a Reindex call on the pool
+ *   k          1..16384, read only when own_out is given
+ *   own_out    i32 [T][k] or NULL (out) the k best entries of each pool by the same scores,
+ *              ascending entry ids, -1 padded
+ *   workspace  device, 256-byte aligned, csa2_replay_select_workspace_size bytes (it holds
+ *              the T x n_entries score matrix), zero-filled before its first use; each call
+ *              leaves it ready.  It starts with the status block (csa2_workspace_status).
+ *              Calls sharing one workspace must not run concurrently.
+ * The scores come from csa2_prefill_chunk's MFMA contraction, which reads the keys once for
+ * all T queries, written out as a score matrix that the filtered selection of
+ * csa2_index_topk then selects from (csa2_topk's kernels for rows beyond its capacity).
+ * They are the same products as csa2_index_score's summed in another order, so a list can
+ * differ from a decode call's only where the last bits of fp32 rounding decide a tie.
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_entries > 2^26), HIP.
+ */
+int csa2_replay_select(const uint16_t* q_idx, const uint8_t* idx_codes, const float* idx_scale,
+                       int32_t n_entries, int32_t ratio, int64_t pos0, int32_t T, int32_t pool_k,
+                       int32_t* pool_out, int32_t* pool_n_out, int32_t k, int32_t* own_out,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_workspace_status -- reads the status block at the start of a csa2_index_topk,
+ * csa2_select_chain or csa2_replay_select workspace.  Enqueues a 12-byte copy on `stream` and synchronizes the
  * stream, so it reports on every call enqueued there before it.
  *   out  host u32 [2] (out):
- *     out[0]  sticky error bits, 0 after correct calls: bit 0 = a chunk waited too long
- *             for its row's threshold, bit 1 = a wave waited too long for its workgroup's
- *             next chunk.  Neither can happen while the calls run to completion; if one
- *             is set, that call's results are undefined and the workspace must be
- *             zero-filled again before its next use.
- *     out[1]  rows whose sampled threshold was too high since the workspace was
- *             zero-filled (each row so reported was selected exactly, by a second scan).
+ *     out[0]  error bits, reserved: always 0 (no kernel of these calls waits on another
+ *             workgroup, so none can give up waiting).
+ *     out[1]  rows selected by the slow path since the workspace was zero-filled: a
+ *             segment left out a key of the row's top-k, or the row's candidates exceeded
+ *             what the selection holds; each such row was scored again and selected
+ *             exactly.
  * Errors: INVALID_ARG (null pointers), ALIGNMENT (workspace not 256-byte aligned), HIP.
  */
 int csa2_workspace_status(const void* workspace, uint32_t* out, void* stream);

@@ -200,6 +200,23 @@ def test_prefill_select_validation(lib):
         assert f(*a) == want, (pos, val)
 
 
+def test_replay_select_validation(lib):
+    f = lib.csa2_replay_select
+    base = [FAKE, FAKE, FAKE, 1 << 20, 1, (1 << 20) - 128, 128, 16384, FAKE, FAKE, 512, FAKE, FAKE,
+            1 << 40, None]
+    for pos, val, want in [(6, 0, -1), (4, 0, -1), (5, -1, -1), (3, -1, -1), (7, 0, -1),
+                           (7, 16385, -1), (10, 0, -1), (10, 16385, -1), (0, None, -1),
+                           (8, None, -1), (1, None, -1), (0, ODD, -2), (9, ODD, -2), (11, ODD, -2),
+                           (13, 100, -3), (12, None, -3), (3, (1 << 26) + 1, -4)]:
+        a = list(base); a[pos] = val
+        assert f(*a) == want, (pos, val)
+    assert lib.csa2_replay_select_workspace_size(0, 1 << 20, 16384) == 0
+    assert lib.csa2_replay_select_workspace_size(128, 1 << 20, 0) == 0
+    # the score matrix dominates: T x n_entries fp32
+    assert lib.csa2_replay_select_workspace_size(128, 1 << 20, 16384) >= 128 * (1 << 20) * 4
+    assert lib.csa2_replay_select_workspace_size(4, 0, 64) > 0
+
+
 def test_binding_rejects_host_tensors():
     # no CPU fallback: the binding refuses tensors that are not on the GPU before any call
     import torch
