@@ -804,24 +804,27 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
 }
 
 // ------------------------------------------------------------ causal score matrix
-// The same contraction written out: S[t][j] = scale_j * (q_t . e2m1(K_j)) for every entry j
-// that position pos0 + t sees (columns a row does not see are left unwritten), each row's
-// visible count and, if asked, min(visible, pool_k).  For a replay chunk, whose queries each
-// keep a pool far larger than the prefill slots hold: the keys are read once for all the
-// queries and the selection runs on the matrix.  Layout: blocked, S[j / 1024][t][j % 1024]
-// (each workgroup writes one contiguous block), or row-major, S[t][j].  A workgroup owns 128
-// query rows (a wave per 32, one A operand set each) and one split of kScoreSplit entries
-// streamed through LDS as in k_prefill_gemm; each tile's 32 x 32 scores go straight from the
-// accumulators to memory (two 128-byte row pieces per store).
+// The same contraction written out: S[t][j] = scale_j * (q_t . e2m1(K_j)) for the entries j
+// that position pos0 + t sees, each row's visible count and, if asked, min(visible,
+// pool_k).  For a replay chunk, whose queries each keep a pool far larger than the prefill
+// slots hold: the keys are read once for all the queries and the selection runs on the
+// matrix.  Layout: blocked, S[j / 1024][t][j % 1024] (each workgroup writes one contiguous
+// block; columns a row does not see hold scores of no meaning), or row-major, S[t][j]
+// (columns a row does not see are left unwritten).  A workgroup owns 128 query rows (a
+// wave per 32) and one split of kScoreSplit entries streamed through LDS as in
+// k_prefill_gemm.  The product is taken transposed, entries x queries (the expanded keys
+// as the A operand), so that a lane's accumulators hold one query's scores for four runs
+// of four consecutive entries: 16-byte stores.
 constexpr int kScoreRows = 128;
 constexpr int kScoreSplit = 1024;
 static_assert(kScoreSplit == 1024, "a split is one block of the blocked layout");
+template <bool BLOCKED>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_causal_scores(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
-    const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, int blocked,
+    const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T,
     float* __restrict__ S, int32_t* __restrict__ n_vis, int pool_k, int32_t* __restrict__ pool_n) {
   __shared__ uint4 s_code[2][kStage * 4];
-  __shared__ float s_sc[2][kStage];
+  __shared__ float4 s_sc[2][kStage / 4];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kScoreRows;
   const int row0 = wg_row0 + wave * 32;
@@ -839,25 +842,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_causal_scores(
   const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
   if (n_active == 0) return;  // workgroup-uniform: before any barrier
 
-  // A operand: query row row0 + rl, dims 64*half .. +63; row of accumulator r and the
-  // entries it sees (0 past T: nothing written)
-  bf16x8 a[8];
+  // B operand: the lane's query t = row0 + rl, dims 64*half + 8kk .. +7 (the k-slice of lane
+  // half `half`, as the keys' A operand below)
+  const int t = row0 + rl;
+  bf16x8 qb[8];
   {
-    const int ar = min(row0 + rl, T - 1);
-    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)ar * kDIdx + 64 * half);
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)min(t, T - 1) * kDIdx + 64 * half);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) a[kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+    for (int kk = 0; kk < 8; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, qp[kk]);
   }
-  int nv[16];
-  float* srow[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    nv[r] = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
-    const size_t tc = (size_t)min(t, T - 1);
-    srow[r] = S + (blocked ? ((size_t)blockIdx.y * (size_t)T + tc) * kScoreSplit - (size_t)e_begin
-                           : tc * (size_t)n_entries);
-  }
+  const int nv = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
+  float* srow = S + (BLOCKED ? ((size_t)blockIdx.y * (size_t)T + (size_t)min(t, T - 1)) * kScoreSplit - (size_t)e_begin
+                             : (size_t)min(t, T - 1) * (size_t)n_entries);
 
   uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
   float psc = 0.f;
@@ -877,29 +873,40 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_causal_scores(
     s_code[buf][stage_blk(tid, 1)] = pc1;
     s_code[buf][stage_blk(tid, 2)] = pc2;
     s_code[buf][stage_blk(tid, 3)] = pc3;
-    s_sc[buf][tid] = psc;
+    reinterpret_cast<float*>(s_sc[buf])[tid] = psc;
     __syncthreads();
     if (st + 1 < n_active) load_stage(st + 1);  // in flight during the MFMAs
     const int st_e0 = e_begin + st * kStage;
     for (int tt = 0; tt < kStage / 32; ++tt) {
       const int e0 = st_e0 + tt * 32;
       if (e0 >= wave_nmax) break;  // wave-uniform: the rest is beyond every row of the wave
-      const int i = tt * 32 + rl;
+      const int i = tt * 32 + rl;  // A operand: entry e0 + rl
       const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
       const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
-      const float sc = s_sc[buf][i];
       const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], fp4x8_bf16(cw[kk]), acc, 0, 0, 0);
-      const int col = e0 + rl;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp4x8_bf16(cw[kk]), qb[kk], acc, 0, 0, 0);
+      // accumulator 4g + i: entry e0 + 8g + 4*half + i of query t
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (col < nv[r]) __builtin_nontemporal_store(acc[r] * sc, srow[r] + col);
+      for (int g = 0; g < 4; ++g) {
+        const float4 sc = s_sc[buf][tt * 8 + 2 * g + half];
+        const int col = e0 + 8 * g + 4 * half;
+        f32x4 v;
+        v[0] = acc[4 * g] * sc.x;
+        v[1] = acc[4 * g + 1] * sc.y;
+        v[2] = acc[4 * g + 2] * sc.z;
+        v[3] = acc[4 * g + 3] * sc.w;
+        if (BLOCKED) {
+          if (t < T) *reinterpret_cast<f32x4*>(srow + col) = v;
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (col + x < nv) srow[col + x] = v[x];
+        }
+      }
     }
-    // the other buffer is rewritten only after the next barrier, which every wave reaches
-    // after its reads of this stage
   }
 }
 
@@ -910,8 +917,12 @@ hipError_t launch_causal_scores(const uint16_t* q_idx, const uint8_t* idx_codes,
   // at least one split, so that the visible counts are written when nothing is visible
   const dim3 grid((unsigned)((T + kScoreRows - 1) / kScoreRows),
                   (unsigned)(n_entries > 0 ? (n_entries + kScoreSplit - 1) / kScoreSplit : 1));
-  hipLaunchKernelGGL(k_causal_scores, grid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale,
-                     n_entries, ratio, pos0, T, blocked ? 1 : 0, scores, n_vis, pool_k, pool_n);
+  if (blocked)
+    hipLaunchKernelGGL(k_causal_scores<true>, grid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
+                       idx_scale, n_entries, ratio, pos0, T, scores, n_vis, pool_k, pool_n);
+  else
+    hipLaunchKernelGGL(k_causal_scores<false>, grid, dim3(kGemmThreads), 0, stream, q_idx, idx_codes,
+                       idx_scale, n_entries, ratio, pos0, T, scores, n_vis, pool_k, pool_n);
   return hipGetLastError();
 }
 
