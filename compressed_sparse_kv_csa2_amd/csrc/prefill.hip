@@ -132,6 +132,13 @@ __device__ __forceinline__ float vmax(float a, float b) {
   return r;
 }
 
+// v_max3_f32, likewise without quieting.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Lane masks of a >= b (floats) and a <= b (ints), straight from v_cmp (every lane active).
 __device__ __forceinline__ uint64_t mask_ge(float a, float b) {
   uint64_t m;
@@ -388,6 +395,197 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
     if (row0 + lane < T)
       ws.ccount[(size_t)(row0 + lane) * ws.n_splits + split] = s_rcnt[wave * kWaveRows + lane];
   }
+}
+
+// PASS 2: the candidates.  The same contraction over every entry, taken transposed (the
+// expanded keys as the A operand, entries x queries): lane l of a wave holds, for its
+// query row0 + 32 s + l % 32, the scores of entries e0 + 8 g + 4 (l / 32) + i (accumulator
+// 4 g + i).  Hits (scores >= the row's threshold) are rare, about one score in 200, so a
+// lane only tests the largest of its 16 scores per tile; a row that may hold a hit gets a
+// record of its 32 scores of the tile in the wave's LDS queue (both of its lanes write
+// their half; positions from the ballot), and once 32 records are queued each lane sorts
+// out half a record.  Slots of a (row, split) list come from the row's LDS counter, taken
+// in queue order, so the list is in entry order as long as the counter serves the lanes of
+// one atomic in lane order; the select checks that and ranks the list itself otherwise.
+constexpr int kRec = 32;                    // queue record: 32 scores (dwords)
+constexpr int kRecBatch = 32;               // records drained at once (two lanes each)
+constexpr int kRecQueue = 2 * kRecBatch;    // a batch + one tile's worth
+static_assert(kRecBatch % 8 == 0, "moving a record by a batch keeps its slot swizzle");
+// 16-byte slot q of record j sits at slot q ^ (j & 7): the lanes of one write (consecutive
+// records, same q) then fall on different banks
+__device__ __forceinline__ int rec_slot(uint32_t j, int q) { return (int)(j * (kRec / 4)) + (q ^ (int)(j & 7u)); }
+__global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
+    const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
+  __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
+  __shared__ float4 s_sc[2][kStage / 4];
+  __shared__ uint32_t s_rcnt[kGemmRows];     // candidates of each of the workgroup's rows
+  __shared__ float s_th[kGemmRows];          // each row's threshold (+inf past T)
+  __shared__ int s_nv[kGemmRows];            // entries each row sees
+  __shared__ float4 s_rec[4][kRecQueue * kRec / 4];
+  __shared__ uint32_t s_rtag[4][kRecQueue];  // record's row | tile offset in the split << 8
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wg_row0 = blockIdx.x * kGemmRows;
+  const int row0 = wg_row0 + wave * kWaveRows;
+  const int split = blockIdx.y;
+  const int e_begin = split * kSplitEntries;
+  const int e_end = min(e_begin + kSplitEntries, n_entries);
+  const int rl = lane & 31, half = lane >> 5;
+  const int wg_nmax = visible(pos0 + min(wg_row0 + kGemmRows - 1, T - 1), ratio, n_entries);
+  const int wave_nmax = row0 < T ? visible(pos0 + min(row0 + kWaveRows - 1, T - 1), ratio, n_entries) : 0;
+  const int e_stop = min(e_end, wg_nmax);
+  const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
+  static_assert(kGemmThreads == kGemmRows, "one row of the workgroup per thread");
+  {
+    const int t = wg_row0 + tid;
+    s_rcnt[tid] = 0u;
+    s_th[tid] = t < T ? ws.theta[t] : __builtin_inff();
+    s_nv[tid] = t < T ? visible(pos0 + t, ratio, n_entries) : 0;
+  }
+  // B operands: query row0 + 32 s + rl, dims 64*half .. +63, and its threshold
+  bf16x8 qb[kSets][8];
+  float th[kSets];
+#pragma unroll
+  for (int s = 0; s < kSets; ++s) {
+    const int t = row0 + 32 * s + rl;
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)min(t, T - 1) * kDIdx + 64 * half);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qb[s][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+    th[s] = t < T ? ws.theta[t] : __builtin_inff();
+  }
+  __syncthreads();
+
+  float4* rq = s_rec[wave];
+  uint32_t* rt = s_rtag[wave];
+  uint32_t qn = 0;  // queued records (wave-uniform)
+  // Lane L takes half L % 2 of record L / 2 of the first n: that half's hits (visible
+  // entries only) go to its row's next slots.
+  auto drain = [&](uint32_t n) {
+    const uint32_t j = (uint32_t)lane >> 1, part = (uint32_t)lane & 1u;
+    if (j < n) {
+      const uint32_t tag = rt[j];
+      const int lr = (int)(tag & 255u);                        // row within the workgroup
+      const int eb = e_begin + (int)(tag >> 8) + 16 * (int)part;  // entry of this half's score 0
+      const float thr = s_th[lr];
+      const int nvr = s_nv[lr];
+      float v[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 x = rq[rec_slot(j, 4 * (int)part + g)];
+        v[4 * g] = x.x;
+        v[4 * g + 1] = x.y;
+        v[4 * g + 2] = x.z;
+        v[4 * g + 3] = x.w;
+      }
+      uint32_t hm = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hm |= (v[r] >= thr ? 1u : 0u) << r;
+      const int nvis = nvr - eb;  // visible entries among this half's 16
+      if (nvis < 16) hm &= nvis > 0 ? (1u << nvis) - 1u : 0u;
+      if (hm != 0u) {
+        uint32_t slot = atomicAdd(&s_rcnt[lr], (uint32_t)__popc(hm));
+        const size_t base = ((size_t)(wg_row0 + lr) * ws.n_splits + split) * kSlots;
+        while (hm != 0u) {
+          const int r = __builtin_ctz(hm);
+          hm &= hm - 1u;
+          if (slot < (uint32_t)kSlots)
+            ws.cand[base + slot] = ((unsigned long long)score_key(v[r]) << 32) | (uint32_t)(eb + r);
+          ++slot;
+        }
+      }
+    }
+  };
+
+  uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
+  float psc = 0.f;
+  auto load_stage = [&](int st) {
+    const int e = min(e_begin + st * kStage + tid, n_entries - 1);
+    const uint4* cp = reinterpret_cast<const uint4*>(codes + (size_t)e * kIdxCodeBytes);
+    pc0 = cp[0];
+    pc1 = cp[1];
+    pc2 = cp[2];
+    pc3 = cp[3];
+    psc = scale[e];
+  };
+  if (n_active > 0) load_stage(0);
+  for (int st = 0; st < n_active; ++st) {
+    const int buf = st & 1;
+    s_code[buf][stage_blk(tid, 0)] = pc0;
+    s_code[buf][stage_blk(tid, 1)] = pc1;
+    s_code[buf][stage_blk(tid, 2)] = pc2;
+    s_code[buf][stage_blk(tid, 3)] = pc3;
+    reinterpret_cast<float*>(s_sc[buf])[tid] = psc;
+    __syncthreads();
+    if (st + 1 < n_active) load_stage(st + 1);  // in flight during the MFMAs
+    const int st_e0 = e_begin + st * kStage;
+    for (int tt = 0; tt < kStage / 32; ++tt) {
+      const int e0 = st_e0 + tt * 32;
+      if (e0 >= wave_nmax) break;  // wave-uniform: the rest of the stage is beyond every row
+      const int i = tt * 32 + rl;  // A operand: entry e0 + rl
+      const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
+      const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      f32x16 acc[kSets];
+#pragma unroll
+      for (int s = 0; s < kSets; ++s) acc[s] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 ka = fp4x8_bf16(cw[kk]);
+#pragma unroll
+        for (int s = 0; s < kSets; ++s)
+          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s][kk], acc[s], 0, 0, 0);
+      }
+      float4 sc[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) sc[g] = s_sc[buf][tt * 8 + 2 * g + half];
+#pragma unroll
+      for (int s = 0; s < kSets; ++s) {
+        float v[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          v[4 * g] = acc[s][4 * g] * sc[g].x;
+          v[4 * g + 1] = acc[s][4 * g + 1] * sc[g].y;
+          v[4 * g + 2] = acc[s][4 * g + 2] * sc[g].z;
+          v[4 * g + 3] = acc[s][4 * g + 3] * sc[g].w;
+        }
+        const float m0 = vmax3(v[0], v[1], v[2]), m1 = vmax3(v[3], v[4], v[5]), m2 = vmax3(v[6], v[7], v[8]);
+        const float m3 = vmax3(v[9], v[10], v[11]), m4 = vmax3(v[12], v[13], v[14]);
+        const float mx = vmax3(vmax3(m0, m1, m2), vmax3(m3, m4, v[15]), m0);
+        const uint64_t m = __ballot(mx >= th[s]);
+        if (m != 0ull) {  // wave-uniform
+          // rows (lane % 32) with a possible hit in either half: one record each
+          const uint32_t pm = (uint32_t)(m | (m >> 32));
+          if ((pm >> rl) & 1u) {
+            const uint32_t j = qn + (uint32_t)__popc(pm & ((1u << rl) - 1u));
+#pragma unroll
+            for (int g = 0; g < 4; ++g)  // entries 8 g + 4 half .. +3 of the tile
+              rq[rec_slot(j, 2 * g + half)] = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+            if (half == 0) rt[j] = (uint32_t)(wave * kWaveRows + 32 * s + rl) | ((uint32_t)(e0 - e_begin) << 8);
+          }
+          qn += (uint32_t)__popc(pm);
+          if (qn >= (uint32_t)kRecBatch) {
+            drain((uint32_t)kRecBatch);
+            // the rest (fewer than a batch) to the front, after every read of the batch (the
+            // wave's LDS operations complete in order)
+            const uint32_t rest = qn - (uint32_t)kRecBatch;
+            const uint32_t j = (uint32_t)lane >> 1, part = (uint32_t)lane & 1u;
+            if (j < rest) {
+              const float4* src = rq + (kRecBatch + j) * (kRec / 4) + 4 * part;
+              float4* dst = rq + j * (kRec / 4) + 4 * part;
+              const float4 x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
+              const uint32_t tg = rt[kRecBatch + j];
+              dst[0] = x0; dst[1] = x1; dst[2] = x2; dst[3] = x3;
+              if (part == 0) rt[j] = tg;
+            }
+            qn = rest;
+          }
+        }
+      }
+    }
+  }
+  drain(qn);
+  __syncthreads();
+  if (wg_row0 + tid < T) ws.ccount[(size_t)(wg_row0 + tid) * ws.n_splits + split] = s_rcnt[tid];
 }
 
 // ---------------------------------------------------------------------------- helpers
@@ -721,8 +919,8 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
       pmask |= 255ull << shift;
     }
     // ---- the selected candidates in ascending entry order: splits hold ascending entry
-    // ranges and a split's slots are in entry order, so each wave compacts one split's
-    // selected slots after the selected entries of the splits before it
+    // ranges, so each wave places one split's selected slots after the selected entries of
+    // the splits before it, each at its rank by entry within the split
     {
       const int wave = tid >> 6, lane = tid & 63;
       auto take = [&](int sp, uint32_t* e) {
@@ -745,8 +943,33 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
         uint32_t e;
         const bool tk = take(sp, &e);
         const unsigned long long m = __ballot(tk);
-        const uint32_t at = s_sel[sp] + lanes_below(m);
-        if (tk && at < (uint32_t)k) orow[at] = (int32_t)e;
+        // the split's slots are normally in entry order already; otherwise each taken entry
+        // is ranked among the taken lanes, bit by bit from the top of its 12-bit offset
+        // (lanes that agree on the higher bits and have a 0 where this lane has a 1 are
+        // below it), and moved to the lane of its rank so the stores go out in order
+        const uint32_t prev = (uint32_t)__shfl_up((int)e, 1);
+        const uint32_t nval = s_co[sp] >> 16;
+        const bool sorted = __ballot(lane >= 1 && (uint32_t)lane < nval && prev >= e) == 0ull;
+        if (sorted) {
+          const uint32_t at = s_sel[sp] + lanes_below(m);
+          if (tk && at < (uint32_t)k) orow[at] = (int32_t)e;
+        } else {
+          const uint32_t off = e - (uint32_t)(sp * kSplitEntries);
+          uint32_t rank = 0;
+          unsigned long long same = m;
+#pragma unroll
+          for (int b = 11; b >= 0; --b) {
+            const bool one = (off >> b) & 1u;
+            const unsigned long long ones = __ballot(one) & m;
+            if (one) rank += (uint32_t)__popcll(same & ~ones);
+            same &= one ? ones : ~ones;
+          }
+          const uint32_t cnt = (uint32_t)__popcll(m);
+          const uint32_t dest = tk ? rank : cnt + lanes_below(~m);
+          const uint32_t ev = (uint32_t)__builtin_amdgcn_ds_permute((int)(dest * 4u), (int)e);
+          const uint32_t at = s_sel[sp] + (uint32_t)lane;
+          if ((uint32_t)lane < cnt && at < (uint32_t)k) orow[at] = (int32_t)ev;
+        }
       }
       for (int i = (int)k_eff + tid; i < k; i += kSelThreads) orow[i] = -1;
     }
@@ -959,7 +1182,7 @@ hipError_t launch_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes
     hipLaunchKernelGGL(k_prefill_theta, dim3(T), dim3(kSelThreads), 0, stream, n_entries, ratio, pos0,
                        T, k, sampled ? kq : k, ws);
   if (n_entries > 0) {
-    hipLaunchKernelGGL((k_prefill_gemm<2, 1, kSplitEntries>), dim3(row_blocks, ws.n_splits),
+    hipLaunchKernelGGL(k_prefill_hits, dim3(row_blocks, ws.n_splits),
                        dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
                        pos0, T, ws);
   }
