@@ -484,12 +484,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
       if (nvis < 16) hm &= nvis > 0 ? (1u << nvis) - 1u : 0u;
       if (hm != 0u) {
         uint32_t slot = atomicAdd(&s_rcnt[lr], (uint32_t)__popc(hm));
-        const size_t base = ((size_t)(wg_row0 + lr) * ws.n_splits + split) * kSlots;
+        unsigned long long* out = ws.cand + ((size_t)(wg_row0 + lr) * ws.n_splits + split) * kSlots;
+        const float* recf = reinterpret_cast<const float*>(rq);
         while (hm != 0u) {
           const int r = __builtin_ctz(hm);
           hm &= hm - 1u;
+          // score r of this half, read back from the record (no register indexing)
+          const int f = 16 * (int)part + r;
+          const float vr = recf[4 * rec_slot(j, f >> 2) + (f & 3)];
           if (slot < (uint32_t)kSlots)
-            ws.cand[base + slot] = ((unsigned long long)score_key(v[r]) << 32) | (uint32_t)(eb + r);
+            out[slot] = ((unsigned long long)score_key(vr) << 32) | (uint32_t)(eb + r);
           ++slot;
         }
       }
@@ -518,14 +522,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
     __syncthreads();
     if (st + 1 < n_active) load_stage(st + 1);  // in flight during the MFMAs
     const int st_e0 = e_begin + st * kStage;
-    for (int tt = 0; tt < kStage / 32; ++tt) {
-      const int e0 = st_e0 + tt * 32;
-      if (e0 >= wave_nmax) break;  // wave-uniform: the rest of the stage is beyond every row
-      const int i = tt * 32 + rl;  // A operand: entry e0 + rl
+    // tiles of the stage that some row of the wave sees (wave-uniform)
+    const int n_tt = min(kStage / 32, max(0, (wave_nmax - st_e0 + 31) / 32));
+    // Software pipelined: the MFMAs of a tile are issued before the screening of the tile
+    // before it, which does not depend on them.
+    auto mfma_tile = [&](int tt, f32x16 (&acc)[kSets]) {
+      const int i = tt * 32 + rl;  // A operand: entry st_e0 + i
       const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
       const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
       const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      f32x16 acc[kSets];
 #pragma unroll
       for (int s = 0; s < kSets; ++s) acc[s] = f32x16{};
 #pragma unroll
@@ -535,6 +540,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
         for (int s = 0; s < kSets; ++s)
           acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s][kk], acc[s], 0, 0, 0);
       }
+    };
+    auto screen = [&](int tt, const f32x16 (&acc)[kSets]) {
+      const int e0 = st_e0 + tt * 32;
       float4 sc[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) sc[g] = s_sc[buf][tt * 8 + 2 * g + half];
@@ -580,6 +588,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
             qn = rest;
           }
         }
+      }
+    };
+    if (n_tt > 0) {
+      f32x16 a0[kSets], a1[kSets];
+      mfma_tile(0, a0);
+      int tt = 1;
+      for (; tt + 1 < n_tt; tt += 2) {
+        mfma_tile(tt, a1);
+        screen(tt - 1, a0);
+        mfma_tile(tt + 1, a0);
+        screen(tt, a1);
+      }
+      if (tt < n_tt) {
+        mfma_tile(tt, a1);
+        screen(tt - 1, a0);
+        screen(tt, a1);
+      } else {
+        screen(tt - 1, a0);
       }
     }
   }
