@@ -37,6 +37,13 @@ constexpr int kMaxReindex = CSA2_MAX_REINDEX;  // Reindex layers one chained cal
 bool fsel_fits(int n_cols, int k);
 bool fsel_len_ok(int n_cols);
 size_t fsel_ws_bytes(int batch, int n_cols, bool chain);
+// Rows of at most 16,384 columns, few of them: scan and top-k in one launch (the row's last
+// workgroup selects), in the filtered selection's workspace.
+bool fsmall_fits(int batch, int n_cols);
+hipError_t launch_fsmall(const uint16_t* q, const uint8_t* codes, const float* scale,
+                         const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
+                         int batch, int n_cols, int k, int32_t* out, float* sout, void* ws,
+                         hipStream_t stream);
 hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* scale,
                        const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
                        int batch, int n_cols, int k, int32_t* out, float* sout, int own_k,

@@ -1301,6 +1301,108 @@ __global__ __launch_bounds__(kT) void k_fpick(FsArgs a, int S) {
   if (L.c.misc[4] != 0u && tid < kRowWords) a.roww[r * kRowWords + tid] = 0u;
 }
 
+// ------------------------------------------------------------------ k_fsmall
+// Rows of at most kSmallCols columns (a Reindex layer's pool), in one launch.  Workgroup
+// (r, p) scores columns [1024 p, 1024 (p + 1)) of row r into the row's key array (0 for an
+// invalid column); the workgroup that finishes its row last (an agent-scope counter: no
+// workgroup waits for another) then takes the row's top-k from the keys, marks the winners
+// in a bitmap and writes each at its bitmap position, so the list comes out in column
+// order.  The counter is returned to zero by that workgroup.
+constexpr int kSmallCols = 16384;
+constexpr int kSmallU = kSmallCols / kT;
+struct SmallLds {
+  uint32_t bm[kSmallCols / 32 + 1];
+  uint32_t wp[kSmallCols / 32 + 1];
+  Core c;
+};
+
+template <bool CAND>
+__global__ __launch_bounds__(kT) void k_fsmall(FsArgs a) {
+  __shared__ SmallLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.runs;  // workgroups per row
+  const int r = (int)blockIdx.x / P, p = (int)blockIdx.x % P;
+  const int b = a.row0 + r;
+  const int n = max(0, min(a.n_valid[b], a.n_cols));
+  const int32_t* cand_row = CAND ? a.cand + (size_t)b * a.n_cols : nullptr;
+  uint32_t* ck = a.ckey + (size_t)r * a.cap;
+  const int c0 = p * kT;
+  const int tb = (1 << 20) - 200000 + (int)blockIdx.x * 8;
+  if (tid == 0) FS_TR(tb, FS_NOW());
+  {
+    // one group of 64 columns per wave, no prefetch: the memory counter that the wait
+    // below drains holds only this group's loads and stores
+    const int quarter = lane & 3, ent = lane >> 2;
+    const int g = c0 + wave * 64;
+    if (g < n) {
+      bf16x2 q[16];
+      load_q(a.q + (size_t)b * kDIdx, quarter, q);
+      const ScanGroup sg = load_group<CAND>(a.codes, a.scale, cand_row, a.seq_base[b], g, n - 1, ent, quarter);
+      const float score = group_score(sg, q, quarter);
+      const int col = g + 16 * quarter + ent;
+      if (col < n) st_ag(&ck[col], sg.own_ok ? score_key(score) : 0u);
+    }
+  }
+  // The keys are agent-scope stores, complete (at the device's coherence point) once this
+  // wave's memory counter drains, before the row's counter moves; the last workgroup reads
+  // them with agent-scope loads.  No cache-wide fence is needed.
+  wait_vm();
+  __syncthreads();
+  if (tid == 0) FS_TR(tb + 1, FS_NOW());
+  if (tid == 0) L.c.misc[4] = add_ag(&a.roww[r * kRowWords + kRwDone], 1u) == (uint32_t)(P - 1) ? 1u : 0u;
+  __syncthreads();
+  if (tid == 0) FS_TR(tb + 2, FS_NOW());
+  if (L.c.misc[4] == 0u) return;  // workgroup-uniform
+  // the row's last workgroup: every key of the row is written
+  if (tid == 0) st_ag(&a.roww[r * kRowWords + kRwDone], 0u);
+  uint32_t kv[kSmallU], c = 0u, mx = 0u;
+  int32_t cid[kSmallU];  // entry id of each column, loaded with the keys
+#pragma unroll
+  for (int u = 0; u < kSmallU; ++u) {
+    const int i = tid + kT * u;
+    kv[u] = i < n ? ld_ag(&ck[i]) : 0u;
+    cid[u] = CAND ? (i < n ? cand_row[i] : -1) : i;
+  }
+#pragma unroll
+  for (int u = 0; u < kSmallU; ++u) {
+    c += kv[u] != 0u ? 1u : 0u;
+    mx = max(mx, kv[u]);
+  }
+  block_sum_max(c, mx, L.c);
+  if (tid == 0) FS_TR(tb + 3, FS_NOW());
+  const Thr t = find_thr_lean<kSmallU>(kv, [&](int, int i) { return (uint32_t)i; }, n, (uint32_t)a.k, c, mx, L.c);
+  if (tid == 0) FS_TR(tb + 4, FS_NOW());
+#pragma unroll
+  for (int u = 0; u < kSmallU; ++u) {
+    const int i = tid + kT * u;
+    const unsigned long long msk = __ballot(i < n && selected(t, kv[u], (uint32_t)i));
+    if (lane == 0) {
+      L.bm[(kT * u + 64 * wave) >> 5] = (uint32_t)msk;
+      L.bm[((kT * u + 64 * wave) >> 5) + 1] = (uint32_t)(msk >> 32);
+    }
+  }
+  if (tid == 0) L.bm[kSmallCols / 32] = 0u;
+  __syncthreads();
+  bitmap_prefix(L.bm, L.wp, n, L.c);
+  if (tid == 0) FS_TR(tb + 5, FS_NOW());
+  int32_t* orow = a.out + (size_t)b * a.k;
+  float* srow = a.sout ? a.sout + (size_t)b * a.k : nullptr;
+#pragma unroll
+  for (int u = 0; u < kSmallU; ++u) {
+    const int i = tid + kT * u;
+    if (i < n && bit_at(L.bm, (uint32_t)i)) {
+      const uint32_t pos = bits_before(L.bm, L.wp, (uint32_t)i);
+      orow[pos] = cid[u];
+      if (srow) srow[pos] = key_score(kv[u]);
+    }
+  }
+  for (int q = (int)t.nsel + tid; q < a.k; q += kT) {
+    orow[q] = -1;
+    if (srow) srow[q] = -__builtin_inff();
+  }
+  if (tid == 0) FS_TR(tb + 6, FS_NOW());
+}
+
 // ---------------------------------------------------------------------------- host side
 constexpr int kMaxDevices = 64;
 
@@ -1467,6 +1569,52 @@ hipError_t launch_fsel(const uint16_t* q, const uint8_t* codes, const float* sca
       hipLaunchKernelGGL(k_fseg<false>, g_seg, dim3(kT), 0, stream, a);
       hipLaunchKernelGGL(k_fpick<false>, g_pick, dim3(kT), 0, stream, a, S);
     }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Short rows, and few enough of them that their workgroups run in about one wave of the
+// device (with more rows the serial selection of each row's last workgroup costs more than
+// the two-launch selection).
+bool fsmall_fits(int batch, int n_cols) {
+  return n_cols >= 1 && n_cols <= kSmallCols &&
+         (long long)batch * ((n_cols + kT - 1) / kT) <= 2LL * max(fs_capacity(), 1);
+}
+
+// Uses the filtered selection's workspace (its key store and row counters).
+hipError_t launch_fsmall(const uint16_t* q, const uint8_t* codes, const float* scale,
+                         const int64_t* seq_base, const int32_t* n_valid, const int32_t* cand,
+                         int batch, int n_cols, int k, int32_t* out, float* sout, void* ws,
+                         hipStream_t stream) {
+  const FsShape s = fs_shape(batch, n_cols, false);
+  const FsParts f = fs_carve(static_cast<char*>(ws), s, false);
+  FsArgs a{};
+  a.q = q;
+  a.codes = codes;
+  a.scale = scale;
+  a.seq_base = seq_base;
+  a.n_valid = n_valid;
+  a.cand = cand;
+  a.n_cols = n_cols;
+  a.runs = (n_cols + kT - 1) / kT;
+  a.batch = batch;
+  a.k = k;
+  a.out = out;
+  a.sout = sout;
+  a.ctrl = f.ctrl;
+  a.roww = f.roww;
+  a.ckey = f.ckey;
+  a.cap = s.cap;
+  for (int r0 = 0; r0 < batch; r0 += s.rows_ws) {
+    a.row0 = r0;
+    a.rows = min(s.rows_ws, batch - r0);
+    const dim3 grid((unsigned)(a.rows * a.runs));
+    if (cand)
+      hipLaunchKernelGGL(k_fsmall<true>, grid, dim3(kT), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_fsmall<false>, grid, dim3(kT), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1,8 +1,7 @@
 """One decode step of the 40-layer CSA2 backbone, sequenced through the C ABI.
 
 Sequencing only: every step runs in the library's kernels (csa2_index_topk,
-csa2_select_chain, csa2_replay_select, csa2_index_score + csa2_topk,
-csa2_sparse_attn_decode, csa2_sparse_attn_prefill); this module holds workspaces and output
+csa2_select_chain, csa2_replay_select, csa2_sparse_attn_decode, csa2_sparse_attn_prefill); this module holds workspaces and output
 buffers and issues the calls in layer order on one stream.
 
 Layer layout ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1-Flash", Q&A on how the
@@ -18,17 +17,17 @@ Layer layout ("DeepSeek-V4.1 模型结构（0）：一张图看懂 DeepSeek-V4.1
   * every layer attends with its own 16 x 512 query over its list plus its own 128-row
     window.
 Each Reindex layer's query arrives at its own layer (it depends on the layers before it in
-a real decoder), so the Reindex selections run per layer: the pool re-scored, then its
-top-k (two launches; for pools of 16,384 this is faster than the single fused launch).
+a real decoder), so the Reindex selections run per layer: csa2_index_topk over the pool
+(for pools of up to 16,384 one launch scores the pool and the last workgroup of each row
+selects).
 """
 from __future__ import annotations
 
 import torch
 
-from . import (attn_workspace, csa2_index_score, csa2_index_topk, csa2_replay_select,
-               csa2_select_chain, csa2_sparse_attn_decode, csa2_sparse_attn_prefill, csa2_topk,
-               index_topk_workspace, replay_select_workspace, select_chain_workspace,
-               topk_workspace)
+from . import (attn_workspace, csa2_index_topk, csa2_replay_select, csa2_select_chain,
+               csa2_sparse_attn_decode, csa2_sparse_attn_prefill, index_topk_workspace,
+               replay_select_workspace, select_chain_workspace)
 
 N_LAYERS = 40
 WINDOW_ONLY = (0, 1)
@@ -56,10 +55,7 @@ class DecodePass:
         dev = torch.device(device)
         self.enc_ws = index_topk_workspace(batch, enc_entries, k, device=dev)
         self.dec_ws = select_chain_workspace(batch, dec_entries, pool, device=dev)
-        # a Reindex layer re-scores the pool and selects in two launches (measured faster than
-        # the single fused launch for pools of this size: 21 against 28 us at batch 4)
-        self.re_ws = topk_workspace(batch, pool, k, device=dev)
-        self.re_scores = torch.empty((batch, pool), dtype=torch.float32, device=dev)
+        self.re_ws = index_topk_workspace(batch, pool, k, device=dev)  # Reindex: the pool re-scored
         self.attn_ws = attn_workspace(batch, k, device=dev)
         self.pool = torch.empty((batch, pool), dtype=torch.int32, device=dev)
         self.pool_valid = torch.full((batch,), pool, dtype=torch.int32, device=dev)
@@ -68,7 +64,7 @@ class DecodePass:
 
     def workspaces(self):
         """The selection workspaces whose status block (csa2_workspace_status) reports errors."""
-        return [self.enc_ws, self.dec_ws]
+        return [self.enc_ws, self.dec_ws, self.re_ws]
 
     def step(self, enc_caches, dec_cache, q_idx, q, swa, swa_len, stream=None, marks=None):
         """enc_caches: three entry caches (layers 2, 8, 14); dec_cache: the decoder's.
@@ -93,10 +89,8 @@ class DecodePass:
                     marks[2].record(stream)
             elif l in REINDEX:
                 c = dec_cache
-                csa2_index_score(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid,
-                                 self.re_scores, cand=self.pool, topk_ws=self.re_ws, stream=stream)
-                csa2_topk(self.re_scores, self.pool_valid, self.K, self.lists[l], cand=self.pool,
-                          hist_fused=True, workspace=self.re_ws, stream=stream)
+                csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid, self.K,
+                                self.lists[l], self.re_ws, self.P, cand=self.pool, stream=stream)
             if l in WINDOW_ONLY:
                 c, idx = dec_cache, None
             else:
@@ -130,8 +124,7 @@ class ReplayChunk:
         dev = torch.device(device)
         self.sel_ws = replay_select_workspace(T, n_entries, pool, device=dev)
         self.attn_ws = attn_workspace(T, k, device=dev)
-        self.re_ws = topk_workspace(T, pool, k, device=dev)  # Reindex: re-score, then select
-        self.re_scores = torch.empty((T, pool), dtype=torch.float32, device=dev)
+        self.re_ws = index_topk_workspace(T, pool, k, device=dev)  # Reindex: the pool re-scored
         self.seq_base = torch.zeros((T,), dtype=torch.int64, device=dev)
         self.pool = torch.empty((T, pool), dtype=torch.int32, device=dev)
         self.pool_valid = torch.empty((T,), dtype=torch.int32, device=dev)  # written by the selection
@@ -140,8 +133,8 @@ class ReplayChunk:
         self.out = torch.empty((N_LAYERS - DECODER_FULL, T, 16, 512), dtype=torch.float32, device=dev)
 
     def workspaces(self):
-        """The selection workspace whose status block (csa2_workspace_status) reports errors."""
-        return [self.sel_ws]
+        """The selection workspaces whose status block (csa2_workspace_status) reports errors."""
+        return [self.sel_ws, self.re_ws]
 
     def step(self, cache, q_idx, q, swa, stream=None, marks=None):
         """cache: the sequence's decoder entries (planes from entry 0); q_idx: {20, 24, 28,
@@ -157,11 +150,8 @@ class ReplayChunk:
             marks[1].record(stream)
         for l in range(DECODER_FULL, N_LAYERS):
             if l in REINDEX:
-                csa2_index_score(q_idx[l], cache.idx_codes, cache.idx_scale, self.seq_base,
-                                 self.pool_valid, self.re_scores, cand=self.pool, topk_ws=self.re_ws,
-                                 stream=stream)
-                csa2_topk(self.re_scores, self.pool_valid, self.K, self.lists[l], cand=self.pool,
-                          hist_fused=True, workspace=self.re_ws, stream=stream)
+                csa2_index_topk(q_idx[l], cache.idx_codes, cache.idx_scale, self.seq_base, self.pool_valid,
+                                self.K, self.lists[l], self.re_ws, self.P, cand=self.pool, stream=stream)
             csa2_sparse_attn_prefill(q[l - DECODER_FULL], cache.kv_codes, cache.kv_scale,
                                      self.lists[list_source(l)], swa[l - DECODER_FULL], self.pos0,
                                      self.out[l - DECODER_FULL], self.attn_ws, stream=stream)
