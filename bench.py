@@ -738,8 +738,8 @@ class Replay:
         # matrix, then the filtered selection reads it; its algorithmic bytes are the keys,
         # read once for all 128 queries (the matrix's write and read are this design's cost)
         return {"kernel": "csa2_replay_select: k_causal_scores (BF16 MFMA score matrix) + "
-                          "k_fseg<false, true> + k_fpick<false> (per-query pool 16,384 and own "
-                          "top-512); the call timed",
+                          "k_fseg_mat + k_fpick<false> (per-query pool 16,384 and own top-512); "
+                          "the call timed",
                 "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS,
                 "work": self.N * IDX_ENTRY_BYTES, "scale": 1e9, "marks": (0, 1)}
 
