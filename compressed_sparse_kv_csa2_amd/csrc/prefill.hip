@@ -21,9 +21,9 @@
 //          32 consecutive 32-entry tiles) as a 16-bit key prefix rounded down.  At least k
 //          groups have maxima >= the k-th largest group maximum, so that value, theta_t,
 //          is a rigorous lower bound on the row's k-th score;
-//   pass 2 recomputes the contraction and writes the scores >= theta_t (typically a few
-//          hundred per row) into the row's slots for this split, in entry order (a wave owns
-//          its rows: slots come from the compare ballots, no atomics);
+//   pass 2 recomputes the contraction (taken transposed, see k_prefill_hits) and writes
+//          the scores >= theta_t (typically several hundred per row) into the row's slots
+//          for this split;
 //   select resolves each row exactly in LDS (largest scores, ties to the lower entry) and
 //          emits the chosen entries in ascending order.  A row whose candidates overflow a split's
 //          slots (only possible with massive score ties) is resolved by recomputing its
@@ -48,7 +48,6 @@ constexpr int kGroupsPerSplit = kStages / kRunStages * 32;  // 128
 constexpr int kSlots = 64;                  // candidate slots per (row, split): one per lane
 static_assert(kSlots == 64, "select copies one split per wave, one slot per lane");
 static_assert(kSplitEntries <= 4096, "queued hits hold the entry within its split in 12 bits");
-constexpr int kQueue = 64 + 256;           // pass-2 hit queue per wave: a batch + 4 rows' worst
 constexpr int kCandLds = 4096;              // candidates a row may gather into LDS
 constexpr int kSelThreads = 256;
 static_assert(kSelThreads == 256, "the theta and select kernels give each of 256 bins a thread");
@@ -139,45 +138,28 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return r;
 }
 
-// Lane masks of a >= b (floats) and a <= b (ints), straight from v_cmp (every lane active).
-__device__ __forceinline__ uint64_t mask_ge(float a, float b) {
-  uint64_t m;
-  asm("v_cmp_ge_f32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
-  return m;
-}
-__device__ __forceinline__ uint64_t mask_le(int a, int b) {
-  uint64_t m;
-  asm("v_cmp_le_i32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
-  return m;
-}
-
 // LDS stage: entry i's 64 code bytes as 4 blocks of 16 bytes, block b at b ^ ((i >> 2) & 3)
 // so that 16 consecutive entries' reads of one block land in 16 distinct bank groups.
 __device__ __forceinline__ int stage_blk(int i, int b) { return i * 4 + (b ^ ((i >> 2) & 3)); }
 
-// PASS 1: group maxima.  PASS 2: candidate slots.
+// PASS 1: group maxima.
 // Accumulator layout of v_mfma_f32_32x32x16_bf16: lane l holds column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  Operands: lane l holds row/column l % 32 and
 // k-slice 8*(l/32)..+7; the dims behind k-step kk for half h are 64h + 8kk .. +7.
 // A wave owns 64 rows as two sets of 32 (set s: rows 32s ..); each expanded B operand
 // feeds one MFMA per set.
-// STRIDE > 1 (pass 1 only): the contraction runs over every STRIDE-th entry (columns are
-// sample indices, column c = entry STRIDE * c), for the sampled threshold.  A workgroup
-// covers SPLIT columns (a multiple of one run of 1,024), SPLIT / 1,024 * 32 groups.
-template <int PASS, int STRIDE, int SPLIT>
-__global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
+// STRIDE > 1: the contraction runs over every STRIDE-th entry (columns are sample indices,
+// column c = entry STRIDE * c), for the sampled threshold.  A workgroup covers SPLIT
+// columns (a multiple of one run of 1,024), SPLIT / 1,024 * 32 groups.
+template <int STRIDE, int SPLIT>
+__global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gmax(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
   __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
   __shared__ float s_sc[2][kStage];
-  // PASS 2: per wave, a queue of hits (score bits; entry - split start | wave row << 12) in
-  // (tile, set, r, lane) order, and the candidate count of each of the workgroup's rows
-  __shared__ uint2 s_q[4][PASS == 2 ? kQueue : 1];
-  __shared__ uint32_t s_rcnt[PASS == 2 ? kGemmRows : 1];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kGemmRows;
   const int row0 = wg_row0 + wave * kWaveRows;
-  static_assert(PASS == 1 || (STRIDE == 1 && SPLIT == kSplitEntries), "pass 2 scans every entry");
   static_assert(SPLIT % (kRunStages * kStage) == 0 && SPLIT <= kSplitEntries, "whole runs");
   constexpr int n_stages = SPLIT / kStage;
   constexpr int groups_per_split = n_stages / kRunStages * 32;
@@ -211,74 +193,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
   // once the entry's last position (STRIDE*col+1)*ratio - 1 is at most pos0 + row0 + w, i.e.
   // once lim <= w - 4*half with lim the lane's offset below (clamped: far from the frontier
   // only its sign matters).
-  // Rows past T need no mask: their maxima are never published and their thresholds are +inf.
+  // Rows past T need no mask: their maxima are never published.
   auto frontier_lim = [&](int col) {
     const int64_t d = ((int64_t)col * STRIDE + 1) * ratio - 1 - (pos0 + row0 + 4 * half);
     return col < n_cols ? (int)max(min(d, (int64_t)1 << 30), -((int64_t)1 << 30)) : (1 << 30);
   };
   auto wrow_h = [&](int s, int r) { return 32 * s + 8 * (r >> 2) + (r & 3); };  // wrow - 4*half
-  // PASS 2: row thresholds; the hit queue's fill (wave-uniform)
-  float th[kSets][16];
-  uint32_t qn = 0;
-  if (PASS == 2) {
-#pragma unroll
-    for (int s = 0; s < kSets; ++s)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = row0 + wrow(s, r);
-        th[s][r] = t < T ? ws.theta[t] : __builtin_inff();
-      }
-    s_rcnt[wave * kWaveRows + lane] = 0u;
-  }
-  // PASS 2: moves queued hits into their rows' slots, 64 at a time (all of them if `all`,
-  // else whole batches, the rest moved to the queue's front).  A hit's slot is its row's
-  // count so far plus the hits of the same row in lower lanes (lanes compared on the six
-  // row bits), so every row's slots stay in queue order, i.e. ascending entries.
-  auto flush = [&](bool all) {
-    uint32_t b = 0;
-    for (; b + 64 <= qn || (all && b < qn); b += 64) {
-      const bool valid = b + lane < qn;
-      const uint2 e = valid ? s_q[wave][b + lane] : make_uint2(0u, 0u);
-      const uint32_t lrow = e.y >> 12;
-      uint64_t eq = __ballot(valid);
-#pragma unroll
-      for (int bit = 0; bit < 6; ++bit) {
-        const bool set = (lrow >> bit) & 1u;
-        const uint64_t bm = __ballot(set);
-        eq &= set ? bm : ~bm;
-      }
-      const uint32_t rank = lanes_below(eq);
-      const bool last = ((eq >> lane) >> 1) == 0ull;  // no higher lane holds this row
-      const uint32_t gr = wave * kWaveRows + lrow;
-      const uint32_t slot = (valid ? s_rcnt[gr] : 0u) + rank;
-      if (valid && slot < (uint32_t)kSlots)
-        ws.cand[((size_t)(row0 + lrow) * ws.n_splits + split) * kSlots + slot] =
-            ((unsigned long long)score_key(__uint_as_float(e.x)) << 32) | (uint32_t)(e_begin + (e.y & 0xfffu));
-      if (valid && last) s_rcnt[gr] = slot + 1u;
-    }
-    if (!all) {
-      if (b + lane < qn) {
-        const uint2 e = s_q[wave][b + lane];  // b >= 64: source and destination are apart
-        s_q[wave][lane] = e;
-      }
-      qn -= b;
-    }
-  };
 
   // one entry per thread per stage: 4 x 16 code bytes + scale, clamped to a real entry
   uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
   float psc = 0.f;
-#define CSA2_LOAD_STAGE(st)                                                                   \
-  do {                                                                                        \
-    const int e_ = min(e_begin + (st) * kStage + tid, n_cols - 1) * STRIDE;                   \
-    const uint4* cp_ = reinterpret_cast<const uint4*>(codes + (size_t)e_ * kIdxCodeBytes);    \
-    pc0 = cp_[0];                                                                             \
-    pc1 = cp_[1];                                                                             \
-    pc2 = cp_[2];                                                                             \
-    pc3 = cp_[3];                                                                             \
-    psc = scale[e_];                                                                          \
-  } while (0)
-  if (n_active > 0) CSA2_LOAD_STAGE(0);
+  auto load_stage = [&](int st) {
+    const int e = min(e_begin + st * kStage + tid, n_cols - 1) * STRIDE;
+    const uint4* cp = reinterpret_cast<const uint4*>(codes + (size_t)e * kIdxCodeBytes);
+    pc0 = cp[0];
+    pc1 = cp[1];
+    pc2 = cp[2];
+    pc3 = cp[3];
+    psc = scale[e];
+  };
+  if (n_active > 0) load_stage(0);
 
   float rm[kSets][16];
 #pragma unroll
@@ -295,7 +229,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
       s_code[buf][stage_blk(tid, 3)] = pc3;
       s_sc[buf][tid] = psc;
       __syncthreads();
-      if (st + 1 < n_active) CSA2_LOAD_STAGE(st + 1);  // in flight during the MFMAs
+      if (st + 1 < n_active) load_stage(st + 1);  // in flight during the MFMAs
 
       const int st_e0 = e_begin + st * kStage;
       for (int tt = 0; tt < kStage / 32; ++tt) {
@@ -317,63 +251,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
             acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][kk], bv, acc[s], 0, 0, 0);
         }
         const int col = e0 + rl;
-        const bool full = e0 + 32 <= wave_nmin;  // wave-uniform: every row sees the tile
-        if (PASS == 1) {
-          if (full) {
+        if (e0 + 32 <= wave_nmin) {  // wave-uniform: every row sees the tile
 #pragma unroll
-            for (int s = 0; s < kSets; ++s)
+          for (int s = 0; s < kSets; ++s)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) rm[s][r] = vmax(acc[s][r] * sc, rm[s][r]);
-          } else {
-            const int lim = frontier_lim(col);
-#pragma unroll
-            for (int s = 0; s < kSets; ++s)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const float v = acc[s][r] * sc;
-                rm[s][r] = lim <= wrow_h(s, r) ? vmax(v, rm[s][r]) : rm[s][r];
-              }
-          }
+            for (int r = 0; r < 16; ++r) rm[s][r] = vmax(acc[s][r] * sc, rm[s][r]);
         } else {
-          const uint32_t tag = (uint32_t)(col - e_begin);
-          auto push = [&](int s, int r, float v, bool hit, uint64_t m) {  // m: the wave's hits
-            if (m == 0ull) return;
-            const uint32_t pos = qn + lanes_below(m);
-            if (hit) s_q[wave][pos] = make_uint2(__float_as_uint(v), tag | ((uint32_t)wrow(s, r) << 12));
-            qn += (uint32_t)__builtin_popcountll(m);
-          };
+          const int lim = frontier_lim(col);
 #pragma unroll
-          for (int s = 0; s < kSets; ++s) {
-            if (full) {
-              // every compare of the set first: the scalar tests that follow then wait for
-              // the vector unit once, not once per row
-              float v[16];
-              uint64_t mk[16];
+          for (int s = 0; s < kSets; ++s)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                v[r] = acc[s][r] * sc;
-                mk[r] = mask_ge(v[r], th[s][r]);
-              }
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                push(s, r, v[r], v[r] >= th[s][r], mk[r]);
-                if ((r & 3) == 3 && qn >= 64u) flush(false);
-              }
-            } else {
-              const int lim = frontier_lim(col);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const float v = acc[s][r] * sc;
-                const int w = wrow_h(s, r);
-                push(s, r, v, v >= th[s][r] && lim <= w, mask_ge(v, th[s][r]) & mask_le(lim, w));
-                if ((r & 3) == 3 && qn >= 64u) flush(false);
-              }
+            for (int r = 0; r < 16; ++r) {
+              const float v = acc[s][r] * sc;
+              rm[s][r] = lim <= wrow_h(s, r) ? vmax(v, rm[s][r]) : rm[s][r];
             }
-          }
         }
       }
     }
-    if (PASS == 1 && (st + 1) % kRunStages == 0) {  // end of a run: publish the group maxima
+    if ((st + 1) % kRunStages == 0) {  // end of a run: publish the group maxima
       const int g = split * groups_per_split + (st / kRunStages) * 32 + rl;
 #pragma unroll
       for (int s = 0; s < kSets; ++s)
@@ -388,12 +283,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gemm(
           rm[s][r] = -__builtin_inff();
         }
     }
-  }
-#undef CSA2_LOAD_STAGE
-  if (PASS == 2) {
-    flush(true);
-    if (row0 + lane < T)
-      ws.ccount[(size_t)(row0 + lane) * ws.n_splits + split] = s_rcnt[wave * kWaveRows + lane];
   }
 }
 
@@ -1061,7 +950,7 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
 // block; columns a row does not see hold scores of no meaning), or row-major, S[t][j]
 // (columns a row does not see are left unwritten).  A workgroup owns 128 query rows (a
 // wave per 32) and one split of kScoreSplit entries streamed through LDS as in
-// k_prefill_gemm.  The product is taken transposed, entries x queries (the expanded keys
+// k_prefill_gmax.  The product is taken transposed, entries x queries (the expanded keys
 // as the A operand), so that a lane's accumulators hold one query's scores for four runs
 // of four consecutive entries: 16-byte stores.
 constexpr int kScoreRows = 128;
@@ -1192,11 +1081,11 @@ hipError_t launch_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes
     const int n_cols = (n_entries + kSampleStride - 1) / kSampleStride;
     const int splits = (n_cols + split - 1) / split;
     ws.G_used = splits * (split / (kRunStages * kStage) * 32);
-    hipLaunchKernelGGL((k_prefill_gemm<1, kSampleStride, split>), dim3(row_blocks, splits),
+    hipLaunchKernelGGL((k_prefill_gmax<kSampleStride, split>), dim3(row_blocks, splits),
                        dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
                        pos0, T, ws);
   } else if (n_entries > 0) {
-    hipLaunchKernelGGL((k_prefill_gemm<1, 1, kSplitEntries>), dim3(row_blocks, ws.n_splits),
+    hipLaunchKernelGGL((k_prefill_gmax<1, kSplitEntries>), dim3(row_blocks, ws.n_splits),
                        dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
                        pos0, T, ws);
   }
