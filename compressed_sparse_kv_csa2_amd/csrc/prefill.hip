@@ -288,21 +288,23 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gmax(
 
 // PASS 2: the candidates.  The same contraction over every entry, taken transposed (the
 // expanded keys as the A operand, entries x queries): lane l of a wave holds, for its
-// query row0 + 32 s + l % 32, the scores of entries e0 + 8 g + 4 (l / 32) + i (accumulator
-// 4 g + i).  Hits (scores >= the row's threshold) are rare, about one score in 200, so a
-// lane only tests the largest of its 16 scores per tile; a row that may hold a hit gets a
-// record of its 32 scores of the tile in the wave's LDS queue (both of its lanes write
-// their half; positions from the ballot), and once 32 records are queued each lane sorts
-// out half a record.  Slots of a (row, split) list come from the row's LDS counter, taken
-// in queue order, so the list is in entry order as long as the counter serves the lanes of
-// one atomic in lane order; the select checks that and ranks the list itself otherwise.
-constexpr int kRec = 32;                    // queue record: 32 scores (dwords)
-constexpr int kRecBatch = 32;               // records drained at once (two lanes each)
+// query row0 + 32 s + l % 32, 16 scores of the tile.  The stage stores each tile's 32
+// entries permuted (entry 16 h + 4 g + i at A row 8 g + 4 h + i), so that accumulator
+// 4 g + i of lane half h = l / 32 is entry 16 h + 4 g + i: each lane holds 16 consecutive
+// entries.  Hits (scores >= the row's threshold) are rare, about one score in 200, so a
+// lane only tests the largest of its 16 scores per tile; a lane that may hold a hit puts
+// its 16 scores in the wave's LDS queue as one record (position from the ballot), and once
+// 64 records are queued each lane sorts out one.  Slots of a (row, split) list come from
+// the row's LDS counter, taken in queue order (a row's lower half before its upper half,
+// tiles in order), so the list is in entry order as long as the counter serves the lanes
+// of one atomic in lane order; the select checks that and ranks the list itself otherwise.
+constexpr int kRecBatch = 64;               // records drained at once (one per lane)
 constexpr int kRecQueue = 2 * kRecBatch;    // a batch + one tile's worth
-static_assert(kRecBatch % 8 == 0, "moving a record by a batch keeps its slot swizzle");
-// 16-byte slot q of record j sits at slot q ^ (j & 7): the lanes of one write (consecutive
-// records, same q) then fall on different banks
-__device__ __forceinline__ int rec_slot(uint32_t j, int q) { return (int)(j * (kRec / 4)) + (q ^ (int)(j & 7u)); }
+// Queue layout: group g (scores 4 g .. 4 g + 3) of record j at s_rec[wave][g][j], so a
+// record is written with one address and four offsets, and the lanes of one access touch
+// consecutive 16-byte slots.
+// A row of the stage: entry e of a tile (e < 32) sits at A row tile_row(e).
+__device__ __forceinline__ int tile_row(int e) { return ((e >> 2) & 3) << 3 | (e >> 4) << 2 | (e & 3); }
 __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
@@ -311,8 +313,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
   __shared__ uint32_t s_rcnt[kGemmRows];     // candidates of each of the workgroup's rows
   __shared__ float s_th[kGemmRows];          // each row's threshold (+inf past T)
   __shared__ int s_nv[kGemmRows];            // entries each row sees
-  __shared__ float4 s_rec[4][kRecQueue * kRec / 4];
-  __shared__ uint32_t s_rtag[4][kRecQueue];  // record's row | tile offset in the split << 8
+  __shared__ float4 s_rec[4][4][kRecQueue];
+  __shared__ uint32_t s_rtag[4][kRecQueue];  // record's row | its first entry's offset in the split << 8
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kGemmRows;
   const int row0 = wg_row0 + wave * kWaveRows;
@@ -344,23 +346,23 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
   }
   __syncthreads();
 
-  float4* rq = s_rec[wave];
+  float4* rq = &s_rec[wave][0][0];
   uint32_t* rt = s_rtag[wave];
   uint32_t qn = 0;  // queued records (wave-uniform)
-  // Lane L takes half L % 2 of record L / 2 of the first n: that half's hits (visible
-  // entries only) go to its row's next slots.
+  // Lane j takes record j of the first n: its hits (visible entries only) go to its row's
+  // next slots.
   auto drain = [&](uint32_t n) {
-    const uint32_t j = (uint32_t)lane >> 1, part = (uint32_t)lane & 1u;
+    const uint32_t j = (uint32_t)lane;
     if (j < n) {
       const uint32_t tag = rt[j];
-      const int lr = (int)(tag & 255u);                        // row within the workgroup
-      const int eb = e_begin + (int)(tag >> 8) + 16 * (int)part;  // entry of this half's score 0
+      const int lr = (int)(tag & 255u);        // row within the workgroup
+      const int eb = e_begin + (int)(tag >> 8);  // entry of the record's score 0
       const float thr = s_th[lr];
       const int nvr = s_nv[lr];
       float v[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 x = rq[rec_slot(j, 4 * (int)part + g)];
+        const float4 x = rq[g * kRecQueue + j];
         v[4 * g] = x.x;
         v[4 * g + 1] = x.y;
         v[4 * g + 2] = x.z;
@@ -369,18 +371,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
       uint32_t hm = 0u;
 #pragma unroll
       for (int r = 0; r < 16; ++r) hm |= (v[r] >= thr ? 1u : 0u) << r;
-      const int nvis = nvr - eb;  // visible entries among this half's 16
+      const int nvis = nvr - eb;  // visible entries among the record's 16
       if (nvis < 16) hm &= nvis > 0 ? (1u << nvis) - 1u : 0u;
       if (hm != 0u) {
         uint32_t slot = atomicAdd(&s_rcnt[lr], (uint32_t)__popc(hm));
         unsigned long long* out = ws.cand + ((size_t)(wg_row0 + lr) * ws.n_splits + split) * kSlots;
-        const float* recf = reinterpret_cast<const float*>(rq);
+        const float* recf = reinterpret_cast<const float*>(rq + j);
         while (hm != 0u) {
           const int r = __builtin_ctz(hm);
           hm &= hm - 1u;
-          // score r of this half, read back from the record (no register indexing)
-          const int f = 16 * (int)part + r;
-          const float vr = recf[4 * rec_slot(j, f >> 2) + (f & 3)];
+          // score r, read back from the record (no register indexing)
+          const float vr = recf[(r >> 2) * (4 * kRecQueue) + (r & 3)];
           if (slot < (uint32_t)kSlots)
             out[slot] = ((unsigned long long)score_key(vr) << 32) | (uint32_t)(eb + r);
           ++slot;
@@ -389,6 +390,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
     }
   };
 
+  // the stage slot of this thread's entry: its tile, its A row
+  const int fill_i = (tid & ~31) | tile_row(tid & 31);
   uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
   float psc = 0.f;
   auto load_stage = [&](int st) {
@@ -403,11 +406,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
   if (n_active > 0) load_stage(0);
   for (int st = 0; st < n_active; ++st) {
     const int buf = st & 1;
-    s_code[buf][stage_blk(tid, 0)] = pc0;
-    s_code[buf][stage_blk(tid, 1)] = pc1;
-    s_code[buf][stage_blk(tid, 2)] = pc2;
-    s_code[buf][stage_blk(tid, 3)] = pc3;
-    reinterpret_cast<float*>(s_sc[buf])[tid] = psc;
+    s_code[buf][stage_blk(fill_i, 0)] = pc0;
+    s_code[buf][stage_blk(fill_i, 1)] = pc1;
+    s_code[buf][stage_blk(fill_i, 2)] = pc2;
+    s_code[buf][stage_blk(fill_i, 3)] = pc3;
+    reinterpret_cast<float*>(s_sc[buf])[fill_i] = psc;
     __syncthreads();
     if (st + 1 < n_active) load_stage(st + 1);  // in flight during the MFMAs
     const int st_e0 = e_begin + st * kStage;
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
     // Software pipelined: the MFMAs of a tile are issued before the screening of the tile
     // before it, which does not depend on them.
     auto mfma_tile = [&](int tt, f32x16 (&acc)[kSets]) {
-      const int i = tt * 32 + rl;  // A operand: entry st_e0 + i
+      const int i = tt * 32 + rl;  // A operand: stage row i
       const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
       const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
       const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
@@ -431,10 +434,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
       }
     };
     auto screen = [&](int tt, const f32x16 (&acc)[kSets]) {
-      const int e0 = st_e0 + tt * 32;
+      // this lane's 16 entries: e0 .. e0 + 15, their scales at stage rows 8 g + 4 half + i
+      const int e0 = st_e0 + tt * 32 + 16 * half;
       float4 sc[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) sc[g] = s_sc[buf][tt * 8 + 2 * g + half];
+      const uint32_t tag_e = (uint32_t)(e0 - e_begin) << 8;
 #pragma unroll
       for (int s = 0; s < kSets; ++s) {
         float v[16];
@@ -448,31 +453,32 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
         const float m0 = vmax3(v[0], v[1], v[2]), m1 = vmax3(v[3], v[4], v[5]), m2 = vmax3(v[6], v[7], v[8]);
         const float m3 = vmax3(v[9], v[10], v[11]), m4 = vmax3(v[12], v[13], v[14]);
         const float mx = vmax3(vmax3(m0, m1, m2), vmax3(m3, m4, v[15]), m0);
-        const uint64_t m = __ballot(mx >= th[s]);
+        const bool cand = mx >= th[s];
+        const uint64_t m = __ballot(cand);
         if (m != 0ull) {  // wave-uniform
-          // rows (lane % 32) with a possible hit in either half: one record each
-          const uint32_t pm = (uint32_t)(m | (m >> 32));
-          if ((pm >> rl) & 1u) {
-            const uint32_t j = qn + (uint32_t)__popc(pm & ((1u << rl) - 1u));
+          if (cand) {
+            const uint32_t j = qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            float4* p = rq + j;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)  // entries 8 g + 4 half .. +3 of the tile
-              rq[rec_slot(j, 2 * g + half)] = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-            if (half == 0) rt[j] = (uint32_t)(wave * kWaveRows + 32 * s + rl) | ((uint32_t)(e0 - e_begin) << 8);
+            for (int g = 0; g < 4; ++g) p[g * kRecQueue] = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+            rt[j] = (uint32_t)(wave * kWaveRows + 32 * s + rl) | tag_e;
           }
-          qn += (uint32_t)__popc(pm);
+          qn += (uint32_t)__popcll(m);
           if (qn >= (uint32_t)kRecBatch) {
             drain((uint32_t)kRecBatch);
             // the rest (fewer than a batch) to the front, after every read of the batch (the
             // wave's LDS operations complete in order)
             const uint32_t rest = qn - (uint32_t)kRecBatch;
-            const uint32_t j = (uint32_t)lane >> 1, part = (uint32_t)lane & 1u;
+            const uint32_t j = (uint32_t)lane;
             if (j < rest) {
-              const float4* src = rq + (kRecBatch + j) * (kRec / 4) + 4 * part;
-              float4* dst = rq + j * (kRec / 4) + 4 * part;
-              const float4 x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
+              float4 x[4];
+#pragma unroll
+              for (int g = 0; g < 4; ++g) x[g] = rq[g * kRecQueue + kRecBatch + j];
               const uint32_t tg = rt[kRecBatch + j];
-              dst[0] = x0; dst[1] = x1; dst[2] = x2; dst[3] = x3;
-              if (part == 0) rt[j] = tg;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) rq[g * kRecQueue + j] = x[g];
+              rt[j] = tg;
             }
             qn = rest;
           }
