@@ -720,6 +720,63 @@ __device__ __forceinline__ float score_row(const bf16x2 (&qq)[64], const uint8_t
   return (a0 + a1) * scale[j];
 }
 
+// A row whose candidates cannot give its top k (a split's slots overflowed, or a sampled
+// threshold let through fewer than k): the whole workgroup recomputes the row's scores in a
+// streaming exact selection (8-bit radix levels over (key, ~entry)) and writes the chosen
+// entries in ascending order.  hist: 256 bins; res: 4 words; scan: 32 words.
+__device__ __forceinline__ void recompute_row(const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
+                                           const float* __restrict__ scale, int t, int n_t, uint32_t k_eff, int k,
+                                           int32_t* orow, uint32_t* hist, uint32_t* s_res, uint32_t* s_scan) {
+  const int tid = threadIdx.x;
+  bf16x2 qq[64];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)t * kDIdx);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = qp[i];
+      qq[4 * i + 0] = __builtin_bit_cast(bf16x2, v.x);
+      qq[4 * i + 1] = __builtin_bit_cast(bf16x2, v.y);
+      qq[4 * i + 2] = __builtin_bit_cast(bf16x2, v.z);
+      qq[4 * i + 3] = __builtin_bit_cast(bf16x2, v.w);
+    }
+  }
+  uint32_t need = k_eff;
+  unsigned long long prefix = 0ull, pmask = 0ull;
+  for (int level = 0; level < 8 && need > 0; ++level) {
+    const int shift = 56 - 8 * level;
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int j = tid; j < n_t; j += kSelThreads) {
+      const unsigned long long comp =
+          ((unsigned long long)score_key(score_row(qq, codes, scale, j)) << 32) | (uint32_t)~(uint32_t)j;
+      if ((comp & pmask) == prefix) atomicAdd(&hist[(comp >> shift) & 255ull], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) find_bin_wave(hist, 256, need, s_res);
+    __syncthreads();
+    need -= s_res[1];
+    prefix |= (unsigned long long)s_res[0] << shift;
+    pmask |= 255ull << shift;
+    __syncthreads();
+  }
+  // composites are unique: select comp >= prefix (all 64 bits resolved) in entry order
+  uint32_t written = 0;
+  for (int c0 = 0; c0 < n_t; c0 += kSelThreads) {
+    const int j = c0 + tid;
+    bool take = false;
+    if (j < n_t) {
+      const unsigned long long comp =
+          ((unsigned long long)score_key(score_row(qq, codes, scale, j)) << 32) | (uint32_t)~(uint32_t)j;
+      take = k_eff > 0 && comp >= prefix;
+    }
+    uint32_t tot;
+    const uint32_t p = block_scan_excl(take ? 1u : 0u, s_scan, &tot);
+    if (take && written + p < (uint32_t)k) orow[written + p] = j;
+    written += tot;
+  }
+  for (int i = (int)written + tid; i < k; i += kSelThreads) orow[i] = -1;
+}
+
 // Exact per-row top-k from the candidate slots (or, on overflow, from recomputed scores),
 // ascending entry ids, -1 padded.
 __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
@@ -897,54 +954,187 @@ __global__ __launch_bounds__(kSelThreads) void k_prefill_select(
     return;
   }
 
-  // ---- overflow: recompute the row's scores in a streaming exact selection
-  bf16x2 qq[64];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + (size_t)t * kDIdx);
+  recompute_row(q_idx, codes, scale, t, n_t, k_eff, k, orow, s_hist[0], s_res, s_scan);
+}
+
+// ---- rows of chunks with at most kRowSplits splits: one wave per row, its candidates in
+// registers (slot `lane` of split u in key[u], ent[u]; key 0 = empty slot, a score's key
+// is never 0), so that a row needs no workgroup barrier and every row of a 4,096-query
+// chunk is resident at once.
+constexpr int kRowSplits = 32;
+constexpr int kSelRowsPerBlock = kSelThreads / 64;
+
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, bool is_max) {
+  // DPP row shifts, then row broadcasts; lane 63 ends with the result
+  const int id = is_max ? 0 : -1;
+  int x = (int)v;
+  auto op = [&](int a, int b) { return is_max ? (int)max((unsigned)a, (unsigned)b) : (int)min((unsigned)a, (unsigned)b); };
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
+// Bin of the need-th largest count of the wave's 256-bin histogram h (lane l holds bins
+// 255 - 4 l .. 252 - 4 l); *above = elements in higher bins, *in_bin = the bin's count.
+__device__ __forceinline__ uint32_t wave_find_bin(const uint32_t* h, uint32_t need, uint32_t* above,
+                                                  uint32_t* in_bin) {
+  const int lane = threadIdx.x & 63;
+  const uint4 hv = reinterpret_cast<const uint4*>(h)[63 - lane];
+  const uint32_t c3 = hv.w, c2 = hv.z, c1 = hv.y, c0 = hv.x;
+  const uint32_t sum = c0 + c1 + c2 + c3;
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint32_t excl = incl - sum;
+  const uint64_t hitm = __ballot(excl < need && need <= incl);
+  const int src = __builtin_amdgcn_readfirstlane(max(__builtin_ffsll((long long)hitm) - 1, 0));
+  uint32_t a = excl, b = 252u - 4u * (uint32_t)lane + 3u, r = c3;
+  if (a + c3 < need) { a += c3; b -= 1; r = c2;
+    if (a + c2 < need) { a += c2; b -= 1; r = c1;
+      if (a + c1 < need) { a += c1; b -= 1; r = c0; } } }
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)a, src);
+  *in_bin = (uint32_t)__builtin_amdgcn_readlane((int)r, src);
+  return (uint32_t)__builtin_amdgcn_readlane((int)b, src);
+}
+
+// One wave: row t's top k_eff (largest scores, ties to the lower entry) among its candidates,
+// written in ascending entry order.  Radix levels of 8 bits over the key bits below those
+// that every candidate shares, then, for keys equal to the threshold key, over the entry.
+// Returns true when the candidates cannot give the top k (a split overflowed its slots, or
+// fewer than k) or a split's slots are out of entry order: the row is then recomputed.
+__device__ __forceinline__ bool select_row_wave(int t, uint32_t k_eff, int k, int32_t* orow,
+                                                const PrefillWs& ws, uint32_t* h) {
+  const int lane = threadIdx.x & 63;
+  const int S = ws.n_splits;
+  const uint32_t c = lane < S ? ws.ccount[(size_t)t * S + lane] : 0u;
+  if (__ballot(c > (uint32_t)kSlots) != 0ull) return true;
+  const uint32_t C = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(c), 63);
+  if (C < k_eff) return true;
+  uint32_t key[kRowSplits], ent[kRowSplits];
+  const unsigned long long* cp = ws.cand + (size_t)t * S * kSlots + lane;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint4 v = qp[i];
-      qq[4 * i + 0] = __builtin_bit_cast(bf16x2, v.x);
-      qq[4 * i + 1] = __builtin_bit_cast(bf16x2, v.y);
-      qq[4 * i + 2] = __builtin_bit_cast(bf16x2, v.z);
-      qq[4 * i + 3] = __builtin_bit_cast(bf16x2, v.w);
+  for (int u = 0; u < kRowSplits; ++u) {
+    const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)c, u);  // 0 for u >= S
+    const unsigned long long v = (uint32_t)lane < n ? cp[(size_t)u * kSlots] : 0ull;
+    key[u] = (uint32_t)(v >> 32);
+    ent[u] = (uint32_t)v;
+  }
+  // take: key != 0 && (key > tkey || (key == tkey && ent <= tent))
+  uint32_t tkey = 0u, tent = 0xffffffffu;
+  uint32_t need = k_eff, remaining = C;
+  if (need < remaining) {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int u = 0; u < kRowSplits; ++u) {
+      mx = max(mx, key[u]);
+      mn = min(mn, key[u] != 0u ? key[u] : 0xffffffffu);
+    }
+    mn = wave_reduce_u32(mn, false);
+    mx = wave_reduce_u32(mx, true);
+    // key bits [lo, 32) are fixed (pfx = key >> lo); every candidate shares those above the
+    // highest bit where the smallest and largest keys differ
+    const uint32_t d = mn ^ mx;
+    int lo = d != 0u ? 32 - __builtin_clz(d) : 0;
+    uint32_t pfx = lo < 32 ? mn >> lo : 0u;
+    bool first = true;
+    while (need < remaining && lo > 0) {
+      const int nlo = max(lo - 8, 0);
+      const uint32_t dmask = (1u << (lo - nlo)) - 1u;
+      reinterpret_cast<uint4*>(h)[lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < kRowSplits; ++u)
+        if (key[u] != 0u && (first || (key[u] >> lo) == pfx)) atomicAdd(&h[(key[u] >> nlo) & dmask], 1u);
+      uint32_t above, in_bin;
+      const uint32_t sel = wave_find_bin(h, need, &above, &in_bin);
+      need -= above;
+      remaining = in_bin;
+      pfx = (pfx << (lo - nlo)) | sel;
+      lo = nlo;
+      first = false;
+    }
+    if (need == remaining) {
+      tkey = pfx << lo;  // every key with this prefix or above
+    } else {
+      // `remaining` candidates hold the threshold key pfx; the `need` of them with the lowest
+      // entries: levels over the entry, digit 255 - (entry bits) so the largest bin is lowest
+      tkey = pfx;
+      uint32_t epfx = 0u;
+      int elo = 32;
+      while (need < remaining && elo > 0) {
+        const int nlo = elo - 8;
+        reinterpret_cast<uint4*>(h)[lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int u = 0; u < kRowSplits; ++u)
+          if (key[u] == tkey && (elo == 32 || (ent[u] >> elo) == epfx))
+            atomicAdd(&h[255u - ((ent[u] >> nlo) & 255u)], 1u);
+        uint32_t above, in_bin;
+        const uint32_t sel = 255u - wave_find_bin(h, need, &above, &in_bin);
+        need -= above;
+        remaining = in_bin;
+        epfx = (epfx << 8) | sel;
+        elo = nlo;
+      }
+      // every entry whose prefix is at or below epfx
+      tent = elo > 0 ? (epfx << elo) | ((1u << elo) - 1u) : epfx;
     }
   }
-  uint32_t need = k_eff;
-  unsigned long long prefix = 0ull, pmask = 0ull;
-  for (int level = 0; level < 8 && need > 0; ++level) {
-    const int shift = 56 - 8 * level;
-    s_hist[0][tid] = 0u;
-    __syncthreads();
-    for (int j = tid; j < n_t; j += kSelThreads) {
-      const unsigned long long comp =
-          ((unsigned long long)score_key(score_row(qq, codes, scale, j)) << 32) | (uint32_t)~(uint32_t)j;
-      if ((comp & pmask) == prefix) atomicAdd(&s_hist[0][(comp >> shift) & 255ull], 1u);
+  // the chosen entries in ascending order: splits hold ascending entry ranges and a split's
+  // slots are in entry order when the slot counter served its lanes in order (a split
+  // found out of order hands the row back)
+  uint32_t base = 0u;
+#pragma unroll
+  for (int u = 0; u < kRowSplits; ++u) {
+    const bool tk = key[u] != 0u && (key[u] > tkey || (key[u] == tkey && ent[u] <= tent));
+    const unsigned long long m = __ballot(tk);
+    if (m != 0ull) {  // uniform
+      const uint32_t e = ent[u];
+      const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x138, 0xf, 0xf, false);  // wave_shr:1
+      // the split's filled slots are lanes 0 .. its count - 1 (the non-zero keys)
+      if (__ballot(lane >= 1 && key[u] != 0u && prev >= e) != 0ull) return true;
+      const uint32_t at = base + lanes_below(m);
+      if (tk && at < (uint32_t)k) orow[at] = (int32_t)e;
+      base += (uint32_t)__popcll(m);
     }
-    __syncthreads();
-    if (tid < 64) find_bin_wave(s_hist[0], 256, need, s_res);
-    __syncthreads();
-    need -= s_res[1];
-    prefix |= (unsigned long long)s_res[0] << shift;
-    pmask |= 255ull << shift;
+  }
+  for (int i = (int)k_eff + lane; i < k; i += 64) orow[i] = -1;
+  return false;
+}
+
+// Grid: ceil(T / 4) workgroups of 4 waves, wave w selecting row 4 b + w; rows the waves
+// hand back are recomputed by the whole workgroup afterwards.
+__global__ __launch_bounds__(kSelThreads) void k_prefill_select_rows(
+    const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, int k,
+    int32_t* __restrict__ idx_out, PrefillWs ws) {
+  __shared__ uint4 s_wh[kSelRowsPerBlock][64];  // each wave's 256-bin histogram
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_res[4];
+  __shared__ uint32_t s_scan[32];
+  __shared__ uint32_t s_redo[kSelRowsPerBlock];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kSelRowsPerBlock + wave;
+  bool redo = false;
+  if (t < T) {
+    const int n_t = visible(pos0 + t, ratio, n_entries);
+    int32_t* orow = idx_out + (size_t)t * k;
+    if (n_t <= k) {  // every visible entry is selected
+      for (int i = lane; i < k; i += 64) orow[i] = i < n_t ? i : -1;
+    } else {
+      redo = select_row_wave(t, (uint32_t)k, k, orow, ws, reinterpret_cast<uint32_t*>(s_wh[wave]));
+    }
+  }
+  if (lane == 0) s_redo[wave] = redo ? 1u : 0u;
+  __syncthreads();
+  for (int w = 0; w < kSelRowsPerBlock; ++w) {
+    if (s_redo[w] == 0u) continue;  // uniform
+    const int tr = blockIdx.x * kSelRowsPerBlock + w;
+    const int n_t = visible(pos0 + tr, ratio, n_entries);
+    recompute_row(q_idx, codes, scale, tr, n_t, (uint32_t)min(k, n_t), k, idx_out + (size_t)tr * k, s_hist,
+                  s_res, s_scan);
     __syncthreads();
   }
-  // composites are unique: select comp >= prefix (all 64 bits resolved) in entry order
-  uint32_t written = 0;
-  for (int c0 = 0; c0 < n_t; c0 += kSelThreads) {
-    const int j = c0 + tid;
-    bool take = false;
-    if (j < n_t) {
-      const unsigned long long comp =
-          ((unsigned long long)score_key(score_row(qq, codes, scale, j)) << 32) | (uint32_t)~(uint32_t)j;
-      take = k_eff > 0 && comp >= prefix;
-    }
-    uint32_t tot;
-    const uint32_t p = block_scan_excl(take ? 1u : 0u, s_scan, &tot);
-    if (take && written + p < (uint32_t)k) orow[written + p] = j;
-    written += tot;
-  }
-  for (int i = (int)written + tid; i < k; i += kSelThreads) orow[i] = -1;
 }
 
 // ------------------------------------------------------------ causal score matrix
@@ -1107,8 +1297,13 @@ hipError_t launch_prefill_select(const uint16_t* q_idx, const uint8_t* idx_codes
                        dim3(kGemmThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio,
                        pos0, T, ws);
   }
-  hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), 0, stream, q_idx, idx_codes,
-                     idx_scale, n_entries, ratio, pos0, T, k, idx_out, ws);
+  if (ws.n_splits <= kRowSplits)
+    hipLaunchKernelGGL(k_prefill_select_rows, dim3((T + kSelRowsPerBlock - 1) / kSelRowsPerBlock),
+                       dim3(kSelThreads), 0, stream, q_idx, idx_codes, idx_scale, n_entries, ratio, pos0,
+                       T, k, idx_out, ws);
+  else
+    hipLaunchKernelGGL(k_prefill_select, dim3(T), dim3(kSelThreads), 0, stream, q_idx, idx_codes,
+                       idx_scale, n_entries, ratio, pos0, T, k, idx_out, ws);
   return hipGetLastError();
 }
 

@@ -117,6 +117,52 @@ def test_prefill_sampled_threshold_too_high_falls_back():
     check_rows(cache, q_idx, q, swa, N, 1, pos0, k, idx, out, range(T))
 
 
+def test_prefill_tied_keys_go_to_lower_entries():
+    # every index key appears four times (25,000 distinct rows at random positions): a row's
+    # threshold score is often shared by entries on both sides of the cut, and the row takes
+    # the lowest of them (sampled threshold, candidates resolved one wave per row)
+    log("prefill tied keys")
+    N, T, pos0, k = 100000, 16, 99000, 512
+    g = torch.Generator().manual_seed(11)
+    base = torch.randn(N // 4, 128, generator=g)
+    x = base[torch.randperm(N, generator=g) % (N // 4)]
+    codes, scale, _ = synth.quantize_index_keys(x)
+    ent = synth.make_entries([N], seed=11, device=DEV)
+    cache = synth.EntryCache(codes.to(DEV), scale.to(DEV), ent.kv_codes, ent.kv_scale,
+                             ent.seq_base, ent.n_entries)
+    q_idx = synth.make_index_queries(T, 11, device=DEV)
+    q = synth.make_queries(T, 11, device=DEV)
+    swa = synth.make_swa(1, T + 127, 11, device=DEV)[0]
+    idx, out = run_prefill(cache, q_idx, q, swa, N, 1, pos0, k)
+    torch.cuda.synchronize()
+    check_rows(cache, q_idx, q, swa, N, 1, pos0, k, idx, out, range(T))
+    keys = oracle.dequant_index_keys(h(cache.idx_codes))
+    kscale = h(cache.idx_scale).astype(np.float64)
+    qi, gi = h(q_idx), h(idx)
+    split_rows = 0
+    for t in range(T):
+        n_t = oracle.visible_entries(pos0 + t, 1, N)
+        s = kscale[:n_t] * (keys[:n_t] @ oracle.formats.bf16_decode(qi[t]))
+        order = np.lexsort((np.arange(n_t), -s))
+        sk = s[order[k - 1]]
+        others = np.abs(s[s != sk] - sk)
+        if (s == sk).sum() > (s[order[:k]] == sk).sum() and others.min() > 1e-4 * abs(sk):
+            # duplicates of the threshold score on both sides of the cut, clear of the rest
+            assert np.array_equal(gi[t], np.sort(order[:k])), f"row {t}: tie not to the lower entries"
+            split_rows += 1
+    log(f"rows whose threshold duplicates were split: {split_rows}")
+    assert split_rows >= 4
+
+
+def test_prefill_rows_of_many_splits():
+    # 140,000 entries: 35 entry splits, more than one wave's registers hold per row, so rows
+    # are resolved a workgroup per row
+    log("prefill 35 splits")
+    N, T, pos0, k = 140000, 16, 139990, 512
+    cache, q_idx, q, swa, idx, out = _case(N, 1, T, pos0, k, seed=13)
+    check_rows(cache, q_idx, q, swa, N, 1, pos0, k, idx, out, range(T))
+
+
 def test_prefill_select_and_reuse_attention_match_chunk():
     # csa2_prefill_select writes the chunk's lists; csa2_sparse_attn_prefill over them with the
     # same queries and window reproduces the chunk's output bit for bit, and a Reuse layer's
