@@ -1404,8 +1404,6 @@ __global__ __launch_bounds__(kT) void k_fsmall(FsArgs a) {
 }
 
 // ---------------------------------------------------------------------------- host side
-constexpr int kMaxDevices = 64;
-
 // Compute units of the current device (the picking grid's size aims at one workgroup
 // each; correctness does not depend on it).
 int fs_capacity() {
