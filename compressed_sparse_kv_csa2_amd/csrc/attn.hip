@@ -19,8 +19,10 @@
 //     [2^14, 2^15) and rounded to fp16 (exact unless an element is below 2^-28 of its
 //     head's largest); the power of two is folded back into the softmax scale.  q . v on
 //     v_mfma_f32_16x16x32_f16 then has exact products and fp32 sums;
-//   * p . v takes p as the sum of two fp16 halves (hi = fp16(p), lo = fp16(p - hi)), two
-//     v_mfma_f32_16x16x16_f16, relative error about 2^-22, fp32 sums.
+//   * p . v takes p as the sum of two fp16 halves (hi = fp16(p), lo = fp16(p - hi)),
+//     relative error about 2^-22, fp32 sums: one v_mfma_f32_16x16x32_f16 per output tile
+//     whose K runs over the hi half at the segment's 16 positions, then the lo half at the
+//     same positions (v's rows given twice).
 // Work split: one 128-thread workgroup (2 waves) per (row, split) walks the split's
 // 16-position segments of the row's list (the k selected entries, then the window rows);
 // wave w owns dims 256 w .. 256 w + 255 of every segment:
@@ -37,8 +39,9 @@
 //            reductions) nor a rescale of the accumulators is needed;
 //   p . v    the dequantised half-segment is also written to the wave's LDS tile (positions
 //            x dims, XOR-swizzled) and read back transposed with ds_read_b64_tr_b16 as the
-//            B operand of 16 output tiles of 16 dims; p (hi from wave 0, lo from wave 1)
-//            goes through LDS the same way.  Two workgroup barriers per segment.
+//            B operand of 16 output tiles of 16 dims; p's hi and lo halves (each wave
+//            writes its heads') go through LDS the same way.  Two workgroup barriers per
+//            segment.
 // A row with several splits leaves (max, sum, acc[16][512]) per split in the workspace and
 // k_attn_merge combines them by log-sum-exp.  exp2 with log2(e) folded into
 // the scale.
@@ -316,8 +319,9 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
   for (int t = 0; t < kHalfTiles; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
   f16* vt = s_v[w];
-  // transposed-read coordinates: lane = 16 g + 4 mm + qq reads row 4 g + mm, columns 4 qq
-  const int tr_row = 4 * g16 + ((lane >> 2) & 3), tr_q = lane & 3;
+  // transposed-read coordinates of p . v: lane = 16 g + 4 mm + qq reads rows
+  // 8 (g % 2) + mm and 8 (g % 2) + 4 + mm, columns 4 qq
+  const int tr_row = 8 * (g16 & 1) + ((lane >> 2) & 3), tr_q = lane & 3;
 
   for (int stage0 = seg_begin; stage0 < seg_end; stage0 += kIdxStage / kSeg) {
     const int stage1 = min(stage0 + kIdxStage / kSeg, seg_end);
@@ -434,21 +438,31 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) acc[t][rr] *= al[rr];
       }
-      // ---- acc += p . v over this wave's half: A = p (head, 4 positions), B = v, transposed
-      const f16x4 a_hi = tr_read(s_p[0] + tr_row * kHeads + 4 * tr_q);
-      const f16x4 a_lo = tr_read(s_p[1] + tr_row * kHeads + 4 * tr_q);
-      const int tsw = vswz(tr_row);
-      // tiles t and t + 8 share the swizzled block's low bits: 8 loop-invariant bases,
+      // ---- acc += p . v over this wave's half: one v_mfma_f32_16x16x32_f16 per tile whose
+      // K = 32 runs over p's hi half at the segment's 16 positions, then its lo half at the
+      // same positions (lane groups 0, 1: hi, positions 0-7, 8-15; groups 2, 3: lo), with v's
+      // rows given twice.  A = p (head, 8 positions), B = v (8 positions, dim), transposed
+      // reads of rows tr_row and tr_row + 4.
+      const f16* pb = s_p[g16 >> 1];
+      const f16x4 pa = tr_read(pb + tr_row * kHeads + 4 * tr_q);
+      const f16x4 pc = tr_read(pb + (tr_row + 4) * kHeads + 4 * tr_q);
+      const f16x8 a8 = __builtin_shufflevector(pa, pc, 0, 1, 2, 3, 4, 5, 6, 7);
+      const int tsw0 = vswz(tr_row), tsw1 = vswz(tr_row + 4);
+      // tiles t and t + 8 share the swizzled block's low bits: loop-invariant bases,
       // immediate offsets
-      const f16* vr[8];
+      const f16* vr0[8];
+      const f16* vr1[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        vr[t] = vt + tr_row * kHalf + 8 * ((2 * t + (tr_q >> 1)) ^ tsw) + 4 * (tr_q & 1);
+      for (int t = 0; t < 8; ++t) {
+        vr0[t] = vt + tr_row * kHalf + 8 * ((2 * t + (tr_q >> 1)) ^ tsw0) + 4 * (tr_q & 1);
+        vr1[t] = vt + (tr_row + 4) * kHalf + 8 * ((2 * t + (tr_q >> 1)) ^ tsw1) + 4 * (tr_q & 1);
+      }
 #pragma unroll
       for (int t = 0; t < kHalfTiles; ++t) {
-        const f16x4 bv = tr_read(vr[t & 7] + 128 * (t >> 3));
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a_hi, bv, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a_lo, bv, acc[t], 0, 0, 0);
+        const f16x4 b0 = tr_read(vr0[t & 7] + 128 * (t >> 3));
+        const f16x4 b1 = tr_read(vr1[t & 7] + 128 * (t >> 3));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                        acc[t], 0, 0, 0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();  // the next segment rewrites this wave's tile
