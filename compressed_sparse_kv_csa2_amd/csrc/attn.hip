@@ -140,12 +140,15 @@ __device__ __forceinline__ float row16(float v) {
   return v;
 }
 
-// Raw bytes of one lane's 64 dims of a position in a segment: main entry (u[0..1] = 32
-// code bytes, sc = its 4 scale bytes), window row (u[0..3] = 64 bytes), or nothing.  Every
-// lane issues the same five loads whatever its kind (unused ones re-read a valid
-// address), so the compiler can keep later segments' loads in flight.
+// Raw bytes of one lane's 64 dims of a position in a segment: main entry (m = 32 code
+// bytes, sc = its 4 scale bytes), window row (w = 64 bytes), or nothing.  Every lane issues
+// all seven loads whatever its kind (a lane of the other kind, or of nothing, reads the
+// sequence's first entry or the first window row, which the segment's other lanes share):
+// no branch, the addresses are one select and one shift-add each, and every lane's loads
+// stay in flight.
 struct Raw {
-  uint4 u[4];
+  uint4 m[2];
+  uint4 w[4];
   uint32_t sc;
   int kind;  // 0 nothing, 1 main entry, 2 window row
 };
@@ -238,7 +241,10 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
   const int n_pos = k + nrows;
   const int n_seg = (n_pos + kSeg - 1) / kSeg;
   const int seg_end = min(seg_begin + segs_per_split, n_seg);
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(qrow);  // any valid 64 bytes
+  // this lane's bytes of entry 0 / window row 0: the gathers add the entry or row offset
+  const uint8_t* code_base = kv_codes + base * kKvCodeBytes + d0 / 2;
+  const uint8_t* scale_base = kv_scale + base * kKvScaleBytes + d0 / 16;
+  const uint8_t* win_base = rows + d0;
 
   // Raw bytes of segment `seg` for this lane (entry id j if its position holds a main
   // entry); nothing at or past segment `stop`
@@ -246,18 +252,16 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
     Raw r;
     const int p = seg * kSeg + n16;
     const int kind = (seg < stop && p < n_pos) ? (p < k ? (j >= 0 ? 1 : 0) : 2) : 0;
-    const int64_t e = base + (kind == 1 ? j : 0);
-    const uint8_t* am = kv_codes + e * kKvCodeBytes + d0 / 2;
-    const uint8_t* aw = rows + (size_t)(kind == 2 ? p - k : 0) * kDKv + d0;
-    const uint8_t* a = kind == 1 ? am : kind == 2 ? aw : dummy;
-    const uint8_t* a2 = kind == 2 ? aw + 32 : a;
-    const uint8_t* asc = kind == 1 ? kv_scale + e * kKvScaleBytes + d0 / 16 : a;
-    r.u[0] = reinterpret_cast<const uint4*>(a)[0];
-    r.u[1] = reinterpret_cast<const uint4*>(a)[1];
-    r.u[2] = reinterpret_cast<const uint4*>(a2)[0];
-    r.u[3] = reinterpret_cast<const uint4*>(a2)[1];
-    r.sc = *reinterpret_cast<const uint32_t*>(asc);
     r.kind = kind;
+    const uint32_t jj = kind == 1 ? (uint32_t)j : 0u;
+    const uint32_t pp = kind == 2 ? (uint32_t)(p - k) : 0u;
+    const uint4* am = reinterpret_cast<const uint4*>(code_base + (uint64_t)jj * kKvCodeBytes);
+    const uint4* aw = reinterpret_cast<const uint4*>(win_base + (uint64_t)pp * kDKv);
+    r.m[0] = am[0];
+    r.m[1] = am[1];
+    r.sc = *reinterpret_cast<const uint32_t*>(scale_base + (uint64_t)jj * kKvScaleBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = aw[i];
     return r;
   };
   // the split's first segment is in flight through q's prologue and the ids' staging
@@ -365,20 +369,20 @@ __global__ __launch_bounds__(kAThreads, 2) void k_attn(
       };
       if (!any_win) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) step(s, deq_main(word_of(r.u[s >> 2], s & 3), sc[s >> 1]));
+        for (int s = 0; s < 8; ++s) step(s, deq_main(word_of(r.m[s >> 2], s & 3), sc[s >> 1]));
       } else if (!any_main) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const uint4 v = r.u[s >> 1];
+          const uint4 v = r.w[s >> 1];
           step(s, (s & 1) ? deq_win(v.z, v.w) : deq_win(v.x, v.y));
         }
       } else {
         const bool win = r.kind == 2;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const uint4 v = r.u[s >> 1];
+          const uint4 v = r.w[s >> 1];
           const f16x8 bw = (s & 1) ? deq_win(v.z, v.w) : deq_win(v.x, v.y);
-          const f16x8 bm = deq_main(word_of(r.u[s >> 2], s & 3), sc[s >> 1]);
+          const f16x8 bm = deq_main(word_of(r.m[s >> 2], s & 3), sc[s >> 1]);
           step(s, win ? bw : bm);
         }
       }
