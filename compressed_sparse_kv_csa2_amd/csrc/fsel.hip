@@ -129,7 +129,7 @@ struct FsArgs {
 
 // LDS the exact-threshold search and the ordered emission share.
 struct Core {
-  uint32_t hist[kBins];
+  uint32_t hist[kBins + 64];  // + one overflow bin per lane (never read)
   unsigned long long pub[64];
   uint32_t scan[32];
   uint32_t red[3 * kNW];
@@ -483,11 +483,11 @@ __device__ __forceinline__ Thr find_thr_lean(const uint32_t (&kk)[U], XF X, int 
 #pragma unroll
   for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
   __syncthreads();
+  // a key below the window (or zero) wraps to a huge bin and lands in the lane's overflow
+  // bin: no branch per key
+  const uint32_t ovf = kBins + (threadIdx.x & 63u);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t v = kk[u];
-    if (v >= lo) atomicAdd(&L.hist[(v - lo) >> 12], 1u);
-  }
+  for (int u = 0; u < U; ++u) atomicAdd(&L.hist[min((kk[u] - lo) >> 12, ovf)], 1u);
   __syncthreads();
   find_bin4(L.hist, need, false, L);  // ends with a barrier
   bool general = uni(L.res[2]) < need;  // the threshold lies below the window
@@ -500,10 +500,7 @@ __device__ __forceinline__ Thr find_thr_lean(const uint32_t (&kk)[U], XF X, int 
     for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t e = kk[u] - lo2;
-      if (e < 4096u) atomicAdd(&L.hist[e], 1u);
-    }
+    for (int u = 0; u < U; ++u) atomicAdd(&L.hist[min(kk[u] - lo2, ovf)], 1u);
     __syncthreads();
     find_bin4(L.hist, need, false, L);
     const uint32_t d = uni(L.res[0]);
@@ -686,11 +683,9 @@ __device__ __forceinline__ uint32_t seg_cut(const uint32_t (&kv)[U], uint32_t ke
 #pragma unroll
   for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
   __syncthreads();
+  const uint32_t ovf = kBins + (threadIdx.x & 63u);  // keys below the window (or zero)
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t v = kv[u];
-    if (v >= lo) atomicAdd(&L.hist[(v - lo) >> 12], 1u);
-  }
+  for (int u = 0; u < U; ++u) atomicAdd(&L.hist[min((kv[u] - lo) >> 12, ovf)], 1u);
   __syncthreads();
   find_bin4(L.hist, keep, false, L);  // ends with a barrier
   uint32_t cut = lo + (uni(L.res[0]) << 12);
@@ -880,6 +875,40 @@ __device__ __forceinline__ void bitmap_prefix(const uint32_t* bm, uint32_t* wp, 
   __syncthreads();
 }
 
+// bm bits of candidates i = threadIdx.x + kT * u (u < U): bit i set where sel(u) holds.  The
+// wave's ballot for u covers words 32 u + 2 wave and 32 u + 2 wave + 1; the U ballots go
+// into one register (lane 2 u + h keeps word half h of ballot u) and out in one store.
+template <int U, class SelF>
+__device__ __forceinline__ void mark_bits(uint32_t* bm, SelF sel) {
+  static_assert(2 * U <= 64, "one word per lane");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t val = 0u;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const unsigned long long m = __ballot(sel(u));
+    val = lane == 2 * u ? (uint32_t)m : val;
+    val = lane == 2 * u + 1 ? (uint32_t)(m >> 32) : val;
+  }
+  if (lane < 2 * U) bm[32 * (lane >> 1) + 2 * wave + (lane & 1)] = val;
+}
+
+// bm bits of the keys kv[u] (candidate i = threadIdx.x + kT * u, zero at and past m) that
+// threshold t selects.  When t takes every key equal to its key (no split by index), the
+// test is one compare.
+template <int U>
+__device__ __forceinline__ void mark_selected(uint32_t* bm, const Thr& t, const uint32_t (&kv)[U], int m) {
+  const int tid = threadIdx.x;
+  if (t.tx == 0xffffffffu) {
+    const uint32_t lo = max(t.tkey, 1u);  // a zero key is never selected
+    mark_bits<U>(bm, [&](int u) { return kv[u] >= lo; });
+  } else {
+    mark_bits<U>(bm, [&](int u) {
+      const int i = tid + kT * u;
+      return (i < m) & selected(t, kv[u], (uint32_t)i);
+    });
+  }
+}
+
 // Marks in L.bm the top-k of the m candidates (key kv[u] of candidate i = threadIdx.x +
 // kT * u, ties to the lower index, i.e. the lower column).  Returns the number selected and
 // the threshold.  Whole workgroup; ends with a barrier.
@@ -891,15 +920,7 @@ __device__ __forceinline__ Thr pick_marked(const uint32_t (&kv)[kU], int m, uint
   for (int u = 0; u < kU; ++u) mx = max(mx, kv[u]);
   block_sum_max(c, mx, L.c);
   const Thr t = find_thr_lean<kU>(kv, [&](int, int i) { return (uint32_t)i; }, m, k, (uint32_t)m, mx, L.c);
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int i = tid + kT * u;
-    const unsigned long long msk = __ballot(i < m && selected(t, kv[u], (uint32_t)i));
-    if (lane == 0) {
-      L.bm[(kT * u + 64 * wave) >> 5] = (uint32_t)msk;
-      L.bm[((kT * u + 64 * wave) >> 5) + 1] = (uint32_t)(msk >> 32);
-    }
-  }
+  mark_selected<kU>(L.bm, t, kv, m);
   if (tid == 0) L.bm[kMaxCand / 32] = 0u;
   __syncthreads();
   return t;
@@ -1073,11 +1094,13 @@ __device__ __forceinline__ void pick_reindex(const FsArgs& a, PickLds& L, int r,
   if (tid == 0) FS_TR(trb + 4, FS_NOW());
   const int b = a.row0 + r;
   const uint32_t* cc = a.ccol + (size_t)r * a.cap;
+  // every bitmap word is written (no bit at or past m), so the reads need no bounds test
   uint32_t kk[kU], c = 0u, mx = 0u;
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int i = tid + kT * u;
-    kk[u] = (i < m && bit_at(L.bm, (uint32_t)i)) ? L.key[i] : 0u;
+    const uint32_t w = L.bm[i >> 5], key = L.key[i];
+    kk[u] = (w >> (i & 31)) & 1u ? key : 0u;
     c += kk[u] != 0u ? 1u : 0u;
     mx = max(mx, kk[u]);
   }
@@ -1085,15 +1108,7 @@ __device__ __forceinline__ void pick_reindex(const FsArgs& a, PickLds& L, int r,
   if (tid == 0) FS_TR(trb, FS_NOW());
   const Thr tr = find_thr_lean<kU>(kk, [&](int, int i) { return (uint32_t)i; }, m, (uint32_t)a.re_k, c, mx, L.c);
   if (tid == 0) FS_TR(trb + 1, FS_NOW());
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int i = tid + kT * u;
-    const unsigned long long msk = __ballot(i < m && selected(tr, kk[u], (uint32_t)i));
-    if (lane == 0) {
-      L.rbm[(kT * u + 64 * wave) >> 5] = (uint32_t)msk;
-      L.rbm[((kT * u + 64 * wave) >> 5) + 1] = (uint32_t)(msk >> 32);
-    }
-  }
+  mark_selected<kU>(L.rbm, tr, kk, m);
   if (tid == 0) L.rbm[kMaxCand / 32] = 0u;
   __syncthreads();
   bitmap_prefix(L.rbm, L.rwp, m, L.c);
@@ -1372,15 +1387,7 @@ __global__ __launch_bounds__(kT) void k_fsmall(FsArgs a) {
   if (tid == 0) FS_TR(tb + 3, FS_NOW());
   const Thr t = find_thr_lean<kSmallU>(kv, [&](int, int i) { return (uint32_t)i; }, n, (uint32_t)a.k, c, mx, L.c);
   if (tid == 0) FS_TR(tb + 4, FS_NOW());
-#pragma unroll
-  for (int u = 0; u < kSmallU; ++u) {
-    const int i = tid + kT * u;
-    const unsigned long long msk = __ballot(i < n && selected(t, kv[u], (uint32_t)i));
-    if (lane == 0) {
-      L.bm[(kT * u + 64 * wave) >> 5] = (uint32_t)msk;
-      L.bm[((kT * u + 64 * wave) >> 5) + 1] = (uint32_t)(msk >> 32);
-    }
-  }
+  mark_selected<kSmallU>(L.bm, t, kv, n);
   if (tid == 0) L.bm[kSmallCols / 32] = 0u;
   __syncthreads();
   bitmap_prefix(L.bm, L.wp, n, L.c);
