@@ -522,13 +522,15 @@ template <int U, class EmitF>
 __device__ __forceinline__ uint32_t emit_reg(uint32_t mine, EmitF emit, Core& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   static_assert(U * kNW <= 1024, "counts fit the scan");
-  uint32_t below[U];
+  static_assert(U <= 64, "one count per lane");
+  uint32_t below[U], cnt = 0u;  // lane u keeps the wave's count for u, stored at once
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const unsigned long long msk = __ballot((mine >> u) & 1u);
     below[u] = lanes_below(msk);
-    if (lane == 0) L.hist[u * kNW + wave] = (uint32_t)__popcll(msk);
+    cnt = lane == u ? (uint32_t)__popcll(msk) : cnt;
   }
+  if (lane < U) L.hist[lane * kNW + wave] = cnt;
   __syncthreads();
   if (wave == 0) {  // U * kNW counts in (u, wave) order = index order
     constexpr int PER = (U * kNW + 63) / 64;
@@ -549,9 +551,12 @@ __device__ __forceinline__ uint32_t emit_reg(uint32_t mine, EmitF emit, Core& L)
     if (lane == 63) L.misc[5] = incl;
   }
   __syncthreads();
+  // every base read before the first is used (one wait, not one per u)
+#pragma unroll
+  for (int u = 0; u < U; ++u) below[u] += L.hist[u * kNW + wave];
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    if ((mine >> u) & 1u) emit(L.hist[u * kNW + wave] + below[u], u, tid + kT * u);
+    if ((mine >> u) & 1u) emit(below[u], u, tid + kT * u);
   const uint32_t total = uni(L.misc[5]);
   __syncthreads();
   return total;
