@@ -468,7 +468,10 @@ __device__ __forceinline__ Thr find_thr(KF K, XF X, int m, uint32_t k, Core& L, 
 // mx (bins of 4,096 values), one of the exact values inside the threshold's bin, done.  The
 // general search runs instead when the threshold lies below that window, or when keys
 // equal to the threshold key must be split by the tie index.  kk[u] = 0 for i >= m.
-template <int U, class XF>
+// DENSE: nearly every key lies in the first window (the pool's candidates), so its histogram
+// pass takes no branch per key (a key below the window wraps to a huge bin and lands in
+// the lane's overflow bin); otherwise keys outside a window skip it.
+template <int U, bool DENSE = false, class XF>
 __device__ __forceinline__ Thr find_thr_lean(const uint32_t (&kk)[U], XF X, int m, uint32_t k, uint32_t c,
                                              uint32_t mx, Core& L) {
   const int tid = threadIdx.x;
@@ -483,11 +486,17 @@ __device__ __forceinline__ Thr find_thr_lean(const uint32_t (&kk)[U], XF X, int 
 #pragma unroll
   for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
   __syncthreads();
-  // a key below the window (or zero) wraps to a huge bin and lands in the lane's overflow
-  // bin: no branch per key
-  const uint32_t ovf = kBins + (threadIdx.x & 63u);
+  if (DENSE) {
+    const uint32_t ovf = kBins + (threadIdx.x & 63u);
 #pragma unroll
-  for (int u = 0; u < U; ++u) atomicAdd(&L.hist[min((kk[u] - lo) >> 12, ovf)], 1u);
+    for (int u = 0; u < U; ++u) atomicAdd(&L.hist[min((kk[u] - lo) >> 12, ovf)], 1u);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t v = kk[u];
+      if (v >= lo) atomicAdd(&L.hist[(v - lo) >> 12], 1u);
+    }
+  }
   __syncthreads();
   find_bin4(L.hist, need, false, L);  // ends with a barrier
   bool general = uni(L.res[2]) < need;  // the threshold lies below the window
@@ -500,7 +509,10 @@ __device__ __forceinline__ Thr find_thr_lean(const uint32_t (&kk)[U], XF X, int 
     for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < U; ++u) atomicAdd(&L.hist[min(kk[u] - lo2, ovf)], 1u);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t e = kk[u] - lo2;  // few keys fall in the threshold's bin
+      if (e < 4096u) atomicAdd(&L.hist[e], 1u);
+    }
     __syncthreads();
     find_bin4(L.hist, need, false, L);
     const uint32_t d = uni(L.res[0]);
@@ -522,15 +534,13 @@ template <int U, class EmitF>
 __device__ __forceinline__ uint32_t emit_reg(uint32_t mine, EmitF emit, Core& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   static_assert(U * kNW <= 1024, "counts fit the scan");
-  static_assert(U <= 64, "one count per lane");
-  uint32_t below[U], cnt = 0u;  // lane u keeps the wave's count for u, stored at once
+  uint32_t below[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const unsigned long long msk = __ballot((mine >> u) & 1u);
     below[u] = lanes_below(msk);
-    cnt = lane == u ? (uint32_t)__popcll(msk) : cnt;
+    if (lane == 0) L.hist[u * kNW + wave] = (uint32_t)__popcll(msk);
   }
-  if (lane < U) L.hist[lane * kNW + wave] = cnt;
   __syncthreads();
   if (wave == 0) {  // U * kNW counts in (u, wave) order = index order
     constexpr int PER = (U * kNW + 63) / 64;
@@ -551,12 +561,9 @@ __device__ __forceinline__ uint32_t emit_reg(uint32_t mine, EmitF emit, Core& L)
     if (lane == 63) L.misc[5] = incl;
   }
   __syncthreads();
-  // every base read before the first is used (one wait, not one per u)
-#pragma unroll
-  for (int u = 0; u < U; ++u) below[u] += L.hist[u * kNW + wave];
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    if ((mine >> u) & 1u) emit(below[u], u, tid + kT * u);
+    if ((mine >> u) & 1u) emit(L.hist[u * kNW + wave] + below[u], u, tid + kT * u);
   const uint32_t total = uni(L.misc[5]);
   __syncthreads();
   return total;
@@ -688,9 +695,12 @@ __device__ __forceinline__ uint32_t seg_cut(const uint32_t (&kv)[U], uint32_t ke
 #pragma unroll
   for (int i = 0; i < kBins / kT; ++i) L.hist[tid + kT * i] = 0u;
   __syncthreads();
-  const uint32_t ovf = kBins + (threadIdx.x & 63u);  // keys below the window (or zero)
+  // most of a segment's keys lie below the window: they skip the histogram
 #pragma unroll
-  for (int u = 0; u < U; ++u) atomicAdd(&L.hist[min((kv[u] - lo) >> 12, ovf)], 1u);
+  for (int u = 0; u < U; ++u) {
+    const uint32_t v = kv[u];
+    if (v >= lo) atomicAdd(&L.hist[(v - lo) >> 12], 1u);
+  }
   __syncthreads();
   find_bin4(L.hist, keep, false, L);  // ends with a barrier
   uint32_t cut = lo + (uni(L.res[0]) << 12);
@@ -924,7 +934,7 @@ __device__ __forceinline__ Thr pick_marked(const uint32_t (&kv)[kU], int m, uint
 #pragma unroll
   for (int u = 0; u < kU; ++u) mx = max(mx, kv[u]);
   block_sum_max(c, mx, L.c);
-  const Thr t = find_thr_lean<kU>(kv, [&](int, int i) { return (uint32_t)i; }, m, k, (uint32_t)m, mx, L.c);
+  const Thr t = find_thr_lean<kU, true>(kv, [&](int, int i) { return (uint32_t)i; }, m, k, (uint32_t)m, mx, L.c);
   mark_selected<kU>(L.bm, t, kv, m);
   if (tid == 0) L.bm[kMaxCand / 32] = 0u;
   __syncthreads();
