@@ -131,12 +131,14 @@ __device__ __forceinline__ float vmax(float a, float b) {
   return r;
 }
 
-// v_max3_f32, likewise without quieting.
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+// x of lane g of this lane's quad (a DPP operand of the instruction that uses it).
+template <int G>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), G * 0x55, 0xf, 0xf, true));
 }
+
+// Largest of three products (canonical, finite): the compiler emits one v_max3_f32.
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // LDS stage: entry i's 64 code bytes as 4 blocks of 16 bytes, block b at b ^ ((i >> 2) & 3)
 // so that 16 consecutive entries' reads of one block land in 16 distinct bank groups.
@@ -288,28 +290,31 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gmax(
 
 // PASS 2: the candidates.  The same contraction over every entry, taken transposed (the
 // expanded keys as the A operand, entries x queries): lane l of a wave holds, for its
-// query row0 + 32 s + l % 32, 16 scores of the tile.  The stage stores each tile's 32
-// entries permuted (entry 16 h + 4 g + i at A row 8 g + 4 h + i), so that accumulator
-// 4 g + i of lane half h = l / 32 is entry 16 h + 4 g + i: each lane holds 16 consecutive
-// entries.  Hits (scores >= the row's threshold) are rare, about one score in 200, so a
-// lane only tests the largest of its 16 scores per tile; a lane that may hold a hit puts
-// its 16 scores in the wave's LDS queue as one record (position from the ballot), and once
-// 64 records are queued each lane sorts out one.  Slots of a (row, split) list come from
-// the row's LDS counter, taken in queue order (a row's lower half before its upper half,
-// tiles in order), so the list is in entry order as long as the counter serves the lanes
-// of one atomic in lane order; the select checks that and ranks the list itself otherwise.
+// query row0 + 32 s + l % 32, 16 scores of the tile.  The A operand is read straight from
+// memory, each lane its 32 code bytes (lane l takes half l / 32 of the codes of A row
+// l % 32), and A rows are assigned entries permuted (entry 16 h + 4 g + i at A row
+// 8 g + 4 h + i), so that accumulator 4 g + i of lane half h = l / 32 is entry
+// 16 h + 4 g + i: each lane holds 16 consecutive entries.  With no stage in LDS the waves
+// run without barriers, and the LDS holds only the record queues.  Hits (scores >= the
+// row's threshold) are rare, about one score in 200, so a lane only tests the largest of
+// its 16 scores per tile; a lane that may hold a hit puts its 16 scores in the wave's LDS
+// queue as one record (position from the ballot), and once 64 records are queued each lane
+// sorts out one.  Slots of a (row, split) list come from
 constexpr int kRecBatch = 64;               // records drained at once (one per lane)
 constexpr int kRecQueue = 2 * kRecBatch;    // a batch + one tile's worth
 // Queue layout: group g (scores 4 g .. 4 g + 3) of record j at s_rec[wave][g][j], so a
 // record is written with one address and four offsets, and the lanes of one access touch
 // consecutive 16-byte slots.
-// A row of the stage: entry e of a tile (e < 32) sits at A row tile_row(e).
-__device__ __forceinline__ int tile_row(int e) { return ((e >> 2) & 3) << 3 | (e >> 4) << 2 | (e & 3); }
+// The entry (within its tile of 32) at A row r: the inverse of e -> 8 ((e >> 2) & 3) +
+// 4 (e >> 4) + (e & 3).
+__device__ __forceinline__ int row_entry(int r) { return ((r >> 2) & 1) << 4 | (r >> 3) << 2 | (r & 3); }
+// A raw buffer over n bytes: loads at offsets past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int n_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n_bytes, 0x00020000);
+}
 __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
-  __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
-  __shared__ float4 s_sc[2][kStage / 4];
   __shared__ uint32_t s_rcnt[kGemmRows];     // candidates of each of the workgroup's rows
   __shared__ float s_th[kGemmRows];          // each row's threshold (+inf past T)
   __shared__ int s_nv[kGemmRows];            // entries each row sees
@@ -322,10 +327,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
   const int e_begin = split * kSplitEntries;
   const int e_end = min(e_begin + kSplitEntries, n_entries);
   const int rl = lane & 31, half = lane >> 5;
-  const int wg_nmax = visible(pos0 + min(wg_row0 + kGemmRows - 1, T - 1), ratio, n_entries);
   const int wave_nmax = row0 < T ? visible(pos0 + min(row0 + kWaveRows - 1, T - 1), ratio, n_entries) : 0;
-  const int e_stop = min(e_end, wg_nmax);
-  const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
+  // tiles of 32 entries that some row of the wave sees (wave-uniform)
+  const int n_tiles = max(0, (min(e_end, wave_nmax) - e_begin + 31) / 32);
   static_assert(kGemmThreads == kGemmRows, "one row of the workgroup per thread");
   {
     const int t = wg_row0 + tid;
@@ -390,118 +394,156 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
     }
   };
 
-  // the stage slot of this thread's entry: its tile, its A row
-  const int fill_i = (tid & ~31) | tile_row(tid & 31);
-  uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
-  float psc = 0.f;
-  auto load_stage = [&](int st) {
-    const int e = min(e_begin + st * kStage + tid, n_entries - 1);
-    const uint4* cp = reinterpret_cast<const uint4*>(codes + (size_t)e * kIdxCodeBytes);
-    pc0 = cp[0];
-    pc1 = cp[1];
-    pc2 = cp[2];
-    pc3 = cp[3];
-    psc = scale[e];
+  // Tile loads, two tiles ahead: lane (rl, half) takes code bytes 32 half .. + 31 of A row
+  // rl, and lane q of each quad the scales of entries 16 half + 4 q .. + 3 (the group whose
+  // A rows its quad's lanes hold as accumulators 4 q .. 4 q + 3).  Entries past the end
+  // read as zeros.
+  const __amdgpu_buffer_rsrc_t rs_code = buffer_over(codes, n_entries * kIdxCodeBytes);
+  const __amdgpu_buffer_rsrc_t rs_scale = buffer_over(scale, n_entries * 4);
+  const int a_off = (e_begin + row_entry(rl)) * kIdxCodeBytes + 32 * half;
+  const int s_off = (e_begin + 16 * half + 4 * (lane & 3)) * 4;
+  struct TileIn {
+    uint4 c0, c1;
+    float sc[4];
   };
-  if (n_active > 0) load_stage(0);
-  for (int st = 0; st < n_active; ++st) {
-    const int buf = st & 1;
-    s_code[buf][stage_blk(fill_i, 0)] = pc0;
-    s_code[buf][stage_blk(fill_i, 1)] = pc1;
-    s_code[buf][stage_blk(fill_i, 2)] = pc2;
-    s_code[buf][stage_blk(fill_i, 3)] = pc3;
-    reinterpret_cast<float*>(s_sc[buf])[fill_i] = psc;
-    __syncthreads();
-    if (st + 1 < n_active) load_stage(st + 1);  // in flight during the MFMAs
-    const int st_e0 = e_begin + st * kStage;
-    // tiles of the stage that some row of the wave sees (wave-uniform)
-    const int n_tt = min(kStage / 32, max(0, (wave_nmax - st_e0 + 31) / 32));
-    // Software pipelined: the MFMAs of a tile are issued before the screening of the tile
-    // before it, which does not depend on them.
-    auto mfma_tile = [&](int tt, f32x16 (&acc)[kSets]) {
-      const int i = tt * 32 + rl;  // A operand: stage row i
-      const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
-      const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
-      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  auto load_tile = [&](int tt, TileIn& in) {
+    const int ct = min(tt, n_tiles - 1);  // past the last tile: a repeat, never used
+    in.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_code, a_off + ct * 32 * kIdxCodeBytes, 0, 0));
+    in.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_code, a_off + ct * 32 * kIdxCodeBytes + 16, 0, 0));
 #pragma unroll
-      for (int s = 0; s < kSets; ++s) acc[s] = f32x16{};
+    for (int i = 0; i < 4; ++i)
+      in.sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_scale, s_off + (ct * 32 + i) * 4, 0, 0));
+  };
+  // Software pipelined: the MFMAs of a tile are issued together with the branch-free part
+  // of the screening of the tile before it (scaling, row maxima, ballots), interleaved so
+  // that one wave keeps the matrix and vector units busy at once; the record writes, which
+  // branch, follow.
+  auto mfma_tile = [&](const TileIn& in, f32x16 (&acc)[kSets]) {
+    const uint32_t cw[8] = {in.c0.x, in.c0.y, in.c0.z, in.c0.w, in.c1.x, in.c1.y, in.c1.z, in.c1.w};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka = fp4x8_bf16(cw[kk]);
+    for (int s = 0; s < kSets; ++s) acc[s] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < kSets; ++s)
-          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s][kk], acc[s], 0, 0, 0);
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 ka = fp4x8_bf16(cw[kk]);
+#pragma unroll
+      for (int s = 0; s < kSets; ++s)
+        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s][kk], acc[s], 0, 0, 0);
+    }
+  };
+  // this lane's 16 entries of a tile: 16 half .. + 15; the scores are scaled in place, every
+  // lane taking group g's scales from lane g of its quad
+  auto screen_math = [&](const float (&sc)[4], f32x16 (&acc)[kSets], uint64_t (&m)[kSets], bool (&cand)[kSets]) {
+    float ow[kSets][4];
+#pragma unroll
+    for (int s = 0; s < kSets; ++s) {
+      ow[s][0] = sc[0], ow[s][1] = sc[1], ow[s][2] = sc[2], ow[s][3] = sc[3];
+      // a copy per set, so that each broadcast has one use and becomes the DPP operand of
+      // its multiply
+      if (s > 0) asm("" : "+v"(ow[s][0]), "+v"(ow[s][1]), "+v"(ow[s][2]), "+v"(ow[s][3]));
+    }
+#pragma unroll
+    for (int s = 0; s < kSets; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[s][i] *= quad_bcast<0>(ow[s][i]);
+        acc[s][4 + i] *= quad_bcast<1>(ow[s][i]);
+        acc[s][8 + i] *= quad_bcast<2>(ow[s][i]);
+        acc[s][12 + i] *= quad_bcast<3>(ow[s][i]);
       }
-    };
-    auto screen = [&](int tt, const f32x16 (&acc)[kSets]) {
-      // this lane's 16 entries: e0 .. e0 + 15, their scales at stage rows 8 g + 4 half + i
-      const int e0 = st_e0 + tt * 32 + 16 * half;
-      float4 sc[4];
+      const f32x16& v = acc[s];
+      const float m0 = vmax3(v[0], v[1], v[2]), m1 = vmax3(v[3], v[4], v[5]), m2 = vmax3(v[6], v[7], v[8]);
+      const float m3 = vmax3(v[9], v[10], v[11]), m4 = vmax3(v[12], v[13], v[14]);
+      const float mx = vmax3(vmax3(m0, m1, m2), vmax3(m3, m4, v[15]), m0);
+      cand[s] = mx >= th[s];
+      m[s] = __ballot(cand[s]);
+    }
+  };
+  auto screen_emit = [&](int tt, const f32x16 (&acc)[kSets], const uint64_t (&m)[kSets],
+                         const bool (&cand)[kSets]) {
+    const uint32_t tag_e = (uint32_t)(tt * 32 + 16 * half) << 8;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) sc[g] = s_sc[buf][tt * 8 + 2 * g + half];
-      const uint32_t tag_e = (uint32_t)(e0 - e_begin) << 8;
+    for (int s = 0; s < kSets; ++s) {
+      if (m[s] != 0ull) {  // wave-uniform
+        if (cand[s]) {
+          const uint32_t j = qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(m[s] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m[s], 0u));
+          float4* p = rq + j;
 #pragma unroll
-      for (int s = 0; s < kSets; ++s) {
-        float v[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          v[4 * g] = acc[s][4 * g] * sc[g].x;
-          v[4 * g + 1] = acc[s][4 * g + 1] * sc[g].y;
-          v[4 * g + 2] = acc[s][4 * g + 2] * sc[g].z;
-          v[4 * g + 3] = acc[s][4 * g + 3] * sc[g].w;
+          for (int g = 0; g < 4; ++g)
+            p[g * kRecQueue] = make_float4(acc[s][4 * g], acc[s][4 * g + 1], acc[s][4 * g + 2], acc[s][4 * g + 3]);
+          rt[j] = (uint32_t)(wave * kWaveRows + 32 * s + rl) | tag_e;
         }
-        const float m0 = vmax3(v[0], v[1], v[2]), m1 = vmax3(v[3], v[4], v[5]), m2 = vmax3(v[6], v[7], v[8]);
-        const float m3 = vmax3(v[9], v[10], v[11]), m4 = vmax3(v[12], v[13], v[14]);
-        const float mx = vmax3(vmax3(m0, m1, m2), vmax3(m3, m4, v[15]), m0);
-        const bool cand = mx >= th[s];
-        const uint64_t m = __ballot(cand);
-        if (m != 0ull) {  // wave-uniform
-          if (cand) {
-            const uint32_t j = qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            float4* p = rq + j;
+        qn += (uint32_t)__popcll(m[s]);
+        if (qn >= (uint32_t)kRecBatch) {
+          drain((uint32_t)kRecBatch);
+          // the rest (fewer than a batch) to the front, after every read of the batch (the
+          // wave's LDS operations complete in order)
+          const uint32_t rest = qn - (uint32_t)kRecBatch;
+          const uint32_t j = (uint32_t)lane;
+          if (j < rest) {
+            float4 x[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) p[g * kRecQueue] = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-            rt[j] = (uint32_t)(wave * kWaveRows + 32 * s + rl) | tag_e;
+            for (int g = 0; g < 4; ++g) x[g] = rq[g * kRecQueue + kRecBatch + j];
+            const uint32_t tg = rt[kRecBatch + j];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) rq[g * kRecQueue + j] = x[g];
+            rt[j] = tg;
           }
-          qn += (uint32_t)__popcll(m);
-          if (qn >= (uint32_t)kRecBatch) {
-            drain((uint32_t)kRecBatch);
-            // the rest (fewer than a batch) to the front, after every read of the batch (the
-            // wave's LDS operations complete in order)
-            const uint32_t rest = qn - (uint32_t)kRecBatch;
-            const uint32_t j = (uint32_t)lane;
-            if (j < rest) {
-              float4 x[4];
-#pragma unroll
-              for (int g = 0; g < 4; ++g) x[g] = rq[g * kRecQueue + kRecBatch + j];
-              const uint32_t tg = rt[kRecBatch + j];
-#pragma unroll
-              for (int g = 0; g < 4; ++g) rq[g * kRecQueue + j] = x[g];
-              rt[j] = tg;
-            }
-            qn = rest;
-          }
+          qn = rest;
         }
       }
-    };
-    if (n_tt > 0) {
-      f32x16 a0[kSets], a1[kSets];
-      mfma_tile(0, a0);
-      int tt = 1;
-      for (; tt + 1 < n_tt; tt += 2) {
-        mfma_tile(tt, a1);
-        screen(tt - 1, a0);
-        mfma_tile(tt + 1, a0);
-        screen(tt, a1);
-      }
-      if (tt < n_tt) {
-        mfma_tile(tt, a1);
-        screen(tt - 1, a0);
-        screen(tt, a1);
-      } else {
-        screen(tt - 1, a0);
-      }
+    }
+  };
+  // one tile's MFMAs (16) with the screening arithmetic of the tile before it: the first A
+  // conversions, then an MFMA every few vector instructions
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+#pragma unroll
+    for (int i = 0; i < 2 * 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    }
+  };
+  if (n_tiles > 0) {
+    f32x16 a0[kSets], a1[kSets];
+    uint64_t m[kSets];
+    bool cand[kSets];
+    TileIn in0, in1;
+    float sc0[4], sc1[4];
+    load_tile(0, in0);
+    load_tile(1, in1);
+    mfma_tile(in0, a0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc0[i] = in0.sc[i];
+    load_tile(2, in0);
+    int tt = 1;
+    for (; tt + 1 < n_tiles; tt += 2) {
+      mfma_tile(in1, a1);
+      screen_math(sc0, a0, m, cand);
+      interleave();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc1[i] = in1.sc[i];
+      load_tile(tt + 2, in1);
+      screen_emit(tt - 1, a0, m, cand);
+      mfma_tile(in0, a0);
+      screen_math(sc1, a1, m, cand);
+      interleave();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc0[i] = in0.sc[i];
+      load_tile(tt + 3, in0);
+      screen_emit(tt, a1, m, cand);
+    }
+    if (tt < n_tiles) {
+      mfma_tile(in1, a1);
+      screen_math(sc0, a0, m, cand);
+      screen_emit(tt - 1, a0, m, cand);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc1[i] = in1.sc[i];
+      screen_math(sc1, a1, m, cand);
+      screen_emit(tt, a1, m, cand);
+    } else {
+      screen_math(sc0, a0, m, cand);
+      screen_emit(tt - 1, a0, m, cand);
     }
   }
   drain(qn);

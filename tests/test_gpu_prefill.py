@@ -82,6 +82,8 @@ def _case(N, ratio, T, pos0, k, seed, zero_q=False):
     (6000, 2, 330, 11660, 256),   # two row blocks, the second ragged inside a wave's row sets
     (8192, 4, 300, 32468, 512),   # V4-style 4:1 compression: one entry per four tokens
     (3000, 4, 64, 0, 512),        # 4:1 from the start of a sequence: rows see 0..16 entries
+    (5003, 2, 50, 9956, 512),     # entry count not a multiple of 4: last rows see every entry
+    (301, 1, 20, 281, 16),        # likewise, a single tile row block
 ])
 def test_prefill_all_rows(N, ratio, T, pos0, k):
     log(f"prefill N={N} ratio={ratio} T={T} pos0={pos0} k={k}")
