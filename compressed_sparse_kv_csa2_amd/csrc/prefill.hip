@@ -144,6 +144,13 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf
 // so that 16 consecutive entries' reads of one block land in 16 distinct bank groups.
 __device__ __forceinline__ int stage_blk(int i, int b) { return i * 4 + (b ^ ((i >> 2) & 3)); }
 
+// The entry (within its tile of 32) at A row r: the inverse of e -> 8 ((e >> 2) & 3) +
+// 4 (e >> 4) + (e & 3).
+__device__ __forceinline__ int row_entry(int r) { return ((r >> 2) & 1) << 4 | (r >> 3) << 2 | (r & 3); }
+// A raw buffer over n bytes: loads at offsets past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int n_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n_bytes, 0x00020000);
+}
 // PASS 1: group maxima.
 // Accumulator layout of v_mfma_f32_32x32x16_bf16: lane l holds column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  Operands: lane l holds row/column l % 32 and
@@ -157,8 +164,6 @@ template <int STRIDE, int SPLIT>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gmax(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
-  __shared__ uint4 s_code[2][kStage * 4];   // 2 x 16 KiB
-  __shared__ float s_sc[2][kStage];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wg_row0 = blockIdx.x * kGemmRows;
   const int row0 = wg_row0 + wave * kWaveRows;
@@ -173,12 +178,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gmax(
   // columns a row sees: the entries it sees, in columns
   auto vis_cols = [&](int64_t pos) { return (visible(pos, ratio, n_entries) + STRIDE - 1) / STRIDE; };
 
-  // columns any row of the workgroup can see, and of this wave's rows
-  const int wg_nmax = vis_cols(pos0 + min(wg_row0 + kGemmRows - 1, T - 1));
+  // columns the wave's rows see: at most, and at least
   const int wave_nmax = row0 < T ? vis_cols(pos0 + min(row0 + kWaveRows - 1, T - 1)) : 0;
   const int wave_nmin = row0 < T ? vis_cols(pos0 + row0) : 0;
-  const int e_stop = min(e_end, wg_nmax);
-  const int n_active = e_stop > e_begin ? (e_stop - e_begin + kStage - 1) / kStage : 0;
 
   // A operands: query row row0 + 32*s + rl, dims 64*half .. +63
   bf16x8 a[kSets][8];
@@ -202,90 +204,112 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_gmax(
   };
   auto wrow_h = [&](int s, int r) { return 32 * s + 8 * (r >> 2) + (r & 3); };  // wrow - 4*half
 
-  // one entry per thread per stage: 4 x 16 code bytes + scale, clamped to a real entry
-  uint4 pc0 = make_uint4(0u, 0u, 0u, 0u), pc1 = pc0, pc2 = pc0, pc3 = pc0;
-  float psc = 0.f;
-  auto load_stage = [&](int st) {
-    const int e = min(e_begin + st * kStage + tid, n_cols - 1) * STRIDE;
-    const uint4* cp = reinterpret_cast<const uint4*>(codes + (size_t)e * kIdxCodeBytes);
-    pc0 = cp[0];
-    pc1 = cp[1];
-    pc2 = cp[2];
-    pc3 = cp[3];
-    psc = scale[e];
+  // B operands straight from memory, two tiles ahead: lane (rl, half) takes code bytes
+  // 32 half .. + 31 of column e0 + rl (entry STRIDE * column) and its scale.  Columns past
+  // the end read as zeros (range-checked buffer loads); their maxima are never published.
+  const __amdgpu_buffer_rsrc_t rs_code = buffer_over(codes, n_entries * kIdxCodeBytes);
+  const __amdgpu_buffer_rsrc_t rs_scale = buffer_over(scale, n_entries * 4);
+  // tiles of 32 columns that some row of the wave sees (wave-uniform)
+  const int n_tiles = max(0, (min(e_end, wave_nmax) - e_begin + 31) / 32);
+  struct TileIn {
+    uint4 c0, c1;
+    float sc;
   };
-  if (n_active > 0) load_stage(0);
+  auto load_tile = [&](int tt, TileIn& in) {
+    const int ct = min(tt, n_tiles - 1);  // past the last tile: a repeat, never used
+    const int e = (e_begin + ct * 32 + rl) * STRIDE;
+    in.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_code, e * kIdxCodeBytes + 32 * half, 0, 0));
+    in.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_code, e * kIdxCodeBytes + 32 * half + 16, 0, 0));
+    in.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_scale, e * 4, 0, 0));
+  };
+  auto mfma_tile = [&](const TileIn& in, f32x16 (&acc)[kSets]) {
+    const uint32_t cw[8] = {in.c0.x, in.c0.y, in.c0.z, in.c0.w, in.c1.x, in.c1.y, in.c1.z, in.c1.w};
+#pragma unroll
+    for (int s = 0; s < kSets; ++s) acc[s] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 bv = fp4x8_bf16(cw[kk]);
+#pragma unroll
+      for (int s = 0; s < kSets; ++s)
+        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][kk], bv, acc[s], 0, 0, 0);
+    }
+  };
 
   float rm[kSets][16];
 #pragma unroll
   for (int s = 0; s < kSets; ++s)
 #pragma unroll
     for (int r = 0; r < 16; ++r) rm[s][r] = -__builtin_inff();
-
-  for (int st = 0; st < n_stages; ++st) {
-    if (st < n_active) {
-      const int buf = st & 1;
-      s_code[buf][stage_blk(tid, 0)] = pc0;
-      s_code[buf][stage_blk(tid, 1)] = pc1;
-      s_code[buf][stage_blk(tid, 2)] = pc2;
-      s_code[buf][stage_blk(tid, 3)] = pc3;
-      s_sc[buf][tid] = psc;
-      __syncthreads();
-      if (st + 1 < n_active) load_stage(st + 1);  // in flight during the MFMAs
-
-      const int st_e0 = e_begin + st * kStage;
-      for (int tt = 0; tt < kStage / 32; ++tt) {
-        const int e0 = st_e0 + tt * 32;
-        if (e0 >= wave_nmax) break;  // wave-uniform: the rest of the stage is beyond every row
-        const int i = tt * 32 + rl;  // entry within the stage
-        const uint4 c0 = s_code[buf][stage_blk(i, 2 * half)];
-        const uint4 c1 = s_code[buf][stage_blk(i, 2 * half + 1)];
-        const float sc = s_sc[buf][i];
-        f32x16 acc[kSets];
+  // the running maxima take tile tt's scaled scores (masked at the causal frontier)
+  auto take_max = [&](int tt, float sc, const f32x16 (&acc)[kSets]) {
+    const int e0 = e_begin + tt * 32;
+    if (e0 + 32 <= wave_nmin) {  // wave-uniform: every row sees the tile
 #pragma unroll
-        for (int s = 0; s < kSets; ++s) acc[s] = f32x16{};
-        const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      for (int s = 0; s < kSets; ++s)
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 bv = fp4x8_bf16(cw[kk]);
-#pragma unroll
-          for (int s = 0; s < kSets; ++s)
-            acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][kk], bv, acc[s], 0, 0, 0);
-        }
-        const int col = e0 + rl;
-        if (e0 + 32 <= wave_nmin) {  // wave-uniform: every row sees the tile
-#pragma unroll
-          for (int s = 0; s < kSets; ++s)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) rm[s][r] = vmax(acc[s][r] * sc, rm[s][r]);
-        } else {
-          const int lim = frontier_lim(col);
-#pragma unroll
-          for (int s = 0; s < kSets; ++s)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float v = acc[s][r] * sc;
-              rm[s][r] = lim <= wrow_h(s, r) ? vmax(v, rm[s][r]) : rm[s][r];
-            }
-        }
-      }
-    }
-    if ((st + 1) % kRunStages == 0) {  // end of a run: publish the group maxima
-      const int g = split * groups_per_split + (st / kRunStages) * 32 + rl;
+        for (int r = 0; r < 16; ++r) rm[s][r] = vmax(acc[s][r] * sc, rm[s][r]);
+    } else {
+      const int lim = frontier_lim(e0 + rl);
 #pragma unroll
       for (int s = 0; s < kSets; ++s)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int t = row0 + wrow(s, r);
-          if (t < T) {
-            const uint16_t key16 =
-                rm[s][r] == -__builtin_inff() ? (uint16_t)0 : (uint16_t)(score_key(rm[s][r]) >> 16);
-            ws.gmax[(size_t)t * ws.G + g] = key16;
-          }
-          rm[s][r] = -__builtin_inff();
+          const float v = acc[s][r] * sc;
+          rm[s][r] = lim <= wrow_h(s, r) ? vmax(v, rm[s][r]) : rm[s][r];
         }
     }
+  };
+  // group g of the split = lane column rl over the 32 tiles of run `run`
+  auto publish = [&](int run) {
+    const int g = split * groups_per_split + run * 32 + rl;
+#pragma unroll
+    for (int s = 0; s < kSets; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = row0 + wrow(s, r);
+        if (t < T) {
+          const uint16_t key16 =
+              rm[s][r] == -__builtin_inff() ? (uint16_t)0 : (uint16_t)(score_key(rm[s][r]) >> 16);
+          ws.gmax[(size_t)t * ws.G + g] = key16;
+        }
+        rm[s][r] = -__builtin_inff();
+      }
+  };
+  // Tiles in order, each one's loads issued two tiles ahead; a run's maxima are published
+  // after its last tile.
+  constexpr int kRuns = n_stages / kRunStages;
+  int run_done = 0;
+  if (n_tiles > 0) {
+    TileIn in0, in1;
+    load_tile(0, in0);
+    load_tile(1, in1);
+    int tt = 0;
+    for (; tt + 1 < n_tiles; tt += 2) {
+      {
+        f32x16 acc[kSets];
+        mfma_tile(in0, acc);
+        const float sc = in0.sc;
+        load_tile(tt + 2, in0);
+        take_max(tt, sc, acc);  // tt is even: a run (32 tiles) ends only at an odd tile
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one tile's accumulators live at a time
+      {
+        f32x16 acc[kSets];
+        mfma_tile(in1, acc);
+        const float sc = in1.sc;
+        load_tile(tt + 3, in1);
+        take_max(tt + 1, sc, acc);
+        if ((tt + 2) % 32 == 0) publish(run_done++);
+      }
+    }
+    if (tt < n_tiles) {
+      f32x16 acc[kSets];
+      mfma_tile(in0, acc);
+      take_max(tt, in0.sc, acc);
+    }
   }
+  // the run holding the wave's last tile, and the runs past every row of the wave (empty)
+  for (; run_done < kRuns; ++run_done) publish(run_done);
 }
 
 // PASS 2: the candidates.  The same contraction over every entry, taken transposed (the
@@ -305,13 +329,6 @@ constexpr int kRecQueue = 2 * kRecBatch;    // a batch + one tile's worth
 // Queue layout: group g (scores 4 g .. 4 g + 3) of record j at s_rec[wave][g][j], so a
 // record is written with one address and four offsets, and the lanes of one access touch
 // consecutive 16-byte slots.
-// The entry (within its tile of 32) at A row r: the inverse of e -> 8 ((e >> 2) & 3) +
-// 4 (e >> 4) + (e & 3).
-__device__ __forceinline__ int row_entry(int r) { return ((r >> 2) & 1) << 4 | (r >> 3) << 2 | (r & 3); }
-// A raw buffer over n bytes: loads at offsets past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int n_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n_bytes, 0x00020000);
-}
 __global__ __launch_bounds__(kGemmThreads, 2) void k_prefill_hits(
     const uint16_t* __restrict__ q_idx, const uint8_t* __restrict__ codes,
     const float* __restrict__ scale, int n_entries, int ratio, int64_t pos0, int T, PrefillWs ws) {
