@@ -22,7 +22,7 @@ __all__ = [
     "csa2_index_topk_workspace_size", "csa2_select_chain_workspace_size", "csa2_attn_workspace_size", "csa2_prefill_workspace_size",
     "topk_workspace", "index_topk_workspace", "select_chain_workspace", "attn_workspace", "prefill_workspace", "lib_path", "load_library",
     "csa2_prefill_select", "csa2_sparse_attn_prefill", "csa2_kv_append", "csa2_swa_append", "CSA2_TOPK_HIST_FUSED", "Csa2Error",
-    "csa2_workspace_status", "workspace_status", "check_workspace", "csa2_sparse_attn_decode_noalloc",
+    "csa2_workspace_status", "workspace_status", "PreparedCall", "check_workspace", "csa2_sparse_attn_decode_noalloc",
     "check_attention_ids", "csa2_replay_select", "csa2_replay_select_workspace_size",
     "replay_select_workspace",
 ]
@@ -108,6 +108,30 @@ def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+class PreparedCall:
+    """A C-ABI call whose arguments were checked and marshalled once: calling it issues the
+    same call again (same buffers, same stream), for steps that repeat their launches.  The
+    buffers' contents may change between calls; their addresses and shapes may not."""
+
+    __slots__ = ("_fn", "_args", "_pre")
+
+    def __init__(self, fn, args, pre=None):
+        self._fn, self._args, self._pre = fn, args, pre
+
+    def __call__(self):
+        if self._pre is not None:
+            self._pre()
+        _check(self._fn(*self._args))
+
+
+def _issue(fn, args, prepare, pre=None):
+    call = PreparedCall(fn, args, pre)
+    if prepare:
+        return call
+    call()
+    return None
 
 
 def _need(t: torch.Tensor, name: str, dtypes, shape=None):
@@ -252,8 +276,9 @@ def csa2_topk(scores, n_valid, k, idx_out, score_out=None, cand=None, hist_fused
 
 
 def csa2_index_topk(q_idx, idx_codes, idx_scale, seq_base, n_valid, k, idx_out, workspace,
-                    n_cols, score_out=None, cand=None, stream=None):
-    """csa2_index_score + csa2_topk in one call: idx_out [B, k] of the n_cols columns."""
+                    n_cols, score_out=None, cand=None, stream=None, prepare=False):
+    """csa2_index_score + csa2_topk in one call: idx_out [B, k] of the n_cols columns.
+    prepare=True returns the checked call as a PreparedCall instead of issuing it."""
     B = q_idx.shape[0]
     _need(q_idx, "q_idx", _BF16, (B, 128))
     _need(idx_codes, "idx_codes", _U8, (None, 64))
@@ -267,17 +292,18 @@ def csa2_index_topk(q_idx, idx_codes, idx_scale, seq_base, n_valid, k, idx_out, 
         _need(cand, "cand", (torch.int32,), (B, n_cols))
     _need(workspace, "workspace", _U8)
     lib = load_library()
-    _check(lib.csa2_index_topk(_ptr(q_idx), _ptr(idx_codes), _ptr(idx_scale), _ptr(seq_base),
-                               _ptr(n_valid), _ptr(cand), B, n_cols, k, _ptr(idx_out),
-                               _ptr(score_out), _ptr(workspace), workspace.numel(),
-                               _stream(stream)))
+    return _issue(lib.csa2_index_topk,
+                  (_ptr(q_idx), _ptr(idx_codes), _ptr(idx_scale), _ptr(seq_base), _ptr(n_valid),
+                   _ptr(cand), B, n_cols, k, _ptr(idx_out), _ptr(score_out), _ptr(workspace),
+                   workspace.numel(), _stream(stream)), prepare)
 
 
 def csa2_select_chain(q_full, idx_codes, idx_scale, seq_base, n_valid, n_cols, pool_out, workspace,
                       k=512, pool_score_out=None, own_out=None, q_re=None, re_out=None,
-                      re_score_out=None, stream=None):
+                      re_score_out=None, stream=None, prepare=False):
     """Full scan -> pool_out [B, pool_k]; own_out [B, k] (the Full layer's top-k inside the
-    pool); re_out [R, B, k] for the Reindex queries q_re [R, B, 128]."""
+    pool); re_out [R, B, k] for the Reindex queries q_re [R, B, 128].  prepare=True returns
+    the checked call as a PreparedCall instead of issuing it."""
     B, pool_k = pool_out.shape
     _need(q_full, "q_full", _BF16, (B, 128))
     _need(idx_codes, "idx_codes", _U8, (None, 64))
@@ -298,11 +324,11 @@ def csa2_select_chain(q_full, idx_codes, idx_scale, seq_base, n_valid, n_cols, p
             _need(re_score_out, "re_score_out", (torch.float32,), (n_re, B, k))
     _need(workspace, "workspace", _U8)
     lib = load_library()
-    _check(lib.csa2_select_chain(_ptr(q_full), _ptr(idx_codes), _ptr(idx_scale), _ptr(seq_base),
-                                 _ptr(n_valid), B, n_cols, pool_k, _ptr(pool_out),
-                                 _ptr(pool_score_out), k, _ptr(own_out), _ptr(q_re), n_re,
-                                 _ptr(re_out), _ptr(re_score_out), _ptr(workspace),
-                                 workspace.numel(), _stream(stream)))
+    return _issue(lib.csa2_select_chain,
+                  (_ptr(q_full), _ptr(idx_codes), _ptr(idx_scale), _ptr(seq_base), _ptr(n_valid), B,
+                   n_cols, pool_k, _ptr(pool_out), _ptr(pool_score_out), k, _ptr(own_out),
+                   _ptr(q_re), n_re, _ptr(re_out), _ptr(re_score_out), _ptr(workspace),
+                   workspace.numel(), _stream(stream)), prepare)
 
 
 def csa2_replay_select(q_idx, idx_codes, idx_scale, n_entries, ratio, pos0, pool_out, workspace,
@@ -352,12 +378,17 @@ def _ids_checked() -> bool:
 
 
 def csa2_sparse_attn_decode(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, out, workspace,
-                            softmax_scale=512 ** -0.5, stream=None, n_entries=None):
+                            softmax_scale=512 ** -0.5, stream=None, n_entries=None, prepare=False):
     """out [B, 16, 512] f32: one softmax over the selected entries and the window rows.
     When n_entries (int32 [B]) is given and the environment sets CSA2_CHECK_IDS=1, the list
-    is range-checked on the host first (check_attention_ids)."""
+    is range-checked on the host before each issue (check_attention_ids).  prepare=True
+    returns the checked call as a PreparedCall instead of issuing it."""
+    pre = None
     if idx is not None and n_entries is not None and _ids_checked():
-        check_attention_ids(idx, n_entries)
+        if prepare:
+            pre = lambda: check_attention_ids(idx, n_entries)
+        else:
+            check_attention_ids(idx, n_entries)
     B = q.shape[0]
     _need(q, "q", _BF16, (B, 16, 512))
     _need(kv_codes, "kv_codes", _U8, (None, 256))
@@ -372,10 +403,10 @@ def csa2_sparse_attn_decode(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, 
     _need(out, "out", (torch.float32,), (B, 16, 512))
     _need(workspace, "workspace", _U8)
     lib = load_library()
-    _check(lib.csa2_sparse_attn_decode(_ptr(q), _ptr(kv_codes), _ptr(kv_scale), _ptr(seq_base),
-                                       _ptr(idx) if k > 0 else None, k, _ptr(swa), _ptr(swa_len),
-                                       float(softmax_scale), B, _ptr(out), _ptr(workspace),
-                                       workspace.numel(), _stream(stream)))
+    return _issue(lib.csa2_sparse_attn_decode,
+                  (_ptr(q), _ptr(kv_codes), _ptr(kv_scale), _ptr(seq_base),
+                   _ptr(idx) if k > 0 else None, k, _ptr(swa), _ptr(swa_len), float(softmax_scale), B,
+                   _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)), prepare, pre)
 
 
 def csa2_sparse_attn_decode_noalloc(q, kv_codes, kv_scale, seq_base, idx, swa, swa_len, out,

@@ -61,6 +61,7 @@ class DecodePass:
         self.pool_valid = torch.full((batch,), pool, dtype=torch.int32, device=dev)
         self.lists = {l: torch.empty((batch, k), dtype=torch.int32, device=dev) for l in SELECTING}
         self.out = torch.empty((N_LAYERS, batch, 16, 512), dtype=torch.float32, device=dev)
+        self._calls, self._calls_key = None, None  # the prepared calls of the last inputs
 
     def workspaces(self):
         """The selection workspaces whose status block (csa2_workspace_status) reports errors."""
@@ -70,37 +71,73 @@ class DecodePass:
         """enc_caches: three entry caches (layers 2, 8, 14); dec_cache: the decoder's.
         q_idx: {selecting layer: bf16 [batch, 128]}; q: bf16 [40, batch, 16, 512];
         swa: E4M3 [40, batch, 128, 512]; swa_len: int32 [batch].  marks (optional): four
-        events recorded before layer 0, around the decoder's Full selection and at the end."""
+        events recorded before layer 0, around the decoder's Full selection and at the end.
+
+        The 40 layers' calls are checked and marshalled once and issued again on later steps
+        whose inputs are the same buffers (addresses, shapes, strides, dtypes) on the same
+        stream: the host's cost per call is then the C call alone."""
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        key = self._key(enc_caches, dec_cache, q_idx, q, swa, swa_len, stream)
+        if key != self._calls_key:
+            self._calls = self._prepare(enc_caches, dec_cache, q_idx, q, swa, swa_len, stream)
+            self._calls_key = key
         if marks is not None:
             marks[0].record(stream)
+        for l, (select, attend) in enumerate(self._calls):
+            if l == DECODER_FULL and marks is not None:
+                marks[1].record(stream)
+            if select is not None:
+                select()
+            if l == DECODER_FULL and marks is not None:
+                marks[2].record(stream)
+            attend()
+        if marks is not None:
+            marks[3].record(stream)
+
+    @staticmethod
+    def _key(enc_caches, dec_cache, q_idx, q, swa, swa_len, stream):
+        def t(x):
+            return (x.data_ptr(), tuple(x.shape), x.stride(), x.dtype)
+
+        def cache(c):
+            return (t(c.idx_codes), t(c.idx_scale), t(c.seq_base), t(c.n_entries), t(c.kv_codes),
+                    t(c.kv_scale))
+
+        return (stream.cuda_stream, tuple(cache(c) for c in enc_caches), cache(dec_cache),
+                tuple(t(q_idx[l]) for l in SELECTING), t(q), t(swa), t(swa_len))
+
+    def _prepare(self, enc_caches, dec_cache, q_idx, q, swa, swa_len, stream):
+        """(selection or None, attention) per layer, checked and marshalled."""
+        calls = []
         for l in range(N_LAYERS):
+            select = None
             if l in ENCODER_FULL:
                 c = enc_caches[ENCODER_FULL.index(l)]
-                csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries, self.K,
-                                self.lists[l], self.enc_ws, self.n_enc, stream=stream)
+                select = csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                                         self.K, self.lists[l], self.enc_ws, self.n_enc, stream=stream,
+                                         prepare=True)
             elif l == DECODER_FULL:
                 c = dec_cache
-                if marks is not None:
-                    marks[1].record(stream)
-                csa2_select_chain(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
-                                  self.n_dec, self.pool, self.dec_ws, k=self.K,
-                                  own_out=self.lists[l], stream=stream)
-                if marks is not None:
-                    marks[2].record(stream)
+                select = csa2_select_chain(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, c.n_entries,
+                                           self.n_dec, self.pool, self.dec_ws, k=self.K,
+                                           own_out=self.lists[l], stream=stream, prepare=True)
             elif l in REINDEX:
                 c = dec_cache
-                csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid, self.K,
-                                self.lists[l], self.re_ws, self.P, cand=self.pool, stream=stream)
+                select = csa2_index_topk(q_idx[l], c.idx_codes, c.idx_scale, c.seq_base, self.pool_valid,
+                                         self.K, self.lists[l], self.re_ws, self.P, cand=self.pool,
+                                         stream=stream, prepare=True)
             if l in WINDOW_ONLY:
                 c, idx = dec_cache, None
             else:
                 src = list_source(l)
                 c = dec_cache if src >= DECODER_FULL else enc_caches[ENCODER_FULL.index(src)]
                 idx = self.lists[src]
-            csa2_sparse_attn_decode(q[l], c.kv_codes, c.kv_scale, c.seq_base, idx, swa[l], swa_len,
-                                    self.out[l], self.attn_ws, stream=stream)
-        if marks is not None:
-            marks[3].record(stream)
+            attend = csa2_sparse_attn_decode(q[l], c.kv_codes, c.kv_scale, c.seq_base, idx, swa[l],
+                                             swa_len, self.out[l], self.attn_ws, stream=stream,
+                                             prepare=True)
+            calls.append((select, attend))
+        return calls
 
 
 class ReplayChunk:
