@@ -168,3 +168,39 @@ def test_graph_replay_equals_eager():
         got = [run.out] + list(run.lists.values())
         assert all(torch.equal(x, y) for x, y in zip(ref, got)), f"replay {rep} differs from eager"
     assert_ws_ok(*run.workspaces())
+
+
+def test_decode_pass_prepares_again_for_new_inputs():
+    # DecodePass reuses its checked and marshalled calls while the inputs are the same
+    # buffers.  A step on other buffers (new queries and windows) must give what a fresh pass
+    # gives on them, and going back to the first buffers must give the first results again.
+    B, n_enc, n_dec = 2, 16384, 32768
+    log(f"model pass re-preparation B={B} enc={n_enc} dec={n_dec}")
+    enc = [synth.make_entries([n_enc] * B, seed=5, device=DEV, field_base=10 * (i + 1)) for i in range(3)]
+    dec = synth.make_entries([n_dec] * B, seed=5, device=DEV)
+    swa_len = torch.tensor([128, 90], dtype=torch.int32, device=DEV)
+
+    def inputs(seed):
+        q_idx = {l: synth.make_index_queries(B, seed, device=DEV, sub=l) for l in model.SELECTING}
+        q = torch.stack([synth.make_queries(B, seed, device=DEV, sub=l) for l in range(40)]).contiguous()
+        swa = torch.stack([synth.make_swa(B, 128, seed, device=DEV, sub=l) for l in range(40)]).contiguous()
+        return q_idx, q, swa
+
+    a, b = inputs(11), inputs(12)
+    run = model.DecodePass(B, n_enc, n_dec, device=DEV)
+    run.step(enc, dec, *a, swa_len)
+    torch.cuda.synchronize()
+    out_a, lists_a = h(run.out).copy(), {l: h(t).copy() for l, t in run.lists.items()}
+    run.step(enc, dec, *b, swa_len)
+    torch.cuda.synchronize()
+    fresh = model.DecodePass(B, n_enc, n_dec, device=DEV)
+    fresh.step(enc, dec, *b, swa_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(h(run.out), h(fresh.out)), "outputs on new inputs differ from a fresh pass"
+    assert all(np.array_equal(h(run.lists[l]), h(fresh.lists[l])) for l in run.lists)
+    assert not np.array_equal(h(run.out), out_a), "the second inputs gave the first outputs"
+    run.step(enc, dec, *a, swa_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(h(run.out), out_a)
+    assert all(np.array_equal(h(run.lists[l]), lists_a[l]) for l in run.lists)
+    assert_ws_ok(*run.workspaces(), *fresh.workspaces())
